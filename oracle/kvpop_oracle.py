@@ -1,0 +1,373 @@
+"""Oracle for the KVpop fixed-budget KV-cache hot path (plain, slow, float64, CPU).
+
+TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import this module.  It shares no code,
+header, table or helper with the HIP library under ``fixed_budget_sparse_amd/``,
+and it never imports that package.
+
+Sources (cited by page title; the section / equation named after each):
+  [Notes]  "KVpop -- Key-Value Cache Compression with Predictive Online Pruning
+           精读笔记" (reading notes, liuzhao09.github.io).  The only page with the
+           method's formulas: B = s + w + k (§2.1), future mass m_t (§2.2),
+           eligible set E(q) (§2.2), Eq. (8) (§2.3), Figure 2 (§2.3), sparse
+           mask M_{q,t} and the rank cutoff tau_q (§2.3), delayed readout (§2.4).
+  [Sum-zh] "技术摘要：KVpop — 基于预测性在线剪枝的键值（KV）缓存压缩"
+           (gist.science summary): budget regions (§2.1), transposed pass
+           returning LSE (§2.2), running threshold over static priorities (§2.4).
+  [Trust]  "信任质量：KV-Cache淘汰中的强制权重" (forced weights in KV-cache
+           eviction): Definition 2.1 (renormalised subset operator m_A) and the
+           identity in the proof of Lemma 2.1.
+
+Arithmetic is float64 (the pages fix no precision); integer outputs are exact.
+
+Readings of points the pages leave open (each also listed in the design notes):
+  R1 causality: the mask of [Notes] §2.3 has no t <= q term; keys after the
+     query are never kept (the teacher is dense *causal* attention, [Notes] §2.2).
+  R2 softmax scale defaults to 1/sqrt(D).
+  R3 LSE is a natural log (Eq. (8) uses exp/log).
+  R4 the target takes the caller's LSE; parity uses the dense causal LSE.
+  R5 the target is the first term of Eq. (8) per query head: no -log N_t, no
+     epsilon, no average over the query group; an empty range gives -inf.
+  R6 priority order: higher priority first, ties to the lower token index;
+     -0 == +0; NaN is treated as -inf.
+  R7 tau_q = INT32_MAX when fewer than k tokens are eligible, -1 when k = 0.
+  R8 query head h reads KV head h // (Hq / Hkv); priorities are per KV head.
+  R9 decode order within a step: token p enters the window, then the token
+     u = p - w leaving the window is kept (if fewer than k long-range tokens are
+     held) or replaces the worst held long-range token iff its priority is
+     strictly larger (worst = lowest priority, ties: highest position), else is
+     dropped; then the step attends.
+"""
+from __future__ import annotations
+
+import math
+from typing import Dict, List, Optional, Sequence
+
+import numpy as np
+
+INT32_MAX = 2 ** 31 - 1
+
+
+# --------------------------------------------------------------------------
+# Priority order and rank  ([Notes] §2.3: rank(t) is the place of token t when
+# tokens are ordered by their static priority; reading R6 for ties/NaN)
+# --------------------------------------------------------------------------
+def canonical_priority(p: np.ndarray) -> np.ndarray:
+    """NaN -> -inf and -0 -> +0 (reading R6)."""
+    p = np.array(p, dtype=np.float64, copy=True)
+    p[np.isnan(p)] = -np.inf
+    p[p == 0.0] = 0.0
+    return p
+
+
+def priority_rank(prio_row: np.ndarray) -> np.ndarray:
+    """rank[t] = position of token t in the order (priority desc, index asc)."""
+    p = canonical_priority(prio_row)
+    S = p.shape[0]
+    order = np.lexsort((np.arange(S), -p))   # primary key -p, then the index
+    rank = np.empty(S, dtype=np.int64)
+    rank[order] = np.arange(S)
+    return rank
+
+
+def priority_ranks(prio: np.ndarray) -> np.ndarray:
+    """priority_rank over every leading index of prio[..., S]."""
+    flat = prio.reshape(-1, prio.shape[-1])
+    out = np.stack([priority_rank(r) for r in flat])
+    return out.reshape(prio.shape)
+
+
+# --------------------------------------------------------------------------
+# Eligible set and long-range top-k  ([Notes] §2.2: E(q) = {t | s <= t <= q - w};
+# [Notes] §2.1 / [Sum-zh] §2.1: k long-range slots among the older tokens)
+# --------------------------------------------------------------------------
+def eligible(q: int, s: int, w: int) -> range:
+    return range(s, max(s, q - w + 1))
+
+
+def kept_long_by_sorting(prio_row: np.ndarray, q: int, s: int, w: int, k: int) -> List[int]:
+    """The long-range kept set at query q: sort E(q) by (priority desc, index
+    asc) and take the first min(k, |E(q)|) tokens."""
+    p = canonical_priority(prio_row)
+    E = list(eligible(q, s, w))
+    E.sort(key=lambda t: (-p[t], t))
+    return sorted(E[:min(k, len(E))])
+
+
+def tau_from_kept(rank_row: np.ndarray, kept_long: Sequence[int], n_eligible: int, k: int) -> int:
+    """tau_q: the rank of the k-th best eligible token (reading R7 for the
+    sentinels)."""
+    if k == 0:
+        return -1
+    if n_eligible < k:
+        return INT32_MAX
+    return int(max(rank_row[t] for t in kept_long))
+
+
+def thresholds_by_sorting(prio: np.ndarray, s: int, w: int, k: int,
+                          rows: Optional[Sequence[int]] = None):
+    """rank[..., S] and tau[..., rows] by sorting E(q) per row (slow: for tiny
+    and sampled cases)."""
+    rank = priority_ranks(prio)
+    S = prio.shape[-1]
+    rows = list(range(S)) if rows is None else list(rows)
+    flat_p = prio.reshape(-1, S)
+    flat_r = rank.reshape(-1, S)
+    tau = np.empty((flat_p.shape[0], len(rows)), dtype=np.int64)
+    for i in range(flat_p.shape[0]):
+        for j, q in enumerate(rows):
+            L = kept_long_by_sorting(flat_p[i], q, s, w, k)
+            tau[i, j] = tau_from_kept(flat_r[i], L, len(eligible(q, s, w)), k)
+    return rank, tau.reshape(prio.shape[:-1] + (len(rows),))
+
+
+def thresholds_by_selection(rank: np.ndarray, s: int, w: int, k: int,
+                            rows: Optional[Sequence[int]] = None) -> np.ndarray:
+    """tau[..., rows]: the k-th smallest of rank[s .. q-w] (np.partition), a
+    second route to the same cutoff."""
+    S = rank.shape[-1]
+    rows = list(range(S)) if rows is None else list(rows)
+    flat = rank.reshape(-1, S)
+    tau = np.empty((flat.shape[0], len(rows)), dtype=np.int64)
+    for j, q in enumerate(rows):
+        n = len(eligible(q, s, w))
+        if k == 0:
+            tau[:, j] = -1
+        elif n < k:
+            tau[:, j] = INT32_MAX
+        else:
+            seg = flat[:, s:q - w + 1]
+            tau[:, j] = np.partition(seg, k - 1, axis=1)[:, k - 1]
+    return tau.reshape(rank.shape[:-1] + (len(rows),))
+
+
+# --------------------------------------------------------------------------
+# Sparse mask  ([Notes] §2.3: M_{q,t} = 1[t<s] or 1[q-t<w] or (1[t in E(q)] and
+# 1[rank(t) <= tau_q]); reading R1 adds t <= q)
+# --------------------------------------------------------------------------
+def mask_rows(rank_row: np.ndarray, tau_rows: np.ndarray, qs: np.ndarray, s: int, w: int) -> np.ndarray:
+    """Boolean mask [len(qs), S] from rank and per-row cutoffs."""
+    S = rank_row.shape[0]
+    t = np.arange(S)[None, :]
+    q = np.asarray(qs)[:, None]
+    tau = np.asarray(tau_rows, dtype=np.int64)[:, None]
+    in_e = (t >= s) & (t <= q - w)
+    m = (t < s) | (q - t < w) | (in_e & (rank_row[None, :] <= tau))
+    return m & (t <= q)
+
+
+def kept_row_by_sorting(prio_row: np.ndarray, q: int, s: int, w: int, k: int) -> np.ndarray:
+    """Sorted kept positions of row q: sinks, window, long-range top-k."""
+    L = set(kept_long_by_sorting(prio_row, q, s, w, k))
+    return np.array([t for t in range(q + 1) if t < s or q - t < w or t in L], dtype=np.int64)
+
+
+# --------------------------------------------------------------------------
+# Attention over a kept set  ([Notes] Figure 1 / §2.3: softmax over the retained
+# set, LSE returned; [Trust] Definition 2.1: the renormalised subset mean m_A)
+# --------------------------------------------------------------------------
+def _attend(z: np.ndarray, v: np.ndarray, keep: np.ndarray):
+    """z [n, S] logits, v [S, D], keep [n, S] -> O [n, D], LSE [n] (natural log)."""
+    z = np.where(keep, z, -np.inf)
+    mx = z.max(axis=1)
+    mx_safe = np.where(np.isfinite(mx), mx, 0.0)
+    e = np.exp(z - mx_safe[:, None])
+    den = e.sum(axis=1)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        lse = np.log(den) + mx_safe
+        o = (e @ v) / den[:, None]
+    return o, lse
+
+
+def default_scale(D: int, scale: float = 0.0) -> float:
+    return scale if scale > 0 else 1.0 / math.sqrt(D)
+
+
+def masked_attention(q, k, v, rank, tau, s, w, scale=0.0, rows=None, block=256):
+    """Sparse attention forward with an explicit mask, row block by row block.
+
+    q [b, Hq, S, D]; k, v [b, Hkv, S, D]; rank [b, Hkv, S]; tau [b, Hkv, S] (the
+    cutoff of every row).  Returns O [b, Hq, n, D] and LSE [b, Hq, n] (float64)
+    for ``rows`` (default: all S rows)."""
+    b, Hq, S, D = q.shape
+    Hkv = k.shape[1]
+    G = Hq // Hkv
+    sc = default_scale(D, scale)
+    rows = np.arange(S) if rows is None else np.asarray(rows)
+    O = np.zeros((b, Hq, len(rows), D))
+    LSE = np.zeros((b, Hq, len(rows)))
+    for bi in range(b):
+        for hq in range(Hq):
+            h = hq // G                                   # reading R8
+            K = k[bi, h].astype(np.float64)
+            V = v[bi, h].astype(np.float64)
+            for a in range(0, len(rows), block):
+                qs = rows[a:a + block]
+                keep = mask_rows(rank[bi, h], tau[bi, h, qs], qs, s, w)
+                z = sc * (q[bi, hq, qs].astype(np.float64) @ K.T)
+                O[bi, hq, a:a + block], LSE[bi, hq, a:a + block] = _attend(z, V, keep)
+    return O, LSE
+
+
+def dense_causal_attention(q, k, v, scale=0.0, rows=None, block=256):
+    """Dense causal attention (every key t <= q kept): the teacher."""
+    b, Hq, S, D = q.shape
+    Hkv = k.shape[1]
+    G = Hq // Hkv
+    sc = default_scale(D, scale)
+    rows = np.arange(S) if rows is None else np.asarray(rows)
+    O = np.zeros((b, Hq, len(rows), D))
+    LSE = np.zeros((b, Hq, len(rows)))
+    t = np.arange(S)[None, :]
+    for bi in range(b):
+        for hq in range(Hq):
+            h = hq // G
+            K = k[bi, h].astype(np.float64)
+            V = v[bi, h].astype(np.float64)
+            for a in range(0, len(rows), block):
+                qs = rows[a:a + block]
+                keep = t <= qs[:, None]
+                z = sc * (q[bi, hq, qs].astype(np.float64) @ K.T)
+                O[bi, hq, a:a + block], LSE[bi, hq, a:a + block] = _attend(z, V, keep)
+    return O, LSE
+
+
+# --------------------------------------------------------------------------
+# Future-attention target  ([Notes] §2.2: m_t = (1/N_t) sum_{d=t+w}^{S-1} A_{d,t};
+# [Notes] §2.3 Eq. (8) and Figure 2: the transposed pass returns
+# log sum_{d>=t+w} exp(l(d,t) - LSE_d), the first term of Eq. (8); reading R5)
+# --------------------------------------------------------------------------
+def future_target_colsum(q, k, lse, w, scale=0.0, block=256):
+    """Column-sum form: P[d,t] = exp(l(d,t) - LSE_d) over the dense causal map,
+    summed down each column over the future queries d >= t + w, then the log.
+
+    q [b, Hq, S, D], k [b, Hkv, S, D], lse [b, Hq, S] -> target [b, Hq, S]."""
+    b, Hq, S, D = q.shape
+    Hkv = k.shape[1]
+    G = Hq // Hkv
+    sc = default_scale(D, scale)
+    out = np.empty((b, Hq, S))
+    t = np.arange(S)[None, :]
+    for bi in range(b):
+        for hq in range(Hq):
+            K = k[bi, hq // G].astype(np.float64)
+            col = np.zeros(S)
+            for a in range(0, S, block):
+                ds = np.arange(a, min(S, a + block))
+                l = sc * (q[bi, hq, ds].astype(np.float64) @ K.T)
+                P = np.exp(l - lse[bi, hq, ds].astype(np.float64)[:, None])
+                future = t <= ds[:, None] - w        # d >= t + w (implies t <= d)
+                col += np.where(future, P, 0.0).sum(axis=0)
+            with np.errstate(divide="ignore"):
+                out[bi, hq] = np.log(col)
+    return out
+
+
+def future_target_eq8(q, k, lse, w, scale=0.0, ts=None):
+    """Row form of Eq. (8)'s first term: for each token t, a log-sum-exp over the
+    future queries d in [t+w, S) of l(d,t) - LSE_d (the transposed pass of
+    Figure 2, key t acting as the query).  Returns [b, Hq, len(ts)]."""
+    b, Hq, S, D = q.shape
+    Hkv = k.shape[1]
+    G = Hq // Hkv
+    sc = default_scale(D, scale)
+    ts = np.arange(S) if ts is None else np.asarray(ts)
+    out = np.empty((b, Hq, len(ts)))
+    for bi in range(b):
+        for hq in range(Hq):
+            Qh = q[bi, hq].astype(np.float64)
+            kv = k[bi, hq // G].astype(np.float64)
+            L = lse[bi, hq].astype(np.float64)
+            for j, t in enumerate(ts):
+                d0 = t + w
+                if d0 > S - 1:
+                    out[bi, hq, j] = -np.inf
+                    continue
+                x = sc * (Qh[d0:] @ kv[t]) - L[d0:]
+                m = x.max()
+                out[bi, hq, j] = m + math.log(np.exp(x - m).sum())
+    return out
+
+
+# --------------------------------------------------------------------------
+# Decode over a fixed-size cache  ([Notes] §2.3: inference keeps only the
+# compact cache; [Notes] §2.4: token u = q - w is scored when it leaves the
+# window; [Sum-zh] §2.1: sinks, protected window, k long-range slots;
+# reading R9 for the order within a step and the replacement rule)
+# --------------------------------------------------------------------------
+class DecodeState:
+    """Explicit sets of held positions for one (sequence, KV head)."""
+
+    def __init__(self, s: int, w: int, k: int):
+        self.s, self.w, self.k = s, w, k
+        self.sinks: List[int] = []
+        self.window: List[int] = []
+        self.long: Dict[int, float] = {}      # position -> priority
+        self.evicted: set = set()
+
+    def step(self, p: int, prio_leaving: float) -> None:
+        s, w, k = self.s, self.w, self.k
+        if p < s:
+            self.sinks.append(p)
+        else:
+            self.window.append(p)
+        u = p - w
+        if u >= s:
+            assert self.window[0] == u
+            self.window.pop(0)
+            pu = prio_leaving
+            if math.isnan(pu):
+                pu = -math.inf
+            if len(self.long) < k:
+                self.long[u] = pu
+            elif k == 0:
+                self.evicted.add(u)
+            else:
+                # worst held long-range token: lowest priority, ties -> highest position
+                m = min(self.long, key=lambda t: (self.long[t], -t))
+                if pu > self.long[m]:
+                    del self.long[m]
+                    self.evicted.add(m)
+                    self.long[u] = pu
+                else:
+                    self.evicted.add(u)
+
+    def held(self) -> np.ndarray:
+        return np.array(sorted(self.sinks + self.window + list(self.long)), dtype=np.int64)
+
+
+def decode_simulate(prio_table: np.ndarray, s: int, w: int, k: int, n_steps: int,
+                    record: Optional[Sequence[int]] = None):
+    """Run steps p = 0..n_steps-1 for one (sequence, KV head).  prio_table[t] is the
+    priority token t receives when it leaves the window.  Returns the held sets
+    at the steps in ``record`` (default: every step) and the final state."""
+    st = DecodeState(s, w, k)
+    rec = set(range(n_steps)) if record is None else set(record)
+    held = {}
+    for p in range(n_steps):
+        u = p - w
+        st.step(p, float(prio_table[u]) if u >= s else float("nan"))
+        if p in rec:
+            held[p] = st.held()
+    return held, st
+
+
+def decode_attention(q_step, k_tokens, v_tokens, held, scale=0.0):
+    """One decode step's output for one sequence.
+
+    q_step [Hq, D]; k_tokens, v_tokens [Hkv, P, D] (token p's K/V is row p);
+    held: list over KV heads of held positions.  Returns o [Hq, D], lse [Hq]."""
+    Hq, D = q_step.shape
+    Hkv = k_tokens.shape[0]
+    G = Hq // Hkv
+    sc = default_scale(D, scale)
+    o = np.zeros((Hq, D))
+    lse = np.zeros(Hq)
+    for hq in range(Hq):
+        h = hq // G
+        idx = np.asarray(held[h])
+        z = sc * (k_tokens[h, idx].astype(np.float64) @ q_step[hq].astype(np.float64))
+        keep = np.ones((1, len(idx)), dtype=bool)
+        oo, ll = _attend(z[None, :], v_tokens[h, idx].astype(np.float64), keep)
+        o[hq], lse[hq] = oo[0], ll[0]
+    return o, lse

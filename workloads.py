@@ -1,0 +1,152 @@
+"""Seeded synthetic workloads for the KVpop fixed-budget KV-cache hot path.
+
+This module only draws inputs: it holds none of the method's arithmetic, so both
+the CPU oracle (``oracle/``) and the HIP library's callers (tests, bench, smoke)
+can take their inputs from here without sharing any computation.
+
+Input recipe (the same for every configuration):
+  * Q, K, V ~ N(0, 1) drawn in float32; keys 0..3 of every (batch, kv-head) are
+    multiplied by 4 (a sink-like mass on the first keys).  For bfloat16
+    configurations the draws are rounded to nearest-even bfloat16 and held as
+    exactly representable float32 values, so host and device see the same bits.
+  * Per-token priorities ~ N(0, 1) float32, one per (batch, kv-head, token).
+  * Decode steps draw q, k_new, v_new ~ N(0, 1) (rounded like Q/K/V) and a
+    priority table prio_table[b, h, t] ~ N(0, 1) for the token leaving the window.
+
+These stand in for Qwen3-4B/8B attention activations at the sequence lengths
+the KVpop paper trains and evaluates at (arXiv 2607.05061, section 4); no
+dataset or trained weights are used.
+
+Seeding: every tensor has its own stream
+``np.random.default_rng([seed, config_id, tensor_id])`` so that any tensor can be
+regenerated independently of the others.
+"""
+from __future__ import annotations
+
+import dataclasses
+from typing import Dict
+
+import numpy as np
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    """Shape and budget of one synthetic workload (one attention layer)."""
+
+    name: str
+    config_id: int
+    batch: int
+    n_q_heads: int
+    n_kv_heads: int
+    head_dim: int
+    seq_len: int
+    dtype: str            # "f32" or "bf16"
+    sink: int
+    window: int
+    topk: int
+    seed: int = 0
+
+    @property
+    def budget(self) -> int:
+        """B = s + w + k, the per-KV-head cache size."""
+        return self.sink + self.window + self.topk
+
+    @property
+    def group(self) -> int:
+        return self.n_q_heads // self.n_kv_heads
+
+
+# The five workloads of the build, in order (ids 0..4).
+TINY = Workload("tiny-f32-S512", 0, 1, 2, 1, 64, 512, "f32", 4, 32, 64)
+QWEN3_4B_S16K = Workload("qwen3-4b-layer-S16384-B2048", 1, 1, 32, 8, 128, 16384, "bf16",
+                         16, 512, 1520)
+QWEN3_8B_S32K = Workload("qwen3-8b-layer-S32768-B4096", 2, 1, 32, 8, 128, 32768, "bf16",
+                         16, 1024, 3056)
+# Decode: 64 sequences, cache of B = 2048 per KV head; seq_len is the number of
+# positions the prio table covers (warm-up 0..4095, timed 4096..5119).
+DECODE_B2048 = Workload("decode-64seq-B2048", 3, 64, 32, 8, 128, 5120, "bf16", 16, 512, 1520)
+LONG_S128K = Workload("long-S131072-B4096", 4, 1, 32, 8, 128, 131072, "bf16", 16, 1024, 3056)
+
+WORKLOADS: Dict[str, Workload] = {w.name: w for w in
+                                  (TINY, QWEN3_4B_S16K, QWEN3_8B_S32K, DECODE_B2048, LONG_S128K)}
+
+# tensor ids for the per-tensor seed streams
+_TID = {"q": 0, "k": 1, "v": 2, "prio": 3, "dec_q": 4, "dec_k": 5, "dec_v": 6,
+        "dec_prio": 7}
+
+
+def rng_for(seed: int, config_id: int, tensor: str, extra: int = 0) -> np.random.Generator:
+    return np.random.default_rng([seed, config_id, _TID[tensor], extra])
+
+
+def round_to_bf16(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to the nearest bfloat16 (ties to even); returns float32.
+
+    Finite inputs only (the draws here are Gaussian)."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    u = x.view(np.uint32).astype(np.uint64)
+    lsb = (u >> 16) & 1
+    u = (u + 0x7FFF + lsb) & 0xFFFF0000
+    return u.astype(np.uint32).view(np.float32)
+
+
+def _normal(rng: np.random.Generator, shape, dtype: str) -> np.ndarray:
+    x = rng.standard_normal(size=shape, dtype=np.float32)
+    return round_to_bf16(x) if dtype == "bf16" else x
+
+
+def make_prefill(wl: Workload, seq_len: int | None = None, batch: int | None = None,
+                 seed: int | None = None, sink_scale_keys: int = 4):
+    """Return dict(q, k, v, prio) as float32 numpy arrays (bf16-exact if bf16).
+
+    Shapes: q [b, Hq, S, D], k/v [b, Hkv, S, D], prio [b, Hkv, S].
+    ``seq_len``/``batch`` override the workload's sizes (for reduced parity cases).
+    """
+    S = wl.seq_len if seq_len is None else seq_len
+    b = wl.batch if batch is None else batch
+    sd = wl.seed if seed is None else seed
+    q = _normal(rng_for(sd, wl.config_id, "q"), (b, wl.n_q_heads, S, wl.head_dim), wl.dtype)
+    k = rng_for(sd, wl.config_id, "k").standard_normal(
+        size=(b, wl.n_kv_heads, S, wl.head_dim), dtype=np.float32)
+    k[:, :, :sink_scale_keys, :] *= 4.0
+    if wl.dtype == "bf16":
+        k = round_to_bf16(k)
+    v = _normal(rng_for(sd, wl.config_id, "v"), (b, wl.n_kv_heads, S, wl.head_dim), wl.dtype)
+    prio = rng_for(sd, wl.config_id, "prio").standard_normal(
+        size=(b, wl.n_kv_heads, S), dtype=np.float32)
+    return {"q": q, "k": k, "v": v, "prio": prio}
+
+
+def make_decode_step(wl: Workload, step: int, batch: int | None = None, seed: int | None = None):
+    """Inputs of decode step ``step`` (the same step index for every sequence).
+
+    Returns dict(q [b, Hq, D], k_new [b, Hkv, D], v_new [b, Hkv, D]) float32
+    (bf16-exact if bf16)."""
+    b = wl.batch if batch is None else batch
+    sd = wl.seed if seed is None else seed
+    D = wl.head_dim
+    q = _normal(rng_for(sd, wl.config_id, "dec_q", step), (b, wl.n_q_heads, D), wl.dtype)
+    kn = rng_for(sd, wl.config_id, "dec_k", step).standard_normal(
+        size=(b, wl.n_kv_heads, D), dtype=np.float32)
+    if step < 4:
+        kn *= 4.0
+    if wl.dtype == "bf16":
+        kn = round_to_bf16(kn)
+    vn = _normal(rng_for(sd, wl.config_id, "dec_v", step), (b, wl.n_kv_heads, D), wl.dtype)
+    return {"q": q, "k_new": kn, "v_new": vn}
+
+
+def make_decode_prio_table(wl: Workload, n_tokens: int | None = None, batch: int | None = None,
+                           seed: int | None = None) -> np.ndarray:
+    """prio_table[b, h, t] ~ N(0,1): the priority token t receives when it leaves
+    the window (read at step t + w)."""
+    b = wl.batch if batch is None else batch
+    T = wl.seq_len if n_tokens is None else n_tokens
+    sd = wl.seed if seed is None else seed
+    return rng_for(sd, wl.config_id, "dec_prio").standard_normal(
+        size=(b, wl.n_kv_heads, T), dtype=np.float32)
+
+
+def scaled(wl: Workload, **over) -> Workload:
+    """A copy of ``wl`` with some fields replaced (reduced parity cases)."""
+    return dataclasses.replace(wl, **over)
