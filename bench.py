@@ -1,0 +1,266 @@
+"""Benchmark of the KVpop fixed-budget sparse hot path on one MI355X.
+
+One step = one pass of the training-side hot path over the Qwen3-4B-shaped
+layer (batch 1, 32 query / 8 KV heads, D 128, S 16384, bf16, s 16, w 512,
+k 1520, B 2048): kvpop_thresholds -> kvpop_masked_attn_fwd ->
+kvpop_future_target (with the dense teacher LSE computed beforehand).
+`value` is the algorithmic TFLOP/s of the forward (4 D flop per kept pair) and
+the target pass (2 D flop per pair d >= t + w) over the whole step's time.
+The decode leg times 1024 steps (p = 4096..5119, after an untimed fill from
+p = 0) of 64 sequences over a B = 2048 cache and reports HBM GB/s.
+
+Prints ONE JSON line.  Inputs are synthetic and seeded (workloads.py) and
+already resident in HBM when the timed regions start.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+MFMA_BF16_PEAK_TFLOPS = 2500.0     # MI355X dense bf16 MFMA (published)
+HBM_PEAK_GBPS = 8000.0             # MI355X HBM3E (published)
+
+
+def fwd_pairs(S, B):
+    """kept (q, t) pairs of one head: sum_q min(q + 1, B)."""
+    if S <= B:
+        return S * (S + 1) // 2
+    return B * (B + 1) // 2 + (S - B) * B
+
+
+def tgt_pairs(S, w):
+    n = max(0, S - w)
+    return n * (n + 1) // 2
+
+
+def decode_bytes_per_step(nseq, hq, hkv, D, Bc, esize=2, out_esize=2):
+    kv = 2 * nseq * hkv * Bc * D * esize
+    q = nseq * hq * D * esize
+    o = nseq * hq * D * out_esize
+    new = 2 * 2 * nseq * hkv * D * esize       # new K/V read and written
+    return kv + q + o + new
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--decode-steps", type=int, default=1024)
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="also run one plain device copy of this many MiB (counter calibration)")
+    return ap.parse_args()
+
+
+def cpu_baseline(x, s, w, k, sample_rows=192, sample_t=48):
+    """Time the oracle (as it stands) on a bounded sample of the same workload."""
+    import numpy as np
+    import oracle as orc
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count() or 1
+    q, kk, v, prio = x["q"], x["k"], x["v"], x["prio"]
+    S, D, Hq = q.shape[2], q.shape[3], q.shape[1]
+    B = s + w + k
+    rows = np.linspace(0, S - 1, sample_rows).astype(np.int64)
+    # target tokens from the last eighth, so the (untimed) teacher LSE is only
+    # needed for the last rows
+    ts = np.linspace(S - S // 8, S - 1 - w, sample_t).astype(np.int64)
+    t0 = time.perf_counter()
+    rank = orc.priority_ranks(prio)
+    tau = orc.thresholds_by_selection(rank, s, w, k, rows=range(S))
+    orc.masked_attention(q, kk, v, rank, tau, s, w, rows=rows)
+    t1 = time.perf_counter()
+    lse_dense = np.zeros((1, Hq, S))
+    need = np.arange(int(ts.min()) + w, S)
+    _, lse_dense[:, :, need] = orc.dense_causal_attention(q, kk, kk, rows=need, block=512)
+    t2 = time.perf_counter()
+    orc.future_target_eq8(q, kk, lse_dense, w, ts=ts)
+    t3 = time.perf_counter()
+    flops = 4 * D * Hq * sum(min(int(r) + 1, B) for r in rows)
+    flops += 2 * D * Hq * sum(S - int(t) - w for t in ts)
+    secs = (t1 - t0) + (t3 - t2)
+    return {"value": flops / secs / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"thresholds for all {S} rows; masked forward on {sample_rows} rows x {Hq} "
+                      f"heads; future target on {sample_t} tokens x {Hq} heads (teacher LSE "
+                      f"untimed); {secs:.1f} s of CPU work",
+            "seconds": round(secs, 2)}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build measures one GPU only; run with --gpus 1"}))
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import fixed_budget_sparse_amd as kv
+    from workloads import DECODE_B2048, QWEN3_4B_S16K, make_prefill
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    wl = QWEN3_4B_S16K
+    s, w, k, S, D, Hq, Hkv = wl.sink, wl.window, wl.topk, wl.seq_len, wl.head_dim, wl.n_q_heads, wl.n_kv_heads
+    x = make_prefill(wl)
+    bf = torch.bfloat16
+    q = torch.from_numpy(x["q"]).to(bf).to(dev)
+    kk = torch.from_numpy(x["k"]).to(bf).to(dev)
+    v = torch.from_numpy(x["v"]).to(bf).to(dev)
+    prio = torch.from_numpy(x["prio"]).to(dev)
+    rank = torch.empty(prio.shape, dtype=torch.int32, device=dev)
+    tau = torch.empty_like(rank)
+    o = torch.empty(q.shape, dtype=bf, device=dev)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+    tgt = torch.empty_like(lse)
+    # teacher (dense causal) LSE: the forward with k >= S, untimed
+    rank_d, tau_d = kv.thresholds(prio, s, w, S)
+    _, lse_teacher = kv.masked_attn_fwd(q, kk, v, rank_d, tau_d, s, w, S, out_dtype=bf)
+    if args.calib_copy_mib:
+        src = torch.empty(args.calib_copy_mib << 18, dtype=torch.float32, device=dev)
+        src.copy_(torch.ones_like(src))
+        dst = src.clone()
+        del src, dst
+    torch.cuda.synchronize()
+
+    ev = lambda: torch.cuda.Event(enable_timing=True)   # noqa: E731
+    times = {"thr": [], "fwd": [], "tgt": []}
+
+    def one_step(record):
+        e0, e1, e2, e3 = ev(), ev(), ev(), ev()
+        e0.record()
+        kv.thresholds(prio, s, w, k, rank=rank, tau=tau)
+        e1.record()
+        kv.masked_attn_fwd(q, kk, v, rank, tau, s, w, k, out_dtype=bf, o=o, lse=lse)
+        e2.record()
+        kv.future_target(q, kk, lse_teacher, w, target=tgt)
+        e3.record()
+        if record is not None:
+            record.append((e0, e1, e2, e3))
+
+    for _ in range(args.warmup):
+        one_step(None)
+    torch.cuda.synchronize()
+    recs = []
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        one_step(recs)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    for e0, e1, e2, e3 in recs:
+        times["thr"].append(e0.elapsed_time(e1))
+        times["fwd"].append(e1.elapsed_time(e2))
+        times["tgt"].append(e2.elapsed_time(e3))
+    ms_step = wall * 1e3 / args.steps
+    B = s + w + k
+    f_fwd = 4 * D * Hq * fwd_pairs(S, B)
+    f_tgt = 2 * D * Hq * tgt_pairs(S, w)
+    avg = {n: sum(t) / len(t) for n, t in times.items()}
+    value = (f_fwd + f_tgt) / (ms_step * 1e-3) / 1e12
+    tgt_tflops = f_tgt / (avg["tgt"] * 1e-3) / 1e12
+    fwd_tflops = f_fwd / (avg["fwd"] * 1e-3) / 1e12
+
+    out = {
+        "metric": "masked fwd+target TFLOP/s (%MFMA peak) S=16k; decode GB/s (%HBM) at B=2048",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "batch": wl.batch, "n_q_heads": Hq, "n_kv_heads": Hkv,
+                   "head_dim": D, "seq_len": S, "sink": s, "window": w, "topk": k, "budget": B,
+                   "step": "thresholds + masked fwd + future target",
+                   "decode_workload": DECODE_B2048.name},
+        "frac_mfma_peak": round(value / MFMA_BF16_PEAK_TFLOPS, 4),
+        "kernels_ms": {n: round(t, 4) for n, t in avg.items()},
+        "fwd_tflops": round(fwd_tflops, 2),
+        "target_tflops": round(tgt_tflops, 2),
+        "roofline": {"bound": "mfma", "kernel": "future_target_kernel",
+                     "achieved": round(tgt_tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tgt_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+                     "traffic": None},
+    }
+
+    if not args.no_decode:
+        out["decode"] = bench_decode(kv, torch, np, dev, args.decode_steps)
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(x, s, w, k)
+    print(json.dumps(out))
+
+
+def bench_decode(kv, torch, np, dev, n_timed):
+    from workloads import DECODE_B2048 as wl
+    s, w, k, D, Hq, Hkv, nseq = wl.sink, wl.window, wl.topk, wl.head_dim, wl.n_q_heads, wl.n_kv_heads, wl.batch
+    Bc = s + w + k
+    bf = torch.bfloat16
+    p_start = 2 * Bc                      # 4096: cache full, ~2k tokens already evicted
+    p_end = p_start + n_timed
+    g = torch.Generator(device=dev)
+    g.manual_seed(1234)
+    prio_table = torch.randn((nseq, Hkv, p_end), generator=g, device=dev)
+    cache = kv.new_decode_cache(nseq, Hkv, D, s, w, k, dtype=bf, device=dev)
+    o = torch.empty((nseq, Hq, D), dtype=bf, device=dev)
+    lse = torch.empty((nseq, Hq), dtype=torch.float32, device=dev)
+    pos_all = torch.arange(p_end, dtype=torch.int32, device=dev)[:, None].repeat(1, nseq).contiguous()
+    zero_prio = torch.zeros((nseq, Hkv), device=dev)
+    pr = kv.Problem(nseq, Hq, Hkv, 0, D, s, w, k, 0.0, 0, 0)
+    n_ws = kv.workspace_size(3, pr)
+    ws = torch.empty(n_ws + 256, dtype=torch.uint8, device=dev)
+    ws = ws[(-ws.data_ptr()) % 256:][:n_ws]
+
+    def prio_at(p):
+        u = p - w
+        return prio_table[:, :, u].contiguous() if u >= 0 else zero_prio
+
+    # untimed fill p = 0 .. p_start-1 with fresh random inputs
+    for p in range(p_start):
+        qd = torch.randn((nseq, Hq, D), generator=g, device=dev).to(bf)
+        kn = torch.randn((nseq, Hkv, D), generator=g, device=dev).to(bf)
+        vn = torch.randn((nseq, Hkv, D), generator=g, device=dev).to(bf)
+        kv.decode_step(cache, pos_all[p], qd, kn, vn, prio_at(p), s, w, k, out_dtype=bf, o=o,
+                       lse=lse, ws=ws)
+    # pre-drawn inputs of the timed steps, resident in HBM
+    qs = torch.randn((n_timed, nseq, Hq, D), generator=g, device=dev).to(bf)
+    kns = torch.randn((n_timed, nseq, Hkv, D), generator=g, device=dev).to(bf)
+    vns = torch.randn((n_timed, nseq, Hkv, D), generator=g, device=dev).to(bf)
+    pls = torch.stack([prio_at(p) for p in range(p_start, p_end)])
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record()
+    for i in range(n_timed):
+        kv.decode_step(cache, pos_all[p_start + i], qs[i], kns[i], vns[i], pls[i], s, w, k,
+                       out_dtype=bf, o=o, lse=lse, ws=ws)
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = e0.elapsed_time(e1)
+    us_step = ms * 1e3 / n_timed
+    nbytes = decode_bytes_per_step(nseq, Hq, Hkv, D, Bc)
+    gbps = nbytes / (us_step * 1e-6) / 1e9
+    return {"workload": wl.name, "steps_timed": n_timed, "positions": [p_start, p_end - 1],
+            "us_per_step": round(us_step, 2), "wall_us_per_step": round(wall * 1e6 / n_timed, 2),
+            "bytes_per_step": nbytes, "GB/s": round(gbps, 1),
+            "frac_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4),
+            "tokens_per_s": round(nseq / (us_step * 1e-6), 1)}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,66 @@
+"""Build libkvpop.so (HIP, gfx950) in-tree with hipcc.
+
+Usage: python -m fixed_budget_sparse_amd.build   (or build_library() from Python)
+
+Every source is compiled for gfx950 only, with packed-FP32 instructions
+disabled, and linked into fixed_budget_sparse_amd/libkvpop.so.
+"""
+from __future__ import annotations
+
+import concurrent.futures
+import os
+import shutil
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+BUILD = os.path.join(ROOT, "_build")
+LIB = os.path.join(PKG, "libkvpop.so")
+SOURCES = ["thresholds.hip", "masked_fwd.hip", "future_target.hip", "decode.hip", "api.hip"]
+
+
+def _hipcc() -> str:
+    for c in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
+        if c and os.path.exists(c):
+            return c
+    raise RuntimeError("hipcc not found (ROCm is required to build libkvpop)")
+
+
+COMMON = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden",
+          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+          "-I", os.path.join(ROOT, "include"), "-Wall", "-Wno-unused-function"]
+
+
+def _compile(src: str, extra) -> str:
+    obj = os.path.join(BUILD, src.replace(".hip", ".o"))
+    cmd = [_hipcc(), *COMMON, *extra, "-c", os.path.join(CSRC, src), "-o", obj]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    errs = "\n".join(l for l in r.stderr.splitlines()
+                     if "packed-fp32-ops' is not a recognized feature" not in l)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed for {src}:\n{errs}")
+    if errs.strip():
+        print(errs, file=sys.stderr)
+    return obj
+
+
+def build_library(extra=(), verbose: bool = True) -> str:
+    """Compile every source and link libkvpop.so; returns its path."""
+    os.makedirs(BUILD, exist_ok=True)
+    with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
+        objs = list(ex.map(lambda s: _compile(s, list(extra)), SOURCES))
+    tmp = LIB + ".tmp"
+    cmd = [_hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed:\n{r.stderr}")
+    os.replace(tmp, LIB)
+    if verbose:
+        print(f"built {LIB}")
+    return LIB
+
+
+if __name__ == "__main__":
+    build_library()

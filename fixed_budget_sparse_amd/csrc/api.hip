@@ -1,0 +1,152 @@
+// libkvpop C ABI: host-side validation, workspace sizing and dispatch.
+// Nothing here allocates device memory or synchronises; every entry point
+// validates all arguments before its first launch.
+#include <math.h>
+
+#include "../../include/kvpop.h"
+#include "kvpop_internal.h"
+
+#define KVPOP_EXPORT extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+using kvpop::Dims;
+
+constexpr int kMaxSeq = 262144;
+constexpr long long kMaxBudget = 1LL << 30;
+
+bool dtype_ok(int32_t d) { return d == KVPOP_BF16 || d == KVPOP_F32; }
+
+// Shape checks shared by every call; `call` selects the per-call rules.
+kvpop_status make_dims(int32_t call, const kvpop_problem* pr, Dims* d) {
+  if (!pr) return KVPOP_ERR_ARG;
+  if (pr->batch < 1 || pr->n_q_heads < 1 || pr->n_kv_heads < 1) return KVPOP_ERR_ARG;
+  if (pr->n_q_heads % pr->n_kv_heads != 0) return KVPOP_ERR_ARG;
+  if (pr->sink < 0 || pr->window < 0 || pr->topk < 0) return KVPOP_ERR_ARG;
+  const long long budget = (long long)pr->sink + pr->window + pr->topk;
+  if (budget > kMaxBudget) return KVPOP_ERR_ARG;
+  if (!dtype_ok(pr->qkv_dtype) || !dtype_ok(pr->out_dtype)) return KVPOP_ERR_ARG;
+  if (!(pr->softmax_scale == pr->softmax_scale) || isinf(pr->softmax_scale)) return KVPOP_ERR_ARG;
+  const int G = pr->n_q_heads / pr->n_kv_heads;
+  if (call != KVPOP_CALL_THRESHOLDS) {
+    if (pr->head_dim != 64 && pr->head_dim != 128) return KVPOP_ERR_UNSUPPORTED;
+    if (G > 32) return KVPOP_ERR_UNSUPPORTED;
+  }
+  if (call == KVPOP_CALL_DECODE) {
+    if (pr->window < 1 || budget < 1) return KVPOP_ERR_ARG;
+  } else {
+    if (pr->seq_len < 1) return KVPOP_ERR_ARG;
+    if (pr->seq_len > kMaxSeq) return KVPOP_ERR_UNSUPPORTED;
+    if (call == KVPOP_CALL_MASKED_FWD && pr->window < 1) return KVPOP_ERR_ARG;
+  }
+  d->b = pr->batch;
+  d->Hq = pr->n_q_heads;
+  d->Hkv = pr->n_kv_heads;
+  d->G = G;
+  d->S = call == KVPOP_CALL_DECODE ? 0 : pr->seq_len;
+  d->D = pr->head_dim;
+  d->s = pr->sink;
+  d->w = pr->window;
+  d->k = pr->topk;
+  d->scale = pr->softmax_scale > 0.0f ? pr->softmax_scale : 1.0f / sqrtf((float)pr->head_dim);
+  d->f32_in = pr->qkv_dtype == KVPOP_F32;
+  d->f32_out = pr->out_dtype == KVPOP_F32;
+  return KVPOP_OK;
+}
+
+size_t ws_bytes(int32_t call, const Dims& d) {
+  switch (call) {
+    case KVPOP_CALL_THRESHOLDS: return kvpop::thresholds_ws_bytes(d);
+    case KVPOP_CALL_MASKED_FWD: return kvpop::fwd_ws_bytes(d);
+    case KVPOP_CALL_FUTURE_TARGET: return kvpop::target_ws_bytes(d);
+    case KVPOP_CALL_DECODE: return kvpop::decode_ws_bytes(d);
+    default: return 0;
+  }
+}
+
+kvpop_status check_ws(int32_t call, const Dims& d, const void* ws, size_t ws_len) {
+  const size_t need = ws_bytes(call, d);
+  if (need == 0) return KVPOP_OK;
+  if (!ws || ws_len < need) return KVPOP_ERR_WORKSPACE;
+  if (((uintptr_t)ws & 255u) != 0) return KVPOP_ERR_ARG;   // regions are carved 256-aligned
+  return KVPOP_OK;
+}
+
+kvpop_status finish(hipError_t e) { return e == hipSuccess ? KVPOP_OK : KVPOP_ERR_HIP; }
+
+}  // namespace
+
+KVPOP_EXPORT size_t kvpop_workspace_size(int32_t call, const kvpop_problem* pr) {
+  Dims d;
+  if (call < KVPOP_CALL_THRESHOLDS || call > KVPOP_CALL_DECODE) return 0;
+  if (make_dims(call, pr, &d) != KVPOP_OK) return 0;
+  return ws_bytes(call, d);
+}
+
+KVPOP_EXPORT kvpop_status kvpop_thresholds(const kvpop_problem* pr, const float* prio,
+                                           int32_t* rank, int32_t* tau, void* ws,
+                                           size_t ws_bytes_, hipStream_t stream) {
+  Dims d;
+  kvpop_status st = make_dims(KVPOP_CALL_THRESHOLDS, pr, &d);
+  if (st != KVPOP_OK) return st;
+  if (!prio || !rank || !tau) return KVPOP_ERR_ARG;
+  st = check_ws(KVPOP_CALL_THRESHOLDS, d, ws, ws_bytes_);
+  if (st != KVPOP_OK) return st;
+  return finish(kvpop::launch_thresholds(d, prio, rank, tau, ws, stream));
+}
+
+KVPOP_EXPORT kvpop_status kvpop_masked_attn_fwd(const kvpop_problem* pr, const void* q,
+                                                const void* k, const void* v,
+                                                const int32_t* rank, const int32_t* tau, void* o,
+                                                float* lse, void* ws, size_t ws_bytes_,
+                                                hipStream_t stream) {
+  Dims d;
+  kvpop_status st = make_dims(KVPOP_CALL_MASKED_FWD, pr, &d);
+  if (st != KVPOP_OK) return st;
+  if (!q || !k || !v || !rank || !tau || !o || !lse) return KVPOP_ERR_ARG;
+  st = check_ws(KVPOP_CALL_MASKED_FWD, d, ws, ws_bytes_);
+  if (st != KVPOP_OK) return st;
+  return finish(kvpop::launch_masked_fwd(d, q, k, v, rank, tau, o, lse, ws, stream));
+}
+
+KVPOP_EXPORT kvpop_status kvpop_future_target(const kvpop_problem* pr, const void* q,
+                                              const void* k, const float* lse, float* target,
+                                              void* ws, size_t ws_bytes_, hipStream_t stream) {
+  Dims d;
+  kvpop_status st = make_dims(KVPOP_CALL_FUTURE_TARGET, pr, &d);
+  if (st != KVPOP_OK) return st;
+  if (!q || !k || !lse || !target) return KVPOP_ERR_ARG;
+  st = check_ws(KVPOP_CALL_FUTURE_TARGET, d, ws, ws_bytes_);
+  if (st != KVPOP_OK) return st;
+  return finish(kvpop::launch_future_target(d, q, k, lse, target, ws, stream));
+}
+
+KVPOP_EXPORT kvpop_status kvpop_decode_step(const kvpop_problem* pr, const kvpop_cache* cache,
+                                            const int32_t* pos, const void* q, const void* k_new,
+                                            const void* v_new, const float* prio_leaving,
+                                            void* o, float* lse, void* ws, size_t ws_bytes_,
+                                            hipStream_t stream) {
+  Dims d;
+  kvpop_status st = make_dims(KVPOP_CALL_DECODE, pr, &d);
+  if (st != KVPOP_OK) return st;
+  if (!cache || !cache->k || !cache->v || !cache->slot_pos || !cache->slot_prio || !cache->ring)
+    return KVPOP_ERR_ARG;
+  if (!pos || !q || !k_new || !v_new || !prio_leaving || !o) return KVPOP_ERR_ARG;
+  st = check_ws(KVPOP_CALL_DECODE, d, ws, ws_bytes_);
+  if (st != KVPOP_OK) return st;
+  kvpop::CacheArgs c{cache->k, cache->v, cache->slot_pos, cache->slot_prio, cache->ring};
+  return finish(kvpop::launch_decode(d, c, pos, q, k_new, v_new, prio_leaving, o, lse, ws, stream));
+}
+
+KVPOP_EXPORT const char* kvpop_status_string(kvpop_status st) {
+  switch (st) {
+    case KVPOP_OK: return "ok";
+    case KVPOP_ERR_ARG: return "invalid argument";
+    case KVPOP_ERR_UNSUPPORTED: return "unsupported problem";
+    case KVPOP_ERR_WORKSPACE: return "workspace too small";
+    case KVPOP_ERR_HIP: return "HIP launch failed";
+    default: return "unknown status";
+  }
+}
+
+KVPOP_EXPORT int32_t kvpop_abi_version(void) { return KVPOP_ABI_VERSION; }

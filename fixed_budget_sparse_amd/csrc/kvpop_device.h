@@ -1,0 +1,93 @@
+// Device-side helpers for the libkvpop kernels (CDNA4 / gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kvpop {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kInt32Max = 0x7fffffff;
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.69314718055994531f;
+constexpr float kNegInf = -__builtin_huge_valf();
+
+// ---------------------------------------------------------------- lanes
+__device__ __forceinline__ int lane_id() { return (int)(threadIdx.x & 63); }
+
+// Number of set bits of `m` in lanes below this one.
+__device__ __forceinline__ int lanes_below(uint64_t m) {
+  return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                        __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+}
+
+__device__ __forceinline__ uint64_t wave_ballot(bool p) {
+  return __builtin_amdgcn_ballot_w64(p);
+}
+
+// Orders LDS accesses of this wave against each other: waits for its
+// outstanding LDS operations and keeps the compiler from moving memory
+// accesses across (used where lanes of one wave exchange data through LDS).
+__device__ __forceinline__ void wave_lds_fence() {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+}
+
+// ---------------------------------------------------------------- numbers
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  bf16x2 v;
+  v[0] = (__bf16)a;   // round to nearest even (v_cvt_pk_bf16_f32)
+  v[1] = (__bf16)b;
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits16) {
+  return __uint_as_float(bits16 << 16);
+}
+
+// Priority with NaN mapped to -inf and -0 to +0.
+__device__ __forceinline__ float canonical_priority(float p) {
+  if (p != p) return kNegInf;
+  if (p == 0.0f) return 0.0f;
+  return p;
+}
+
+// Unsigned key whose ascending order is the priority order (priority
+// descending); equal priorities give equal keys, so a stable sort by key keeps
+// ties in index order.
+__device__ __forceinline__ uint32_t priority_sort_key(float p) {
+  uint32_t u = __float_as_uint(canonical_priority(p));
+  uint32_t asc = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return ~asc;
+}
+
+// ---------------------------------------------------------------- MFMA
+// v_mfma_f32_32x32x16_bf16: D[32x32] += A[32x16] * B[16x32].  Lane l supplies
+// A[l%32][8*(l/32) .. +7] and B[8*(l/32) .. +7][l%32]; it holds
+// D[8*j + 4*(l/32) + r][l%32] in element 4*j + r (j, r in 0..3).
+__device__ __forceinline__ f32x16 mfma32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+// v_mfma_f32_32x32x2_f32: lane l supplies A[l%32][l/32] and B[l/32][l%32];
+// the D layout is the one above.
+__device__ __forceinline__ f32x16 mfma32x32x2(float a, float b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8, u); }
+
+__device__ __forceinline__ bf16x8 pack_bf16x8(const float* p) {
+  uint4 u;
+  u.x = pack_bf16x2(p[0], p[1]);
+  u.y = pack_bf16x2(p[2], p[3]);
+  u.z = pack_bf16x2(p[4], p[5]);
+  u.w = pack_bf16x2(p[6], p[7]);
+  return as_bf16x8(u);
+}
+
+}  // namespace kvpop

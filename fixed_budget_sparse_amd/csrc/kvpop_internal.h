@@ -1,0 +1,52 @@
+// Internal definitions shared by the libkvpop HIP sources (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace kvpop {
+
+// ---------------------------------------------------------------- problem
+struct Dims {
+  int b, Hq, Hkv, G, S, D;
+  int s, w, k;
+  float scale;        // softmax scale (resolved: > 0)
+  bool f32_in;        // q/k/v (and decode cache) in float32, else bfloat16
+  bool f32_out;       // attention output in float32, else bfloat16
+  int nseg() const { return b * Hkv; }
+  long long budget() const { return (long long)s + w + k; }
+};
+
+// Workspace carving: every region is 256-byte aligned.
+inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Sizes, tilings and launchers of each call (defined in the .hip files).
+size_t thresholds_ws_bytes(const Dims& d);
+hipError_t launch_thresholds(const Dims& d, const float* prio, int* rank, int* tau,
+                             void* ws, hipStream_t st);
+
+int fwd_rows_per_head(const Dims& d);          // query rows per head in one tile
+size_t fwd_ws_bytes(const Dims& d);
+hipError_t launch_masked_fwd(const Dims& d, const void* q, const void* k, const void* v,
+                             const int* rank, const int* tau, void* o, float* lse,
+                             void* ws, hipStream_t st);
+
+size_t target_ws_bytes(const Dims& d);
+hipError_t launch_future_target(const Dims& d, const void* q, const void* k, const float* lse,
+                                float* target, void* ws, hipStream_t st);
+
+struct CacheArgs {
+  void* k;
+  void* v;
+  int* slot_pos;
+  float* slot_prio;
+  int* ring;
+};
+int decode_splits(const Dims& d);
+size_t decode_ws_bytes(const Dims& d);
+hipError_t launch_decode(const Dims& d, const CacheArgs& c, const int* pos, const void* q,
+                         const void* k_new, const void* v_new, const float* prio_leaving,
+                         void* o, float* lse, void* ws, hipStream_t st);
+
+}  // namespace kvpop

@@ -1,0 +1,467 @@
+// kvpop_masked_attn_fwd: causal GQA attention under the fixed-budget sparse
+// mask (KVpop reading notes §2.3: M[q,t] = 1[t<s] or 1[q-t<w] or
+// (1[t in E(q)] and 1[rank(t) <= tau_q]); Figure 1: softmax over the retained
+// set; gist.science summary §2.2: the operator returns the log-sum-exp).
+//
+// Design (gfx950):
+//  * A workgroup owns one query tile of one KV head: m = 128 / G query rows of
+//    each of the G query heads that share the KV head, stacked into 128 MFMA
+//    rows (4 waves x 32).  The G heads share priorities, hence the mask and
+//    the key list, so one gathered key set feeds all of them.
+//  * The tile's candidate keys are the sinks, the long-range keys of its first
+//    row q0 ({t in E(q0) : rank(t) <= tau_q0}, exactly k keys, listed in rank
+//    order by a small pre-pass) and the contiguous band [q0-w+1, q_hi].  Since
+//    tau is non-increasing in q once k tokens are eligible and an evicted
+//    token never returns, this covers every kept key of every row.  Kept keys
+//    are scattered over the whole prefix, so instead of skipping key blocks
+//    the kernel gathers the candidates into dense 64-key chunks in LDS.
+//  * Per chunk: S^T = K Q^T with v_mfma_f32_32x32x16_bf16 (each lane then owns
+//    one query row), the A8 mask from (t, rank(t)) and (q, tau_q) only on
+//    chunks that are not kept by every row, online softmax in the exp2
+//    domain, and O^T = V^T P^T with V staged transposed, so P feeds the second
+//    MFMA straight from registers and O stays row-per-lane.
+//  * float32 inputs use v_mfma_f32_32x32x2_f32 with the same lane layouts.
+#include <type_traits>
+
+#include "kvpop_device.h"
+#include "kvpop_internal.h"
+
+namespace kvpop {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kRowsPerTile = 128;   // stacked query rows per workgroup
+constexpr int kChunk = 64;          // keys per chunk
+
+struct FwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const int* rank;
+  const int* tau;
+  const int2* list;    // [nseg, ntiles, cap] (token, rank) of listed long-range keys
+  const int* count;    // [nseg, ntiles]
+  void* o;
+  float* lse;
+  int S, Hq, Hkv, G, m, ntiles, s, w, cap;
+  float scale_log2;    // softmax scale * log2(e)
+};
+
+// order[rank[t]] = t
+__global__ __launch_bounds__(256) void order_from_rank_kernel(const int* __restrict__ rank,
+                                                              int* __restrict__ order, int S,
+                                                              long long total) {
+  const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (i >= total) return;
+  const long long seg = i / S;
+  const int t = (int)(i - seg * S);
+  const int r = rank[i];
+  if ((unsigned)r < (unsigned)S) order[seg * S + r] = t;
+}
+
+// Lists, in rank order, the long-range keys of each tile's first row q0 when
+// its cutoff is finite: tokens t in [s, q0 - w] with rank(t) <= tau_q0.
+__global__ __launch_bounds__(256) void tile_list_kernel(const int* __restrict__ order,
+                                                        const int* __restrict__ tau, int S,
+                                                        int s, int w, int m, int ntiles, int cap,
+                                                        int2* __restrict__ list,
+                                                        int* __restrict__ count) {
+  __shared__ int wsum[4];
+  const int tile = blockIdx.x, seg = blockIdx.y;
+  const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
+  const int q0 = tile * m;
+  const int e_hi = q0 - w;
+  const int tq0 = tau[(size_t)seg * S + q0];
+  int* cnt_out = count + (size_t)seg * ntiles + tile;
+  if (e_hi < s || tq0 < 0 || tq0 == kInt32Max || cap == 0) {
+    if (tid == 0) *cnt_out = 0;
+    return;
+  }
+  const int scan_end = min(tq0, S - 1);
+  const int* ord = order + (size_t)seg * S;
+  int2* out = list + ((size_t)seg * ntiles + tile) * cap;
+  int base = 0;
+  for (int i0 = 0; i0 <= scan_end; i0 += 256) {
+    const int i = i0 + tid;
+    const int t = i <= scan_end ? ord[i] : -1;
+    const bool keep = t >= s && t <= e_hi;
+    const uint64_t bal = wave_ballot(keep);
+    if (lane == 0) wsum[wave] = __builtin_popcountll(bal);
+    __syncthreads();
+    int wofs = 0, total = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int c = wsum[j];
+      wofs += j < wave ? c : 0;
+      total += c;
+    }
+    const int pos = base + wofs + lanes_below(bal);
+    if (keep && pos < cap) out[pos] = make_int2(t, i);
+    base += total;
+    __syncthreads();
+  }
+  if (tid == 0) *cnt_out = min(base, cap);
+}
+
+// LDS geometry
+template <int D, bool kF32>
+struct FwdLds {
+  // bf16: K row-major [64][D+8]; V transposed [D][64+8] with permuted columns
+  // f32:  K row-major [64][D+1]; V row-major [64][D+4]
+  static constexpr int KS = kF32 ? D + 1 : D + 8;
+  static constexpr int VS = kF32 ? D + 4 : kChunk + 8;
+  static constexpr int kBytes = kF32 ? kChunk * KS * 4 : kChunk * KS * 2;
+  static constexpr int vBytes = kF32 ? kChunk * VS * 4 : D * VS * 2;
+};
+
+template <int D, bool kF32In, bool kF32Out>
+__global__ __launch_bounds__(kThreads, 2) void masked_fwd_kernel(FwdArgs a) {
+  using L = FwdLds<D, kF32In>;
+  __shared__ __attribute__((aligned(16))) unsigned char k_lds[L::kBytes];
+  __shared__ __attribute__((aligned(16))) unsigned char v_lds[L::vBytes];
+  __shared__ int kd_t[kChunk];
+  __shared__ int kd_r[kChunk];
+  __shared__ int s_flag;
+  __shared__ int s_min_tau;
+
+  const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
+  const int hh = lane >> 5, li = lane & 31;
+  const int tile = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int S = a.S, s = a.s, w = a.w, m = a.m, G = a.G;
+  const size_t seg = (size_t)b * a.Hkv + h;
+  const int* rank = a.rank + seg * S;
+  const int* tau = a.tau + seg * S;
+  const int q0 = tile * m;
+  const int q_hi = min(q0 + m - 1, S - 1);
+
+  // this lane's query row
+  const int rr = wave * 32 + li;
+  const int g = rr / m;
+  const int q = q0 + (rr - g * m);
+  const bool row_ok = g < G && q < S;
+  const int hq = h * G + (g < G ? g : 0);
+  const int tau_q = row_ok ? tau[q] : -1;
+
+  if (tid == 0) s_min_tau = kInt32Max;
+  __syncthreads();
+  if (tid < m && q0 + tid < S) atomicMin(&s_min_tau, tau[q0 + tid]);
+
+  // key segments of the tile: sinks | long-range | band
+  const int n_sink = min(s, q_hi + 1);
+  const int e_hi = q0 - w;
+  const int tq0 = tau[q0];
+  int n_long = 0;
+  bool listed = false;
+  if (e_hi >= s && tq0 >= 0) {
+    if (tq0 == kInt32Max) {
+      n_long = e_hi - s + 1;
+    } else {
+      listed = true;
+      n_long = a.count[seg * a.ntiles + tile];
+    }
+  }
+  const int band_lo = max(s, q0 - w + 1);
+  const int n_band = max(0, q_hi - band_lo + 1);
+  const int nk = n_sink + n_long + n_band;
+  const int2* lst = a.list + (seg * a.ntiles + tile) * (size_t)a.cap;
+
+  // query operand (B of S^T = K Q^T): lane holds row li, dims [16ks + 8hh, +8)
+  constexpr int NKS = kF32In ? D / 2 : D / 16;
+  typedef typename std::conditional<kF32In, float, bf16x8>::type QOp;
+  QOp qop[NKS];
+  {
+    const size_t qrow = (((size_t)b * a.Hq + hq) * S + (row_ok ? q : 0)) * D;
+    if constexpr (kF32In) {
+      const float* qp = (const float*)a.q + qrow;
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) qop[ks] = row_ok ? qp[2 * ks + hh] : 0.0f;
+    } else {
+      const uint16_t* qp = (const uint16_t*)a.q + qrow;
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+        uint4 u = make_uint4(0, 0, 0, 0);
+        if (row_ok) u = *(const uint4*)(qp + 16 * ks + 8 * hh);
+        qop[ks] = as_bf16x8(u);
+      }
+    }
+  }
+
+  f32x16 oacc[D / 32];
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) oacc[db] = f32x16{};
+  float m_run = kNegInf, l_run = 0.0f;
+
+  const size_t kvbase = seg * (size_t)S * D;
+  __syncthreads();   // s_min_tau complete
+  const int min_tau = s_min_tau;
+
+  for (int c0 = 0; c0 < nk; c0 += kChunk) {
+    // ---- chunk key descriptors (wave 0)
+    if (tid < kChunk) {
+      const int j = c0 + tid;
+      int t = -1, r = 0;
+      if (j < n_sink) {
+        t = j;
+      } else if (j < n_sink + n_long) {
+        const int jj = j - n_sink;
+        if (listed) {
+          const int2 e = lst[jj];
+          t = e.x;
+          r = e.y;
+        } else {
+          t = s + jj;
+          r = rank[t];
+        }
+      } else if (j < nk) {
+        t = band_lo + (j - n_sink - n_long);
+        r = rank[t];
+      }
+      if (t >= S) t = -1;
+      kd_t[tid] = t;
+      kd_r[tid] = r;
+      // kept by every row of the tile?
+      const bool always = t >= 0 && t <= q0 && (t < s || t > q_hi - w || r <= min_tau);
+      const uint64_t bal = wave_ballot(!always);
+      if (tid == 0) s_flag = bal != 0;
+    }
+    __syncthreads();
+
+    // ---- gather K and V rows of the chunk into LDS
+    if constexpr (!kF32In) {
+      const uint16_t* kg = (const uint16_t*)a.k + kvbase;
+      const uint16_t* vg = (const uint16_t*)a.v + kvbase;
+      uint16_t* kl = (uint16_t*)k_lds;
+      uint16_t* vl = (uint16_t*)v_lds;
+      constexpr int PPR = D / 8;   // 16-byte pieces per row
+#pragma unroll
+      for (int i = 0; i < kChunk * PPR / kThreads; ++i) {
+        const int p = tid + i * kThreads;
+        const int key = p / PPR, piece = p % PPR;
+        const int t = kd_t[key];
+        uint4 val = make_uint4(0, 0, 0, 0);
+        if (t >= 0) val = *(const uint4*)(kg + (size_t)t * D + piece * 8);
+        *(uint4*)(kl + key * L::KS + piece * 8) = val;
+      }
+      // V^T: column c = 16*ks + 8*hh + e of LDS row d holds key
+      // 16*ks + 8*(e>>2) + 4*hh + (e&3) of the chunk (the P operand layout)
+#pragma unroll
+      for (int i = 0; i < 8 * (D / 2) / kThreads; ++i) {
+        const int task = tid + i * kThreads;
+        const int grp = task / (D / 2), dp = task % (D / 2);
+        uint32_t x[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int jkey = 16 * (grp >> 1) + 8 * (e >> 2) + 4 * (grp & 1) + (e & 3);
+          const int t = kd_t[jkey];
+          x[e] = t >= 0 ? *(const uint32_t*)(vg + (size_t)t * D + 2 * dp) : 0u;
+        }
+        uint4 lo, hi;
+        lo.x = (x[0] & 0xffffu) | (x[1] << 16);
+        lo.y = (x[2] & 0xffffu) | (x[3] << 16);
+        lo.z = (x[4] & 0xffffu) | (x[5] << 16);
+        lo.w = (x[6] & 0xffffu) | (x[7] << 16);
+        hi.x = (x[0] >> 16) | (x[1] & 0xffff0000u);
+        hi.y = (x[2] >> 16) | (x[3] & 0xffff0000u);
+        hi.z = (x[4] >> 16) | (x[5] & 0xffff0000u);
+        hi.w = (x[6] >> 16) | (x[7] & 0xffff0000u);
+        *(uint4*)(vl + (2 * dp) * L::VS + grp * 8) = lo;
+        *(uint4*)(vl + (2 * dp + 1) * L::VS + grp * 8) = hi;
+      }
+    } else {
+      const float* kg = (const float*)a.k + kvbase;
+      const float* vg = (const float*)a.v + kvbase;
+      float* kl = (float*)k_lds;
+      float* vl = (float*)v_lds;
+      constexpr int PPR = D / 4;
+#pragma unroll
+      for (int i = 0; i < kChunk * PPR / kThreads; ++i) {
+        const int p = tid + i * kThreads;
+        const int key = p / PPR, piece = p % PPR;
+        const int t = kd_t[key];
+        float4 kv4 = make_float4(0.f, 0.f, 0.f, 0.f), vv4 = kv4;
+        if (t >= 0) {
+          kv4 = *(const float4*)(kg + (size_t)t * D + piece * 4);
+          vv4 = *(const float4*)(vg + (size_t)t * D + piece * 4);
+        }
+        float* kd = kl + key * L::KS + piece * 4;
+        kd[0] = kv4.x; kd[1] = kv4.y; kd[2] = kv4.z; kd[3] = kv4.w;
+        *(float4*)(vl + key * L::VS + piece * 4) = vv4;
+      }
+    }
+    __syncthreads();
+
+    // ---- S^T = K Q^T for the two 32-key blocks
+    f32x16 sacc[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      sacc[kb] = f32x16{};
+      if constexpr (!kF32In) {
+        const uint16_t* kl = (const uint16_t*)k_lds + (32 * kb + li) * L::KS + 8 * hh;
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks)
+          sacc[kb] = mfma32x32x16(as_bf16x8(*(const uint4*)(kl + 16 * ks)), qop[ks], sacc[kb]);
+      } else {
+        const float* kl = (const float*)k_lds + (32 * kb + li) * L::KS + hh;
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) sacc[kb] = mfma32x32x2(kl[2 * ks], qop[ks], sacc[kb]);
+      }
+    }
+
+    // ---- mask, online softmax (log2 domain)
+    float x[32];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) x[kb * 16 + e] = sacc[kb][e] * a.scale_log2;
+    if (s_flag) {
+      // branch-free: bitwise tests and a select per score (a short-circuit
+      // form here was compiled into divergent branches that lost a store)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int jj = 32 * kb + 8 * (e >> 2) + 4 * hh + (e & 3);
+          const int t = kd_t[jj], rt = kd_r[jj];
+          const bool keep = row_ok & (t >= 0) & (t <= q) &
+                            ((t < s) | (t > q - w) | (rt <= tau_q));
+          x[kb * 16 + e] = keep ? x[kb * 16 + e] : kNegInf;
+        }
+    }
+    float mc = x[0];
+#pragma unroll
+    for (int e = 1; e < 32; ++e) mc = fmaxf(mc, x[e]);
+    mc = fmaxf(mc, __shfl_xor(mc, 32));
+    const float m_new = fmaxf(m_run, mc);
+    const float m_use = m_new == kNegInf ? 0.0f : m_new;
+    const float alpha = exp2_fast(m_run - m_use);
+    float ps = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 32; ++e) {
+      x[e] = exp2_fast(x[e] - m_use);
+      ps += x[e];
+    }
+    l_run = l_run * alpha + ps;
+    m_run = m_new;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) oacc[db] *= alpha;
+
+    // ---- O^T += V^T P^T
+    if constexpr (!kF32In) {
+      bf16x8 pk[4];
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) pk[ks] = pack_bf16x8(&x[(ks >> 1) * 16 + 8 * (ks & 1)]);
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) {
+        const uint16_t* vl = (const uint16_t*)v_lds + (32 * db + li) * L::VS + 8 * hh;
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+          oacc[db] = mfma32x32x16(as_bf16x8(*(const uint4*)(vl + 16 * ks)), pk[ks], oacc[db]);
+      }
+    } else {
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) {
+        const float* vl = (const float*)v_lds + 32 * db + li;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const int key = 32 * kb + 8 * (e >> 2) + 4 * hh + (e & 3);
+            oacc[db] = mfma32x32x2(vl[key * L::VS], x[kb * 16 + e], oacc[db]);
+          }
+      }
+    }
+    __syncthreads();
+  }
+
+  // ---- epilogue: O = acc / l, LSE = (m + log2 l) ln 2
+  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  if (row_ok) {
+    const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+    const size_t orow = (((size_t)b * a.Hq + hq) * S + q) * D;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int d = 32 * db + 8 * j + 4 * hh;
+        const float o0 = oacc[db][4 * j] * inv, o1 = oacc[db][4 * j + 1] * inv;
+        const float o2 = oacc[db][4 * j + 2] * inv, o3 = oacc[db][4 * j + 3] * inv;
+        if constexpr (kF32Out) {
+          *(float4*)((float*)a.o + orow + d) = make_float4(o0, o1, o2, o3);
+        } else {
+          *(uint2*)((uint16_t*)a.o + orow + d) = make_uint2(pack_bf16x2(o0, o1), pack_bf16x2(o2, o3));
+        }
+      }
+    if (hh == 0)
+      a.lse[((size_t)b * a.Hq + hq) * S + q] =
+          l_tot > 0.0f ? (m_run + log2f(l_tot)) * kLn2 : kNegInf;
+  }
+}
+
+template <int D, bool kF32In, bool kF32Out>
+void launch_fwd_kernel(const FwdArgs& a, int b, hipStream_t st) {
+  hipLaunchKernelGGL((masked_fwd_kernel<D, kF32In, kF32Out>), dim3(a.ntiles, a.Hkv, b),
+                     dim3(kThreads), 0, st, a);
+}
+
+}  // namespace
+
+int fwd_rows_per_head(const Dims& d) { return kRowsPerTile / d.G; }
+
+static int fwd_ntiles(const Dims& d) {
+  const int m = fwd_rows_per_head(d);
+  return (d.S + m - 1) / m;
+}
+
+static int fwd_list_cap(const Dims& d) { return d.k < d.S ? d.k : d.S; }
+
+size_t fwd_ws_bytes(const Dims& d) {
+  const size_t nseg = d.nseg(), nt = fwd_ntiles(d);
+  size_t bytes = align256(nseg * d.S * 4);                              // order
+  bytes += align256(nseg * nt * 4);                                     // counts
+  bytes += align256(nseg * nt * (size_t)fwd_list_cap(d) * 8);           // lists
+  return bytes;
+}
+
+hipError_t launch_masked_fwd(const Dims& d, const void* q, const void* k, const void* v,
+                             const int* rank, const int* tau, void* o, float* lse, void* ws,
+                             hipStream_t st) {
+  const int nseg = d.nseg(), nt = fwd_ntiles(d), m = fwd_rows_per_head(d);
+  const int cap = fwd_list_cap(d);
+  char* p = (char*)ws;
+  int* order = (int*)p; p += align256((size_t)nseg * d.S * 4);
+  int* count = (int*)p; p += align256((size_t)nseg * nt * 4);
+  int2* list = (int2*)p;
+
+  const long long total = (long long)nseg * d.S;
+  hipLaunchKernelGGL(order_from_rank_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0,
+                     st, rank, order, d.S, total);
+  hipLaunchKernelGGL(tile_list_kernel, dim3(nt, nseg), dim3(256), 0, st, order, tau, d.S, d.s,
+                     d.w, m, nt, cap, list, count);
+
+  FwdArgs a;
+  a.q = q; a.k = k; a.v = v; a.rank = rank; a.tau = tau; a.list = list; a.count = count;
+  a.o = o; a.lse = lse;
+  a.S = d.S; a.Hq = d.Hq; a.Hkv = d.Hkv; a.G = d.G; a.m = m; a.ntiles = nt;
+  a.s = d.s; a.w = d.w; a.cap = cap;
+  a.scale_log2 = d.scale * 1.4426950408889634f;
+  if (d.D == 128) {
+    if (d.f32_in) {
+      if (d.f32_out) launch_fwd_kernel<128, true, true>(a, d.b, st);
+      else launch_fwd_kernel<128, true, false>(a, d.b, st);
+    } else {
+      if (d.f32_out) launch_fwd_kernel<128, false, true>(a, d.b, st);
+      else launch_fwd_kernel<128, false, false>(a, d.b, st);
+    }
+  } else {
+    if (d.f32_in) {
+      if (d.f32_out) launch_fwd_kernel<64, true, true>(a, d.b, st);
+      else launch_fwd_kernel<64, true, false>(a, d.b, st);
+    } else {
+      if (d.f32_out) launch_fwd_kernel<64, false, true>(a, d.b, st);
+      else launch_fwd_kernel<64, false, false>(a, d.b, st);
+    }
+  }
+  return hipGetLastError();
+}
+
+}  // namespace kvpop

@@ -1,0 +1,187 @@
+/* kvpop.h — C ABI of libkvpop: the data-parallel hot path of KVpop's
+ * fixed-budget sparse KV cache on AMD Instinct MI355X (gfx950).
+ *
+ * The method (sources cited by page title):
+ *   [Notes]  "KVpop -- Key-Value Cache Compression with Predictive Online Pruning
+ *            精读笔记" (reading notes on arXiv 2607.05061), the page with the
+ *            method's formulas.
+ *   [Sum-zh] "技术摘要：KVpop — 基于预测性在线剪枝的键值（KV）缓存压缩".
+ * Every KV head keeps B = s + w + k entries ([Notes] §2.1): s sink tokens, the
+ * w most recent tokens (a protected window) and the k best older tokens under a
+ * static per-token priority.  The sparse mask of [Notes] §2.3 is
+ *   M[q,t] = (t < s) or (q - t < w) or (s <= t <= q - w and rank(t) <= tau_q)
+ * taken together with causality (t <= q), where rank(t) is the place of t in
+ * the priority order and tau_q the rank of the k-th best eligible token.
+ *
+ * Conventions shared by every call
+ *   - Pointers are DEVICE pointers, allocated and owned by the caller.  The
+ *     library allocates and frees nothing and keeps no state between calls.
+ *   - Every call only enqueues kernels on `stream` and returns; nothing
+ *     synchronises.  Arguments are validated on the host first: on any error
+ *     nothing is launched and a non-zero status is returned.  A failed launch
+ *     returns KVPOP_ERR_HIP.  No C++ exception crosses the ABI.
+ *   - Tensors are contiguous, row-major, in the shapes given below.
+ *   - `ws` is caller-owned scratch of at least kvpop_workspace_size(call, pr)
+ *     bytes (NULL allowed when that size is 0); its contents on entry are
+ *     ignored and on exit undefined.  Calls that share a workspace or outputs
+ *     must not overlap in time.
+ *   - Priority order: higher priority first, ties to the lower token index;
+ *     -0 equals +0 and NaN counts as -inf.
+ *   - Query head h reads KV head h / (Hq / Hkv).  Priorities, ranks, cutoffs
+ *     and decode caches are per KV head.
+ *   - Logs are natural logs.
+ */
+#ifndef KVPOP_H
+#define KVPOP_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KVPOP_ABI_VERSION 1
+
+typedef enum {
+  KVPOP_OK = 0,
+  KVPOP_ERR_ARG = 1,          /* invalid argument (shape, NULL pointer, budget) */
+  KVPOP_ERR_UNSUPPORTED = 2,  /* valid but outside what the kernels implement  */
+  KVPOP_ERR_WORKSPACE = 3,    /* ws_bytes smaller than kvpop_workspace_size()   */
+  KVPOP_ERR_HIP = 4           /* a kernel launch failed                          */
+} kvpop_status;
+
+typedef enum { KVPOP_BF16 = 0, KVPOP_F32 = 1 } kvpop_dtype;
+
+typedef enum {
+  KVPOP_CALL_THRESHOLDS = 0,
+  KVPOP_CALL_MASKED_FWD = 1,
+  KVPOP_CALL_FUTURE_TARGET = 2,
+  KVPOP_CALL_DECODE = 3
+} kvpop_call;
+
+/* Problem description shared by all calls.
+ *   batch       sequences (>= 1)
+ *   n_q_heads   Hq; n_kv_heads Hkv; Hq % Hkv == 0 and 1 <= Hq/Hkv <= 32
+ *   seq_len     S (prefill calls; 1 <= S <= 262144); ignored by decode
+ *   head_dim    D in {64, 128}
+ *   sink, window, topk   s >= 0, w >= 0, k >= 0 with s + w + k <= 2^30;
+ *               w >= 1 for the forward and decode calls
+ *   softmax_scale  logit scale; <= 0 selects 1/sqrt(D)
+ *   qkv_dtype   KVPOP_BF16 or KVPOP_F32 (dtype of q, k, v and the decode cache)
+ *   out_dtype   dtype of the attention output o (KVPOP_BF16 or KVPOP_F32) */
+typedef struct {
+  int32_t batch;
+  int32_t n_q_heads;
+  int32_t n_kv_heads;
+  int32_t seq_len;
+  int32_t head_dim;
+  int32_t sink;
+  int32_t window;
+  int32_t topk;
+  float softmax_scale;
+  int32_t qkv_dtype;
+  int32_t out_dtype;
+} kvpop_problem;
+
+/* Fixed-size decode cache of capacity Bc = s + w + k slots per (sequence, KV
+ * head) ([Notes] §2.3: inference keeps only the compact cache; [Sum-zh] §4.3:
+ * the fixed per-head budget keeps memory constant).  All arrays are caller
+ * owned, persist between decode calls and may be copied to checkpoint.
+ *   k, v       [batch, Hkv, Bc, D] in qkv_dtype
+ *   slot_pos   [batch, Hkv, Bc] int32: token position held by each slot
+ *   slot_prio  [batch, Hkv, Bc] float: priority of the long-range token held
+ *   ring       [batch, Hkv, w]  int32: slot of window position p mod w
+ * Slots 0 .. min(p, Bc)-1 are the held tokens before step p; slot order is
+ * unspecified. */
+typedef struct {
+  void* k;
+  void* v;
+  int32_t* slot_pos;
+  float* slot_prio;
+  int32_t* ring;
+} kvpop_cache;
+
+/* Bytes of scratch the call needs for problem `pr` (0 for an invalid problem). */
+size_t kvpop_workspace_size(int32_t call, const kvpop_problem* pr);
+
+/* Per-token ranks and per-query top-k cutoffs ([Notes] §2.3: rank(t) by the
+ * static priority, tau_q = rank of the k-th best token of E(q); [Notes] §2.2:
+ * E(q) = {t | s <= t <= q - w}; [Sum-zh] §2.4: a running threshold over static
+ * priorities replaces per-row sorting).
+ *   prio  [batch, Hkv, S] float (values for t < s are read but never matter)
+ *   rank  [batch, Hkv, S] int32 out: a permutation of 0..S-1 per (b, h)
+ *   tau   [batch, Hkv, S] int32 out: for |E(q)| >= k >= 1 the k-th smallest
+ *         rank over E(q); INT32_MAX when |E(q)| < k; -1 when k == 0.
+ * Exact: results are unique integers. */
+kvpop_status kvpop_thresholds(const kvpop_problem* pr, const float* prio,
+                              int32_t* rank, int32_t* tau,
+                              void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Causal GQA attention restricted to the sparse mask M above, generated in the
+ * kernel from (rank, tau) with no S x S mask stored ([Notes] §2.3, Figure 1;
+ * [Sum-zh] §2.2: the sparse operator also returns the log-sum-exp).
+ *   q    [batch, Hq, S, D]  qkv_dtype
+ *   k, v [batch, Hkv, S, D] qkv_dtype
+ *   rank, tau  as produced by kvpop_thresholds for the same (s, w, k)
+ *   o    [batch, Hq, S, D]  out_dtype: softmax over the kept keys of each row
+ *   lse  [batch, Hq, S] float: ln sum_{kept t} exp(scale <q_q, k_t>)
+ * Float results; accumulation in float32.  With k >= S this is dense causal
+ * attention, whose lse is the teacher LSE kvpop_future_target takes. */
+kvpop_status kvpop_masked_attn_fwd(const kvpop_problem* pr, const void* q,
+                                   const void* k, const void* v,
+                                   const int32_t* rank, const int32_t* tau,
+                                   void* o, float* lse,
+                                   void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Training-only transposed pass ([Notes] §2.2 future mass m_t, §2.3 Eq. (8)
+ * and Figure 2): keys act as queries and queries as keys, the original
+ * query's LSE is subtracted and only d >= t + w is summed, so no S x S
+ * probability map is formed.
+ *   q    [batch, Hq, S, D], k [batch, Hkv, S, D]  qkv_dtype
+ *   lse  [batch, Hq, S] float: the dense causal (teacher) LSE of each query
+ *   target [batch, Hq, S] float out:
+ *          ln sum_{d = t+w}^{S-1} exp(scale <q_d, k_t> - lse_d), -inf when t + w > S - 1
+ * This is the first term of Eq. (8) per query head (no -ln N_t, no average
+ * over the query group).  w >= 0.  The sum runs without a running maximum,
+ * which is exact in float32 whenever every exponent is <= 0, i.e. whenever
+ * lse_d is at least every logit of row d (true for the dense causal LSE). */
+kvpop_status kvpop_future_target(const kvpop_problem* pr, const void* q,
+                                 const void* k, const float* lse, float* target,
+                                 void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* One decode step for every sequence ([Notes] §2.2 newcomer t_new = q - w,
+ * §2.4 the token leaving the window is scored then; [Sum-zh] §2.1 budget).
+ * At position p of sequence b, for each KV head:
+ *   1. token p enters the window;
+ *   2. token u = p - w, if u >= s, leaves the window: it is kept when fewer
+ *      than k long-range tokens are held, otherwise it replaces the worst held
+ *      long-range token (lowest priority, ties: highest position) iff its
+ *      priority is strictly larger, else it is dropped; the freed slot takes
+ *      token p;
+ *   3. the G query heads attend over the min(p+1, Bc) held tokens.
+ *   cache      as above (updated in place)
+ *   pos        [batch] int32 device: p of each sequence; p == 0 starts a new
+ *              sequence (the cache contents are ignored); p < 0 skips the
+ *              sequence (cache untouched, o = 0, lse = -inf).  Steps of one
+ *              sequence must come in order p = 0, 1, 2, ...
+ *   q          [batch, Hq, D]  qkv_dtype
+ *   k_new, v_new [batch, Hkv, D] qkv_dtype: K/V of token p
+ *   prio_leaving [batch, Hkv] float: priority of token p - w (read iff p - w >= s)
+ *   o          [batch, Hq, D] out_dtype;  lse [batch, Hq] float or NULL
+ * Cache membership is exact and equals the kept set of forward row p for the
+ * same priorities. */
+kvpop_status kvpop_decode_step(const kvpop_problem* pr, const kvpop_cache* cache,
+                               const int32_t* pos, const void* q,
+                               const void* k_new, const void* v_new,
+                               const float* prio_leaving, void* o, float* lse,
+                               void* ws, size_t ws_bytes, hipStream_t stream);
+
+const char* kvpop_status_string(kvpop_status st);
+int32_t kvpop_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* KVPOP_H */

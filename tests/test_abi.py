@@ -1,0 +1,102 @@
+"""Host-only checks of the libkvpop C ABI: the library loads, exports every
+symbol include/kvpop.h declares, sizes workspaces, and rejects invalid
+arguments before launching anything (no GPU is touched by these calls)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import fixed_budget_sparse_amd as kv
+from fixed_budget_sparse_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kvpop.h")
+
+
+def _lib():
+    if not os.path.exists(kv.library_path()):
+        pytest.skip("libkvpop.so not built")
+    return kv.lib()
+
+
+def test_header_symbols_exported():
+    L = _lib()
+    declared = set(re.findall(r"\b(kvpop_[a-z_]+)\s*\(", open(HEADER).read()))
+    assert declared == set(kv.EXPORTED_SYMBOLS)
+    for name in declared:
+        assert hasattr(L, name), name
+    assert kv.abi_version() == 1
+    assert L.kvpop_status_string(3).decode() == "workspace too small"
+
+
+def _pr(**over):
+    base = dict(batch=1, n_q_heads=32, n_kv_heads=8, seq_len=16384, head_dim=128, sink=16,
+                window=512, topk=1520)
+    base.update(over)
+    return B.Problem(**base)
+
+
+def test_workspace_sizes():
+    _lib()
+    pr = _pr()
+    for call in range(4):
+        n = kv.workspace_size(call, pr)
+        assert (n > 0) == (call != B.CALL_FUTURE_TARGET)
+    # invalid problems size to 0
+    assert kv.workspace_size(0, _pr(n_q_heads=30)) == 0
+    assert kv.workspace_size(1, _pr(head_dim=96)) == 0
+    assert kv.workspace_size(1, _pr(window=0)) == 0
+    assert kv.workspace_size(9, pr) == 0
+    # the threshold workspace scales with batch * heads * S
+    assert kv.workspace_size(0, _pr(seq_len=32768)) > kv.workspace_size(0, pr)
+
+
+def _call_thresholds(pr, prio=1, rank=1, tau=1, ws=None, n=0):
+    L = _lib()
+    c = pr.c()
+    vp = ctypes.c_void_p
+    return L.kvpop_thresholds(ctypes.byref(c), vp(prio), vp(rank), vp(tau), vp(ws), n, vp(0))
+
+
+def test_error_paths_return_before_launch():
+    L = _lib()
+    vp = ctypes.c_void_p
+    # bad shapes
+    assert _call_thresholds(_pr(n_q_heads=31)) == 1
+    assert _call_thresholds(_pr(seq_len=0)) == 1
+    assert _call_thresholds(_pr(sink=-1)) == 1
+    assert _call_thresholds(_pr(seq_len=1 << 20)) == 2
+    # NULL outputs
+    assert _call_thresholds(_pr(), prio=None) == 1
+    # short workspace
+    pr = _pr()
+    n = kv.workspace_size(0, pr)
+    assert _call_thresholds(pr, ws=256, n=n - 1) == 3
+    assert _call_thresholds(pr, ws=None, n=n) == 3
+    # misaligned workspace
+    assert _call_thresholds(pr, ws=4096 + 4, n=n) == 1
+    # forward: w >= 1, D in {64,128}, G <= 32
+    c = _pr(window=0).c()
+    assert L.kvpop_masked_attn_fwd(ctypes.byref(c), *[vp(1)] * 7, vp(256), 1 << 40, vp(0)) == 1
+    c = _pr(head_dim=80).c()
+    assert L.kvpop_masked_attn_fwd(ctypes.byref(c), *[vp(1)] * 7, vp(256), 1 << 40, vp(0)) == 2
+    c = _pr(n_q_heads=64, n_kv_heads=1).c()
+    assert L.kvpop_future_target(ctypes.byref(c), *[vp(1)] * 4, vp(0), 0, vp(0)) == 2
+    c = _pr(qkv_dtype=7).c()
+    assert L.kvpop_future_target(ctypes.byref(c), *[vp(1)] * 4, vp(0), 0, vp(0)) == 1
+    # decode: NULL cache, missing pointers, short workspace
+    c = _pr().c()
+    assert L.kvpop_decode_step(ctypes.byref(c), None, *[vp(1)] * 7, vp(256), 1 << 40, vp(0)) == 1
+    cache = B._Cache(1, 1, 1, 1, 1)
+    assert L.kvpop_decode_step(ctypes.byref(c), ctypes.byref(cache), *[vp(1)] * 5, vp(0), vp(1),
+                               vp(256), 1 << 40, vp(0)) == 1
+    assert L.kvpop_decode_step(ctypes.byref(c), ctypes.byref(cache), *[vp(1)] * 7, vp(256), 16,
+                               vp(0)) == 3
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    _lib()
+    with pytest.raises(kv.KvpopError):
+        kv.thresholds(torch.zeros(1, 1, 8), 0, 1, 2)
