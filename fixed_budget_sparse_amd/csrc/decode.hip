@@ -5,18 +5,25 @@
 // scored then (the delayed readout), competing for the k long-range slots;
 // gist.science summary §2.1: B = s + w + k entries per KV head.
 //
-// Three kernels per step, all on the caller's stream:
-//  1. decide (one workgroup per (sequence, KV head)): reads the slot metadata,
+// Two kernels per step, on the caller's stream:
+//  1. decide (one wave per (sequence, KV head)): reads the slot metadata,
 //     picks the slot token p takes (slot p while the cache fills; afterwards
 //     the slot of u when u is dropped, or of the worst held long-range token
-//     when u replaces it), updates slot_pos / slot_prio / ring and writes the
-//     new K/V row into that slot.  The choice is exact integer/compare work.
-//  2. attend (split-K): every wave streams 32-slot blocks of K and V from HBM
-//     with coalesced loads, stages them in its own LDS region (V transposed)
-//     and runs S^T = K Q^T and O^T = V^T P^T on MFMA with the G query heads of
-//     the KV head as the 32 MFMA rows, keeping a per-wave online softmax; it
-//     writes a partial (max, sum, unnormalised O).
-//  3. combine: merges the partials of each query head into o and lse.
+//     when u replaces it), updates slot_pos / slot_prio / ring, writes the new
+//     K/V row into that slot.  The choice is exact integer/compare work; the
+//     worst token is found with a wave shuffle reduction.
+//  2. attend (split-K only when there are too few (sequence, KV head) pairs
+//     to fill the chip): every wave streams 32-slot blocks of K and V from
+//     HBM with coalesced loads, prefetching the next block into registers
+//     while the current one is in its private LDS region (V transposed), and
+//     runs S^T = K Q^T and O^T = V^T P^T on MFMA with the G query heads of the
+//     KV head as the MFMA rows, keeping an online softmax.  The 4 waves merge
+//     in LDS; with one split the workgroup writes o and lse, otherwise a
+//     partial (max, sum, unnormalised O).
+//  3. combine (only with several splits): merges the partials into o and lse.
+// A device-scope fence per workgroup (to let the last one merge) would write
+// back and invalidate the L2 of its XCD on this multi-XCD part, so the merge
+// across workgroups is a separate kernel.
 // The attention reads only K/V, so the metadata update of step 1 cannot race
 // with it, and stream order makes the new row visible to step 2.
 #include <type_traits>
@@ -30,7 +37,7 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kWaves = 4;
 constexpr int kBlk = 32;          // slots per wave iteration
-constexpr int kTargetBlocks = 2048;
+constexpr int kTargetBlocks = 512;   // 2 resident workgroups per CU
 
 struct DecArgs {
   void* ck;
@@ -45,34 +52,41 @@ struct DecArgs {
   const float* prio_leaving;
   void* o;
   float* lse;
-  float* part;          // [b, Hq, nparts, D + 2]: max (log2 units), sum, O
-  int Hq, Hkv, G, s, w, k, Bc, spl, nparts;
+  float* part;          // [b, Hq, nsplit, D + 2]: max (log2 units), sum, unnormalised O
+  int Hq, Hkv, G, s, w, k, Bc, spl, nsplit;
   float scale_log2;
 };
 
+// (priority, position, slot) of the worst long-range candidate seen so far:
+// lowest priority, ties to the highest position; slot < 0 means none.
+struct Worst {
+  float p;
+  int pos, slot;
+};
+
+__device__ __forceinline__ bool worse_than(const Worst& a, const Worst& b) {
+  return a.slot >= 0 && (b.slot < 0 || a.p < b.p || (a.p == b.p && a.pos > b.pos));
+}
+
 template <int D, bool kF32>
-__global__ __launch_bounds__(kThreads) void decode_decide_kernel(DecArgs a) {
-  __shared__ float r_prio[kThreads];
-  __shared__ int r_pos[kThreads];
-  __shared__ int r_slot[kThreads];
-  __shared__ int s_new;
-  const int tid = threadIdx.x;
+__global__ __launch_bounds__(64) void decode_decide_kernel(DecArgs a) {
+  const int lane = threadIdx.x;
   const int h = blockIdx.x, b = blockIdx.y;
-  const int p = a.pos[b];
-  if (p < 0) return;
   const int s = a.s, w = a.w, k = a.k, Bc = a.Bc;
   const size_t seg = (size_t)b * a.Hkv + h;
+  const int p = a.pos[b];
+  if (p < 0) return;
   int* spos = a.slot_pos + seg * Bc;
   float* sprio = a.slot_prio + seg * Bc;
   int* ring = a.ring + seg * w;
   const int u = p - w;
-  int u_slot = -1;
+  int u_slot = -1, ns;
   float pu = 0.0f;
-  bool keep_u = false;     // u becomes (or stays) a long-range token in its own slot
+  bool keep_u = false;      // u becomes a long-range token in its own slot
 
   if (p < Bc) {
     // filling: token p takes slot p; u (if eligible) joins the long-range set
-    if (tid == 0) s_new = p;
+    ns = p;
     if (p > 0 && u >= s) {
       u_slot = ring[p % w];
       pu = canonical_priority(a.prio_leaving[seg]);
@@ -83,47 +97,28 @@ __global__ __launch_bounds__(kThreads) void decode_decide_kernel(DecArgs a) {
     u_slot = ring[p % w];
     pu = canonical_priority(a.prio_leaving[seg]);
     if (k == 0) {
-      if (tid == 0) s_new = u_slot;
+      ns = u_slot;
     } else {
-      float bp = __builtin_huge_valf();
-      int bpos = -1, bslot = -1;
-      for (int j = tid; j < Bc; j += kThreads) {
+      Worst best{__builtin_huge_valf(), -1, -1};
+      for (int j = lane; j < Bc; j += 64) {
         const int sp = spos[j];
-        if (sp >= s && sp < u) {
-          const float pr = sprio[j];
-          if (pr < bp || (pr == bp && sp > bpos)) {
-            bp = pr;
-            bpos = sp;
-            bslot = j;
-          }
-        }
+        const Worst c{sprio[j], sp, j};
+        if (sp >= s && sp < u && worse_than(c, best)) best = c;
       }
-      r_prio[tid] = bp;
-      r_pos[tid] = bpos;
-      r_slot[tid] = bslot;
-      __syncthreads();
-      for (int off = kThreads / 2; off > 0; off >>= 1) {
-        if (tid < off) {
-          const float op = r_prio[tid + off];
-          const int opos = r_pos[tid + off];
-          if (r_slot[tid + off] >= 0 &&
-              (r_slot[tid] < 0 || op < r_prio[tid] || (op == r_prio[tid] && opos > r_pos[tid]))) {
-            r_prio[tid] = op;
-            r_pos[tid] = opos;
-            r_slot[tid] = r_slot[tid + off];
-          }
-        }
-        __syncthreads();
+#pragma unroll
+      for (int off = 32; off > 0; off >>= 1) {
+        Worst o;
+        o.p = __shfl_xor(best.p, off);
+        o.pos = __shfl_xor(best.pos, off);
+        o.slot = __shfl_xor(best.slot, off);
+        if (worse_than(o, best)) best = o;
       }
-      const int worst = r_slot[0];
-      keep_u = worst >= 0 && pu > r_prio[0];
-      if (tid == 0) s_new = keep_u ? worst : u_slot;
+      keep_u = best.slot >= 0 && pu > best.p;
+      ns = keep_u ? best.slot : u_slot;
     }
   }
-  __syncthreads();   // every read of the metadata precedes the updates below
-  const int ns = s_new;
   if ((unsigned)ns >= (unsigned)Bc) return;   // inconsistent cache state: leave it untouched
-  if (tid == 0) {
+  if (lane == 0) {
     if (keep_u && (unsigned)u_slot < (unsigned)Bc) sprio[u_slot] = pu;
     ring[p % w] = ns;
     spos[ns] = p;
@@ -131,13 +126,13 @@ __global__ __launch_bounds__(kThreads) void decode_decide_kernel(DecArgs a) {
   }
   // the new token's K/V row goes into its slot
   constexpr int kWords = D * (kF32 ? 4 : 2) / 4;
-  if (tid < kWords) {
-    const uint32_t* kn = (const uint32_t*)a.k_new + seg * kWords;
-    const uint32_t* vn = (const uint32_t*)a.v_new + seg * kWords;
-    uint32_t* kc = (uint32_t*)a.ck + (seg * Bc + ns) * kWords;
-    uint32_t* vc = (uint32_t*)a.cv + (seg * Bc + ns) * kWords;
-    kc[tid] = kn[tid];
-    vc[tid] = vn[tid];
+  const uint32_t* kn = (const uint32_t*)a.k_new + seg * kWords;
+  const uint32_t* vn = (const uint32_t*)a.v_new + seg * kWords;
+  uint32_t* kc = (uint32_t*)a.ck + (seg * Bc + ns) * kWords;
+  uint32_t* vc = (uint32_t*)a.cv + (seg * Bc + ns) * kWords;
+  for (int i = lane; i < kWords; i += 64) {
+    kc[i] = kn[i];
+    vc[i] = vn[i];
   }
 }
 
@@ -150,11 +145,15 @@ struct DecLds {
   static constexpr int kBytes = kF32 ? kBlk * KS * 4 : kBlk * KS * 2;
   static constexpr int vBytes = kF32 ? kBlk * VS * 4 : D * VS * 2;
   static constexpr int waveBytes = ((kBytes + vBytes + 15) / 16) * 16;
+  // K: 16-byte pieces per lane; V: 32-bit words per lane (bf16: 4 groups x 8 keys per dim pair)
+  static constexpr int KPL = kBlk * (D * (kF32 ? 4 : 2) / 16) / 64;
+  static constexpr int VPL = kF32 ? KPL : 4 * (D / 2) / 64 * 8;
 };
 
-template <int D, bool kF32>
+template <int D, bool kF32, bool kF32Out>
 __global__ __launch_bounds__(kThreads, 2) void decode_attend_kernel(DecArgs a) {
   using L = DecLds<D, kF32>;
+  static_assert(kWaves * L::waveBytes >= kWaves * 32 * (D + 2) * 4, "merge area");
   __shared__ __attribute__((aligned(16))) unsigned char lds[kWaves * L::waveBytes];
   const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
   const int hh = lane >> 5, li = lane & 31;
@@ -196,33 +195,63 @@ __global__ __launch_bounds__(kThreads, 2) void decode_attend_kernel(DecArgs a) {
   float m_run = kNegInf, l_run = 0.0f;
   const size_t cbase = seg * (size_t)Bc * D;
 
-  for (int blk = j_lo + wave * kBlk; blk < j_hi; blk += kWaves * kBlk) {
-    // ---- stage 32 slots of K (row-major) and V into this wave's LDS
+  // ---- staging of one 32-slot block: HBM -> registers -> this wave's LDS
+  uint4 kst[L::KPL];
+  uint32_t vst[kF32 ? 1 : L::VPL];
+  uint4 vst4[kF32 ? L::KPL : 1];
+  auto load_blk = [&](int blk) {
     if constexpr (!kF32) {
       const uint16_t* kg = (const uint16_t*)a.ck + cbase;
       const uint16_t* vg = (const uint16_t*)a.cv + cbase;
+      constexpr int PPR = D / 8;
+#pragma unroll
+      for (int i = 0; i < L::KPL; ++i) {
+        const int pi = lane + 64 * i;
+        const int slot = blk + pi / PPR;
+        kst[i] = slot < j_hi ? *(const uint4*)(kg + (size_t)slot * D + (pi % PPR) * 8)
+                             : make_uint4(0, 0, 0, 0);
+      }
+#pragma unroll
+      for (int i = 0; i < L::VPL / 8; ++i) {
+        const int task = lane + 64 * i;
+        const int grp = task / (D / 2), dp = task % (D / 2);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int slot = blk + 16 * (grp >> 1) + 8 * (e >> 2) + 4 * (grp & 1) + (e & 3);
+          vst[8 * i + e] = slot < j_hi ? *(const uint32_t*)(vg + (size_t)slot * D + 2 * dp) : 0u;
+        }
+      }
+    } else {
+      const float* kg = (const float*)a.ck + cbase;
+      const float* vg = (const float*)a.cv + cbase;
+      constexpr int PPR = D / 4;
+#pragma unroll
+      for (int i = 0; i < L::KPL; ++i) {
+        const int pi = lane + 64 * i;
+        const int slot = blk + pi / PPR;
+        const size_t off = (size_t)slot * D + (pi % PPR) * 4;
+        kst[i] = slot < j_hi ? *(const uint4*)(kg + off) : make_uint4(0, 0, 0, 0);
+        vst4[i] = slot < j_hi ? *(const uint4*)(vg + off) : make_uint4(0, 0, 0, 0);
+      }
+    }
+  };
+  auto store_blk = [&]() {
+    if constexpr (!kF32) {
       uint16_t* kl = (uint16_t*)my;
       uint16_t* vl = (uint16_t*)(my + L::kBytes);
       constexpr int PPR = D / 8;
 #pragma unroll
-      for (int i = 0; i < kBlk * PPR / 64; ++i) {
+      for (int i = 0; i < L::KPL; ++i) {
         const int pi = lane + 64 * i;
-        const int row = pi / PPR, piece = pi % PPR;
-        const int slot = blk + row;
-        uint4 val = make_uint4(0, 0, 0, 0);
-        if (slot < j_hi) val = *(const uint4*)(kg + (size_t)slot * D + piece * 8);
-        *(uint4*)(kl + row * L::KS + piece * 8) = val;
+        *(uint4*)(kl + (pi / PPR) * L::KS + (pi % PPR) * 8) = kst[i];
       }
+      // V^T: column c = 16*ks + 8*hh + e of LDS row d holds slot
+      // 16*ks + 8*(e>>2) + 4*hh + (e&3) of the block (the P operand layout)
 #pragma unroll
-      for (int i = 0; i < 4 * (D / 2) / 64; ++i) {
+      for (int i = 0; i < L::VPL / 8; ++i) {
         const int task = lane + 64 * i;
         const int grp = task / (D / 2), dp = task % (D / 2);
-        uint32_t x[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int slot = blk + 16 * (grp >> 1) + 8 * (e >> 2) + 4 * (grp & 1) + (e & 3);
-          x[e] = slot < j_hi ? *(const uint32_t*)(vg + (size_t)slot * D + 2 * dp) : 0u;
-        }
+        const uint32_t* x = &vst[8 * i];
         uint4 lo, hi;
         lo.x = (x[0] & 0xffffu) | (x[1] << 16);
         lo.y = (x[2] & 0xffffu) | (x[3] << 16);
@@ -236,27 +265,29 @@ __global__ __launch_bounds__(kThreads, 2) void decode_attend_kernel(DecArgs a) {
         *(uint4*)(vl + (2 * dp + 1) * L::VS + grp * 8) = hi;
       }
     } else {
-      const float* kg = (const float*)a.ck + cbase;
-      const float* vg = (const float*)a.cv + cbase;
       float* kl = (float*)my;
       float* vl = (float*)(my + L::kBytes);
       constexpr int PPR = D / 4;
 #pragma unroll
-      for (int i = 0; i < kBlk * PPR / 64; ++i) {
+      for (int i = 0; i < L::KPL; ++i) {
         const int pi = lane + 64 * i;
         const int row = pi / PPR, piece = pi % PPR;
-        const int slot = blk + row;
-        float4 kv4 = make_float4(0.f, 0.f, 0.f, 0.f), vv4 = kv4;
-        if (slot < j_hi) {
-          kv4 = *(const float4*)(kg + (size_t)slot * D + piece * 4);
-          vv4 = *(const float4*)(vg + (size_t)slot * D + piece * 4);
-        }
         float* kd = kl + row * L::KS + piece * 4;
-        kd[0] = kv4.x; kd[1] = kv4.y; kd[2] = kv4.z; kd[3] = kv4.w;
-        *(float4*)(vl + row * L::VS + piece * 4) = vv4;
+        kd[0] = __uint_as_float(kst[i].x);
+        kd[1] = __uint_as_float(kst[i].y);
+        kd[2] = __uint_as_float(kst[i].z);
+        kd[3] = __uint_as_float(kst[i].w);
+        *(uint4*)(vl + row * L::VS + piece * 4) = vst4[i];
       }
     }
+  };
+
+  int blk = j_lo + wave * kBlk;
+  if (blk < j_hi) load_blk(blk);
+  for (; blk < j_hi; blk += kWaves * kBlk) {
+    store_blk();
     wave_lds_fence();
+    if (blk + kWaves * kBlk < j_hi) load_blk(blk + kWaves * kBlk);   // in flight during the math
 
     // ---- S^T = K Q^T (32 slots x 32 rows)
     f32x16 sacc = f32x16{};
@@ -317,56 +348,99 @@ __global__ __launch_bounds__(kThreads, 2) void decode_attend_kernel(DecArgs a) {
     wave_lds_fence();
   }
 
-  // ---- this wave's partial for each query head row
+  // ---- merge the 4 waves in LDS: mg[wave][row][0] = max, [1] = sum, [2..] = O
   const float l_tot = l_run + __shfl_xor(l_run, 32);
+  __syncthreads();                               // staging areas are free now
+  float* mg = (float*)lds;
+  constexpr int RS = D + 2;
   if (row_ok) {
-    float* pp = a.part + (((size_t)b * a.Hq + hq) * a.nparts + split * kWaves + wave) * (D + 2);
+    float* r = mg + (wave * 32 + li) * RS;
     if (hh == 0) {
-      pp[0] = m_run;
-      pp[1] = l_tot;
+      r[0] = m_run;
+      r[1] = l_tot;
     }
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int d = 32 * db + 8 * j + 4 * hh;
+      for (int j = 0; j < 4; ++j)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) pp[2 + d + r] = oacc[db][4 * j + r];
+        for (int rr = 0; rr < 4; ++rr) r[2 + 32 * db + 8 * j + 4 * hh + rr] = oacc[db][4 * j + rr];
+  }
+  __syncthreads();
+
+  const int nsplit = a.nsplit;
+  auto write_out = [&](int g, int d, float M, float Ls, float Od) {
+    const size_t oi = ((size_t)b * a.Hq + h * G + g) * D + d;
+    const float inv = Ls > 0.0f ? 1.0f / Ls : 0.0f;
+    if constexpr (kF32Out) ((float*)a.o)[oi] = Od * inv;
+    else ((__bf16*)a.o)[oi] = (__bf16)(Od * inv);
+    if (d == 0 && a.lse)
+      a.lse[(size_t)b * a.Hq + h * G + g] = Ls > 0.0f ? (M + log2f(Ls)) * kLn2 : kNegInf;
+  };
+  for (int idx = tid; idx < G * D; idx += kThreads) {
+    const int g = idx / D, d = idx % D;
+    float M = kNegInf;
+#pragma unroll
+    for (int wv = 0; wv < kWaves; ++wv) M = fmaxf(M, mg[(wv * 32 + g) * RS]);
+    float Ls = 0.0f, Od = 0.0f;
+    if (M != kNegInf) {
+#pragma unroll
+      for (int wv = 0; wv < kWaves; ++wv) {
+        const float* r = mg + (wv * 32 + g) * RS;
+        const float wt = exp2_fast(r[0] - M);
+        Ls += r[1] * wt;
+        Od += r[2 + d] * wt;
       }
+    }
+    if (nsplit == 1) {
+      write_out(g, d, M, Ls, Od);
+    } else {
+      float* pp = a.part + (((size_t)b * a.Hq + h * G + g) * nsplit + split) * RS;
+      if (d == 0) {
+        pp[0] = M;
+        pp[1] = Ls;
+      }
+      pp[2 + d] = Od;
+    }
   }
 }
 
+// Merges the per-split partials of one (sequence, KV head) into o and lse.
 template <int D, bool kF32Out>
-__global__ __launch_bounds__(128) void decode_combine_kernel(DecArgs a) {
-  const int hq = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
-  const float* pp = a.part + ((size_t)b * a.Hq + hq) * a.nparts * (D + 2);
-  float M = kNegInf;
-  for (int j = 0; j < a.nparts; ++j) M = fmaxf(M, pp[j * (D + 2)]);
-  float Lsum = 0.0f, od = 0.0f;
-  if (M != kNegInf) {
-    for (int j = 0; j < a.nparts; ++j) {
-      const float mj = pp[j * (D + 2)];
-      const float wgt = exp2_fast(mj - M);        // 0 for empty partials (mj = -inf)
-      Lsum += pp[j * (D + 2) + 1] * wgt;
-      if (tid < D) od += pp[j * (D + 2) + 2 + tid] * wgt;
+__global__ __launch_bounds__(kThreads) void decode_combine_kernel(DecArgs a) {
+  constexpr int RS = D + 2;
+  const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+  const int G = a.G, nsplit = a.nsplit;
+  for (int idx = tid; idx < G * D; idx += kThreads) {
+    const int g = idx / D, d = idx % D;
+    const size_t hq = (size_t)b * a.Hq + h * G + g;
+    const float* pp = a.part + hq * nsplit * RS;
+    float M = kNegInf;
+    for (int j = 0; j < nsplit; ++j) M = fmaxf(M, pp[j * RS]);
+    float Ls = 0.0f, Od = 0.0f;
+    if (M != kNegInf) {
+#pragma unroll 4
+      for (int j = 0; j < nsplit; ++j) {
+        const float wt = exp2_fast(pp[j * RS] - M);
+        Ls += pp[j * RS + 1] * wt;
+        Od += pp[j * RS + 2 + d] * wt;
+      }
     }
+    const float inv = Ls > 0.0f ? 1.0f / Ls : 0.0f;
+    if constexpr (kF32Out) ((float*)a.o)[hq * D + d] = Od * inv;
+    else ((__bf16*)a.o)[hq * D + d] = (__bf16)(Od * inv);
+    if (d == 0 && a.lse) a.lse[hq] = Ls > 0.0f ? (M + log2f(Ls)) * kLn2 : kNegInf;
   }
-  const float inv = Lsum > 0.0f ? 1.0f / Lsum : 0.0f;
-  if (tid < D) {
-    const size_t oi = ((size_t)b * a.Hq + hq) * D + tid;
-    if constexpr (kF32Out) ((float*)a.o)[oi] = od * inv;
-    else ((__bf16*)a.o)[oi] = (__bf16)(od * inv);
-  }
-  if (tid == 0 && a.lse)
-    a.lse[(size_t)b * a.Hq + hq] = Lsum > 0.0f ? (M + log2f(Lsum)) * kLn2 : kNegInf;
 }
 
 template <int D, bool kF32, bool kF32Out>
-void launch_dec(const DecArgs& a, int b, int nsplit, hipStream_t st) {
-  hipLaunchKernelGGL((decode_decide_kernel<D, kF32>), dim3(a.Hkv, b), dim3(kThreads), 0, st, a);
-  hipLaunchKernelGGL((decode_attend_kernel<D, kF32>), dim3(nsplit, a.Hkv, b), dim3(kThreads), 0,
-                     st, a);
-  hipLaunchKernelGGL((decode_combine_kernel<D, kF32Out>), dim3(a.Hq, b), dim3(128), 0, st, a);
+void launch_dec(const DecArgs& a, int b, hipStream_t st) {
+  hipLaunchKernelGGL((decode_decide_kernel<D, kF32>), dim3(a.Hkv, b), dim3(64), 0, st, a);
+  hipLaunchKernelGGL((decode_attend_kernel<D, kF32, kF32Out>), dim3(a.nsplit, a.Hkv, b),
+                     dim3(kThreads), 0, st, a);
+  if (a.nsplit > 1)
+    hipLaunchKernelGGL((decode_combine_kernel<D, kF32Out>), dim3(a.Hkv, b), dim3(kThreads), 0, st,
+                       a);
 }
 
 }  // namespace
@@ -395,7 +469,7 @@ int decode_splits(const Dims& d) {
 
 size_t decode_ws_bytes(const Dims& d) {
   const int ns = decode_splits(d);
-  return align256((size_t)d.b * d.Hq * ns * kWaves * (d.D + 2) * 4);
+  return ns > 1 ? align256((size_t)d.b * d.Hq * ns * (d.D + 2) * 4) : 0;
 }
 
 hipError_t launch_decode(const Dims& d, const CacheArgs& c, const int* pos, const void* q,
@@ -406,25 +480,26 @@ hipError_t launch_decode(const Dims& d, const CacheArgs& c, const int* pos, cons
   DecArgs a;
   a.ck = c.k; a.cv = c.v; a.slot_pos = c.slot_pos; a.slot_prio = c.slot_prio; a.ring = c.ring;
   a.pos = pos; a.q = q; a.k_new = k_new; a.v_new = v_new; a.prio_leaving = prio_leaving;
-  a.o = o; a.lse = lse; a.part = (float*)ws;
+  a.o = o; a.lse = lse;
+  a.part = (float*)ws;
   a.Hq = d.Hq; a.Hkv = d.Hkv; a.G = d.G; a.s = d.s; a.w = d.w; a.k = d.k;
-  a.Bc = (int)d.budget(); a.spl = spl; a.nparts = nsplit * kWaves;
+  a.Bc = (int)d.budget(); a.spl = spl; a.nsplit = nsplit;
   a.scale_log2 = d.scale * 1.4426950408889634f;
   if (d.D == 128) {
     if (d.f32_in) {
-      if (d.f32_out) launch_dec<128, true, true>(a, d.b, nsplit, st);
-      else launch_dec<128, true, false>(a, d.b, nsplit, st);
+      if (d.f32_out) launch_dec<128, true, true>(a, d.b, st);
+      else launch_dec<128, true, false>(a, d.b, st);
     } else {
-      if (d.f32_out) launch_dec<128, false, true>(a, d.b, nsplit, st);
-      else launch_dec<128, false, false>(a, d.b, nsplit, st);
+      if (d.f32_out) launch_dec<128, false, true>(a, d.b, st);
+      else launch_dec<128, false, false>(a, d.b, st);
     }
   } else {
     if (d.f32_in) {
-      if (d.f32_out) launch_dec<64, true, true>(a, d.b, nsplit, st);
-      else launch_dec<64, true, false>(a, d.b, nsplit, st);
+      if (d.f32_out) launch_dec<64, true, true>(a, d.b, st);
+      else launch_dec<64, true, false>(a, d.b, st);
     } else {
-      if (d.f32_out) launch_dec<64, false, true>(a, d.b, nsplit, st);
-      else launch_dec<64, false, false>(a, d.b, nsplit, st);
+      if (d.f32_out) launch_dec<64, false, true>(a, d.b, st);
+      else launch_dec<64, false, false>(a, d.b, st);
     }
   }
   return hipGetLastError();

@@ -11,15 +11,21 @@
 // to the caller).
 //
 // Design (gfx950):
-//  * A workgroup owns 128 key rows t (4 waves x 32) of one query head.  It
-//    streams the future queries d in 64-column chunks staged in LDS, shared
-//    by the 4 waves; each wave keeps its 32 key rows as the MFMA B operand in
-//    registers, so X^T[d][t] = Q K^T leaves every lane owning one row t.
-//  * Each score becomes exp2(x * scale log2 e - LSE_d log2 e) and is summed
-//    directly: with the dense LSE every exponent is <= 0, so no running
-//    maximum or rescaling is needed (3 VALU operations per score).
+//  * A workgroup owns 256 key rows t of one query head: each of its 4 waves
+//    keeps two 32-row blocks of K as MFMA B operands in registers, so every
+//    Q operand read from LDS feeds two v_mfma_f32_32x32x16_bf16.
+//  * The future queries d stream through LDS in 64-row chunks shared by the 4
+//    waves, double-buffered: the global loads of chunk c+1 are issued before
+//    the math of chunk c and stored to the other buffer after it, so one
+//    barrier per chunk suffices and the load latency hides behind the MFMAs.
+//  * X^T = Q K^T leaves every lane owning one row t; each score becomes
+//    exp2(x * scale log2 e - LSE_d log2 e) and is summed directly: with the
+//    dense LSE every exponent is <= 0, so no running maximum is needed.
 //  * Chunks wholly below a wave's first row + w are skipped; the d >= t + w
-//    test runs only on the chunks that straddle the band.
+//    test (a select) runs only on chunks that straddle the band.
+//  * Blocks are renumbered so that each XCD (its own L2) works through whole
+//    heads: consecutive logical blocks are consecutive key tiles of one head,
+//    which read the same Q stream.
 #include <type_traits>
 
 #include "kvpop_device.h"
@@ -29,7 +35,8 @@ namespace kvpop {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kRowsPerTile = 128;
+constexpr int kWaveRows = 64;                    // two 32-row MFMA blocks per wave
+constexpr int kRowsPerTile = 4 * kWaveRows;
 constexpr int kChunk = 64;
 
 struct TgtArgs {
@@ -37,141 +44,183 @@ struct TgtArgs {
   const void* k;
   const float* lse;
   float* target;
-  int S, Hq, Hkv, G, w;
+  int S, Hq, Hkv, G, w, ntiles;
   float scale_log2;
+};
+
+template <int D, bool kF32>
+struct TgtGeom {
+  static constexpr int esz = kF32 ? 4 : 2;
+  static constexpr int QS = kF32 ? D + 1 : D + 8;           // LDS row stride (elements)
+  static constexpr int bufBytes = ((kChunk * QS * esz + 15) / 16) * 16;
+  static constexpr int PPR = D * esz / 16;                   // 16-byte pieces per Q row
+  static constexpr int NPIECE = kChunk * PPR / kThreads;     // pieces per thread per chunk
+  static constexpr int NKS = kF32 ? D / 2 : D / 16;          // MFMA k-steps
 };
 
 template <int D, bool kF32In>
 __global__ __launch_bounds__(kThreads, 2) void future_target_kernel(TgtArgs a) {
-  constexpr int QS = kF32In ? D + 1 : D + 8;                 // LDS row stride (elements)
-  constexpr int qBytes = kChunk * QS * (kF32In ? 4 : 2);
-  __shared__ __attribute__((aligned(16))) unsigned char q_lds[qBytes];
-  __shared__ __attribute__((aligned(16))) float nlse[kChunk];  // -LSE_d * log2(e)
+  using Gm = TgtGeom<D, kF32In>;
+  __shared__ __attribute__((aligned(16))) unsigned char q_lds[2][Gm::bufBytes];
+  __shared__ __attribute__((aligned(16))) float nlse[2][kChunk];   // -LSE_d * log2(e)
 
   const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
   const int hh = lane >> 5, li = lane & 31;
-  const int tile = blockIdx.x, hq = blockIdx.y, b = blockIdx.z;
+  const int L = xcd_logical_block((int)blockIdx.x, (int)gridDim.x);
+  const int tile = L % a.ntiles;
+  const int hq = (L / a.ntiles) % a.Hq;
+  const int b = L / (a.ntiles * a.Hq);
   const int S = a.S, w = a.w;
   const int h = hq / a.G;
   const int t0 = tile * kRowsPerTile;
-  const int t = t0 + wave * 32 + li;              // this lane's key row
-  const int t_first = t0 + wave * 32;
-  const int t_last = min(t_first + 31, S - 1);
+  const int rbase = t0 + wave * kWaveRows;        // this wave's first key row
   float* out = a.target + ((size_t)b * a.Hq + hq) * S;
 
   const int d_start = t0 + w;                      // first query any row of the tile needs
   if (d_start > S - 1) {
-    if (hh == 0 && t < S) out[t] = kNegInf;
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+      const int t = rbase + 32 * rb + li;
+      if (hh == 0 && t < S) out[t] = kNegInf;
+    }
     return;
   }
 
-  // key operand (B of X^T = Q K^T): row t, dims [16ks + 8hh, +8)
-  constexpr int NKS = kF32In ? D / 2 : D / 16;
+  // key operands (B of X^T = Q K^T): rows rbase + 32 rb + li, dims [16ks + 8hh, +8)
   typedef typename std::conditional<kF32In, float, bf16x8>::type KOp;
-  KOp kop[NKS];
-  {
+  KOp kop[2][Gm::NKS];
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb) {
+    const int t = rbase + 32 * rb + li;
     const bool ok = t < S;
     const size_t krow = (((size_t)b * a.Hkv + h) * S + (ok ? t : 0)) * D;
     if constexpr (kF32In) {
       const float* kp = (const float*)a.k + krow;
 #pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) kop[ks] = ok ? kp[2 * ks + hh] : 0.0f;
+      for (int ks = 0; ks < Gm::NKS; ++ks) kop[rb][ks] = ok ? kp[2 * ks + hh] : 0.0f;
     } else {
       const uint16_t* kp = (const uint16_t*)a.k + krow;
 #pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) {
+      for (int ks = 0; ks < Gm::NKS; ++ks) {
         uint4 u = make_uint4(0, 0, 0, 0);
         if (ok) u = *(const uint4*)(kp + 16 * ks + 8 * hh);
-        kop[ks] = as_bf16x8(u);
+        kop[rb][ks] = as_bf16x8(u);
       }
     }
   }
 
-  const size_t qbase = ((size_t)b * a.Hq + hq) * S * D;
+  const unsigned char* qg = (const unsigned char*)a.q + ((size_t)b * a.Hq + hq) * S * D * Gm::esz;
   const float* lse = a.lse + ((size_t)b * a.Hq + hq) * S;
-  float sum = 0.0f;
 
-  for (int d0 = d_start; d0 < S; d0 += kChunk) {
-    // ---- stage Q rows d0 .. d0+63 and their -LSE
-    if constexpr (!kF32In) {
-      const uint16_t* qg = (const uint16_t*)a.q + qbase;
-      uint16_t* ql = (uint16_t*)q_lds;
-      constexpr int PPR = D / 8;
+  // staging of one chunk: global -> registers, registers -> LDS buffer
+  uint4 stage[Gm::NPIECE];
+  float stage_lse = 0.0f;
+  auto load_chunk = [&](int d0) {
 #pragma unroll
-      for (int i = 0; i < kChunk * PPR / kThreads; ++i) {
-        const int p = tid + i * kThreads;
-        const int row = p / PPR, piece = p % PPR;
-        const int d = d0 + row;
-        uint4 val = make_uint4(0, 0, 0, 0);
-        if (d < S) val = *(const uint4*)(qg + (size_t)d * D + piece * 8);
-        *(uint4*)(ql + row * QS + piece * 8) = val;
-      }
-    } else {
-      const float* qg = (const float*)a.q + qbase;
-      float* ql = (float*)q_lds;
-      constexpr int PPR = D / 4;
-#pragma unroll
-      for (int i = 0; i < kChunk * PPR / kThreads; ++i) {
-        const int p = tid + i * kThreads;
-        const int row = p / PPR, piece = p % PPR;
-        const int d = d0 + row;
-        float4 val = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (d < S) val = *(const float4*)(qg + (size_t)d * D + piece * 4);
-        float* dst = ql + row * QS + piece * 4;
-        dst[0] = val.x; dst[1] = val.y; dst[2] = val.z; dst[3] = val.w;
-      }
+    for (int i = 0; i < Gm::NPIECE; ++i) {
+      const int p = tid + i * kThreads;
+      const int row = p / Gm::PPR, piece = p % Gm::PPR;
+      const int d = d0 + row;
+      stage[i] = make_uint4(0, 0, 0, 0);
+      if (d < S) stage[i] = *(const uint4*)(qg + (size_t)d * D * Gm::esz + piece * 16);
     }
     if (tid < kChunk) {
       const int d = d0 + tid;
-      nlse[tid] = d < S ? -lse[d] * kLog2e : kNegInf;
+      stage_lse = d < S ? -lse[d] * kLog2e : kNegInf;
     }
-    __syncthreads();
+  };
+  auto store_chunk = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < Gm::NPIECE; ++i) {
+      const int p = tid + i * kThreads;
+      const int row = p / Gm::PPR, piece = p % Gm::PPR;
+      if constexpr (kF32In) {
+        float* dst = (float*)q_lds[buf] + row * Gm::QS + piece * 4;
+        dst[0] = __uint_as_float(stage[i].x);
+        dst[1] = __uint_as_float(stage[i].y);
+        dst[2] = __uint_as_float(stage[i].z);
+        dst[3] = __uint_as_float(stage[i].w);
+      } else {
+        *(uint4*)((uint16_t*)q_lds[buf] + row * Gm::QS + piece * 8) = stage[i];
+      }
+    }
+    if (tid < kChunk) nlse[buf][tid] = stage_lse;
+  };
 
-    // ---- this wave's rows need d >= t + w: skip chunks wholly below
-    if (d0 + kChunk - 1 >= t_first + w) {
-      const bool need_mask = d0 < t_last + w || d0 + kChunk - 1 > S - 1;
+  float sum[2] = {0.0f, 0.0f};
+  const int nchunks = (S - d_start + kChunk - 1) / kChunk;
+  load_chunk(d_start);
+  store_chunk(0);
+  __syncthreads();
+
+  for (int c = 0; c < nchunks; ++c) {
+    const int d0 = d_start + c * kChunk;
+    const int buf = c & 1;
+    const bool has_next = c + 1 < nchunks;
+    if (has_next) load_chunk(d0 + kChunk);
+
+    // this wave's rows need d >= t + w: skip chunks wholly below
+    if (d0 + kChunk - 1 >= rbase + w) {
+      const bool need_mask = d0 < rbase + kWaveRows - 1 + w || d0 + kChunk - 1 > S - 1;
 #pragma unroll
       for (int cb = 0; cb < 2; ++cb) {
-        f32x16 acc = f32x16{};
+        f32x16 acc0 = f32x16{}, acc1 = f32x16{};
         if constexpr (!kF32In) {
-          const uint16_t* ql = (const uint16_t*)q_lds + (32 * cb + li) * QS + 8 * hh;
+          const uint16_t* ql = (const uint16_t*)q_lds[buf] + (32 * cb + li) * Gm::QS + 8 * hh;
 #pragma unroll
-          for (int ks = 0; ks < NKS; ++ks)
-            acc = mfma32x32x16(as_bf16x8(*(const uint4*)(ql + 16 * ks)), kop[ks], acc);
+          for (int ks = 0; ks < Gm::NKS; ++ks) {
+            const bf16x8 av = as_bf16x8(*(const uint4*)(ql + 16 * ks));
+            acc0 = mfma32x32x16(av, kop[0][ks], acc0);
+            acc1 = mfma32x32x16(av, kop[1][ks], acc1);
+          }
         } else {
-          const float* ql = (const float*)q_lds + (32 * cb + li) * QS + hh;
+          const float* ql = (const float*)q_lds[buf] + (32 * cb + li) * Gm::QS + hh;
 #pragma unroll
-          for (int ks = 0; ks < NKS; ++ks) acc = mfma32x32x2(ql[2 * ks], kop[ks], acc);
+          for (int ks = 0; ks < Gm::NKS; ++ks) {
+            const float av = ql[2 * ks];
+            acc0 = mfma32x32x2(av, kop[0][ks], acc0);
+            acc1 = mfma32x32x2(av, kop[1][ks], acc1);
+          }
         }
-        // lane holds columns d = d0 + 32cb + 8j + 4hh + r for row t
+        // lane holds columns d = d0 + 32cb + 8j + 4hh + r of rows rbase + 32rb + li
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int dl = 32 * cb + 8 * j + 4 * hh;
-          const f32x4 bias = *(const f32x4*)(&nlse[dl]);
+          const f32x4 bias = *(const f32x4*)(&nlse[buf][dl]);
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            float p = exp2_fast(fmaf(acc[4 * j + r], a.scale_log2, bias[r]));
-            if (need_mask) {   // wave-uniform; the test itself is a select
+            float p0 = exp2_fast(fmaf(acc0[4 * j + r], a.scale_log2, bias[r]));
+            float p1 = exp2_fast(fmaf(acc1[4 * j + r], a.scale_log2, bias[r]));
+            if (need_mask) {     // wave-uniform; the tests are selects
               const int d = d0 + dl + r;
-              p = ((d >= t + w) & (d < S)) ? p : 0.0f;
+              const int t_0 = rbase + li;
+              p0 = ((d >= t_0 + w) & (d < S)) ? p0 : 0.0f;
+              p1 = ((d >= t_0 + 32 + w) & (d < S)) ? p1 : 0.0f;
             }
-            sum += p;
+            sum[0] += p0;
+            sum[1] += p1;
           }
         }
       }
     }
+    if (has_next) store_chunk(buf ^ 1);
     __syncthreads();
   }
 
-  const float tot = sum + __shfl_xor(sum, 32);
-  if (hh == 0 && t < S) out[t] = tot > 0.0f ? log2f(tot) * kLn2 : kNegInf;
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb) {
+    const float tot = sum[rb] + __shfl_xor(sum[rb], 32);
+    const int t = rbase + 32 * rb + li;
+    if (hh == 0 && t < S) out[t] = tot > 0.0f ? log2f(tot) * kLn2 : kNegInf;
+  }
 }
 
 template <int D, bool kF32In>
-void launch_tgt(const TgtArgs& a, int b, hipStream_t st) {
-  const int ntiles = (a.S + kRowsPerTile - 1) / kRowsPerTile;
-  hipLaunchKernelGGL((future_target_kernel<D, kF32In>), dim3(ntiles, a.Hq, b), dim3(kThreads), 0,
-                     st, a);
+void launch_tgt(TgtArgs a, int b, hipStream_t st) {
+  a.ntiles = (a.S + kRowsPerTile - 1) / kRowsPerTile;
+  const long long n = (long long)a.ntiles * a.Hq * b;
+  hipLaunchKernelGGL((future_target_kernel<D, kF32In>), dim3((unsigned)n), dim3(kThreads), 0, st,
+                     a);
 }
 
 }  // namespace
@@ -182,7 +231,7 @@ hipError_t launch_future_target(const Dims& d, const void* q, const void* k, con
                                 float* target, void*, hipStream_t st) {
   TgtArgs a;
   a.q = q; a.k = k; a.lse = lse; a.target = target;
-  a.S = d.S; a.Hq = d.Hq; a.Hkv = d.Hkv; a.G = d.G; a.w = d.w;
+  a.S = d.S; a.Hq = d.Hq; a.Hkv = d.Hkv; a.G = d.G; a.w = d.w; a.ntiles = 0;
   a.scale_log2 = d.scale * 1.4426950408889634f;
   if (d.D == 128) {
     if (d.f32_in) launch_tgt<128, true>(a, d.b, st);

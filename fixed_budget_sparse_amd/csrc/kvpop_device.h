@@ -36,6 +36,17 @@ __device__ __forceinline__ void wave_lds_fence() {
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 }
 
+// Workgroups of a 1-D grid are dispatched round-robin over the 8 XCDs, each
+// with its own L2.  This maps the hardware block id to a logical id such that
+// every XCD receives a contiguous range of logical ids (a bijection on
+// [0, n)), so neighbouring logical blocks, which share data, share an L2.
+__device__ __forceinline__ int xcd_logical_block(int bid, int n) {
+  constexpr int kXcds = 8;
+  const int q = n / kXcds, r = n % kXcds;
+  const int x = bid % kXcds, j = bid / kXcds;
+  return (x < r ? x * (q + 1) : r * (q + 1) + (x - r) * q) + j;
+}
+
 // ---------------------------------------------------------------- numbers
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 

@@ -117,16 +117,19 @@ struct FwdLds {
 template <int D, bool kF32In, bool kF32Out>
 __global__ __launch_bounds__(kThreads, 2) void masked_fwd_kernel(FwdArgs a) {
   using L = FwdLds<D, kF32In>;
-  __shared__ __attribute__((aligned(16))) unsigned char k_lds[L::kBytes];
-  __shared__ __attribute__((aligned(16))) unsigned char v_lds[L::vBytes];
-  __shared__ int kd_t[kChunk];
-  __shared__ int kd_r[kChunk];
-  __shared__ int s_flag;
+  __shared__ __attribute__((aligned(16))) unsigned char k_lds[2][L::kBytes];
+  __shared__ __attribute__((aligned(16))) unsigned char v_lds[2][L::vBytes];
+  __shared__ __attribute__((aligned(16))) int kd_t[3][kChunk];
+  __shared__ __attribute__((aligned(16))) int kd_r[3][kChunk];
+  __shared__ int s_flag[3];
   __shared__ int s_min_tau;
 
   const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
   const int hh = lane >> 5, li = lane & 31;
-  const int tile = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int Lb = xcd_logical_block((int)blockIdx.x, (int)gridDim.x);
+  const int tile = Lb % a.ntiles;
+  const int h = (Lb / a.ntiles) % a.Hkv;
+  const int b = Lb / (a.ntiles * a.Hkv);
   const int S = a.S, s = a.s, w = a.w, m = a.m, G = a.G;
   const size_t seg = (size_t)b * a.Hkv + h;
   const int* rank = a.rank + seg * S;
@@ -195,8 +198,8 @@ __global__ __launch_bounds__(kThreads, 2) void masked_fwd_kernel(FwdArgs a) {
   __syncthreads();   // s_min_tau complete
   const int min_tau = s_min_tau;
 
-  for (int c0 = 0; c0 < nk; c0 += kChunk) {
-    // ---- chunk key descriptors (wave 0)
+  // ---- key descriptors (token, rank) of the chunk starting at c0 (wave 0)
+  auto make_desc = [&](int c0, int db) {
     if (tid < kChunk) {
       const int j = c0 + tid;
       int t = -1, r = 0;
@@ -217,44 +220,72 @@ __global__ __launch_bounds__(kThreads, 2) void masked_fwd_kernel(FwdArgs a) {
         r = rank[t];
       }
       if (t >= S) t = -1;
-      kd_t[tid] = t;
-      kd_r[tid] = r;
+      kd_t[db][tid] = t;
+      kd_r[db][tid] = r;
       // kept by every row of the tile?
-      const bool always = t >= 0 && t <= q0 && (t < s || t > q_hi - w || r <= min_tau);
+      const bool always = (t >= 0) & (t <= q0) & ((t < s) | (t > q_hi - w) | (r <= min_tau));
       const uint64_t bal = wave_ballot(!always);
-      if (tid == 0) s_flag = bal != 0;
+      if (tid == 0) s_flag[db] = bal != 0;
     }
-    __syncthreads();
+  };
 
-    // ---- gather K and V rows of the chunk into LDS
+  // ---- gather of one chunk: HBM -> registers -> LDS (V transposed)
+  constexpr int PPR = kF32In ? D / 4 : D / 8;            // 16-byte pieces per row
+  constexpr int KP = kChunk * PPR / kThreads;            // K pieces per thread
+  constexpr int VT = kF32In ? 1 : 8 * (D / 2) / kThreads;  // bf16 V^T tasks per thread
+  uint4 kst[KP];
+  uint4 vst4[kF32In ? KP : 1];
+  uint32_t vst[kF32In ? 1 : 8 * VT];
+  auto load_chunk = [&](int db) {
     if constexpr (!kF32In) {
       const uint16_t* kg = (const uint16_t*)a.k + kvbase;
       const uint16_t* vg = (const uint16_t*)a.v + kvbase;
-      uint16_t* kl = (uint16_t*)k_lds;
-      uint16_t* vl = (uint16_t*)v_lds;
-      constexpr int PPR = D / 8;   // 16-byte pieces per row
 #pragma unroll
-      for (int i = 0; i < kChunk * PPR / kThreads; ++i) {
+      for (int i = 0; i < KP; ++i) {
         const int p = tid + i * kThreads;
-        const int key = p / PPR, piece = p % PPR;
-        const int t = kd_t[key];
-        uint4 val = make_uint4(0, 0, 0, 0);
-        if (t >= 0) val = *(const uint4*)(kg + (size_t)t * D + piece * 8);
-        *(uint4*)(kl + key * L::KS + piece * 8) = val;
+        const int t = kd_t[db][p / PPR];
+        kst[i] = t >= 0 ? *(const uint4*)(kg + (size_t)t * D + (p % PPR) * 8)
+                        : make_uint4(0, 0, 0, 0);
+      }
+#pragma unroll
+      for (int i = 0; i < VT; ++i) {
+        const int task = tid + i * kThreads;
+        const int grp = task / (D / 2), dp = task % (D / 2);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int t = kd_t[db][16 * (grp >> 1) + 8 * (e >> 2) + 4 * (grp & 1) + (e & 3)];
+          vst[8 * i + e] = t >= 0 ? *(const uint32_t*)(vg + (size_t)t * D + 2 * dp) : 0u;
+        }
+      }
+    } else {
+      const float* kg = (const float*)a.k + kvbase;
+      const float* vg = (const float*)a.v + kvbase;
+#pragma unroll
+      for (int i = 0; i < KP; ++i) {
+        const int p = tid + i * kThreads;
+        const int t = kd_t[db][p / PPR];
+        const size_t off = (size_t)t * D + (p % PPR) * 4;
+        kst[i] = t >= 0 ? *(const uint4*)(kg + off) : make_uint4(0, 0, 0, 0);
+        vst4[i] = t >= 0 ? *(const uint4*)(vg + off) : make_uint4(0, 0, 0, 0);
+      }
+    }
+  };
+  auto store_chunk = [&](int kb) {
+    if constexpr (!kF32In) {
+      uint16_t* kl = (uint16_t*)k_lds[kb];
+      uint16_t* vl = (uint16_t*)v_lds[kb];
+#pragma unroll
+      for (int i = 0; i < KP; ++i) {
+        const int p = tid + i * kThreads;
+        *(uint4*)(kl + (p / PPR) * L::KS + (p % PPR) * 8) = kst[i];
       }
       // V^T: column c = 16*ks + 8*hh + e of LDS row d holds key
       // 16*ks + 8*(e>>2) + 4*hh + (e&3) of the chunk (the P operand layout)
 #pragma unroll
-      for (int i = 0; i < 8 * (D / 2) / kThreads; ++i) {
+      for (int i = 0; i < VT; ++i) {
         const int task = tid + i * kThreads;
         const int grp = task / (D / 2), dp = task % (D / 2);
-        uint32_t x[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int jkey = 16 * (grp >> 1) + 8 * (e >> 2) + 4 * (grp & 1) + (e & 3);
-          const int t = kd_t[jkey];
-          x[e] = t >= 0 ? *(const uint32_t*)(vg + (size_t)t * D + 2 * dp) : 0u;
-        }
+        const uint32_t* x = &vst[8 * i];
         uint4 lo, hi;
         lo.x = (x[0] & 0xffffu) | (x[1] << 16);
         lo.y = (x[2] & 0xffffu) | (x[3] << 16);
@@ -268,63 +299,56 @@ __global__ __launch_bounds__(kThreads, 2) void masked_fwd_kernel(FwdArgs a) {
         *(uint4*)(vl + (2 * dp + 1) * L::VS + grp * 8) = hi;
       }
     } else {
-      const float* kg = (const float*)a.k + kvbase;
-      const float* vg = (const float*)a.v + kvbase;
-      float* kl = (float*)k_lds;
-      float* vl = (float*)v_lds;
-      constexpr int PPR = D / 4;
+      float* kl = (float*)k_lds[kb];
+      float* vl = (float*)v_lds[kb];
 #pragma unroll
-      for (int i = 0; i < kChunk * PPR / kThreads; ++i) {
+      for (int i = 0; i < KP; ++i) {
         const int p = tid + i * kThreads;
         const int key = p / PPR, piece = p % PPR;
-        const int t = kd_t[key];
-        float4 kv4 = make_float4(0.f, 0.f, 0.f, 0.f), vv4 = kv4;
-        if (t >= 0) {
-          kv4 = *(const float4*)(kg + (size_t)t * D + piece * 4);
-          vv4 = *(const float4*)(vg + (size_t)t * D + piece * 4);
-        }
         float* kd = kl + key * L::KS + piece * 4;
-        kd[0] = kv4.x; kd[1] = kv4.y; kd[2] = kv4.z; kd[3] = kv4.w;
-        *(float4*)(vl + key * L::VS + piece * 4) = vv4;
+        kd[0] = __uint_as_float(kst[i].x);
+        kd[1] = __uint_as_float(kst[i].y);
+        kd[2] = __uint_as_float(kst[i].z);
+        kd[3] = __uint_as_float(kst[i].w);
+        *(uint4*)(vl + key * L::VS + piece * 4) = vst4[i];
       }
     }
-    __syncthreads();
+  };
 
-    // ---- S^T = K Q^T for the two 32-key blocks
+  // ---- one chunk: S^T = K Q^T, mask, online softmax, O^T += V^T P^T
+  auto compute = [&](int kb, int db) {
     f32x16 sacc[2];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      sacc[kb] = f32x16{};
+    for (int blk = 0; blk < 2; ++blk) {
+      sacc[blk] = f32x16{};
       if constexpr (!kF32In) {
-        const uint16_t* kl = (const uint16_t*)k_lds + (32 * kb + li) * L::KS + 8 * hh;
+        const uint16_t* kl = (const uint16_t*)k_lds[kb] + (32 * blk + li) * L::KS + 8 * hh;
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks)
-          sacc[kb] = mfma32x32x16(as_bf16x8(*(const uint4*)(kl + 16 * ks)), qop[ks], sacc[kb]);
+          sacc[blk] = mfma32x32x16(as_bf16x8(*(const uint4*)(kl + 16 * ks)), qop[ks], sacc[blk]);
       } else {
-        const float* kl = (const float*)k_lds + (32 * kb + li) * L::KS + hh;
+        const float* kl = (const float*)k_lds[kb] + (32 * blk + li) * L::KS + hh;
 #pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) sacc[kb] = mfma32x32x2(kl[2 * ks], qop[ks], sacc[kb]);
+        for (int ks = 0; ks < NKS; ++ks) sacc[blk] = mfma32x32x2(kl[2 * ks], qop[ks], sacc[blk]);
       }
     }
-
-    // ---- mask, online softmax (log2 domain)
     float x[32];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) x[kb * 16 + e] = sacc[kb][e] * a.scale_log2;
-    if (s_flag) {
+      for (int e = 0; e < 16; ++e) x[blk * 16 + e] = sacc[blk][e] * a.scale_log2;
+    if (s_flag[db]) {
       // branch-free: bitwise tests and a select per score (a short-circuit
       // form here was compiled into divergent branches that lost a store)
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
-          const int jj = 32 * kb + 8 * (e >> 2) + 4 * hh + (e & 3);
-          const int t = kd_t[jj], rt = kd_r[jj];
+          const int jj = 32 * blk + 8 * (e >> 2) + 4 * hh + (e & 3);
+          const int t = kd_t[db][jj], rt = kd_r[db][jj];
           const bool keep = row_ok & (t >= 0) & (t <= q) &
                             ((t < s) | (t > q - w) | (rt <= tau_q));
-          x[kb * 16 + e] = keep ? x[kb * 16 + e] : kNegInf;
+          x[blk * 16 + e] = keep ? x[blk * 16 + e] : kNegInf;
         }
     }
     float mc = x[0];
@@ -343,33 +367,51 @@ __global__ __launch_bounds__(kThreads, 2) void masked_fwd_kernel(FwdArgs a) {
     l_run = l_run * alpha + ps;
     m_run = m_new;
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db) oacc[db] *= alpha;
+    for (int d2 = 0; d2 < D / 32; ++d2) oacc[d2] *= alpha;
 
-    // ---- O^T += V^T P^T
     if constexpr (!kF32In) {
       bf16x8 pk[4];
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) pk[ks] = pack_bf16x8(&x[(ks >> 1) * 16 + 8 * (ks & 1)]);
 #pragma unroll
-      for (int db = 0; db < D / 32; ++db) {
-        const uint16_t* vl = (const uint16_t*)v_lds + (32 * db + li) * L::VS + 8 * hh;
+      for (int d2 = 0; d2 < D / 32; ++d2) {
+        const uint16_t* vl = (const uint16_t*)v_lds[kb] + (32 * d2 + li) * L::VS + 8 * hh;
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks)
-          oacc[db] = mfma32x32x16(as_bf16x8(*(const uint4*)(vl + 16 * ks)), pk[ks], oacc[db]);
+          oacc[d2] = mfma32x32x16(as_bf16x8(*(const uint4*)(vl + 16 * ks)), pk[ks], oacc[d2]);
       }
     } else {
 #pragma unroll
-      for (int db = 0; db < D / 32; ++db) {
-        const float* vl = (const float*)v_lds + 32 * db + li;
+      for (int d2 = 0; d2 < D / 32; ++d2) {
+        const float* vl = (const float*)v_lds[kb] + 32 * d2 + li;
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+        for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
           for (int e = 0; e < 16; ++e) {
-            const int key = 32 * kb + 8 * (e >> 2) + 4 * hh + (e & 3);
-            oacc[db] = mfma32x32x2(vl[key * L::VS], x[kb * 16 + e], oacc[db]);
+            const int key = 32 * blk + 8 * (e >> 2) + 4 * hh + (e & 3);
+            oacc[d2] = mfma32x32x2(vl[key * L::VS], x[blk * 16 + e], oacc[d2]);
           }
       }
     }
+  };
+
+  // ---- software pipeline: descriptors two chunks ahead, K/V one chunk ahead
+  const int nchunk = (nk + kChunk - 1) / kChunk;
+  make_desc(0, 0);
+  if (nchunk > 1) make_desc(kChunk, 1);
+  __syncthreads();
+  if (nchunk > 0) {
+    load_chunk(0);
+    store_chunk(0);
+  }
+  __syncthreads();
+  for (int c = 0; c < nchunk; ++c) {
+    const int kb = c & 1, db = c % 3;
+    const bool has_next = c + 1 < nchunk;
+    if (has_next) load_chunk((c + 1) % 3);      // in flight during the math below
+    compute(kb, db);
+    if (has_next) store_chunk(kb ^ 1);
+    if (c + 2 < nchunk) make_desc((c + 2) * kChunk, (c + 2) % 3);
     __syncthreads();
   }
 
@@ -379,12 +421,12 @@ __global__ __launch_bounds__(kThreads, 2) void masked_fwd_kernel(FwdArgs a) {
     const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
     const size_t orow = (((size_t)b * a.Hq + hq) * S + q) * D;
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db)
+    for (int d2 = 0; d2 < D / 32; ++d2)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const int d = 32 * db + 8 * j + 4 * hh;
-        const float o0 = oacc[db][4 * j] * inv, o1 = oacc[db][4 * j + 1] * inv;
-        const float o2 = oacc[db][4 * j + 2] * inv, o3 = oacc[db][4 * j + 3] * inv;
+        const int d = 32 * d2 + 8 * j + 4 * hh;
+        const float o0 = oacc[d2][4 * j] * inv, o1 = oacc[d2][4 * j + 1] * inv;
+        const float o2 = oacc[d2][4 * j + 2] * inv, o3 = oacc[d2][4 * j + 3] * inv;
         if constexpr (kF32Out) {
           *(float4*)((float*)a.o + orow + d) = make_float4(o0, o1, o2, o3);
         } else {
@@ -399,8 +441,9 @@ __global__ __launch_bounds__(kThreads, 2) void masked_fwd_kernel(FwdArgs a) {
 
 template <int D, bool kF32In, bool kF32Out>
 void launch_fwd_kernel(const FwdArgs& a, int b, hipStream_t st) {
-  hipLaunchKernelGGL((masked_fwd_kernel<D, kF32In, kF32Out>), dim3(a.ntiles, a.Hkv, b),
-                     dim3(kThreads), 0, st, a);
+  const long long n = (long long)a.ntiles * a.Hkv * b;
+  hipLaunchKernelGGL((masked_fwd_kernel<D, kF32In, kF32Out>), dim3((unsigned)n), dim3(kThreads), 0,
+                     st, a);
 }
 
 }  // namespace
