@@ -3,7 +3,7 @@
 // validates all arguments before its first launch.
 #include <math.h>
 
-#include "../../include/kvpop.h"
+#include "kvpop.h"
 #include "kvpop_internal.h"
 
 #define KVPOP_EXPORT extern "C" __attribute__((visibility("default")))

@@ -155,7 +155,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_attend_kernel(DecArgs a) {
   using L = DecLds<D, kF32>;
   static_assert(kWaves * L::waveBytes >= kWaves * 32 * (D + 2) * 4, "merge area");
   __shared__ __attribute__((aligned(16))) unsigned char lds[kWaves * L::waveBytes];
-  const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
+  const int tid = threadIdx.x, lane = lane_id(), wave = wave_id();
   const int hh = lane >> 5, li = lane & 31;
   const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int Bc = a.Bc, G = a.G;

@@ -64,7 +64,7 @@ __global__ __launch_bounds__(kThreads, 2) void future_target_kernel(TgtArgs a) {
   __shared__ __attribute__((aligned(16))) unsigned char q_lds[2][Gm::bufBytes];
   __shared__ __attribute__((aligned(16))) float nlse[2][kChunk];   // -LSE_d * log2(e)
 
-  const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
+  const int tid = threadIdx.x, lane = lane_id(), wave = wave_id();
   const int hh = lane >> 5, li = lane & 31;
   const int L = xcd_logical_block((int)blockIdx.x, (int)gridDim.x);
   const int tile = L % a.ntiles;
@@ -113,16 +113,17 @@ __global__ __launch_bounds__(kThreads, 2) void future_target_kernel(TgtArgs a) {
   const float* lse = a.lse + ((size_t)b * a.Hq + hq) * S;
 
   // staging of one chunk: global -> registers, registers -> LDS buffer
-  uint4 stage[Gm::NPIECE];
+  typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
+  u32x4v stage[Gm::NPIECE];
   float stage_lse = 0.0f;
   auto load_chunk = [&](int d0) {
 #pragma unroll
     for (int i = 0; i < Gm::NPIECE; ++i) {
       const int p = tid + i * kThreads;
       const int row = p / Gm::PPR, piece = p % Gm::PPR;
-      const int d = d0 + row;
-      stage[i] = make_uint4(0, 0, 0, 0);
-      if (d < S) stage[i] = *(const uint4*)(qg + (size_t)d * D * Gm::esz + piece * 16);
+      // rows past the end repeat the last row: their -LSE is -inf, so they add 0
+      const int d = min(d0 + row, S - 1);
+      stage[i] = *(const u32x4v*)(qg + (size_t)d * D * Gm::esz + piece * 16);
     }
     if (tid < kChunk) {
       const int d = d0 + tid;
@@ -136,12 +137,12 @@ __global__ __launch_bounds__(kThreads, 2) void future_target_kernel(TgtArgs a) {
       const int row = p / Gm::PPR, piece = p % Gm::PPR;
       if constexpr (kF32In) {
         float* dst = (float*)q_lds[buf] + row * Gm::QS + piece * 4;
-        dst[0] = __uint_as_float(stage[i].x);
-        dst[1] = __uint_as_float(stage[i].y);
-        dst[2] = __uint_as_float(stage[i].z);
-        dst[3] = __uint_as_float(stage[i].w);
+        dst[0] = __uint_as_float(stage[i][0]);
+        dst[1] = __uint_as_float(stage[i][1]);
+        dst[2] = __uint_as_float(stage[i][2]);
+        dst[3] = __uint_as_float(stage[i][3]);
       } else {
-        *(uint4*)((uint16_t*)q_lds[buf] + row * Gm::QS + piece * 8) = stage[i];
+        *(u32x4v*)((uint16_t*)q_lds[buf] + row * Gm::QS + piece * 8) = stage[i];
       }
     }
     if (tid < kChunk) nlse[buf][tid] = stage_lse;
@@ -159,49 +160,63 @@ __global__ __launch_bounds__(kThreads, 2) void future_target_kernel(TgtArgs a) {
     const bool has_next = c + 1 < nchunks;
     if (has_next) load_chunk(d0 + kChunk);
 
-    // this wave's rows need d >= t + w: skip chunks wholly below
+    // this wave's rows need d >= t + w: skip chunks wholly below; the d >= t + w
+    // test is compiled only into the variant run on chunks straddling the band
     if (d0 + kChunk - 1 >= rbase + w) {
-      const bool need_mask = d0 < rbase + kWaveRows - 1 + w || d0 + kChunk - 1 > S - 1;
+      auto chunk_math = [&](auto masked) {
+        // four independent accumulator chains: (column block cb) x (row block rb)
+        f32x16 acc[2][2];
 #pragma unroll
-      for (int cb = 0; cb < 2; ++cb) {
-        f32x16 acc0 = f32x16{}, acc1 = f32x16{};
+        for (int cb = 0; cb < 2; ++cb) acc[cb][0] = acc[cb][1] = f32x16{};
         if constexpr (!kF32In) {
-          const uint16_t* ql = (const uint16_t*)q_lds[buf] + (32 * cb + li) * Gm::QS + 8 * hh;
+          const uint16_t* ql = (const uint16_t*)q_lds[buf] + li * Gm::QS + 8 * hh;
 #pragma unroll
           for (int ks = 0; ks < Gm::NKS; ++ks) {
-            const bf16x8 av = as_bf16x8(*(const uint4*)(ql + 16 * ks));
-            acc0 = mfma32x32x16(av, kop[0][ks], acc0);
-            acc1 = mfma32x32x16(av, kop[1][ks], acc1);
+#pragma unroll
+            for (int cb = 0; cb < 2; ++cb) {
+              const bf16x8 av = as_bf16x8(*(const uint4*)(ql + 32 * cb * Gm::QS + 16 * ks));
+              acc[cb][0] = mfma32x32x16(av, kop[0][ks], acc[cb][0]);
+              acc[cb][1] = mfma32x32x16(av, kop[1][ks], acc[cb][1]);
+            }
           }
         } else {
-          const float* ql = (const float*)q_lds[buf] + (32 * cb + li) * Gm::QS + hh;
+          const float* ql = (const float*)q_lds[buf] + li * Gm::QS + hh;
 #pragma unroll
           for (int ks = 0; ks < Gm::NKS; ++ks) {
-            const float av = ql[2 * ks];
-            acc0 = mfma32x32x2(av, kop[0][ks], acc0);
-            acc1 = mfma32x32x2(av, kop[1][ks], acc1);
+#pragma unroll
+            for (int cb = 0; cb < 2; ++cb) {
+              const float av = ql[32 * cb * Gm::QS + 2 * ks];
+              acc[cb][0] = mfma32x32x2(av, kop[0][ks], acc[cb][0]);
+              acc[cb][1] = mfma32x32x2(av, kop[1][ks], acc[cb][1]);
+            }
           }
         }
         // lane holds columns d = d0 + 32cb + 8j + 4hh + r of rows rbase + 32rb + li
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int dl = 32 * cb + 8 * j + 4 * hh;
-          const f32x4 bias = *(const f32x4*)(&nlse[buf][dl]);
+        for (int cb = 0; cb < 2; ++cb)
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            float p0 = exp2_fast(fmaf(acc0[4 * j + r], a.scale_log2, bias[r]));
-            float p1 = exp2_fast(fmaf(acc1[4 * j + r], a.scale_log2, bias[r]));
-            if (need_mask) {     // wave-uniform; the tests are selects
-              const int d = d0 + dl + r;
-              const int t_0 = rbase + li;
-              p0 = ((d >= t_0 + w) & (d < S)) ? p0 : 0.0f;
-              p1 = ((d >= t_0 + 32 + w) & (d < S)) ? p1 : 0.0f;
+          for (int j = 0; j < 4; ++j) {
+            const int dl = 32 * cb + 8 * j + 4 * hh;
+            const f32x4 bias = *(const f32x4*)(&nlse[buf][dl]);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              float p0 = exp2_fast(fmaf(acc[cb][0][4 * j + r], a.scale_log2, bias[r]));
+              float p1 = exp2_fast(fmaf(acc[cb][1][4 * j + r], a.scale_log2, bias[r]));
+              if constexpr (decltype(masked)::value) {   // selects, no branches
+                const int d = d0 + dl + r;
+                const int t_0 = rbase + li;
+                p0 = ((d >= t_0 + w) & (d < S)) ? p0 : 0.0f;
+                p1 = ((d >= t_0 + 32 + w) & (d < S)) ? p1 : 0.0f;
+              }
+              sum[0] += p0;
+              sum[1] += p1;
             }
-            sum[0] += p0;
-            sum[1] += p1;
           }
-        }
-      }
+      };
+      if (d0 < rbase + kWaveRows - 1 + w || d0 + kChunk - 1 > S - 1)
+        chunk_math(std::true_type{});
+      else
+        chunk_math(std::false_type{});
     }
     if (has_next) store_chunk(buf ^ 1);
     __syncthreads();

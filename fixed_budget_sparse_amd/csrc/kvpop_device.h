@@ -19,6 +19,13 @@ constexpr float kNegInf = -__builtin_huge_valf();
 // ---------------------------------------------------------------- lanes
 __device__ __forceinline__ int lane_id() { return (int)(threadIdx.x & 63); }
 
+// Wave index within the workgroup, in a scalar register: values derived from
+// it are provably wave-uniform, so branches on them stay scalar branches
+// instead of per-lane exec masking.
+__device__ __forceinline__ int wave_id() {
+  return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+}
+
 // Number of set bits of `m` in lanes below this one.
 __device__ __forceinline__ int lanes_below(uint64_t m) {
   return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),

@@ -68,7 +68,7 @@ __global__ __launch_bounds__(256) void tile_list_kernel(const int* __restrict__ 
                                                         int* __restrict__ count) {
   __shared__ int wsum[4];
   const int tile = blockIdx.x, seg = blockIdx.y;
-  const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
+  const int tid = threadIdx.x, lane = lane_id(), wave = wave_id();
   const int q0 = tile * m;
   const int e_hi = q0 - w;
   const int tq0 = tau[(size_t)seg * S + q0];
@@ -124,7 +124,7 @@ __global__ __launch_bounds__(kThreads, 2) void masked_fwd_kernel(FwdArgs a) {
   __shared__ int s_flag[3];
   __shared__ int s_min_tau;
 
-  const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
+  const int tid = threadIdx.x, lane = lane_id(), wave = wave_id();
   const int hh = lane >> 5, li = lane & 31;
   const int Lb = xcd_logical_block((int)blockIdx.x, (int)gridDim.x);
   const int tile = Lb % a.ntiles;
@@ -332,12 +332,12 @@ __global__ __launch_bounds__(kThreads, 2) void masked_fwd_kernel(FwdArgs a) {
         for (int ks = 0; ks < NKS; ++ks) sacc[blk] = mfma32x32x2(kl[2 * ks], qop[ks], sacc[blk]);
       }
     }
-    float x[32];
+    float x[32];   // raw logits <q, k>
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) x[blk * 16 + e] = sacc[blk][e] * a.scale_log2;
-    if (s_flag[db]) {
+      for (int e = 0; e < 16; ++e) x[blk * 16 + e] = sacc[blk][e];
+    if (__builtin_amdgcn_readfirstlane(s_flag[db])) {   // uniform: a scalar branch
       // branch-free: bitwise tests and a select per score (a short-circuit
       // form here was compiled into divergent branches that lost a store)
 #pragma unroll
@@ -355,19 +355,26 @@ __global__ __launch_bounds__(kThreads, 2) void masked_fwd_kernel(FwdArgs a) {
 #pragma unroll
     for (int e = 1; e < 32; ++e) mc = fmaxf(mc, x[e]);
     mc = fmaxf(mc, __shfl_xor(mc, 32));
-    const float m_new = fmaxf(m_run, mc);
-    const float m_use = m_new == kNegInf ? 0.0f : m_new;
-    const float alpha = exp2_fast(m_run - m_use);
+    // online softmax with a lazily moved reference max (m_run, raw units): it
+    // moves only when some row's max grows by more than 2^8 in the exp2
+    // domain, so the O rescale is skipped on most chunks; scores stay <= 2^8
+    const float c = a.scale_log2;
+    if (wave_ballot(mc * c > m_run * c + 8.0f) != 0) {
+      const float m_new = fmaxf(m_run, mc);
+      const float alpha = m_new == kNegInf ? 1.0f : exp2_fast((m_run - m_new) * c);
+      l_run *= alpha;
+      m_run = m_new;
+#pragma unroll
+      for (int d2 = 0; d2 < D / 32; ++d2) oacc[d2] *= alpha;
+    }
+    const float mb = m_run == kNegInf ? 0.0f : -m_run * c;
     float ps = 0.0f;
 #pragma unroll
     for (int e = 0; e < 32; ++e) {
-      x[e] = exp2_fast(x[e] - m_use);
+      x[e] = exp2_fast(fmaf(x[e], c, mb));
       ps += x[e];
     }
-    l_run = l_run * alpha + ps;
-    m_run = m_new;
-#pragma unroll
-    for (int d2 = 0; d2 < D / 32; ++d2) oacc[d2] *= alpha;
+    l_run += ps;
 
     if constexpr (!kF32In) {
       bf16x8 pk[4];
@@ -435,7 +442,7 @@ __global__ __launch_bounds__(kThreads, 2) void masked_fwd_kernel(FwdArgs a) {
       }
     if (hh == 0)
       a.lse[((size_t)b * a.Hq + hq) * S + q] =
-          l_tot > 0.0f ? (m_run + log2f(l_tot)) * kLn2 : kNegInf;
+          l_tot > 0.0f ? (m_run * a.scale_log2 + log2f(l_tot)) * kLn2 : kNegInf;
   }
 }
 

@@ -202,7 +202,7 @@ __global__ __launch_bounds__(256) void tau_kernel(const int* __restrict__ rank,
   uint32_t* bitmap = smem;
   int* newr = (int*)(smem + nwords);        // rank of the newcomer of each chunk row
   int* taus = newr + chunk;
-  const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
+  const int tid = threadIdx.x, lane = lane_id(), wave = wave_id();
   const int seg = blockIdx.y;
   const int q0 = blockIdx.x * chunk;
   const int nq = min(chunk, S - q0);
