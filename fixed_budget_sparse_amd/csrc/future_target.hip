@@ -35,7 +35,8 @@ namespace kvpop {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kWaveRows = 64;                    // two 32-row MFMA blocks per wave
+constexpr int kRB = 2;                           // 32-row MFMA blocks per wave
+constexpr int kWaveRows = 32 * kRB;
 constexpr int kRowsPerTile = 4 * kWaveRows;
 constexpr int kChunk = 64;
 
@@ -79,7 +80,7 @@ __global__ __launch_bounds__(kThreads, 2) void future_target_kernel(TgtArgs a) {
   const int d_start = t0 + w;                      // first query any row of the tile needs
   if (d_start > S - 1) {
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb) {
+    for (int rb = 0; rb < kRB; ++rb) {
       const int t = rbase + 32 * rb + li;
       if (hh == 0 && t < S) out[t] = kNegInf;
     }
@@ -88,9 +89,9 @@ __global__ __launch_bounds__(kThreads, 2) void future_target_kernel(TgtArgs a) {
 
   // key operands (B of X^T = Q K^T): rows rbase + 32 rb + li, dims [16ks + 8hh, +8)
   typedef typename std::conditional<kF32In, float, bf16x8>::type KOp;
-  KOp kop[2][Gm::NKS];
+  KOp kop[kRB][Gm::NKS];
 #pragma unroll
-  for (int rb = 0; rb < 2; ++rb) {
+  for (int rb = 0; rb < kRB; ++rb) {
     const int t = rbase + 32 * rb + li;
     const bool ok = t < S;
     const size_t krow = (((size_t)b * a.Hkv + h) * S + (ok ? t : 0)) * D;
@@ -148,82 +149,173 @@ __global__ __launch_bounds__(kThreads, 2) void future_target_kernel(TgtArgs a) {
     if (tid < kChunk) nlse[buf][tid] = stage_lse;
   };
 
-  float sum[2] = {0.0f, 0.0f};
+  float sum[kRB];
+#pragma unroll
+  for (int rb = 0; rb < kRB; ++rb) sum[rb] = 0.0f;
   const int nchunks = (S - d_start + kChunk - 1) / kChunk;
   load_chunk(d_start);
   store_chunk(0);
   __syncthreads();
 
+  // One 32-column block of MFMAs: acc[rb] = Q_block K_rb^T.
+  auto mfma_block = [&](f32x16 (&acc)[kRB], int buf, int cb) {
+#pragma unroll
+    for (int rb = 0; rb < kRB; ++rb) acc[rb] = f32x16{};
+    if constexpr (!kF32In) {
+      const uint16_t* ql = (const uint16_t*)q_lds[buf] + (32 * cb + li) * Gm::QS + 8 * hh;
+#pragma unroll
+      for (int ks = 0; ks < Gm::NKS; ++ks) {
+        const bf16x8 av = as_bf16x8(*(const uint4*)(ql + 16 * ks));
+#pragma unroll
+        for (int rb = 0; rb < kRB; ++rb) acc[rb] = mfma32x32x16(av, kop[rb][ks], acc[rb]);
+      }
+    } else {
+      const float* ql = (const float*)q_lds[buf] + (32 * cb + li) * Gm::QS + hh;
+#pragma unroll
+      for (int ks = 0; ks < Gm::NKS; ++ks) {
+        const float av = ql[2 * ks];
+#pragma unroll
+        for (int rb = 0; rb < kRB; ++rb) acc[rb] = mfma32x32x2(av, kop[rb][ks], acc[rb]);
+      }
+    }
+  };
+  // exp2 and row sums of one block: the lane holds columns
+  // d = d0 + 32cb + 8j + 4hh + r of rows rbase + 32rb + li
+  auto exp_block = [&](const f32x16 (&acc)[kRB], int buf, int cb, int d0, auto masked) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int dl = 32 * cb + 8 * j + 4 * hh;
+      const f32x4 bias = *(const f32x4*)(&nlse[buf][dl]);
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int rb = 0; rb < kRB; ++rb) {
+          float p = exp2_fast(fmaf(acc[rb][4 * j + r], a.scale_log2, bias[r]));
+          if constexpr (decltype(masked)::value) {   // selects, no branches
+            const int d = d0 + dl + r;
+            p = ((d >= rbase + 32 * rb + li + w) & (d < S)) ? p : 0.0f;
+          }
+          sum[rb] += p;
+        }
+    }
+  };
+  // The MFMAs of one block interleaved with the exp work of another
+  // (independent) block, in a fixed order so the matrix and vector units run
+  // together: all operand reads first, then 8 groups of two MFMAs and four
+  // scores (fma, exp2, add) each, pinned with scheduling barriers.
+  auto fused = [&](auto doM, auto doE, auto maskE, f32x16 (&accM)[kRB], int mbuf, int mcb,
+                   const f32x16 (&accE)[kRB], int ebuf, int ecb, int d0E) {
+    constexpr bool kM = decltype(doM)::value, kE = decltype(doE)::value;
+    constexpr bool kMask = decltype(maskE)::value;
+    constexpr int NK = Gm::NKS;              // 8 (D = 128, bf16)
+    constexpr int kPer = 32 / NK;            // scores per group: 4, all with one bias vector
+    const uint16_t* ql = (const uint16_t*)q_lds[mbuf] + (32 * mcb + li) * Gm::QS + 8 * hh;
+    const float* nb = &nlse[ebuf][32 * ecb + 4 * hh];
+    // operands two k-steps ahead, bias one group ahead
+    bf16x8 a0{}, a1{};
+    f32x4 b0{};
+    if constexpr (kM) {
+      a0 = as_bf16x8(*(const uint4*)(ql));
+      a1 = as_bf16x8(*(const uint4*)(ql + 16));
+      accM[0] = accM[1] = f32x16{};
+    }
+    if constexpr (kE) b0 = *(const f32x4*)(nb);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int ks = 0; ks < NK; ++ks) {
+      bf16x8 a2 = a1;
+      if constexpr (kM)
+        if (ks + 2 < NK) a2 = as_bf16x8(*(const uint4*)(ql + 16 * (ks + 2)));
+      f32x4 b1 = b0;
+      if constexpr (kE)
+        if (ks + 1 < NK) b1 = *(const f32x4*)(nb + 8 * ((((ks + 1) * kPer) & 15) >> 2));
+      if constexpr (kM) {
+        accM[0] = mfma32x32x16(a0, kop[0][ks], accM[0]);
+        accM[1] = mfma32x32x16(a0, kop[1][ks], accM[1]);
+      }
+      if constexpr (kE) {
+#pragma unroll
+        for (int i = 0; i < kPer; ++i) {
+          const int idx = kPer * ks + i, rb = idx >> 4, e = idx & 15;
+          float p = exp2_fast(fmaf(accE[rb][e], a.scale_log2, b0[e & 3]));
+          if constexpr (kMask) {   // a select, no branch
+            const int d = d0E + 32 * ecb + 8 * (e >> 2) + 4 * hh + (e & 3);
+            p = ((d >= rbase + 32 * rb + li + w) & (d < S)) ? p : 0.0f;
+          }
+          sum[rb] += p;
+        }
+      }
+      a0 = a1;
+      a1 = a2;
+      b0 = b1;
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  using T_ = std::true_type;
+  using F_ = std::false_type;
+
+  // Software pipeline over chunks: while the MFMAs of column block 0 of chunk
+  // c run, the exps of block 1 of chunk c-1 are computed; while the MFMAs of
+  // block 1 of chunk c run, the exps of block 0 of chunk c are computed.
+  f32x16 accA[kRB], accB[kRB];
+  bool pend = false, pend_mask = false;   // block 1 of the previous chunk awaits its exps
+  int pend_d0 = 0, pend_buf = 0;
   for (int c = 0; c < nchunks; ++c) {
     const int d0 = d_start + c * kChunk;
     const int buf = c & 1;
     const bool has_next = c + 1 < nchunks;
     if (has_next) load_chunk(d0 + kChunk);
-
-    // this wave's rows need d >= t + w: skip chunks wholly below; the d >= t + w
-    // test is compiled only into the variant run on chunks straddling the band
-    if (d0 + kChunk - 1 >= rbase + w) {
-      auto chunk_math = [&](auto masked) {
-        // four independent accumulator chains: (column block cb) x (row block rb)
-        f32x16 acc[2][2];
-#pragma unroll
-        for (int cb = 0; cb < 2; ++cb) acc[cb][0] = acc[cb][1] = f32x16{};
-        if constexpr (!kF32In) {
-          const uint16_t* ql = (const uint16_t*)q_lds[buf] + li * Gm::QS + 8 * hh;
-#pragma unroll
-          for (int ks = 0; ks < Gm::NKS; ++ks) {
-#pragma unroll
-            for (int cb = 0; cb < 2; ++cb) {
-              const bf16x8 av = as_bf16x8(*(const uint4*)(ql + 32 * cb * Gm::QS + 16 * ks));
-              acc[cb][0] = mfma32x32x16(av, kop[0][ks], acc[cb][0]);
-              acc[cb][1] = mfma32x32x16(av, kop[1][ks], acc[cb][1]);
-            }
-          }
-        } else {
-          const float* ql = (const float*)q_lds[buf] + li * Gm::QS + hh;
-#pragma unroll
-          for (int ks = 0; ks < Gm::NKS; ++ks) {
-#pragma unroll
-            for (int cb = 0; cb < 2; ++cb) {
-              const float av = ql[32 * cb * Gm::QS + 2 * ks];
-              acc[cb][0] = mfma32x32x2(av, kop[0][ks], acc[cb][0]);
-              acc[cb][1] = mfma32x32x2(av, kop[1][ks], acc[cb][1]);
-            }
-          }
-        }
-        // lane holds columns d = d0 + 32cb + 8j + 4hh + r of rows rbase + 32rb + li
-#pragma unroll
-        for (int cb = 0; cb < 2; ++cb)
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const int dl = 32 * cb + 8 * j + 4 * hh;
-            const f32x4 bias = *(const f32x4*)(&nlse[buf][dl]);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              float p0 = exp2_fast(fmaf(acc[cb][0][4 * j + r], a.scale_log2, bias[r]));
-              float p1 = exp2_fast(fmaf(acc[cb][1][4 * j + r], a.scale_log2, bias[r]));
-              if constexpr (decltype(masked)::value) {   // selects, no branches
-                const int d = d0 + dl + r;
-                const int t_0 = rbase + li;
-                p0 = ((d >= t_0 + w) & (d < S)) ? p0 : 0.0f;
-                p1 = ((d >= t_0 + 32 + w) & (d < S)) ? p1 : 0.0f;
-              }
-              sum[0] += p0;
-              sum[1] += p1;
-            }
-          }
-      };
-      if (d0 < rbase + kWaveRows - 1 + w || d0 + kChunk - 1 > S - 1)
-        chunk_math(std::true_type{});
-      else
-        chunk_math(std::false_type{});
+    // this wave's rows need d >= t + w: chunks wholly below are skipped; the
+    // d >= t + w test is compiled only into the straddling-chunk variant
+    const bool active = d0 + kChunk - 1 >= rbase + w;
+    const bool msk = d0 < rbase + kWaveRows - 1 + w || d0 + kChunk - 1 > S - 1;
+    if constexpr (!kF32In && kRB == 2 && D == 128) {
+      // block 0 of chunk c (MFMA) with block 1 of chunk c-1 (exp), then
+      // block 1 of chunk c (MFMA) with block 0 of chunk c (exp)
+      if (active && pend) {
+        if (pend_mask) fused(T_{}, T_{}, T_{}, accA, buf, 0, accB, pend_buf, 1, pend_d0);
+        else fused(T_{}, T_{}, F_{}, accA, buf, 0, accB, pend_buf, 1, pend_d0);
+      } else if (active) {
+        fused(T_{}, F_{}, F_{}, accA, buf, 0, accB, pend_buf, 1, pend_d0);
+      } else if (pend) {
+        if (pend_mask) fused(F_{}, T_{}, T_{}, accA, buf, 0, accB, pend_buf, 1, pend_d0);
+        else fused(F_{}, T_{}, F_{}, accA, buf, 0, accB, pend_buf, 1, pend_d0);
+      }
+      if (active) {
+        if (msk) fused(T_{}, T_{}, T_{}, accB, buf, 1, accA, buf, 0, d0);
+        else fused(T_{}, T_{}, F_{}, accB, buf, 1, accA, buf, 0, d0);
+      }
+    } else {
+      if (active) mfma_block(accA, buf, 0);
+      if (pend) {
+        if (pend_mask) exp_block(accB, pend_buf, 1, pend_d0, std::true_type{});
+        else exp_block(accB, pend_buf, 1, pend_d0, std::false_type{});
+      }
+      if (active) {
+        mfma_block(accB, buf, 1);
+        if (msk) exp_block(accA, buf, 0, d0, std::true_type{});
+        else exp_block(accA, buf, 0, d0, std::false_type{});
+      }
     }
+    pend = active;
+    pend_mask = msk;
+    pend_d0 = d0;
+    pend_buf = buf;
     if (has_next) store_chunk(buf ^ 1);
     __syncthreads();
   }
+  if (pend) {
+    if constexpr (!kF32In && kRB == 2 && D == 128) {
+      if (pend_mask) fused(F_{}, T_{}, T_{}, accA, 0, 0, accB, pend_buf, 1, pend_d0);
+      else fused(F_{}, T_{}, F_{}, accA, 0, 0, accB, pend_buf, 1, pend_d0);
+    } else {
+      if (pend_mask) exp_block(accB, pend_buf, 1, pend_d0, std::true_type{});
+      else exp_block(accB, pend_buf, 1, pend_d0, std::false_type{});
+    }
+  }
 
 #pragma unroll
-  for (int rb = 0; rb < 2; ++rb) {
+  for (int rb = 0; rb < kRB; ++rb) {
     const float tot = sum[rb] + __shfl_xor(sum[rb], 32);
     const int t = rbase + 32 * rb + li;
     if (hh == 0 && t < S) out[t] = tot > 0.0f ? log2f(tot) * kLn2 : kNegInf;

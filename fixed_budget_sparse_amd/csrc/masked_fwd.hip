@@ -4,9 +4,9 @@
 // set; gist.science summary §2.2: the operator returns the log-sum-exp).
 //
 // Design (gfx950):
-//  * A workgroup owns one query tile of one KV head: m = 128 / G query rows of
-//    each of the G query heads that share the KV head, stacked into 128 MFMA
-//    rows (4 waves x 32).  The G heads share priorities, hence the mask and
+//  * A workgroup owns one query tile of one KV head: m = 256 / G query rows of
+//    each of the G query heads that share the KV head, stacked into 256 MFMA
+//    rows (8 waves x 32).  The G heads share priorities, hence the mask and
 //    the key list, so one gathered key set feeds all of them.
 //  * The tile's candidate keys are the sinks, the long-range keys of its first
 //    row q0 ({t in E(q0) : rank(t) <= tau_q0}, exactly k keys, listed in rank
@@ -29,8 +29,8 @@
 namespace kvpop {
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kRowsPerTile = 128;   // stacked query rows per workgroup
+constexpr int kThreads = 512;       // 8 waves
+constexpr int kRowsPerTile = 256;   // stacked query rows per workgroup (8 waves x 32)
 constexpr int kChunk = 64;          // keys per chunk
 
 struct FwdArgs {
@@ -115,7 +115,7 @@ struct FwdLds {
 };
 
 template <int D, bool kF32In, bool kF32Out>
-__global__ __launch_bounds__(kThreads, 2) void masked_fwd_kernel(FwdArgs a) {
+__global__ __launch_bounds__(kThreads, 1) void masked_fwd_kernel(FwdArgs a) {
   using L = FwdLds<D, kF32In>;
   __shared__ __attribute__((aligned(16))) unsigned char k_lds[2][L::kBytes];
   __shared__ __attribute__((aligned(16))) unsigned char v_lds[2][L::vBytes];
@@ -232,10 +232,13 @@ __global__ __launch_bounds__(kThreads, 2) void masked_fwd_kernel(FwdArgs a) {
   // ---- gather of one chunk: HBM -> registers -> LDS (V transposed)
   constexpr int PPR = kF32In ? D / 4 : D / 8;            // 16-byte pieces per row
   constexpr int KP = kChunk * PPR / kThreads;            // K pieces per thread
-  constexpr int VT = kF32In ? 1 : 8 * (D / 2) / kThreads;  // bf16 V^T tasks per thread
+  // bf16 V^T tasks: (key pair, 8-dim octet); two 16-byte row loads each
+  constexpr int NVT = 32 * (D / 8);
+  constexpr int VT = kF32In ? 1 : (NVT + kThreads - 1) / kThreads;  // per thread
+  typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
   uint4 kst[KP];
   uint4 vst4[kF32In ? KP : 1];
-  uint32_t vst[kF32In ? 1 : 8 * VT];
+  u32x4v vpair[kF32In ? 1 : 2 * VT];
   auto load_chunk = [&](int db) {
     if constexpr (!kF32In) {
       const uint16_t* kg = (const uint16_t*)a.k + kvbase;
@@ -250,12 +253,12 @@ __global__ __launch_bounds__(kThreads, 2) void masked_fwd_kernel(FwdArgs a) {
 #pragma unroll
       for (int i = 0; i < VT; ++i) {
         const int task = tid + i * kThreads;
-        const int grp = task / (D / 2), dp = task % (D / 2);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int t = kd_t[db][16 * (grp >> 1) + 8 * (e >> 2) + 4 * (grp & 1) + (e & 3)];
-          vst[8 * i + e] = t >= 0 ? *(const uint32_t*)(vg + (size_t)t * D + 2 * dp) : 0u;
-        }
+        if (NVT % kThreads != 0 && task >= NVT) break;
+        const int pr = task & 31, oc = task >> 5;   // pairs fastest: distinct LDS banks
+        const int t0 = kd_t[db][2 * pr], t1 = kd_t[db][2 * pr + 1];
+        const u32x4v z = {0u, 0u, 0u, 0u};
+        vpair[2 * i] = t0 >= 0 ? *(const u32x4v*)(vg + (size_t)t0 * D + 8 * oc) : z;
+        vpair[2 * i + 1] = t1 >= 0 ? *(const u32x4v*)(vg + (size_t)t1 * D + 8 * oc) : z;
       }
     } else {
       const float* kg = (const float*)a.k + kvbase;
@@ -279,24 +282,23 @@ __global__ __launch_bounds__(kThreads, 2) void masked_fwd_kernel(FwdArgs a) {
         const int p = tid + i * kThreads;
         *(uint4*)(kl + (p / PPR) * L::KS + (p % PPR) * 8) = kst[i];
       }
-      // V^T: column c = 16*ks + 8*hh + e of LDS row d holds key
-      // 16*ks + 8*(e>>2) + 4*hh + (e&3) of the chunk (the P operand layout)
+      // V^T: column c = 16*ks + 8*hh + 4*a + r of LDS row d holds key
+      // 16*ks + 8*a + 4*hh + r of the chunk (the P operand layout); a key pair
+      // (2pr, 2pr+1) lands in two adjacent columns, so each dim is one word
 #pragma unroll
       for (int i = 0; i < VT; ++i) {
         const int task = tid + i * kThreads;
-        const int grp = task / (D / 2), dp = task % (D / 2);
-        const uint32_t* x = &vst[8 * i];
-        uint4 lo, hi;
-        lo.x = (x[0] & 0xffffu) | (x[1] << 16);
-        lo.y = (x[2] & 0xffffu) | (x[3] << 16);
-        lo.z = (x[4] & 0xffffu) | (x[5] << 16);
-        lo.w = (x[6] & 0xffffu) | (x[7] << 16);
-        hi.x = (x[0] >> 16) | (x[1] & 0xffff0000u);
-        hi.y = (x[2] >> 16) | (x[3] & 0xffff0000u);
-        hi.z = (x[4] >> 16) | (x[5] & 0xffff0000u);
-        hi.w = (x[6] >> 16) | (x[7] & 0xffff0000u);
-        *(uint4*)(vl + (2 * dp) * L::VS + grp * 8) = lo;
-        *(uint4*)(vl + (2 * dp + 1) * L::VS + grp * 8) = hi;
+        if (NVT % kThreads != 0 && task >= NVT) break;
+        const int pr = task & 31, oc = task >> 5;   // pairs fastest: distinct LDS banks
+        const int j0 = 2 * pr;
+        const int c0 = 16 * (j0 >> 4) + 8 * ((j0 >> 2) & 1) + 4 * ((j0 >> 3) & 1) + (j0 & 3);
+        const u32x4v x0 = vpair[2 * i], x1 = vpair[2 * i + 1];
+        uint16_t* col = vl + (8 * oc) * L::VS + c0;
+#pragma unroll
+        for (int dp = 0; dp < 4; ++dp) {
+          *(uint32_t*)(col + (2 * dp) * L::VS) = (x0[dp] & 0xffffu) | (x1[dp] << 16);
+          *(uint32_t*)(col + (2 * dp + 1) * L::VS) = (x0[dp] >> 16) | (x1[dp] & 0xffff0000u);
+        }
       }
     } else {
       float* kl = (float*)k_lds[kb];
