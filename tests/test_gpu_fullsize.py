@@ -1,0 +1,220 @@
+"""GPU parity at the full workload sizes, in the launch configurations the
+benchmark times: the Qwen3-4B-shaped layer (S = 16384, B = 2048), the
+Qwen3-8B-shaped layer (S = 32768, B = 4096), the long-context layer
+(S = 131072, B = 4096), the 64-sequence decode at B = 2048 and the 8-sequence
+decode over 131072 steps.
+
+The oracle cannot evaluate these sizes whole, so outputs are compared where it
+can compute them one by one: every rank, the cutoffs of every row (or of a
+sample of rows plus all boundary rows at S = 131072), the forward on sampled
+query rows of every head, the future target on every token of one head (on
+sampled tokens at S = 32768) with the teacher LSE computed by the oracle, and
+decode cache membership of every (sequence, KV head) plus outputs of a few
+sequences at sampled steps.  Inputs are drawn on the device by the seeded
+generators of ``workloads``; host copies feed the oracle."""
+import numpy as np
+import pytest
+import torch
+
+import fixed_budget_sparse_amd as kv
+import oracle as orc
+import workloads as W
+from gpu_util import TOL, announce, device, host
+
+pytestmark = pytest.mark.gpu
+
+PREFILL = {"qwen3-4b-S16384": W.QWEN3_4B_S16K, "qwen3-8b-S32768": W.QWEN3_8B_S32K,
+           "long-S131072": W.LONG_S128K}
+
+
+def _boundary_rows(S, s, w, B, extra, seed):
+    """Rows at every boundary the mask and the tiling have, plus random rows."""
+    base = [0, 1, 2, 3, s - 1, s, s + 1, w - 2, w - 1, w, w + 1, s + w - 1, s + w, s + w + 1,
+            B - 1, B, B + 1, B + w - 1, B + w, 63, 64, 127, 128, 255, 256, 511, 512,
+            S // 2, S - 257, S - 256, S - 65, S - 64, S - 2, S - 1]
+    rng = np.random.default_rng(seed)
+    rows = np.concatenate([np.array(base), rng.integers(0, S, extra)])
+    return np.unique(rows[(rows >= 0) & (rows < S)])
+
+
+def _bf16_half_ulp(x):
+    """Half a bfloat16 ulp at |x|: the rounding of a bfloat16 output itself,
+    allowed on top of the computation's tolerance."""
+    a = np.maximum(np.abs(x), 2.0 ** -126)
+    return 2.0 ** (np.floor(np.log2(a)) - 8)
+
+
+def _inputs(wl):
+    dev = device()
+    x = W.make_prefill_device(wl, dev)
+    torch.cuda.synchronize()
+    return x
+
+
+@pytest.mark.parametrize("name", list(PREFILL))
+def test_full_thresholds(name):
+    wl = PREFILL[name]
+    announce(f"full thresholds {name}")
+    dev = device()
+    S, s, w, k = wl.seq_len, wl.sink, wl.window, wl.topk
+    prio_d = W.make_prefill_device(wl, dev)["prio"]
+    rank, tau = kv.thresholds(prio_d, s, w, k)
+    torch.cuda.synchronize()
+    prio = host(prio_d)
+    rank_o = orc.priority_ranks(prio)
+    assert np.array_equal(host(rank), rank_o)
+    if S <= 32768:
+        rows = np.arange(S)
+    else:
+        rows = np.union1d(_boundary_rows(S, s, w, s + w + k, 256, 3), np.arange(0, S, 509))
+    tau_o = orc.thresholds_by_selection(rank_o, s, w, k, rows=rows)
+    assert np.array_equal(host(tau)[..., rows], tau_o)
+
+
+@pytest.mark.parametrize("name", list(PREFILL))
+def test_full_masked_fwd_sampled_rows(name):
+    wl = PREFILL[name]
+    announce(f"full masked_fwd {name}")
+    S, s, w, k = wl.seq_len, wl.sink, wl.window, wl.topk
+    x = _inputs(wl)
+    rank, tau = kv.thresholds(x["prio"], s, w, k)
+    o, lse = kv.masked_attn_fwd(x["q"], x["k"], x["v"], rank, tau, s, w, k,
+                                out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    rows = _boundary_rows(S, s, w, s + w + k, 48 if S > 32768 else 96, 5)
+    rank_o = orc.priority_ranks(host(x["prio"]))
+    tau_full = np.zeros(rank_o.shape, np.int64)
+    tau_full[..., rows] = orc.thresholds_by_selection(rank_o, s, w, k, rows=rows)
+    q_rows = host(x["q"][:, :, torch.as_tensor(rows, device=x["q"].device)])
+    # masked_attention indexes q by row number: place the sampled rows in a
+    # zero array of the full shape only along the sampled rows' positions
+    qh = np.zeros(x["q"].shape, np.float32)
+    qh[:, :, rows] = q_rows
+    O, LSE = orc.masked_attention(qh, host(x["k"]), host(x["v"]), rank_o, tau_full, s, w,
+                                  rows=rows)
+    og = host(o)[:, :, rows]
+    lg = host(lse)[:, :, rows]
+    tol = TOL["bf16"]
+    assert np.isfinite(og).all() and np.isfinite(lg).all()
+    err = np.abs(og - O) - _bf16_half_ulp(np.maximum(np.abs(O), np.abs(og)))
+    assert err.max() <= tol["o"], err.max()
+    assert np.abs(lg - LSE).max() <= tol["lse"], np.abs(lg - LSE).max()
+
+
+@pytest.mark.parametrize("name", ["qwen3-4b-S16384", "qwen3-8b-S32768"])
+def test_full_teacher_lse_and_target(name):
+    """The dense teacher (k >= S) on sampled rows, then the future target of one
+    query head driven by the oracle's teacher LSE (every head receives that
+    head's LSE; only the checked head is compared)."""
+    wl = PREFILL[name]
+    announce(f"full target {name}")
+    S, s, w = wl.seq_len, wl.sink, wl.window
+    G = wl.group
+    x = _inputs(wl)
+    hq = 5 if S <= 16384 else wl.n_q_heads - 1
+    h = hq // G
+    rank_d, tau_d = kv.thresholds(x["prio"], s, w, S)
+    _, lse_dense = kv.masked_attn_fwd(x["q"], x["k"], x["v"], rank_d, tau_d, s, w, S,
+                                      out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    qh = host(x["q"][:, hq:hq + 1])
+    kh = host(x["k"][:, h:h + 1])
+    vh = host(x["v"][:, h:h + 1])
+    _, L = orc.dense_causal_attention(qh, kh, vh)            # teacher LSE [1, 1, S]
+    rows = _boundary_rows(S, s, w, 2048, 256, 7)
+    assert np.abs(host(lse_dense)[0, hq, rows] - L[0, 0, rows]).max() <= TOL["bf16"]["lse"]
+    L32 = L.astype(np.float32)
+    lse_in = torch.from_numpy(L32).to(x["q"].device).expand(1, wl.n_q_heads, S).contiguous()
+    tgt = kv.future_target(x["q"], x["k"], lse_in, w)
+    torch.cuda.synchronize()
+    tg = host(tgt)[0, hq]
+    if S <= 16384:
+        T = orc.future_target_colsum(qh, kh, L32.astype(np.float64), w)[0, 0]
+        ts = np.arange(S)
+    else:
+        ts = _boundary_rows(S, s, w, 2048, 384, 9)
+        T = orc.future_target_eq8(qh, kh, L32.astype(np.float64), w, ts=ts)[0, 0]
+    tg = tg[ts]
+    assert np.array_equal(np.isneginf(tg), np.isneginf(T))
+    sel = T > -20
+    assert sel.sum() > len(ts) // 2
+    assert np.abs(tg[sel] - T[sel]).max() <= TOL["bf16"]["tgt"], np.abs(tg[sel] - T[sel]).max()
+
+
+def _decode_run(wl, n_steps, check_steps, out_seqs):
+    """Runs decode steps 0..n_steps-1 over every sequence; at each step of
+    ``check_steps`` compares cache membership of every (sequence, KV head) with
+    the oracle's kept set of that row, and o/LSE of ``out_seqs``."""
+    dev = device()
+    nseq, Hq, Hkv, D = wl.batch, wl.n_q_heads, wl.n_kv_heads, wl.head_dim
+    s, w, k = wl.sink, wl.window, wl.topk
+    Bc = s + w + k
+    st = W.make_decode_stream_device(wl, dev, n_steps)
+    kn_all, vn_all, prio_t = st["k_new"], st["v_new"], st["prio_table"]
+    prio_h = host(prio_t)
+    rank_o = orc.priority_ranks(prio_h)                 # [nseq, Hkv, n_steps]
+    cache = kv.new_decode_cache(nseq, Hkv, D, s, w, k, dtype=torch.bfloat16, device=dev)
+    pos_all = torch.arange(n_steps, dtype=torch.int32, device=dev)[:, None].repeat(1, nseq)
+    zero_prio = torch.zeros((nseq, Hkv), device=dev)
+    prio_steps = prio_t.permute(2, 0, 1).contiguous()   # [n_steps, nseq, Hkv]
+    q_fixed = W.make_decode_query_device(wl, dev, 0)
+    o = torch.empty((nseq, Hq, D), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((nseq, Hq), dtype=torch.float32, device=dev)
+    pr = kv.Problem(nseq, Hq, Hkv, 0, D, s, w, k, 0.0, 0, 0)
+    n_ws = kv.workspace_size(3, pr)
+    ws_raw = torch.empty(n_ws + 256, dtype=torch.uint8, device=dev)
+    ws = ws_raw[(-ws_raw.data_ptr()) % 256:][:n_ws]
+    checks = sorted(set(int(c) for c in check_steps if 0 <= c < n_steps))
+    done = 0
+    for p in range(n_steps):
+        check = done < len(checks) and checks[done] == p
+        qd = W.make_decode_query_device(wl, dev, p) if check else q_fixed
+        pl = prio_steps[p - w] if p >= w else zero_prio
+        kv.decode_step(cache, pos_all[p], qd, kn_all[p], vn_all[p], pl, s, w, k,
+                       out_dtype=torch.bfloat16, o=o, lse=lse, ws=ws)
+        if not check:
+            continue
+        done += 1
+        torch.cuda.synchronize()
+        n = min(p + 1, Bc)
+        sp = host(cache.slot_pos)[:, :, :n]
+        tau = orc.thresholds_by_selection(rank_o, s, w, k, rows=[p])[..., 0]   # [nseq, Hkv]
+        held = {}
+        for b in range(nseq):
+            for h in range(Hkv):
+                keep = orc.mask_rows(rank_o[b, h, :p + 1], tau[b, h:h + 1], np.array([p]), s, w)[0]
+                want = np.flatnonzero(keep)
+                assert len(want) == n, (p, b, h)
+                assert np.array_equal(np.sort(sp[b, h]), want), (p, b, h)
+                held[(b, h)] = want
+        qh, oh, lh = host(qd), host(o), host(lse)
+        for b in out_seqs:
+            idx = [held[(b, h)] for h in range(Hkv)]
+            kt = np.stack([host(kn_all[torch.as_tensor(idx[h], device=dev), b, h])
+                           for h in range(Hkv)])
+            vt = np.stack([host(vn_all[torch.as_tensor(idx[h], device=dev), b, h])
+                           for h in range(Hkv)])
+            local = [np.arange(n)] * Hkv
+            oo, ll = orc.decode_attention(qh[b], kt, vt, local)
+            ulp = _bf16_half_ulp(np.maximum(np.abs(oo), np.abs(oh[b])))
+            assert (np.abs(oh[b] - oo) - ulp).max() <= TOL["bf16"]["o"], (p, b)
+            assert np.abs(lh[b] - ll).max() <= TOL["bf16"]["lse"], (p, b)
+    assert done == len(checks)
+
+
+def test_full_decode_b2048():
+    """64 sequences, B = 2048, steps 0..5119 (the benchmark times 4096..5119)."""
+    wl = W.DECODE_B2048
+    announce("full decode 64 x B2048, 5120 steps")
+    s, w, Bc = wl.sink, wl.window, wl.budget
+    checks = [0, s - 1, s, w - 1, w, w + s, Bc - 1, Bc, Bc + 1, 2 * Bc - 1, 2 * Bc, 4607, 5119]
+    _decode_run(wl, 5120, checks, out_seqs=[0, 37, 63])
+
+
+def test_full_decode_long_131072_steps():
+    """8 sequences, B = 4096, decoding to 131072 steps with the constant cache."""
+    wl = W.scaled(W.LONG_S128K, batch=8)
+    announce("full decode 8 x B4096, 131072 steps")
+    Bc = wl.budget
+    checks = [Bc - 1, Bc, 2 * Bc, 65535, 131071]
+    _decode_run(wl, 131072, checks, out_seqs=[0, 7])

@@ -150,3 +150,72 @@ def make_decode_prio_table(wl: Workload, n_tokens: int | None = None, batch: int
 def scaled(wl: Workload, **over) -> Workload:
     """A copy of ``wl`` with some fields replaced (reduced parity cases)."""
     return dataclasses.replace(wl, **over)
+
+
+# --------------------------------------------------------------------------
+# Device-side draws for the full-size cases.  The same recipe (N(0,1), keys
+# 0..3 x4, bfloat16 rounding to nearest even, N(0,1) priorities) drawn with
+# torch's seeded generator directly in device memory, so that inputs of
+# hundreds of millions of elements need not pass through the host.  Host
+# copies of whatever a check needs are taken from these tensors.
+# --------------------------------------------------------------------------
+def torch_seed(seed: int, config_id: int, tensor: str, extra: int = 0) -> int:
+    """A 63-bit seed for torch.Generator, one per (seed, config, tensor, extra)."""
+    st = np.random.SeedSequence([seed, config_id, _TID[tensor], extra]).generate_state(2)
+    return int((int(st[0]) << 31) ^ int(st[1])) & ((1 << 63) - 1)
+
+
+def _device_normal(shape, seed: int, device, dtype: str, scale_first: int = 0):
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    x = torch.randn(shape, generator=g, device=device, dtype=torch.float32)
+    if scale_first:
+        x[..., :scale_first, :] *= 4.0
+    return x.to(torch.bfloat16) if dtype == "bf16" else x
+
+
+def make_prefill_device(wl: Workload, device, seq_len: int | None = None,
+                        batch: int | None = None, seed: int | None = None,
+                        sink_scale_keys: int = 4):
+    """dict(q, k, v, prio) as device tensors: q [b, Hq, S, D], k/v [b, Hkv, S, D]
+    in bfloat16 (float32 for float32 workloads), prio [b, Hkv, S] float32."""
+    S = wl.seq_len if seq_len is None else seq_len
+    b = wl.batch if batch is None else batch
+    sd = wl.seed if seed is None else seed
+    c = wl.config_id
+    D = wl.head_dim
+    q = _device_normal((b, wl.n_q_heads, S, D), torch_seed(sd, c, "q"), device, wl.dtype)
+    k = _device_normal((b, wl.n_kv_heads, S, D), torch_seed(sd, c, "k"), device, wl.dtype,
+                       sink_scale_keys)
+    v = _device_normal((b, wl.n_kv_heads, S, D), torch_seed(sd, c, "v"), device, wl.dtype)
+    prio = _device_normal((b, wl.n_kv_heads, S, 1), torch_seed(sd, c, "prio"), device, "f32")
+    return {"q": q, "k": k, "v": v, "prio": prio[..., 0].contiguous()}
+
+
+def make_decode_stream_device(wl: Workload, device, n_steps: int, batch: int | None = None,
+                              seed: int | None = None):
+    """Per-step decode inputs for steps 0..n_steps-1 as device tensors:
+    k_new/v_new [n_steps, b, Hkv, D] (token p's K/V at index p; tokens 0..3 x4)
+    and prio_table [b, Hkv, n_steps] float32 (read at step t + w)."""
+    b = wl.batch if batch is None else batch
+    sd = wl.seed if seed is None else seed
+    c = wl.config_id
+    D = wl.head_dim
+    shape = (b, wl.n_kv_heads, n_steps, D)
+    k = _device_normal(shape, torch_seed(sd, c, "dec_k"), device, wl.dtype, 4)
+    v = _device_normal(shape, torch_seed(sd, c, "dec_v"), device, wl.dtype)
+    prio = _device_normal((b, wl.n_kv_heads, n_steps, 1), torch_seed(sd, c, "dec_prio"),
+                          device, "f32")
+    return {"k_new": k.permute(2, 0, 1, 3).contiguous(),
+            "v_new": v.permute(2, 0, 1, 3).contiguous(),
+            "prio_table": prio[..., 0].contiguous()}
+
+
+def make_decode_query_device(wl: Workload, device, step: int, batch: int | None = None,
+                             seed: int | None = None):
+    """The query of decode step ``step``: [b, Hq, D] on the device."""
+    b = wl.batch if batch is None else batch
+    sd = wl.seed if seed is None else seed
+    return _device_normal((b, wl.n_q_heads, wl.head_dim), torch_seed(sd, wl.config_id, "dec_q",
+                                                                     step), device, wl.dtype)
