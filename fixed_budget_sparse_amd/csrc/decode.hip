@@ -6,12 +6,12 @@
 // gist.science summary §2.1: B = s + w + k entries per KV head.
 //
 // Two kernels per step, on the caller's stream:
-//  1. decide (one wave per (sequence, KV head)): reads the slot metadata,
+//  1. decide (one workgroup per (sequence, KV head)): reads the slot metadata,
 //     picks the slot token p takes (slot p while the cache fills; afterwards
 //     the slot of u when u is dropped, or of the worst held long-range token
 //     when u replaces it), updates slot_pos / slot_prio / ring, writes the new
 //     K/V row into that slot.  The choice is exact integer/compare work; the
-//     worst token is found with a wave shuffle reduction.
+//     worst token is found with wave shuffle and LDS reductions.
 //  2. attend (split-K only when there are too few (sequence, KV head) pairs
 //     to fill the chip): every wave streams 32-slot blocks of K and V from
 //     HBM with coalesced loads, prefetching the next block into registers
@@ -68,9 +68,24 @@ __device__ __forceinline__ bool worse_than(const Worst& a, const Worst& b) {
   return a.slot >= 0 && (b.slot < 0 || a.p < b.p || (a.p == b.p && a.pos > b.pos));
 }
 
+constexpr int kDecideThreads = 256;
+constexpr int kDecideUnroll = 8;   // slot loads in flight per thread
+
+__device__ __forceinline__ void wave_reduce_worst(Worst& best) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    Worst o;
+    o.p = __shfl_xor(best.p, off);
+    o.pos = __shfl_xor(best.pos, off);
+    o.slot = __shfl_xor(best.slot, off);
+    if (worse_than(o, best)) best = o;
+  }
+}
+
 template <int D, bool kF32>
-__global__ __launch_bounds__(64) void decode_decide_kernel(DecArgs a) {
-  const int lane = threadIdx.x;
+__global__ __launch_bounds__(kDecideThreads) void decode_decide_kernel(DecArgs a) {
+  __shared__ Worst s_worst[kDecideThreads / 64];
+  const int tid = threadIdx.x, lane = lane_id(), wave = wave_id();
   const int h = blockIdx.x, b = blockIdx.y;
   const int s = a.s, w = a.w, k = a.k, Bc = a.Bc;
   const size_t seg = (size_t)b * a.Hkv + h;
@@ -99,26 +114,37 @@ __global__ __launch_bounds__(64) void decode_decide_kernel(DecArgs a) {
     if (k == 0) {
       ns = u_slot;
     } else {
+      // every thread issues all its slot loads before comparing (the scan is
+      // latency-bound otherwise), then a wave and a workgroup reduction
       Worst best{__builtin_huge_valf(), -1, -1};
-      for (int j = lane; j < Bc; j += 64) {
-        const int sp = spos[j];
-        const Worst c{sprio[j], sp, j};
-        if (sp >= s && sp < u && worse_than(c, best)) best = c;
-      }
+      for (int j0 = tid; j0 < Bc; j0 += kDecideThreads * kDecideUnroll) {
+        int sp[kDecideUnroll];
+        float pr[kDecideUnroll];
 #pragma unroll
-      for (int off = 32; off > 0; off >>= 1) {
-        Worst o;
-        o.p = __shfl_xor(best.p, off);
-        o.pos = __shfl_xor(best.pos, off);
-        o.slot = __shfl_xor(best.slot, off);
-        if (worse_than(o, best)) best = o;
+        for (int i = 0; i < kDecideUnroll; ++i) {
+          const int j = j0 + i * kDecideThreads;
+          sp[i] = j < Bc ? spos[j] : -1;
+          pr[i] = j < Bc ? sprio[j] : 0.0f;
+        }
+#pragma unroll
+        for (int i = 0; i < kDecideUnroll; ++i) {
+          const Worst c{pr[i], sp[i], j0 + i * kDecideThreads};
+          if (sp[i] >= s && sp[i] < u && worse_than(c, best)) best = c;
+        }
       }
+      wave_reduce_worst(best);
+      if (lane == 0) s_worst[wave] = best;
+      __syncthreads();
+      best = s_worst[0];
+#pragma unroll
+      for (int i = 1; i < kDecideThreads / 64; ++i)
+        if (worse_than(s_worst[i], best)) best = s_worst[i];
       keep_u = best.slot >= 0 && pu > best.p;
       ns = keep_u ? best.slot : u_slot;
     }
   }
   if ((unsigned)ns >= (unsigned)Bc) return;   // inconsistent cache state: leave it untouched
-  if (lane == 0) {
+  if (tid == 0) {
     if (keep_u && (unsigned)u_slot < (unsigned)Bc) sprio[u_slot] = pu;
     ring[p % w] = ns;
     spos[ns] = p;
@@ -130,7 +156,7 @@ __global__ __launch_bounds__(64) void decode_decide_kernel(DecArgs a) {
   const uint32_t* vn = (const uint32_t*)a.v_new + seg * kWords;
   uint32_t* kc = (uint32_t*)a.ck + (seg * Bc + ns) * kWords;
   uint32_t* vc = (uint32_t*)a.cv + (seg * Bc + ns) * kWords;
-  for (int i = lane; i < kWords; i += 64) {
+  for (int i = tid; i < kWords; i += kDecideThreads) {
     kc[i] = kn[i];
     vc[i] = vn[i];
   }
@@ -145,9 +171,10 @@ struct DecLds {
   static constexpr int kBytes = kF32 ? kBlk * KS * 4 : kBlk * KS * 2;
   static constexpr int vBytes = kF32 ? kBlk * VS * 4 : D * VS * 2;
   static constexpr int waveBytes = ((kBytes + vBytes + 15) / 16) * 16;
-  // K: 16-byte pieces per lane; V: 32-bit words per lane (bf16: 4 groups x 8 keys per dim pair)
+  // K: 16-byte pieces per lane; bf16 V: (slot pair, 8-dim octet) tasks per
+  // lane, each two 16-byte row loads
   static constexpr int KPL = kBlk * (D * (kF32 ? 4 : 2) / 16) / 64;
-  static constexpr int VPL = kF32 ? KPL : 4 * (D / 2) / 64 * 8;
+  static constexpr int VTL = (kBlk / 2) * (D / 8) / 64;
 };
 
 template <int D, bool kF32, bool kF32Out>
@@ -196,8 +223,9 @@ __global__ __launch_bounds__(kThreads, 2) void decode_attend_kernel(DecArgs a) {
   const size_t cbase = seg * (size_t)Bc * D;
 
   // ---- staging of one 32-slot block: HBM -> registers -> this wave's LDS
+  typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
   uint4 kst[L::KPL];
-  uint32_t vst[kF32 ? 1 : L::VPL];
+  u32x4v vpair[kF32 ? 1 : 2 * L::VTL];
   uint4 vst4[kF32 ? L::KPL : 1];
   auto load_blk = [&](int blk) {
     if constexpr (!kF32) {
@@ -212,14 +240,13 @@ __global__ __launch_bounds__(kThreads, 2) void decode_attend_kernel(DecArgs a) {
                              : make_uint4(0, 0, 0, 0);
       }
 #pragma unroll
-      for (int i = 0; i < L::VPL / 8; ++i) {
+      for (int i = 0; i < L::VTL; ++i) {
         const int task = lane + 64 * i;
-        const int grp = task / (D / 2), dp = task % (D / 2);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int slot = blk + 16 * (grp >> 1) + 8 * (e >> 2) + 4 * (grp & 1) + (e & 3);
-          vst[8 * i + e] = slot < j_hi ? *(const uint32_t*)(vg + (size_t)slot * D + 2 * dp) : 0u;
-        }
+        const int pr = task & 15, oc = task >> 4;      // pairs fastest: distinct LDS banks
+        const int s0 = blk + 2 * pr;
+        const u32x4v z = {0u, 0u, 0u, 0u};
+        vpair[2 * i] = s0 < j_hi ? *(const u32x4v*)(vg + (size_t)s0 * D + 8 * oc) : z;
+        vpair[2 * i + 1] = s0 + 1 < j_hi ? *(const u32x4v*)(vg + (size_t)(s0 + 1) * D + 8 * oc) : z;
       }
     } else {
       const float* kg = (const float*)a.ck + cbase;
@@ -245,24 +272,22 @@ __global__ __launch_bounds__(kThreads, 2) void decode_attend_kernel(DecArgs a) {
         const int pi = lane + 64 * i;
         *(uint4*)(kl + (pi / PPR) * L::KS + (pi % PPR) * 8) = kst[i];
       }
-      // V^T: column c = 16*ks + 8*hh + e of LDS row d holds slot
-      // 16*ks + 8*(e>>2) + 4*hh + (e&3) of the block (the P operand layout)
+      // V^T: column c = 16*ks + 8*hh + 4*a + r of LDS row d holds slot
+      // 16*ks + 8*a + 4*hh + r of the block (the P operand layout); a slot
+      // pair lands in two adjacent columns, so each dim is one 32-bit word
 #pragma unroll
-      for (int i = 0; i < L::VPL / 8; ++i) {
+      for (int i = 0; i < L::VTL; ++i) {
         const int task = lane + 64 * i;
-        const int grp = task / (D / 2), dp = task % (D / 2);
-        const uint32_t* x = &vst[8 * i];
-        uint4 lo, hi;
-        lo.x = (x[0] & 0xffffu) | (x[1] << 16);
-        lo.y = (x[2] & 0xffffu) | (x[3] << 16);
-        lo.z = (x[4] & 0xffffu) | (x[5] << 16);
-        lo.w = (x[6] & 0xffffu) | (x[7] << 16);
-        hi.x = (x[0] >> 16) | (x[1] & 0xffff0000u);
-        hi.y = (x[2] >> 16) | (x[3] & 0xffff0000u);
-        hi.z = (x[4] >> 16) | (x[5] & 0xffff0000u);
-        hi.w = (x[6] >> 16) | (x[7] & 0xffff0000u);
-        *(uint4*)(vl + (2 * dp) * L::VS + grp * 8) = lo;
-        *(uint4*)(vl + (2 * dp + 1) * L::VS + grp * 8) = hi;
+        const int pr = task & 15, oc = task >> 4;
+        const int j0 = 2 * pr;
+        const int c0 = 16 * (j0 >> 4) + 8 * ((j0 >> 2) & 1) + 4 * ((j0 >> 3) & 1) + (j0 & 3);
+        const u32x4v x0 = vpair[2 * i], x1 = vpair[2 * i + 1];
+        uint16_t* col = vl + (8 * oc) * L::VS + c0;
+#pragma unroll
+        for (int dp = 0; dp < 4; ++dp) {
+          *(uint32_t*)(col + (2 * dp) * L::VS) = (x0[dp] & 0xffffu) | (x1[dp] << 16);
+          *(uint32_t*)(col + (2 * dp + 1) * L::VS) = (x0[dp] >> 16) | (x1[dp] & 0xffff0000u);
+        }
       }
     } else {
       float* kl = (float*)my;
@@ -435,7 +460,8 @@ __global__ __launch_bounds__(kThreads) void decode_combine_kernel(DecArgs a) {
 
 template <int D, bool kF32, bool kF32Out>
 void launch_dec(const DecArgs& a, int b, hipStream_t st) {
-  hipLaunchKernelGGL((decode_decide_kernel<D, kF32>), dim3(a.Hkv, b), dim3(64), 0, st, a);
+  hipLaunchKernelGGL((decode_decide_kernel<D, kF32>), dim3(a.Hkv, b), dim3(kDecideThreads), 0, st,
+                     a);
   hipLaunchKernelGGL((decode_attend_kernel<D, kF32, kF32Out>), dim3(a.nsplit, a.Hkv, b),
                      dim3(kThreads), 0, st, a);
   if (a.nsplit > 1)
