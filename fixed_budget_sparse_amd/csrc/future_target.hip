@@ -110,6 +110,13 @@ __global__ __launch_bounds__(kThreads, 2) void future_target_kernel(TgtArgs a) {
     }
   }
 
+  // complete the key loads here: loads still in flight at the loop entry make
+  // the compiler wait for every newer load before the loop's first MFMA
+#pragma unroll
+  for (int rb = 0; rb < kRB; ++rb)
+#pragma unroll
+    for (int ks = 0; ks < Gm::NKS; ++ks) asm volatile("" : "+v"(kop[rb][ks]));
+
   const unsigned char* qg = (const unsigned char*)a.q + ((size_t)b * a.Hq + hq) * S * D * Gm::esz;
   const float* lse = a.lse + ((size_t)b * a.Hq + hq) * S;
 
@@ -126,12 +133,11 @@ __global__ __launch_bounds__(kThreads, 2) void future_target_kernel(TgtArgs a) {
       const int d = min(d0 + row, S - 1);
       stage[i] = *(const u32x4v*)(qg + (size_t)d * D * Gm::esz + piece * 16);
     }
-    if (tid < kChunk) {
-      const int d = d0 + tid;
-      stage_lse = d < S ? -lse[d] * kLog2e : kNegInf;
-    }
+    // the raw value only: arithmetic on it here would wait for all the loads
+    // above; it is scaled when stored
+    if (tid < kChunk) stage_lse = lse[min(d0 + tid, S - 1)];
   };
-  auto store_chunk = [&](int buf) {
+  auto store_chunk = [&](int buf, int d0) {
 #pragma unroll
     for (int i = 0; i < Gm::NPIECE; ++i) {
       const int p = tid + i * kThreads;
@@ -146,7 +152,7 @@ __global__ __launch_bounds__(kThreads, 2) void future_target_kernel(TgtArgs a) {
         *(u32x4v*)((uint16_t*)q_lds[buf] + row * Gm::QS + piece * 8) = stage[i];
       }
     }
-    if (tid < kChunk) nlse[buf][tid] = stage_lse;
+    if (tid < kChunk) nlse[buf][tid] = d0 + tid < S ? -stage_lse * kLog2e : kNegInf;
   };
 
   float sum[kRB];
@@ -154,7 +160,7 @@ __global__ __launch_bounds__(kThreads, 2) void future_target_kernel(TgtArgs a) {
   for (int rb = 0; rb < kRB; ++rb) sum[rb] = 0.0f;
   const int nchunks = (S - d_start + kChunk - 1) / kChunk;
   load_chunk(d_start);
-  store_chunk(0);
+  store_chunk(0, d_start);
   __syncthreads();
 
   // One 32-column block of MFMAs: acc[rb] = Q_block K_rb^T.
@@ -301,7 +307,7 @@ __global__ __launch_bounds__(kThreads, 2) void future_target_kernel(TgtArgs a) {
     pend_mask = msk;
     pend_d0 = d0;
     pend_buf = buf;
-    if (has_next) store_chunk(buf ^ 1);
+    if (has_next) store_chunk(buf ^ 1, d0 + kChunk);
     __syncthreads();
   }
   if (pend) {

@@ -189,6 +189,12 @@ __global__ __launch_bounds__(kThreads, 1) void masked_fwd_kernel(FwdArgs a) {
     }
   }
 
+  // complete the query loads here: loads still in flight at the loop entry
+  // made the compiler wait for every newer load (the whole next-chunk gather)
+  // before the first MFMA of each chunk
+#pragma unroll
+  for (int ks = 0; ks < NKS; ++ks) asm volatile("" : "+v"(qop[ks]));
+
   f32x16 oacc[D / 32];
 #pragma unroll
   for (int db = 0; db < D / 32; ++db) oacc[db] = f32x16{};
@@ -198,34 +204,42 @@ __global__ __launch_bounds__(kThreads, 1) void masked_fwd_kernel(FwdArgs a) {
   __syncthreads();   // s_min_tau complete
   const int min_tau = s_min_tau;
 
-  // ---- key descriptors (token, rank) of the chunk starting at c0 (wave 0)
-  auto make_desc = [&](int c0, int db) {
-    if (tid < kChunk) {
-      const int j = c0 + tid;
-      int t = -1, r = 0;
-      if (j < n_sink) {
-        t = j;
-      } else if (j < n_sink + n_long) {
-        const int jj = j - n_sink;
-        if (listed) {
-          const int2 e = lst[jj];
-          t = e.x;
-          r = e.y;
-        } else {
-          t = s + jj;
-          r = rank[t];
-        }
-      } else if (j < nk) {
-        t = band_lo + (j - n_sink - n_long);
-        r = rank[t];
-      }
+  // ---- key descriptors of the chunk starting at c0, built by wave 0 in two
+  // halves: desc_load issues the (branch-free, clamped) global reads into
+  // registers, desc_store, one compute phase later, publishes token and
+  // masking rank to LDS with the chunk's mask class:
+  //   0  every key kept by every row of the tile (no mask),
+  //   1  every key is a sink or lies at or below q0 - w for the whole tile, so
+  //      a row keeps it iff rank' <= tau_q (rank' = -1 for sinks),
+  //   2  otherwise (window edge, causal diagonal, padding): the full test.
+  int pd_t = -1, pd_r = 0;
+  int2 pd_l = make_int2(-1, 0);
+  auto desc_load = [&](int c0) {
+    if (wave == 0) {
+      const int j = c0 + lane;
+      const bool in_sink = j < n_sink;
+      const bool in_long = !in_sink && j < n_sink + n_long;
+      const bool in_band = !in_sink && !in_long && j < nk;
+      const int t = in_sink ? j
+                    : in_long ? s + (j - n_sink)
+                    : in_band ? band_lo + (j - n_sink - n_long) : -1;
+      if (listed) pd_l = lst[min(max(j - n_sink, 0), max(n_long - 1, 0))];
+      pd_r = rank[min(max(t, 0), S - 1)];
+      pd_t = (in_long && listed) ? -2 : t;    // -2: token and rank from the list
+    }
+  };
+  auto desc_store = [&](int db) {
+    if (wave == 0) {
+      int t = pd_t == -2 ? pd_l.x : pd_t;
+      const int r = pd_t == -2 ? pd_l.y : pd_r;
       if (t >= S) t = -1;
-      kd_t[db][tid] = t;
-      kd_r[db][tid] = r;
-      // kept by every row of the tile?
+      const int rq = (t >= 0) & (t < s) ? -1 : r;
+      kd_t[db][lane] = t;
+      kd_r[db][lane] = rq;
       const bool always = (t >= 0) & (t <= q0) & ((t < s) | (t > q_hi - w) | (r <= min_tau));
-      const uint64_t bal = wave_ballot(!always);
-      if (tid == 0) s_flag[db] = bal != 0;
+      const bool simple = (t >= 0) & (t <= q0) & ((t < s) | (t <= q0 - w));
+      const uint64_t not_always = wave_ballot(!always), not_simple = wave_ballot(!simple);
+      if (lane == 0) s_flag[db] = not_always == 0 ? 0 : (not_simple == 0 ? 1 : 2);
     }
   };
 
@@ -235,10 +249,15 @@ __global__ __launch_bounds__(kThreads, 1) void masked_fwd_kernel(FwdArgs a) {
   // bf16 V^T tasks: (key pair, 8-dim octet); two 16-byte row loads each
   constexpr int NVT = 32 * (D / 8);
   constexpr int VT = kF32In ? 1 : (NVT + kThreads - 1) / kThreads;  // per thread
+  // native 4-wide vectors: HIP's uint4 arrays captured by the lambdas below
+  // were placed in scratch memory
   typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
-  uint4 kst[KP];
-  uint4 vst4[kF32In ? KP : 1];
+  u32x4v kst[KP];
+  u32x4v vst4[kF32In ? KP : 1];
   u32x4v vpair[kF32In ? 1 : 2 * VT];
+  // Padding slots (token -1) load row 0 instead: every such key is masked
+  // (its probability is exactly 0), so only finiteness matters, and the loads
+  // stay unconditional (no exec-masked branches, all addresses issued at once).
   auto load_chunk = [&](int db) {
     if constexpr (!kF32In) {
       const uint16_t* kg = (const uint16_t*)a.k + kvbase;
@@ -246,19 +265,17 @@ __global__ __launch_bounds__(kThreads, 1) void masked_fwd_kernel(FwdArgs a) {
 #pragma unroll
       for (int i = 0; i < KP; ++i) {
         const int p = tid + i * kThreads;
-        const int t = kd_t[db][p / PPR];
-        kst[i] = t >= 0 ? *(const uint4*)(kg + (size_t)t * D + (p % PPR) * 8)
-                        : make_uint4(0, 0, 0, 0);
+        const int t = max(kd_t[db][p / PPR], 0);
+        kst[i] = *(const u32x4v*)(kg + (size_t)t * D + (p % PPR) * 8);
       }
 #pragma unroll
       for (int i = 0; i < VT; ++i) {
         const int task = tid + i * kThreads;
         if (NVT % kThreads != 0 && task >= NVT) break;
         const int pr = task & 31, oc = task >> 5;   // pairs fastest: distinct LDS banks
-        const int t0 = kd_t[db][2 * pr], t1 = kd_t[db][2 * pr + 1];
-        const u32x4v z = {0u, 0u, 0u, 0u};
-        vpair[2 * i] = t0 >= 0 ? *(const u32x4v*)(vg + (size_t)t0 * D + 8 * oc) : z;
-        vpair[2 * i + 1] = t1 >= 0 ? *(const u32x4v*)(vg + (size_t)t1 * D + 8 * oc) : z;
+        const int t0 = max(kd_t[db][2 * pr], 0), t1 = max(kd_t[db][2 * pr + 1], 0);
+        vpair[2 * i] = *(const u32x4v*)(vg + (size_t)t0 * D + 8 * oc);
+        vpair[2 * i + 1] = *(const u32x4v*)(vg + (size_t)t1 * D + 8 * oc);
       }
     } else {
       const float* kg = (const float*)a.k + kvbase;
@@ -266,10 +283,10 @@ __global__ __launch_bounds__(kThreads, 1) void masked_fwd_kernel(FwdArgs a) {
 #pragma unroll
       for (int i = 0; i < KP; ++i) {
         const int p = tid + i * kThreads;
-        const int t = kd_t[db][p / PPR];
+        const int t = max(kd_t[db][p / PPR], 0);
         const size_t off = (size_t)t * D + (p % PPR) * 4;
-        kst[i] = t >= 0 ? *(const uint4*)(kg + off) : make_uint4(0, 0, 0, 0);
-        vst4[i] = t >= 0 ? *(const uint4*)(vg + off) : make_uint4(0, 0, 0, 0);
+        kst[i] = *(const u32x4v*)(kg + off);
+        vst4[i] = *(const u32x4v*)(vg + off);
       }
     }
   };
@@ -280,7 +297,7 @@ __global__ __launch_bounds__(kThreads, 1) void masked_fwd_kernel(FwdArgs a) {
 #pragma unroll
       for (int i = 0; i < KP; ++i) {
         const int p = tid + i * kThreads;
-        *(uint4*)(kl + (p / PPR) * L::KS + (p % PPR) * 8) = kst[i];
+        *(u32x4v*)(kl + (p / PPR) * L::KS + (p % PPR) * 8) = kst[i];
       }
       // V^T: column c = 16*ks + 8*hh + 4*a + r of LDS row d holds key
       // 16*ks + 8*a + 4*hh + r of the chunk (the P operand layout); a key pair
@@ -312,7 +329,7 @@ __global__ __launch_bounds__(kThreads, 1) void masked_fwd_kernel(FwdArgs a) {
         kd[1] = __uint_as_float(kst[i].y);
         kd[2] = __uint_as_float(kst[i].z);
         kd[3] = __uint_as_float(kst[i].w);
-        *(uint4*)(vl + key * L::VS + piece * 4) = vst4[i];
+        *(u32x4v*)(vl + key * L::VS + piece * 4) = vst4[i];
       }
     }
   };
@@ -339,7 +356,16 @@ __global__ __launch_bounds__(kThreads, 1) void masked_fwd_kernel(FwdArgs a) {
     for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
       for (int e = 0; e < 16; ++e) x[blk * 16 + e] = sacc[blk][e];
-    if (__builtin_amdgcn_readfirstlane(s_flag[db])) {   // uniform: a scalar branch
+    const int mclass = __builtin_amdgcn_readfirstlane(s_flag[db]);   // uniform
+    if (mclass == 1) {
+#pragma unroll
+      for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int jj = 32 * blk + 8 * (e >> 2) + 4 * hh + (e & 3);
+          x[blk * 16 + e] = kd_r[db][jj] <= tau_q ? x[blk * 16 + e] : kNegInf;
+        }
+    } else if (mclass == 2) {
       // branch-free: bitwise tests and a select per score (a short-circuit
       // form here was compiled into divergent branches that lost a store)
 #pragma unroll
@@ -406,8 +432,12 @@ __global__ __launch_bounds__(kThreads, 1) void masked_fwd_kernel(FwdArgs a) {
 
   // ---- software pipeline: descriptors two chunks ahead, K/V one chunk ahead
   const int nchunk = (nk + kChunk - 1) / kChunk;
-  make_desc(0, 0);
-  if (nchunk > 1) make_desc(kChunk, 1);
+  desc_load(0);
+  desc_store(0);
+  if (nchunk > 1) {
+    desc_load(kChunk);
+    desc_store(1);
+  }
   __syncthreads();
   if (nchunk > 0) {
     load_chunk(0);
@@ -418,9 +448,10 @@ __global__ __launch_bounds__(kThreads, 1) void masked_fwd_kernel(FwdArgs a) {
     const int kb = c & 1, db = c % 3;
     const bool has_next = c + 1 < nchunk;
     if (has_next) load_chunk((c + 1) % 3);      // in flight during the math below
+    if (c + 2 < nchunk) desc_load((c + 2) * kChunk);
     compute(kb, db);
     if (has_next) store_chunk(kb ^ 1);
-    if (c + 2 < nchunk) make_desc((c + 2) * kChunk, (c + 2) % 3);
+    if (c + 2 < nchunk) desc_store((c + 2) % 3);
     __syncthreads();
   }
 
