@@ -351,11 +351,8 @@ __global__ __launch_bounds__(kThreads, 1) void masked_fwd_kernel(FwdArgs a) {
         for (int ks = 0; ks < NKS; ++ks) sacc[blk] = mfma32x32x2(kl[2 * ks], qop[ks], sacc[blk]);
       }
     }
-    float x[32];   // raw logits <q, k>
-#pragma unroll
-    for (int blk = 0; blk < 2; ++blk)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) x[blk * 16 + e] = sacc[blk][e];
+    // the mask, max and exps work in place on the accumulators (a separate
+    // copy of the scores was materialised with 32 moves per chunk)
     const int mclass = __builtin_amdgcn_readfirstlane(s_flag[db]);   // uniform
     if (mclass == 1) {
 #pragma unroll
@@ -363,7 +360,7 @@ __global__ __launch_bounds__(kThreads, 1) void masked_fwd_kernel(FwdArgs a) {
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
           const int jj = 32 * blk + 8 * (e >> 2) + 4 * hh + (e & 3);
-          x[blk * 16 + e] = kd_r[db][jj] <= tau_q ? x[blk * 16 + e] : kNegInf;
+          sacc[blk][e] = kd_r[db][jj] <= tau_q ? sacc[blk][e] : kNegInf;
         }
     } else if (mclass == 2) {
       // branch-free: bitwise tests and a select per score (a short-circuit
@@ -376,12 +373,14 @@ __global__ __launch_bounds__(kThreads, 1) void masked_fwd_kernel(FwdArgs a) {
           const int t = kd_t[db][jj], rt = kd_r[db][jj];
           const bool keep = row_ok & (t >= 0) & (t <= q) &
                             ((t < s) | (t > q - w) | (rt <= tau_q));
-          x[blk * 16 + e] = keep ? x[blk * 16 + e] : kNegInf;
+          sacc[blk][e] = keep ? sacc[blk][e] : kNegInf;
         }
     }
-    float mc = x[0];
+    float mc = sacc[0][0];
 #pragma unroll
-    for (int e = 1; e < 32; ++e) mc = fmaxf(mc, x[e]);
+    for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) mc = fmaxf(mc, sacc[blk][e]);
     mc = fmaxf(mc, __shfl_xor(mc, 32));
     // online softmax with a lazily moved reference max (m_run, raw units): it
     // moves only when some row's max grows by more than 2^8 in the exp2
@@ -398,16 +397,27 @@ __global__ __launch_bounds__(kThreads, 1) void masked_fwd_kernel(FwdArgs a) {
     const float mb = m_run == kNegInf ? 0.0f : -m_run * c;
     float ps = 0.0f;
 #pragma unroll
-    for (int e = 0; e < 32; ++e) {
-      x[e] = exp2_fast(fmaf(x[e], c, mb));
-      ps += x[e];
-    }
+    for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        sacc[blk][e] = exp2_fast(fmaf(sacc[blk][e], c, mb));
+        ps += sacc[blk][e];
+      }
     l_run += ps;
 
     if constexpr (!kF32In) {
       bf16x8 pk[4];
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) pk[ks] = pack_bf16x8(&x[(ks >> 1) * 16 + 8 * (ks & 1)]);
+      for (int ks = 0; ks < 4; ++ks) {
+        const f32x16& src = sacc[ks >> 1];
+        const int o8 = 8 * (ks & 1);
+        uint4 u;
+        u.x = pack_bf16x2(src[o8 + 0], src[o8 + 1]);
+        u.y = pack_bf16x2(src[o8 + 2], src[o8 + 3]);
+        u.z = pack_bf16x2(src[o8 + 4], src[o8 + 5]);
+        u.w = pack_bf16x2(src[o8 + 6], src[o8 + 7]);
+        pk[ks] = as_bf16x8(u);
+      }
 #pragma unroll
       for (int d2 = 0; d2 < D / 32; ++d2) {
         const uint16_t* vl = (const uint16_t*)v_lds[kb] + (32 * d2 + li) * L::VS + 8 * hh;
@@ -424,7 +434,7 @@ __global__ __launch_bounds__(kThreads, 1) void masked_fwd_kernel(FwdArgs a) {
 #pragma unroll
           for (int e = 0; e < 16; ++e) {
             const int key = 32 * blk + 8 * (e >> 2) + 4 * hh + (e & 3);
-            oacc[d2] = mfma32x32x2(vl[key * L::VS], x[blk * 16 + e], oacc[d2]);
+            oacc[d2] = mfma32x32x2(vl[key * L::VS], sacc[blk][e], oacc[d2]);
           }
       }
     }
