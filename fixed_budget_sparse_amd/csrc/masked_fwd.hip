@@ -32,6 +32,7 @@ namespace {
 constexpr int kThreads = 512;       // 8 waves
 constexpr int kRowsPerTile = 256;   // stacked query rows per workgroup (8 waves x 32)
 constexpr int kChunk = 64;          // keys per chunk
+constexpr int kDesc = 4;            // key-descriptor slots (chunks c .. c+3 live)
 
 struct FwdArgs {
   const void* q;
@@ -119,9 +120,9 @@ __global__ __launch_bounds__(kThreads, 1) void masked_fwd_kernel(FwdArgs a) {
   using L = FwdLds<D, kF32In>;
   __shared__ __attribute__((aligned(16))) unsigned char k_lds[2][L::kBytes];
   __shared__ __attribute__((aligned(16))) unsigned char v_lds[2][L::vBytes];
-  __shared__ __attribute__((aligned(16))) int kd_t[3][kChunk];
-  __shared__ __attribute__((aligned(16))) int kd_r[3][kChunk];
-  __shared__ int s_flag[3];
+  __shared__ __attribute__((aligned(16))) int kd_t[kDesc][kChunk];
+  __shared__ __attribute__((aligned(16))) int kd_r[kDesc][kChunk];
+  __shared__ int s_flag[kDesc];
   __shared__ int s_min_tau;
 
   const int tid = threadIdx.x, lane = lane_id(), wave = wave_id();
@@ -233,7 +234,7 @@ __global__ __launch_bounds__(kThreads, 1) void masked_fwd_kernel(FwdArgs a) {
       int t = pd_t == -2 ? pd_l.x : pd_t;
       const int r = pd_t == -2 ? pd_l.y : pd_r;
       if (t >= S) t = -1;
-      const int rq = (t >= 0) & (t < s) ? -1 : r;
+      const int rq = ((t >= 0) & (t < s)) ? -1 : r;
       kd_t[db][lane] = t;
       kd_r[db][lane] = rq;
       const bool always = (t >= 0) & (t <= q0) & ((t < s) | (t > q_hi - w) | (r <= min_tau));
@@ -243,9 +244,10 @@ __global__ __launch_bounds__(kThreads, 1) void masked_fwd_kernel(FwdArgs a) {
     }
   };
 
-  // ---- gather of one chunk: HBM -> registers -> LDS (V transposed)
+  // ---- gathers: HBM -> registers -> LDS.  K of chunk j is staged two
+  // chunks ahead, V (transposed) one chunk ahead.
   constexpr int PPR = kF32In ? D / 4 : D / 8;            // 16-byte pieces per row
-  constexpr int KP = kChunk * PPR / kThreads;            // K pieces per thread
+  constexpr int KP = kChunk * PPR / kThreads;            // K (or f32 V) pieces per thread
   // bf16 V^T tasks: (key pair, 8-dim octet); two 16-byte row loads each
   constexpr int NVT = 32 * (D / 8);
   constexpr int VT = kF32In ? 1 : (NVT + kThreads - 1) / kThreads;  // per thread
@@ -258,16 +260,18 @@ __global__ __launch_bounds__(kThreads, 1) void masked_fwd_kernel(FwdArgs a) {
   // Padding slots (token -1) load row 0 instead: every such key is masked
   // (its probability is exactly 0), so only finiteness matters, and the loads
   // stay unconditional (no exec-masked branches, all addresses issued at once).
-  auto load_chunk = [&](int db) {
-    if constexpr (!kF32In) {
-      const uint16_t* kg = (const uint16_t*)a.k + kvbase;
-      const uint16_t* vg = (const uint16_t*)a.v + kvbase;
+  auto load_k = [&](int db) {
+    const unsigned char* kg = (const unsigned char*)a.k + kvbase * (kF32In ? 4 : 2);
 #pragma unroll
-      for (int i = 0; i < KP; ++i) {
-        const int p = tid + i * kThreads;
-        const int t = max(kd_t[db][p / PPR], 0);
-        kst[i] = *(const u32x4v*)(kg + (size_t)t * D + (p % PPR) * 8);
-      }
+    for (int i = 0; i < KP; ++i) {
+      const int p = tid + i * kThreads;
+      const int t = max(kd_t[db][p / PPR], 0);
+      kst[i] = *(const u32x4v*)(kg + ((size_t)t * PPR + p % PPR) * 16);
+    }
+  };
+  auto load_v = [&](int db) {
+    if constexpr (!kF32In) {
+      const uint16_t* vg = (const uint16_t*)a.v + kvbase;
 #pragma unroll
       for (int i = 0; i < VT; ++i) {
         const int task = tid + i * kThreads;
@@ -278,27 +282,34 @@ __global__ __launch_bounds__(kThreads, 1) void masked_fwd_kernel(FwdArgs a) {
         vpair[2 * i + 1] = *(const u32x4v*)(vg + (size_t)t1 * D + 8 * oc);
       }
     } else {
-      const float* kg = (const float*)a.k + kvbase;
       const float* vg = (const float*)a.v + kvbase;
 #pragma unroll
       for (int i = 0; i < KP; ++i) {
         const int p = tid + i * kThreads;
         const int t = max(kd_t[db][p / PPR], 0);
-        const size_t off = (size_t)t * D + (p % PPR) * 4;
-        kst[i] = *(const u32x4v*)(kg + off);
-        vst4[i] = *(const u32x4v*)(vg + off);
+        vst4[i] = *(const u32x4v*)(vg + (size_t)t * D + (p % PPR) * 4);
       }
     }
   };
-  auto store_chunk = [&](int kb) {
-    if constexpr (!kF32In) {
-      uint16_t* kl = (uint16_t*)k_lds[kb];
-      uint16_t* vl = (uint16_t*)v_lds[kb];
+  auto store_k = [&](int kb) {
 #pragma unroll
-      for (int i = 0; i < KP; ++i) {
-        const int p = tid + i * kThreads;
-        *(u32x4v*)(kl + (p / PPR) * L::KS + (p % PPR) * 8) = kst[i];
+    for (int i = 0; i < KP; ++i) {
+      const int p = tid + i * kThreads;
+      const int key = p / PPR, piece = p % PPR;
+      if constexpr (!kF32In) {
+        *(u32x4v*)((uint16_t*)k_lds[kb] + key * L::KS + piece * 8) = kst[i];
+      } else {
+        float* kd = (float*)k_lds[kb] + key * L::KS + piece * 4;
+        kd[0] = __uint_as_float(kst[i].x);
+        kd[1] = __uint_as_float(kst[i].y);
+        kd[2] = __uint_as_float(kst[i].z);
+        kd[3] = __uint_as_float(kst[i].w);
       }
+    }
+  };
+  auto store_v = [&](int vb) {
+    if constexpr (!kF32In) {
+      uint16_t* vl = (uint16_t*)v_lds[vb];
       // V^T: column c = 16*ks + 8*hh + 4*a + r of LDS row d holds key
       // 16*ks + 8*a + 4*hh + r of the chunk (the P operand layout); a key pair
       // (2pr, 2pr+1) lands in two adjacent columns, so each dim is one word
@@ -306,7 +317,7 @@ __global__ __launch_bounds__(kThreads, 1) void masked_fwd_kernel(FwdArgs a) {
       for (int i = 0; i < VT; ++i) {
         const int task = tid + i * kThreads;
         if (NVT % kThreads != 0 && task >= NVT) break;
-        const int pr = task & 31, oc = task >> 5;   // pairs fastest: distinct LDS banks
+        const int pr = task & 31, oc = task >> 5;
         const int j0 = 2 * pr;
         const int c0 = 16 * (j0 >> 4) + 8 * ((j0 >> 2) & 1) + 4 * ((j0 >> 3) & 1) + (j0 & 3);
         const u32x4v x0 = vpair[2 * i], x1 = vpair[2 * i + 1];
@@ -318,41 +329,36 @@ __global__ __launch_bounds__(kThreads, 1) void masked_fwd_kernel(FwdArgs a) {
         }
       }
     } else {
-      float* kl = (float*)k_lds[kb];
-      float* vl = (float*)v_lds[kb];
+      float* vl = (float*)v_lds[vb];
 #pragma unroll
       for (int i = 0; i < KP; ++i) {
         const int p = tid + i * kThreads;
-        const int key = p / PPR, piece = p % PPR;
-        float* kd = kl + key * L::KS + piece * 4;
-        kd[0] = __uint_as_float(kst[i].x);
-        kd[1] = __uint_as_float(kst[i].y);
-        kd[2] = __uint_as_float(kst[i].z);
-        kd[3] = __uint_as_float(kst[i].w);
-        *(u32x4v*)(vl + key * L::VS + piece * 4) = vst4[i];
+        *(u32x4v*)(vl + (p / PPR) * L::VS + (p % PPR) * 4) = vst4[i];
       }
     }
   };
 
-  // ---- one chunk: S^T = K Q^T, mask, online softmax, O^T += V^T P^T
-  auto compute = [&](int kb, int db) {
-    f32x16 sacc[2];
+  // ---- S^T = K Q^T for one chunk (32 keys x 32 rows per block, 2 blocks)
+  auto qk = [&](int kb, f32x16 (&acc)[2]) {
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk) {
-      sacc[blk] = f32x16{};
+      acc[blk] = f32x16{};
       if constexpr (!kF32In) {
         const uint16_t* kl = (const uint16_t*)k_lds[kb] + (32 * blk + li) * L::KS + 8 * hh;
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks)
-          sacc[blk] = mfma32x32x16(as_bf16x8(*(const uint4*)(kl + 16 * ks)), qop[ks], sacc[blk]);
+          acc[blk] = mfma32x32x16(as_bf16x8(*(const uint4*)(kl + 16 * ks)), qop[ks], acc[blk]);
       } else {
         const float* kl = (const float*)k_lds[kb] + (32 * blk + li) * L::KS + hh;
 #pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) sacc[blk] = mfma32x32x2(kl[2 * ks], qop[ks], sacc[blk]);
+        for (int ks = 0; ks < NKS; ++ks) acc[blk] = mfma32x32x2(kl[2 * ks], qop[ks], acc[blk]);
       }
     }
-    // the mask, max and exps work in place on the accumulators (a separate
-    // copy of the scores was materialised with 32 moves per chunk)
+  };
+
+  // ---- mask and online-softmax bookkeeping of one chunk (in place on the
+  // scores); returns the exponent bias -m_run * c
+  auto softmax_pre = [&](f32x16 (&sc)[2], int db, auto&& before_rescale) -> float {
     const int mclass = __builtin_amdgcn_readfirstlane(s_flag[db]);   // uniform
     if (mclass == 1) {
 #pragma unroll
@@ -360,7 +366,7 @@ __global__ __launch_bounds__(kThreads, 1) void masked_fwd_kernel(FwdArgs a) {
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
           const int jj = 32 * blk + 8 * (e >> 2) + 4 * hh + (e & 3);
-          sacc[blk][e] = kd_r[db][jj] <= tau_q ? sacc[blk][e] : kNegInf;
+          sc[blk][e] = kd_r[db][jj] <= tau_q ? sc[blk][e] : kNegInf;
         }
     } else if (mclass == 2) {
       // branch-free: bitwise tests and a select per score (a short-circuit
@@ -373,43 +379,48 @@ __global__ __launch_bounds__(kThreads, 1) void masked_fwd_kernel(FwdArgs a) {
           const int t = kd_t[db][jj], rt = kd_r[db][jj];
           const bool keep = row_ok & (t >= 0) & (t <= q) &
                             ((t < s) | (t > q - w) | (rt <= tau_q));
-          sacc[blk][e] = keep ? sacc[blk][e] : kNegInf;
+          sc[blk][e] = keep ? sc[blk][e] : kNegInf;
         }
     }
-    float mc = sacc[0][0];
+    float mc = sc[0][0];
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) mc = fmaxf(mc, sacc[blk][e]);
+      for (int e = 0; e < 16; ++e) mc = fmaxf(mc, sc[blk][e]);
     mc = fmaxf(mc, __shfl_xor(mc, 32));
-    // online softmax with a lazily moved reference max (m_run, raw units): it
-    // moves only when some row's max grows by more than 2^8 in the exp2
-    // domain, so the O rescale is skipped on most chunks; scores stay <= 2^8
+    // lazily moved reference max (m_run, raw units): it moves only when some
+    // row's max grows by more than 2^8 in the exp2 domain, so the O rescale is
+    // skipped on most chunks; probabilities stay <= 2^8
     const float c = a.scale_log2;
     if (wave_ballot(mc * c > m_run * c + 8.0f) != 0) {
       const float m_new = fmaxf(m_run, mc);
       const float alpha = m_new == kNegInf ? 1.0f : exp2_fast((m_run - m_new) * c);
+      before_rescale();   // pending PV work joins O before it is rescaled
       l_run *= alpha;
       m_run = m_new;
 #pragma unroll
       for (int d2 = 0; d2 < D / 32; ++d2) oacc[d2] *= alpha;
     }
-    const float mb = m_run == kNegInf ? 0.0f : -m_run * c;
+    return m_run == kNegInf ? 0.0f : -m_run * c;
+  };
+  // ---- probabilities: exp2, row sum, bf16 pack (straight-line)
+  typedef typename std::conditional<kF32In, f32x16, bf16x8>::type POp;
+  constexpr int NP = kF32In ? 2 : 4;
+  auto softmax_exp = [&](f32x16 (&sc)[2], float mb, POp (&pk)[NP]) {
+    const float c = a.scale_log2;
     float ps = 0.0f;
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        sacc[blk][e] = exp2_fast(fmaf(sacc[blk][e], c, mb));
-        ps += sacc[blk][e];
+        sc[blk][e] = exp2_fast(fmaf(sc[blk][e], c, mb));
+        ps += sc[blk][e];
       }
     l_run += ps;
-
     if constexpr (!kF32In) {
-      bf16x8 pk[4];
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
-        const f32x16& src = sacc[ks >> 1];
+        const f32x16& src = sc[ks >> 1];
         const int o8 = 8 * (ks & 1);
         uint4 u;
         u.x = pack_bf16x2(src[o8 + 0], src[o8 + 1]);
@@ -418,9 +429,18 @@ __global__ __launch_bounds__(kThreads, 1) void masked_fwd_kernel(FwdArgs a) {
         u.w = pack_bf16x2(src[o8 + 6], src[o8 + 7]);
         pk[ks] = as_bf16x8(u);
       }
+    } else {
+      pk[0] = sc[0];
+      pk[1] = sc[1];
+    }
+  };
+
+  // ---- O^T += V^T P^T
+  auto pv = [&](int vb, const POp (&pk)[NP]) {
+    if constexpr (!kF32In) {
 #pragma unroll
       for (int d2 = 0; d2 < D / 32; ++d2) {
-        const uint16_t* vl = (const uint16_t*)v_lds[kb] + (32 * d2 + li) * L::VS + 8 * hh;
+        const uint16_t* vl = (const uint16_t*)v_lds[vb] + (32 * d2 + li) * L::VS + 8 * hh;
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks)
           oacc[d2] = mfma32x32x16(as_bf16x8(*(const uint4*)(vl + 16 * ks)), pk[ks], oacc[d2]);
@@ -428,41 +448,183 @@ __global__ __launch_bounds__(kThreads, 1) void masked_fwd_kernel(FwdArgs a) {
     } else {
 #pragma unroll
       for (int d2 = 0; d2 < D / 32; ++d2) {
-        const float* vl = (const float*)v_lds[kb] + 32 * d2 + li;
+        const float* vl = (const float*)v_lds[vb] + 32 * d2 + li;
 #pragma unroll
         for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
           for (int e = 0; e < 16; ++e) {
             const int key = 32 * blk + 8 * (e >> 2) + 4 * hh + (e & 3);
-            oacc[d2] = mfma32x32x2(vl[key * L::VS], sacc[blk][e], oacc[d2]);
+            oacc[d2] = mfma32x32x2(vl[key * L::VS], pk[blk][e], oacc[d2]);
           }
       }
     }
   };
 
-  // ---- software pipeline: descriptors two chunks ahead, K/V one chunk ahead
+  // ---- bf16: one fused region per chunk, in explicit issue order (a wave
+  // issues in order, so the overlap of the matrix and vector units is
+  // written out; a scheduling fence after each slot keeps the compiler from
+  // regrouping).  Slot i issues QK MFMA i of chunk c+1 (the two 32-key
+  // blocks alternate: independent accumulators), PV MFMA i of chunk c-1 (the
+  // output blocks rotate), and the exps of chunk c (32 / slots per slot);
+  // exps are summed and packed to bf16 one slot later, so nothing waits on an
+  // exp just issued; P(c-1) operand p is last read in the slot where P(c)
+  // operand p is still being built.  LDS operand reads run two slots ahead.
+  constexpr int NQM = 2 * NKS;          // QK MFMAs per chunk (= slots)
+  constexpr int NB = D / 32;            // output blocks of O^T
+  constexpr int NPV = NB * 4;           // PV MFMAs per chunk
+  constexpr int EPM = 32 / NQM;         // exps per slot
+  static_assert(kF32In || (NQM == NPV && NQM >= 4 && 32 % NQM == 0), "slot schedule");
+  auto region = [&](int kb, f32x16 (&nx)[2], f32x16 (&sc)[2], float mb, const POp (&pkp)[NP],
+                    POp (&pkc)[NP], int vb, float& ps, int kb_st, int vb_st) {
+    if constexpr (!kF32In) {
+      const uint16_t* kl = (const uint16_t*)k_lds[kb] + li * L::KS + 8 * hh;
+      const uint16_t* vl = (const uint16_t*)v_lds[vb] + li * L::VS + 8 * hh;
+      auto rk = [&](int i) {   // QK operand i: block i & 1, k-step i >> 1
+        return as_bf16x8(*(const uint4*)(kl + (i & 1) * 32 * L::KS + 16 * (i >> 1)));
+      };
+      auto rv = [&](int j) {   // PV operand j: output block j % NB, k-step j / NB
+        return as_bf16x8(*(const uint4*)(vl + (j % NB) * 32 * L::VS + 16 * (j / NB)));
+      };
+      auto pack = [&](int pidx) {
+        const f32x16& src = sc[pidx >> 1];
+        const int o8 = 8 * (pidx & 1);
+        uint4 u;
+        u.x = pack_bf16x2(src[o8 + 0], src[o8 + 1]);
+        u.y = pack_bf16x2(src[o8 + 2], src[o8 + 3]);
+        u.z = pack_bf16x2(src[o8 + 4], src[o8 + 5]);
+        u.w = pack_bf16x2(src[o8 + 6], src[o8 + 7]);
+        pkc[pidx] = as_bf16x8(u);
+      };
+      const float c = a.scale_log2;
+      bf16x8 kn = rk(0), vn = rv(0);   // operands one slot ahead
+      nx[0] = f32x16{};
+      nx[1] = f32x16{};
+      ps = 0.0f;
+#pragma unroll
+      for (int i = 0; i <= NQM; ++i) {
+        if (i < NQM) {
+          const bf16x8 ak = kn, av = vn;
+          if (i + 1 < NQM) {
+            kn = rk(i + 1);
+            vn = rv(i + 1);
+          }
+          nx[i & 1] = mfma32x32x16(ak, qop[i >> 1], nx[i & 1]);
+          oacc[i % NB] = mfma32x32x16(av, pkp[i / NB], oacc[i % NB]);
+#pragma unroll
+          for (int u = 0; u < EPM; ++u) {
+            const int e = EPM * i + u;
+            sc[e >> 4][e & 15] = exp2_fast(fmaf(sc[e >> 4][e & 15], c, mb));
+          }
+          if (i == NQM / 4) store_k(kb_st);
+          if (i == NQM / 2) store_v(vb_st);
+        }
+        if (i > 0) {
+#pragma unroll
+          for (int u = 0; u < EPM; ++u) {
+            const int e = EPM * (i - 1) + u;
+            ps += sc[e >> 4][e & 15];
+          }
+          if ((EPM * i) % 8 == 0) {   // elements 8p .. 8p+7 done
+            const int pidx = EPM * i / 8 - 1;
+            pack(pidx);
+            // used here: P(c) is consumed only in the next iteration, and the
+            // exps would otherwise be sunk past the region to the loop's end
+            asm volatile("" ::"v"(pkc[pidx]));
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      asm volatile("" ::"v"(ps));
+    }
+  };
+
   const int nchunk = (nk + kChunk - 1) / kChunk;
-  desc_load(0);
-  desc_store(0);
-  if (nchunk > 1) {
-    desc_load(kChunk);
-    desc_store(1);
+#pragma unroll
+  for (int j = 0; j < kDesc - 1; ++j) {   // every slot starts valid (tokens -1 past the end)
+    desc_load(j * kChunk);
+    desc_store(j);
   }
   __syncthreads();
-  if (nchunk > 0) {
-    load_chunk(0);
-    store_chunk(0);
-  }
-  __syncthreads();
-  for (int c = 0; c < nchunk; ++c) {
-    const int kb = c & 1, db = c % 3;
-    const bool has_next = c + 1 < nchunk;
-    if (has_next) load_chunk((c + 1) % 3);      // in flight during the math below
-    if (c + 2 < nchunk) desc_load((c + 2) * kChunk);
-    compute(kb, db);
-    if (has_next) store_chunk(kb ^ 1);
-    if (c + 2 < nchunk) desc_store((c + 2) % 3);
+  f32x16 sA[2], sB[2];
+  POp pkA[NP], pkB[NP];
+  if constexpr (!kF32In) {
+    // ---- bf16 software pipeline.  Entering iteration c >= 1: the scores of
+    // chunk c and P of chunk c-1 are in registers, K(c+1) and V(c-1) are in
+    // LDS, descriptors of c .. c+2 are published.  Per iteration: gathers of
+    // K(c+2) and V(c) and the descriptor reads of chunk c+3 are issued;
+    // mask / max of chunk c (a rescale of O first completes PV(c-1)); the
+    // fused region (QK c+1, exps c, PV c-1, LDS stores of K(c+2) and V(c));
+    // descriptors of chunk c+3; barrier.  Past the last chunk the gathers
+    // and QK run on descriptors of tokens -1 (row 0) and their results are
+    // unused, which keeps the region free of branches.  Unrolled by two so
+    // score and P buffers swap roles without register copies.
+    load_k(0);
+    store_k(0);
+    load_k(1);
+    store_k(1);
+    {   // V buffer 1 starts at zero: iteration 0 runs its PV slots on it
+      uint4* vz = (uint4*)v_lds[1];
+      for (int i = tid; i < (int)(L::vBytes / 16); i += kThreads) vz[i] = make_uint4(0, 0, 0, 0);
+    }
     __syncthreads();
+    qk(0, sA);
+    {   // iteration 0: no PV yet
+      load_k(2 % kDesc);
+      load_v(0);
+      desc_load(3 * kChunk);
+      const float mb = softmax_pre(sA, 0, [] {});
+#pragma unroll
+      for (int p = 0; p < NP; ++p) pkB[p] = POp{};
+      float ps;
+      region(1, sB, sA, mb, pkB, pkA, 1, ps, 0, 0);
+      l_run += ps;
+      desc_store(3 % kDesc);
+      __syncthreads();
+    }
+    auto step = [&](int c, f32x16 (&cur)[2], f32x16 (&nxt)[2], POp (&pkp)[NP], POp (&pkc)[NP]) {
+      load_k((c + 2) % kDesc);
+      load_v(c % kDesc);
+      desc_load((c + 3) * kChunk);
+      // a rescale first completes PV(c-1) and zeroes P(c-1), so the region's
+      // PV MFMAs then add exactly 0
+      const float mb = softmax_pre(cur, c % kDesc, [&] {
+        pv((c - 1) & 1, pkp);
+#pragma unroll
+        for (int p = 0; p < NP; ++p) pkp[p] = POp{};
+      });
+      float ps;
+      region((c + 1) & 1, nxt, cur, mb, pkp, pkc, (c - 1) & 1, ps, c & 1, c & 1);
+      l_run += ps;
+      desc_store((c + 3) % kDesc);
+      __syncthreads();
+    };
+    for (int c = 1; c < nchunk; c += 2) {
+      step(c, sB, sA, pkA, pkB);
+      if (c + 1 < nchunk) step(c + 1, sA, sB, pkB, pkA);
+    }
+    // PV of the last chunk (its P is in pkA when its index is even)
+    if ((nchunk - 1) & 1) pv((nchunk - 1) & 1, pkB);
+    else pv((nchunk - 1) & 1, pkA);
+  } else {
+    // ---- float32 inputs: K one chunk ahead, V staged with it, steps in order
+    load_k(0);
+    load_v(0);
+    store_k(0);
+    store_v(0);
+    __syncthreads();
+    for (int c = 0; c < nchunk; ++c) {
+      load_k((c + 1) % kDesc);
+      load_v((c + 1) % kDesc);
+      desc_load((c + 3) * kChunk);
+      qk(c & 1, sA);
+      const float mb = softmax_pre(sA, c % kDesc, [] {});
+      softmax_exp(sA, mb, pkA);
+      pv(c & 1, pkA);
+      store_k((c + 1) & 1);
+      store_v((c + 1) & 1);
+      desc_store((c + 3) % kDesc);
+      __syncthreads();
+    }
   }
 
   // ---- epilogue: O = acc / l, LSE = (m + log2 l) ln 2
