@@ -13,13 +13,16 @@
 //
 // Cutoffs: the sequential Fenwick-tree scan is replaced by independent chunks
 // of queries.  A workgroup builds an S-bit LDS bitmap of the ranks of E(q0) for
-// its first query q0, selects the k-th set bit with a block prefix count, then
-// steps through the chunk: each step adds the rank of the newcomer q - w; while
-// fewer than k tokens are eligible the cutoff is open (INT32_MAX); when the
-// k-th arrives the cutoff is the highest set bit; afterwards a newcomer ranked
-// below the cutoff moves it to the next lower set bit (inserting one element
-// below the k-th order statistic moves it to its predecessor), found with a
-// wavefront ballot over 64 bitmap words at a time.
+// its first query q0 (ballots over the rank order), selects the k-th set bit
+// with a block prefix count, and then either computes every later query of
+// the chunk in parallel from a small candidate set (when k tokens are already
+// eligible at q0; see tau_kernel) or, in the early chunks, steps through it:
+// each step adds the rank of the newcomer q - w; while fewer than k tokens are
+// eligible the cutoff is open (INT32_MAX); when the k-th arrives the cutoff is
+// the highest set bit; afterwards a newcomer ranked below the cutoff moves it
+// to the next lower set bit (inserting one element below the k-th order
+// statistic moves it to its predecessor), found with a wavefront ballot over
+// 64 bitmap words at a time.
 #include "kvpop_device.h"
 #include "kvpop_internal.h"
 
@@ -33,7 +36,7 @@ constexpr int kRadix = 256;
 
 int sort_tiles(int S) { return (S + kSortTile - 1) / kSortTile; }
 
-int tau_chunk(int S) { return S <= 32768 ? 256 : 512; }
+int tau_chunk(int S) { return S <= 16384 ? 64 : S <= 65536 ? 128 : 256; }
 
 // ---------------------------------------------------------------- sort
 template <bool kFirst>
@@ -58,30 +61,6 @@ __global__ __launch_bounds__(kSortThreads) void radix_hist_kernel(
     hist[((size_t)seg * kRadix + dg) * ntiles + tile] = h[dg];
 }
 
-// Exclusive prefix of one segment's histogram in (digit, tile) order.
-__global__ __launch_bounds__(kRadix) void radix_scan_kernel(uint32_t* __restrict__ hist,
-                                                            int ntiles) {
-  __shared__ uint32_t tot[kRadix];
-  const int seg = blockIdx.x, dg = threadIdx.x;
-  uint32_t* row = hist + ((size_t)seg * kRadix + dg) * ntiles;
-  uint32_t sum = 0;
-  for (int t = 0; t < ntiles; ++t) sum += row[t];
-  tot[dg] = sum;
-  __syncthreads();
-  for (int off = 1; off < kRadix; off <<= 1) {
-    const uint32_t add = dg >= off ? tot[dg - off] : 0u;
-    __syncthreads();
-    tot[dg] += add;
-    __syncthreads();
-  }
-  uint32_t run = tot[dg] - sum;
-  for (int t = 0; t < ntiles; ++t) {
-    const uint32_t c = row[t];
-    row[t] = run;
-    run += c;
-  }
-}
-
 // Mask of the lanes holding the same 8-bit digit (valid lanes only).
 __device__ __forceinline__ uint64_t same_digit_lanes(uint32_t dig, bool valid) {
   uint64_t m = wave_ballot(valid);
@@ -94,12 +73,18 @@ __device__ __forceinline__ uint64_t same_digit_lanes(uint32_t dig, bool valid) {
   return m;
 }
 
-template <bool kFirst>
+// One pass of the stable scatter.  Every workgroup derives its own write
+// offsets from the segment's per-tile digit counts (exclusive prefix over
+// digits of the totals, plus the counts of the earlier tiles); the last pass
+// writes rank[token] = place and order[place] = token instead of keys.
+template <bool kFirst, bool kLast>
 __global__ __launch_bounds__(kSortThreads) void radix_scatter_kernel(
     const float* __restrict__ prio, const uint32_t* __restrict__ keys_in,
     const int* __restrict__ vals_in, uint32_t* __restrict__ keys_out, int* __restrict__ vals_out,
-    const uint32_t* __restrict__ hist, int S, int ntiles, int shift) {
+    int* __restrict__ rank_out, const uint32_t* __restrict__ hist, int S, int ntiles, int shift) {
+  static_assert(kSortThreads == kRadix, "one thread per digit");
   __shared__ uint32_t offs[4][kRadix];   // per-wave running write offset of each digit
+  __shared__ uint32_t dsum[kRadix];
   const int tile = blockIdx.x, seg = blockIdx.y;
   const int lane = lane_id(), wave = threadIdx.x >> 6;
   for (int i = threadIdx.x; i < 4 * kRadix; i += kSortThreads) (&offs[0][0])[i] = 0;
@@ -128,9 +113,25 @@ __global__ __launch_bounds__(kSortThreads) void radix_scatter_kernel(
     const uint64_t peers = same_digit_lanes(dig, valid);
     if (valid && lane == __builtin_ctzll(peers)) offs[wave][dig] += (uint32_t)__builtin_popcountll(peers);
   }
-  __syncthreads();
-  for (int dg = threadIdx.x; dg < kRadix; dg += kSortThreads) {
-    uint32_t run = hist[((size_t)seg * kRadix + dg) * ntiles + tile];
+  {
+    // this tile's first write position of each digit
+    const int dg = threadIdx.x;
+    const uint32_t* row = hist + ((size_t)seg * kRadix + dg) * ntiles;
+    uint32_t tot = 0, before = 0;
+    for (int t = 0; t < ntiles; ++t) {
+      const uint32_t c = row[t];
+      before += t < tile ? c : 0u;
+      tot += c;
+    }
+    dsum[dg] = tot;
+    __syncthreads();
+    for (int off = 1; off < kRadix; off <<= 1) {
+      const uint32_t add = dg >= off ? dsum[dg - off] : 0u;
+      __syncthreads();
+      dsum[dg] += add;
+      __syncthreads();
+    }
+    uint32_t run = dsum[dg] - tot + before;
     for (int wv = 0; wv < 4; ++wv) {
       const uint32_t c = offs[wv][dg];
       offs[wv][dg] = run;
@@ -149,8 +150,13 @@ __global__ __launch_bounds__(kSortThreads) void radix_scatter_kernel(
     if (valid) {
       start = offs[wave][dig];
       const uint32_t pos = start + (uint32_t)lanes_below(peers);
-      keys_out[base + pos] = key[i];
-      vals_out[base + pos] = val[i];
+      if constexpr (kLast) {
+        rank_out[base + val[i]] = (int)pos;
+        vals_out[base + pos] = val[i];
+      } else {
+        keys_out[base + pos] = key[i];
+        vals_out[base + pos] = val[i];
+      }
     }
     wave_lds_fence();
     if (valid && lane == __builtin_ctzll(peers))
@@ -159,16 +165,6 @@ __global__ __launch_bounds__(kSortThreads) void radix_scatter_kernel(
   }
 }
 
-__global__ __launch_bounds__(256) void rank_from_order_kernel(const int* __restrict__ order,
-                                                              int* __restrict__ rank, int S,
-                                                              long long total) {
-  const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
-  if (i >= total) return;
-  const long long seg = i / S;
-  const int place = (int)(i - seg * S);
-  const int t = order[i];
-  if ((unsigned)t < (unsigned)S) rank[seg * S + t] = place;
-}
 
 // ---------------------------------------------------------------- cutoffs
 // Highest set bit of the bitmap with index < x (-1 if none).  Called by all 64
@@ -192,73 +188,200 @@ __device__ int highest_bit_below(const uint32_t* bm, int x, int lane) {
   return -1;
 }
 
+// Block-wide inclusive prefix sum of v (one value per thread, 256 threads).
+__device__ int block_scan_incl(int v, int* sc) {
+  const int tid = threadIdx.x;
+  sc[tid] = v;
+  __syncthreads();
+  for (int off = 1; off < 256; off <<= 1) {
+    const int add = tid >= off ? sc[tid - off] : 0;
+    __syncthreads();
+    sc[tid] += add;
+    __syncthreads();
+  }
+  const int r = sc[tid];
+  __syncthreads();
+  return r;
+}
+
+// One workgroup per chunk of queries [q0, q0 + nq) of one segment.
+//   E(q0) bitmap: bit r set iff the token of rank r (order[r]) lies in
+//   [s, q0 - w]; built with wave ballots over the rank order (no atomics).
+//   tau0 = k-th smallest set bit (a block prefix of word popcounts).
+// If |E(q0)| >= k every later query of the chunk is computed in parallel:
+// a newcomer u = q - w matters only if its rank is below tau0 (otherwise the
+// k smallest do not change); with J such newcomers in the chunk, T = the
+// min(J+1, k) largest of the k smallest ranks of E(q0) and N = the J
+// newcomers, tau_q is the (j_q + 1)-th largest of the candidates present at q
+// (T always, a newcomer from its arrival on), j_q = newcomers arrived by q.
+// (Each such arrival moves the k-th order statistic down by one place among
+// the present candidates, and it never falls below T's smallest.)
+// Otherwise (early chunks, fewer than k eligible at q0) one wave steps
+// through the chunk: while fewer than k tokens are eligible the cutoff is
+// open; when the k-th arrives it is the highest set bit; afterwards a
+// newcomer ranked below the cutoff moves it to the next lower set bit.
 __global__ __launch_bounds__(256) void tau_kernel(const int* __restrict__ rank,
+                                                  const int* __restrict__ order,
                                                   int* __restrict__ tau, int S, int s, int w,
                                                   int k, int chunk) {
   extern __shared__ uint32_t smem[];
-  __shared__ int cnt[256];
-  __shared__ int s_tau0;
+  __shared__ int sc[256];
+  __shared__ int s_tau0, s_J, s_nT;
   const int nwords = (S + 31) >> 5;
   uint32_t* bitmap = smem;
-  int* newr = (int*)(smem + nwords);        // rank of the newcomer of each chunk row
+  int* newr = (int*)(smem + nwords);        // rank of the newcomer at each chunk position
   int* taus = newr + chunk;
+  int* jpre = taus + chunk;                 // newcomers below tau0 arrived by each position
+  int* Tv = jpre + chunk;                   // T ascending (<= chunk + 1 entries)
+  int* Nv = Tv + chunk + 1;                 // N ranks (arrival order)
+  int* Na = Nv + chunk;                     // N arrival positions
+  int* Cv = Na + chunk;                     // candidates, descending rank (<= 2 chunk + 1)
+  int* Ca = Cv + 2 * chunk + 1;             // their arrival positions (0 for T)
   const int tid = threadIdx.x, lane = lane_id(), wave = wave_id();
   const int seg = blockIdx.y;
   const int q0 = blockIdx.x * chunk;
   const int nq = min(chunk, S - q0);
   const int* rk = rank + (size_t)seg * S;
+  const int* ord = order + (size_t)seg * S;
   int* out = tau + (size_t)seg * S + q0;
   if (k == 0) {
     for (int i = tid; i < nq; i += 256) out[i] = -1;
     return;
   }
   if (tid == 0) s_tau0 = kInt32Max;   // stays open unless the k-th bit is found
-  for (int i = tid; i < nwords; i += 256) bitmap[i] = 0u;
   for (int i = tid; i < nq; i += 256) {
     const int t = q0 + i - w;
     const int r = t >= s ? rk[t] : -1;
     newr[i] = (unsigned)r < (unsigned)S ? r : -1;
   }
-  __syncthreads();
   const int e_hi = q0 - w;                  // E(q0) = [s, e_hi]
   const int n0 = max(0, e_hi - s + 1);
-  for (int t = s + tid; t <= e_hi; t += 256) {
-    const int r = rk[t];
-    if ((unsigned)r < (unsigned)S) atomicOr(&bitmap[r >> 5], 1u << (r & 31));
-  }
-  __syncthreads();
-  if (n0 >= k) {
-    // k-th smallest set bit: per-thread word range, block prefix of counts
-    const int wpt = (nwords + 255) / 256;
-    const int w0 = tid * wpt, w1 = min(nwords, w0 + wpt);
-    int c = 0;
-    for (int i = w0; i < w1; ++i) c += __builtin_popcount(bitmap[i]);
-    cnt[tid] = c;
-    __syncthreads();
-    for (int off = 1; off < 256; off <<= 1) {
-      const int add = tid >= off ? cnt[tid - off] : 0;
-      __syncthreads();
-      cnt[tid] += add;
-      __syncthreads();
+  constexpr int kU = 8;   // rank-order loads in flight per lane
+  for (int base = wave * 64 * kU; base < S; base += 256 * kU) {
+    int tv[kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int r = base + 64 * u + lane;
+      tv[u] = r < S ? ord[r] : -1;
     }
-    const int excl = cnt[tid] - c;
-    if (excl < k && excl + c >= k) {
-      int need = k - excl;
-      for (int i = w0; i < w1; ++i) {
-        uint32_t wd = bitmap[i];
-        const int pc = __builtin_popcount(wd);
-        if (need <= pc) {
-          for (int j = 1; j < need; ++j) wd &= wd - 1u;
-          s_tau0 = (i << 5) + __builtin_ctz(wd);
-          break;
-        }
-        need -= pc;
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int r0 = base + 64 * u;
+      const uint64_t m = wave_ballot(tv[u] >= s && tv[u] <= e_hi);
+      if (lane == 0 && r0 < S) {
+        bitmap[r0 >> 5] = (uint32_t)m;
+        if ((r0 >> 5) + 1 < nwords) bitmap[(r0 >> 5) + 1] = (uint32_t)(m >> 32);
       }
     }
   }
   __syncthreads();
-  if (wave == 0) {
-    int tc = s_tau0;
+  // per-thread word range and its popcount prefix (reused for T below)
+  const int wpt = (nwords + 255) / 256;
+  const int w0 = min(nwords, tid * wpt), w1 = min(nwords, w0 + wpt);
+  int c = 0;
+  for (int i = w0; i < w1; ++i) c += __builtin_popcount(bitmap[i]);
+  const int excl = block_scan_incl(c, sc) - c;
+  if (n0 >= k && excl < k && excl + c >= k) {
+    int need = k - excl;
+    for (int i = w0; i < w1; ++i) {
+      uint32_t wd = bitmap[i];
+      const int pc = __builtin_popcount(wd);
+      if (need <= pc) {
+        for (int j = 1; j < need; ++j) wd &= wd - 1u;
+        s_tau0 = (i << 5) + __builtin_ctz(wd);
+        break;
+      }
+      need -= pc;
+    }
+  }
+  __syncthreads();
+  const int tau0 = s_tau0;
+
+  if (n0 >= k) {
+    // ---- parallel path
+    const int ppt = (nq + 255) / 256;           // positions per thread (contiguous)
+    const int p0 = min(nq, tid * ppt), p1 = min(nq, p0 + ppt);
+    int mine = 0;
+    for (int i = p0; i < p1; ++i) mine += (i > 0) & (newr[i] >= 0) & (newr[i] < tau0);
+    const int incl = block_scan_incl(mine, sc);
+    int run = incl - mine;
+    for (int i = p0; i < p1; ++i) {
+      const bool mt = (i > 0) & (newr[i] >= 0) & (newr[i] < tau0);
+      if (mt) {
+        Nv[run] = newr[i];
+        Na[run] = i;
+      }
+      run += mt;
+      jpre[i] = run;
+    }
+    if (tid == 255) {
+      s_J = incl;
+      s_nT = min(incl + 1, k);
+    }
+    __syncthreads();
+    const int J = s_J, nT = s_nT;
+    // T: set bits with global index in [k - nT, k - 1], ascending
+    if (excl < k && excl + c > k - nT) {
+      int g = excl;
+      for (int i = w0; i < w1 && g < k; ++i) {
+        uint32_t wd = bitmap[i];
+        while (wd && g < k) {
+          const int b = __builtin_ctz(wd);
+          wd &= wd - 1u;
+          if (g >= k - nT) Tv[g - (k - nT)] = (i << 5) + b;
+          ++g;
+        }
+      }
+    }
+    __syncthreads();
+    // candidate positions in descending rank order (ranks are distinct)
+    for (int a = tid; a < nT + J; a += 256) {
+      int v, arr;
+      if (a < nT) {
+        v = Tv[a];
+        arr = 0;
+      } else {
+        v = Nv[a - nT];
+        arr = Na[a - nT];
+      }
+      int above = 0;
+      for (int b = 0; b < J; ++b) above += Nv[b] > v;
+      if (a < nT) {
+        above += nT - 1 - a;
+      } else {
+        for (int b = 0; b < nT; ++b) above += Tv[b] > v;
+      }
+      Cv[above] = v;
+      Ca[above] = arr;
+    }
+    __syncthreads();
+    // each wave steps through the candidates in lockstep (broadcast reads
+    // whose addresses do not depend on the data), 8 at a time, until every
+    // lane has found its (j + 1)-th present candidate
+    const int nC = nT + J;
+    for (int ib = wave * 64; ib < nq; ib += 256) {
+      const int i = ib + lane;
+      const int need = i < nq ? jpre[i] + 1 : 0;
+      int cnt = 0, t = tau0;
+      bool done = i >= nq;
+      for (int a0 = 0; a0 < nC; a0 += 8) {
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int a = a0 + u;
+          const bool pres = a < nC && Ca[a] <= i;
+          cnt += pres;
+          if (!done && pres && cnt == need) {
+            t = Cv[a];
+            done = true;
+          }
+        }
+        if (wave_ballot(!done) == 0) break;
+      }
+      if (i < nq) taus[i] = t;
+    }
+  } else if (wave == 0) {
+    // ---- sequential path (fewer than k eligible at q0)
+    int tc = tau0;
     int n = n0;
     if (lane == 0) taus[0] = n < k ? kInt32Max : tc;
     for (int i = 1; i < nq; ++i) {
@@ -309,29 +432,27 @@ hipError_t launch_thresholds(const Dims& d, const float* prio, int* rank, int* t
     if (pass == 0) {
       hipLaunchKernelGGL(radix_hist_kernel<true>, g, dim3(kSortThreads), 0, st, prio, nullptr, S,
                          ntiles, shift, hist);
+      hipLaunchKernelGGL((radix_scatter_kernel<true, false>), g, dim3(kSortThreads), 0, st, prio,
+                         nullptr, nullptr, kout, vout, nullptr, hist, S, ntiles, shift);
     } else {
       hipLaunchKernelGGL(radix_hist_kernel<false>, g, dim3(kSortThreads), 0, st, nullptr, kin, S,
                          ntiles, shift, hist);
-    }
-    hipLaunchKernelGGL(radix_scan_kernel, dim3(nseg), dim3(kRadix), 0, st, hist, ntiles);
-    if (pass == 0) {
-      hipLaunchKernelGGL(radix_scatter_kernel<true>, g, dim3(kSortThreads), 0, st, prio, nullptr,
-                         nullptr, kout, vout, hist, S, ntiles, shift);
-    } else {
-      hipLaunchKernelGGL(radix_scatter_kernel<false>, g, dim3(kSortThreads), 0, st, nullptr, kin,
-                         vin, kout, vout, hist, S, ntiles, shift);
+      if (pass < 3)
+        hipLaunchKernelGGL((radix_scatter_kernel<false, false>), g, dim3(kSortThreads), 0, st,
+                           nullptr, kin, vin, kout, vout, nullptr, hist, S, ntiles, shift);
+      else   // last pass: rank and the rank order (the token at each place)
+        hipLaunchKernelGGL((radix_scatter_kernel<false, true>), g, dim3(kSortThreads), 0, st,
+                           nullptr, kin, vin, nullptr, vout, rank, hist, S, ntiles, shift);
     }
     kin = kout;
     vin = vout;
   }
-  const long long total = (long long)n;
-  hipLaunchKernelGGL(rank_from_order_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0,
-                     st, vin, rank, S, total);
   const int chunk = tau_chunk(S);
   const int nchunks = (S + chunk - 1) / chunk;
-  const size_t lds = (size_t)((S + 31) >> 5) * 4 + (size_t)chunk * 8;
-  hipLaunchKernelGGL(tau_kernel, dim3(nchunks, nseg), dim3(256), lds, st, rank, tau, S, d.s, d.w,
-                     d.k, chunk);
+  // bitmap + newr, taus, jpre, T, N (rank, arrival), candidates (rank, arrival)
+  const size_t lds = (size_t)((S + 31) >> 5) * 4 + (size_t)(10 * chunk + 3) * 4;
+  hipLaunchKernelGGL(tau_kernel, dim3(nchunks, nseg), dim3(256), lds, st, rank, vin, tau, S,
+                     d.s, d.w, d.k, chunk);
   return hipGetLastError();
 }
 
