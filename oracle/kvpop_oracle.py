@@ -37,6 +37,9 @@ Readings of points the pages leave open (each also listed in the design notes):
      held) or replaces the worst held long-range token iff its priority is
      strictly larger (worst = lowest priority, ties: highest position), else is
      dropped; then the step attends.
+  R10 the target score's N_t is the number of future queries S - t - w; where
+     there are none (t + w > S - 1) the future mass is 0 and the score is
+     log(eps).
 """
 from __future__ import annotations
 
@@ -287,6 +290,37 @@ def future_target_eq8(q, k, lse, w, scale=0.0, ts=None):
                 m = x.max()
                 out[bi, hq, j] = m + math.log(np.exp(x - m).sum())
     return out
+
+
+def target_score(q, k, lse, w, eps, scale=0.0, block=256):
+    """Target score per KV head ([Notes] §2.2): the future mass of query group g,
+    m_t = (1/N_t) sum_{d=t+w}^{S-1} A_{d,t} with A the dense causal attention
+    probabilities exp(l(d,t) - LSE_d) and N_t = S - t - w future queries, is
+    averaged over the G query heads of the KV head and logged with eps:
+    r_{h,t} = log(eps + (1/G) sum_g m_t^{(h,g)}).  Where N_t = 0 the mass is 0
+    (reading R10).  q [b, Hq, S, D], k [b, Hkv, S, D], lse [b, Hq, S] ->
+    r [b, Hkv, S] (float64)."""
+    b, Hq, S, D = q.shape
+    Hkv = k.shape[1]
+    G = Hq // Hkv
+    sc = default_scale(D, scale)
+    t = np.arange(S)
+    n_t = S - t - w
+    mass = np.zeros((b, Hkv, S))
+    for bi in range(b):
+        for hq in range(Hq):
+            K = k[bi, hq // G].astype(np.float64)
+            col = np.zeros(S)
+            for a in range(0, S, block):
+                ds = np.arange(a, min(S, a + block))
+                A = np.exp(sc * (q[bi, hq, ds].astype(np.float64) @ K.T)
+                           - lse[bi, hq, ds].astype(np.float64)[:, None])
+                col += np.where(t[None, :] <= ds[:, None] - w, A, 0.0).sum(axis=0)
+            with np.errstate(divide="ignore", invalid="ignore"):
+                m = np.where(n_t > 0, col / np.maximum(n_t, 1), 0.0)
+            mass[bi, hq // G] += m / G
+    with np.errstate(divide="ignore"):
+        return np.log(eps + mass)
 
 
 # --------------------------------------------------------------------------
