@@ -20,5 +20,7 @@ from .binding import (  # noqa: F401
     future_target,
     decode_step,
     new_decode_cache,
+    cache_from_prefill,
+    target_score,
     EXPORTED_SYMBOLS,
 )

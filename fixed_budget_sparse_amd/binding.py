@@ -19,6 +19,7 @@ _LIB_PATH = os.path.join(_HERE, "libkvpop.so")
 
 KVPOP_BF16, KVPOP_F32 = 0, 1
 CALL_THRESHOLDS, CALL_MASKED_FWD, CALL_FUTURE_TARGET, CALL_DECODE = 0, 1, 2, 3
+CALL_CACHE_FROM_PREFILL, CALL_TARGET_SCORE = 4, 5
 
 EXPORTED_SYMBOLS = (
     "kvpop_workspace_size",
@@ -26,6 +27,8 @@ EXPORTED_SYMBOLS = (
     "kvpop_masked_attn_fwd",
     "kvpop_future_target",
     "kvpop_decode_step",
+    "kvpop_cache_from_prefill",
+    "kvpop_target_score",
     "kvpop_status_string",
     "kvpop_abi_version",
 )
@@ -72,8 +75,10 @@ def lib() -> ctypes.CDLL:
         L.kvpop_future_target.argtypes = [P, vp, vp, vp, vp, vp, sz, vp]
         L.kvpop_decode_step.argtypes = [P, ctypes.POINTER(_Cache), vp, vp, vp, vp, vp, vp, vp,
                                         vp, sz, vp]
+        L.kvpop_cache_from_prefill.argtypes = [P, ctypes.POINTER(_Cache), vp, vp, vp, vp, vp, vp]
+        L.kvpop_target_score.argtypes = [P, vp, ctypes.c_float, vp, vp]
         for f in ("kvpop_thresholds", "kvpop_masked_attn_fwd", "kvpop_future_target",
-                  "kvpop_decode_step"):
+                  "kvpop_decode_step", "kvpop_cache_from_prefill", "kvpop_target_score"):
             getattr(L, f).restype = ctypes.c_int
         L.kvpop_status_string.argtypes = [ctypes.c_int]
         L.kvpop_status_string.restype = ctypes.c_char_p
@@ -289,3 +294,45 @@ def decode_step(cache: DecodeCache, pos: torch.Tensor, q: torch.Tensor, k_new: t
                                     _vp(k_new), _vp(v_new), _vp(prio_leaving), _vp(o), _vp(lse),
                                     _vp(ws), n, _stream(dev)), "kvpop_decode_step")
     return o, lse
+
+
+def cache_from_prefill(cache: DecodeCache, k: torch.Tensor, v: torch.Tensor, prio: torch.Tensor,
+                       rank: torch.Tensor, tau: torch.Tensor, sink: int, window: int,
+                       topk: int) -> DecodeCache:
+    """Fill `cache` with the kept set of the prompt's last row (see
+    kvpop_cache_from_prefill); decoding then continues at p = S."""
+    b, hkv, S, D = k.shape
+    dev = k.device
+    Bc = sink + window + topk
+    _need(k, "k", (b, hkv, S, D), k.dtype, dev)
+    _need(v, "v", (b, hkv, S, D), k.dtype, dev)
+    _need(prio, "prio", (b, hkv, S), torch.float32, dev)
+    _need(rank, "rank", (b, hkv, S), torch.int32, dev)
+    _need(tau, "tau", (b, hkv, S), torch.int32, dev)
+    _need(cache.k, "cache.k", (b, hkv, Bc, D), k.dtype, dev)
+    _need(cache.v, "cache.v", (b, hkv, Bc, D), k.dtype, dev)
+    _need(cache.slot_pos, "cache.slot_pos", (b, hkv, Bc), torch.int32, dev)
+    _need(cache.slot_prio, "cache.slot_prio", (b, hkv, Bc), torch.float32, dev)
+    _need(cache.ring, "cache.ring", (b, hkv, window), torch.int32, dev)
+    pr = Problem(b, hkv, hkv, S, D, sink, window, topk, 0.0, _dtype_code(k.dtype), 0)
+    c, cc = pr.c(), cache.c()
+    _status(lib().kvpop_cache_from_prefill(ctypes.byref(c), ctypes.byref(cc), _vp(k), _vp(v),
+                                           _vp(prio), _vp(rank), _vp(tau), _stream(dev)),
+            "kvpop_cache_from_prefill")
+    return cache
+
+
+def target_score(target: torch.Tensor, n_kv_heads: int, window: int, eps: float,
+                 score: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Aggregated target score [b, Hkv, S] from the per-query-head future
+    target [b, Hq, S] (see kvpop_target_score)."""
+    b, hq, S = target.shape
+    dev = target.device
+    _need(target, "target", (b, hq, S), torch.float32, dev)
+    score = torch.empty((b, n_kv_heads, S), dtype=torch.float32, device=dev) if score is None else score
+    _need(score, "score", (b, n_kv_heads, S), torch.float32, dev)
+    pr = Problem(b, hq, n_kv_heads, S, 128, 0, window, 0, 0.0, 0, 0)
+    c = pr.c()
+    _status(lib().kvpop_target_score(ctypes.byref(c), _vp(target), float(eps), _vp(score),
+                                     _stream(dev)), "kvpop_target_score")
+    return score

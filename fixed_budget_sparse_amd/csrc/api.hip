@@ -28,13 +28,14 @@ kvpop_status make_dims(int32_t call, const kvpop_problem* pr, Dims* d) {
   if (!dtype_ok(pr->qkv_dtype) || !dtype_ok(pr->out_dtype)) return KVPOP_ERR_ARG;
   if (!(pr->softmax_scale == pr->softmax_scale) || isinf(pr->softmax_scale)) return KVPOP_ERR_ARG;
   const int G = pr->n_q_heads / pr->n_kv_heads;
-  if (call != KVPOP_CALL_THRESHOLDS) {
+  if (call != KVPOP_CALL_THRESHOLDS && call != KVPOP_CALL_TARGET_SCORE) {
     if (pr->head_dim != 64 && pr->head_dim != 128) return KVPOP_ERR_UNSUPPORTED;
     if (G > 32) return KVPOP_ERR_UNSUPPORTED;
   }
   if (call == KVPOP_CALL_DECODE) {
     if (pr->window < 1 || budget < 1) return KVPOP_ERR_ARG;
   } else {
+    if (call == KVPOP_CALL_CACHE_FROM_PREFILL && pr->window < 1) return KVPOP_ERR_ARG;
     if (pr->seq_len < 1) return KVPOP_ERR_ARG;
     if (pr->seq_len > kMaxSeq) return KVPOP_ERR_UNSUPPORTED;
     if (call == KVPOP_CALL_MASKED_FWD && pr->window < 1) return KVPOP_ERR_ARG;
@@ -136,6 +137,31 @@ KVPOP_EXPORT kvpop_status kvpop_decode_step(const kvpop_problem* pr, const kvpop
   if (st != KVPOP_OK) return st;
   kvpop::CacheArgs c{cache->k, cache->v, cache->slot_pos, cache->slot_prio, cache->ring};
   return finish(kvpop::launch_decode(d, c, pos, q, k_new, v_new, prio_leaving, o, lse, ws, stream));
+}
+
+KVPOP_EXPORT kvpop_status kvpop_cache_from_prefill(const kvpop_problem* pr,
+                                                   const kvpop_cache* cache, const void* k,
+                                                   const void* v, const float* prio,
+                                                   const int32_t* rank, const int32_t* tau,
+                                                   hipStream_t stream) {
+  Dims d;
+  kvpop_status st = make_dims(KVPOP_CALL_CACHE_FROM_PREFILL, pr, &d);
+  if (st != KVPOP_OK) return st;
+  if (!cache || !cache->k || !cache->v || !cache->slot_pos || !cache->slot_prio || !cache->ring)
+    return KVPOP_ERR_ARG;
+  if (!k || !v || !prio || !rank || !tau) return KVPOP_ERR_ARG;
+  kvpop::CacheArgs c{cache->k, cache->v, cache->slot_pos, cache->slot_prio, cache->ring};
+  return finish(kvpop::launch_cache_from_prefill(d, c, k, v, prio, rank, tau, stream));
+}
+
+KVPOP_EXPORT kvpop_status kvpop_target_score(const kvpop_problem* pr, const float* target,
+                                             float eps, float* score, hipStream_t stream) {
+  Dims d;
+  kvpop_status st = make_dims(KVPOP_CALL_TARGET_SCORE, pr, &d);
+  if (st != KVPOP_OK) return st;
+  if (!target || !score) return KVPOP_ERR_ARG;
+  if (!(eps >= 0.0f) || isinf(eps)) return KVPOP_ERR_ARG;
+  return finish(kvpop::launch_target_score(d, target, eps, score, stream));
 }
 
 KVPOP_EXPORT const char* kvpop_status_string(kvpop_status st) {

@@ -356,4 +356,41 @@ hipError_t launch_future_target(const Dims& d, const void* q, const void* k, con
   return hipGetLastError();
 }
 
+// Target score ([Notes] §2.2): r_{h,t} = log(eps + (1/G) sum_g m_t^{(h,g)}) with
+// m_t = exp(target_g[t]) / N_t, N_t = S - t - w future queries (the mean is 0
+// where there are none).  One thread per (b, h, t); every exponent
+// target_g[t] - ln N_t is <= 0 for the dense LSE (a probability sum over N_t
+// queries is at most N_t), so the sum needs no maximum.
+namespace {
+__global__ __launch_bounds__(256) void target_score_kernel(const float* __restrict__ target,
+                                                           float* __restrict__ score, int Hq,
+                                                           int Hkv, int S, int w, float eps,
+                                                           long long total) {
+  const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (i >= total) return;
+  const int G = Hq / Hkv;
+  const long long bh = i / S;
+  const int t = (int)(i - bh * S);
+  const int b = (int)(bh / Hkv), h = (int)(bh % Hkv);
+  const int nt = S - t - w;
+  float mean = 0.0f;
+  if (nt > 0) {
+    const float lnn = logf((float)nt);
+    float acc = 0.0f;
+    for (int g = 0; g < G; ++g)
+      acc += expf(target[((size_t)b * Hq + (size_t)h * G + g) * S + t] - lnn);
+    mean = acc / (float)G;
+  }
+  score[i] = logf(eps + mean);
+}
+}  // namespace
+
+hipError_t launch_target_score(const Dims& d, const float* target, float eps, float* score,
+                               hipStream_t st) {
+  const long long total = (long long)d.b * d.Hkv * d.S;
+  hipLaunchKernelGGL(target_score_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, st,
+                     target, score, d.Hq, d.Hkv, d.S, d.w, eps, total);
+  return hipGetLastError();
+}
+
 }  // namespace kvpop

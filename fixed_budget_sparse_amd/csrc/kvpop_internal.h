@@ -49,4 +49,10 @@ hipError_t launch_decode(const Dims& d, const CacheArgs& c, const int* pos, cons
                          const void* k_new, const void* v_new, const float* prio_leaving,
                          void* o, float* lse, void* ws, hipStream_t st);
 
+hipError_t launch_cache_from_prefill(const Dims& d, const CacheArgs& c, const void* k,
+                                     const void* v, const float* prio, const int* rank,
+                                     const int* tau, hipStream_t st);
+hipError_t launch_target_score(const Dims& d, const float* target, float eps, float* score,
+                               hipStream_t st);
+
 }  // namespace kvpop

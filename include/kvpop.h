@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define KVPOP_ABI_VERSION 1
+#define KVPOP_ABI_VERSION 2
 
 typedef enum {
   KVPOP_OK = 0,
@@ -58,7 +58,9 @@ typedef enum {
   KVPOP_CALL_THRESHOLDS = 0,
   KVPOP_CALL_MASKED_FWD = 1,
   KVPOP_CALL_FUTURE_TARGET = 2,
-  KVPOP_CALL_DECODE = 3
+  KVPOP_CALL_DECODE = 3,
+  KVPOP_CALL_CACHE_FROM_PREFILL = 4,
+  KVPOP_CALL_TARGET_SCORE = 5
 } kvpop_call;
 
 /* Problem description shared by all calls.
@@ -177,6 +179,41 @@ kvpop_status kvpop_decode_step(const kvpop_problem* pr, const kvpop_cache* cache
                                const void* k_new, const void* v_new,
                                const float* prio_leaving, void* o, float* lse,
                                void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Prefill -> decode handoff ([Notes] §2.3: inference keeps only the compact
+ * cache; after a prompt it holds the kept set of the prompt's last row under
+ * the mask above).  For each (sequence, KV head), with p = S - 1 (S =
+ * seq_len, the prompt length):
+ *   cache  out: slots 0 .. min(S, Bc)-1 hold the sinks (t < s), the
+ *          long-range tokens of E(p) with rank(t) <= tau_p, and the window
+ *          (p - t < w); a long-range slot's slot_prio is the token's priority
+ *          (NaN as -inf, -0 as +0), other slots get 0; ring[t mod w] is the
+ *          slot of each window token; slots min(S, Bc) .. Bc-1 get slot_pos
+ *          -1.  The K/V rows are copied into their slots.  This is the state
+ *          kvpop_decode_step reaches after steps 0 .. p with the same
+ *          priorities (up to slot order), so decoding continues at p = S.
+ *   k, v   [batch, Hkv, S, D] qkv_dtype: the prompt's keys and values
+ *   prio   [batch, Hkv, S] float; rank, tau from kvpop_thresholds for the same
+ *          (s, w, k)
+ * Requires w >= 1 and D in {64, 128}; uses no workspace. */
+kvpop_status kvpop_cache_from_prefill(const kvpop_problem* pr, const kvpop_cache* cache,
+                                      const void* k, const void* v, const float* prio,
+                                      const int32_t* rank, const int32_t* tau,
+                                      hipStream_t stream);
+
+/* Target score of each (KV head, token) ([Notes] §2.2: the future mass
+ * m_t = (1/N_t) sum_{d=t+w}^{S-1} A_{d,t} of query group g, aggregated as
+ * r_{h,t} = log(eps + (1/G) sum_g m_t^{(h,g)})).  N_t = S - t - w, the number
+ * of future queries.
+ *   target [batch, Hq, S] float: kvpop_future_target's output,
+ *          ln sum_{d >= t+w} A_{d,t} per query head
+ *   eps    >= 0, finite
+ *   score  [batch, Hkv, S] float out: log(eps + (1/G) sum_g exp(target_g - ln N_t));
+ *          where t + w > S - 1 (N_t = 0) the mean is 0 and score = log(eps)
+ *          (-inf for eps = 0)
+ * Uses no workspace. */
+kvpop_status kvpop_target_score(const kvpop_problem* pr, const float* target, float eps,
+                                float* score, hipStream_t stream);
 
 const char* kvpop_status_string(kvpop_status st);
 int32_t kvpop_abi_version(void);

@@ -26,7 +26,7 @@ def test_header_symbols_exported():
     assert declared == set(kv.EXPORTED_SYMBOLS)
     for name in declared:
         assert hasattr(L, name), name
-    assert kv.abi_version() == 1
+    assert kv.abi_version() == 2
     assert L.kvpop_status_string(3).decode() == "workspace too small"
 
 

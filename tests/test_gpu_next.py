@@ -1,0 +1,202 @@
+"""GPU parity of the calls beyond the hot path's core: the target score per KV
+head and the study of a sparse-LSE target ([Notes] §2.2, §2.3), and the
+prefill -> decode cache handoff ([Notes] §2.3).  Integer outputs bit-exact,
+floats within the stated tolerances; every call goes through the C ABI."""
+import numpy as np
+import pytest
+import torch
+
+import fixed_budget_sparse_amd as kv
+import oracle as orc
+from gpu_util import TOL, announce, device, host, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def _rand(shape, seed, scale_keys=False):
+    x = np.random.default_rng(seed).standard_normal(shape).astype(np.float32)
+    if scale_keys:
+        x[..., :4, :] *= 4
+    return x
+
+
+def _bf16(x):
+    from workloads import round_to_bf16
+    return round_to_bf16(x)
+
+
+# ---------------------------------------------------------------- target score
+SCORE_CASES = [
+    # b, Hq, Hkv, S, D, w, eps
+    (1, 8, 2, 640, 128, 32, 1e-6),
+    (2, 4, 2, 300, 64, 0, 1e-3),
+    (1, 6, 2, 257, 128, 17, 0.0),      # eps = 0: -inf where no future query
+    (1, 4, 4, 200, 128, 300, 1e-6),    # w >= S: log(eps) everywhere
+]
+
+
+@pytest.mark.parametrize("case", SCORE_CASES, ids=lambda c: "b{}q{}kv{}S{}D{}w{}eps{}".format(*c))
+def test_target_score_parity(case):
+    b, hq, hkv, S, D, w, eps = case
+    announce(f"target_score {case}")
+    q = _bf16(_rand((b, hq, S, D), 51))
+    k = _bf16(_rand((b, hkv, S, D), 52, scale_keys=True))
+    _, LSE = orc.dense_causal_attention(q, k, k)
+    L32 = LSE.astype(np.float32)
+    R = orc.target_score(q, k, L32.astype(np.float64), w, eps)
+    # the score kernel alone, on the oracle's targets
+    T = orc.future_target_colsum(q, k, L32.astype(np.float64), w)
+    r1 = host(kv.target_score(to_dev(T.astype(np.float32)), hkv, w, eps))
+    fin = np.isfinite(R)
+    assert np.array_equal(np.isneginf(r1), np.isneginf(R))
+    assert np.abs(r1[fin] - R[fin]).max() <= 1e-5
+    # the whole chain: GPU target, then GPU score
+    tgt = kv.future_target(to_dev(q, torch.bfloat16), to_dev(k, torch.bfloat16), to_dev(L32), w)
+    r2 = host(kv.target_score(tgt, hkv, w, eps))
+    assert np.array_equal(np.isneginf(r2), np.isneginf(R))
+    sel = fin & (R > -20)
+    if sel.any():
+        assert np.abs(r2[sel] - R[sel]).max() <= TOL["bf16"]["tgt"], np.abs(r2[sel] - R[sel]).max()
+
+
+def test_target_with_sparse_lse():
+    """The approximate target of [Sum-zh] §2.2 / [Notes] §2.3: the transposed
+    pass driven by the sparse forward's LSE instead of the teacher's.  It
+    matches the oracle fed with the oracle's sparse LSE, and it is never below
+    the exact target (a sparse LSE is at most the dense one)."""
+    device()
+    b, hq, hkv, S, D, s, w, k = 1, 8, 2, 700, 128, 4, 40, 100
+    announce("target with sparse LSE")
+    q = _bf16(_rand((b, hq, S, D), 61))
+    kk = _bf16(_rand((b, hkv, S, D), 62, scale_keys=True))
+    v = _bf16(_rand((b, hkv, S, D), 63))
+    prio = _rand((b, hkv, S), 64)
+    td = torch.bfloat16
+    rank, tau = kv.thresholds(to_dev(prio), s, w, k)
+    _, lse_sparse = kv.masked_attn_fwd(to_dev(q, td), to_dev(kk, td), to_dev(v, td), rank, tau, s,
+                                       w, k, out_dtype=torch.float32)
+    tgt_sparse = host(kv.future_target(to_dev(q, td), to_dev(kk, td), lse_sparse, w))
+    rank_o = orc.priority_ranks(prio)
+    tau_o = orc.thresholds_by_selection(rank_o, s, w, k)
+    _, LS = orc.masked_attention(q, kk, v, rank_o, tau_o, s, w)
+    T_s = orc.future_target_colsum(q, kk, LS.astype(np.float32).astype(np.float64), w)
+    _, LD = orc.dense_causal_attention(q, kk, kk)
+    T_d = orc.future_target_colsum(q, kk, LD.astype(np.float32).astype(np.float64), w)
+    sel = np.isfinite(T_s) & (T_s > -20)
+    assert np.abs(tgt_sparse[sel] - T_s[sel]).max() <= TOL["bf16"]["tgt"]
+    fin = np.isfinite(T_d)
+    assert (T_s[fin] >= T_d[fin] - 1e-9).all()
+    assert (tgt_sparse[fin] >= T_d[fin] - TOL["bf16"]["tgt"]).all()
+
+
+# ---------------------------------------------------------------- handoff
+HANDOFF_CASES = [
+    # nseq, Hkv, D, S, s, w, k, prio kind, dtype
+    (2, 2, 128, 300, 4, 16, 40, "normal", "bf16"),     # full cache (S > Bc)
+    (2, 1, 128, 30, 4, 16, 40, "normal", "bf16"),      # partial fill (S < Bc)
+    (1, 2, 64, 200, 3, 9, 20, "ties", "f32"),          # ties, NaN, +-inf; float32 cache
+    (1, 2, 128, 100, 2, 7, 0, "normal", "bf16"),       # k = 0: sinks + window
+    (1, 1, 128, 20, 2, 40, 10, "normal", "bf16"),      # w > S: no eligible token
+    (1, 2, 128, 1, 1, 1, 5, "normal", "bf16"),         # a one-token prompt
+]
+
+
+def _prio(kind, shape, seed):
+    rng = np.random.default_rng(seed)
+    p = rng.standard_normal(shape).astype(np.float32)
+    if kind == "ties":
+        p = np.round(p * 2).astype(np.float32)
+        p.flat[rng.integers(0, p.size, max(1, p.size // 30))] = np.nan
+        p.flat[rng.integers(0, p.size, max(1, p.size // 50))] = np.inf
+        p.flat[rng.integers(0, p.size, max(1, p.size // 50))] = -np.inf
+        p[p == 0] = -0.0
+    return p
+
+
+@pytest.mark.parametrize("case", HANDOFF_CASES, ids=lambda c: "n{}kv{}D{}S{}s{}w{}k{}-{}-{}".format(*c))
+def test_cache_from_prefill(case):
+    nseq, hkv, D, S, s, w, k, kind, dt = case
+    announce(f"cache_from_prefill {case}")
+    dev = device()
+    td = torch.bfloat16 if dt == "bf16" else torch.float32
+    Bc = s + w + k
+    prio = _prio(kind, (nseq, hkv, S), 71)
+    K = _rand((nseq, hkv, S, D), 72)
+    V = _rand((nseq, hkv, S, D), 73)
+    if dt == "bf16":
+        K, V = _bf16(K), _bf16(V)
+    rank, tau = kv.thresholds(to_dev(prio), s, w, k)
+    cache = kv.new_decode_cache(nseq, hkv, D, s, w, k, dtype=td, device=dev)
+    cache.slot_pos.fill_(12345)            # every slot must be rewritten
+    kv.cache_from_prefill(cache, to_dev(K, td), to_dev(V, td), to_dev(prio), rank, tau, s, w, k)
+    torch.cuda.synchronize()
+    sp, sprio, ring = host(cache.slot_pos), host(cache.slot_prio), host(cache.ring)
+    ck, cv = host(cache.k), host(cache.v)
+    p = S - 1
+    n = min(S, Bc)
+    canon = orc.canonical_priority(prio)
+    for b in range(nseq):
+        for h in range(hkv):
+            want = orc.kept_row_by_sorting(prio[b, h], p, s, w, k)
+            assert len(want) == n
+            assert sorted(sp[b, h, :n].tolist()) == want.tolist(), (b, h)
+            assert (sp[b, h, n:] == -1).all()
+            for j in range(n):
+                t = int(sp[b, h, j])
+                is_long = s <= t <= p - w
+                want_p = np.float32(canon[b, h, t]) if is_long else np.float32(0.0)
+                assert np.array_equal(np.float32(sprio[b, h, j]).view(np.uint32),
+                                      want_p.view(np.uint32)), (b, h, j, t)
+                assert np.array_equal(ck[b, h, j], K[b, h, t]) and np.array_equal(cv[b, h, j], V[b, h, t])
+                if p - t < w:
+                    assert ring[b, h, t % w] == j, (b, h, t)
+
+
+def test_handoff_then_decode():
+    """Decoding on from the handoff keeps the cache equal (as sets) to a cache
+    decoded from position 0 and to the oracle's kept rows, and the outputs match
+    the oracle's attention over them."""
+    dev = device()
+    nseq, hq, hkv, D, s, w, k = 2, 8, 2, 128, 3, 8, 24
+    S, steps = 120, 50
+    announce("handoff then decode")
+    td = torch.bfloat16
+    Bc = s + w + k
+    T = S + steps
+    prio = _rand((nseq, hkv, T), 81)
+    K = _bf16(_rand((nseq, hkv, T, D), 82))
+    V = _bf16(_rand((nseq, hkv, T, D), 83))
+    Qd = _bf16(_rand((T, nseq, hq, D), 84))
+    rank, tau = kv.thresholds(to_dev(np.ascontiguousarray(prio[:, :, :S])), s, w, k)
+    ca = kv.new_decode_cache(nseq, hkv, D, s, w, k, dtype=td, device=dev)
+    kv.cache_from_prefill(ca, to_dev(np.ascontiguousarray(K[:, :, :S]), td),
+                          to_dev(np.ascontiguousarray(V[:, :, :S]), td),
+                          to_dev(np.ascontiguousarray(prio[:, :, :S])), rank, tau, s, w, k)
+    cb = kv.new_decode_cache(nseq, hkv, D, s, w, k, dtype=td, device=dev)
+
+    def step(cache, p):
+        u = p - w
+        pl = prio[:, :, u] if u >= 0 else np.zeros((nseq, hkv), np.float32)
+        return kv.decode_step(cache, to_dev(np.full(nseq, p, np.int32)), to_dev(Qd[p], td),
+                              to_dev(np.ascontiguousarray(K[:, :, p]), td),
+                              to_dev(np.ascontiguousarray(V[:, :, p]), td),
+                              to_dev(np.ascontiguousarray(pl)), s, w, k)
+
+    for p in range(S):
+        step(cb, p)
+    for p in range(S, T):
+        oa, la = step(ca, p)
+        step(cb, p)
+        n = min(p + 1, Bc)
+        spa, spb = host(ca.slot_pos)[:, :, :n], host(cb.slot_pos)[:, :, :n]
+        held = []
+        for b in range(nseq):
+            for h in range(hkv):
+                want = orc.kept_row_by_sorting(prio[b, h], p, s, w, k)
+                assert sorted(spa[b, h].tolist()) == want.tolist(), (p, b, h)
+                assert sorted(spb[b, h].tolist()) == want.tolist(), (p, b, h)
+                held.append(want)
+        for b in range(nseq):
+            oo, ll = orc.decode_attention(Qd[p, b], K[b], V[b], held[b * hkv:(b + 1) * hkv])
+            assert np.abs(host(oa)[b] - oo).max() <= TOL["bf16"]["o"], (p, b)
+            assert np.abs(host(la)[b] - ll).max() <= TOL["bf16"]["lse"], (p, b)
