@@ -6,8 +6,9 @@ k 1520, B 2048): kvpop_thresholds -> kvpop_masked_attn_fwd ->
 kvpop_future_target (with the dense teacher LSE computed beforehand).
 `value` is the algorithmic TFLOP/s of the forward (4 D flop per kept pair) and
 the target pass (2 D flop per pair d >= t + w) over the whole step's time.
-The decode leg times 1024 steps (p = 4096..5119, after an untimed fill from
-p = 0) of 64 sequences over a B = 2048 cache and reports HBM GB/s.
+The decode leg fills a B = 2048 cache of 64 sequences from a 4096-token
+prompt (thresholds + kvpop_cache_from_prefill, timed on their own), then times
+1024 decode steps (p = 4096..5119) and reports HBM GB/s.
 
 Prints ONE JSON line.  Inputs are synthetic and seeded (workloads.py) and
 already resident in HBM when the timed regions start.
@@ -48,6 +49,17 @@ def decode_bytes_per_step(nseq, hq, hkv, D, Bc, esize=2, out_esize=2):
     return kv + q + o + new
 
 
+def handoff_bytes(nseq, hkv, S, D, s, w, k, esize=2):
+    """Algorithmic HBM bytes of one prefill -> decode handoff: the ranks of the
+    last row's eligible range, tau, the survivors' priorities, the slot
+    metadata and ring written, and min(S, B) K and V rows read and written."""
+    Bc = s + w + k
+    n = min(S, Bc)
+    n_e = max(0, (S - 1 - w) - s + 1)
+    per_head = n_e * 4 + 4 + min(k, n_e) * 4 + Bc * 8 + w * 4 + 4 * n * D * esize
+    return nseq * hkv * per_head
+
+
 def measured_traffic(kernel, workload):
     """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
     summary (FETCH_SIZE and WRITE_SIZE scaled by a plain-copy calibration), or
@@ -71,6 +83,33 @@ def measured_traffic(kernel, workload):
         return int(fields["traffic_bytes_per_launch"])
     except (KeyError, OSError, ValueError):
         return None
+
+
+def sparse_lse_study(kv, torch, q, kk, lse_sparse, tgt, score, s, w, k, eps):
+    """The approximate target (the sparse forward's LSE in place of the
+    teacher's) against the exact one: how far the target and the score move,
+    and how much the kept set of the last row changes when each score serves
+    as the priority."""
+    S, hkv = q.shape[2], kk.shape[1]
+    tgt_sp = kv.future_target(q, kk, lse_sparse, w)
+    score_sp = kv.target_score(tgt_sp, hkv, w, eps)
+    sel = torch.isfinite(tgt) & (tgt > -20)
+    d = (tgt_sp - tgt)[sel].double()
+    ds = (score_sp - score)[torch.isfinite(score)].double()
+    p = S - 1
+    kept = []
+    for sc in (score, score_sp):
+        rank, tau = kv.thresholds(sc, s, w, k)
+        kept.append(rank[:, :, s:p - w + 1] <= tau[:, :, p:p + 1])
+    both = (kept[0] & kept[1]).sum(-1).double()
+    overlap = both / kept[0].sum(-1).double()
+    torch.cuda.synchronize()
+    return {"target_diff": {"min": round(d.min().item(), 6), "mean": round(d.mean().item(), 6),
+                            "p99": round(torch.quantile(d.float(), 0.99).item(), 6),
+                            "max": round(d.max().item(), 6), "n": int(d.numel())},
+            "score_diff": {"mean": round(ds.mean().item(), 6), "max": round(ds.abs().max().item(), 6)},
+            "last_row_kept_overlap": {"mean": round(overlap.mean().item(), 4),
+                                      "min": round(overlap.min().item(), 4)}}
 
 
 def parse():
@@ -188,6 +227,20 @@ def main():
         times["fwd"].append(e1.elapsed_time(e2))
         times["tgt"].append(e2.elapsed_time(e3))
     ms_step = wall * 1e3 / args.steps
+    # the target score per KV head, timed alone, then the sparse-LSE study
+    # (untimed): `lse` holds the last step's sparse LSE, `tgt` the exact target
+    eps = 1e-6
+    score = torch.empty((1, Hkv, S), dtype=torch.float32, device=dev)
+    kv.target_score(tgt, Hkv, w, eps, score=score)
+    torch.cuda.synchronize()
+    es, ee = ev(), ev()
+    es.record()
+    for _ in range(20):
+        kv.target_score(tgt, Hkv, w, eps, score=score)
+    ee.record()
+    torch.cuda.synchronize()
+    score_us = es.elapsed_time(ee) * 1e3 / 20
+    study = sparse_lse_study(kv, torch, q, kk, lse, tgt, score, s, w, k, eps)
     B = s + w + k
     f_fwd = 4 * D * Hq * fwd_pairs(S, B)
     f_tgt = 2 * D * Hq * tgt_pairs(S, w)
@@ -222,6 +275,10 @@ def main():
                      "unit": "TFLOP/s", "frac": round(tgt_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
                      "traffic": measured_traffic("future_target", "qwen3-4b-S16384"),
                      "traffic_unit": "bytes/launch"},
+        "target_score": {"us": round(score_us, 2), "eps": eps,
+                         "bytes": 4 * (Hq + Hkv) * S,
+                         "GB/s": round(4 * (Hq + Hkv) * S / (score_us * 1e-6) / 1e9, 1)},
+        "sparse_lse_study": study,
     }
 
     if not args.no_decode:
@@ -255,13 +312,29 @@ def bench_decode(kv, torch, np, dev, n_timed):
         u = p - w
         return prio_table[:, :, u].contiguous() if u >= 0 else zero_prio
 
-    # untimed fill p = 0 .. p_start-1 with fresh random inputs
-    for p in range(p_start):
-        qd = torch.randn((nseq, Hq, D), generator=g, device=dev).to(bf)
-        kn = torch.randn((nseq, Hkv, D), generator=g, device=dev).to(bf)
-        vn = torch.randn((nseq, Hkv, D), generator=g, device=dev).to(bf)
-        kv.decode_step(cache, pos_all[p], qd, kn, vn, prio_at(p), s, w, k, out_dtype=bf, o=o,
-                       lse=lse, ws=ws)
+    # the cache after a prompt of p_start tokens: thresholds over the prompt's
+    # priorities, then the handoff of the last row's kept set (timed apart;
+    # the handoff rewrites the whole cache, so repeats are idempotent)
+    kp = torch.randn((nseq, Hkv, p_start, D), generator=g, device=dev).to(bf)
+    vp = torch.randn((nseq, Hkv, p_start, D), generator=g, device=dev).to(bf)
+    prio_prompt = prio_table[:, :, :p_start].contiguous()
+    rank_p = torch.empty(prio_prompt.shape, dtype=torch.int32, device=dev)
+    tau_p = torch.empty_like(rank_p)
+    ho_ms = {"thresholds": [], "cache_from_prefill": []}
+    for rep in range(12):
+        a, b_, c_ = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+        a.record()
+        kv.thresholds(prio_prompt, s, w, k, rank=rank_p, tau=tau_p)
+        b_.record()
+        kv.cache_from_prefill(cache, kp, vp, prio_prompt, rank_p, tau_p, s, w, k)
+        c_.record()
+        torch.cuda.synchronize()
+        if rep >= 2:
+            ho_ms["thresholds"].append(a.elapsed_time(b_))
+            ho_ms["cache_from_prefill"].append(b_.elapsed_time(c_))
+    ho_avg = {n: sum(t) / len(t) for n, t in ho_ms.items()}
+    ho_bytes = handoff_bytes(nseq, Hkv, p_start, D, s, w, k)
+    del kp, vp
     # pre-drawn inputs of the timed steps, resident in HBM
     qs = torch.randn((n_timed, nseq, Hq, D), generator=g, device=dev).to(bf)
     kns = torch.randn((n_timed, nseq, Hkv, D), generator=g, device=dev).to(bf)
@@ -285,7 +358,13 @@ def bench_decode(kv, torch, np, dev, n_timed):
             "us_per_step": round(us_step, 2), "wall_us_per_step": round(wall * 1e6 / n_timed, 2),
             "bytes_per_step": nbytes, "GB/s": round(gbps, 1),
             "frac_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4),
-            "tokens_per_s": round(nseq / (us_step * 1e-6), 1)}
+            "tokens_per_s": round(nseq / (us_step * 1e-6), 1),
+            "handoff": {"prompt_tokens": p_start,
+                        "thresholds_ms": round(ho_avg["thresholds"], 4),
+                        "cache_from_prefill_ms": round(ho_avg["cache_from_prefill"], 4),
+                        "cache_from_prefill_bytes": ho_bytes,
+                        "cache_from_prefill_GB/s":
+                            round(ho_bytes / (ho_avg["cache_from_prefill"] * 1e-3) / 1e9, 1)}}
 
 
 if __name__ == "__main__":

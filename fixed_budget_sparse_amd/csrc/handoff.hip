@@ -5,19 +5,23 @@
 // p = S - 1 under the forward's mask (§2.3: sinks t < s, the protected window
 // q - t < w, and the long-range tokens of E(p) = [s, p - w] with
 // rank(t) <= tau_p), which is exactly the set decode reaches after steps
-// 0 .. p with the same static priorities.  One workgroup per (sequence, KV
-// head):
-//   1. the long-range survivors of row p are counted, prefix-summed over the
-//      four waves and placed with wave ballots, in token order;
-//   2. slots 0 .. n-1 (n = min(S, s + w + k)) receive the sinks, the
-//      long-range tokens and the window, in that order; a long-range slot
-//      keeps the token's priority (NaN as -inf, -0 as +0, as the decode step
-//      compares them), ring[t mod w] = slot of each window token, and slots
-//      n .. Bc-1 are marked empty (position -1);
-//   3. after a barrier the K and V rows are copied into their slots, 16
-//      bytes per lane.
-// Decode then continues at p = S; while S < Bc the next tokens take slots
-// S, S+1, ... as in a decode that started at 0.
+// 0 .. p with the same static priorities.
+//
+// Slots 0 .. n-1 (n = min(S, s + w + k)) receive the sinks, the long-range
+// tokens in token order and the window, in that order; slots n .. Bc-1 are
+// marked empty (position -1).  A long-range slot keeps the token's priority
+// (NaN as -inf, -0 as +0, as the decode step compares them) and
+// ring[t mod w] = slot of each token of the last w positions.
+//
+// Grid (Hkv, batch, ceil(Bc / kSlots)): one workgroup per (sequence, KV head,
+// block of kSlots slots), so the row copies spread over the whole chip.  Each
+// workgroup counts the long-range survivors of its (sequence, head) (per-wave
+// counts over contiguous token ranges, prefix-summed over the waves), places
+// with wave ballots only those that land in its slot block, writes that
+// block's slot metadata and ring entries and keeps the block's token
+// positions in LDS; after a barrier it copies its K and V rows, 16 bytes per
+// lane.  Decode then continues at p = S; while S < Bc the next tokens take
+// slots S, S+1, ... as in a decode that started at 0.
 #include "kvpop_device.h"
 #include "kvpop_internal.h"
 
@@ -25,7 +29,10 @@ namespace kvpop {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kUnroll = 8;   // rank loads in flight per lane
+constexpr int kWaves = kThreads / 64;
+constexpr int kUnroll = 8;    // rank loads in flight per lane
+constexpr int kSlots = 512;   // cache slots per workgroup
+constexpr int kCopyUnroll = 4;
 
 struct HandoffArgs {
   void* ck;
@@ -42,11 +49,13 @@ struct HandoffArgs {
 };
 
 __global__ __launch_bounds__(kThreads) void cache_from_prefill_kernel(HandoffArgs a) {
-  __shared__ int s_cnt[kThreads / 64];
+  __shared__ int s_cnt[kWaves];
+  __shared__ int s_pos[kSlots];
   const int tid = threadIdx.x, lane = lane_id(), wave = wave_id();
   const int h = blockIdx.x, b = blockIdx.y;
   const size_t seg = (size_t)b * a.Hkv + h;
   const int S = a.S, s = a.s, w = a.w, Bc = a.Bc;
+  const int j0 = blockIdx.z * kSlots, j1 = min(j0 + kSlots, Bc);   // this block's slots
   const int p = S - 1;
   const int* rk = a.rank + seg * S;
   const float* pr = a.prio + seg * S;
@@ -62,7 +71,7 @@ __global__ __launch_bounds__(kThreads) void cache_from_prefill_kernel(HandoffArg
   const int n_win = max(0, p - win_lo + 1);
 
   // ---- 1. long-range survivors: each wave owns a contiguous token range
-  const int per_wave = (n_e + 3) / 4;
+  const int per_wave = (n_e + kWaves - 1) / kWaves;
   const int t_lo = e_lo + wave * per_wave, t_hi = min(e_hi + 1, t_lo + per_wave);
   // branch-free test; the load index is clamped into the range (loops below
   // only run while base < t_hi, so t_hi - 1 is a valid token)
@@ -80,56 +89,74 @@ __global__ __launch_bounds__(kThreads) void cache_from_prefill_kernel(HandoffArg
   int slot = n_sink;                                   // long-range slots follow the sinks
   for (int wv = 0; wv < wave; ++wv) slot += s_cnt[wv];
   int n_long = 0;
-  for (int wv = 0; wv < kThreads / 64; ++wv) n_long += s_cnt[wv];
-  for (int base = t_lo; base < t_hi; base += 64 * kUnroll) {
-    bool kp[kUnroll];
+  for (int wv = 0; wv < kWaves; ++wv) n_long += s_cnt[wv];
+  // place only where this wave's slots [slot, slot + cnt) meet [j0, j1)
+  if (slot < j1 && slot + cnt > j0) {
+    for (int base = t_lo; base < t_hi && slot < j1; base += 64 * kUnroll) {
+      bool kp[kUnroll];
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) kp[u] = kept(base + 64 * u + lane);
+      for (int u = 0; u < kUnroll; ++u) kp[u] = kept(base + 64 * u + lane);
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const uint64_t m = wave_ballot(kp[u]);
-      if (kp[u]) {
+      for (int u = 0; u < kUnroll; ++u) {
+        const uint64_t m = wave_ballot(kp[u]);
         const int j = slot + lanes_below(m);
-        const int t = base + 64 * u + lane;
-        spos[j] = t;
-        sprio[j] = canonical_priority(pr[t]);
+        if (kp[u] && j >= j0 && j < j1) {
+          const int t = base + 64 * u + lane;
+          s_pos[j - j0] = t;
+          spos[j] = t;
+          sprio[j] = canonical_priority(pr[t]);
+        }
+        slot += __builtin_popcountll(m);
       }
-      slot += __builtin_popcountll(m);
     }
   }
 
-  // ---- 2. sinks, window, ring, empty slots
+  // ---- 2. sinks, window, ring and empty slots of this block
   const int n = n_sink + n_long + n_win;               // = min(S, Bc)
-  for (int j = tid; j < n_sink; j += kThreads) {
-    spos[j] = j;
-    sprio[j] = 0.0f;
-    if (j > p - w) ring[j % w] = j;                    // a sink inside the last w positions
-  }
-  for (int i = tid; i < n_win; i += kThreads) {
-    const int j = n_sink + n_long + i, t = win_lo + i;
+  const int w_lo = n_sink + n_long;                    // first window slot
+  for (int j = j0 + tid; j < j1; j += kThreads) {
+    int t = -1;
+    if (j < n_sink) {
+      t = j;
+    } else if (j >= w_lo && j < n) {
+      t = win_lo + (j - w_lo);
+    } else if (j < n) {
+      continue;                                        // long-range: placed above
+    }
+    s_pos[j - j0] = t;
     spos[j] = t;
     sprio[j] = 0.0f;
-    ring[t % w] = j;
+    if (t >= 0 && t > p - w) ring[t % w] = j;          // a token of the last w positions
   }
-  for (int j = n + tid; j < Bc; j += kThreads) {
-    spos[j] = -1;
-    sprio[j] = 0.0f;
-  }
-  __syncthreads();   // slot positions written above are read back below
+  __syncthreads();   // s_pos complete
 
-  // ---- 3. K/V rows into their slots
+  // ---- 3. K/V rows of this block's occupied slots
   const int pieces = a.row_bytes / 16;
+  const int nj = max(0, min(j1, n) - j0);
+  const long long total = (long long)nj * pieces;
   const unsigned char* kg = (const unsigned char*)a.k + seg * (size_t)S * a.row_bytes;
   const unsigned char* vg = (const unsigned char*)a.v + seg * (size_t)S * a.row_bytes;
-  unsigned char* kc = (unsigned char*)a.ck + seg * (size_t)Bc * a.row_bytes;
-  unsigned char* vc = (unsigned char*)a.cv + seg * (size_t)Bc * a.row_bytes;
-  for (long long i = tid; i < (long long)n * pieces; i += kThreads) {
-    const int j = (int)(i / pieces), pc = (int)(i % pieces);
-    const int t = spos[j];
-    const size_t src = (size_t)t * a.row_bytes + (size_t)pc * 16;
-    const size_t dst = (size_t)j * a.row_bytes + (size_t)pc * 16;
-    *(uint4*)(kc + dst) = *(const uint4*)(kg + src);
-    *(uint4*)(vc + dst) = *(const uint4*)(vg + src);
+  unsigned char* kc = (unsigned char*)a.ck + (seg * (size_t)Bc + j0) * a.row_bytes;
+  unsigned char* vc = (unsigned char*)a.cv + (seg * (size_t)Bc + j0) * a.row_bytes;
+  for (long long base = tid; base < total; base += (long long)kThreads * kCopyUnroll) {
+    uint4 kr[kCopyUnroll], vr[kCopyUnroll];
+    size_t dst[kCopyUnroll];
+#pragma unroll
+    for (int u = 0; u < kCopyUnroll; ++u) {
+      const long long i = min(base + (long long)kThreads * u, total - 1);   // clamped: in range
+      const int jj = (int)(i / pieces), pc = (int)(i % pieces);
+      const size_t src = (size_t)s_pos[jj] * a.row_bytes + (size_t)pc * 16;
+      dst[u] = (size_t)jj * a.row_bytes + (size_t)pc * 16;
+      kr[u] = *(const uint4*)(kg + src);
+      vr[u] = *(const uint4*)(vg + src);
+    }
+#pragma unroll
+    for (int u = 0; u < kCopyUnroll; ++u) {
+      if (base + (long long)kThreads * u < total) {
+        *(uint4*)(kc + dst[u]) = kr[u];
+        *(uint4*)(vc + dst[u]) = vr[u];
+      }
+    }
   }
 }
 
@@ -144,7 +171,8 @@ hipError_t launch_cache_from_prefill(const Dims& d, const CacheArgs& c, const vo
   a.Hkv = d.Hkv; a.S = d.S; a.s = d.s; a.w = d.w; a.topk = d.k;
   a.Bc = (int)d.budget();
   a.row_bytes = d.D * (d.f32_in ? 4 : 2);
-  hipLaunchKernelGGL(cache_from_prefill_kernel, dim3(d.Hkv, d.b), dim3(kThreads), 0, st, a);
+  const unsigned parts = (unsigned)((a.Bc + kSlots - 1) / kSlots);
+  hipLaunchKernelGGL(cache_from_prefill_kernel, dim3(d.Hkv, d.b, parts), dim3(kThreads), 0, st, a);
   return hipGetLastError();
 }
 

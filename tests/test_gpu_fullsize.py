@@ -141,10 +141,33 @@ def test_full_teacher_lse_and_target(name):
     assert np.abs(tg[sel] - T[sel]).max() <= TOL["bf16"]["tgt"], np.abs(tg[sel] - T[sel]).max()
 
 
-def _decode_run(wl, n_steps, check_steps, out_seqs):
-    """Runs decode steps 0..n_steps-1 over every sequence; at each step of
-    ``check_steps`` compares cache membership of every (sequence, KV head) with
-    the oracle's kept set of that row, and o/LSE of ``out_seqs``."""
+def _held_sets(cache, rank_o, p, s, w, k, Bc):
+    """Cache membership of every (sequence, KV head) after row p, checked
+    against the oracle's kept set of that row; returns the sets."""
+    nseq, Hkv = rank_o.shape[:2]
+    n = min(p + 1, Bc)
+    sp = host(cache.slot_pos)
+    assert (sp[:, :, n:] == -1).all(), p
+    sp = sp[:, :, :n]
+    tau = orc.thresholds_by_selection(rank_o, s, w, k, rows=[p])[..., 0]   # [nseq, Hkv]
+    held = {}
+    for b in range(nseq):
+        for h in range(Hkv):
+            keep = orc.mask_rows(rank_o[b, h, :p + 1], tau[b, h:h + 1], np.array([p]), s, w)[0]
+            want = np.flatnonzero(keep)
+            assert len(want) == n, (p, b, h)
+            assert np.array_equal(np.sort(sp[b, h]), want), (p, b, h)
+            held[(b, h)] = want
+    return held
+
+
+def _decode_run(wl, n_steps, check_steps, out_seqs, handoff_at=0):
+    """Runs decode steps over every sequence; at each step of ``check_steps``
+    compares cache membership of every (sequence, KV head) with the oracle's
+    kept set of that row, and o/LSE of ``out_seqs``.  With ``handoff_at`` > 0
+    the cache is first filled from a prompt of that many tokens
+    (kvpop_thresholds + kvpop_cache_from_prefill, checked the same way, with
+    its K/V rows and long-range priorities) and decoding starts there."""
     dev = device()
     nseq, Hq, Hkv, D = wl.batch, wl.n_q_heads, wl.n_kv_heads, wl.head_dim
     s, w, k = wl.sink, wl.window, wl.topk
@@ -164,9 +187,34 @@ def _decode_run(wl, n_steps, check_steps, out_seqs):
     n_ws = kv.workspace_size(3, pr)
     ws_raw = torch.empty(n_ws + 256, dtype=torch.uint8, device=dev)
     ws = ws_raw[(-ws_raw.data_ptr()) % 256:][:n_ws]
-    checks = sorted(set(int(c) for c in check_steps if 0 <= c < n_steps))
+    checks = sorted(set(int(c) for c in check_steps if handoff_at <= c < n_steps))
+    if handoff_at > 0:
+        S = handoff_at
+        kp = kn_all[:S].permute(1, 2, 0, 3).contiguous()      # [nseq, Hkv, S, D]
+        vp = vn_all[:S].permute(1, 2, 0, 3).contiguous()
+        pp = prio_t[:, :, :S].contiguous()
+        rank_p, tau_p = kv.thresholds(pp, s, w, k)
+        kv.cache_from_prefill(cache, kp, vp, pp, rank_p, tau_p, s, w, k)
+        torch.cuda.synchronize()
+        held = _held_sets(cache, rank_o, S - 1, s, w, k, Bc)
+        n = min(S, Bc)
+        sp = cache.slot_pos[:, :, :n].long()
+        idx = sp[..., None].expand(-1, -1, -1, D)
+        assert torch.equal(cache.k[:, :, :n], torch.gather(kp, 2, idx))
+        assert torch.equal(cache.v[:, :, :n], torch.gather(vp, 2, idx))
+        canon = orc.canonical_priority(prio_h[:, :, :S])
+        sph, sprio = host(cache.slot_pos)[:, :, :n], host(cache.slot_prio)[:, :, :n]
+        is_long = (sph >= s) & (sph <= S - 1 - w)
+        want_p = np.where(is_long, np.take_along_axis(canon, np.maximum(sph, 0), 2), 0.0)
+        assert np.array_equal(sprio.astype(np.float32).view(np.uint32),
+                              want_p.astype(np.float32).view(np.uint32))
+        ring = host(cache.ring)
+        for t in range(max(0, S - w), S):
+            j = ring[:, :, t % w]
+            assert (np.take_along_axis(sph, j[..., None], 2)[..., 0] == t).all(), t
+        del kp, vp, held
     done = 0
-    for p in range(n_steps):
+    for p in range(handoff_at, n_steps):
         check = done < len(checks) and checks[done] == p
         qd = W.make_decode_query_device(wl, dev, p) if check else q_fixed
         pl = prio_steps[p - w] if p >= w else zero_prio
@@ -177,16 +225,7 @@ def _decode_run(wl, n_steps, check_steps, out_seqs):
         done += 1
         torch.cuda.synchronize()
         n = min(p + 1, Bc)
-        sp = host(cache.slot_pos)[:, :, :n]
-        tau = orc.thresholds_by_selection(rank_o, s, w, k, rows=[p])[..., 0]   # [nseq, Hkv]
-        held = {}
-        for b in range(nseq):
-            for h in range(Hkv):
-                keep = orc.mask_rows(rank_o[b, h, :p + 1], tau[b, h:h + 1], np.array([p]), s, w)[0]
-                want = np.flatnonzero(keep)
-                assert len(want) == n, (p, b, h)
-                assert np.array_equal(np.sort(sp[b, h]), want), (p, b, h)
-                held[(b, h)] = want
+        held = _held_sets(cache, rank_o, p, s, w, k, Bc)
         qh, oh, lh = host(qd), host(o), host(lse)
         for b in out_seqs:
             idx = [held[(b, h)] for h in range(Hkv)]
@@ -209,6 +248,14 @@ def test_full_decode_b2048():
     s, w, Bc = wl.sink, wl.window, wl.budget
     checks = [0, s - 1, s, w - 1, w, w + s, Bc - 1, Bc, Bc + 1, 2 * Bc - 1, 2 * Bc, 4607, 5119]
     _decode_run(wl, 5120, checks, out_seqs=[0, 37, 63])
+
+
+def test_full_handoff_b2048_then_decode():
+    """64 sequences, B = 2048: the cache filled from a 4096-token prompt, as
+    the benchmark's decode leg does, then decode steps 4096..4607."""
+    wl = W.DECODE_B2048
+    announce("full handoff 64 x B2048 from a 4096-token prompt, then 512 steps")
+    _decode_run(wl, 4608, [4096, 4097, 4350, 4607], out_seqs=[0, 63], handoff_at=4096)
 
 
 def test_full_decode_long_131072_steps():

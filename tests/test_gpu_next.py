@@ -98,6 +98,9 @@ HANDOFF_CASES = [
     (1, 2, 128, 100, 2, 7, 0, "normal", "bf16"),       # k = 0: sinks + window
     (1, 1, 128, 20, 2, 40, 10, "normal", "bf16"),      # w > S: no eligible token
     (1, 2, 128, 1, 1, 1, 5, "normal", "bf16"),         # a one-token prompt
+    (1, 2, 128, 1500, 4, 100, 600, "normal", "bf16"),  # B = 704: two slot blocks, long range crosses
+    (2, 1, 64, 600, 5, 300, 900, "ties", "bf16"),      # B = 1205, partial fill over three blocks
+    (1, 1, 128, 2000, 600, 64, 300, "normal", "f32"),  # sinks fill the first block and more
 ]
 
 
