@@ -40,6 +40,16 @@ Readings of points the pages leave open (each also listed in the design notes):
   R10 the target score's N_t is the number of future queries S - t - w; where
      there are none (t + w > S - 1) the future mass is 0 and the score is
      log(eps).
+  R11 the decayed target score r(q, t) = r_t + floor((q - t)/n) log(gamma_h) is
+     evaluated in float32 as one rounded product followed by one rounded sum
+     (the labels are integer decisions taken on it, so both implementations
+     take them in that precision); NaN scores count as -inf and -0 as +0.
+  R12 teacher boundary labels: the teacher keeps the first min(k, |E(q)|)
+     tokens of E(q) = [s, q - w] in the order (decayed score desc, index asc);
+     t_bnd is the last kept token in that order (it may be t_new itself) and
+     y = +1 if t_new = q - w is kept, -1 if not.  Without a newcomer
+     (q - w < s) there is no label: y = 0, t_bnd = -1; with k = 0 nothing is
+     kept: y = -1, t_bnd = -1.
 """
 from __future__ import annotations
 
@@ -321,6 +331,61 @@ def target_score(q, k, lse, w, eps, scale=0.0, block=256):
             mass[bi, hq // G] += m / G
     with np.errstate(divide="ignore"):
         return np.log(eps + mass)
+
+
+# --------------------------------------------------------------------------
+# Teacher boundary labels  ([Notes] §2.2: the decayed target score, the
+# teacher's top-k over E(q), the boundary token t_bnd and the label y_{q,h};
+# readings R11, R12)
+# --------------------------------------------------------------------------
+def decayed_scores(score_row: np.ndarray, q: int, n: int, log_gamma: float,
+                   ts: np.ndarray) -> np.ndarray:
+    """r(q, t) = r_t + floor((q - t) / n) * log(gamma) for the tokens ``ts``
+    (float32 product, then float32 sum; NaN -> -inf, -0 -> +0; reading R11)."""
+    age = ((q - ts) // n).astype(np.float32)
+    r = score_row[ts].astype(np.float32) + age * np.float32(log_gamma)
+    r = r.astype(np.float32)
+    r[np.isnan(r)] = -np.inf
+    r[r == 0] = 0.0
+    return r
+
+
+def teacher_kept(score_row: np.ndarray, q: int, s: int, w: int, k: int, n: int,
+                 log_gamma: float) -> np.ndarray:
+    """The teacher's kept long-range tokens at query q, best first: the first
+    min(k, |E(q)|) tokens of E(q) = [s, q - w] by decayed score (descending),
+    ties to the lower index (reading R12)."""
+    ts = np.arange(s, q - w + 1)
+    if len(ts) == 0 or k == 0:
+        return ts[:0]
+    r = decayed_scores(score_row, q, n, log_gamma, ts)
+    order = np.lexsort((ts, -r.astype(np.float64)))   # primary key -r, then the index
+    return ts[order[:min(k, len(ts))]]
+
+
+def boundary_labels(score: np.ndarray, log_gamma: np.ndarray, n: int, s: int, w: int, k: int,
+                    rows: Optional[Sequence[int]] = None):
+    """Teacher boundary labels ([Notes] §2.2, reading R12).  score [b, Hkv, S]
+    (the target score r^tgt), log_gamma [Hkv] -> (t_bnd, y), int32 [b, Hkv, S]:
+    for every query q with a newcomer t_new = q - w >= s, t_bnd is the lowest
+    ranked token the teacher keeps in E(q) and y = +1 / -1 as t_new is kept or
+    not; other rows hold t_bnd = -1, y = 0 (k = 0: y = -1)."""
+    b, H, S = score.shape
+    t_bnd = np.full((b, H, S), -1, dtype=np.int32)
+    y = np.zeros((b, H, S), dtype=np.int32)
+    for bi in range(b):
+        for h in range(H):
+            for q in (range(S) if rows is None else rows):
+                t_new = q - w
+                if t_new < s:
+                    continue
+                kept = teacher_kept(score[bi, h], q, s, w, k, n, float(log_gamma[h]))
+                if len(kept) == 0:
+                    y[bi, h, q] = -1
+                    continue
+                t_bnd[bi, h, q] = kept[-1]
+                y[bi, h, q] = 1 if t_new in set(kept.tolist()) else -1
+    return t_bnd, y
 
 
 # --------------------------------------------------------------------------
