@@ -112,6 +112,27 @@ def sparse_lse_study(kv, torch, q, kk, lse_sparse, tgt, score, s, w, k, eps):
                                       "min": round(overlap.min().item(), 4)}}
 
 
+def bench_labels(kv, torch, score, s, w, k, ev, reps=5):
+    """Teacher boundary labels over the step's target score (decay step 64,
+    seeded per-head log gamma), timed on their own."""
+    from workloads import LABEL_DECAY_STEP, QWEN3_4B_S16K, make_label_inputs
+    lg = torch.from_numpy(make_label_inputs(QWEN3_4B_S16K)["log_gamma"]).to(score.device)
+    tb, y = kv.boundary_labels(score, lg, LABEL_DECAY_STEP, s, w, k)
+    torch.cuda.synchronize()
+    e0, e1 = ev(), ev()
+    e0.record()
+    for _ in range(reps):
+        kv.boundary_labels(score, lg, LABEL_DECAY_STEP, s, w, k, t_bnd=tb, y=y)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    hkv, S = score.shape[1], score.shape[2]
+    rows = hkv * max(0, S - s - w)
+    kept = (y == 1).sum().item() / max(1, rows)
+    return {"ms": round(ms, 4), "decay_step": LABEL_DECAY_STEP, "labelled_rows": rows,
+            "rows_per_s": round(rows / (ms * 1e-3), 1), "frac_newcomer_kept": round(kept, 4)}
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -241,6 +262,7 @@ def main():
     torch.cuda.synchronize()
     score_us = es.elapsed_time(ee) * 1e3 / 20
     study = sparse_lse_study(kv, torch, q, kk, lse, tgt, score, s, w, k, eps)
+    labels = bench_labels(kv, torch, score, s, w, k, ev)
     B = s + w + k
     f_fwd = 4 * D * Hq * fwd_pairs(S, B)
     f_tgt = 2 * D * Hq * tgt_pairs(S, w)
@@ -279,6 +301,7 @@ def main():
                          "bytes": 4 * (Hq + Hkv) * S,
                          "GB/s": round(4 * (Hq + Hkv) * S / (score_us * 1e-6) / 1e9, 1)},
         "sparse_lse_study": study,
+        "boundary_labels": labels,
     }
 
     if not args.no_decode:

@@ -22,5 +22,6 @@ from .binding import (  # noqa: F401
     new_decode_cache,
     cache_from_prefill,
     target_score,
+    boundary_labels,
     EXPORTED_SYMBOLS,
 )

@@ -19,7 +19,7 @@ _LIB_PATH = os.path.join(_HERE, "libkvpop.so")
 
 KVPOP_BF16, KVPOP_F32 = 0, 1
 CALL_THRESHOLDS, CALL_MASKED_FWD, CALL_FUTURE_TARGET, CALL_DECODE = 0, 1, 2, 3
-CALL_CACHE_FROM_PREFILL, CALL_TARGET_SCORE = 4, 5
+CALL_CACHE_FROM_PREFILL, CALL_TARGET_SCORE, CALL_BOUNDARY_LABELS = 4, 5, 6
 
 EXPORTED_SYMBOLS = (
     "kvpop_workspace_size",
@@ -29,6 +29,7 @@ EXPORTED_SYMBOLS = (
     "kvpop_decode_step",
     "kvpop_cache_from_prefill",
     "kvpop_target_score",
+    "kvpop_boundary_labels",
     "kvpop_status_string",
     "kvpop_abi_version",
 )
@@ -77,8 +78,10 @@ def lib() -> ctypes.CDLL:
                                         vp, sz, vp]
         L.kvpop_cache_from_prefill.argtypes = [P, ctypes.POINTER(_Cache), vp, vp, vp, vp, vp, vp]
         L.kvpop_target_score.argtypes = [P, vp, ctypes.c_float, vp, vp]
+        L.kvpop_boundary_labels.argtypes = [P, vp, vp, ctypes.c_int32, vp, vp, vp]
         for f in ("kvpop_thresholds", "kvpop_masked_attn_fwd", "kvpop_future_target",
-                  "kvpop_decode_step", "kvpop_cache_from_prefill", "kvpop_target_score"):
+                  "kvpop_decode_step", "kvpop_cache_from_prefill", "kvpop_target_score",
+                  "kvpop_boundary_labels"):
             getattr(L, f).restype = ctypes.c_int
         L.kvpop_status_string.argtypes = [ctypes.c_int]
         L.kvpop_status_string.restype = ctypes.c_char_p
@@ -336,3 +339,25 @@ def target_score(target: torch.Tensor, n_kv_heads: int, window: int, eps: float,
     _status(lib().kvpop_target_score(ctypes.byref(c), _vp(target), float(eps), _vp(score),
                                      _stream(dev)), "kvpop_target_score")
     return score
+
+
+def boundary_labels(score: torch.Tensor, log_gamma: torch.Tensor, decay_step: int, sink: int,
+                    window: int, topk: int, t_bnd: Optional[torch.Tensor] = None,
+                    y: Optional[torch.Tensor] = None):
+    """t_bnd, y = boundary_labels(score[b, Hkv, S], log_gamma[Hkv], n, s, w, k):
+    the teacher's boundary token and label of every query row (see
+    kvpop_boundary_labels)."""
+    b, hkv, S = score.shape
+    dev = score.device
+    _need(score, "score", (b, hkv, S), torch.float32)
+    _need(log_gamma, "log_gamma", (hkv,), torch.float32, dev)
+    t_bnd = torch.empty((b, hkv, S), dtype=torch.int32, device=dev) if t_bnd is None else t_bnd
+    y = torch.empty((b, hkv, S), dtype=torch.int32, device=dev) if y is None else y
+    _need(t_bnd, "t_bnd", (b, hkv, S), torch.int32, dev)
+    _need(y, "y", (b, hkv, S), torch.int32, dev)
+    pr = Problem(b, hkv, hkv, S, 128, sink, window, topk, 0.0, 0, 0)
+    c = pr.c()
+    _status(lib().kvpop_boundary_labels(ctypes.byref(c), _vp(score), _vp(log_gamma),
+                                        int(decay_step), _vp(t_bnd), _vp(y), _stream(dev)),
+            "kvpop_boundary_labels")
+    return t_bnd, y

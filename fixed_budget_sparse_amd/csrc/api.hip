@@ -28,7 +28,8 @@ kvpop_status make_dims(int32_t call, const kvpop_problem* pr, Dims* d) {
   if (!dtype_ok(pr->qkv_dtype) || !dtype_ok(pr->out_dtype)) return KVPOP_ERR_ARG;
   if (!(pr->softmax_scale == pr->softmax_scale) || isinf(pr->softmax_scale)) return KVPOP_ERR_ARG;
   const int G = pr->n_q_heads / pr->n_kv_heads;
-  if (call != KVPOP_CALL_THRESHOLDS && call != KVPOP_CALL_TARGET_SCORE) {
+  if (call != KVPOP_CALL_THRESHOLDS && call != KVPOP_CALL_TARGET_SCORE &&
+      call != KVPOP_CALL_BOUNDARY_LABELS) {
     if (pr->head_dim != 64 && pr->head_dim != 128) return KVPOP_ERR_UNSUPPORTED;
     if (G > 32) return KVPOP_ERR_UNSUPPORTED;
   }
@@ -162,6 +163,18 @@ KVPOP_EXPORT kvpop_status kvpop_target_score(const kvpop_problem* pr, const floa
   if (!target || !score) return KVPOP_ERR_ARG;
   if (!(eps >= 0.0f) || isinf(eps)) return KVPOP_ERR_ARG;
   return finish(kvpop::launch_target_score(d, target, eps, score, stream));
+}
+
+KVPOP_EXPORT kvpop_status kvpop_boundary_labels(const kvpop_problem* pr, const float* score,
+                                                const float* log_gamma, int32_t decay_step,
+                                                int32_t* t_bnd, int32_t* y, hipStream_t stream) {
+  Dims d;
+  kvpop_status st = make_dims(KVPOP_CALL_BOUNDARY_LABELS, pr, &d);
+  if (st != KVPOP_OK) return st;
+  if (!score || !log_gamma || !t_bnd || !y) return KVPOP_ERR_ARG;
+  if (decay_step < 1) return KVPOP_ERR_ARG;
+  if (d.S > kvpop::labels_max_seq()) return KVPOP_ERR_UNSUPPORTED;
+  return finish(kvpop::launch_boundary_labels(d, score, log_gamma, decay_step, t_bnd, y, stream));
 }
 
 KVPOP_EXPORT const char* kvpop_status_string(kvpop_status st) {

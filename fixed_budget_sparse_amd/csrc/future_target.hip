@@ -155,9 +155,13 @@ __global__ __launch_bounds__(kThreads, 2) void future_target_kernel(TgtArgs a) {
     if (tid < kChunk) nlse[buf][tid] = d0 + tid < S ? -stage_lse * kLog2e : kNegInf;
   };
 
-  float sum[kRB];
+  // four partial sums per row block (by column mod 4), so consecutive adds
+  // of a group do not wait on each other
+  float sum[kRB][4];
 #pragma unroll
-  for (int rb = 0; rb < kRB; ++rb) sum[rb] = 0.0f;
+  for (int rb = 0; rb < kRB; ++rb)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) sum[rb][r] = 0.0f;
   const int nchunks = (S - d_start + kChunk - 1) / kChunk;
   load_chunk(d_start);
   store_chunk(0, d_start);
@@ -201,7 +205,7 @@ __global__ __launch_bounds__(kThreads, 2) void future_target_kernel(TgtArgs a) {
             const int d = d0 + dl + r;
             p = ((d >= rbase + 32 * rb + li + w) & (d < S)) ? p : 0.0f;
           }
-          sum[rb] += p;
+          sum[rb][r] += p;
         }
     }
   };
@@ -217,7 +221,9 @@ __global__ __launch_bounds__(kThreads, 2) void future_target_kernel(TgtArgs a) {
     constexpr int kPer = 32 / NK;            // scores per group: 4, all with one bias vector
     const uint16_t* ql = (const uint16_t*)q_lds[mbuf] + (32 * mcb + li) * Gm::QS + 8 * hh;
     const float* nb = &nlse[ebuf][32 * ecb + 4 * hh];
-    // operands two k-steps ahead, bias one group ahead
+    // operands two k-steps ahead, bias one group ahead; each group reads its
+    // bias before its operand, so the next group waits only for the bias and
+    // the operand read stays in flight
     bf16x8 a0{}, a1{};
     f32x4 b0{};
     if constexpr (kM) {
@@ -229,12 +235,12 @@ __global__ __launch_bounds__(kThreads, 2) void future_target_kernel(TgtArgs a) {
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int ks = 0; ks < NK; ++ks) {
-      bf16x8 a2 = a1;
-      if constexpr (kM)
-        if (ks + 2 < NK) a2 = as_bf16x8(*(const uint4*)(ql + 16 * (ks + 2)));
       f32x4 b1 = b0;
       if constexpr (kE)
         if (ks + 1 < NK) b1 = *(const f32x4*)(nb + 8 * ((((ks + 1) * kPer) & 15) >> 2));
+      bf16x8 a2 = a1;
+      if constexpr (kM)
+        if (ks + 2 < NK) a2 = as_bf16x8(*(const uint4*)(ql + 16 * (ks + 2)));
       if constexpr (kM) {
         accM[0] = mfma32x32x16(a0, kop[0][ks], accM[0]);
         accM[1] = mfma32x32x16(a0, kop[1][ks], accM[1]);
@@ -248,7 +254,7 @@ __global__ __launch_bounds__(kThreads, 2) void future_target_kernel(TgtArgs a) {
             const int d = d0E + 32 * ecb + 8 * (e >> 2) + 4 * hh + (e & 3);
             p = ((d >= rbase + 32 * rb + li + w) & (d < S)) ? p : 0.0f;
           }
-          sum[rb] += p;
+          sum[rb][e & 3] += p;
         }
       }
       a0 = a1;
@@ -322,7 +328,8 @@ __global__ __launch_bounds__(kThreads, 2) void future_target_kernel(TgtArgs a) {
 
 #pragma unroll
   for (int rb = 0; rb < kRB; ++rb) {
-    const float tot = sum[rb] + __shfl_xor(sum[rb], 32);
+    const float part = (sum[rb][0] + sum[rb][1]) + (sum[rb][2] + sum[rb][3]);
+    const float tot = part + __shfl_xor(part, 32);
     const int t = rbase + 32 * rb + li;
     if (hh == 0 && t < S) out[t] = tot > 0.0f ? log2f(tot) * kLn2 : kNegInf;
   }

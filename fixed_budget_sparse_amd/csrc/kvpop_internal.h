@@ -55,4 +55,8 @@ hipError_t launch_cache_from_prefill(const Dims& d, const CacheArgs& c, const vo
 hipError_t launch_target_score(const Dims& d, const float* target, float eps, float* score,
                                hipStream_t st);
 
+int labels_max_seq();
+hipError_t launch_boundary_labels(const Dims& d, const float* score, const float* log_gamma,
+                                  int decay_step, int32_t* t_bnd, int32_t* y, hipStream_t st);
+
 }  // namespace kvpop

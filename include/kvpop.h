@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define KVPOP_ABI_VERSION 2
+#define KVPOP_ABI_VERSION 3
 
 typedef enum {
   KVPOP_OK = 0,
@@ -60,7 +60,8 @@ typedef enum {
   KVPOP_CALL_FUTURE_TARGET = 2,
   KVPOP_CALL_DECODE = 3,
   KVPOP_CALL_CACHE_FROM_PREFILL = 4,
-  KVPOP_CALL_TARGET_SCORE = 5
+  KVPOP_CALL_TARGET_SCORE = 5,
+  KVPOP_CALL_BOUNDARY_LABELS = 6
 } kvpop_call;
 
 /* Problem description shared by all calls.
@@ -214,6 +215,29 @@ kvpop_status kvpop_cache_from_prefill(const kvpop_problem* pr, const kvpop_cache
  * Uses no workspace. */
 kvpop_status kvpop_target_score(const kvpop_problem* pr, const float* target, float eps,
                                 float* score, hipStream_t stream);
+
+/* Teacher boundary labels ([Notes] §2.2: the decayed target score
+ * r(q, t) = r_t + floor((q - t)/n) log(gamma_h), the teacher's top-k over
+ * E(q) = {t | s <= t <= q - w}, the boundary token t_bnd and the label y of
+ * the newcomer t_new = q - w).  For each (sequence, KV head, query q):
+ *   the decayed score is computed in float32 as one rounded product and one
+ *   rounded sum (NaN counts as -inf, -0 as +0); the teacher keeps the first
+ *   min(k, |E(q)|) tokens of E(q) in the order (decayed score descending,
+ *   index ascending);
+ *   t_bnd  [batch, Hkv, S] int32 out: the last kept token in that order (it may
+ *          be t_new itself)
+ *   y      [batch, Hkv, S] int32 out: +1 if t_new is kept, -1 if it is not
+ *   rows with q - w < s (no newcomer) get t_bnd = -1, y = 0; with k = 0
+ *   nothing is kept and rows with a newcomer get t_bnd = -1, y = -1.
+ *   score      [batch, Hkv, S] float: the target score r_t (kvpop_target_score)
+ *   log_gamma  [Hkv] float (device): log(gamma_h), expected finite (the pages
+ *              take gamma_h in (0, 1), i.e. a negative value)
+ *   decay_step n >= 1
+ * Requires S <= 32768 (KVPOP_ERR_UNSUPPORTED above); head_dim and the dtypes
+ * are ignored.  Uses no workspace. */
+kvpop_status kvpop_boundary_labels(const kvpop_problem* pr, const float* score,
+                                   const float* log_gamma, int32_t decay_step, int32_t* t_bnd,
+                                   int32_t* y, hipStream_t stream);
 
 const char* kvpop_status_string(kvpop_status st);
 int32_t kvpop_abi_version(void);

@@ -26,7 +26,7 @@ def test_header_symbols_exported():
     assert declared == set(kv.EXPORTED_SYMBOLS)
     for name in declared:
         assert hasattr(L, name), name
-    assert kv.abi_version() == 2
+    assert kv.abi_version() == 3
     assert L.kvpop_status_string(3).decode() == "workspace too small"
 
 
@@ -93,6 +93,18 @@ def test_error_paths_return_before_launch():
                                vp(256), 1 << 40, vp(0)) == 1
     assert L.kvpop_decode_step(ctypes.byref(c), ctypes.byref(cache), *[vp(1)] * 7, vp(256), 16,
                                vp(0)) == 3
+
+
+def test_label_error_paths():
+    L = _lib()
+    vp = ctypes.c_void_p
+    c = _pr().c()
+    assert L.kvpop_boundary_labels(ctypes.byref(c), vp(1), vp(1), 0, vp(1), vp(1), vp(0)) == 1
+    assert L.kvpop_boundary_labels(ctypes.byref(c), vp(1), None, 4, vp(1), vp(1), vp(0)) == 1
+    c = _pr(seq_len=32769).c()
+    assert L.kvpop_boundary_labels(ctypes.byref(c), vp(1), vp(1), 4, vp(1), vp(1), vp(0)) == 2
+    c = _pr(seq_len=0).c()
+    assert L.kvpop_boundary_labels(ctypes.byref(c), vp(1), vp(1), 4, vp(1), vp(1), vp(0)) == 1
 
 
 def test_binding_refuses_cpu_tensors():

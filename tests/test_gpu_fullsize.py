@@ -258,6 +258,35 @@ def test_full_handoff_b2048_then_decode():
     _decode_run(wl, 4608, [4096, 4097, 4350, 4607], out_seqs=[0, 63], handoff_at=4096)
 
 
+def test_full_boundary_labels():
+    """Teacher boundary labels on the 16k layer's shape (8 KV heads, S = 16384,
+    s 16, w 512, k 1520, decay step 64) from seeded stand-in target scores;
+    sampled rows (the first labelled rows, rows around k eligible tokens,
+    random rows and the last rows) are compared exactly with the oracle."""
+    wl = W.QWEN3_4B_S16K
+    announce("full boundary labels 8 x S16384")
+    s, w, k, S = wl.sink, wl.window, wl.topk, wl.seq_len
+    x = W.make_label_inputs(wl)
+    dev = device()
+    tb, y = kv.boundary_labels(torch.from_numpy(x["score"]).to(dev),
+                               torch.from_numpy(x["log_gamma"]).to(dev), W.LABEL_DECAY_STEP,
+                               s, w, k)
+    tb, y = host(tb), host(y)
+    rng = np.random.default_rng(17)
+    rows = sorted(set(list(range(s + w - 3, s + w + 40)) + list(range(s + w + k - 20, s + w + k + 20))
+                      + rng.integers(0, S, 150).tolist() + list(range(S - 30, S))))
+    want_t, want_y = orc.boundary_labels(x["score"], x["log_gamma"], W.LABEL_DECAY_STEP, s, w, k,
+                                         rows=rows)
+    assert np.array_equal(tb[..., rows], want_t[..., rows])
+    assert np.array_equal(y[..., rows], want_y[..., rows])
+    # every row: y in {-1, +1} exactly where a newcomer exists, t_bnd in E(q)
+    q = np.arange(S)
+    lab = q - w >= s
+    assert (y[..., ~lab] == 0).all() and (tb[..., ~lab] == -1).all()
+    assert (np.abs(y[..., lab]) == 1).all()
+    assert ((tb[..., lab] >= s) & (tb[..., lab] <= (q - w)[lab])).all()
+
+
 def test_full_decode_long_131072_steps():
     """8 sequences, B = 4096, decoding to 131072 steps with the constant cache."""
     wl = W.scaled(W.LONG_S128K, batch=8)

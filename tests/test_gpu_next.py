@@ -203,3 +203,53 @@ def test_handoff_then_decode():
             oo, ll = orc.decode_attention(Qd[p, b], K[b], V[b], held[b * hkv:(b + 1) * hkv])
             assert np.abs(host(oa)[b] - oo).max() <= TOL["bf16"]["o"], (p, b)
             assert np.abs(host(la)[b] - ll).max() <= TOL["bf16"]["lse"], (p, b)
+
+
+# ---------------------------------------------------------------- boundary labels
+LABEL_CASES = [
+    # b, Hkv, S, s, w, k, n, log_gamma per head, score kind, rows (None = all)
+    (1, 2, 300, 4, 16, 40, 8, (-0.3, -0.05), "normal", None),
+    (2, 1, 257, 2, 5, 17, 3, (-0.5,), "ties", None),           # ties, NaN, +-inf
+    (1, 2, 200, 3, 7, 0, 4, (-0.2, -0.1), "normal", None),     # k = 0
+    (1, 1, 180, 1, 4, 500, 5, (-0.4,), "normal", None),        # k > S: all eligible kept
+    (1, 2, 220, 0, 0, 25, 1, (-1.0, -0.01), "normal", None),   # n = 1, w = 0, s = 0
+    (1, 1, 240, 2, 3, 30, 6, (0.0,), "ties", None),            # no decay
+    (1, 1, 150, 2, 3, 20, 4, (-0.25,), "equal", None),         # every score equal
+    (1, 2, 5000, 16, 64, 300, 64, (-0.1, -0.02), "normal",     # 16 keys per thread
+     list(range(0, 100)) + list(range(2000, 2040)) + list(range(4900, 5000))),
+    (1, 1, 20000, 16, 128, 1000, 64, (-0.05,), "ties",          # 32 keys per thread
+     list(range(1100, 1160)) + list(range(19900, 20000))),
+]
+
+
+def _label_scores(kind, shape, seed):
+    rng = np.random.default_rng(seed)
+    x = (rng.standard_normal(shape) * 1.5 - 9.5).astype(np.float32)
+    if kind == "ties":
+        x = np.round(x * 4).astype(np.float32) / 4
+        x.flat[rng.integers(0, x.size, max(1, x.size // 30))] = np.nan
+        x.flat[rng.integers(0, x.size, max(1, x.size // 60))] = -np.inf
+        x.flat[rng.integers(0, x.size, max(1, x.size // 60))] = np.inf
+    elif kind == "equal":
+        x[:] = np.float32(-3.0)
+    return x
+
+
+@pytest.mark.parametrize("case", LABEL_CASES,
+                         ids=lambda c: "b{}h{}S{}s{}w{}k{}n{}-{}".format(*c[:7], c[8]))
+def test_boundary_labels_parity(case):
+    b, hkv, S, s, w, k, n, lgs, kind, rows = case
+    announce(f"boundary_labels {case[:9]}")
+    dev = device()
+    score = _label_scores(kind, (b, hkv, S), 91)
+    lg = np.array(lgs, np.float32)
+    tb, y = kv.boundary_labels(to_dev(score), to_dev(lg), n, s, w, k)
+    tb, y = host(tb), host(y)
+    want_t, want_y = orc.boundary_labels(score, lg, n, s, w, k, rows=rows)
+    sel = np.arange(S) if rows is None else np.array(rows)
+    assert np.array_equal(tb[..., sel], want_t[..., sel])
+    assert np.array_equal(y[..., sel], want_y[..., sel])
+    if rows is not None:
+        # rows the oracle skipped still carry a valid label
+        assert set(np.unique(y).tolist()) <= {-1, 0, 1}
+        assert ((tb >= -1) & (tb < S)).all()

@@ -12,6 +12,10 @@ Input recipe (the same for every configuration):
   * Per-token priorities ~ N(0, 1) float32, one per (batch, kv-head, token).
   * Decode steps draw q, k_new, v_new ~ N(0, 1) (rounded like Q/K/V) and a
     priority table prio_table[b, h, t] ~ N(0, 1) for the token leaving the window.
+  * Teacher-label inputs: stand-in target scores r_t ~ N(-9.5, 1.5) float32 per
+    (batch, kv-head, token) (the log of a future attention mass averaged over
+    ~10^4 queries sits near there), per-head log(gamma_h) ~ U(-0.25, -0.01)
+    and a decay step of 64 tokens (the pages give no values for n or gamma).
 
 These stand in for Qwen3-4B/8B attention activations at the sequence lengths
 the KVpop paper trains and evaluates at (arXiv 2607.05061, section 4); no
@@ -72,7 +76,9 @@ WORKLOADS: Dict[str, Workload] = {w.name: w for w in
 
 # tensor ids for the per-tensor seed streams
 _TID = {"q": 0, "k": 1, "v": 2, "prio": 3, "dec_q": 4, "dec_k": 5, "dec_v": 6,
-        "dec_prio": 7}
+        "dec_prio": 7, "label_score": 8, "label_gamma": 9}
+
+LABEL_DECAY_STEP = 64
 
 
 def rng_for(seed: int, config_id: int, tensor: str, extra: int = 0) -> np.random.Generator:
@@ -145,6 +151,20 @@ def make_decode_prio_table(wl: Workload, n_tokens: int | None = None, batch: int
     sd = wl.seed if seed is None else seed
     return rng_for(sd, wl.config_id, "dec_prio").standard_normal(
         size=(b, wl.n_kv_heads, T), dtype=np.float32)
+
+
+def make_label_inputs(wl: Workload, seq_len: int | None = None, batch: int | None = None,
+                      seed: int | None = None):
+    """Teacher-label inputs: score [b, Hkv, S] float32 (stand-in target scores)
+    and log_gamma [Hkv] float32."""
+    b = wl.batch if batch is None else batch
+    S = wl.seq_len if seq_len is None else seq_len
+    sd = wl.seed if seed is None else seed
+    score = (rng_for(sd, wl.config_id, "label_score").standard_normal(
+        size=(b, wl.n_kv_heads, S), dtype=np.float32) * np.float32(1.5) - np.float32(9.5))
+    log_gamma = rng_for(sd, wl.config_id, "label_gamma").uniform(
+        -0.25, -0.01, size=wl.n_kv_heads).astype(np.float32)
+    return {"score": score.astype(np.float32), "log_gamma": log_gamma}
 
 
 def scaled(wl: Workload, **over) -> Workload:
