@@ -222,6 +222,49 @@ def masked_attention(q, k, v, rank, tau, s, w, scale=0.0, rows=None, block=256):
     return O, LSE
 
 
+def masked_attention_backward(q, k, v, rank, tau, s, w, dout, scale=0.0, block=256):
+    """Gradients of the sparse attention forward ([Notes] §2.3: the student's
+    forward over the kept set; its backward is what training the sparse
+    student with distillation needs, [Notes] §2.1) for an upstream gradient
+    ``dout`` of O (the LSE output is taken as not differentiated).  Per query
+    head and row i over the kept keys K_i, with P_it the renormalised
+    probabilities and z_it = scale <q_i, k_t>:
+        dV_t  = sum_i P_it dO_i                  (summed over the query group)
+        dP_it = <dO_i, v_t>,  D_i = sum_t P_it dP_it
+        dZ_it = P_it (dP_it - D_i)               (softmax Jacobian)
+        dQ_i  = scale sum_t dZ_it k_t,  dK_t = scale sum_i dZ_it q_i (group sum).
+    q, dout [b, Hq, S, D]; k, v [b, Hkv, S, D] -> dQ like q, dK and dV like k
+    (float64)."""
+    b, Hq, S, D = q.shape
+    Hkv = k.shape[1]
+    G = Hq // Hkv
+    sc = default_scale(D, scale)
+    dQ = np.zeros((b, Hq, S, D))
+    dK = np.zeros((b, Hkv, S, D))
+    dV = np.zeros((b, Hkv, S, D))
+    for bi in range(b):
+        for hq in range(Hq):
+            h = hq // G                                   # reading R8
+            K = k[bi, h].astype(np.float64)
+            V = v[bi, h].astype(np.float64)
+            for a in range(0, S, block):
+                qs = np.arange(a, min(S, a + block))
+                keep = mask_rows(rank[bi, h], tau[bi, h, qs], qs, s, w)
+                Q = q[bi, hq, qs].astype(np.float64)
+                dO = dout[bi, hq, qs].astype(np.float64)
+                z = np.where(keep, sc * (Q @ K.T), -np.inf)
+                mx = z.max(axis=1, keepdims=True)
+                e = np.where(keep, np.exp(z - mx), 0.0)
+                P = e / e.sum(axis=1, keepdims=True)
+                dP = dO @ V.T
+                Drow = (P * dP).sum(axis=1, keepdims=True)
+                dZ = P * (dP - Drow)
+                dQ[bi, hq, qs] = sc * (dZ @ K)
+                dK[bi, h] += sc * (dZ.T @ Q)
+                dV[bi, h] += P.T @ dO
+    return dQ, dK, dV
+
+
 def dense_causal_attention(q, k, v, scale=0.0, rows=None, block=256):
     """Dense causal attention (every key t <= q kept): the teacher."""
     b, Hq, S, D = q.shape
