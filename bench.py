@@ -112,6 +112,27 @@ def sparse_lse_study(kv, torch, q, kk, lse_sparse, tgt, score, s, w, k, eps):
                                       "min": round(overlap.min().item(), 4)}}
 
 
+def bench_backward(kv, torch, q, kk, v, o, lse, rank, tau, s, w, k, ev, reps=3):
+    """Backward of the step's sparse forward (its O and LSE) for a seeded
+    upstream gradient dO; algorithmic work 8 D flop per kept pair per query
+    head (the dP, dQ, dK and dV products)."""
+    from workloads import QWEN3_4B_S16K, make_grad_device
+    dout = make_grad_device(QWEN3_4B_S16K, q.device)
+    dq, dk, dv = kv.masked_attn_bwd(q, kk, v, o, lse, rank, tau, dout, s, w, k)
+    torch.cuda.synchronize()
+    e0, e1 = ev(), ev()
+    e0.record()
+    for _ in range(reps):
+        kv.masked_attn_bwd(q, kk, v, o, lse, rank, tau, dout, s, w, k, dq=dq, dk=dk, dv=dv)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    Hq, S, D = q.shape[1], q.shape[2], q.shape[3]
+    flop = 8 * D * Hq * fwd_pairs(S, s + w + k)
+    return {"ms": round(ms, 4), "tflops": round(flop / (ms * 1e-3) / 1e12, 2), "flop": flop,
+            "frac_mfma_peak": round(flop / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)}
+
+
 def bench_labels(kv, torch, score, s, w, k, ev, reps=5):
     """Teacher boundary labels over the step's target score (decay step 64,
     seeded per-head log gamma), timed on their own."""
@@ -263,6 +284,7 @@ def main():
     score_us = es.elapsed_time(ee) * 1e3 / 20
     study = sparse_lse_study(kv, torch, q, kk, lse, tgt, score, s, w, k, eps)
     labels = bench_labels(kv, torch, score, s, w, k, ev)
+    backward = bench_backward(kv, torch, q, kk, v, o, lse, rank, tau, s, w, k, ev)
     B = s + w + k
     f_fwd = 4 * D * Hq * fwd_pairs(S, B)
     f_tgt = 2 * D * Hq * tgt_pairs(S, w)
@@ -302,6 +324,7 @@ def main():
                          "GB/s": round(4 * (Hq + Hkv) * S / (score_us * 1e-6) / 1e9, 1)},
         "sparse_lse_study": study,
         "boundary_labels": labels,
+        "backward": backward,
     }
 
     if not args.no_decode:

@@ -23,5 +23,6 @@ from .binding import (  # noqa: F401
     cache_from_prefill,
     target_score,
     boundary_labels,
+    masked_attn_bwd,
     EXPORTED_SYMBOLS,
 )

@@ -19,7 +19,7 @@ _LIB_PATH = os.path.join(_HERE, "libkvpop.so")
 
 KVPOP_BF16, KVPOP_F32 = 0, 1
 CALL_THRESHOLDS, CALL_MASKED_FWD, CALL_FUTURE_TARGET, CALL_DECODE = 0, 1, 2, 3
-CALL_CACHE_FROM_PREFILL, CALL_TARGET_SCORE, CALL_BOUNDARY_LABELS = 4, 5, 6
+CALL_CACHE_FROM_PREFILL, CALL_TARGET_SCORE, CALL_BOUNDARY_LABELS, CALL_MASKED_BWD = 4, 5, 6, 7
 
 EXPORTED_SYMBOLS = (
     "kvpop_workspace_size",
@@ -30,6 +30,7 @@ EXPORTED_SYMBOLS = (
     "kvpop_cache_from_prefill",
     "kvpop_target_score",
     "kvpop_boundary_labels",
+    "kvpop_masked_attn_bwd",
     "kvpop_status_string",
     "kvpop_abi_version",
 )
@@ -79,9 +80,10 @@ def lib() -> ctypes.CDLL:
         L.kvpop_cache_from_prefill.argtypes = [P, ctypes.POINTER(_Cache), vp, vp, vp, vp, vp, vp]
         L.kvpop_target_score.argtypes = [P, vp, ctypes.c_float, vp, vp]
         L.kvpop_boundary_labels.argtypes = [P, vp, vp, ctypes.c_int32, vp, vp, vp]
+        L.kvpop_masked_attn_bwd.argtypes = [P] + [vp] * 12 + [sz, vp]
         for f in ("kvpop_thresholds", "kvpop_masked_attn_fwd", "kvpop_future_target",
                   "kvpop_decode_step", "kvpop_cache_from_prefill", "kvpop_target_score",
-                  "kvpop_boundary_labels"):
+                  "kvpop_boundary_labels", "kvpop_masked_attn_bwd"):
             getattr(L, f).restype = ctypes.c_int
         L.kvpop_status_string.argtypes = [ctypes.c_int]
         L.kvpop_status_string.restype = ctypes.c_char_p
@@ -361,3 +363,40 @@ def boundary_labels(score: torch.Tensor, log_gamma: torch.Tensor, decay_step: in
                                         int(decay_step), _vp(t_bnd), _vp(y), _stream(dev)),
             "kvpop_boundary_labels")
     return t_bnd, y
+
+
+def masked_attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
+                    lse: torch.Tensor, rank: torch.Tensor, tau: torch.Tensor, dout: torch.Tensor,
+                    sink: int, window: int, topk: int, softmax_scale: float = 0.0,
+                    dq: Optional[torch.Tensor] = None, dk: Optional[torch.Tensor] = None,
+                    dv: Optional[torch.Tensor] = None):
+    """dq, dk, dv = masked_attn_bwd(q, k, v, o, lse, rank, tau, dout, s, w, k): the
+    gradients of masked_attn_fwd for the upstream gradient dout of o (see
+    kvpop_masked_attn_bwd); q, k, v, dout bfloat16, o and lse the forward's."""
+    b, hq, S, D = q.shape
+    hkv = k.shape[1]
+    dev = q.device
+    bf = torch.bfloat16
+    _need(q, "q", (b, hq, S, D), bf)
+    _need(k, "k", (b, hkv, S, D), bf, dev)
+    _need(v, "v", (b, hkv, S, D), bf, dev)
+    _need(dout, "dout", (b, hq, S, D), bf, dev)
+    _need(o, "o", (b, hq, S, D), o.dtype, dev)
+    _need(lse, "lse", (b, hq, S), torch.float32, dev)
+    _need(rank, "rank", (b, hkv, S), torch.int32, dev)
+    _need(tau, "tau", (b, hkv, S), torch.int32, dev)
+    f32 = torch.float32
+    dq = torch.empty((b, hq, S, D), dtype=f32, device=dev) if dq is None else dq
+    dk = torch.empty((b, hkv, S, D), dtype=f32, device=dev) if dk is None else dk
+    dv = torch.empty((b, hkv, S, D), dtype=f32, device=dev) if dv is None else dv
+    _need(dq, "dq", (b, hq, S, D), f32, dev)
+    _need(dk, "dk", (b, hkv, S, D), f32, dev)
+    _need(dv, "dv", (b, hkv, S, D), f32, dev)
+    pr = Problem(b, hq, hkv, S, D, sink, window, topk, softmax_scale, _dtype_code(bf),
+                 _dtype_code(o.dtype))
+    ws, n = _workspace(CALL_MASKED_BWD, pr, dev)
+    c = pr.c()
+    _status(lib().kvpop_masked_attn_bwd(ctypes.byref(c), _vp(q), _vp(k), _vp(v), _vp(o), _vp(lse),
+                                        _vp(rank), _vp(tau), _vp(dout), _vp(dq), _vp(dk), _vp(dv),
+                                        _vp(ws), n, _stream(dev)), "kvpop_masked_attn_bwd")
+    return dq, dk, dv

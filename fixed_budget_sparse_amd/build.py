@@ -19,7 +19,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libkvpop.so")
 SOURCES = ["thresholds.hip", "masked_fwd.hip", "future_target.hip", "decode.hip", "handoff.hip",
-           "labels.hip", "api.hip"]
+           "labels.hip", "backward.hip", "api.hip"]
 
 
 def _hipcc() -> str:

@@ -39,7 +39,10 @@ kvpop_status make_dims(int32_t call, const kvpop_problem* pr, Dims* d) {
     if (call == KVPOP_CALL_CACHE_FROM_PREFILL && pr->window < 1) return KVPOP_ERR_ARG;
     if (pr->seq_len < 1) return KVPOP_ERR_ARG;
     if (pr->seq_len > kMaxSeq) return KVPOP_ERR_UNSUPPORTED;
-    if (call == KVPOP_CALL_MASKED_FWD && pr->window < 1) return KVPOP_ERR_ARG;
+    if ((call == KVPOP_CALL_MASKED_FWD || call == KVPOP_CALL_MASKED_BWD) && pr->window < 1)
+      return KVPOP_ERR_ARG;
+    if (call == KVPOP_CALL_MASKED_BWD && pr->qkv_dtype != KVPOP_BF16)
+      return KVPOP_ERR_UNSUPPORTED;
   }
   d->b = pr->batch;
   d->Hq = pr->n_q_heads;
@@ -62,6 +65,7 @@ size_t ws_bytes(int32_t call, const Dims& d) {
     case KVPOP_CALL_MASKED_FWD: return kvpop::fwd_ws_bytes(d);
     case KVPOP_CALL_FUTURE_TARGET: return kvpop::target_ws_bytes(d);
     case KVPOP_CALL_DECODE: return kvpop::decode_ws_bytes(d);
+    case KVPOP_CALL_MASKED_BWD: return kvpop::bwd_ws_bytes(d);
     default: return 0;
   }
 }
@@ -80,7 +84,7 @@ kvpop_status finish(hipError_t e) { return e == hipSuccess ? KVPOP_OK : KVPOP_ER
 
 KVPOP_EXPORT size_t kvpop_workspace_size(int32_t call, const kvpop_problem* pr) {
   Dims d;
-  if (call < KVPOP_CALL_THRESHOLDS || call > KVPOP_CALL_DECODE) return 0;
+  if (call < KVPOP_CALL_THRESHOLDS || call > KVPOP_CALL_MASKED_BWD) return 0;
   if (make_dims(call, pr, &d) != KVPOP_OK) return 0;
   return ws_bytes(call, d);
 }
@@ -163,6 +167,23 @@ KVPOP_EXPORT kvpop_status kvpop_target_score(const kvpop_problem* pr, const floa
   if (!target || !score) return KVPOP_ERR_ARG;
   if (!(eps >= 0.0f) || isinf(eps)) return KVPOP_ERR_ARG;
   return finish(kvpop::launch_target_score(d, target, eps, score, stream));
+}
+
+KVPOP_EXPORT kvpop_status kvpop_masked_attn_bwd(const kvpop_problem* pr, const void* q,
+                                                const void* k, const void* v, const void* o,
+                                                const float* lse, const int32_t* rank,
+                                                const int32_t* tau, const void* dout, float* dq,
+                                                float* dk, float* dv, void* ws, size_t ws_bytes_,
+                                                hipStream_t stream) {
+  Dims d;
+  kvpop_status st = make_dims(KVPOP_CALL_MASKED_BWD, pr, &d);
+  if (st != KVPOP_OK) return st;
+  if (!q || !k || !v || !o || !lse || !rank || !tau || !dout || !dq || !dk || !dv)
+    return KVPOP_ERR_ARG;
+  st = check_ws(KVPOP_CALL_MASKED_BWD, d, ws, ws_bytes_);
+  if (st != KVPOP_OK) return st;
+  return finish(kvpop::launch_masked_bwd(d, q, k, v, o, lse, rank, tau, dout, dq, dk, dv, ws,
+                                         stream));
 }
 
 KVPOP_EXPORT kvpop_status kvpop_boundary_labels(const kvpop_problem* pr, const float* score,

@@ -1,0 +1,576 @@
+// kvpop_masked_attn_bwd: gradients of the fixed-budget sparse attention.
+//
+// The student's forward attends over the kept set of KVpop reading notes §2.3
+// (M[q,t] = 1[t<s] or 1[q-t<w] or (1[t in E(q)] and 1[rank(t) <= tau_q]),
+// causal); training the sparse student (§2.1: distillation against the dense
+// teacher) needs its backward.  With P the renormalised probabilities over the
+// kept keys (rebuilt from the forward's LSE), for an upstream gradient dO:
+//   dP_it = <dO_i, v_t>,  D_i = <dO_i, O_i> (= sum_t P_it dP_it),
+//   dS_it = P_it (dP_it - D_i),
+//   dQ_i = scale sum_t dS_it k_t,  dK_t = scale sum_i dS_it q_i,
+//   dV_t = sum_i P_it dO_i,
+// with dK, dV summed over the query heads that share the KV head.
+//
+// Design (gfx950):
+//  * bwd_dot_kernel: D_i from dO and the forward's O.
+//  * dQ, query-major (bwd_dq_kernel): the forward's tiles (m rows of each of
+//    the G query heads stacked into 256 rows, 8 waves of 32) and its key plan
+//    (sinks, the listed long-range keys of the tile's first row, the band);
+//    per 64-key chunk K and V are gathered into LDS (K also transposed with
+//    the columns permuted to the register layout of dS), then per wave
+//    S^T = K Q^T and dP^T = V dO^T on MFMA, dS in registers, and
+//    dQ^T += K^T dS^T on MFMA with dS as the B operand.
+//  * dK, dV, key-major (bwd_dkdv_kernel): key t is kept by the contiguous rows
+//    [t, q_end(t)] (tau never increases with q), so a tile of keys needs the
+//    rows [min t, max q_end].  bwd_qend_kernel finds q_end(t) by binary search
+//    on tau; bwd_key_order_kernel groups keys into 64-key tiles: keys that
+//    live at most w + 64 rows in token order, the others by q_end (a counting
+//    sort over 64-row buckets), which keeps the rows a tile visits close to
+//    the rows its keys need.  Per tile (2 waves of 32 keys, K and V operands in
+//    registers) the rows stream in 32-row chunks aligned to multiples of 32
+//    (so every key's sums are formed in the same order whatever its tile):
+//    S = Q K^T and dP = dO V^T on MFMA, then dV^T += dO^T P and
+//    dK^T += Q^T dS with Q and dO staged transposed (permuted columns).
+//  * bf16 inputs, float32 accumulation, P and dS rounded to bf16 as MFMA
+//    operands; dQ, dK, dV are written in float32.
+#include "kvpop_device.h"
+#include "kvpop_internal.h"
+
+namespace kvpop {
+namespace {
+
+constexpr int kQThreads = 512;      // dQ: 8 waves x 32 stacked rows
+constexpr int kQChunk = 64;         // dQ: keys per chunk
+constexpr int kKTile = 64;          // dK/dV: keys per workgroup (2 waves x 32)
+constexpr int kKThreads = 128;
+constexpr int kRChunk = 32;         // dK/dV: query rows per chunk
+
+typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
+
+// LDS column of key j (0..63) in a transposed tile whose columns follow the
+// register layout of an MFMA result used as a B operand: column
+// 16 ks + 8 hh + 4 a + r holds key 16 ks + 8 a + 4 hh + r.
+__device__ __forceinline__ int perm_col(int j) {
+  return 16 * (j >> 4) + 8 * ((j >> 2) & 1) + 4 * ((j >> 3) & 1) + (j & 3);
+}
+
+// Keep test of the sparse mask for row q and key t (rank rk), tau_q = tq.
+__device__ __forceinline__ bool kept(int q, int t, int rk, int tq, int s, int w) {
+  return (t >= 0) & (t <= q) & ((t < s) | (q - t < w) | (rk <= tq));
+}
+
+// ---------------------------------------------------------------- D_i
+template <int D, bool kF32Out>
+__global__ __launch_bounds__(256) void bwd_dot_kernel(const uint16_t* __restrict__ dout,
+                                                      const void* __restrict__ o,
+                                                      float* __restrict__ dvec, long long rows) {
+  constexpr int LPR = D / 8;          // lanes per row, 8 elements each
+  constexpr int RPW = 64 / LPR;       // rows per wave
+  const long long wv = ((long long)blockIdx.x * 256 + threadIdx.x) >> 6;
+  const int lane = lane_id();
+  const long long row = wv * RPW + lane / LPR;
+  const int part = lane % LPR;
+  float acc = 0.0f;
+  if (row < rows) {
+    const uint4 u = *(const uint4*)(dout + row * D + part * 8);
+    const uint32_t uw[4] = {u.x, u.y, u.z, u.w};
+    float ov[8];
+    if constexpr (kF32Out) {
+      const float4 a = *(const float4*)((const float*)o + row * D + part * 8);
+      const float4 b = *(const float4*)((const float*)o + row * D + part * 8 + 4);
+      ov[0] = a.x; ov[1] = a.y; ov[2] = a.z; ov[3] = a.w;
+      ov[4] = b.x; ov[5] = b.y; ov[6] = b.z; ov[7] = b.w;
+    } else {
+      const uint4 x = *(const uint4*)((const uint16_t*)o + row * D + part * 8);
+      const uint32_t xw[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        ov[2 * i] = bf16_bits_to_f32(xw[i] & 0xffffu);
+        ov[2 * i + 1] = bf16_bits_to_f32(xw[i] >> 16);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      acc += bf16_bits_to_f32(uw[i] & 0xffffu) * ov[2 * i];
+      acc += bf16_bits_to_f32(uw[i] >> 16) * ov[2 * i + 1];
+    }
+  }
+#pragma unroll
+  for (int off = LPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
+  if (part == 0 && row < rows) dvec[row] = acc;
+}
+
+// ---------------------------------------------------------------- key plan
+// q_end(t): the last row keeping key t.  Sinks live to the end; the window
+// keeps rows t .. t + w - 1; after that row q keeps t iff rank(t) <= tau_q,
+// and tau never increases with q, so the rows are a prefix found by bisection.
+__global__ __launch_bounds__(256) void bwd_qend_kernel(const int* __restrict__ rank,
+                                                       const int* __restrict__ tau,
+                                                       int* __restrict__ qend, int S, int s, int w,
+                                                       long long total) {
+  const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (i >= total) return;
+  const long long seg = i / S;
+  const int t = (int)(i - seg * S);
+  const int* tq = tau + seg * S;
+  int e;
+  if (t < s || t + w > S - 1) {
+    e = S - 1;                          // a sink, or the window reaches the end
+  } else {
+    const int r = rank[i];
+    int lo = t + w, hi = S - 1;
+    if (tq[lo] < r) {
+      e = t + w - 1;
+    } else {
+      while (lo < hi) {                 // invariant: tq[lo] >= r
+        const int mid = lo + (hi - lo + 1) / 2;
+        if (tq[mid] >= r) lo = mid;
+        else hi = mid - 1;
+      }
+      e = lo;
+    }
+  }
+  qend[i] = e;
+}
+
+// Key order of the dK/dV tiles, one workgroup per (sequence, KV head):
+// bucket = t / 64 for keys living at most w + 64 rows, else S/64 + q_end / 64;
+// a counting sort over the buckets (order inside a bucket is free).
+__global__ __launch_bounds__(1024) void bwd_key_order_kernel(const int* __restrict__ qend,
+                                                             int* __restrict__ korder, int S,
+                                                             int w) {
+  extern __shared__ int bk[];       // nb counters, then nb offsets
+  const int seg = blockIdx.x, tid = threadIdx.x;
+  const int nb1 = (S + 63) / 64, nb = 2 * nb1;
+  const int* qe = qend + (size_t)seg * S;
+  int* out = korder + (size_t)seg * S;
+  for (int i = tid; i < nb; i += 1024) bk[i] = 0;
+  __syncthreads();
+  auto bucket = [&](int t) {
+    const int e = qe[t];
+    return (e - t + 1 <= w + 64) ? t / 64 : nb1 + e / 64;
+  };
+  for (int t = tid; t < S; t += 1024) atomicAdd(&bk[bucket(t)], 1);
+  __syncthreads();
+  if (tid == 0) {                   // exclusive scan (nb <= 8192)
+    int run = 0;
+    for (int i = 0; i < nb; ++i) {
+      const int c = bk[i];
+      bk[nb + i] = run;
+      run += c;
+    }
+  }
+  __syncthreads();
+  for (int t = tid; t < S; t += 1024) out[atomicAdd(&bk[nb + bucket(t)], 1)] = t;
+}
+
+// ---------------------------------------------------------------- dQ
+struct BwdArgs {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const uint16_t* dout;
+  const float* lse;
+  const float* dvec;
+  const int* rank;
+  const int* tau;
+  const int* qend;
+  const int* korder;
+  const int2* list;
+  const int* count;
+  float* dq;
+  float* dk;
+  float* dv;
+  int S, Hq, Hkv, G, m, ntiles, ktiles, s, w, cap;
+  float scale, scale_log2;
+};
+
+template <int D>
+struct QLds {
+  static constexpr int RS = D + 8;          // row-major rows (bf16 elements)
+  static constexpr int TS = kQChunk + 8;    // transposed rows
+};
+
+template <int D>
+__global__ __launch_bounds__(kQThreads, 1) void bwd_dq_kernel(BwdArgs a) {
+  using L = QLds<D>;
+  constexpr int NKS = D / 16;
+  constexpr int PPR = D / 8;                 // 16-byte pieces per row
+  __shared__ __attribute__((aligned(16))) uint16_t k_lds[kQChunk * L::RS];
+  __shared__ __attribute__((aligned(16))) uint16_t v_lds[kQChunk * L::RS];
+  __shared__ __attribute__((aligned(16))) uint16_t kt_lds[D * L::TS];
+  __shared__ int kd_t[kQChunk], kd_r[kQChunk];
+
+  const int tid = threadIdx.x, lane = lane_id(), wave = wave_id();
+  const int hh = lane >> 5, li = lane & 31;
+  const int tile = blockIdx.x % a.ntiles;
+  const int h = (blockIdx.x / a.ntiles) % a.Hkv;
+  const int b = blockIdx.x / (a.ntiles * a.Hkv);
+  const int S = a.S, s = a.s, w = a.w, m = a.m, G = a.G;
+  const size_t seg = (size_t)b * a.Hkv + h;
+  const int* rank = a.rank + seg * S;
+  const int* tau = a.tau + seg * S;
+  const int q0 = tile * m;
+  const int q_hi = min(q0 + m - 1, S - 1);
+
+  const int rr = wave * 32 + li;
+  const int g = rr / m;
+  const int q = q0 + (rr - g * m);
+  const bool row_ok = g < G && q < S;
+  const int hq = h * G + (g < G ? g : 0);
+  const size_t qrow = ((size_t)b * a.Hq + hq) * S + (row_ok ? q : 0);
+  const int tau_q = row_ok ? tau[q] : -1;
+  const float lse2 = row_ok ? a.lse[qrow] * kLog2e : 0.0f;
+  const float drow = row_ok ? a.dvec[qrow] : 0.0f;
+
+  // key segments of the tile: sinks | long-range | band
+  const int n_sink = min(s, q_hi + 1);
+  const int e_hi = q0 - w;
+  const int tq0 = tau[q0];
+  int n_long = 0;
+  bool listed = false;
+  if (e_hi >= s && tq0 >= 0) {
+    if (tq0 == kInt32Max) {
+      n_long = e_hi - s + 1;
+    } else {
+      listed = true;
+      n_long = a.count[seg * a.ntiles + tile];
+    }
+  }
+  const int band_lo = max(s, q0 - w + 1);
+  const int n_band = max(0, q_hi - band_lo + 1);
+  const int nk = n_sink + n_long + n_band;
+  const int2* lst = a.list + (seg * a.ntiles + tile) * (size_t)a.cap;
+
+  // B operands: Q^T and dO^T of this lane's row, dims [16 ks + 8 hh, +8)
+  bf16x8 qop[NKS], dop[NKS];
+#pragma unroll
+  for (int ks = 0; ks < NKS; ++ks) {
+    uint4 u = make_uint4(0, 0, 0, 0), x = make_uint4(0, 0, 0, 0);
+    if (row_ok) {
+      u = *(const uint4*)(a.q + qrow * D + 16 * ks + 8 * hh);
+      x = *(const uint4*)(a.dout + qrow * D + 16 * ks + 8 * hh);
+    }
+    qop[ks] = as_bf16x8(u);
+    dop[ks] = as_bf16x8(x);
+  }
+  f32x16 dqacc[D / 32];
+#pragma unroll
+  for (int d2 = 0; d2 < D / 32; ++d2) dqacc[d2] = f32x16{};
+
+  const size_t kvbase = seg * (size_t)S * D;
+  for (int c0 = 0; c0 < nk; c0 += kQChunk) {
+    // descriptors (token, rank of the chunk's keys; -1: padding)
+    if (tid < kQChunk) {
+      const int j = c0 + tid;
+      int t = -1, r = 0;
+      if (j < n_sink) {
+        t = j;
+        r = -1;
+      } else if (j < n_sink + n_long) {
+        if (listed) {
+          const int2 e = lst[j - n_sink];
+          t = e.x;
+          r = e.y;
+        } else {
+          t = s + (j - n_sink);
+          r = rank[t];
+        }
+      } else if (j < nk) {
+        t = band_lo + (j - n_sink - n_long);
+        r = rank[t];
+      }
+      kd_t[tid] = t;
+      kd_r[tid] = r;
+    }
+    __syncthreads();
+    // gather K, V rows: row-major K and V, transposed K with permuted columns
+    for (int task = tid; task < kQChunk * PPR; task += kQThreads) {
+      const int j = task / PPR, pc = task % PPR;
+      const int t = kd_t[j];
+      u32x4v kx = {0, 0, 0, 0}, vx = {0, 0, 0, 0};
+      if (t >= 0) {
+        kx = *(const u32x4v*)(a.k + kvbase + (size_t)t * D + 8 * pc);
+        vx = *(const u32x4v*)(a.v + kvbase + (size_t)t * D + 8 * pc);
+      }
+      *(u32x4v*)(k_lds + j * L::RS + 8 * pc) = kx;
+      *(u32x4v*)(v_lds + j * L::RS + 8 * pc) = vx;
+      const int col = perm_col(j);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        kt_lds[(8 * pc + 2 * e) * L::TS + col] = (uint16_t)(kx[e] & 0xffffu);
+        kt_lds[(8 * pc + 2 * e + 1) * L::TS + col] = (uint16_t)(kx[e] >> 16);
+      }
+    }
+    __syncthreads();
+
+    // S^T = K Q^T and dP^T = V dO^T: two 32-key blocks, lane owns its row
+    f32x16 sacc[2], pacc[2];
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk) {
+      sacc[blk] = f32x16{};
+      pacc[blk] = f32x16{};
+      const uint16_t* kl = k_lds + (32 * blk + li) * L::RS + 8 * hh;
+      const uint16_t* vl = v_lds + (32 * blk + li) * L::RS + 8 * hh;
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+        sacc[blk] = mfma32x32x16(as_bf16x8(*(const uint4*)(kl + 16 * ks)), qop[ks], sacc[blk]);
+        pacc[blk] = mfma32x32x16(as_bf16x8(*(const uint4*)(vl + 16 * ks)), dop[ks], pacc[blk]);
+      }
+    }
+    // dS = P (dP - D_i), P = exp(S scale - LSE_i) on kept keys
+    float dsv[2][16];
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int j = 32 * blk + 8 * (e >> 2) + 4 * hh + (e & 3);
+        const bool kp = row_ok && kept(q, kd_t[j], kd_r[j], tau_q, s, w);
+        const float p = kp ? exp2_fast(fmaf(sacc[blk][e], a.scale_log2, -lse2)) : 0.0f;
+        dsv[blk][e] = p * (pacc[blk][e] - drow);
+      }
+    bf16x8 pk[4];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) pk[ks] = pack_bf16x8(&dsv[ks >> 1][8 * (ks & 1)]);
+    // dQ^T += K^T dS^T
+#pragma unroll
+    for (int d2 = 0; d2 < D / 32; ++d2) {
+      const uint16_t* ktl = kt_lds + (32 * d2 + li) * L::TS + 8 * hh;
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+        dqacc[d2] = mfma32x32x16(as_bf16x8(*(const uint4*)(ktl + 16 * ks)), pk[ks], dqacc[d2]);
+    }
+    __syncthreads();   // the chunk's LDS is rewritten next
+  }
+
+  if (row_ok) {
+    float* out = a.dq + qrow * D;
+#pragma unroll
+    for (int d2 = 0; d2 < D / 32; ++d2)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int d = 32 * d2 + 8 * j + 4 * hh;
+        *(float4*)(out + d) = make_float4(dqacc[d2][4 * j] * a.scale, dqacc[d2][4 * j + 1] * a.scale,
+                                          dqacc[d2][4 * j + 2] * a.scale,
+                                          dqacc[d2][4 * j + 3] * a.scale);
+      }
+  }
+}
+
+// ---------------------------------------------------------------- dK, dV
+template <int D>
+struct KLds {
+  static constexpr int RS = D + 8;          // row-major rows
+  static constexpr int TS = kRChunk + 8;    // transposed rows
+};
+
+template <int D>
+__global__ __launch_bounds__(kKThreads) void bwd_dkdv_kernel(BwdArgs a) {
+  using L = KLds<D>;
+  constexpr int NKS = D / 16;
+  constexpr int PPR = D / 8;
+  __shared__ __attribute__((aligned(16))) uint16_t q_lds[kRChunk * L::RS];
+  __shared__ __attribute__((aligned(16))) uint16_t o_lds[kRChunk * L::RS];    // dO
+  __shared__ __attribute__((aligned(16))) uint16_t qt_lds[D * L::TS];
+  __shared__ __attribute__((aligned(16))) uint16_t ot_lds[D * L::TS];
+  __shared__ float r_lse[kRChunk], r_d[kRChunk];
+  __shared__ int r_tau[kRChunk];
+  __shared__ int s_lo[2], s_hi[2];
+
+  const int tid = threadIdx.x, lane = lane_id(), wave = wave_id();
+  const int hh = lane >> 5, li = lane & 31;
+  const int tile = blockIdx.x;
+  const int h = blockIdx.y % a.Hkv, b = blockIdx.y / a.Hkv;
+  const int S = a.S, s = a.s, w = a.w, G = a.G;
+  const size_t seg = (size_t)b * a.Hkv + h;
+  const int* tau = a.tau + seg * S;
+
+  // this lane's key
+  const int slot = tile * kKTile + 32 * wave + li;
+  const int t = slot < S ? a.korder[seg * S + slot] : -1;
+  const int rk = t >= 0 ? a.rank[seg * S + t] : 0;
+  const int qe = t >= 0 ? a.qend[seg * S + t] : -1;
+  const int rk_m = (t >= 0 && t < s) ? -1 : rk;
+  const size_t kvbase = seg * (size_t)S * D;
+
+  // rows the tile needs: [min t, max q_end]
+  int lo = t >= 0 ? t : kInt32Max, hi = t >= 0 ? qe : -1;
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    lo = min(lo, __shfl_xor(lo, off));
+    hi = max(hi, __shfl_xor(hi, off));
+  }
+  if (lane == 0) {
+    s_lo[wave] = lo;
+    s_hi[wave] = hi;
+  }
+
+  // B operands: K^T and V^T of this lane's key, dims [16 ks + 8 hh, +8)
+  bf16x8 kop[NKS], vop[NKS];
+#pragma unroll
+  for (int ks = 0; ks < NKS; ++ks) {
+    uint4 u = make_uint4(0, 0, 0, 0), x = make_uint4(0, 0, 0, 0);
+    if (t >= 0) {
+      u = *(const uint4*)(a.k + kvbase + (size_t)t * D + 16 * ks + 8 * hh);
+      x = *(const uint4*)(a.v + kvbase + (size_t)t * D + 16 * ks + 8 * hh);
+    }
+    kop[ks] = as_bf16x8(u);
+    vop[ks] = as_bf16x8(x);
+  }
+  f32x16 dkacc[D / 32], dvacc[D / 32];
+#pragma unroll
+  for (int d2 = 0; d2 < D / 32; ++d2) {
+    dkacc[d2] = f32x16{};
+    dvacc[d2] = f32x16{};
+  }
+  __syncthreads();
+  const int r_lo = min(s_lo[0], s_lo[1]), r_hi = max(s_hi[0], s_hi[1]);
+
+  for (int gg = 0; gg < G && r_lo <= r_hi; ++gg) {
+    const int hq = h * G + gg;
+    const size_t hrow = ((size_t)b * a.Hq + hq) * S;
+    for (int c0 = (r_lo / kRChunk) * kRChunk; c0 <= r_hi; c0 += kRChunk) {
+      // stage the chunk's rows: Q, dO row-major and transposed (permuted)
+      for (int task = tid; task < kRChunk * PPR; task += kKThreads) {
+        const int i = task / PPR, pc = task % PPR;
+        const int qq = c0 + i;
+        u32x4v qx = {0, 0, 0, 0}, ox = {0, 0, 0, 0};
+        if (qq < S) {
+          qx = *(const u32x4v*)(a.q + (hrow + qq) * D + 8 * pc);
+          ox = *(const u32x4v*)(a.dout + (hrow + qq) * D + 8 * pc);
+        }
+        *(u32x4v*)(q_lds + i * L::RS + 8 * pc) = qx;
+        *(u32x4v*)(o_lds + i * L::RS + 8 * pc) = ox;
+        const int col = perm_col(i);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          qt_lds[(8 * pc + 2 * e) * L::TS + col] = (uint16_t)(qx[e] & 0xffffu);
+          qt_lds[(8 * pc + 2 * e + 1) * L::TS + col] = (uint16_t)(qx[e] >> 16);
+          ot_lds[(8 * pc + 2 * e) * L::TS + col] = (uint16_t)(ox[e] & 0xffffu);
+          ot_lds[(8 * pc + 2 * e + 1) * L::TS + col] = (uint16_t)(ox[e] >> 16);
+        }
+      }
+      if (tid < kRChunk) {
+        const int qq = c0 + tid;
+        const bool ok = qq < S;
+        r_lse[tid] = ok ? a.lse[hrow + qq] * kLog2e : 0.0f;
+        r_d[tid] = ok ? a.dvec[hrow + qq] : 0.0f;
+        r_tau[tid] = ok ? tau[qq] : -1;
+      }
+      __syncthreads();
+
+      // S = Q K^T and dP = dO V^T (32 rows x 32 keys): lane owns its key
+      f32x16 sacc = f32x16{}, pacc = f32x16{};
+      {
+        const uint16_t* ql = q_lds + li * L::RS + 8 * hh;
+        const uint16_t* ol = o_lds + li * L::RS + 8 * hh;
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) {
+          sacc = mfma32x32x16(as_bf16x8(*(const uint4*)(ql + 16 * ks)), kop[ks], sacc);
+          pacc = mfma32x32x16(as_bf16x8(*(const uint4*)(ol + 16 * ks)), vop[ks], pacc);
+        }
+      }
+      float pv[16], dsv[16];
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int i = 8 * (e >> 2) + 4 * hh + (e & 3);
+        const int qq = c0 + i;
+        const bool kp = (qq < S) && kept(qq, t, rk_m, r_tau[i], s, w);
+        const float p = kp ? exp2_fast(fmaf(sacc[e], a.scale_log2, -r_lse[i])) : 0.0f;
+        pv[e] = p;
+        dsv[e] = p * (pacc[e] - r_d[i]);
+      }
+      bf16x8 pp[2], ps[2];
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        pp[ks] = pack_bf16x8(&pv[8 * ks]);
+        ps[ks] = pack_bf16x8(&dsv[8 * ks]);
+      }
+      // dV^T += dO^T P and dK^T += Q^T dS
+#pragma unroll
+      for (int d2 = 0; d2 < D / 32; ++d2) {
+        const uint16_t* otl = ot_lds + (32 * d2 + li) * L::TS + 8 * hh;
+        const uint16_t* qtl = qt_lds + (32 * d2 + li) * L::TS + 8 * hh;
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          dvacc[d2] = mfma32x32x16(as_bf16x8(*(const uint4*)(otl + 16 * ks)), pp[ks], dvacc[d2]);
+          dkacc[d2] = mfma32x32x16(as_bf16x8(*(const uint4*)(qtl + 16 * ks)), ps[ks], dkacc[d2]);
+        }
+      }
+      __syncthreads();   // the chunk's LDS is rewritten next
+    }
+  }
+
+  if (t >= 0) {
+    float* dko = a.dk + kvbase + (size_t)t * D;
+    float* dvo = a.dv + kvbase + (size_t)t * D;
+#pragma unroll
+    for (int d2 = 0; d2 < D / 32; ++d2)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int d = 32 * d2 + 8 * j + 4 * hh;
+        *(float4*)(dko + d) = make_float4(dkacc[d2][4 * j] * a.scale, dkacc[d2][4 * j + 1] * a.scale,
+                                          dkacc[d2][4 * j + 2] * a.scale,
+                                          dkacc[d2][4 * j + 3] * a.scale);
+        *(float4*)(dvo + d) = make_float4(dvacc[d2][4 * j], dvacc[d2][4 * j + 1],
+                                          dvacc[d2][4 * j + 2], dvacc[d2][4 * j + 3]);
+      }
+  }
+}
+
+template <int D>
+void launch_bwd_kernels(const Dims& d, BwdArgs a, const void* o, hipStream_t st) {
+  const long long rows = (long long)d.b * d.Hq * d.S;
+  constexpr int RPB = 4 * (64 / (D / 8));     // rows per 256-thread block
+  const unsigned nblk = (unsigned)((rows + RPB - 1) / RPB);
+  if (d.f32_out)
+    hipLaunchKernelGGL((bwd_dot_kernel<D, true>), dim3(nblk), dim3(256), 0, st, a.dout, o,
+                       (float*)a.dvec, rows);
+  else
+    hipLaunchKernelGGL((bwd_dot_kernel<D, false>), dim3(nblk), dim3(256), 0, st, a.dout, o,
+                       (float*)a.dvec, rows);
+  const long long nq = (long long)a.ntiles * d.Hkv * d.b;
+  hipLaunchKernelGGL((bwd_dq_kernel<D>), dim3((unsigned)nq), dim3(kQThreads), 0, st, a);
+  hipLaunchKernelGGL((bwd_dkdv_kernel<D>), dim3(a.ktiles, d.nseg()), dim3(kKThreads), 0, st, a);
+}
+
+}  // namespace
+
+size_t bwd_ws_bytes(const Dims& d) {
+  const size_t rows = (size_t)d.b * d.Hq * d.S, keys = (size_t)d.nseg() * d.S;
+  return fwd_ws_bytes(d) + align256(rows * 4) + 2 * align256(keys * 4);
+}
+
+hipError_t launch_masked_bwd(const Dims& d, const void* q, const void* k, const void* v,
+                             const void* o, const float* lse, const int* rank, const int* tau,
+                             const void* dout, float* dq, float* dk, float* dv, void* ws,
+                             hipStream_t st) {
+  const FwdPlan pl = launch_fwd_plan(d, rank, tau, ws, st);
+  char* p = (char*)ws + fwd_ws_bytes(d);
+  const size_t rows = (size_t)d.b * d.Hq * d.S, keys = (size_t)d.nseg() * d.S;
+  float* dvec = (float*)p; p += align256(rows * 4);
+  int* qend = (int*)p; p += align256(keys * 4);
+  int* korder = (int*)p;
+
+  hipLaunchKernelGGL(bwd_qend_kernel, dim3((unsigned)((keys + 255) / 256)), dim3(256), 0, st, rank,
+                     tau, qend, d.S, d.s, d.w, (long long)keys);
+  const int nb = 2 * ((d.S + 63) / 64);
+  hipLaunchKernelGGL(bwd_key_order_kernel, dim3(d.nseg()), dim3(1024), (size_t)nb * 2 * 4, st, qend,
+                     korder, d.S, d.w);
+
+  BwdArgs a;
+  a.q = (const uint16_t*)q; a.k = (const uint16_t*)k; a.v = (const uint16_t*)v;
+  a.dout = (const uint16_t*)dout; a.lse = lse; a.dvec = dvec; a.rank = rank; a.tau = tau;
+  a.qend = qend; a.korder = korder; a.list = pl.list; a.count = pl.count;
+  a.dq = dq; a.dk = dk; a.dv = dv;
+  a.S = d.S; a.Hq = d.Hq; a.Hkv = d.Hkv; a.G = d.G; a.m = pl.m; a.ntiles = pl.ntiles;
+  a.ktiles = (d.S + kKTile - 1) / kKTile;
+  a.s = d.s; a.w = d.w; a.cap = pl.cap;
+  a.scale = d.scale;
+  a.scale_log2 = d.scale * 1.4426950408889634f;
+  if (d.D == 128) launch_bwd_kernels<128>(d, a, o, st);
+  else launch_bwd_kernels<64>(d, a, o, st);
+  return hipGetLastError();
+}
+
+}  // namespace kvpop

@@ -32,6 +32,23 @@ hipError_t launch_masked_fwd(const Dims& d, const void* q, const void* k, const 
                              const int* rank, const int* tau, void* o, float* lse,
                              void* ws, hipStream_t st);
 
+// The forward's per-tile key plan (tiles of m query rows per head; listed
+// long-range keys of each tile's first row in rank order), built into the
+// first fwd_ws_bytes(d) bytes of `ws`; the backward reuses it.
+struct FwdPlan {
+  const int2* list;   // [nseg, ntiles, cap] (token, rank)
+  const int* count;   // [nseg, ntiles]
+  int m, ntiles, cap;
+};
+FwdPlan launch_fwd_plan(const Dims& d, const int* rank, const int* tau, void* ws,
+                        hipStream_t st);
+
+size_t bwd_ws_bytes(const Dims& d);
+hipError_t launch_masked_bwd(const Dims& d, const void* q, const void* k, const void* v,
+                             const void* o, const float* lse, const int* rank, const int* tau,
+                             const void* dout, float* dq, float* dk, float* dv, void* ws,
+                             hipStream_t st);
+
 size_t target_ws_bytes(const Dims& d);
 hipError_t launch_future_target(const Dims& d, const void* q, const void* k, const float* lse,
                                 float* target, void* ws, hipStream_t st);

@@ -677,9 +677,8 @@ size_t fwd_ws_bytes(const Dims& d) {
   return bytes;
 }
 
-hipError_t launch_masked_fwd(const Dims& d, const void* q, const void* k, const void* v,
-                             const int* rank, const int* tau, void* o, float* lse, void* ws,
-                             hipStream_t st) {
+FwdPlan launch_fwd_plan(const Dims& d, const int* rank, const int* tau, void* ws,
+                        hipStream_t st) {
   const int nseg = d.nseg(), nt = fwd_ntiles(d), m = fwd_rows_per_head(d);
   const int cap = fwd_list_cap(d);
   char* p = (char*)ws;
@@ -692,6 +691,18 @@ hipError_t launch_masked_fwd(const Dims& d, const void* q, const void* k, const 
                      st, rank, order, d.S, total);
   hipLaunchKernelGGL(tile_list_kernel, dim3(nt, nseg), dim3(256), 0, st, order, tau, d.S, d.s,
                      d.w, m, nt, cap, list, count);
+  FwdPlan pl;
+  pl.list = list; pl.count = count; pl.m = m; pl.ntiles = nt; pl.cap = cap;
+  return pl;
+}
+
+hipError_t launch_masked_fwd(const Dims& d, const void* q, const void* k, const void* v,
+                             const int* rank, const int* tau, void* o, float* lse, void* ws,
+                             hipStream_t st) {
+  const FwdPlan pl = launch_fwd_plan(d, rank, tau, ws, st);
+  const int2* list = pl.list;
+  const int* count = pl.count;
+  const int m = pl.m, nt = pl.ntiles, cap = pl.cap;
 
   FwdArgs a;
   a.q = q; a.k = k; a.v = v; a.rank = rank; a.tau = tau; a.list = list; a.count = count;

@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define KVPOP_ABI_VERSION 3
+#define KVPOP_ABI_VERSION 4
 
 typedef enum {
   KVPOP_OK = 0,
@@ -61,7 +61,8 @@ typedef enum {
   KVPOP_CALL_DECODE = 3,
   KVPOP_CALL_CACHE_FROM_PREFILL = 4,
   KVPOP_CALL_TARGET_SCORE = 5,
-  KVPOP_CALL_BOUNDARY_LABELS = 6
+  KVPOP_CALL_BOUNDARY_LABELS = 6,
+  KVPOP_CALL_MASKED_BWD = 7
 } kvpop_call;
 
 /* Problem description shared by all calls.
@@ -238,6 +239,30 @@ kvpop_status kvpop_target_score(const kvpop_problem* pr, const float* target, fl
 kvpop_status kvpop_boundary_labels(const kvpop_problem* pr, const float* score,
                                    const float* log_gamma, int32_t decay_step, int32_t* t_bnd,
                                    int32_t* y, hipStream_t stream);
+
+/* Backward of kvpop_masked_attn_fwd: the gradients that training the sparse
+ * student needs ([Notes] §2.3: attention over the kept set M[q,t]; §2.1:
+ * distillation against the dense teacher).  With P the kept-set
+ * probabilities rebuilt from the forward's LSE and dO the gradient of O:
+ *   D_i = <dO_i, O_i>,  dS_it = P_it (<dO_i, v_t> - D_i),
+ *   dq_i = scale sum_t dS_it k_t,  dk_t = scale sum_i dS_it q_i,
+ *   dv_t = sum_i P_it dO_i,
+ * dk and dv summed over the query heads that share the KV head; the LSE
+ * output is taken as not differentiated.
+ *   q, dout [batch, Hq, S, D] bf16; k, v [batch, Hkv, S, D] bf16
+ *   o      [batch, Hq, S, D] out_dtype: the forward's output
+ *   lse    [batch, Hq, S] float: the forward's LSE
+ *   rank, tau  the same arrays the forward took
+ *   dq     [batch, Hq, S, D] float out; dk, dv [batch, Hkv, S, D] float out
+ *          (every element written)
+ * Requires qkv_dtype = KVPOP_BF16 (KVPOP_ERR_UNSUPPORTED otherwise),
+ * D in {64, 128}, w >= 1; P and dS are rounded to bf16 as MFMA operands,
+ * sums in float32.  Workspace: kvpop_workspace_size(KVPOP_CALL_MASKED_BWD). */
+kvpop_status kvpop_masked_attn_bwd(const kvpop_problem* pr, const void* q, const void* k,
+                                   const void* v, const void* o, const float* lse,
+                                   const int32_t* rank, const int32_t* tau, const void* dout,
+                                   float* dq, float* dk, float* dv, void* ws, size_t ws_bytes,
+                                   hipStream_t stream);
 
 const char* kvpop_status_string(kvpop_status st);
 int32_t kvpop_abi_version(void);

@@ -33,3 +33,10 @@ def announce(msg: str):
 # float32 inputs: float32 accumulation only, so much tighter)
 TOL = {"bf16": {"o": 1e-2, "lse": 1e-3, "tgt": 5e-3},
        "f32": {"o": 1e-4, "lse": 1e-4, "tgt": 1e-4}}
+
+# Gradients of the masked attention: P and dS enter the MFMA products rounded
+# to bfloat16 (relative error 2^-9 per term) and every sum is float32, so each
+# gradient tensor is held to 1e-2 relative in the Frobenius norm and 2e-2 of
+# its largest entry per element; one wrongly masked key moves an element by
+# O(its size).
+BWD_TOL = {"fro": 1e-2, "max": 2e-2}

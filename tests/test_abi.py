@@ -26,7 +26,7 @@ def test_header_symbols_exported():
     assert declared == set(kv.EXPORTED_SYMBOLS)
     for name in declared:
         assert hasattr(L, name), name
-    assert kv.abi_version() == 3
+    assert kv.abi_version() == 4
     assert L.kvpop_status_string(3).decode() == "workspace too small"
 
 
@@ -105,6 +105,21 @@ def test_label_error_paths():
     assert L.kvpop_boundary_labels(ctypes.byref(c), vp(1), vp(1), 4, vp(1), vp(1), vp(0)) == 2
     c = _pr(seq_len=0).c()
     assert L.kvpop_boundary_labels(ctypes.byref(c), vp(1), vp(1), 4, vp(1), vp(1), vp(0)) == 1
+
+
+def test_backward_error_paths():
+    L = _lib()
+    vp = ctypes.c_void_p
+    args = [vp(1)] * 11
+    c = _pr(qkv_dtype=1).c()          # float32 inputs: not implemented
+    assert L.kvpop_masked_attn_bwd(ctypes.byref(c), *args, vp(256), 1 << 40, vp(0)) == 2
+    c = _pr(window=0).c()
+    assert L.kvpop_masked_attn_bwd(ctypes.byref(c), *args, vp(256), 1 << 40, vp(0)) == 1
+    c = _pr().c()
+    assert L.kvpop_masked_attn_bwd(ctypes.byref(c), *args, vp(256), 16, vp(0)) == 3
+    assert L.kvpop_masked_attn_bwd(ctypes.byref(c), *args[:10], None, vp(256), 1 << 40,
+                                   vp(0)) == 1
+    assert kv.workspace_size(B.CALL_MASKED_BWD, _pr()) > kv.workspace_size(1, _pr())
 
 
 def test_binding_refuses_cpu_tensors():

@@ -19,7 +19,7 @@ import torch
 import fixed_budget_sparse_amd as kv
 import oracle as orc
 import workloads as W
-from gpu_util import TOL, announce, device, host
+from gpu_util import BWD_TOL, TOL, announce, device, host
 
 pytestmark = pytest.mark.gpu
 
@@ -285,6 +285,38 @@ def test_full_boundary_labels():
     assert (y[..., ~lab] == 0).all() and (tb[..., ~lab] == -1).all()
     assert (np.abs(y[..., lab]) == 1).all()
     assert ((tb[..., lab] >= s) & (tb[..., lab] <= (q - w)[lab])).all()
+
+
+def test_full_masked_bwd_one_kv_head():
+    """Backward of the 16k layer (all 32 query / 8 KV heads on the GPU); the
+    oracle recomputes KV head 5 and its four query heads in full (every
+    element of dq, dk, dv), with the tolerance of the reduced cases."""
+    BWD_FRO, BWD_MAX = BWD_TOL["fro"], BWD_TOL["max"]
+    wl = W.QWEN3_4B_S16K
+    announce("full masked_attn_bwd 32 x S16384, KV head 5 checked")
+    S, s, w, k = wl.seq_len, wl.sink, wl.window, wl.topk
+    x = _inputs(wl)
+    dev = device()
+    dout = W.make_grad_device(wl, dev)
+    rank, tau = kv.thresholds(x["prio"], s, w, k)
+    o, lse = kv.masked_attn_fwd(x["q"], x["k"], x["v"], rank, tau, s, w, k,
+                                out_dtype=torch.bfloat16)
+    dq, dk, dv = kv.masked_attn_bwd(x["q"], x["k"], x["v"], o, lse, rank, tau, dout, s, w, k)
+    torch.cuda.synchronize()
+    h, G = 5, wl.n_q_heads // wl.n_kv_heads
+    qs = slice(h * G, (h + 1) * G)
+    prio = host(x["prio"][:, h:h + 1])
+    rank_o = orc.priority_ranks(prio)
+    tau_o = orc.thresholds_by_selection(rank_o, s, w, k)
+    rq, rk, rv = orc.masked_attention_backward(host(x["q"][:, qs]), host(x["k"][:, h:h + 1]),
+                                               host(x["v"][:, h:h + 1]), rank_o, tau_o, s, w,
+                                               host(dout[:, qs]))
+    for name, got, ref in (("dq", host(dq[:, qs]), rq), ("dk", host(dk[:, h:h + 1]), rk),
+                           ("dv", host(dv[:, h:h + 1]), rv)):
+        err = got.astype(np.float64) - ref
+        fro = np.linalg.norm(err) / np.linalg.norm(ref)
+        mx = np.abs(err).max() / np.abs(ref).max()
+        assert fro <= BWD_FRO and mx <= BWD_MAX, (name, fro, mx)
 
 
 def test_full_decode_long_131072_steps():

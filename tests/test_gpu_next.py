@@ -8,7 +8,7 @@ import torch
 
 import fixed_budget_sparse_amd as kv
 import oracle as orc
-from gpu_util import TOL, announce, device, host, to_dev
+from gpu_util import BWD_TOL, TOL, announce, device, host, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -253,3 +253,42 @@ def test_boundary_labels_parity(case):
         # rows the oracle skipped still carry a valid label
         assert set(np.unique(y).tolist()) <= {-1, 0, 1}
         assert ((tb >= -1) & (tb < S)).all()
+
+
+# ---------------------------------------------------------------- backward
+BWD_FRO, BWD_MAX = BWD_TOL["fro"], BWD_TOL["max"]
+BWD_CASES = [
+    # b, Hq, Hkv, S, D, s, w, k, forward output dtype
+    (1, 8, 2, 300, 128, 4, 16, 40, "f32"),
+    (2, 4, 1, 200, 64, 3, 9, 20, "bf16"),       # D = 64, bf16 O
+    (1, 4, 4, 257, 128, 2, 7, 0, "f32"),        # k = 0, G = 1
+    (1, 8, 1, 130, 128, 1, 1, 500, "f32"),      # k >= S: dense causal; w = 1; G = 8
+    (1, 2, 2, 64, 128, 0, 5, 10, "f32"),        # s = 0
+    (1, 8, 2, 1500, 128, 8, 64, 200, "bf16"),   # several tiles, listed long-range keys
+]
+
+
+@pytest.mark.parametrize("case", BWD_CASES, ids=lambda c: "b{}q{}kv{}S{}D{}s{}w{}k{}-{}".format(*c))
+def test_masked_attn_bwd_parity(case):
+    b, hq, hkv, S, D, s, w, k, odt = case
+    announce(f"masked_attn_bwd {case}")
+    device()
+    td = torch.bfloat16
+    q = _bf16(_rand((b, hq, S, D), 101))
+    kk = _bf16(_rand((b, hkv, S, D), 102, scale_keys=True))
+    v = _bf16(_rand((b, hkv, S, D), 103))
+    dout = _bf16(_rand((b, hq, S, D), 104))
+    prio = _rand((b, hkv, S), 105)
+    rank, tau = kv.thresholds(to_dev(prio), s, w, k)
+    o, lse = kv.masked_attn_fwd(to_dev(q, td), to_dev(kk, td), to_dev(v, td), rank, tau, s, w, k,
+                                out_dtype=torch.float32 if odt == "f32" else td)
+    dq, dk, dv = kv.masked_attn_bwd(to_dev(q, td), to_dev(kk, td), to_dev(v, td), o, lse, rank, tau,
+                                    to_dev(dout, td), s, w, k)
+    rank_o = orc.priority_ranks(prio)
+    tau_o = orc.thresholds_by_selection(rank_o, s, w, k)
+    rq, rk, rv = orc.masked_attention_backward(q, kk, v, rank_o, tau_o, s, w, dout)
+    for name, got, ref in (("dq", host(dq), rq), ("dk", host(dk), rk), ("dv", host(dv), rv)):
+        err = got.astype(np.float64) - ref
+        fro = np.linalg.norm(err) / np.linalg.norm(ref)
+        mx = np.abs(err).max() / np.abs(ref).max()
+        assert fro <= BWD_FRO and mx <= BWD_MAX, (name, fro, mx)

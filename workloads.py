@@ -12,6 +12,7 @@ Input recipe (the same for every configuration):
   * Per-token priorities ~ N(0, 1) float32, one per (batch, kv-head, token).
   * Decode steps draw q, k_new, v_new ~ N(0, 1) (rounded like Q/K/V) and a
     priority table prio_table[b, h, t] ~ N(0, 1) for the token leaving the window.
+  * Upstream gradients dO of the attention output ~ N(0, 1), rounded like Q.
   * Teacher-label inputs: stand-in target scores r_t ~ N(-9.5, 1.5) float32 per
     (batch, kv-head, token) (the log of a future attention mass averaged over
     ~10^4 queries sits near there), per-head log(gamma_h) ~ U(-0.25, -0.01)
@@ -76,7 +77,7 @@ WORKLOADS: Dict[str, Workload] = {w.name: w for w in
 
 # tensor ids for the per-tensor seed streams
 _TID = {"q": 0, "k": 1, "v": 2, "prio": 3, "dec_q": 4, "dec_k": 5, "dec_v": 6,
-        "dec_prio": 7, "label_score": 8, "label_gamma": 9}
+        "dec_prio": 7, "label_score": 8, "label_gamma": 9, "dout": 10}
 
 LABEL_DECAY_STEP = 64
 
@@ -211,6 +212,15 @@ def make_prefill_device(wl: Workload, device, seq_len: int | None = None,
     v = _device_normal((b, wl.n_kv_heads, S, D), torch_seed(sd, c, "v"), device, wl.dtype)
     prio = _device_normal((b, wl.n_kv_heads, S, 1), torch_seed(sd, c, "prio"), device, "f32")
     return {"q": q, "k": k, "v": v, "prio": prio[..., 0].contiguous()}
+
+
+def make_grad_device(wl: Workload, device, seq_len: int | None = None, seed: int | None = None):
+    """Upstream gradient dO ~ N(0, 1) of the attention output, [b, Hq, S, D],
+    rounded like Q (bfloat16 for bfloat16 workloads), on the device."""
+    S = wl.seq_len if seq_len is None else seq_len
+    sd = wl.seed if seed is None else seed
+    return _device_normal((wl.batch, wl.n_q_heads, S, wl.head_dim),
+                          torch_seed(sd, wl.config_id, "dout"), device, wl.dtype)
 
 
 def make_decode_stream_device(wl: Workload, device, n_steps: int, batch: int | None = None,
