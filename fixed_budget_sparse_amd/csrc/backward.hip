@@ -28,11 +28,17 @@
 //    sort over 64-row buckets), which keeps the rows a tile visits close to
 //    the rows its keys need.  Per tile (2 waves of 32 keys, K and V operands in
 //    registers) the rows stream in 32-row chunks aligned to multiples of 32
-//    (so every key's sums are formed in the same order whatever its tile):
+//    (so every key's sums are formed in the same order whatever its tile),
+//    double-buffered in LDS, with the loads of the chunk after next in flight
+//    during the math (two register stages), workgroups mapped so that each
+//    XCD works through whole (sequence, KV head)s in plan order:
 //    S = Q K^T and dP = dO V^T on MFMA, then dV^T += dO^T P and
-//    dK^T += Q^T dS with Q and dO staged transposed (permuted columns).
+//    dK^T += Q^T dS with Q and dO staged transposed (permuted columns, one
+//    32-bit word per dim for each pair of rows).
 //  * bf16 inputs, float32 accumulation, P and dS rounded to bf16 as MFMA
 //    operands; dQ, dK, dV are written in float32.
+#include <type_traits>
+
 #include "kvpop_device.h"
 #include "kvpop_internal.h"
 
@@ -243,17 +249,19 @@ __global__ __launch_bounds__(kQThreads, 1) void bwd_dq_kernel(BwdArgs a) {
   const int2* lst = a.list + (seg * a.ntiles + tile) * (size_t)a.cap;
 
   // B operands: Q^T and dO^T of this lane's row, dims [16 ks + 8 hh, +8)
+  // (unconditional loads of a valid row, zeroed for padding rows, completed
+  // here so that the chunk loop does not wait on them)
   bf16x8 qop[NKS], dop[NKS];
 #pragma unroll
   for (int ks = 0; ks < NKS; ++ks) {
-    uint4 u = make_uint4(0, 0, 0, 0), x = make_uint4(0, 0, 0, 0);
-    if (row_ok) {
-      u = *(const uint4*)(a.q + qrow * D + 16 * ks + 8 * hh);
-      x = *(const uint4*)(a.dout + qrow * D + 16 * ks + 8 * hh);
-    }
-    qop[ks] = as_bf16x8(u);
-    dop[ks] = as_bf16x8(x);
+    u32x4v u = *(const u32x4v*)(a.q + qrow * D + 16 * ks + 8 * hh);
+    u32x4v x = *(const u32x4v*)(a.dout + qrow * D + 16 * ks + 8 * hh);
+    if (!row_ok) u = x = u32x4v{0, 0, 0, 0};
+    qop[ks] = __builtin_bit_cast(bf16x8, u);
+    dop[ks] = __builtin_bit_cast(bf16x8, x);
   }
+#pragma unroll
+  for (int ks = 0; ks < NKS; ++ks) asm volatile("" : "+v"(qop[ks]), "+v"(dop[ks]));
   f32x16 dqacc[D / 32];
 #pragma unroll
   for (int d2 = 0; d2 < D / 32; ++d2) dqacc[d2] = f32x16{};
@@ -360,27 +368,37 @@ __global__ __launch_bounds__(kQThreads, 1) void bwd_dq_kernel(BwdArgs a) {
 // ---------------------------------------------------------------- dK, dV
 template <int D>
 struct KLds {
-  static constexpr int RS = D + 8;          // row-major rows
+  static constexpr int RS = D + 8;          // row-major rows (bf16 elements)
   static constexpr int TS = kRChunk + 8;    // transposed rows
+  // one stage: Q and dO row-major and transposed, then LSE, D and tau per row
+  static constexpr int kQ = 0;
+  static constexpr int kO = kQ + kRChunk * RS * 2;
+  static constexpr int kQT = kO + kRChunk * RS * 2;
+  static constexpr int kOT = kQT + D * TS * 2;
+  static constexpr int kLse = kOT + D * TS * 2;
+  static constexpr int kD = kLse + kRChunk * 4;
+  static constexpr int kTau = kD + kRChunk * 4;
+  static constexpr int kStage = kTau + kRChunk * 4;
 };
 
 template <int D>
 __global__ __launch_bounds__(kKThreads) void bwd_dkdv_kernel(BwdArgs a) {
   using L = KLds<D>;
   constexpr int NKS = D / 16;
-  constexpr int PPR = D / 8;
-  __shared__ __attribute__((aligned(16))) uint16_t q_lds[kRChunk * L::RS];
-  __shared__ __attribute__((aligned(16))) uint16_t o_lds[kRChunk * L::RS];    // dO
-  __shared__ __attribute__((aligned(16))) uint16_t qt_lds[D * L::TS];
-  __shared__ __attribute__((aligned(16))) uint16_t ot_lds[D * L::TS];
-  __shared__ float r_lse[kRChunk], r_d[kRChunk];
-  __shared__ int r_tau[kRChunk];
+  constexpr int PPR = D / 8;                         // 16-byte pieces per row
+  constexpr int NTASK = (kRChunk / 2) * PPR;         // (row pair, piece) per tensor
+  constexpr int TPT = NTASK / kKThreads;             // tasks per thread
+  static_assert(NTASK % kKThreads == 0, "row-pair tasks must split evenly");
+  __shared__ __attribute__((aligned(16))) unsigned char stage[2][L::kStage];
   __shared__ int s_lo[2], s_hi[2];
 
   const int tid = threadIdx.x, lane = lane_id(), wave = wave_id();
   const int hh = lane >> 5, li = lane & 31;
-  const int tile = blockIdx.x;
-  const int h = blockIdx.y % a.Hkv, b = blockIdx.y / a.Hkv;
+  // tiles of one (sequence, KV head) go to one XCD in plan order, so the
+  // workgroups sharing an L2 read overlapping rows
+  const int Lb = xcd_logical_block((int)blockIdx.x, (int)gridDim.x);
+  const int tile = Lb % a.ktiles, sg = Lb / a.ktiles;
+  const int h = sg % a.Hkv, b = sg / a.Hkv;
   const int S = a.S, s = a.s, w = a.w, G = a.G;
   const size_t seg = (size_t)b * a.Hkv + h;
   const int* tau = a.tau + seg * S;
@@ -406,16 +424,22 @@ __global__ __launch_bounds__(kKThreads) void bwd_dkdv_kernel(BwdArgs a) {
   }
 
   // B operands: K^T and V^T of this lane's key, dims [16 ks + 8 hh, +8)
+  // (loaded unconditionally from a clamped row, then zeroed for padding, and
+  // completed here: loads still pending at the loop would make the compiler
+  // wait for the loop's own prefetch before the first MFMA of every chunk)
   bf16x8 kop[NKS], vop[NKS];
+  {
+    const size_t krow = kvbase + (size_t)(t >= 0 ? t : 0) * D;
 #pragma unroll
-  for (int ks = 0; ks < NKS; ++ks) {
-    uint4 u = make_uint4(0, 0, 0, 0), x = make_uint4(0, 0, 0, 0);
-    if (t >= 0) {
-      u = *(const uint4*)(a.k + kvbase + (size_t)t * D + 16 * ks + 8 * hh);
-      x = *(const uint4*)(a.v + kvbase + (size_t)t * D + 16 * ks + 8 * hh);
+    for (int ks = 0; ks < NKS; ++ks) {
+      u32x4v u = *(const u32x4v*)(a.k + krow + 16 * ks + 8 * hh);
+      u32x4v x = *(const u32x4v*)(a.v + krow + 16 * ks + 8 * hh);
+      if (t < 0) u = x = u32x4v{0, 0, 0, 0};
+      kop[ks] = __builtin_bit_cast(bf16x8, u);
+      vop[ks] = __builtin_bit_cast(bf16x8, x);
     }
-    kop[ks] = as_bf16x8(u);
-    vop[ks] = as_bf16x8(x);
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) asm volatile("" : "+v"(kop[ks]), "+v"(vop[ks]));
   }
   f32x16 dkacc[D / 32], dvacc[D / 32];
 #pragma unroll
@@ -425,80 +449,142 @@ __global__ __launch_bounds__(kKThreads) void bwd_dkdv_kernel(BwdArgs a) {
   }
   __syncthreads();
   const int r_lo = min(s_lo[0], s_lo[1]), r_hi = max(s_hi[0], s_hi[1]);
+  // work items: (query head, 32-row chunk) pairs, chunks aligned to 32 rows
+  const int c_first = r_lo <= r_hi ? r_lo / kRChunk : 0;
+  const int n_chunk = r_lo <= r_hi ? r_hi / kRChunk - c_first + 1 : 0;
+  const int n_items = G * n_chunk;
 
-  for (int gg = 0; gg < G && r_lo <= r_hi; ++gg) {
-    const int hq = h * G + gg;
-    const size_t hrow = ((size_t)b * a.Hq + hq) * S;
-    for (int c0 = (r_lo / kRChunk) * kRChunk; c0 <= r_hi; c0 += kRChunk) {
-      // stage the chunk's rows: Q, dO row-major and transposed (permuted)
-      for (int task = tid; task < kRChunk * PPR; task += kKThreads) {
-        const int i = task / PPR, pc = task % PPR;
-        const int qq = c0 + i;
-        u32x4v qx = {0, 0, 0, 0}, ox = {0, 0, 0, 0};
-        if (qq < S) {
-          qx = *(const u32x4v*)(a.q + (hrow + qq) * D + 8 * pc);
-          ox = *(const u32x4v*)(a.dout + (hrow + qq) * D + 8 * pc);
-        }
-        *(u32x4v*)(q_lds + i * L::RS + 8 * pc) = qx;
-        *(u32x4v*)(o_lds + i * L::RS + 8 * pc) = ox;
-        const int col = perm_col(i);
+  // staging: each task is (row pair p, piece pc); lanes of a wave cover 16
+  // pairs of 4 pieces, so their transposed word stores spread over the banks
+  u32x4v rq_[2][TPT][2], ro_[2][TPT][2];
+  float rv_[2][3] = {{0.0f, 0.0f, 0.0f}, {0.0f, 0.0f, 0.0f}};
+  auto load = [&](int item, auto slot) {
+    constexpr int sl = decltype(slot)::value;
+    auto& rq = rq_[sl];
+    auto& ro = ro_[sl];
+    auto& r_val = rv_[sl];
+    const int gg = item / n_chunk, c0 = (c_first + item % n_chunk) * kRChunk;
+    const size_t hrow = ((size_t)b * a.Hq + h * G + gg) * S;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          qt_lds[(8 * pc + 2 * e) * L::TS + col] = (uint16_t)(qx[e] & 0xffffu);
-          qt_lds[(8 * pc + 2 * e + 1) * L::TS + col] = (uint16_t)(qx[e] >> 16);
-          ot_lds[(8 * pc + 2 * e) * L::TS + col] = (uint16_t)(ox[e] & 0xffffu);
-          ot_lds[(8 * pc + 2 * e + 1) * L::TS + col] = (uint16_t)(ox[e] >> 16);
-        }
+    for (int i = 0; i < TPT; ++i) {
+      const int task = tid + i * kKThreads;
+      const int p = task & 15, pc = task >> 4;
+#pragma unroll
+      for (int r = 0; r < 2; ++r) {
+        const int qq = min(c0 + 2 * p + r, S - 1);   // rows past the end: masked below
+        rq[i][r] = *(const u32x4v*)(a.q + (hrow + qq) * D + 8 * pc);
+        ro[i][r] = *(const u32x4v*)(a.dout + (hrow + qq) * D + 8 * pc);
       }
-      if (tid < kRChunk) {
-        const int qq = c0 + tid;
-        const bool ok = qq < S;
-        r_lse[tid] = ok ? a.lse[hrow + qq] * kLog2e : 0.0f;
-        r_d[tid] = ok ? a.dvec[hrow + qq] : 0.0f;
-        r_tau[tid] = ok ? tau[qq] : -1;
+    }
+    if (tid < kRChunk) {
+      const int qq = min(c0 + tid, S - 1);
+      r_val[0] = a.lse[hrow + qq];
+      r_val[1] = a.dvec[hrow + qq];
+      r_val[2] = __int_as_float(tau[qq]);
+    }
+  };
+  auto store = [&](int buf, auto slot) {
+    constexpr int sl = decltype(slot)::value;
+    auto& rq = rq_[sl];
+    auto& ro = ro_[sl];
+    auto& r_val = rv_[sl];
+    unsigned char* st = stage[buf];
+    uint16_t* ql = (uint16_t*)(st + L::kQ);
+    uint16_t* ol = (uint16_t*)(st + L::kO);
+    uint32_t* qt = (uint32_t*)(st + L::kQT);
+    uint32_t* ot = (uint32_t*)(st + L::kOT);
+#pragma unroll
+    for (int i = 0; i < TPT; ++i) {
+      const int task = tid + i * kKThreads;
+      const int p = task & 15, pc = task >> 4;
+#pragma unroll
+      for (int r = 0; r < 2; ++r) {
+        *(u32x4v*)(ql + (2 * p + r) * L::RS + 8 * pc) = rq[i][r];
+        *(u32x4v*)(ol + (2 * p + r) * L::RS + 8 * pc) = ro[i][r];
       }
-      __syncthreads();
+      // rows 2p and 2p+1 sit in adjacent columns: one word per dim
+      const int cw = perm_col(2 * p) >> 1;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t qa = rq[i][0][e], qb = rq[i][1][e];
+        const uint32_t oa = ro[i][0][e], ob = ro[i][1][e];
+        const int d0 = 8 * pc + 2 * e;
+        qt[d0 * (L::TS / 2) + cw] = (qa & 0xffffu) | (qb << 16);
+        qt[(d0 + 1) * (L::TS / 2) + cw] = (qa >> 16) | (qb & 0xffff0000u);
+        ot[d0 * (L::TS / 2) + cw] = (oa & 0xffffu) | (ob << 16);
+        ot[(d0 + 1) * (L::TS / 2) + cw] = (oa >> 16) | (ob & 0xffff0000u);
+      }
+    }
+    if (tid < kRChunk) {
+      ((float*)(st + L::kLse))[tid] = r_val[0] * kLog2e;
+      ((float*)(st + L::kD))[tid] = r_val[1];
+      ((int*)(st + L::kTau))[tid] = __float_as_int(r_val[2]);
+    }
+  };
 
-      // S = Q K^T and dP = dO V^T (32 rows x 32 keys): lane owns its key
-      f32x16 sacc = f32x16{}, pacc = f32x16{};
-      {
-        const uint16_t* ql = q_lds + li * L::RS + 8 * hh;
-        const uint16_t* ol = o_lds + li * L::RS + 8 * hh;
+  // item it is staged in LDS buffer it & 1 and held in registers slot it & 1
+  // two items ahead: loads of item it+2 are issued while item it computes
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
+  if (n_items > 0) {
+    load(0, S0{});
+    store(0, S0{});
+  }
+  if (n_items > 1) load(1, S1{});
+  __syncthreads();
+  for (int it = 0; it < n_items; ++it) {
+    const int buf = it & 1;
+    const int c0 = (c_first + it % n_chunk) * kRChunk;
+    if (it + 2 < n_items) {                          // into the slot item it vacated
+      if (buf == 0) load(it + 2, S0{});
+      else load(it + 2, S1{});
+    }
+    const unsigned char* st = stage[buf];
+    const uint16_t* ql = (const uint16_t*)(st + L::kQ) + li * L::RS + 8 * hh;
+    const uint16_t* ol = (const uint16_t*)(st + L::kO) + li * L::RS + 8 * hh;
+    const float* r_lse = (const float*)(st + L::kLse);
+    const float* r_d = (const float*)(st + L::kD);
+    const int* r_tau = (const int*)(st + L::kTau);
+
+    // S = Q K^T and dP = dO V^T (32 rows x 32 keys): lane owns its key
+    f32x16 sacc = f32x16{}, pacc = f32x16{};
 #pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) {
-          sacc = mfma32x32x16(as_bf16x8(*(const uint4*)(ql + 16 * ks)), kop[ks], sacc);
-          pacc = mfma32x32x16(as_bf16x8(*(const uint4*)(ol + 16 * ks)), vop[ks], pacc);
-        }
-      }
-      float pv[16], dsv[16];
+    for (int ks = 0; ks < NKS; ++ks) {
+      sacc = mfma32x32x16(as_bf16x8(*(const uint4*)(ql + 16 * ks)), kop[ks], sacc);
+      pacc = mfma32x32x16(as_bf16x8(*(const uint4*)(ol + 16 * ks)), vop[ks], pacc);
+    }
+    float pv[16], dsv[16];
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int i = 8 * (e >> 2) + 4 * hh + (e & 3);
-        const int qq = c0 + i;
-        const bool kp = (qq < S) && kept(qq, t, rk_m, r_tau[i], s, w);
-        const float p = kp ? exp2_fast(fmaf(sacc[e], a.scale_log2, -r_lse[i])) : 0.0f;
-        pv[e] = p;
-        dsv[e] = p * (pacc[e] - r_d[i]);
-      }
-      bf16x8 pp[2], ps[2];
+    for (int e = 0; e < 16; ++e) {
+      const int i = 8 * (e >> 2) + 4 * hh + (e & 3);
+      const int qq = c0 + i;
+      const bool kp = (qq < S) && kept(qq, t, rk_m, r_tau[i], s, w);
+      const float p = kp ? exp2_fast(fmaf(sacc[e], a.scale_log2, -r_lse[i])) : 0.0f;
+      pv[e] = p;
+      dsv[e] = p * (pacc[e] - r_d[i]);
+    }
+    bf16x8 pp[2], ps[2];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      pp[ks] = pack_bf16x8(&pv[8 * ks]);
+      ps[ks] = pack_bf16x8(&dsv[8 * ks]);
+    }
+    // dV^T += dO^T P and dK^T += Q^T dS
+#pragma unroll
+    for (int d2 = 0; d2 < D / 32; ++d2) {
+      const uint16_t* otl = (const uint16_t*)(st + L::kOT) + (32 * d2 + li) * L::TS + 8 * hh;
+      const uint16_t* qtl = (const uint16_t*)(st + L::kQT) + (32 * d2 + li) * L::TS + 8 * hh;
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
-        pp[ks] = pack_bf16x8(&pv[8 * ks]);
-        ps[ks] = pack_bf16x8(&dsv[8 * ks]);
+        dvacc[d2] = mfma32x32x16(as_bf16x8(*(const uint4*)(otl + 16 * ks)), pp[ks], dvacc[d2]);
+        dkacc[d2] = mfma32x32x16(as_bf16x8(*(const uint4*)(qtl + 16 * ks)), ps[ks], dkacc[d2]);
       }
-      // dV^T += dO^T P and dK^T += Q^T dS
-#pragma unroll
-      for (int d2 = 0; d2 < D / 32; ++d2) {
-        const uint16_t* otl = ot_lds + (32 * d2 + li) * L::TS + 8 * hh;
-        const uint16_t* qtl = qt_lds + (32 * d2 + li) * L::TS + 8 * hh;
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-          dvacc[d2] = mfma32x32x16(as_bf16x8(*(const uint4*)(otl + 16 * ks)), pp[ks], dvacc[d2]);
-          dkacc[d2] = mfma32x32x16(as_bf16x8(*(const uint4*)(qtl + 16 * ks)), ps[ks], dkacc[d2]);
-        }
-      }
-      __syncthreads();   // the chunk's LDS is rewritten next
     }
+    if (it + 1 < n_items) {                          // item it+1 into the other stage
+      if (buf == 0) store(1, S1{});
+      else store(0, S0{});
+    }
+    __syncthreads();
   }
 
   if (t >= 0) {
@@ -531,7 +617,8 @@ void launch_bwd_kernels(const Dims& d, BwdArgs a, const void* o, hipStream_t st)
                        (float*)a.dvec, rows);
   const long long nq = (long long)a.ntiles * d.Hkv * d.b;
   hipLaunchKernelGGL((bwd_dq_kernel<D>), dim3((unsigned)nq), dim3(kQThreads), 0, st, a);
-  hipLaunchKernelGGL((bwd_dkdv_kernel<D>), dim3(a.ktiles, d.nseg()), dim3(kKThreads), 0, st, a);
+  hipLaunchKernelGGL((bwd_dkdv_kernel<D>), dim3((unsigned)(a.ktiles * d.nseg())), dim3(kKThreads), 0,
+                     st, a);
 }
 
 }  // namespace
