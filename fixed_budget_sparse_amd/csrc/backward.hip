@@ -26,9 +26,11 @@
 //    on tau; bwd_key_order_kernel groups keys into 64-key tiles: keys that
 //    live at most w + 64 rows in token order, the others by q_end (a counting
 //    sort over 64-row buckets), which keeps the rows a tile visits close to
-//    the rows its keys need.  Per tile (2 waves of 32 keys, K and V operands in
-//    registers) the rows stream in 32-row chunks aligned to multiples of 32
-//    (so every key's sums are formed in the same order whatever its tile),
+//    the rows its keys need.  Per workgroup (4 waves of 32 keys: two
+//    consecutive 64-key groups of the plan share every staged chunk; K and V
+//    operands in registers) the rows stream in 32-row chunks aligned to
+//    multiples of 32 (so every key's sums are formed in the same order
+//    whatever its tile),
 //    double-buffered in LDS, with the loads of the chunk after next in flight
 //    during the math (two register stages), workgroups mapped so that each
 //    XCD works through whole (sequence, KV head)s in plan order:
@@ -47,8 +49,9 @@ namespace {
 
 constexpr int kQThreads = 512;      // dQ: 8 waves x 32 stacked rows
 constexpr int kQChunk = 64;         // dQ: keys per chunk
-constexpr int kKTile = 64;          // dK/dV: keys per workgroup (2 waves x 32)
-constexpr int kKThreads = 128;
+constexpr int kKWaves = 4;          // dK/dV: waves per workgroup, 32 keys each
+constexpr int kKTile = 32 * kKWaves;
+constexpr int kKThreads = 64 * kKWaves;
 constexpr int kRChunk = 32;         // dK/dV: query rows per chunk
 
 typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
@@ -387,10 +390,10 @@ __global__ __launch_bounds__(kKThreads) void bwd_dkdv_kernel(BwdArgs a) {
   constexpr int NKS = D / 16;
   constexpr int PPR = D / 8;                         // 16-byte pieces per row
   constexpr int NTASK = (kRChunk / 2) * PPR;         // (row pair, piece) per tensor
-  constexpr int TPT = NTASK / kKThreads;             // tasks per thread
-  static_assert(NTASK % kKThreads == 0, "row-pair tasks must split evenly");
+  constexpr int TPT = (NTASK + kKThreads - 1) / kKThreads;   // tasks per thread
+  constexpr bool kPartial = NTASK % kKThreads != 0;           // some threads idle (D = 64)
   __shared__ __attribute__((aligned(16))) unsigned char stage[2][L::kStage];
-  __shared__ int s_lo[2], s_hi[2];
+  __shared__ int s_lo[kKWaves], s_hi[kKWaves];
 
   const int tid = threadIdx.x, lane = lane_id(), wave = wave_id();
   const int hh = lane >> 5, li = lane & 31;
@@ -448,7 +451,12 @@ __global__ __launch_bounds__(kKThreads) void bwd_dkdv_kernel(BwdArgs a) {
     dvacc[d2] = f32x16{};
   }
   __syncthreads();
-  const int r_lo = min(s_lo[0], s_lo[1]), r_hi = max(s_hi[0], s_hi[1]);
+  int r_lo = s_lo[0], r_hi = s_hi[0];
+#pragma unroll
+  for (int wv = 1; wv < kKWaves; ++wv) {
+    r_lo = min(r_lo, s_lo[wv]);
+    r_hi = max(r_hi, s_hi[wv]);
+  }
   // work items: (query head, 32-row chunk) pairs, chunks aligned to 32 rows
   const int c_first = r_lo <= r_hi ? r_lo / kRChunk : 0;
   const int n_chunk = r_lo <= r_hi ? r_hi / kRChunk - c_first + 1 : 0;
@@ -468,6 +476,7 @@ __global__ __launch_bounds__(kKThreads) void bwd_dkdv_kernel(BwdArgs a) {
 #pragma unroll
     for (int i = 0; i < TPT; ++i) {
       const int task = tid + i * kKThreads;
+      if (kPartial && task >= NTASK) break;           // whole waves idle
       const int p = task & 15, pc = task >> 4;
 #pragma unroll
       for (int r = 0; r < 2; ++r) {
@@ -496,6 +505,7 @@ __global__ __launch_bounds__(kKThreads) void bwd_dkdv_kernel(BwdArgs a) {
 #pragma unroll
     for (int i = 0; i < TPT; ++i) {
       const int task = tid + i * kKThreads;
+      if (kPartial && task >= NTASK) break;
       const int p = task & 15, pc = task >> 4;
 #pragma unroll
       for (int r = 0; r < 2; ++r) {
