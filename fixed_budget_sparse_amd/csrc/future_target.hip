@@ -125,13 +125,16 @@ __global__ __launch_bounds__(kThreads, 2) void future_target_kernel(TgtArgs a) {
   u32x4v stage[Gm::NPIECE];
   float stage_lse = 0.0f;
   auto load_chunk = [&](int d0) {
+    // a buffer descriptor over rows d0 .. S-1: each lane's offset is the same
+    // for every chunk and rows past the end read as zeros (their -LSE is
+    // -inf, so they add 0), with no per-chunk address arithmetic
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(qg + (size_t)d0 * D * Gm::esz), (short)0, (S - d0) * D * Gm::esz, 0x00020000);
 #pragma unroll
     for (int i = 0; i < Gm::NPIECE; ++i) {
       const int p = tid + i * kThreads;
       const int row = p / Gm::PPR, piece = p % Gm::PPR;
-      // rows past the end repeat the last row: their -LSE is -inf, so they add 0
-      const int d = min(d0 + row, S - 1);
-      stage[i] = *(const u32x4v*)(qg + (size_t)d * D * Gm::esz + piece * 16);
+      stage[i] = __builtin_amdgcn_raw_buffer_load_b128(rs, row * D * Gm::esz + piece * 16, 0, 0);
     }
     // the raw value only: arithmetic on it here would wait for all the loads
     // above; it is scaled when stored
