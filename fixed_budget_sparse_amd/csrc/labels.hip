@@ -132,13 +132,15 @@ __device__ __forceinline__ void wave_find_bin(int* hist, int need, bool clear, i
   wave_lds_fence();
 }
 
-// Exact selection by one wave over `n` items in increasing token order
-// (get(i, key, t) gives item i's key and token; t < 0 marks no item): the
-// token of the need-th item in the order (key descending, token ascending) and
-// its key.  Uses `hist` (kSelBins bins, zero on entry and on return).
+// Exact selection by one wave over `n` items (get(i, key, t) gives item i's
+// key and token; t < 0 marks no item): the token of the need-th item in the
+// order (key descending, token ascending) and its key.  With `ordered` the
+// items come in increasing token order and equal keys are resolved by a scan;
+// otherwise by ranking the equal items' tokens pairwise.  Uses `hist`
+// (kSelBins bins, zero on entry and on return).
 template <class Get>
-__device__ __forceinline__ void wave_select(int* hist, int n, int need, Get get, int& t_out,
-                                            uint32_t& key_out) {
+__device__ __forceinline__ void wave_select(int* hist, int n, int need, bool ordered, Get get,
+                                            int& t_out, uint32_t& key_out) {
   const int lane = lane_id();
   uint32_t lo = 0xffffffffu, hi = 0u;
   for (int base = 0; base < n; base += 64) {
@@ -176,8 +178,32 @@ __device__ __forceinline__ void wave_select(int* hist, int n, int need, Get get,
     top = shift;
   }
   const uint32_t xkey = lo + prefix;
-  // the need-th item with this key, in token order
   int found = -1;
+  if (!ordered) {
+    // the item with this key whose token has exactly need-1 smaller tokens
+    // among the items with this key
+    for (int base = 0; base < n && found < 0; base += 64) {
+      uint32_t key;
+      int t;
+      get(base + lane, key, t);
+      const bool eq = t >= 0 && key == xkey;
+      int below = 0;
+      if (wave_ballot(eq) != 0) {
+        for (int j = 0; j < n; ++j) {
+          uint32_t kj;
+          int tj;
+          get(j, kj, tj);
+          below += (tj >= 0 && kj == xkey && tj < t) ? 1 : 0;
+        }
+      }
+      const uint64_t hm = wave_ballot(eq && below == need - 1);
+      if (hm) found = __shfl(t, (int)__builtin_ctzll(hm));
+    }
+    t_out = found;
+    key_out = xkey;
+    return;
+  }
+  // the need-th item with this key, in token order
   for (int base = 0; base < n && found < 0; base += 64) {
     uint32_t key;
     int t;
@@ -271,27 +297,64 @@ __global__ __launch_bounds__(NW * 64) void boundary_labels_kernel(LabelArgs a) {
   int* cand_t = cand_t_all + wave * NC;
   uint32_t* cand_k = cand_k_all + wave * NC;
 
-  // this wave's run of consecutive queries
+  // this wave's run of consecutive queries; the candidate list of the
+  // previous query's bin is kept and patched when the bin stays the same
   const int per = (q_hi - q_first + NW - 1) / NW;
   const int qa = q_first + wave * per, qb = min(q_hi, qa + per);
+  int cur_bin = -1, cur_count = 0;
+  bool have_list = false;
+  // removals and additions of a step, in the (then idle) selection histogram
+  constexpr int kPatch = kSelBins / 4;
+  int* rem_t = sel;
+  int* add_t = sel + kPatch;
+  uint32_t* add_k = (uint32_t*)(sel + 2 * kPatch);
   for (int q = qa; q < qb; ++q) {
     const int t_new = q - w;
     const int n_e = t_new - s + 1;
     const int kk = min(k, n_e);
 
     // ---- 1. histogram of the bins of the decayed scores
+    int n_rem = 0, n_add = 0;
     if (q > qa) {
       // from q-1: tokens t = q (mod n) of E(q-1) age by one step, then the
-      // newcomer joins (its age is floor(w / n))
+      // newcomer joins (its age is floor(w / n)); changes to the kept list's
+      // bin are recorded
       const int t0 = s + (((q - s) % n) + n) % n;      // first such token >= s
       const int m0 = (q - t0) / n;                      // its age at q
-      for (int i = lane; t0 + i * n <= t_new - 1; i += 64) {
-        const int t = t0 + i * n;
+      const int n_age = t_new - 1 >= t0 ? (t_new - 1 - t0) / n + 1 : 0;
+      for (int base = 0; base < n_age; base += 64) {
+        const int i = base + lane;
+        const bool ok = i < n_age;
+        const int t = t0 + min(i, n_age - 1) * n;
         const float v = sc[t];
-        atomicAdd(&hist[bin_of(decayed(v, m0 - i - 1, lg))], -1);
-        atomicAdd(&hist[bin_of(decayed(v, m0 - i, lg))], 1);
+        const float ro = decayed(v, m0 - i - 1, lg), rn = decayed(v, m0 - i, lg);
+        const int ob = bin_of(ro), nb = bin_of(rn);
+        if (ok) {
+          atomicAdd(&hist[ob], -1);
+          atomicAdd(&hist[nb], 1);
+        }
+        if (have_list) {
+          const bool rm = ok && ob == cur_bin, ad = ok && nb == cur_bin;
+          const uint64_t mr = wave_ballot(rm), ma = wave_ballot(ad);
+          if (rm && n_rem + lanes_below(mr) < kPatch) rem_t[n_rem + lanes_below(mr)] = t;
+          if (ad && n_add + lanes_below(ma) < kPatch) {
+            add_t[n_add + lanes_below(ma)] = t;
+            add_k[n_add + lanes_below(ma)] = score_key(rn);
+          }
+          n_rem += __builtin_popcountll(mr);
+          n_add += __builtin_popcountll(ma);
+        }
       }
-      if (lane == 0) atomicAdd(&hist[bin_of(decayed(sc[t_new], w / n, lg))], 1);
+      const float r_new = decayed(sc[t_new], w / n, lg);
+      const int b_new = bin_of(r_new);
+      if (lane == 0) {
+        atomicAdd(&hist[b_new], 1);
+        if (have_list && b_new == cur_bin && n_add < kPatch) {
+          add_t[n_add] = t_new;
+          add_k[n_add] = score_key(r_new);
+        }
+      }
+      if (have_list && b_new == cur_bin) ++n_add;
     } else {
       // the run's first query: every eligible token (kU per lane in flight;
       // loads past t_new are clamped and add nothing)
@@ -318,8 +381,43 @@ __global__ __launch_bounds__(NW * 64) void boundary_labels_kernel(LabelArgs a) {
 
     int t_sel;
     uint32_t key_sel;
-    if (count <= NC) {
-      // ---- 2. the bin's tokens, in index order, into the candidate buffer
+    bool ordered = true;
+    bool patched = false;
+    if (count <= NC && have_list && bin == cur_bin && n_rem <= kPatch && n_add <= kPatch) {
+      // ---- 2a. same bin as the previous query: drop the removed tokens from
+      // the list (compacted in place) and append the additions
+      int kept = 0;
+      for (int base = 0; base < cur_count; base += 64) {
+        const int i = base + lane;
+        const bool okk = i < cur_count;
+        const int tt = okk ? cand_t[i] : -1;
+        const uint32_t kt = okk ? cand_k[i] : 0u;
+        bool keep = okk;
+        for (int r = 0; r < n_rem; ++r) keep &= tt != rem_t[r];
+        const uint64_t m = wave_ballot(keep);
+        if (keep) {
+          cand_t[kept + lanes_below(m)] = tt;
+          cand_k[kept + lanes_below(m)] = kt;
+        }
+        kept += __builtin_popcountll(m);
+        wave_lds_fence();
+      }
+      if (kept + n_add == count) {
+        for (int j = lane; j < n_add; j += 64) {
+          cand_t[kept + j] = add_t[j];
+          cand_k[kept + j] = add_k[j];
+        }
+        patched = true;
+        ordered = false;
+      }
+    }
+    // the selection histogram held the patch lists: clear it
+    if (q > qa && have_list) {
+      for (int j = lane; j < kSelBins; j += 64) sel[j] = 0;
+    }
+    wave_lds_fence();
+    if (count <= NC && !patched) {
+      // ---- 2b. the bin's tokens, in index order, into the candidate buffer
       int placed = 0;
       AgeWalk ag;
       ag.init(q, s + lane, n);
@@ -347,9 +445,11 @@ __global__ __launch_bounds__(NW * 64) void boundary_labels_kernel(LabelArgs a) {
         }
       }
       wave_lds_fence();
+    }
+    if (count <= NC) {
       // ---- 3. exact selection among the candidates
       wave_select(
-          sel, count, need,
+          sel, count, need, ordered,
           [&](int i, uint32_t& key, int& t) {
             const bool ok = i < count;
             key = ok ? cand_k[i] : 0u;
@@ -359,7 +459,7 @@ __global__ __launch_bounds__(NW * 64) void boundary_labels_kernel(LabelArgs a) {
     } else {
       // heavy ties: exact selection over all of E(q), keys computed per pass
       wave_select(
-          sel, n_e, kk,
+          sel, n_e, kk, true,
           [&](int i, uint32_t& key, int& t) {
             t = s + i;
             if (t > t_new) {
@@ -372,6 +472,9 @@ __global__ __launch_bounds__(NW * 64) void boundary_labels_kernel(LabelArgs a) {
           t_sel, key_sel);
     }
     wave_lds_fence();   // the buffers are rewritten for the wave's next query
+    have_list = count <= NC;
+    cur_bin = bin;
+    cur_count = count;
 
     if (lane == 0) {
       const uint32_t key_new = score_key(decayed(sc[t_new], w / n, lg));

@@ -215,6 +215,7 @@ LABEL_CASES = [
     (1, 2, 220, 0, 0, 25, 1, (-1.0, -0.01), "normal", None),   # n = 1, w = 0, s = 0
     (1, 1, 240, 2, 3, 30, 6, (0.0,), "ties", None),            # no decay
     (1, 1, 150, 2, 3, 20, 4, (-0.25,), "equal", None),         # every score equal
+    (1, 1, 1500, 8, 32, 200, 16, (-0.15,), "ties", None),      # kept bin lists patched across ties
     (1, 2, 5000, 16, 64, 300, 64, (-0.1, -0.02), "normal",     # 16 keys per thread
      list(range(0, 100)) + list(range(2000, 2040)) + list(range(4900, 5000))),
     (1, 1, 20000, 16, 128, 1000, 64, (-0.05,), "ties",          # 32 keys per thread
