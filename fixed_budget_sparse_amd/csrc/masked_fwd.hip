@@ -61,13 +61,17 @@ __global__ __launch_bounds__(256) void order_from_rank_kernel(const int* __restr
 }
 
 // Lists, in rank order, the long-range keys of each tile's first row q0 when
-// its cutoff is finite: tokens t in [s, q0 - w] with rank(t) <= tau_q0.
+// its cutoff is finite: tokens t in [s, q0 - w] with rank(t) <= tau_q0.  A
+// round covers 4 x 256 places of the rank order, each wave a contiguous run of
+// 256 of them (four loads in flight per lane, ballots in place order), and
+// ends in one barrier (the wave counts are double-buffered).
 __global__ __launch_bounds__(256) void tile_list_kernel(const int* __restrict__ order,
                                                         const int* __restrict__ tau, int S,
                                                         int s, int w, int m, int ntiles, int cap,
                                                         int2* __restrict__ list,
                                                         int* __restrict__ count) {
-  __shared__ int wsum[4];
+  constexpr int kU = 4;
+  __shared__ int wsum[2][4];
   const int tile = blockIdx.x, seg = blockIdx.y;
   const int tid = threadIdx.x, lane = lane_id(), wave = wave_id();
   const int q0 = tile * m;
@@ -82,24 +86,39 @@ __global__ __launch_bounds__(256) void tile_list_kernel(const int* __restrict__ 
   const int* ord = order + (size_t)seg * S;
   int2* out = list + ((size_t)seg * ntiles + tile) * cap;
   int base = 0;
-  for (int i0 = 0; i0 <= scan_end; i0 += 256) {
-    const int i = i0 + tid;
-    const int t = i <= scan_end ? ord[i] : -1;
-    const bool keep = t >= s && t <= e_hi;
-    const uint64_t bal = wave_ballot(keep);
-    if (lane == 0) wsum[wave] = __builtin_popcountll(bal);
+  for (int i0 = 0, r = 0; i0 <= scan_end; i0 += 256 * kU, ++r) {
+    const int w0 = i0 + wave * 64 * kU;   // this wave's run: places w0 .. w0 + 255
+    int t[kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int i = w0 + 64 * u + lane;
+      t[u] = ord[min(i, scan_end)];
+      if (i > scan_end) t[u] = -1;
+    }
+    uint64_t bal[kU];
+    int wcount = 0;
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      bal[u] = wave_ballot(t[u] >= s && t[u] <= e_hi);
+      wcount += __builtin_popcountll(bal[u]);
+    }
+    if (lane == 0) wsum[r & 1][wave] = wcount;
     __syncthreads();
-    int wofs = 0, total = 0;
+    int pos = base, total = 0;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int c = wsum[j];
-      wofs += j < wave ? c : 0;
+      const int c = wsum[r & 1][j];
+      pos += j < wave ? c : 0;
       total += c;
     }
-    const int pos = base + wofs + lanes_below(bal);
-    if (keep && pos < cap) out[pos] = make_int2(t, i);
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const bool keep = t[u] >= s && t[u] <= e_hi;
+      const int at = pos + lanes_below(bal[u]);
+      if (keep && at < cap) out[at] = make_int2(t[u], w0 + 64 * u + lane);
+      pos += __builtin_popcountll(bal[u]);
+    }
     base += total;
-    __syncthreads();
   }
   if (tid == 0) *cnt_out = min(base, cap);
 }

@@ -166,6 +166,131 @@ __global__ __launch_bounds__(kSortThreads) void radix_scatter_kernel(
 }
 
 
+// The whole sort of one sequence's priorities in one workgroup when they fit
+// in LDS (S <= 16384: 4-byte keys and 2-byte token indices): the same four
+// stable 8-bit passes, with the keys kept in registers and exchanged through
+// LDS between passes instead of through HBM, so the rank costs one launch.
+// 16 waves; wave `wave` owns places [wave * 64 * ipl, +64 * ipl) of the
+// current order, item i of a lane at place wbase + 64 i + lane.
+constexpr int kLdsSortThreads = 1024;
+constexpr int kLdsSortWaves = kLdsSortThreads / 64;
+constexpr int kLdsSortItems = 16;
+constexpr int kLdsSortMaxS = kLdsSortThreads * kLdsSortItems;
+
+size_t lds_sort_bytes(int S) {
+  return (size_t)kLdsSortWaves * kRadix * 4 + 16 + (size_t)S * 4 + align256((size_t)S * 2);
+}
+
+__global__ __launch_bounds__(kLdsSortThreads) void lds_rank_kernel(const float* __restrict__ prio,
+                                                                   int S, int* __restrict__ rank,
+                                                                   int* __restrict__ order) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char dyn[];
+  uint32_t* offs = reinterpret_cast<uint32_t*>(dyn);          // [waves][256]
+  int* wtot = reinterpret_cast<int*>(offs + kLdsSortWaves * kRadix);   // [4]
+  uint32_t* skey = reinterpret_cast<uint32_t*>(wtot + 4);     // [S]
+  uint16_t* sval = reinterpret_cast<uint16_t*>(skey + S);     // [S]
+  const int tid = threadIdx.x, lane = lane_id(), wave = wave_id();
+  const size_t base = (size_t)blockIdx.x * S;
+  const int ipl = (S + kLdsSortThreads - 1) / kLdsSortThreads;   // items per lane
+  const int wbase = wave * 64 * ipl;
+  uint32_t key[kLdsSortItems], pos[kLdsSortItems];
+  int val[kLdsSortItems];
+  uint64_t peers[kLdsSortItems];
+#pragma unroll
+  for (int i = 0; i < kLdsSortItems; ++i) {
+    const int idx = wbase + 64 * i + lane;
+    const bool valid = i < ipl && idx < S;
+    key[i] = valid ? priority_sort_key(prio[base + idx]) : 0xffffffffu;
+    val[i] = idx;
+    pos[i] = 0;
+  }
+  for (int pass = 0; pass < 4; ++pass) {
+    const int shift = 8 * pass;
+    for (int j = tid; j < kLdsSortWaves * kRadix; j += kLdsSortThreads) offs[j] = 0;
+    __syncthreads();
+    // count each digit per wave
+#pragma unroll
+    for (int i = 0; i < kLdsSortItems; ++i) {
+      if (i < ipl) {
+        const bool valid = wbase + 64 * i + lane < S;
+        const uint32_t dig = (key[i] >> shift) & 255u;
+        peers[i] = same_digit_lanes(dig, valid);
+        if (valid && lane == __builtin_ctzll(peers[i]))
+          offs[wave * kRadix + dig] += (uint32_t)__builtin_popcountll(peers[i]);
+      }
+    }
+    __syncthreads();
+    // first place of each (wave, digit): digits in order, waves in order
+    int tot = 0, incl = 0;
+    if (tid < kRadix) {
+      for (int wv = 0; wv < kLdsSortWaves; ++wv) tot += (int)offs[wv * kRadix + tid];
+      incl = tot;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const int v = __shfl_up(incl, off);
+        if (lane >= off) incl += v;
+      }
+      if (lane == 63) wtot[wave] = incl;
+    }
+    __syncthreads();
+    if (tid < kRadix) {
+      uint32_t run = (uint32_t)(incl - tot);
+      for (int wv = 0; wv < wave; ++wv) run += (uint32_t)wtot[wv];
+      for (int wv = 0; wv < kLdsSortWaves; ++wv) {
+        const uint32_t c = offs[wv * kRadix + tid];
+        offs[wv * kRadix + tid] = run;
+        run += c;
+      }
+    }
+    __syncthreads();
+    // place every key; lanes of one digit read the running place, then the
+    // lowest of them advances it (LDS operations of a wave execute in order)
+#pragma unroll
+    for (int i = 0; i < kLdsSortItems; ++i) {
+      if (i < ipl) {
+        const bool valid = wbase + 64 * i + lane < S;
+        const uint32_t dig = (key[i] >> shift) & 255u;
+        uint32_t start = 0;
+        if (valid) {
+          start = offs[wave * kRadix + dig];
+          pos[i] = start + (uint32_t)lanes_below(peers[i]);
+        }
+        wave_lds_fence();
+        if (valid && lane == __builtin_ctzll(peers[i]))
+          offs[wave * kRadix + dig] = start + (uint32_t)__builtin_popcountll(peers[i]);
+        wave_lds_fence();
+      }
+    }
+    if (pass < 3) {
+      // every wave finished reading the previous order before the last barrier
+#pragma unroll
+      for (int i = 0; i < kLdsSortItems; ++i) {
+        if (i < ipl && wbase + 64 * i + lane < S) {
+          skey[pos[i]] = key[i];
+          sval[pos[i]] = (uint16_t)val[i];
+        }
+      }
+      __syncthreads();
+#pragma unroll
+      for (int i = 0; i < kLdsSortItems; ++i) {
+        const int idx = wbase + 64 * i + lane;
+        if (i < ipl && idx < S) {
+          key[i] = skey[idx];
+          val[i] = (int)sval[idx];
+        }
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < kLdsSortItems; ++i) {
+        if (i < ipl && wbase + 64 * i + lane < S) {
+          rank[base + val[i]] = (int)pos[i];
+          order[base + pos[i]] = val[i];
+        }
+      }
+    }
+  }
+}
+
 // ---------------------------------------------------------------- cutoffs
 // Highest set bit of the bitmap with index < x (-1 if none).  Called by all 64
 // lanes of one wave with the same x.
@@ -425,7 +550,17 @@ hipError_t launch_thresholds(const Dims& d, const float* prio, int* rank, int* t
   const dim3 g(ntiles, nseg);
   uint32_t* kin = nullptr;
   int* vin = nullptr;
-  for (int pass = 0; pass < 4; ++pass) {
+  const bool in_lds = S <= kLdsSortMaxS;
+  if (in_lds) {
+    const size_t lds = lds_sort_bytes(S);
+    // more than 64 KiB of dynamic LDS must be allowed explicitly (160 KiB per CU)
+    (void)hipFuncSetAttribute((const void*)lds_rank_kernel,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    hipLaunchKernelGGL(lds_rank_kernel, dim3(nseg), dim3(kLdsSortThreads), lds, st, prio, S, rank,
+                       valsA);
+    vin = valsA;
+  }
+  for (int pass = 0; pass < 4 && !in_lds; ++pass) {
     const int shift = 8 * pass;
     uint32_t* kout = (pass & 1) ? keysB : keysA;
     int* vout = (pass & 1) ? valsB : valsA;
