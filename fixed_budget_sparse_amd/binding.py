@@ -245,6 +245,14 @@ class DecodeCache:
         return _Cache(self.k.data_ptr(), self.v.data_ptr(), self.slot_pos.data_ptr(),
                       self.slot_prio.data_ptr(), self.ring.data_ptr())
 
+    def reset(self) -> None:
+        """Back to the empty state of new_decode_cache, in place (same memory)."""
+        self.k.zero_()
+        self.v.zero_()
+        self.slot_pos.fill_(-1)
+        self.slot_prio.zero_()
+        self.ring.zero_()
+
     def clone(self) -> "DecodeCache":
         return DecodeCache(*(t.clone() for t in (self.k, self.v, self.slot_pos, self.slot_prio,
                                                  self.ring)))

@@ -5,27 +5,29 @@
 // scored then (the delayed readout), competing for the k long-range slots;
 // gist.science summary §2.1: B = s + w + k entries per KV head.
 //
-// Two kernels per step, on the caller's stream:
-//  1. decide (one workgroup per (sequence, KV head)): reads the slot metadata,
-//     picks the slot token p takes (slot p while the cache fills; afterwards
-//     the slot of u when u is dropped, or of the worst held long-range token
-//     when u replaces it), updates slot_pos / slot_prio / ring, writes the new
-//     K/V row into that slot.  The choice is exact integer/compare work; the
-//     worst token is found with wave shuffle and LDS reductions.
-//  2. attend (split-K only when there are too few (sequence, KV head) pairs
-//     to fill the chip): every wave streams 32-slot blocks of K and V from
-//     HBM with coalesced loads, prefetching the next block into registers
-//     while the current one is in its private LDS region (V transposed), and
-//     runs S^T = K Q^T and O^T = V^T P^T on MFMA with the G query heads of the
-//     KV head as the MFMA rows, keeping an online softmax.  The 4 waves merge
-//     in LDS; with one split the workgroup writes o and lse, otherwise a
-//     partial (max, sum, unnormalised O).
-//  3. combine (only with several splits): merges the partials into o and lse.
+// One kernel per step (two with split-K), on the caller's stream:
+//  1. attend, one workgroup per (sequence, KV head, split): first the step's
+//     decision from the slot metadata as it stands — the slot token p takes
+//     (slot p while the cache fills; afterwards the slot of u when u is
+//     dropped, or of the worst held long-range token when u replaces it),
+//     exact integer/compare work with the worst token found by wave shuffle
+//     and LDS reductions; every split of the pair computes the same decision.
+//     Then every wave streams 32-slot blocks of K and V from HBM with
+//     coalesced loads, the new token's row read from k_new / v_new in place
+//     of its slot, prefetching the next block into registers while the
+//     current one is in its private LDS region (V transposed), and runs
+//     S^T = K Q^T and O^T = V^T P^T on MFMA with the G query heads of the KV
+//     head as the MFMA rows, keeping an online softmax.  The 4 waves merge in
+//     LDS; with one split the workgroup writes o and lse and the metadata
+//     update, otherwise a partial (max, sum, unnormalised O), split 0 records
+//     the decision.  The split owning the new token's slot writes its K/V row
+//     there at the end (no other workgroup reads that slot in this step).
+//  2. combine (only with several splits, after every split has read the
+//     metadata): applies the recorded metadata update and merges the
+//     partials into o and lse.
 // A device-scope fence per workgroup (to let the last one merge) would write
 // back and invalidate the L2 of its XCD on this multi-XCD part, so the merge
 // across workgroups is a separate kernel.
-// The attention reads only K/V, so the metadata update of step 1 cannot race
-// with it, and stream order makes the new row visible to step 2.
 #include <type_traits>
 
 #include "kvpop_device.h"
@@ -53,6 +55,7 @@ struct DecArgs {
   void* o;
   float* lse;
   float* part;          // [b, Hq, nsplit, D + 2]: max (log2 units), sum, unnormalised O
+  int* dec;             // [b, Hkv, 4] the step's decision, applied by the combine (splits > 1)
   int Hq, Hkv, G, s, w, k, Bc, spl, nsplit;
   float scale_log2;
 };
@@ -82,40 +85,43 @@ __device__ __forceinline__ void wave_reduce_worst(Worst& best) {
   }
 }
 
-template <int D, bool kF32>
-__global__ __launch_bounds__(kDecideThreads) void decode_decide_kernel(DecArgs a) {
-  __shared__ Worst s_worst[kDecideThreads / 64];
-  const int tid = threadIdx.x, lane = lane_id(), wave = wave_id();
-  const int h = blockIdx.x, b = blockIdx.y;
-  const int s = a.s, w = a.w, k = a.k, Bc = a.Bc;
-  const size_t seg = (size_t)b * a.Hkv + h;
-  const int p = a.pos[b];
-  if (p < 0) return;
-  int* spos = a.slot_pos + seg * Bc;
-  float* sprio = a.slot_prio + seg * Bc;
-  int* ring = a.ring + seg * w;
-  const int u = p - w;
-  int u_slot = -1, ns;
-  float pu = 0.0f;
-  bool keep_u = false;      // u becomes a long-range token in its own slot
+// The leave decision of step p for one (sequence, KV head), from the slot
+// metadata as it stands before the step: the slot token p takes (slot p while
+// the cache fills; afterwards the slot of u = p - w when u is dropped, or of
+// the worst held long-range token when u replaces it) and the priority u
+// keeps.  Every workgroup of the pair computes it (all its threads take part;
+// the slot scan issues all its loads before comparing, then a wave and a
+// workgroup reduction).  ns < 0: no step (p < 0) or an inconsistent cache.
+struct Decision {
+  int ns, u_slot;
+  float pu;
+  bool keep_u;
+};
 
+__device__ Decision decide_step(const DecArgs& a, size_t seg, int p, Worst* s_worst) {
+  const int tid = threadIdx.x, lane = lane_id(), wave = wave_id();
+  const int s = a.s, w = a.w, k = a.k, Bc = a.Bc;
+  const int* spos = a.slot_pos + seg * Bc;
+  const float* sprio = a.slot_prio + seg * Bc;
+  const int* ring = a.ring + seg * w;
+  Decision dc{-1, -1, 0.0f, false};
+  if (p < 0) return dc;
+  const int u = p - w;
   if (p < Bc) {
     // filling: token p takes slot p; u (if eligible) joins the long-range set
-    ns = p;
+    dc.ns = p;
     if (p > 0 && u >= s) {
-      u_slot = ring[p % w];
-      pu = canonical_priority(a.prio_leaving[seg]);
-      keep_u = true;
+      dc.u_slot = ring[p % w];
+      dc.pu = canonical_priority(a.prio_leaving[seg]);
+      dc.keep_u = true;
     }
   } else {
     // full: u = p - w >= s + k; it is kept iff it beats the worst long-range token
-    u_slot = ring[p % w];
-    pu = canonical_priority(a.prio_leaving[seg]);
+    dc.u_slot = ring[p % w];
+    dc.pu = canonical_priority(a.prio_leaving[seg]);
     if (k == 0) {
-      ns = u_slot;
+      dc.ns = dc.u_slot;
     } else {
-      // every thread issues all its slot loads before comparing (the scan is
-      // latency-bound otherwise), then a wave and a workgroup reduction
       Worst best{__builtin_huge_valf(), -1, -1};
       for (int j0 = tid; j0 < Bc; j0 += kDecideThreads * kDecideUnroll) {
         int sp[kDecideUnroll];
@@ -139,27 +145,24 @@ __global__ __launch_bounds__(kDecideThreads) void decode_decide_kernel(DecArgs a
 #pragma unroll
       for (int i = 1; i < kDecideThreads / 64; ++i)
         if (worse_than(s_worst[i], best)) best = s_worst[i];
-      keep_u = best.slot >= 0 && pu > best.p;
-      ns = keep_u ? best.slot : u_slot;
+      dc.keep_u = best.slot >= 0 && dc.pu > best.p;
+      dc.ns = dc.keep_u ? best.slot : dc.u_slot;
     }
   }
-  if ((unsigned)ns >= (unsigned)Bc) return;   // inconsistent cache state: leave it untouched
-  if (tid == 0) {
-    if (keep_u && (unsigned)u_slot < (unsigned)Bc) sprio[u_slot] = pu;
-    ring[p % w] = ns;
-    spos[ns] = p;
-    sprio[ns] = 0.0f;
-  }
-  // the new token's K/V row goes into its slot
-  constexpr int kWords = D * (kF32 ? 4 : 2) / 4;
-  const uint32_t* kn = (const uint32_t*)a.k_new + seg * kWords;
-  const uint32_t* vn = (const uint32_t*)a.v_new + seg * kWords;
-  uint32_t* kc = (uint32_t*)a.ck + (seg * Bc + ns) * kWords;
-  uint32_t* vc = (uint32_t*)a.cv + (seg * Bc + ns) * kWords;
-  for (int i = tid; i < kWords; i += kDecideThreads) {
-    kc[i] = kn[i];
-    vc[i] = vn[i];
-  }
+  if ((unsigned)dc.ns >= (unsigned)Bc) dc.ns = -1;   // inconsistent cache state: no update
+  return dc;
+}
+
+// The metadata update of a decision (one thread).
+__device__ __forceinline__ void apply_decision(const DecArgs& a, size_t seg, int p,
+                                               const Decision& dc) {
+  const int Bc = a.Bc, w = a.w;
+  if (dc.ns < 0) return;
+  float* sprio = a.slot_prio + seg * Bc;
+  if (dc.keep_u && (unsigned)dc.u_slot < (unsigned)Bc) sprio[dc.u_slot] = dc.pu;
+  a.ring[seg * w + p % w] = dc.ns;
+  a.slot_pos[seg * Bc + dc.ns] = p;
+  sprio[dc.ns] = 0.0f;
 }
 
 template <int D, bool kF32>
@@ -182,6 +185,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_attend_kernel(DecArgs a) {
   using L = DecLds<D, kF32>;
   static_assert(kWaves * L::waveBytes >= kWaves * 32 * (D + 2) * 4, "merge area");
   __shared__ __attribute__((aligned(16))) unsigned char lds[kWaves * L::waveBytes];
+  __shared__ Worst s_worst[kWaves];
   const int tid = threadIdx.x, lane = lane_id(), wave = wave_id();
   const int hh = lane >> 5, li = lane & 31;
   const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
@@ -222,7 +226,10 @@ __global__ __launch_bounds__(kThreads, 2) void decode_attend_kernel(DecArgs a) {
   float m_run = kNegInf, l_run = 0.0f;
   const size_t cbase = seg * (size_t)Bc * D;
 
-  // ---- staging of one 32-slot block: HBM -> registers -> this wave's LDS
+  // ---- staging of one 32-slot block: HBM -> registers -> this wave's LDS.
+  // The slot the step's new token takes (ns_sub) is read from k_new / v_new
+  // in place of its old content.
+  int ns_sub = -1;
   typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
   uint4 kst[L::KPL];
   u32x4v vpair[kF32 ? 1 : 2 * L::VTL];
@@ -231,12 +238,16 @@ __global__ __launch_bounds__(kThreads, 2) void decode_attend_kernel(DecArgs a) {
     if constexpr (!kF32) {
       const uint16_t* kg = (const uint16_t*)a.ck + cbase;
       const uint16_t* vg = (const uint16_t*)a.cv + cbase;
+      const uint16_t* kn = (const uint16_t*)a.k_new + seg * D;
+      const uint16_t* vn = (const uint16_t*)a.v_new + seg * D;
+      auto krow = [&](int slot) { return slot == ns_sub ? kn : kg + (size_t)slot * D; };
+      auto vrow = [&](int slot) { return slot == ns_sub ? vn : vg + (size_t)slot * D; };
       constexpr int PPR = D / 8;
 #pragma unroll
       for (int i = 0; i < L::KPL; ++i) {
         const int pi = lane + 64 * i;
         const int slot = blk + pi / PPR;
-        kst[i] = slot < j_hi ? *(const uint4*)(kg + (size_t)slot * D + (pi % PPR) * 8)
+        kst[i] = slot < j_hi ? *(const uint4*)(krow(slot) + (pi % PPR) * 8)
                              : make_uint4(0, 0, 0, 0);
       }
 #pragma unroll
@@ -245,20 +256,24 @@ __global__ __launch_bounds__(kThreads, 2) void decode_attend_kernel(DecArgs a) {
         const int pr = task & 15, oc = task >> 4;      // pairs fastest: distinct LDS banks
         const int s0 = blk + 2 * pr;
         const u32x4v z = {0u, 0u, 0u, 0u};
-        vpair[2 * i] = s0 < j_hi ? *(const u32x4v*)(vg + (size_t)s0 * D + 8 * oc) : z;
-        vpair[2 * i + 1] = s0 + 1 < j_hi ? *(const u32x4v*)(vg + (size_t)(s0 + 1) * D + 8 * oc) : z;
+        vpair[2 * i] = s0 < j_hi ? *(const u32x4v*)(vrow(s0) + 8 * oc) : z;
+        vpair[2 * i + 1] = s0 + 1 < j_hi ? *(const u32x4v*)(vrow(s0 + 1) + 8 * oc) : z;
       }
     } else {
       const float* kg = (const float*)a.ck + cbase;
       const float* vg = (const float*)a.cv + cbase;
+      const float* kn = (const float*)a.k_new + seg * D;
+      const float* vn = (const float*)a.v_new + seg * D;
       constexpr int PPR = D / 4;
 #pragma unroll
       for (int i = 0; i < L::KPL; ++i) {
         const int pi = lane + 64 * i;
         const int slot = blk + pi / PPR;
-        const size_t off = (size_t)slot * D + (pi % PPR) * 4;
-        kst[i] = slot < j_hi ? *(const uint4*)(kg + off) : make_uint4(0, 0, 0, 0);
-        vst4[i] = slot < j_hi ? *(const uint4*)(vg + off) : make_uint4(0, 0, 0, 0);
+        const int piece = (pi % PPR) * 4;
+        const float* kr = slot == ns_sub ? kn : kg + (size_t)slot * D;
+        const float* vr = slot == ns_sub ? vn : vg + (size_t)slot * D;
+        kst[i] = slot < j_hi ? *(const uint4*)(kr + piece) : make_uint4(0, 0, 0, 0);
+        vst4[i] = slot < j_hi ? *(const uint4*)(vr + piece) : make_uint4(0, 0, 0, 0);
       }
     }
   };
@@ -307,8 +322,65 @@ __global__ __launch_bounds__(kThreads, 2) void decode_attend_kernel(DecArgs a) {
     }
   };
 
+  // the first block's loads are issued before the step's decision (its slot
+  // is patched afterwards); the new token's K/V row is written to its slot
+  // at the end by the split that owns the slot (no other workgroup reads
+  // that slot in this step)
   int blk = j_lo + wave * kBlk;
   if (blk < j_hi) load_blk(blk);
+  const Decision dc = decide_step(a, seg, p, s_worst);
+  const int ns = dc.ns;
+  __syncthreads();   // every metadata read of this workgroup is done
+  if (tid == 0) {
+    if (a.nsplit == 1) {
+      apply_decision(a, seg, p, dc);
+    } else if (split == 0) {
+      int* rec = a.dec + seg * 4;
+      rec[0] = ns;
+      rec[1] = dc.u_slot;
+      rec[2] = dc.keep_u ? 1 : 0;
+      rec[3] = __float_as_int(dc.pu);
+    }
+  }
+  ns_sub = ns;
+  if (blk < j_hi && ns >= blk && ns < blk + kBlk) {
+    // patch the new token's row into the first block (unconditional loads of
+    // the one new row, then selects)
+    const int r = ns - blk;
+    if constexpr (!kF32) {
+      const uint16_t* kn = (const uint16_t*)a.k_new + seg * D;
+      const uint16_t* vn = (const uint16_t*)a.v_new + seg * D;
+      constexpr int PPR = D / 8;
+#pragma unroll
+      for (int i = 0; i < L::KPL; ++i) {
+        const int pi = lane + 64 * i;
+        const uint4 nk = *(const uint4*)(kn + (pi % PPR) * 8);
+        if (pi / PPR == r) kst[i] = nk;
+      }
+#pragma unroll
+      for (int i = 0; i < L::VTL; ++i) {
+        const int task = lane + 64 * i;
+        const int pr = task & 15, oc = task >> 4;
+        const u32x4v nv = *(const u32x4v*)(vn + 8 * oc);
+        if (2 * pr == r) vpair[2 * i] = nv;
+        if (2 * pr + 1 == r) vpair[2 * i + 1] = nv;
+      }
+    } else {
+      const float* kn = (const float*)a.k_new + seg * D;
+      const float* vn = (const float*)a.v_new + seg * D;
+      constexpr int PPR = D / 4;
+#pragma unroll
+      for (int i = 0; i < L::KPL; ++i) {
+        const int pi = lane + 64 * i;
+        const uint4 nk = *(const uint4*)(kn + (pi % PPR) * 4);
+        const uint4 nv = *(const uint4*)(vn + (pi % PPR) * 4);
+        if (pi / PPR == r) {
+          kst[i] = nk;
+          vst4[i] = nv;
+        }
+      }
+    }
+  }
   for (; blk < j_hi; blk += kWaves * kBlk) {
     store_blk();
     wave_lds_fence();
@@ -428,14 +500,34 @@ __global__ __launch_bounds__(kThreads, 2) void decode_attend_kernel(DecArgs a) {
       pp[2 + d] = Od;
     }
   }
+  // the new token's K/V row into its slot, by the split that owns the slot
+  if (ns >= j_lo && ns < j_hi) {
+    constexpr int kWords = D * (kF32 ? 4 : 2) / 4;
+    const uint32_t* knw = (const uint32_t*)a.k_new + seg * kWords;
+    const uint32_t* vnw = (const uint32_t*)a.v_new + seg * kWords;
+    uint32_t* kc = (uint32_t*)a.ck + (seg * Bc + ns) * kWords;
+    uint32_t* vc = (uint32_t*)a.cv + (seg * Bc + ns) * kWords;
+    for (int i = tid; i < kWords; i += kThreads) {
+      kc[i] = knw[i];
+      vc[i] = vnw[i];
+    }
+  }
 }
 
-// Merges the per-split partials of one (sequence, KV head) into o and lse.
+// Merges the per-split partials of one (sequence, KV head) into o and lse,
+// and applies the step's metadata update (recorded by split 0: every split
+// has read the metadata by now).
 template <int D, bool kF32Out>
 __global__ __launch_bounds__(kThreads) void decode_combine_kernel(DecArgs a) {
   constexpr int RS = D + 2;
   const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
   const int G = a.G, nsplit = a.nsplit;
+  if (tid == 0) {
+    const size_t seg = (size_t)b * a.Hkv + h;
+    const int* rec = a.dec + seg * 4;
+    const Decision dc{rec[0], rec[1], __int_as_float(rec[3]), rec[2] != 0};
+    apply_decision(a, seg, a.pos[b], dc);
+  }
   for (int idx = tid; idx < G * D; idx += kThreads) {
     const int g = idx / D, d = idx % D;
     const size_t hq = (size_t)b * a.Hq + h * G + g;
@@ -460,8 +552,6 @@ __global__ __launch_bounds__(kThreads) void decode_combine_kernel(DecArgs a) {
 
 template <int D, bool kF32, bool kF32Out>
 void launch_dec(const DecArgs& a, int b, hipStream_t st) {
-  hipLaunchKernelGGL((decode_decide_kernel<D, kF32>), dim3(a.Hkv, b), dim3(kDecideThreads), 0, st,
-                     a);
   hipLaunchKernelGGL((decode_attend_kernel<D, kF32, kF32Out>), dim3(a.nsplit, a.Hkv, b),
                      dim3(kThreads), 0, st, a);
   if (a.nsplit > 1)
@@ -495,7 +585,9 @@ int decode_splits(const Dims& d) {
 
 size_t decode_ws_bytes(const Dims& d) {
   const int ns = decode_splits(d);
-  return ns > 1 ? align256((size_t)d.b * d.Hq * ns * (d.D + 2) * 4) : 0;
+  return ns > 1 ? align256((size_t)d.b * d.Hq * ns * (d.D + 2) * 4) +
+                      align256((size_t)d.nseg() * 4 * 4)
+                : 0;
 }
 
 hipError_t launch_decode(const Dims& d, const CacheArgs& c, const int* pos, const void* q,
@@ -508,6 +600,8 @@ hipError_t launch_decode(const Dims& d, const CacheArgs& c, const int* pos, cons
   a.pos = pos; a.q = q; a.k_new = k_new; a.v_new = v_new; a.prio_leaving = prio_leaving;
   a.o = o; a.lse = lse;
   a.part = (float*)ws;
+  a.dec = nsplit > 1 ? (int*)((char*)ws + align256((size_t)d.b * d.Hq * nsplit * (d.D + 2) * 4))
+                     : nullptr;
   a.Hq = d.Hq; a.Hkv = d.Hkv; a.G = d.G; a.s = d.s; a.w = d.w; a.k = d.k;
   a.Bc = (int)d.budget(); a.spl = spl; a.nsplit = nsplit;
   a.scale_log2 = d.scale * 1.4426950408889634f;
