@@ -154,6 +154,154 @@ def bench_labels(kv, torch, score, s, w, k, ev, reps=5):
             "rows_per_s": round(rows / (ms * 1e-3), 1), "frac_newcomer_kept": round(kept, 4)}
 
 
+def bench_layer_c3(kv, torch, dev, ev, reps=5):
+    """The Qwen3-8B-shaped layer (S 32768, B 4096): thresholds, masked forward
+    and target pass, each timed on its own and end to end (teacher LSE from
+    the dense forward beforehand, untimed)."""
+    from workloads import QWEN3_8B_S32K as wl, make_prefill_device
+    s, w, k, S, D, Hq = wl.sink, wl.window, wl.topk, wl.seq_len, wl.head_dim, wl.n_q_heads
+    x = make_prefill_device(wl, dev)
+    q, kk, v, prio = x["q"], x["k"], x["v"], x["prio"]
+    bf = torch.bfloat16
+    rank_d, tau_d = kv.thresholds(prio, s, w, S)
+    _, lse_t = kv.masked_attn_fwd(q, kk, v, rank_d, tau_d, s, w, S, out_dtype=bf)
+    del rank_d, tau_d
+    rank, tau = kv.thresholds(prio, s, w, k)
+    o, lse = kv.masked_attn_fwd(q, kk, v, rank, tau, s, w, k, out_dtype=bf)
+    tgt = kv.future_target(q, kk, lse_t, w)
+    torch.cuda.synchronize()
+    t = {"thresholds": [], "fwd": [], "target": [], "end_to_end": []}
+    for _ in range(reps):
+        e = [ev() for _ in range(4)]
+        e[0].record()
+        kv.thresholds(prio, s, w, k, rank=rank, tau=tau)
+        e[1].record()
+        kv.masked_attn_fwd(q, kk, v, rank, tau, s, w, k, out_dtype=bf, o=o, lse=lse)
+        e[2].record()
+        kv.future_target(q, kk, lse_t, w, target=tgt)
+        e[3].record()
+        torch.cuda.synchronize()
+        t["thresholds"].append(e[0].elapsed_time(e[1]))
+        t["fwd"].append(e[1].elapsed_time(e[2]))
+        t["target"].append(e[2].elapsed_time(e[3]))
+        t["end_to_end"].append(e[0].elapsed_time(e[3]))
+    med = {n: sorted(v_)[len(v_) // 2] for n, v_ in t.items()}
+    f_fwd = 4 * D * Hq * fwd_pairs(S, s + w + k)
+    f_tgt = 2 * D * Hq * tgt_pairs(S, w)
+    return {"workload": wl.name, "reps": reps, "thresholds_us": round(med["thresholds"] * 1e3, 1),
+            "fwd_ms": round(med["fwd"], 4),
+            "fwd_tflops": round(f_fwd / (med["fwd"] * 1e-3) / 1e12, 2),
+            "target_ms": round(med["target"], 4),
+            "target_tflops": round(f_tgt / (med["target"] * 1e-3) / 1e12, 2),
+            "end_to_end_ms": round(med["end_to_end"], 4),
+            "end_to_end_tflops": round((f_fwd + f_tgt) / (med["end_to_end"] * 1e-3) / 1e12, 2)}
+
+
+def bench_long_c5(kv, torch, dev, ev, reps=3, n_layers=4):
+    """Long context (S 131072, B 4096): thresholds + masked forward of one
+    layer; then 8 sequences decoded from position 0 to 131071 over
+    `n_layers` independent layer caches in turn (so that no cache is served
+    from the last-level cache between its steps), reporting the steady state
+    (positions >= B, full caches) and the whole run, and the device memory
+    held across the steps."""
+    from workloads import LONG_S128K as wl, make_decode_stream_device, make_prefill_device, scaled
+    s, w, k, S, D, Hq, Hkv = (wl.sink, wl.window, wl.topk, wl.seq_len, wl.head_dim,
+                              wl.n_q_heads, wl.n_kv_heads)
+    Bc = s + w + k
+    bf = torch.bfloat16
+    x = make_prefill_device(wl, dev)
+    q, kk, v, prio = x["q"], x["k"], x["v"], x["prio"]
+    rank, tau = kv.thresholds(prio, s, w, k)
+    o, lse = kv.masked_attn_fwd(q, kk, v, rank, tau, s, w, k, out_dtype=bf)
+    torch.cuda.synchronize()
+    t = {"thresholds": [], "fwd": [], "end_to_end": []}
+    for _ in range(reps):
+        e = [ev() for _ in range(3)]
+        e[0].record()
+        kv.thresholds(prio, s, w, k, rank=rank, tau=tau)
+        e[1].record()
+        kv.masked_attn_fwd(q, kk, v, rank, tau, s, w, k, out_dtype=bf, o=o, lse=lse)
+        e[2].record()
+        torch.cuda.synchronize()
+        t["thresholds"].append(e[0].elapsed_time(e[1]))
+        t["fwd"].append(e[1].elapsed_time(e[2]))
+        t["end_to_end"].append(e[0].elapsed_time(e[2]))
+    med = {n: sorted(v_)[len(v_) // 2] for n, v_ in t.items()}
+    f_fwd = 4 * D * Hq * fwd_pairs(S, Bc)
+    del x, q, kk, v, prio, rank, tau, o, lse
+    torch.cuda.empty_cache()
+
+    dwl = scaled(wl, batch=8)
+    nseq, n_steps = dwl.batch, S
+    st = make_decode_stream_device(dwl, dev, n_steps)
+    kn_all, vn_all = st["k_new"], st["v_new"]
+    prio_steps = st["prio_table"].permute(2, 0, 1).contiguous()    # [n_steps, nseq, Hkv]
+    del st
+    g = torch.Generator(device=dev)
+    g.manual_seed(4321)
+    n_q = 1024
+    qs = torch.randn((n_q, nseq, Hq, D), generator=g, device=dev).to(bf)
+    caches = [kv.new_decode_cache(nseq, Hkv, D, s, w, k, dtype=bf, device=dev)
+              for _ in range(n_layers)]
+    pos_all = torch.arange(n_steps, dtype=torch.int32, device=dev)[:, None].repeat(1, nseq)
+    zero_prio = torch.zeros((nseq, Hkv), device=dev)
+    o = torch.empty((nseq, Hq, D), dtype=bf, device=dev)
+    lse = torch.empty((nseq, Hq), dtype=torch.float32, device=dev)
+    pr = kv.Problem(nseq, Hq, Hkv, 0, D, s, w, k, 0.0, 0, 0)
+    n_ws = kv.workspace_size(3, pr)
+    ws_raw = torch.empty(n_ws + 256, dtype=torch.uint8, device=dev)
+    ws = ws_raw[(-ws_raw.data_ptr()) % 256:][:n_ws]
+    # eager steps: at these sizes the kernels keep the GPU busy (the trace of
+    # a step shows no launch gaps), and the inputs are passed by pointer; the
+    # step is also capturable in a HIP graph (see the graph replay test)
+    torch.cuda.synchronize()
+    torch.cuda.reset_peak_memory_stats(dev)
+    mem0 = torch.cuda.memory_allocated(dev)
+    e_start, e_full, e_end = ev(), ev(), ev()
+    t0 = time.perf_counter()
+    e_start.record()
+    for p in range(n_steps):
+        if p == Bc:
+            e_full.record()
+        pl = prio_steps[p - w] if p >= w else zero_prio
+        for c in caches:
+            kv.decode_step(c, pos_all[p], qs[p % n_q], kn_all[p], vn_all[p], pl, s, w, k,
+                           out_dtype=bf, o=o, lse=lse, ws=ws)
+        if p % 16384 == 16383:
+            print(f"[bench] long decode at position {p + 1} of {n_steps}", file=sys.stderr,
+                  flush=True)
+    e_end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    mem1 = torch.cuda.memory_allocated(dev)
+    peak = torch.cuda.max_memory_allocated(dev)
+    ms_all = e_start.elapsed_time(e_end)
+    ms_full = e_full.elapsed_time(e_end)
+    steps_full = n_steps - Bc
+    us_layer_step = ms_full * 1e3 / (steps_full * n_layers)
+    nbytes = decode_bytes_per_step(nseq, Hq, Hkv, D, Bc)
+    gbps = nbytes / (us_layer_step * 1e-6) / 1e9
+    cache_bytes = sum(c.k.numel() * 2 * 2 + c.slot_pos.numel() * 8 + c.ring.numel() * 4
+                      for c in caches)
+    return {"workload": wl.name, "reps": reps,
+            "thresholds_us": round(med["thresholds"] * 1e3, 1),
+            "fwd_ms": round(med["fwd"], 4),
+            "fwd_tflops": round(f_fwd / (med["fwd"] * 1e-3) / 1e12, 2),
+            "end_to_end_ms": round(med["end_to_end"], 4),
+            "decode": {"sequences": nseq, "positions": [0, n_steps - 1], "layer_caches": n_layers,
+                       "steady_state": {"positions": [Bc, n_steps - 1],
+                                        "us_per_layer_step": round(us_layer_step, 2),
+                                        "bytes_per_layer_step": nbytes,
+                                        "GB/s": round(gbps, 1),
+                                        "frac_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4)},
+                       "all_steps": {"ms": round(ms_all, 1), "wall_s": round(wall, 2),
+                                     "tokens_per_s_per_layer":
+                                         round(nseq * n_steps / (ms_all * 1e-3), 1)},
+                       "device_memory": {"caches_bytes": cache_bytes,
+                                         "allocated_before": mem0, "allocated_after": mem1,
+                                         "peak_during": peak}}}
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -162,6 +310,8 @@ def parse():
     ap.add_argument("--decode-steps", type=int, default=1024)
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-other-configs", action="store_true",
+                    help="skip the S 32768 layer and the S 131072 long-context legs")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run one plain device copy of this many MiB (counter calibration)")
     return ap.parse_args()
@@ -329,6 +479,11 @@ def main():
 
     if not args.no_decode:
         out["decode"] = bench_decode(kv, torch, np, dev, args.decode_steps)
+    if not args.no_other_configs:
+        del q, kk, v, o, lse, tgt, lse_teacher, rank_d, tau_d
+        torch.cuda.empty_cache()
+        out["other_configs"] = {"qwen3-8b-layer": bench_layer_c3(kv, torch, dev, ev),
+                                "long-context": bench_long_c5(kv, torch, dev, ev)}
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(x, s, w, k)
     print(json.dumps(out))
