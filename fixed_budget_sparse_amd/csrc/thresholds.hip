@@ -195,7 +195,6 @@ __global__ __launch_bounds__(kLdsSortThreads) void lds_rank_kernel(const float* 
   const int wbase = wave * 64 * ipl;
   uint32_t key[kLdsSortItems], pos[kLdsSortItems];
   int val[kLdsSortItems];
-  uint64_t peers[kLdsSortItems];
 #pragma unroll
   for (int i = 0; i < kLdsSortItems; ++i) {
     const int idx = wbase + 64 * i + lane;
@@ -208,15 +207,24 @@ __global__ __launch_bounds__(kLdsSortThreads) void lds_rank_kernel(const float* 
     const int shift = 8 * pass;
     for (int j = tid; j < kLdsSortWaves * kRadix; j += kLdsSortThreads) offs[j] = 0;
     __syncthreads();
-    // count each digit per wave
+    // count each digit per wave; every key keeps its place among the wave's
+    // keys of its digit (the running count read before the lowest lane of its
+    // digit advances it; LDS operations of a wave execute in order)
 #pragma unroll
     for (int i = 0; i < kLdsSortItems; ++i) {
       if (i < ipl) {
         const bool valid = wbase + 64 * i + lane < S;
         const uint32_t dig = (key[i] >> shift) & 255u;
-        peers[i] = same_digit_lanes(dig, valid);
-        if (valid && lane == __builtin_ctzll(peers[i]))
-          offs[wave * kRadix + dig] += (uint32_t)__builtin_popcountll(peers[i]);
+        const uint64_t peers = same_digit_lanes(dig, valid);
+        uint32_t run = 0;
+        if (valid) {
+          run = offs[wave * kRadix + dig];
+          pos[i] = run + (uint32_t)lanes_below(peers);
+        }
+        wave_lds_fence();
+        if (valid && lane == __builtin_ctzll(peers))
+          offs[wave * kRadix + dig] = run + (uint32_t)__builtin_popcountll(peers);
+        wave_lds_fence();
       }
     }
     __syncthreads();
@@ -243,23 +251,11 @@ __global__ __launch_bounds__(kLdsSortThreads) void lds_rank_kernel(const float* 
       }
     }
     __syncthreads();
-    // place every key; lanes of one digit read the running place, then the
-    // lowest of them advances it (LDS operations of a wave execute in order)
+    // place every key: its (wave, digit) start plus its place among them
 #pragma unroll
     for (int i = 0; i < kLdsSortItems; ++i) {
-      if (i < ipl) {
-        const bool valid = wbase + 64 * i + lane < S;
-        const uint32_t dig = (key[i] >> shift) & 255u;
-        uint32_t start = 0;
-        if (valid) {
-          start = offs[wave * kRadix + dig];
-          pos[i] = start + (uint32_t)lanes_below(peers[i]);
-        }
-        wave_lds_fence();
-        if (valid && lane == __builtin_ctzll(peers[i]))
-          offs[wave * kRadix + dig] = start + (uint32_t)__builtin_popcountll(peers[i]);
-        wave_lds_fence();
-      }
+      if (i < ipl && wbase + 64 * i + lane < S)
+        pos[i] += offs[wave * kRadix + ((key[i] >> shift) & 255u)];
     }
     if (pass < 3) {
       // every wave finished reading the previous order before the last barrier

@@ -37,6 +37,8 @@ THR_CASES = [
     (2, 3, 9000, 0, 1, 37, "ties"),          # heavy ties, NaN, +-inf
     (1, 1, 4097, 1, 1, 1, "increasing"),     # cutoff moves every step
     (1, 1, 3000, 5, 9, 100, "decreasing"),   # cutoff never moves
+    (1, 2, 16384, 3, 7, 500, "ties"),        # largest one-workgroup rank
+    (1, 1, 16385, 3, 7, 500, "ties"),        # smallest multi-workgroup rank
 ]
 
 
