@@ -464,8 +464,8 @@ __global__ __launch_bounds__(kKThreads) void bwd_dkdv_kernel(BwdArgs a) {
 
   // staging: each task is (row pair p, piece pc); lanes of a wave cover 16
   // pairs of 4 pieces, so their transposed word stores spread over the banks
-  u32x4v rq_[2][TPT][2], ro_[2][TPT][2];
-  float rv_[2][3] = {{0.0f, 0.0f, 0.0f}, {0.0f, 0.0f, 0.0f}};
+  u32x4v rq_[1][TPT][2], ro_[1][TPT][2];
+  float rv_[1][3] = {{0.0f, 0.0f, 0.0f}};
   auto load = [&](int item, auto slot) {
     constexpr int sl = decltype(slot)::value;
     auto& rq = rq_[sl];
@@ -485,8 +485,8 @@ __global__ __launch_bounds__(kKThreads) void bwd_dkdv_kernel(BwdArgs a) {
         ro[i][r] = *(const u32x4v*)(a.dout + (hrow + qq) * D + 8 * pc);
       }
     }
-    if (tid < kRChunk) {
-      const int qq = min(c0 + tid, S - 1);
+    {   // every lane loads (no exec-masked loads); lanes below kRChunk store
+      const int qq = min(c0 + (tid & (kRChunk - 1)), S - 1);
       r_val[0] = a.lse[hrow + qq];
       r_val[1] = a.dvec[hrow + qq];
       r_val[2] = __int_as_float(tau[qq]);
@@ -532,23 +532,24 @@ __global__ __launch_bounds__(kKThreads) void bwd_dkdv_kernel(BwdArgs a) {
     }
   };
 
-  // item it is staged in LDS buffer it & 1 and held in registers slot it & 1
-  // two items ahead: loads of item it+2 are issued while item it computes
+  // Item it is staged in LDS buffer it & 1.  One register stage: after item
+  // it's math, item it+1 (loaded one item earlier) goes from registers to the
+  // other buffer and the loads of item it+2 are issued into the freed
+  // registers, so each item's global loads have a whole item of math to land.
+  // The loads are unconditional (past the last item they repeat it): loads
+  // into one of two register sets chosen at run time were compiled as loads
+  // into temporaries plus copies that waited for them at once, which exposed
+  // the whole load latency on every item.
   using S0 = std::integral_constant<int, 0>;
-  using S1 = std::integral_constant<int, 1>;
   if (n_items > 0) {
     load(0, S0{});
     store(0, S0{});
+    load(min(1, n_items - 1), S0{});
+    __syncthreads();
   }
-  if (n_items > 1) load(1, S1{});
-  __syncthreads();
   for (int it = 0; it < n_items; ++it) {
     const int buf = it & 1;
     const int c0 = (c_first + it % n_chunk) * kRChunk;
-    if (it + 2 < n_items) {                          // into the slot item it vacated
-      if (buf == 0) load(it + 2, S0{});
-      else load(it + 2, S1{});
-    }
     const unsigned char* st = stage[buf];
     const uint16_t* ql = (const uint16_t*)(st + L::kQ) + li * L::RS + 8 * hh;
     const uint16_t* ol = (const uint16_t*)(st + L::kO) + li * L::RS + 8 * hh;
@@ -563,15 +564,26 @@ __global__ __launch_bounds__(kKThreads) void bwd_dkdv_kernel(BwdArgs a) {
       sacc = mfma32x32x16(as_bf16x8(*(const uint4*)(ql + 16 * ks)), kop[ks], sacc);
       pacc = mfma32x32x16(as_bf16x8(*(const uint4*)(ol + 16 * ks)), vop[ks], pacc);
     }
+    // branch-free: the exp of every score, then a select (a masked score's
+    // exp may overflow; it is never used); the row values in 4-wide reads
     float pv[16], dsv[16];
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const int i = 8 * (e >> 2) + 4 * hh + (e & 3);
-      const int qq = c0 + i;
-      const bool kp = (qq < S) && kept(qq, t, rk_m, r_tau[i], s, w);
-      const float p = kp ? exp2_fast(fmaf(sacc[e], a.scale_log2, -r_lse[i])) : 0.0f;
-      pv[e] = p;
-      dsv[e] = p * (pacc[e] - r_d[i]);
+    for (int j = 0; j < 4; ++j) {
+      const int i0 = 8 * j + 4 * hh;
+      const f32x4 lse4 = *(const f32x4*)(r_lse + i0);
+      const f32x4 d4 = *(const f32x4*)(r_d + i0);
+      const int4 tau4 = *(const int4*)(r_tau + i0);
+      const int tq[4] = {tau4.x, tau4.y, tau4.z, tau4.w};
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int e = 4 * j + r;
+        const int qq = c0 + i0 + r;
+        const bool kp = (qq < S) & kept(qq, t, rk_m, tq[r], s, w);
+        const float ex = exp2_fast(fmaf(sacc[e], a.scale_log2, -lse4[r]));
+        const float p = kp ? ex : 0.0f;
+        pv[e] = p;
+        dsv[e] = p * (pacc[e] - d4[r]);
+      }
     }
     bf16x8 pp[2], ps[2];
 #pragma unroll
@@ -590,10 +602,8 @@ __global__ __launch_bounds__(kKThreads) void bwd_dkdv_kernel(BwdArgs a) {
         dkacc[d2] = mfma32x32x16(as_bf16x8(*(const uint4*)(qtl + 16 * ks)), ps[ks], dkacc[d2]);
       }
     }
-    if (it + 1 < n_items) {                          // item it+1 into the other stage
-      if (buf == 0) store(1, S1{});
-      else store(0, S0{});
-    }
+    if (it + 1 < n_items) store(buf ^ 1, S0{});       // item it+1 into the other buffer
+    load(min(it + 2, n_items - 1), S0{});             // item it+2 into the freed registers
     __syncthreads();
   }
 
