@@ -208,7 +208,8 @@ __global__ __launch_bounds__(kQThreads, 1) void bwd_dq_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t k_lds[kQChunk * L::RS];
   __shared__ __attribute__((aligned(16))) uint16_t v_lds[kQChunk * L::RS];
   __shared__ __attribute__((aligned(16))) uint16_t kt_lds[D * L::TS];
-  __shared__ int kd_t[kQChunk], kd_r[kQChunk];
+  __shared__ __attribute__((aligned(16))) int kd_t[kQChunk];
+  __shared__ __attribute__((aligned(16))) int kd_r[kQChunk];
 
   const int tid = threadIdx.x, lane = lane_id(), wave = wave_id();
   const int hh = lane >> 5, li = lane & 31;
@@ -295,22 +296,32 @@ __global__ __launch_bounds__(kQThreads, 1) void bwd_dq_kernel(BwdArgs a) {
       kd_r[tid] = r;
     }
     __syncthreads();
-    // gather K, V rows: row-major K and V, transposed K with permuted columns
-    for (int task = tid; task < kQChunk * PPR; task += kQThreads) {
-      const int j = task / PPR, pc = task % PPR;
-      const int t = kd_t[j];
-      u32x4v kx = {0, 0, 0, 0}, vx = {0, 0, 0, 0};
-      if (t >= 0) {
-        kx = *(const u32x4v*)(a.k + kvbase + (size_t)t * D + 8 * pc);
-        vx = *(const u32x4v*)(a.v + kvbase + (size_t)t * D + 8 * pc);
+    // gather K, V rows: row-major K and V, transposed K with permuted columns.
+    // A task is (key pair, 16-byte piece); keys 2p and 2p+1 sit in adjacent
+    // transposed columns, so each dim is one 32-bit word, and the 32 pairs of
+    // a half-wave spread over the banks.  Loads are unconditional from a
+    // valid row (padding slots read row 0 and are zeroed).
+    for (int task = tid; task < (kQChunk / 2) * PPR; task += kQThreads) {
+      const int p = task & (kQChunk / 2 - 1), pc = task / (kQChunk / 2);
+      u32x4v kx[2], vx[2];
+#pragma unroll
+      for (int r = 0; r < 2; ++r) {
+        const int t = kd_t[2 * p + r];
+        const size_t row = kvbase + (size_t)max(t, 0) * D + 8 * pc;
+        kx[r] = *(const u32x4v*)(a.k + row);
+        vx[r] = *(const u32x4v*)(a.v + row);
+        if (t < 0) kx[r] = vx[r] = u32x4v{0, 0, 0, 0};
+        *(u32x4v*)(k_lds + (2 * p + r) * L::RS + 8 * pc) = kx[r];
+        *(u32x4v*)(v_lds + (2 * p + r) * L::RS + 8 * pc) = vx[r];
       }
-      *(u32x4v*)(k_lds + j * L::RS + 8 * pc) = kx;
-      *(u32x4v*)(v_lds + j * L::RS + 8 * pc) = vx;
-      const int col = perm_col(j);
+      uint32_t* ktw = (uint32_t*)kt_lds;
+      const int cw = perm_col(2 * p) >> 1;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        kt_lds[(8 * pc + 2 * e) * L::TS + col] = (uint16_t)(kx[e] & 0xffffu);
-        kt_lds[(8 * pc + 2 * e + 1) * L::TS + col] = (uint16_t)(kx[e] >> 16);
+        const uint32_t ka = kx[0][e], kb = kx[1][e];
+        const int d0 = 8 * pc + 2 * e;
+        ktw[d0 * (L::TS / 2) + cw] = (ka & 0xffffu) | (kb << 16);
+        ktw[(d0 + 1) * (L::TS / 2) + cw] = (ka >> 16) | (kb & 0xffff0000u);
       }
     }
     __syncthreads();
@@ -329,16 +340,25 @@ __global__ __launch_bounds__(kQThreads, 1) void bwd_dq_kernel(BwdArgs a) {
         pacc[blk] = mfma32x32x16(as_bf16x8(*(const uint4*)(vl + 16 * ks)), dop[ks], pacc[blk]);
       }
     }
-    // dS = P (dP - D_i), P = exp(S scale - LSE_i) on kept keys
+    // dS = P (dP - D_i), P = exp(S scale - LSE_i) on kept keys (branch-free:
+    // the exp of every score, then a select; the key data in 4-wide reads)
     float dsv[2][16];
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int j = 32 * blk + 8 * (e >> 2) + 4 * hh + (e & 3);
-        const bool kp = row_ok && kept(q, kd_t[j], kd_r[j], tau_q, s, w);
-        const float p = kp ? exp2_fast(fmaf(sacc[blk][e], a.scale_log2, -lse2)) : 0.0f;
-        dsv[blk][e] = p * (pacc[blk][e] - drow);
+      for (int jj = 0; jj < 4; ++jj) {
+        const int j0 = 32 * blk + 8 * jj + 4 * hh;
+        const int4 t4 = *(const int4*)(kd_t + j0);
+        const int4 r4 = *(const int4*)(kd_r + j0);
+        const int tv[4] = {t4.x, t4.y, t4.z, t4.w}, rv[4] = {r4.x, r4.y, r4.z, r4.w};
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int e = 4 * jj + r;
+          const bool kp = row_ok & kept(q, tv[r], rv[r], tau_q, s, w);
+          const float ex = exp2_fast(fmaf(sacc[blk][e], a.scale_log2, -lse2));
+          const float p = kp ? ex : 0.0f;
+          dsv[blk][e] = p * (pacc[blk][e] - drow);
+        }
       }
     bf16x8 pk[4];
 #pragma unroll
