@@ -312,6 +312,10 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-other-configs", action="store_true",
                     help="skip the S 32768 layer and the S 131072 long-context legs")
+    ap.add_argument("--no-overlap", dest="overlap", action="store_false",
+                    help="run the target pass after the forward on one stream")
+    ap.add_argument("--no-isolated", dest="isolated", action="store_false",
+                    help="skip the forward and target timed alone after the step")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run one plain device copy of this many MiB (counter calibration)")
     return ap.parse_args()
@@ -392,18 +396,36 @@ def main():
 
     ev = lambda: torch.cuda.Event(enable_timing=True)   # noqa: E731
     times = {"thr": [], "fwd": [], "tgt": []}
+    # The target pass reads only Q, K and the teacher LSE, so it does not wait
+    # for the cutoffs or the forward: it runs on a second stream (default
+    # priority) beside them, and the step ends when both streams are done.
+    # The cutoff kernels fill only a few CUs; the target fills the rest.
+    main_stream = torch.cuda.current_stream(dev)
+    tgt_stream = torch.cuda.Stream(dev) if args.overlap else main_stream
 
     def one_step(record):
-        e0, e1, e2, e3 = ev(), ev(), ev(), ev()
-        e0.record()
+        e0, e1, e2, e3, e4, e5 = ev(), ev(), ev(), ev(), ev(), ev()
+        def target():
+            with torch.cuda.stream(tgt_stream):
+                e4.record(tgt_stream)
+                kv.future_target(q, kk, lse_teacher, w, target=tgt)
+                e5.record(tgt_stream)
+
+        e0.record(main_stream)
+        if args.overlap:
+            tgt_stream.wait_event(e0)
+            target()
         kv.thresholds(prio, s, w, k, rank=rank, tau=tau)
-        e1.record()
+        e1.record(main_stream)
         kv.masked_attn_fwd(q, kk, v, rank, tau, s, w, k, out_dtype=bf, o=o, lse=lse)
-        e2.record()
-        kv.future_target(q, kk, lse_teacher, w, target=tgt)
-        e3.record()
+        e2.record(main_stream)
+        if args.overlap:
+            main_stream.wait_event(e5)
+        else:
+            target()
+        e3.record(main_stream)
         if record is not None:
-            record.append((e0, e1, e2, e3))
+            record.append((e0, e1, e2, e3, e4, e5))
 
     for _ in range(args.warmup):
         one_step(None)
@@ -414,11 +436,28 @@ def main():
         one_step(recs)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    for e0, e1, e2, e3 in recs:
+    step_ev = []
+    for e0, e1, e2, e3, e4, e5 in recs:
         times["thr"].append(e0.elapsed_time(e1))
         times["fwd"].append(e1.elapsed_time(e2))
-        times["tgt"].append(e2.elapsed_time(e3))
+        times["tgt"].append(e4.elapsed_time(e5))
+        step_ev.append(e0.elapsed_time(e3))
     ms_step = wall * 1e3 / args.steps
+    # after the timed region: the forward and the target each alone on the
+    # chip (in the step they share it), 10 launches each
+    iso = {}
+    alone = (("fwd", lambda: kv.masked_attn_fwd(q, kk, v, rank, tau, s, w, k, out_dtype=bf,
+                                                o=o, lse=lse)),
+             ("tgt", lambda: kv.future_target(q, kk, lse_teacher, w, target=tgt)))
+    for name, fn in alone if args.isolated else ():
+        fn()
+        ea, eb = ev(), ev()
+        ea.record()
+        for _ in range(10):
+            fn()
+        eb.record()
+        torch.cuda.synchronize()
+        iso[name] = ea.elapsed_time(eb) / 10
     # the target score per KV head, timed alone, then the sparse-LSE study
     # (untimed): `lse` holds the last step's sparse LSE, `tgt` the exact target
     eps = 1e-6
@@ -458,10 +497,15 @@ def main():
         "data": "synthetic",
         "config": {"workload": wl.name, "batch": wl.batch, "n_q_heads": Hq, "n_kv_heads": Hkv,
                    "head_dim": D, "seq_len": S, "sink": s, "window": w, "topk": k, "budget": B,
-                   "step": "thresholds + masked fwd + future target",
+                   "step": ("thresholds + masked fwd, future target on a second stream beside them"
+                            if args.overlap else "thresholds + masked fwd + future target"),
                    "decode_workload": DECODE_B2048.name},
         "frac_mfma_peak": round(value / MFMA_BF16_PEAK_TFLOPS, 4),
         "kernels_ms": {n: round(t, 4) for n, t in avg.items()},
+        "step_ms_events": round(sum(step_ev) / len(step_ev), 4),
+        "isolated_ms": {n: round(t, 4) for n, t in iso.items()} or None,
+        "isolated_tflops": {"fwd": round(f_fwd / (iso["fwd"] * 1e-3) / 1e12, 2),
+                            "tgt": round(f_tgt / (iso["tgt"] * 1e-3) / 1e12, 2)} if iso else None,
         "fwd_tflops": round(fwd_tflops, 2),
         "target_tflops": round(tgt_tflops, 2),
         "roofline": {"bound": "mfma", "kernel": "future_target_kernel",
