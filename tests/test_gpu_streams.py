@@ -1,0 +1,65 @@
+"""Calls issued on two streams at once give the results of the same calls in order.
+
+The future target needs only Q, K and the teacher LSE, so a training step can
+run it on a second stream while the cutoffs and the sparse forward run on the
+first (the bench does).  The library keeps no state between calls and every
+scratch buffer is the caller's, so concurrent calls on distinct buffers must
+not interfere: every output of the overlapped calls must equal, bit for bit,
+the output of the same calls run one after another (the kernels are
+deterministic), over several overlapped repetitions."""
+import pytest
+import torch
+
+import fixed_budget_sparse_amd as kv
+from gpu_util import announce, device
+
+pytestmark = pytest.mark.gpu
+
+
+def test_target_beside_thresholds_and_forward():
+    announce("two streams: future target beside thresholds + forward, S=4096, 32/8 heads")
+    dev = device()
+    b, hq, hkv, S, D, s, w, k = 1, 32, 8, 4096, 128, 16, 512, 1520
+    bf = torch.bfloat16
+    g = torch.Generator(device=dev)
+    g.manual_seed(2024)
+    q = torch.randn((b, hq, S, D), generator=g, device=dev).to(bf)
+    kk = torch.randn((b, hkv, S, D), generator=g, device=dev)
+    kk[:, :, :4] *= 4.0
+    kk = kk.to(bf)
+    v = torch.randn((b, hkv, S, D), generator=g, device=dev).to(bf)
+    prio = torch.randn((b, hkv, S), generator=g, device=dev)
+    rank_d, tau_d = kv.thresholds(prio, s, w, S)
+    _, lse_teacher = kv.masked_attn_fwd(q, kk, v, rank_d, tau_d, s, w, S, out_dtype=bf)
+
+    # in order, one stream
+    rank0, tau0 = kv.thresholds(prio, s, w, k)
+    o0, lse0 = kv.masked_attn_fwd(q, kk, v, rank0, tau0, s, w, k, out_dtype=bf)
+    tgt0 = kv.future_target(q, kk, lse_teacher, w)
+    torch.cuda.synchronize()
+
+    main = torch.cuda.current_stream(dev)
+    side = torch.cuda.Stream(dev)
+    rank = torch.empty_like(rank0)
+    tau = torch.empty_like(tau0)
+    o = torch.empty_like(o0)
+    lse = torch.empty_like(lse0)
+    tgt = torch.empty_like(tgt0)
+    for rep in range(3):
+        for t in (rank, tau, o, lse, tgt):
+            t.zero_()
+        start = torch.cuda.Event()
+        start.record(main)
+        side.wait_event(start)
+        with torch.cuda.stream(side):
+            kv.future_target(q, kk, lse_teacher, w, target=tgt)
+            done = torch.cuda.Event()
+            done.record(side)
+        kv.thresholds(prio, s, w, k, rank=rank, tau=tau)
+        kv.masked_attn_fwd(q, kk, v, rank, tau, s, w, k, out_dtype=bf, o=o, lse=lse)
+        main.wait_event(done)
+        torch.cuda.synchronize()
+        assert torch.equal(rank, rank0) and torch.equal(tau, tau0), rep
+        assert torch.equal(o.view(torch.int16), o0.view(torch.int16)), rep
+        assert torch.equal(lse.view(torch.int32), lse0.view(torch.int32)), rep
+        assert torch.equal(tgt.view(torch.int32), tgt0.view(torch.int32)), rep
