@@ -22,8 +22,9 @@
 //    dQ^T += K^T dS^T on MFMA with dS as the B operand.
 //  * dK, dV, key-major (bwd_dkdv_kernel): key t is kept by the contiguous rows
 //    [t, q_end(t)] (tau never increases with q), so a tile of keys needs the
-//    rows [min t, max q_end].  bwd_qend_kernel finds q_end(t) by binary search
-//    on tau; bwd_key_order_kernel groups keys into 64-key tiles: keys that
+//    rows [min t, max q_end], and the mask of a (row, key) pair is the
+//    interval test t <= q <= q_end(t).  bwd_qend_kernel finds q_end(t) by
+//    binary search on tau; bwd_key_order_kernel groups keys into 64-key tiles: keys that
 //    live at most w + 64 rows in token order, the others by q_end (a counting
 //    sort over 64-row buckets), which keeps the rows a tile visits close to
 //    the rows its keys need.  Per workgroup (4 waves of 32 keys: two
@@ -393,15 +394,14 @@ template <int D>
 struct KLds {
   static constexpr int RS = D + 8;          // row-major rows (bf16 elements)
   static constexpr int TS = kRChunk + 8;    // transposed rows
-  // one stage: Q and dO row-major and transposed, then LSE, D and tau per row
+  // one stage: Q and dO row-major and transposed, then LSE and D per row
   static constexpr int kQ = 0;
   static constexpr int kO = kQ + kRChunk * RS * 2;
   static constexpr int kQT = kO + kRChunk * RS * 2;
   static constexpr int kOT = kQT + D * TS * 2;
   static constexpr int kLse = kOT + D * TS * 2;
   static constexpr int kD = kLse + kRChunk * 4;
-  static constexpr int kTau = kD + kRChunk * 4;
-  static constexpr int kStage = kTau + kRChunk * 4;
+  static constexpr int kStage = kD + kRChunk * 4;
 };
 
 template <int D>
@@ -422,16 +422,22 @@ __global__ __launch_bounds__(kKThreads) void bwd_dkdv_kernel(BwdArgs a) {
   const int Lb = xcd_logical_block((int)blockIdx.x, (int)gridDim.x);
   const int tile = Lb % a.ktiles, sg = Lb / a.ktiles;
   const int h = sg % a.Hkv, b = sg / a.Hkv;
-  const int S = a.S, s = a.s, w = a.w, G = a.G;
+  const int S = a.S, G = a.G;
   const size_t seg = (size_t)b * a.Hkv + h;
-  const int* tau = a.tau + seg * S;
 
   // this lane's key
   const int slot = tile * kKTile + 32 * wave + li;
   const int t = slot < S ? a.korder[seg * S + slot] : -1;
-  const int rk = t >= 0 ? a.rank[seg * S + t] : 0;
   const int qe = t >= 0 ? a.qend[seg * S + t] : -1;
-  const int rk_m = (t >= 0 && t < s) ? -1 : rk;
+  // The rows that keep key t are exactly [t, q_end(t)]: tau never increases
+  // with q, so once a key leaves the kept set it never returns (sinks and
+  // keys whose window reaches the end have q_end = S - 1).  A row q keeps it
+  // iff 0 <= q - t <= q_end(t) - t: one unsigned compare, the same decision as
+  // the mask test from rank and tau.  Rows past S - 1 exceed q_end; a padding
+  // slot takes t = S + 32, above every row a chunk holds (q - t wraps to a
+  // large unsigned value), with span 0.
+  const unsigned span = t >= 0 ? (unsigned)(qe - t) : 0u;
+  const int t_m = t >= 0 ? t : S + kRChunk;
   const size_t kvbase = seg * (size_t)S * D;
 
   // rows the tile needs: [min t, max q_end]
@@ -485,13 +491,22 @@ __global__ __launch_bounds__(kKThreads) void bwd_dkdv_kernel(BwdArgs a) {
   // staging: each task is (row pair p, piece pc); lanes of a wave cover 16
   // pairs of 4 pieces, so their transposed word stores spread over the banks
   u32x4v rq_[1][TPT][2], ro_[1][TPT][2];
-  float rv_[1][3] = {{0.0f, 0.0f, 0.0f}};
-  auto load = [&](int item, auto slot) {
+  float rv_[1][2] = {{0.0f, 0.0f}};
+  // items in order: query head gg, then chunk ci; the (gg, ci) of an item are
+  // stepped rather than divided out of its index (scalar division is a long
+  // instruction sequence, and one wave per SIMD runs it in line)
+  struct ItemPos {
+    int gg, ci;
+  };
+  auto next_pos = [&](ItemPos p) {
+    return p.ci + 1 < n_chunk ? ItemPos{p.gg, p.ci + 1} : ItemPos{p.gg + 1, 0};
+  };
+  auto load = [&](ItemPos ip, auto slot) {
     constexpr int sl = decltype(slot)::value;
     auto& rq = rq_[sl];
     auto& ro = ro_[sl];
     auto& r_val = rv_[sl];
-    const int gg = item / n_chunk, c0 = (c_first + item % n_chunk) * kRChunk;
+    const int gg = ip.gg, c0 = (c_first + ip.ci) * kRChunk;
     const size_t hrow = ((size_t)b * a.Hq + h * G + gg) * S;
 #pragma unroll
     for (int i = 0; i < TPT; ++i) {
@@ -509,7 +524,6 @@ __global__ __launch_bounds__(kKThreads) void bwd_dkdv_kernel(BwdArgs a) {
       const int qq = min(c0 + (tid & (kRChunk - 1)), S - 1);
       r_val[0] = a.lse[hrow + qq];
       r_val[1] = a.dvec[hrow + qq];
-      r_val[2] = __int_as_float(tau[qq]);
     }
   };
   auto store = [&](int buf, auto slot) {
@@ -548,7 +562,6 @@ __global__ __launch_bounds__(kKThreads) void bwd_dkdv_kernel(BwdArgs a) {
     if (tid < kRChunk) {
       ((float*)(st + L::kLse))[tid] = r_val[0] * kLog2e;
       ((float*)(st + L::kD))[tid] = r_val[1];
-      ((int*)(st + L::kTau))[tid] = __float_as_int(r_val[2]);
     }
   };
 
@@ -561,21 +574,22 @@ __global__ __launch_bounds__(kKThreads) void bwd_dkdv_kernel(BwdArgs a) {
   // into temporaries plus copies that waited for them at once, which exposed
   // the whole load latency on every item.
   using S0 = std::integral_constant<int, 0>;
+  ItemPos cur{0, 0};                                  // item it
+  ItemPos ahead = n_items > 1 ? next_pos(cur) : cur;  // item min(it + 1, n_items - 1)
   if (n_items > 0) {
-    load(0, S0{});
+    load(cur, S0{});
     store(0, S0{});
-    load(min(1, n_items - 1), S0{});
+    load(ahead, S0{});
     __syncthreads();
   }
   for (int it = 0; it < n_items; ++it) {
     const int buf = it & 1;
-    const int c0 = (c_first + it % n_chunk) * kRChunk;
+    const int c0 = (c_first + cur.ci) * kRChunk;
     const unsigned char* st = stage[buf];
     const uint16_t* ql = (const uint16_t*)(st + L::kQ) + li * L::RS + 8 * hh;
     const uint16_t* ol = (const uint16_t*)(st + L::kO) + li * L::RS + 8 * hh;
     const float* r_lse = (const float*)(st + L::kLse);
     const float* r_d = (const float*)(st + L::kD);
-    const int* r_tau = (const int*)(st + L::kTau);
 
     // S = Q K^T and dP = dO V^T (32 rows x 32 keys): lane owns its key
     f32x16 sacc = f32x16{}, pacc = f32x16{};
@@ -592,13 +606,10 @@ __global__ __launch_bounds__(kKThreads) void bwd_dkdv_kernel(BwdArgs a) {
       const int i0 = 8 * j + 4 * hh;
       const f32x4 lse4 = *(const f32x4*)(r_lse + i0);
       const f32x4 d4 = *(const f32x4*)(r_d + i0);
-      const int4 tau4 = *(const int4*)(r_tau + i0);
-      const int tq[4] = {tau4.x, tau4.y, tau4.z, tau4.w};
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int e = 4 * j + r;
-        const int qq = c0 + i0 + r;
-        const bool kp = (qq < S) & kept(qq, t, rk_m, tq[r], s, w);
+        const bool kp = (unsigned)(c0 + i0 + r - t_m) <= span;
         const float ex = exp2_fast(fmaf(sacc[e], a.scale_log2, -lse4[r]));
         const float p = kp ? ex : 0.0f;
         pv[e] = p;
@@ -623,7 +634,9 @@ __global__ __launch_bounds__(kKThreads) void bwd_dkdv_kernel(BwdArgs a) {
       }
     }
     if (it + 1 < n_items) store(buf ^ 1, S0{});       // item it+1 into the other buffer
-    load(min(it + 2, n_items - 1), S0{});             // item it+2 into the freed registers
+    if (it + 2 < n_items) ahead = next_pos(ahead);    // item min(it + 2, n_items - 1)
+    load(ahead, S0{});                                // into the freed registers
+    cur = next_pos(cur);
     __syncthreads();
   }
 
