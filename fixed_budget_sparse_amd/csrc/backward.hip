@@ -64,10 +64,6 @@ __device__ __forceinline__ int perm_col(int j) {
   return 16 * (j >> 4) + 8 * ((j >> 2) & 1) + 4 * ((j >> 3) & 1) + (j & 3);
 }
 
-// Keep test of the sparse mask for row q and key t (rank rk), tau_q = tq.
-__device__ __forceinline__ bool kept(int q, int t, int rk, int tq, int s, int w) {
-  return (t >= 0) & (t <= q) & ((t < s) | (q - t < w) | (rk <= tq));
-}
 
 // ---------------------------------------------------------------- D_i
 template <int D, bool kF32Out>
@@ -219,7 +215,7 @@ __global__ __launch_bounds__(kQThreads, 1) void bwd_dq_kernel(BwdArgs a) {
   const int b = blockIdx.x / (a.ntiles * a.Hkv);
   const int S = a.S, s = a.s, w = a.w, m = a.m, G = a.G;
   const size_t seg = (size_t)b * a.Hkv + h;
-  const int* rank = a.rank + seg * S;
+  const int* qend = a.qend + seg * S;
   const int* tau = a.tau + seg * S;
   const int q0 = tile * m;
   const int q_hi = min(q0 + m - 1, S - 1);
@@ -230,7 +226,6 @@ __global__ __launch_bounds__(kQThreads, 1) void bwd_dq_kernel(BwdArgs a) {
   const bool row_ok = g < G && q < S;
   const int hq = h * G + (g < G ? g : 0);
   const size_t qrow = ((size_t)b * a.Hq + hq) * S + (row_ok ? q : 0);
-  const int tau_q = row_ok ? tau[q] : -1;
   const float lse2 = row_ok ? a.lse[qrow] * kLog2e : 0.0f;
   const float drow = row_ok ? a.dvec[qrow] : 0.0f;
 
@@ -273,28 +268,23 @@ __global__ __launch_bounds__(kQThreads, 1) void bwd_dq_kernel(BwdArgs a) {
 
   const size_t kvbase = seg * (size_t)S * D;
   for (int c0 = 0; c0 < nk; c0 += kQChunk) {
-    // descriptors (token, rank of the chunk's keys; -1: padding)
+    // descriptors: token and span q_end(t) - t of the chunk's keys (token
+    // -1 and span 0 for padding).  Row q keeps key t iff t <= q <= q_end(t)
+    // (tau never increases with q, so the rows that keep a key are one
+    // interval), one unsigned compare per score; a padding key fails it
+    // (q + 1 > 0).
     if (tid < kQChunk) {
       const int j = c0 + tid;
-      int t = -1, r = 0;
+      int t = -1;
       if (j < n_sink) {
         t = j;
-        r = -1;
       } else if (j < n_sink + n_long) {
-        if (listed) {
-          const int2 e = lst[j - n_sink];
-          t = e.x;
-          r = e.y;
-        } else {
-          t = s + (j - n_sink);
-          r = rank[t];
-        }
+        t = listed ? lst[j - n_sink].x : s + (j - n_sink);
       } else if (j < nk) {
         t = band_lo + (j - n_sink - n_long);
-        r = rank[t];
       }
       kd_t[tid] = t;
-      kd_r[tid] = r;
+      kd_r[tid] = t >= 0 ? qend[t] - t : 0;
     }
     __syncthreads();
     // gather K, V rows: row-major K and V, transposed K with permuted columns.
@@ -355,7 +345,7 @@ __global__ __launch_bounds__(kQThreads, 1) void bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int e = 4 * jj + r;
-          const bool kp = row_ok & kept(q, tv[r], rv[r], tau_q, s, w);
+          const bool kp = row_ok & ((unsigned)(q - tv[r]) <= (unsigned)rv[r]);
           const float ex = exp2_fast(fmaf(sacc[blk][e], a.scale_log2, -lse2));
           const float p = kp ? ex : 0.0f;
           dsv[blk][e] = p * (pacc[blk][e] - drow);
