@@ -31,13 +31,13 @@
 //    consecutive 64-key groups of the plan share every staged chunk; K and V
 //    operands in registers) the rows stream in 32-row chunks aligned to
 //    multiples of 32 (so every key's sums are formed in the same order
-//    whatever its tile),
-//    double-buffered in LDS, with the loads of the chunk after next in flight
-//    during the math (two register stages), workgroups mapped so that each
+//    whatever its tile), in three LDS stages, with the loads of the chunk
+//    after next in flight during the math, workgroups mapped so that each
 //    XCD works through whole (sequence, KV head)s in plan order:
 //    S = Q K^T and dP = dO V^T on MFMA, then dV^T += dO^T P and
 //    dK^T += Q^T dS with Q and dO staged transposed (permuted columns, one
-//    32-bit word per dim for each pair of rows).
+//    32-bit word per dim for each pair of rows); the dV and dK products of a
+//    chunk run during the next chunk's P and dS math.
 //  * bf16 inputs, float32 accumulation, P and dS rounded to bf16 as MFMA
 //    operands; dQ, dK, dV are written in float32.
 #include <type_traits>
@@ -402,7 +402,7 @@ __global__ __launch_bounds__(kKThreads) void bwd_dkdv_kernel(BwdArgs a) {
   constexpr int NTASK = (kRChunk / 2) * PPR;         // (row pair, piece) per tensor
   constexpr int TPT = (NTASK + kKThreads - 1) / kKThreads;   // tasks per thread
   constexpr bool kPartial = NTASK % kKThreads != 0;           // some threads idle (D = 64)
-  __shared__ __attribute__((aligned(16))) unsigned char stage[2][L::kStage];
+  __shared__ __attribute__((aligned(16))) unsigned char stage[3][L::kStage];
   __shared__ int s_lo[kKWaves], s_hi[kKWaves];
 
   const int tid = threadIdx.x, lane = lane_id(), wave = wave_id();
@@ -555,15 +555,30 @@ __global__ __launch_bounds__(kKThreads) void bwd_dkdv_kernel(BwdArgs a) {
     }
   };
 
-  // Item it is staged in LDS buffer it & 1.  One register stage: after item
-  // it's math, item it+1 (loaded one item earlier) goes from registers to the
-  // other buffer and the loads of item it+2 are issued into the freed
-  // registers, so each item's global loads have a whole item of math to land.
+  // Item it is staged in LDS buffer it % 3, and the dV and dK products of an
+  // item run one iteration late: iteration it runs the S and dP products of
+  // item it beside the store of item it+1 (loaded one iteration earlier) into
+  // the buffer of item it-2, then the probability and dS math of item it
+  // beside the dV and dK products of item it-1 (its P and dS kept in
+  // registers), and issues the loads of item it+2 into the freed registers.
   // The loads are unconditional (past the last item they repeat it): loads
   // into one of two register sets chosen at run time were compiled as loads
   // into temporaries plus copies that waited for them at once, which exposed
   // the whole load latency on every item.
   using S0 = std::integral_constant<int, 0>;
+  auto dkdv = [&](int buf, const bf16x8 (&pp)[2], const bf16x8 (&ps)[2]) {
+    const unsigned char* st = stage[buf];
+#pragma unroll
+    for (int d2 = 0; d2 < D / 32; ++d2) {   // dV^T += dO^T P and dK^T += Q^T dS
+      const uint16_t* otl = (const uint16_t*)(st + L::kOT) + (32 * d2 + li) * L::TS + 8 * hh;
+      const uint16_t* qtl = (const uint16_t*)(st + L::kQT) + (32 * d2 + li) * L::TS + 8 * hh;
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        dvacc[d2] = mfma32x32x16(as_bf16x8(*(const uint4*)(otl + 16 * ks)), pp[ks], dvacc[d2]);
+        dkacc[d2] = mfma32x32x16(as_bf16x8(*(const uint4*)(qtl + 16 * ks)), ps[ks], dkacc[d2]);
+      }
+    }
+  };
   ItemPos cur{0, 0};                                  // item it
   ItemPos ahead = n_items > 1 ? next_pos(cur) : cur;  // item min(it + 1, n_items - 1)
   if (n_items > 0) {
@@ -572,10 +587,12 @@ __global__ __launch_bounds__(kKThreads) void bwd_dkdv_kernel(BwdArgs a) {
     load(ahead, S0{});
     __syncthreads();
   }
-  for (int it = 0; it < n_items; ++it) {
-    const int buf = it & 1;
+  bf16x8 ppA[2], psA[2], ppB[2], psB[2];
+  auto step = [&](int it, const bf16x8 (&pp_prev)[2], const bf16x8 (&ps_prev)[2],
+                  bf16x8 (&pp)[2], bf16x8 (&ps)[2]) {
+    const int b_cur = it % 3, b_prev = (it + 2) % 3, b_st = (it + 1) % 3;
     const int c0 = (c_first + cur.ci) * kRChunk;
-    const unsigned char* st = stage[buf];
+    const unsigned char* st = stage[b_cur];
     const uint16_t* ql = (const uint16_t*)(st + L::kQ) + li * L::RS + 8 * hh;
     const uint16_t* ol = (const uint16_t*)(st + L::kO) + li * L::RS + 8 * hh;
     const float* r_lse = (const float*)(st + L::kLse);
@@ -588,6 +605,12 @@ __global__ __launch_bounds__(kKThreads) void bwd_dkdv_kernel(BwdArgs a) {
       sacc = mfma32x32x16(as_bf16x8(*(const uint4*)(ql + 16 * ks)), kop[ks], sacc);
       pacc = mfma32x32x16(as_bf16x8(*(const uint4*)(ol + 16 * ks)), vop[ks], pacc);
     }
+    // item it+1 into item it-2's buffer (its last reads were the dV and dK
+    // products of the previous iteration)
+    if (it + 1 < n_items) store(b_st, S0{});
+    // dV and dK of item it-1 (none before the first item: its buffer holds no
+    // staged rows yet, and 0 times a stale NaN would not add 0)
+    if (it > 0) dkdv(b_prev, pp_prev, ps_prev);
     // branch-free: the exp of every score, then a select (a masked score's
     // exp may overflow; it is never used); the row values in 4-wide reads
     float pv[16], dsv[16];
@@ -606,28 +629,23 @@ __global__ __launch_bounds__(kKThreads) void bwd_dkdv_kernel(BwdArgs a) {
         dsv[e] = p * (pacc[e] - d4[r]);
       }
     }
-    bf16x8 pp[2], ps[2];
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
       pp[ks] = pack_bf16x8(&pv[8 * ks]);
       ps[ks] = pack_bf16x8(&dsv[8 * ks]);
     }
-    // dV^T += dO^T P and dK^T += Q^T dS
-#pragma unroll
-    for (int d2 = 0; d2 < D / 32; ++d2) {
-      const uint16_t* otl = (const uint16_t*)(st + L::kOT) + (32 * d2 + li) * L::TS + 8 * hh;
-      const uint16_t* qtl = (const uint16_t*)(st + L::kQT) + (32 * d2 + li) * L::TS + 8 * hh;
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        dvacc[d2] = mfma32x32x16(as_bf16x8(*(const uint4*)(otl + 16 * ks)), pp[ks], dvacc[d2]);
-        dkacc[d2] = mfma32x32x16(as_bf16x8(*(const uint4*)(qtl + 16 * ks)), ps[ks], dkacc[d2]);
-      }
-    }
-    if (it + 1 < n_items) store(buf ^ 1, S0{});       // item it+1 into the other buffer
     if (it + 2 < n_items) ahead = next_pos(ahead);    // item min(it + 2, n_items - 1)
     load(ahead, S0{});                                // into the freed registers
     cur = next_pos(cur);
     __syncthreads();
+  };
+  for (int it = 0; it < n_items; it += 2) {   // by two: the P / dS sets swap roles
+    step(it, ppB, psB, ppA, psA);
+    if (it + 1 < n_items) step(it + 1, ppA, psA, ppB, psB);
+  }
+  if (n_items > 0) {   // dV and dK of the last item
+    if ((n_items - 1) & 1) dkdv((n_items - 1) % 3, ppB, psB);
+    else dkdv((n_items - 1) % 3, ppA, psA);
   }
 
   if (t >= 0) {
