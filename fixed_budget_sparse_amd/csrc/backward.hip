@@ -585,9 +585,14 @@ __global__ __launch_bounds__(kKThreads) void bwd_dkdv_kernel(BwdArgs a) {
     load(cur, S0{});
     store(0, S0{});
     load(ahead, S0{});
+    {   // the first iteration's dV and dK products read buffer 2's transposed
+        // tiles with zero P and dS: zero them (0 times a stale NaN is not 0)
+      uint4* z = (uint4*)(stage[2] + L::kQT);
+      for (int i = tid; i < (L::kLse - L::kQT) / 16; i += kKThreads) z[i] = make_uint4(0, 0, 0, 0);
+    }
     __syncthreads();
   }
-  bf16x8 ppA[2], psA[2], ppB[2], psB[2];
+  bf16x8 ppA[2] = {}, psA[2] = {}, ppB[2] = {}, psB[2] = {};
   auto step = [&](int it, const bf16x8 (&pp_prev)[2], const bf16x8 (&ps_prev)[2],
                   bf16x8 (&pp)[2], bf16x8 (&ps)[2]) {
     const int b_cur = it % 3, b_prev = (it + 2) % 3, b_st = (it + 1) % 3;
@@ -608,9 +613,9 @@ __global__ __launch_bounds__(kKThreads) void bwd_dkdv_kernel(BwdArgs a) {
     // item it+1 into item it-2's buffer (its last reads were the dV and dK
     // products of the previous iteration)
     if (it + 1 < n_items) store(b_st, S0{});
-    // dV and dK of item it-1 (none before the first item: its buffer holds no
-    // staged rows yet, and 0 times a stale NaN would not add 0)
-    if (it > 0) dkdv(b_prev, pp_prev, ps_prev);
+    // dV and dK of item it-1 (in the first iteration zero operands on the
+    // zeroed transposed tiles of buffer 2, which add exactly 0)
+    dkdv(b_prev, pp_prev, ps_prev);
     // branch-free: the exp of every score, then a select (a masked score's
     // exp may overflow; it is never used); the row values in 4-wide reads
     float pv[16], dsv[16];
