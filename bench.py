@@ -599,10 +599,16 @@ def bench_decode(kv, torch, np, dev, n_timed):
     us_step = ms * 1e3 / n_timed
     nbytes = decode_bytes_per_step(nseq, Hq, Hkv, D, Bc)
     gbps = nbytes / (us_step * 1e-6) / 1e9
+    traffic = measured_traffic("decode_attend", wl.name)
     return {"workload": wl.name, "steps_timed": n_timed, "positions": [p_start, p_end - 1],
             "us_per_step": round(us_step, 2), "wall_us_per_step": round(wall * 1e6 / n_timed, 2),
             "bytes_per_step": nbytes, "GB/s": round(gbps, 1),
             "frac_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4),
+            # DRAM bytes per step from the committed counter summary (None once
+            # the kernel's sources change): the algorithmic bytes plus the slot
+            # metadata the step reads
+            "traffic": traffic,
+            "traffic_GB/s": round(traffic / (us_step * 1e-6) / 1e9, 1) if traffic else None,
             "tokens_per_s": round(nseq / (us_step * 1e-6), 1),
             "handoff": {"prompt_tokens": p_start,
                         "thresholds_ms": round(ho_avg["thresholds"], 4),
