@@ -185,10 +185,31 @@ def bench_layer_c3(kv, torch, dev, ev, reps=5):
         t["fwd"].append(e[1].elapsed_time(e[2]))
         t["target"].append(e[2].elapsed_time(e[3]))
         t["end_to_end"].append(e[0].elapsed_time(e[3]))
+    # end to end with the target on a second stream beside thresholds +
+    # forward, as in the step of the 16k layer
+    main_stream = torch.cuda.current_stream(dev)
+    side = torch.cuda.Stream(dev)
+    t["overlapped"] = []
+    for _ in range(reps):
+        e0, e1, done = ev(), ev(), ev()
+        e0.record(main_stream)
+        side.wait_event(e0)
+        with torch.cuda.stream(side):
+            kv.future_target(q, kk, lse_t, w, target=tgt)
+            done.record(side)
+        kv.thresholds(prio, s, w, k, rank=rank, tau=tau)
+        kv.masked_attn_fwd(q, kk, v, rank, tau, s, w, k, out_dtype=bf, o=o, lse=lse)
+        main_stream.wait_event(done)
+        e1.record(main_stream)
+        torch.cuda.synchronize()
+        t["overlapped"].append(e0.elapsed_time(e1))
     med = {n: sorted(v_)[len(v_) // 2] for n, v_ in t.items()}
     f_fwd = 4 * D * Hq * fwd_pairs(S, s + w + k)
     f_tgt = 2 * D * Hq * tgt_pairs(S, w)
     return {"workload": wl.name, "reps": reps, "thresholds_us": round(med["thresholds"] * 1e3, 1),
+            "end_to_end_overlapped_ms": round(med["overlapped"], 4),
+            "end_to_end_overlapped_tflops":
+                round((f_fwd + f_tgt) / (med["overlapped"] * 1e-3) / 1e12, 2),
             "fwd_ms": round(med["fwd"], 4),
             "fwd_tflops": round(f_fwd / (med["fwd"] * 1e-3) / 1e12, 2),
             "target_ms": round(med["target"], 4),
