@@ -18,6 +18,8 @@
 //    waves, double-buffered: the global loads of chunk c+1 are issued before
 //    the math of chunk c and stored to the other buffer after it, so one
 //    barrier per chunk suffices and the load latency hides behind the MFMAs.
+//    Their LSE biases take three slots, since the exps of a chunk's last
+//    column block run in the next iteration.
 //  * X^T = Q K^T leaves every lane owning one row t; each score becomes
 //    exp2(x * scale log2 e - LSE_d log2 e) and is summed directly: with the
 //    dense LSE every exponent is <= 0, so no running maximum is needed.
@@ -63,7 +65,11 @@ template <int D, bool kF32In>
 __global__ __launch_bounds__(kThreads, 2) void future_target_kernel(TgtArgs a) {
   using Gm = TgtGeom<D, kF32In>;
   __shared__ __attribute__((aligned(16))) unsigned char q_lds[2][Gm::bufBytes];
-  __shared__ __attribute__((aligned(16))) float nlse[2][kChunk];   // -LSE_d * log2(e)
+  // -LSE_d * log2(e) of a chunk's queries, in three slots: a wave still
+  // reading the previous chunk's biases (the exps of its last block run in
+  // the next iteration) must not see them overwritten by the store of the
+  // chunk after next, which other waves may reach first
+  __shared__ __attribute__((aligned(16))) float nlse[3][kChunk];
 
   const int tid = threadIdx.x, lane = lane_id(), wave = wave_id();
   const int hh = lane >> 5, li = lane & 31;
@@ -140,7 +146,7 @@ __global__ __launch_bounds__(kThreads, 2) void future_target_kernel(TgtArgs a) {
     // above; it is scaled when stored
     if (tid < kChunk) stage_lse = lse[min(d0 + tid, S - 1)];
   };
-  auto store_chunk = [&](int buf, int d0) {
+  auto store_chunk = [&](int buf, int nsl, int d0) {
 #pragma unroll
     for (int i = 0; i < Gm::NPIECE; ++i) {
       const int p = tid + i * kThreads;
@@ -155,7 +161,7 @@ __global__ __launch_bounds__(kThreads, 2) void future_target_kernel(TgtArgs a) {
         *(u32x4v*)((uint16_t*)q_lds[buf] + row * Gm::QS + piece * 8) = stage[i];
       }
     }
-    if (tid < kChunk) nlse[buf][tid] = d0 + tid < S ? -stage_lse * kLog2e : kNegInf;
+    if (tid < kChunk) nlse[nsl][tid] = d0 + tid < S ? -stage_lse * kLog2e : kNegInf;
   };
 
   // four partial sums per row block (by column mod 4), so consecutive adds
@@ -167,7 +173,7 @@ __global__ __launch_bounds__(kThreads, 2) void future_target_kernel(TgtArgs a) {
     for (int r = 0; r < 4; ++r) sum[rb][r] = 0.0f;
   const int nchunks = (S - d_start + kChunk - 1) / kChunk;
   load_chunk(d_start);
-  store_chunk(0, d_start);
+  store_chunk(0, 0, d_start);
   __syncthreads();
 
   // One 32-column block of MFMAs: acc[rb] = Q_block K_rb^T.
@@ -194,11 +200,11 @@ __global__ __launch_bounds__(kThreads, 2) void future_target_kernel(TgtArgs a) {
   };
   // exp2 and row sums of one block: the lane holds columns
   // d = d0 + 32cb + 8j + 4hh + r of rows rbase + 32rb + li
-  auto exp_block = [&](const f32x16 (&acc)[kRB], int buf, int cb, int d0, auto masked) {
+  auto exp_block = [&](const f32x16 (&acc)[kRB], int slot, int cb, int d0, auto masked) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int dl = 32 * cb + 8 * j + 4 * hh;
-      const f32x4 bias = *(const f32x4*)(&nlse[buf][dl]);
+      const f32x4 bias = *(const f32x4*)(&nlse[slot][dl]);
 #pragma unroll
       for (int r = 0; r < 4; ++r)
 #pragma unroll
@@ -217,13 +223,13 @@ __global__ __launch_bounds__(kThreads, 2) void future_target_kernel(TgtArgs a) {
   // together: all operand reads first, then 8 groups of two MFMAs and four
   // scores (fma, exp2, add) each, pinned with scheduling barriers.
   auto fused = [&](auto doM, auto doE, auto maskE, f32x16 (&accM)[kRB], int mbuf, int mcb,
-                   const f32x16 (&accE)[kRB], int ebuf, int ecb, int d0E) {
+                   const f32x16 (&accE)[kRB], int eslot, int ecb, int d0E) {
     constexpr bool kM = decltype(doM)::value, kE = decltype(doE)::value;
     constexpr bool kMask = decltype(maskE)::value;
     constexpr int NK = Gm::NKS;              // 8 (D = 128, bf16)
     constexpr int kPer = 32 / NK;            // scores per group: 4, all with one bias vector
     const uint16_t* ql = (const uint16_t*)q_lds[mbuf] + (32 * mcb + li) * Gm::QS + 8 * hh;
-    const float* nb = &nlse[ebuf][32 * ecb + 4 * hh];
+    const float* nb = &nlse[eslot][32 * ecb + 4 * hh];
     // operands two k-steps ahead, bias one group ahead; each group reads its
     // bias before its operand, so the next group waits only for the bias and
     // the operand read stays in flight
@@ -274,7 +280,8 @@ __global__ __launch_bounds__(kThreads, 2) void future_target_kernel(TgtArgs a) {
   // block 1 of chunk c run, the exps of block 0 of chunk c are computed.
   f32x16 accA[kRB], accB[kRB];
   bool pend = false, pend_mask = false;   // block 1 of the previous chunk awaits its exps
-  int pend_d0 = 0, pend_buf = 0;
+  int pend_d0 = 0, pend_nsl = 0;
+  int nsl = 0;                            // bias slot of chunk c (c mod 3)
   for (int c = 0; c < nchunks; ++c) {
     const int d0 = d_start + c * kChunk;
     const int buf = c & 1;
@@ -288,44 +295,45 @@ __global__ __launch_bounds__(kThreads, 2) void future_target_kernel(TgtArgs a) {
       // block 0 of chunk c (MFMA) with block 1 of chunk c-1 (exp), then
       // block 1 of chunk c (MFMA) with block 0 of chunk c (exp)
       if (active && pend) {
-        if (pend_mask) fused(T_{}, T_{}, T_{}, accA, buf, 0, accB, pend_buf, 1, pend_d0);
-        else fused(T_{}, T_{}, F_{}, accA, buf, 0, accB, pend_buf, 1, pend_d0);
+        if (pend_mask) fused(T_{}, T_{}, T_{}, accA, buf, 0, accB, pend_nsl, 1, pend_d0);
+        else fused(T_{}, T_{}, F_{}, accA, buf, 0, accB, pend_nsl, 1, pend_d0);
       } else if (active) {
-        fused(T_{}, F_{}, F_{}, accA, buf, 0, accB, pend_buf, 1, pend_d0);
+        fused(T_{}, F_{}, F_{}, accA, buf, 0, accB, pend_nsl, 1, pend_d0);
       } else if (pend) {
-        if (pend_mask) fused(F_{}, T_{}, T_{}, accA, buf, 0, accB, pend_buf, 1, pend_d0);
-        else fused(F_{}, T_{}, F_{}, accA, buf, 0, accB, pend_buf, 1, pend_d0);
+        if (pend_mask) fused(F_{}, T_{}, T_{}, accA, buf, 0, accB, pend_nsl, 1, pend_d0);
+        else fused(F_{}, T_{}, F_{}, accA, buf, 0, accB, pend_nsl, 1, pend_d0);
       }
       if (active) {
-        if (msk) fused(T_{}, T_{}, T_{}, accB, buf, 1, accA, buf, 0, d0);
-        else fused(T_{}, T_{}, F_{}, accB, buf, 1, accA, buf, 0, d0);
+        if (msk) fused(T_{}, T_{}, T_{}, accB, buf, 1, accA, nsl, 0, d0);
+        else fused(T_{}, T_{}, F_{}, accB, buf, 1, accA, nsl, 0, d0);
       }
     } else {
       if (active) mfma_block(accA, buf, 0);
       if (pend) {
-        if (pend_mask) exp_block(accB, pend_buf, 1, pend_d0, std::true_type{});
-        else exp_block(accB, pend_buf, 1, pend_d0, std::false_type{});
+        if (pend_mask) exp_block(accB, pend_nsl, 1, pend_d0, std::true_type{});
+        else exp_block(accB, pend_nsl, 1, pend_d0, std::false_type{});
       }
       if (active) {
         mfma_block(accB, buf, 1);
-        if (msk) exp_block(accA, buf, 0, d0, std::true_type{});
-        else exp_block(accA, buf, 0, d0, std::false_type{});
+        if (msk) exp_block(accA, nsl, 0, d0, std::true_type{});
+        else exp_block(accA, nsl, 0, d0, std::false_type{});
       }
     }
     pend = active;
     pend_mask = msk;
     pend_d0 = d0;
-    pend_buf = buf;
-    if (has_next) store_chunk(buf ^ 1, d0 + kChunk);
+    pend_nsl = nsl;
+    nsl = nsl == 2 ? 0 : nsl + 1;
+    if (has_next) store_chunk(buf ^ 1, nsl, d0 + kChunk);
     __syncthreads();
   }
   if (pend) {
     if constexpr (!kF32In && kRB == 2 && D == 128) {
-      if (pend_mask) fused(F_{}, T_{}, T_{}, accA, 0, 0, accB, pend_buf, 1, pend_d0);
-      else fused(F_{}, T_{}, F_{}, accA, 0, 0, accB, pend_buf, 1, pend_d0);
+      if (pend_mask) fused(F_{}, T_{}, T_{}, accA, 0, 0, accB, pend_nsl, 1, pend_d0);
+      else fused(F_{}, T_{}, F_{}, accA, 0, 0, accB, pend_nsl, 1, pend_d0);
     } else {
-      if (pend_mask) exp_block(accB, pend_buf, 1, pend_d0, std::true_type{});
-      else exp_block(accB, pend_buf, 1, pend_d0, std::false_type{});
+      if (pend_mask) exp_block(accB, pend_nsl, 1, pend_d0, std::true_type{});
+      else exp_block(accB, pend_nsl, 1, pend_d0, std::false_type{});
     }
   }
 

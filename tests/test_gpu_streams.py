@@ -6,7 +6,9 @@ first (the bench does).  The library keeps no state between calls and every
 scratch buffer is the caller's, so concurrent calls on distinct buffers must
 not interfere: every output of the overlapped calls must equal, bit for bit,
 the output of the same calls run one after another (the kernels are
-deterministic), over several overlapped repetitions."""
+deterministic), over several overlapped repetitions.  (This test found a race in
+the target kernel: a chunk's LSE biases overwritten while a slower wave still
+read them, which only shows when other kernels share the chip.)"""
 import pytest
 import torch
 
@@ -16,10 +18,14 @@ from gpu_util import announce, device
 pytestmark = pytest.mark.gpu
 
 
-def test_target_beside_thresholds_and_forward():
-    announce("two streams: future target beside thresholds + forward, S=4096, 32/8 heads")
+@pytest.mark.parametrize("S", [4096, 16384])
+def test_target_beside_thresholds_and_forward(S):
+    """S = 16384 is the 16k layer the bench times, in its launch configuration
+    (its outputs in order are checked against the oracle on sampled rows by
+    the full-size tests)."""
+    announce(f"two streams: future target beside thresholds + forward, S={S}, 32/8 heads")
     dev = device()
-    b, hq, hkv, S, D, s, w, k = 1, 32, 8, 4096, 128, 16, 512, 1520
+    b, hq, hkv, D, s, w, k = 1, 32, 8, 128, 16, 512, 1520
     bf = torch.bfloat16
     g = torch.Generator(device=dev)
     g.manual_seed(2024)
@@ -45,7 +51,7 @@ def test_target_beside_thresholds_and_forward():
     o = torch.empty_like(o0)
     lse = torch.empty_like(lse0)
     tgt = torch.empty_like(tgt0)
-    for rep in range(3):
+    for rep in range(4):
         for t in (rank, tau, o, lse, tgt):
             t.zero_()
         start = torch.cuda.Event()
