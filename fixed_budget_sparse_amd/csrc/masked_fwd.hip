@@ -594,6 +594,9 @@ __global__ __launch_bounds__(kThreads, 1) void masked_fwd_kernel(FwdArgs a) {
       const float mb = softmax_pre(sA, 0, [] {});
 #pragma unroll
       for (int p = 0; p < NP; ++p) pkB[p] = POp{};
+      // the region stores K(2) over K(0): every wave's qk(0) must have read
+      // it (later iterations overwrite a buffer read before the last barrier)
+      __syncthreads();
       float ps;
       region(1, sB, sA, mb, pkB, pkA, 1, ps, 0, 0);
       l_run += ps;
