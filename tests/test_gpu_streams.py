@@ -69,3 +69,81 @@ def test_target_beside_thresholds_and_forward(S):
         assert torch.equal(o.view(torch.int16), o0.view(torch.int16)), rep
         assert torch.equal(lse.view(torch.int32), lse0.view(torch.int32)), rep
         assert torch.equal(tgt.view(torch.int32), tgt0.view(torch.int32)), rep
+
+
+def _load_on(stream, a, b, n=12):
+    """Queue n large bf16 products on `stream` (a load that shares the chip)."""
+    with torch.cuda.stream(stream):
+        for _ in range(n):
+            torch.matmul(a, b)
+
+
+def _same(x, y):
+    if x.dtype in (torch.bfloat16, torch.float16):
+        return torch.equal(x.view(torch.int16), y.view(torch.int16))
+    if x.dtype == torch.float32:
+        return torch.equal(x.view(torch.int32), y.view(torch.int32))
+    return torch.equal(x, y)
+
+
+def test_every_call_beside_a_load():
+    """Each call of the library, run while another stream keeps the chip busy
+    (so its waves progress out of step, as they do beside other kernels),
+    returns exactly what it returns alone: a race between the waves of a
+    workgroup over LDS or workspace would show as a difference here."""
+    announce("every call beside a matmul load on a second stream")
+    dev = device()
+    bf = torch.bfloat16
+    g = torch.Generator(device=dev)
+    g.manual_seed(99)
+    b, hq, hkv, S, D, s, w, k = 1, 16, 4, 4096, 128, 8, 256, 700
+    q = torch.randn((b, hq, S, D), generator=g, device=dev).to(bf)
+    kk = torch.randn((b, hkv, S, D), generator=g, device=dev).to(bf)
+    v = torch.randn((b, hkv, S, D), generator=g, device=dev).to(bf)
+    prio = torch.randn((b, hkv, S), generator=g, device=dev)
+    dout = torch.randn((b, hq, S, D), generator=g, device=dev).to(bf)
+    lg = -0.01 * torch.rand((hkv,), generator=g, device=dev)
+    nseq = 8
+    kv_prompt = torch.randn((nseq, hkv, 2048, D), generator=g, device=dev).to(bf)
+    vv_prompt = torch.randn((nseq, hkv, 2048, D), generator=g, device=dev).to(bf)
+    pr_prompt = torch.randn((nseq, hkv, 2048), generator=g, device=dev)
+    qd = torch.randn((nseq, hq, D), generator=g, device=dev).to(bf)
+    kn = torch.randn((nseq, hkv, D), generator=g, device=dev).to(bf)
+    vn = torch.randn((nseq, hkv, D), generator=g, device=dev).to(bf)
+    pl = torch.randn((nseq, hkv), generator=g, device=dev)
+    pos = torch.full((nseq,), 2048, dtype=torch.int32, device=dev)
+    ma = torch.randn((4096, 4096), generator=g, device=dev).to(bf)
+    mb = torch.randn((4096, 4096), generator=g, device=dev).to(bf)
+
+    def run_all():
+        out = {}
+        rank, tau = kv.thresholds(prio, s, w, k)
+        out["rank"], out["tau"] = rank, tau
+        o, lse = kv.masked_attn_fwd(q, kk, v, rank, tau, s, w, k, out_dtype=bf)
+        out["o"], out["lse"] = o, lse
+        out["tgt"] = kv.future_target(q, kk, lse, w)
+        out["score"] = kv.target_score(out["tgt"], hkv, w, 1e-6)
+        out["t_bnd"], out["y"] = kv.boundary_labels(out["score"], lg, 64, s, w, k)
+        out["dq"], out["dk"], out["dv"] = kv.masked_attn_bwd(q, kk, v, o, lse, rank, tau, dout,
+                                                             s, w, k)
+        rp, tp = kv.thresholds(pr_prompt, s, w, k)
+        cache = kv.new_decode_cache(nseq, hkv, D, s, w, k, dtype=bf, device=dev)
+        kv.cache_from_prefill(cache, kv_prompt, vv_prompt, pr_prompt, rp, tp, s, w, k)
+        od, ld = kv.decode_step(cache, pos, qd, kn, vn, pl, s, w, k, out_dtype=bf)
+        out["od"], out["ld"] = od, ld
+        out["cache_pos"], out["cache_k"] = cache.slot_pos, cache.k
+        return out
+
+    ref = run_all()
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream(dev)
+    main = torch.cuda.current_stream(dev)
+    for rep in range(3):
+        start = torch.cuda.Event()
+        start.record(main)
+        side.wait_event(start)
+        _load_on(side, ma, mb)
+        got = run_all()
+        torch.cuda.synchronize()
+        for name, want in ref.items():
+            assert _same(got[name], want), (rep, name)
