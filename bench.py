@@ -333,8 +333,10 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-other-configs", action="store_true",
                     help="skip the S 32768 layer and the S 131072 long-context legs")
-    ap.add_argument("--no-overlap", dest="overlap", action="store_false",
-                    help="run the target pass after the forward on one stream")
+    ap.add_argument("--overlap", choices=("full", "thresholds", "none"), default="full",
+                    help="full: the target on a second stream beside thresholds + forward; "
+                         "thresholds: beside the thresholds only, the forward after it; "
+                         "none: the three in order on one stream")
     ap.add_argument("--no-isolated", dest="isolated", action="store_false",
                     help="skip the forward and target timed alone after the step")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
@@ -422,10 +424,10 @@ def main():
     # priority) beside them, and the step ends when both streams are done.
     # The cutoff kernels fill only a few CUs; the target fills the rest.
     main_stream = torch.cuda.current_stream(dev)
-    tgt_stream = torch.cuda.Stream(dev) if args.overlap else main_stream
+    tgt_stream = torch.cuda.Stream(dev) if args.overlap != "none" else main_stream
 
     def one_step(record):
-        e0, e1, e2, e3, e4, e5 = ev(), ev(), ev(), ev(), ev(), ev()
+        e0, e1, e2, e3, e4, e5, e6 = ev(), ev(), ev(), ev(), ev(), ev(), ev()
         def target():
             with torch.cuda.stream(tgt_stream):
                 e4.record(tgt_stream)
@@ -433,20 +435,23 @@ def main():
                 e5.record(tgt_stream)
 
         e0.record(main_stream)
-        if args.overlap:
+        if args.overlap != "none":
             tgt_stream.wait_event(e0)
             target()
         kv.thresholds(prio, s, w, k, rank=rank, tau=tau)
         e1.record(main_stream)
+        if args.overlap == "thresholds":
+            main_stream.wait_event(e5)   # the forward runs after the target
+        e6.record(main_stream)
         kv.masked_attn_fwd(q, kk, v, rank, tau, s, w, k, out_dtype=bf, o=o, lse=lse)
         e2.record(main_stream)
-        if args.overlap:
+        if args.overlap == "full":
             main_stream.wait_event(e5)
-        else:
+        elif args.overlap == "none":
             target()
         e3.record(main_stream)
         if record is not None:
-            record.append((e0, e1, e2, e3, e4, e5))
+            record.append((e0, e1, e2, e3, e4, e5, e6))
 
     for _ in range(args.warmup):
         one_step(None)
@@ -458,9 +463,9 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     step_ev = []
-    for e0, e1, e2, e3, e4, e5 in recs:
+    for e0, e1, e2, e3, e4, e5, e6 in recs:
         times["thr"].append(e0.elapsed_time(e1))
-        times["fwd"].append(e1.elapsed_time(e2))
+        times["fwd"].append(e6.elapsed_time(e2))
         times["tgt"].append(e4.elapsed_time(e5))
         step_ev.append(e0.elapsed_time(e3))
     ms_step = wall * 1e3 / args.steps
@@ -518,8 +523,11 @@ def main():
         "data": "synthetic",
         "config": {"workload": wl.name, "batch": wl.batch, "n_q_heads": Hq, "n_kv_heads": Hkv,
                    "head_dim": D, "seq_len": S, "sink": s, "window": w, "topk": k, "budget": B,
-                   "step": ("thresholds + masked fwd, future target on a second stream beside them"
-                            if args.overlap else "thresholds + masked fwd + future target"),
+                   "step": {"full": "thresholds + masked fwd, future target on a second "
+                                    "stream beside them",
+                            "thresholds": "future target on a second stream beside the "
+                                          "thresholds, then the masked fwd",
+                            "none": "thresholds + masked fwd + future target"}[args.overlap],
                    "decode_workload": DECODE_B2048.name},
         "frac_mfma_peak": round(value / MFMA_BF16_PEAK_TFLOPS, 4),
         "kernels_ms": {n: round(t, 4) for n, t in avg.items()},
