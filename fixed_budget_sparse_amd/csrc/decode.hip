@@ -407,7 +407,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_attend_kernel(DecArgs a) {
     float mc = x[0];
 #pragma unroll
     for (int e = 1; e < 16; ++e) mc = fmaxf(mc, x[e]);
-    mc = fmaxf(mc, __shfl_xor(mc, 32));
+    mc = halves_max(mc);
     const float m_new = fmaxf(m_run, mc);
     const float m_use = m_new == kNegInf ? 0.0f : m_new;
     const float alpha = exp2_fast(m_run - m_use);
@@ -446,7 +446,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_attend_kernel(DecArgs a) {
   }
 
   // ---- merge the 4 waves in LDS: mg[wave][row][0] = max, [1] = sum, [2..] = O
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  const float l_tot = halves_sum(l_run);
   __syncthreads();                               // staging areas are free now
   float* mg = (float*)lds;
   constexpr int RS = D + 2;

@@ -340,7 +340,7 @@ __global__ __launch_bounds__(kThreads, 2) void future_target_kernel(TgtArgs a) {
 #pragma unroll
   for (int rb = 0; rb < kRB; ++rb) {
     const float part = (sum[rb][0] + sum[rb][1]) + (sum[rb][2] + sum[rb][3]);
-    const float tot = part + __shfl_xor(part, 32);
+    const float tot = halves_sum(part);
     const int t = rbase + 32 * rb + li;
     if (hh == 0 && t < S) out[t] = tot > 0.0f ? log2f(tot) * kLn2 : kNegInf;
   }

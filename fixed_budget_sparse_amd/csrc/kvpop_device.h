@@ -54,6 +54,22 @@ __device__ __forceinline__ int xcd_logical_block(int bid, int n) {
   return (x < r ? x * (q + 1) : r * (q + 1) + (x - r) * q) + j;
 }
 
+// max and sum of a lane's value with that of lane ^ 32: v_permlane32_swap
+// (gfx950) returns, in every lane l, the values of lanes l & 31 and
+// (l & 31) + 32 (checked on the device), so one VALU instruction replaces an
+// LDS permute round trip; both operations commute, so the result is the same
+// in both halves
+__device__ __forceinline__ float halves_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float halves_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // ---------------------------------------------------------------- numbers
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 

@@ -406,7 +406,7 @@ __global__ __launch_bounds__(kThreads, 1) void masked_fwd_kernel(FwdArgs a) {
     for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
       for (int e = 0; e < 16; ++e) mc = fmaxf(mc, sc[blk][e]);
-    mc = fmaxf(mc, __shfl_xor(mc, 32));
+    mc = halves_max(mc);
     // lazily moved reference max (m_run, raw units): it moves only when some
     // row's max grows by more than 2^8 in the exp2 domain, so the O rescale is
     // skipped on most chunks; probabilities stay <= 2^8
@@ -650,7 +650,7 @@ __global__ __launch_bounds__(kThreads, 1) void masked_fwd_kernel(FwdArgs a) {
   }
 
   // ---- epilogue: O = acc / l, LSE = (m + log2 l) ln 2
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  const float l_tot = halves_sum(l_run);
   if (row_ok) {
     const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
     const size_t orow = (((size_t)b * a.Hq + hq) * S + q) * D;
