@@ -206,7 +206,7 @@ __global__ __launch_bounds__(kQThreads, 1) void bwd_dq_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t v_lds[kQChunk * L::RS];
   __shared__ __attribute__((aligned(16))) uint16_t kt_lds[D * L::TS];
   __shared__ __attribute__((aligned(16))) int kd_t[kQChunk];
-  __shared__ __attribute__((aligned(16))) int kd_r[kQChunk];
+  __shared__ __attribute__((aligned(16))) int kd_span[kQChunk];   // q_end(t) - t
 
   const int tid = threadIdx.x, lane = lane_id(), wave = wave_id();
   const int hh = lane >> 5, li = lane & 31;
@@ -284,7 +284,7 @@ __global__ __launch_bounds__(kQThreads, 1) void bwd_dq_kernel(BwdArgs a) {
         t = band_lo + (j - n_sink - n_long);
       }
       kd_t[tid] = t;
-      kd_r[tid] = t >= 0 ? qend[t] - t : 0;
+      kd_span[tid] = t >= 0 ? qend[t] - t : 0;
     }
     __syncthreads();
     // gather K, V rows: row-major K and V, transposed K with permuted columns.
@@ -340,7 +340,7 @@ __global__ __launch_bounds__(kQThreads, 1) void bwd_dq_kernel(BwdArgs a) {
       for (int jj = 0; jj < 4; ++jj) {
         const int j0 = 32 * blk + 8 * jj + 4 * hh;
         const int4 t4 = *(const int4*)(kd_t + j0);
-        const int4 r4 = *(const int4*)(kd_r + j0);
+        const int4 r4 = *(const int4*)(kd_span + j0);
         const int tv[4] = {t4.x, t4.y, t4.z, t4.w}, rv[4] = {r4.x, r4.y, r4.z, r4.w};
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
