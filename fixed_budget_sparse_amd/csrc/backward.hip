@@ -23,7 +23,7 @@
 //  * dK, dV, key-major (bwd_dkdv_kernel): key t is kept by the contiguous rows
 //    [t, q_end(t)] (tau never increases with q), so a tile of keys needs the
 //    rows [min t, max q_end], and the mask of a (row, key) pair is the
-//    interval test t <= q <= q_end(t).  bwd_qend_kernel finds q_end(t) by
+//    interval test t <= q <= q_end(t).  The forward plan finds q_end(t) by
 //    binary search on tau; bwd_key_order_kernel groups keys into 64-key tiles: keys that
 //    live at most w + 64 rows in token order, the others by q_end (a counting
 //    sort over 64-row buckets), which keeps the rows a tile visits close to
@@ -104,39 +104,6 @@ __global__ __launch_bounds__(256) void bwd_dot_kernel(const uint16_t* __restrict
 #pragma unroll
   for (int off = LPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
   if (part == 0 && row < rows) dvec[row] = acc;
-}
-
-// ---------------------------------------------------------------- key plan
-// q_end(t): the last row keeping key t.  Sinks live to the end; the window
-// keeps rows t .. t + w - 1; after that row q keeps t iff rank(t) <= tau_q,
-// and tau never increases with q, so the rows are a prefix found by bisection.
-__global__ __launch_bounds__(256) void bwd_qend_kernel(const int* __restrict__ rank,
-                                                       const int* __restrict__ tau,
-                                                       int* __restrict__ qend, int S, int s, int w,
-                                                       long long total) {
-  const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
-  if (i >= total) return;
-  const long long seg = i / S;
-  const int t = (int)(i - seg * S);
-  const int* tq = tau + seg * S;
-  int e;
-  if (t < s || t + w > S - 1) {
-    e = S - 1;                          // a sink, or the window reaches the end
-  } else {
-    const int r = rank[i];
-    int lo = t + w, hi = S - 1;
-    if (tq[lo] < r) {
-      e = t + w - 1;
-    } else {
-      while (lo < hi) {                 // invariant: tq[lo] >= r
-        const int mid = lo + (hi - lo + 1) / 2;
-        if (tq[mid] >= r) lo = mid;
-        else hi = mid - 1;
-      }
-      e = lo;
-    }
-  }
-  qend[i] = e;
 }
 
 // Key order of the dK/dV tiles, one workgroup per (sequence, KV head):
@@ -691,7 +658,7 @@ void launch_bwd_kernels(const Dims& d, BwdArgs a, const void* o, hipStream_t st)
 
 size_t bwd_ws_bytes(const Dims& d) {
   const size_t rows = (size_t)d.b * d.Hq * d.S, keys = (size_t)d.nseg() * d.S;
-  return fwd_ws_bytes(d) + align256(rows * 4) + 2 * align256(keys * 4);
+  return fwd_ws_bytes(d) + align256(rows * 4) + align256(keys * 4);
 }
 
 hipError_t launch_masked_bwd(const Dims& d, const void* q, const void* k, const void* v,
@@ -702,11 +669,9 @@ hipError_t launch_masked_bwd(const Dims& d, const void* q, const void* k, const 
   char* p = (char*)ws + fwd_ws_bytes(d);
   const size_t rows = (size_t)d.b * d.Hq * d.S, keys = (size_t)d.nseg() * d.S;
   float* dvec = (float*)p; p += align256(rows * 4);
-  int* qend = (int*)p; p += align256(keys * 4);
   int* korder = (int*)p;
-
-  hipLaunchKernelGGL(bwd_qend_kernel, dim3((unsigned)((keys + 255) / 256)), dim3(256), 0, st, rank,
-                     tau, qend, d.S, d.s, d.w, (long long)keys);
+  const int* qend = pl.qend;   // q_end(t), computed by the forward plan
+  (void)keys;
   const int nb = 2 * ((d.S + 63) / 64);
   hipLaunchKernelGGL(bwd_key_order_kernel, dim3(d.nseg()), dim3(1024), (size_t)nb * 2 * 4, st, qend,
                      korder, d.S, d.w);

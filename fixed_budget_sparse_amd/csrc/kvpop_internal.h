@@ -36,8 +36,9 @@ hipError_t launch_masked_fwd(const Dims& d, const void* q, const void* k, const 
 // long-range keys of each tile's first row in rank order), built into the
 // first fwd_ws_bytes(d) bytes of `ws`; the backward reuses it.
 struct FwdPlan {
-  const int2* list;   // [nseg, ntiles, cap] (token, rank)
+  const int2* list;   // [nseg, ntiles, cap] (token, q_end(token))
   const int* count;   // [nseg, ntiles]
+  const int* qend;    // [nseg, S]: the last row that keeps each token
   int m, ntiles, cap;
 };
 FwdPlan launch_fwd_plan(const Dims& d, const int* rank, const int* tau, void* ws,

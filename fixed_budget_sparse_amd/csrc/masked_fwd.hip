@@ -16,8 +16,10 @@
 //    are scattered over the whole prefix, so instead of skipping key blocks
 //    the kernel gathers the candidates into dense 64-key chunks in LDS.
 //  * Per chunk: S^T = K Q^T with v_mfma_f32_32x32x16_bf16 (each lane then owns
-//    one query row), the A8 mask from (t, rank(t)) and (q, tau_q) only on
-//    chunks that are not kept by every row, online softmax in the exp2
+//    one query row), the A8 mask only on chunks that are not kept by every
+//    row, as the interval test t <= q <= q_end(t) (q_end from a small
+//    pre-pass: tau never increases with q, so the rows that keep a token are
+//    one interval), online softmax in the exp2
 //    domain, and O^T = V^T P^T with V staged transposed, so P feeds the second
 //    MFMA straight from registers and O stays row-per-lane.
 //  * float32 inputs use v_mfma_f32_32x32x2_f32 with the same lane layouts.
@@ -40,8 +42,9 @@ struct FwdArgs {
   const void* v;
   const int* rank;
   const int* tau;
-  const int2* list;    // [nseg, ntiles, cap] (token, rank) of listed long-range keys
+  const int2* list;    // [nseg, ntiles, cap] (token, q_end) of listed long-range keys
   const int* count;    // [nseg, ntiles]
+  const int* qend;     // [nseg, S] last row that keeps each token
   void* o;
   float* lse;
   int S, Hq, Hkv, G, m, ntiles, s, w, cap;
@@ -60,13 +63,49 @@ __global__ __launch_bounds__(256) void order_from_rank_kernel(const int* __restr
   if ((unsigned)r < (unsigned)S) order[seg * S + r] = t;
 }
 
+// q_end(t): the last row that keeps token t.  tau never increases with q, so
+// the rows that keep t are the interval [t, q_end(t)]: S - 1 for a sink or a
+// token whose window reaches the end, t + w - 1 when the token is not kept
+// once it leaves the window, else the last q >= t + w with tau_q >= rank(t),
+// found by bisection.  Row q then keeps t iff t <= q <= q_end(t).
+__global__ __launch_bounds__(256) void key_end_kernel(const int* __restrict__ rank,
+                                                      const int* __restrict__ tau,
+                                                      int* __restrict__ qend, int S, int s, int w,
+                                                      long long total) {
+  const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (i >= total) return;
+  const long long seg = i / S;
+  const int t = (int)(i - seg * S);
+  const int* tq = tau + seg * S;
+  int e;
+  if (t < s || t + w > S - 1) {
+    e = S - 1;
+  } else {
+    const int r = rank[i];
+    int lo = t + w, hi = S - 1;
+    if (tq[lo] < r) {
+      e = t + w - 1;
+    } else {
+      while (lo < hi) {                 // invariant: tq[lo] >= r
+        const int mid = lo + (hi - lo + 1) / 2;
+        if (tq[mid] >= r) lo = mid;
+        else hi = mid - 1;
+      }
+      e = lo;
+    }
+  }
+  qend[i] = e;
+}
+
 // Lists, in rank order, the long-range keys of each tile's first row q0 when
 // its cutoff is finite: tokens t in [s, q0 - w] with rank(t) <= tau_q0.  A
 // round covers 4 x 256 places of the rank order, each wave a contiguous run of
 // 256 of them (four loads in flight per lane, ballots in place order), and
-// ends in one barrier (the wave counts are double-buffered).
+// ends in one barrier (the wave counts are double-buffered).  Entries are
+// (token, q_end(token)).
 __global__ __launch_bounds__(256) void tile_list_kernel(const int* __restrict__ order,
-                                                        const int* __restrict__ tau, int S,
+                                                        const int* __restrict__ tau,
+                                                        const int* __restrict__ qend, int S,
                                                         int s, int w, int m, int ntiles, int cap,
                                                         int2* __restrict__ list,
                                                         int* __restrict__ count) {
@@ -84,6 +123,7 @@ __global__ __launch_bounds__(256) void tile_list_kernel(const int* __restrict__ 
   }
   const int scan_end = min(tq0, S - 1);
   const int* ord = order + (size_t)seg * S;
+  const int* qe = qend + (size_t)seg * S;
   int2* out = list + ((size_t)seg * ntiles + tile) * cap;
   int base = 0;
   for (int i0 = 0, r = 0; i0 <= scan_end; i0 += 256 * kU, ++r) {
@@ -115,7 +155,7 @@ __global__ __launch_bounds__(256) void tile_list_kernel(const int* __restrict__ 
     for (int u = 0; u < kU; ++u) {
       const bool keep = t[u] >= s && t[u] <= e_hi;
       const int at = pos + lanes_below(bal[u]);
-      if (keep && at < cap) out[at] = make_int2(t[u], w0 + 64 * u + lane);
+      if (keep && at < cap) out[at] = make_int2(t[u], qe[max(t[u], 0)]);
       pos += __builtin_popcountll(bal[u]);
     }
     base += total;
@@ -142,7 +182,6 @@ __global__ __launch_bounds__(kThreads, 1) void masked_fwd_kernel(FwdArgs a) {
   __shared__ __attribute__((aligned(16))) int kd_t[kDesc][kChunk];
   __shared__ __attribute__((aligned(16))) int kd_r[kDesc][kChunk];
   __shared__ int s_flag[kDesc];
-  __shared__ int s_min_tau;
 
   const int tid = threadIdx.x, lane = lane_id(), wave = wave_id();
   const int hh = lane >> 5, li = lane & 31;
@@ -152,7 +191,7 @@ __global__ __launch_bounds__(kThreads, 1) void masked_fwd_kernel(FwdArgs a) {
   const int b = Lb / (a.ntiles * a.Hkv);
   const int S = a.S, s = a.s, w = a.w, m = a.m, G = a.G;
   const size_t seg = (size_t)b * a.Hkv + h;
-  const int* rank = a.rank + seg * S;
+  const int* qend = a.qend + seg * S;
   const int* tau = a.tau + seg * S;
   const int q0 = tile * m;
   const int q_hi = min(q0 + m - 1, S - 1);
@@ -163,11 +202,7 @@ __global__ __launch_bounds__(kThreads, 1) void masked_fwd_kernel(FwdArgs a) {
   const int q = q0 + (rr - g * m);
   const bool row_ok = g < G && q < S;
   const int hq = h * G + (g < G ? g : 0);
-  const int tau_q = row_ok ? tau[q] : -1;
 
-  if (tid == 0) s_min_tau = kInt32Max;
-  __syncthreads();
-  if (tid < m && q0 + tid < S) atomicMin(&s_min_tau, tau[q0 + tid]);
 
   // key segments of the tile: sinks | long-range | band
   const int n_sink = min(s, q_hi + 1);
@@ -221,17 +256,15 @@ __global__ __launch_bounds__(kThreads, 1) void masked_fwd_kernel(FwdArgs a) {
   float m_run = kNegInf, l_run = 0.0f;
 
   const size_t kvbase = seg * (size_t)S * D;
-  __syncthreads();   // s_min_tau complete
-  const int min_tau = s_min_tau;
 
   // ---- key descriptors of the chunk starting at c0, built by wave 0 in two
   // halves: desc_load issues the (branch-free, clamped) global reads into
-  // registers, desc_store, one compute phase later, publishes token and
-  // masking rank to LDS with the chunk's mask class:
-  //   0  every key kept by every row of the tile (no mask),
-  //   1  every key is a sink or lies at or below q0 - w for the whole tile, so
-  //      a row keeps it iff rank' <= tau_q (rank' = -1 for sinks),
-  //   2  otherwise (window edge, causal diagonal, padding): the full test.
+  // registers, desc_store, one compute phase later, publishes the token and
+  // its span q_end(t) - t to LDS with the chunk's mask class: 0 when every
+  // key is kept by every row of the tile (t <= q0 and q_end(t) >= q_hi), so no
+  // mask runs, else 2: row q keeps key t iff t <= q <= q_end(t), the A8 mask
+  // as one unsigned compare (tau never increases with q, so the rows that
+  // keep a key are one interval); padding keys (token -1, span 0) fail it.
   int pd_t = -1, pd_r = 0;
   int2 pd_l = make_int2(-1, 0);
   auto desc_load = [&](int c0) {
@@ -244,22 +277,20 @@ __global__ __launch_bounds__(kThreads, 1) void masked_fwd_kernel(FwdArgs a) {
                     : in_long ? s + (j - n_sink)
                     : in_band ? band_lo + (j - n_sink - n_long) : -1;
       if (listed) pd_l = lst[min(max(j - n_sink, 0), max(n_long - 1, 0))];
-      pd_r = rank[min(max(t, 0), S - 1)];
-      pd_t = (in_long && listed) ? -2 : t;    // -2: token and rank from the list
+      pd_r = qend[min(max(t, 0), S - 1)];
+      pd_t = (in_long && listed) ? -2 : t;    // -2: token and q_end from the list
     }
   };
   auto desc_store = [&](int db) {
     if (wave == 0) {
       int t = pd_t == -2 ? pd_l.x : pd_t;
-      const int r = pd_t == -2 ? pd_l.y : pd_r;
+      const int e = pd_t == -2 ? pd_l.y : pd_r;
       if (t >= S) t = -1;
-      const int rq = ((t >= 0) & (t < s)) ? -1 : r;
       kd_t[db][lane] = t;
-      kd_r[db][lane] = rq;
-      const bool always = (t >= 0) & (t <= q0) & ((t < s) | (t > q_hi - w) | (r <= min_tau));
-      const bool simple = (t >= 0) & (t <= q0) & ((t < s) | (t <= q0 - w));
-      const uint64_t not_always = wave_ballot(!always), not_simple = wave_ballot(!simple);
-      if (lane == 0) s_flag[db] = not_always == 0 ? 0 : (not_simple == 0 ? 1 : 2);
+      kd_r[db][lane] = t >= 0 ? e - t : 0;
+      const bool always = (t >= 0) & (t <= q0) & (e >= q_hi);
+      const uint64_t not_always = wave_ballot(!always);
+      if (lane == 0) s_flag[db] = not_always == 0 ? 0 : 2;
     }
   };
 
@@ -379,25 +410,16 @@ __global__ __launch_bounds__(kThreads, 1) void masked_fwd_kernel(FwdArgs a) {
   // scores); returns the exponent bias -m_run * c
   auto softmax_pre = [&](f32x16 (&sc)[2], int db, auto&& before_rescale) -> float {
     const int mclass = __builtin_amdgcn_readfirstlane(s_flag[db]);   // uniform
-    if (mclass == 1) {
+    if (mclass != 0) {
+      // branch-free: one unsigned compare and a select per score (a
+      // short-circuit form of an older mask was compiled into divergent
+      // branches that lost a store)
 #pragma unroll
       for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
           const int jj = 32 * blk + 8 * (e >> 2) + 4 * hh + (e & 3);
-          sc[blk][e] = kd_r[db][jj] <= tau_q ? sc[blk][e] : kNegInf;
-        }
-    } else if (mclass == 2) {
-      // branch-free: bitwise tests and a select per score (a short-circuit
-      // form here was compiled into divergent branches that lost a store)
-#pragma unroll
-      for (int blk = 0; blk < 2; ++blk)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int jj = 32 * blk + 8 * (e >> 2) + 4 * hh + (e & 3);
-          const int t = kd_t[db][jj], rt = kd_r[db][jj];
-          const bool keep = row_ok & (t >= 0) & (t <= q) &
-                            ((t < s) | (t > q - w) | (rt <= tau_q));
+          const bool keep = (unsigned)(q - kd_t[db][jj]) <= (unsigned)kd_r[db][jj];
           sc[blk][e] = keep ? sc[blk][e] : kNegInf;
         }
     }
@@ -694,6 +716,7 @@ static int fwd_list_cap(const Dims& d) { return d.k < d.S ? d.k : d.S; }
 size_t fwd_ws_bytes(const Dims& d) {
   const size_t nseg = d.nseg(), nt = fwd_ntiles(d);
   size_t bytes = align256(nseg * d.S * 4);                              // order
+  bytes += align256(nseg * d.S * 4);                                    // q_end
   bytes += align256(nseg * nt * 4);                                     // counts
   bytes += align256(nseg * nt * (size_t)fwd_list_cap(d) * 8);           // lists
   return bytes;
@@ -705,16 +728,20 @@ FwdPlan launch_fwd_plan(const Dims& d, const int* rank, const int* tau, void* ws
   const int cap = fwd_list_cap(d);
   char* p = (char*)ws;
   int* order = (int*)p; p += align256((size_t)nseg * d.S * 4);
+  int* qend = (int*)p; p += align256((size_t)nseg * d.S * 4);
   int* count = (int*)p; p += align256((size_t)nseg * nt * 4);
   int2* list = (int2*)p;
 
   const long long total = (long long)nseg * d.S;
-  hipLaunchKernelGGL(order_from_rank_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0,
-                     st, rank, order, d.S, total);
-  hipLaunchKernelGGL(tile_list_kernel, dim3(nt, nseg), dim3(256), 0, st, order, tau, d.S, d.s,
-                     d.w, m, nt, cap, list, count);
+  const unsigned nblk = (unsigned)((total + 255) / 256);
+  hipLaunchKernelGGL(order_from_rank_kernel, dim3(nblk), dim3(256), 0, st, rank, order, d.S,
+                     total);
+  hipLaunchKernelGGL(key_end_kernel, dim3(nblk), dim3(256), 0, st, rank, tau, qend, d.S, d.s, d.w,
+                     total);
+  hipLaunchKernelGGL(tile_list_kernel, dim3(nt, nseg), dim3(256), 0, st, order, tau, qend, d.S,
+                     d.s, d.w, m, nt, cap, list, count);
   FwdPlan pl;
-  pl.list = list; pl.count = count; pl.m = m; pl.ntiles = nt; pl.cap = cap;
+  pl.list = list; pl.count = count; pl.qend = qend; pl.m = m; pl.ntiles = nt; pl.cap = cap;
   return pl;
 }
 
@@ -728,6 +755,7 @@ hipError_t launch_masked_fwd(const Dims& d, const void* q, const void* k, const 
 
   FwdArgs a;
   a.q = q; a.k = k; a.v = v; a.rank = rank; a.tau = tau; a.list = list; a.count = count;
+  a.qend = pl.qend;
   a.o = o; a.lse = lse;
   a.S = d.S; a.Hq = d.Hq; a.Hkv = d.Hkv; a.G = d.G; a.m = m; a.ntiles = nt;
   a.s = d.s; a.w = d.w; a.cap = cap;
