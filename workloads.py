@@ -61,7 +61,7 @@ class Workload:
         return self.n_q_heads // self.n_kv_heads
 
 
-# The five workloads of the build, in order (ids 0..4).
+# The five workloads, in order (ids 0..4): tiny reference, 16k and 32k layers, decode, long context.
 TINY = Workload("tiny-f32-S512", 0, 1, 2, 1, 64, 512, "f32", 4, 32, 64)
 QWEN3_4B_S16K = Workload("qwen3-4b-layer-S16384-B2048", 1, 1, 32, 8, 128, 16384, "bf16",
                          16, 512, 1520)
