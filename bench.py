@@ -384,7 +384,7 @@ def cpu_baseline(x, s, w, k, sample_rows=3072, sample_t=512):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "the path runs on one GPU: every KV head of the layer is on it (see the sharding notes); run with --gpus 1"}))
+        print(json.dumps({"error": "the path runs on one GPU, which holds every KV head of the layer; run with --gpus 1"}))
         sys.exit(2)
     import numpy as np
     import torch
