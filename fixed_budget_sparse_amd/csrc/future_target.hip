@@ -23,6 +23,15 @@
 //  * X^T = Q K^T leaves every lane owning one row t; each score becomes
 //    exp2(x * scale log2 e - LSE_d log2 e) and is summed directly: with the
 //    dense LSE every exponent is <= 0, so no running maximum is needed.
+//  * Any other LSE (the sparse operator's, which can lie below a dropped
+//    key's logit) may push a term past float32's range.  Such a sum cannot
+//    overflow unnoticed: a row whose max-free total leaves [2^-100, 2^100]
+//    makes its workgroup recompute the tile with a running maximum per row
+//    (rescaling its sum whenever the maximum grows), which is exact for any
+//    finite LSE.  With the dense LSE every total lies in that range (it is a
+//    sum of at most S probabilities, each <= 1, of which the largest is not
+//    tiny unless the target is below -69), so the dense path pays one flag
+//    and one barrier.
 //  * Chunks wholly below a wave's first row + w are skipped; the d >= t + w
 //    test (a select) runs only on chunks that straddle the band.
 //  * Blocks are renumbered so that each XCD (its own L2) works through whole
@@ -61,6 +70,105 @@ struct TgtGeom {
   static constexpr int NKS = kF32 ? D / 2 : D / 16;          // MFMA k-steps
 };
 
+// The exact pass for an arbitrary (finite) LSE: the tile's future queries
+// stream through LDS one 64-row chunk at a time; each lane keeps, for each of
+// its rows, a running maximum m of the exponents (log2 units) and the sum of
+// exp2(e - m), rescaled whenever m grows; the two lanes of a row merge theirs
+// at the end.  Slow next to the max-free pipeline, and only run for tiles
+// whose max-free sums left float32's range.  Writes the tile's targets.
+template <int D, bool kF32In, typename KOp>
+__device__ __forceinline__ void rescaled_pass(
+    const TgtArgs& a, const KOp (&kop)[kRB][TgtGeom<D, kF32In>::NKS],
+    unsigned char (&q_lds)[2][TgtGeom<D, kF32In>::bufBytes], float (&nlse)[3][kChunk], int rbase,
+    int t0, int b, int hq) {
+  using Gm = TgtGeom<D, kF32In>;
+  const int tid = threadIdx.x, lane = lane_id();
+  const int hh = lane >> 5, li = lane & 31;
+  const int S = a.S, w = a.w;
+  const int d_start = t0 + w;
+  const unsigned char* qg = (const unsigned char*)a.q + ((size_t)b * a.Hq + hq) * S * D * Gm::esz;
+  const float* lse = a.lse + ((size_t)b * a.Hq + hq) * S;
+  float m[kRB], l[kRB];
+#pragma unroll
+  for (int rb = 0; rb < kRB; ++rb) {
+    m[rb] = kNegInf;
+    l[rb] = 0.0f;
+  }
+  for (int d0 = d_start; d0 < S; d0 += kChunk) {
+    __syncthreads();   // every wave is done with the previous chunk
+    for (int p = tid; p < kChunk * Gm::PPR; p += kThreads) {
+      const int row = p / Gm::PPR, piece = p % Gm::PPR;
+      uint4 u = make_uint4(0, 0, 0, 0);
+      if (d0 + row < S) u = *(const uint4*)(qg + ((size_t)(d0 + row) * D) * Gm::esz + piece * 16);
+      if constexpr (kF32In) {
+        float* dst = (float*)q_lds[0] + row * Gm::QS + piece * 4;
+        dst[0] = __uint_as_float(u.x);
+        dst[1] = __uint_as_float(u.y);
+        dst[2] = __uint_as_float(u.z);
+        dst[3] = __uint_as_float(u.w);
+      } else {
+        *(uint4*)((uint16_t*)q_lds[0] + row * Gm::QS + piece * 8) = u;
+      }
+    }
+    if (tid < kChunk) nlse[0][tid] = d0 + tid < S ? -lse[d0 + tid] * kLog2e : kNegInf;
+    __syncthreads();
+    if (d0 + kChunk - 1 < rbase + w) continue;   // every row of this wave starts later
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb) {
+      f32x16 acc[kRB];
+#pragma unroll
+      for (int rb = 0; rb < kRB; ++rb) acc[rb] = f32x16{};
+#pragma unroll
+      for (int ks = 0; ks < Gm::NKS; ++ks) {
+        if constexpr (kF32In) {
+          const float av = ((const float*)q_lds[0])[(32 * cb + li) * Gm::QS + hh + 2 * ks];
+#pragma unroll
+          for (int rb = 0; rb < kRB; ++rb) acc[rb] = mfma32x32x2(av, kop[rb][ks], acc[rb]);
+        } else {
+          const bf16x8 av = as_bf16x8(
+              *(const uint4*)((const uint16_t*)q_lds[0] + (32 * cb + li) * Gm::QS + 8 * hh + 16 * ks));
+#pragma unroll
+          for (int rb = 0; rb < kRB; ++rb) acc[rb] = mfma32x32x16(av, kop[rb][ks], acc[rb]);
+        }
+      }
+#pragma unroll
+      for (int rb = 0; rb < kRB; ++rb) {
+        const int t = rbase + 32 * rb + li;
+        // exponent of element i in log2 units, -inf outside d >= t + w, d < S
+        // (evaluated twice, for the block maximum and for the sum, rather
+        // than held: this pass is rare and registers are not)
+        auto expo = [&](int i) {
+          const int dl = 32 * cb + 8 * (i >> 2) + 4 * hh + (i & 3);
+          const int d = d0 + dl;
+          const float x = fmaf(acc[rb][i], a.scale_log2, nlse[0][dl]);
+          return (d >= t + w && d < S) ? x : kNegInf;
+        };
+        float bm = kNegInf;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) bm = fmaxf(bm, expo(i));
+        if (bm == kNegInf) continue;   // nothing of this block in the row's range
+        if (bm > m[rb]) {
+          l[rb] *= exp2_fast(m[rb] - bm);   // m = -inf: l is 0 and stays 0
+          m[rb] = bm;
+        }
+        float acc_l = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc_l += exp2_fast(expo(i) - m[rb]);
+        l[rb] += acc_l;
+      }
+    }
+  }
+  float* out = a.target + ((size_t)b * a.Hq + hq) * S;
+#pragma unroll
+  for (int rb = 0; rb < kRB; ++rb) {
+    const float mm = halves_max(m[rb]);
+    const float part = mm == kNegInf ? 0.0f : l[rb] * exp2_fast(m[rb] - mm);
+    const float ll = halves_sum(part);
+    const int t = rbase + 32 * rb + li;
+    if (hh == 0 && t < S) out[t] = ll > 0.0f ? (mm + log2f(ll)) * kLn2 : kNegInf;
+  }
+}
+
 template <int D, bool kF32In>
 __global__ __launch_bounds__(kThreads, 2) void future_target_kernel(TgtArgs a) {
   using Gm = TgtGeom<D, kF32In>;
@@ -70,6 +178,7 @@ __global__ __launch_bounds__(kThreads, 2) void future_target_kernel(TgtArgs a) {
   // the next iteration) must not see them overwritten by the store of the
   // chunk after next, which other waves may reach first
   __shared__ __attribute__((aligned(16))) float nlse[3][kChunk];
+  __shared__ int redo;   // some row of the tile needs the running-maximum pass
 
   const int tid = threadIdx.x, lane = lane_id(), wave = wave_id();
   const int hh = lane >> 5, li = lane & 31;
@@ -172,6 +281,7 @@ __global__ __launch_bounds__(kThreads, 2) void future_target_kernel(TgtArgs a) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) sum[rb][r] = 0.0f;
   const int nchunks = (S - d_start + kChunk - 1) / kChunk;
+  if (tid == 0) redo = 0;
   load_chunk(d_start);
   store_chunk(0, 0, d_start);
   __syncthreads();
@@ -337,12 +447,29 @@ __global__ __launch_bounds__(kThreads, 2) void future_target_kernel(TgtArgs a) {
     }
   }
 
+  // A row whose range d >= t + w is not empty has a total in [2^-100, 2^100]
+  // unless its exponents left the range the max-free sum covers; then the
+  // whole workgroup (barriers) recomputes the tile with a running maximum.
+  float tot[kRB];
+  bool bad = false;
 #pragma unroll
   for (int rb = 0; rb < kRB; ++rb) {
     const float part = (sum[rb][0] + sum[rb][1]) + (sum[rb][2] + sum[rb][3]);
-    const float tot = halves_sum(part);
+    tot[rb] = halves_sum(part);
     const int t = rbase + 32 * rb + li;
-    if (hh == 0 && t < S) out[t] = tot > 0.0f ? log2f(tot) * kLn2 : kNegInf;
+    const bool nonempty = t + w <= S - 1;
+    bad |= nonempty && !(tot[rb] >= 0x1p-100f && tot[rb] <= 0x1p100f);
+  }
+  if (bad) redo = 1;   // every writer stores the same value
+  __syncthreads();
+  if (redo) {
+    rescaled_pass<D, kF32In>(a, kop, q_lds, nlse, rbase, t0, b, hq);
+    return;
+  }
+#pragma unroll
+  for (int rb = 0; rb < kRB; ++rb) {
+    const int t = rbase + 32 * rb + li;
+    if (hh == 0 && t < S) out[t] = tot[rb] > 0.0f ? log2f(tot[rb]) * kLn2 : kNegInf;
   }
 }
 
@@ -376,9 +503,13 @@ hipError_t launch_future_target(const Dims& d, const void* q, const void* k, con
 
 // Target score ([Notes] §2.2): r_{h,t} = log(eps + (1/G) sum_g m_t^{(h,g)}) with
 // m_t = exp(target_g[t]) / N_t, N_t = S - t - w future queries (the mean is 0
-// where there are none).  One thread per (b, h, t); every exponent
-// target_g[t] - ln N_t is <= 0 for the dense LSE (a probability sum over N_t
-// queries is at most N_t), so the sum needs no maximum.
+// where there are none).  One thread per (b, h, t).  The exponents
+// x_g = target_g[t] - ln N_t are <= 0 for the dense LSE (a probability sum
+// over N_t queries is at most N_t) but not for a sparse one, so the mean is
+// taken relative to the group's largest exponent m:
+//   mean = e^m A,  A = (1/G) sum_g e^(x_g - m) in [1/G, 1],
+//   score = log(eps + e^m A)            for m <= 0 (e^m cannot overflow),
+//         = m + log(eps e^-m + A)       for m > 0  (e^-m cannot overflow).
 namespace {
 __global__ __launch_bounds__(256) void target_score_kernel(const float* __restrict__ target,
                                                            float* __restrict__ score, int Hq,
@@ -391,15 +522,22 @@ __global__ __launch_bounds__(256) void target_score_kernel(const float* __restri
   const int t = (int)(i - bh * S);
   const int b = (int)(bh / Hkv), h = (int)(bh % Hkv);
   const int nt = S - t - w;
-  float mean = 0.0f;
+  const float* tg = target + ((size_t)b * Hq + (size_t)h * G) * S + t;
+  float r = logf(eps);                        // no future query: the mean is 0
   if (nt > 0) {
     const float lnn = logf((float)nt);
-    float acc = 0.0f;
-    for (int g = 0; g < G; ++g)
-      acc += expf(target[((size_t)b * Hq + (size_t)h * G + g) * S + t] - lnn);
-    mean = acc / (float)G;
+    float m = kNegInf;
+    for (int g = 0; g < G; ++g) m = fmaxf(m, tg[(size_t)g * S] - lnn);
+    if (m != kNegInf) {
+      float acc = 0.0f;
+      for (int g = 0; g < G; ++g) acc += expf(tg[(size_t)g * S] - lnn - m);
+      const float A = acc / (float)G;
+      if (m > 0.0f) r = m + logf(eps * expf(-m) + A);
+      else if (eps > 0.0f) r = logf(eps + expf(m) * A);
+      else r = m + logf(A);
+    }
   }
-  score[i] = logf(eps + mean);
+  score[i] = r;
 }
 }  // namespace
 

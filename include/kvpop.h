@@ -148,9 +148,14 @@ kvpop_status kvpop_masked_attn_fwd(const kvpop_problem* pr, const void* q,
  *   target [batch, Hq, S] float out:
  *          ln sum_{d = t+w}^{S-1} exp(scale <q_d, k_t> - lse_d), -inf when t + w > S - 1
  * This is the first term of Eq. (8) per query head (no -ln N_t, no average
- * over the query group).  w >= 0.  The sum runs without a running maximum,
- * which is exact in float32 whenever every exponent is <= 0, i.e. whenever
- * lse_d is at least every logit of row d (true for the dense causal LSE). */
+ * over the query group).  w >= 0.  Any finite lse is accepted: the teacher's
+ * dense causal LSE (every exponent <= 0, the fast path: the sum runs without
+ * a running maximum) or an approximation such as the sparse operator's LSE
+ * ([Sum-zh] §2.2, [Notes] §2.3), which can lie below a dropped key's logit;
+ * a tile whose max-free sums leave float32's safe range [2^-100, 2^100] is
+ * recomputed in the same launch with a running maximum per row, so the
+ * result never overflows to +inf and never underflows to -inf for a
+ * non-empty range.  A non-finite lse gives unspecified values. */
 kvpop_status kvpop_future_target(const kvpop_problem* pr, const void* q,
                                  const void* k, const float* lse, float* target,
                                  void* ws, size_t ws_bytes, hipStream_t stream);
@@ -212,7 +217,9 @@ kvpop_status kvpop_cache_from_prefill(const kvpop_problem* pr, const kvpop_cache
  *   eps    >= 0, finite
  *   score  [batch, Hkv, S] float out: log(eps + (1/G) sum_g exp(target_g - ln N_t));
  *          where t + w > S - 1 (N_t = 0) the mean is 0 and score = log(eps)
- *          (-inf for eps = 0)
+ *          (-inf for eps = 0).  The mean is taken relative to the group's
+ *          largest exponent, so targets above ln N_t (a sparse LSE) do not
+ *          overflow.
  * Uses no workspace. */
 kvpop_status kvpop_target_score(const kvpop_problem* pr, const float* target, float eps,
                                 float* score, hipStream_t stream);

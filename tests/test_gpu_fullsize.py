@@ -7,10 +7,12 @@ decode over 131072 steps.
 The oracle cannot evaluate these sizes whole, so outputs are compared where it
 can compute them one by one: every rank, the cutoffs of every row (or of a
 sample of rows plus all boundary rows at S = 131072), the forward on sampled
-query rows of every head, the future target on every token of one head (on
-sampled tokens at S = 32768) with the teacher LSE computed by the oracle, and
-decode cache membership of every (sequence, KV head) plus outputs of a few
-sequences at sampled steps.  Inputs are drawn on the device by the seeded
+query rows of every head and on every row of the four query heads of one KV
+head, the teacher LSE of every row and the future target on every token of
+those four heads (sampled tokens at S = 32768) with the teacher LSE computed
+by the oracle, and decode cache membership of every (sequence, KV head) plus
+outputs of a few sequences at sampled steps.  The every-row checks run the
+oracle in worker processes (``oracle_pool``).  Inputs are drawn on the device by the seeded
 generators of ``workloads``; host copies feed the oracle."""
 import numpy as np
 import pytest
@@ -19,6 +21,7 @@ import torch
 import fixed_budget_sparse_amd as kv
 import oracle as orc
 import workloads as W
+import oracle_pool
 from gpu_util import BWD_TOL, TOL, announce, device, host
 
 pytestmark = pytest.mark.gpu
@@ -101,43 +104,73 @@ def test_full_masked_fwd_sampled_rows(name):
     assert np.abs(lg - LSE).max() <= tol["lse"], np.abs(lg - LSE).max()
 
 
+# one KV head checked on every row: KV head 1 at S = 16384, the last KV head
+# at S = 32768 (its four query heads)
+EVERY_ROW_HEAD = {"qwen3-4b-S16384": 1, "qwen3-8b-S32768": 7}
+
+
+@pytest.mark.parametrize("name", ["qwen3-4b-S16384", "qwen3-8b-S32768"])
+def test_full_masked_fwd_one_kv_head_every_row(name):
+    """The forward of the whole layer, in the benchmark's launch configuration
+    (bf16 output); the oracle evaluates every row of the four query heads of
+    one KV head, so every tile, the long-range key lists of every tile and
+    the ragged end are checked."""
+    wl = PREFILL[name]
+    h = EVERY_ROW_HEAD[name]
+    G = wl.group
+    announce(f"full masked_fwd {name}, every row of KV head {h}")
+    S, s, w, k = wl.seq_len, wl.sink, wl.window, wl.topk
+    x = _inputs(wl)
+    rank, tau = kv.thresholds(x["prio"], s, w, k)
+    o, lse = kv.masked_attn_fwd(x["q"], x["k"], x["v"], rank, tau, s, w, k,
+                                out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    qs = slice(h * G, (h + 1) * G)
+    rank_o = orc.priority_ranks(host(x["prio"][:, h:h + 1]))
+    tau_o = orc.thresholds_by_selection(rank_o, s, w, k)
+    assert np.array_equal(host(tau[:, h:h + 1]), tau_o)
+    O, LSE = oracle_pool.masked_attention_all_rows(host(x["q"][:, qs]), host(x["k"][:, h:h + 1]),
+                                                   host(x["v"][:, h:h + 1]), rank_o, tau_o, s, w)
+    og, lg = host(o[:, qs]), host(lse[:, qs])
+    assert np.isfinite(og).all() and np.isfinite(lg).all()
+    err = np.abs(og - O) - _bf16_half_ulp(np.maximum(np.abs(O), np.abs(og)))
+    assert err.max() <= TOL["bf16"]["o"], err.max()
+    assert np.abs(lg - LSE).max() <= TOL["bf16"]["lse"], np.abs(lg - LSE).max()
+
+
 @pytest.mark.parametrize("name", ["qwen3-4b-S16384", "qwen3-8b-S32768"])
 def test_full_teacher_lse_and_target(name):
-    """The dense teacher (k >= S) on sampled rows, then the future target of one
-    query head driven by the oracle's teacher LSE (every head receives that
-    head's LSE; only the checked head is compared)."""
+    """The dense teacher (k >= S) and the future target of the whole layer;
+    the oracle evaluates the teacher LSE of every row and the target of every
+    token (of sampled tokens at S = 32768) of the four query heads of one KV
+    head, with the target driven by the oracle's teacher LSE (the other heads
+    receive the GPU's teacher LSE)."""
     wl = PREFILL[name]
-    announce(f"full target {name}")
-    S, s, w = wl.seq_len, wl.sink, wl.window
+    h = EVERY_ROW_HEAD[name]
     G = wl.group
+    qs = slice(h * G, (h + 1) * G)
+    announce(f"full target {name}, KV head {h}")
+    S, s, w = wl.seq_len, wl.sink, wl.window
     x = _inputs(wl)
-    hq = 5 if S <= 16384 else wl.n_q_heads - 1
-    h = hq // G
     rank_d, tau_d = kv.thresholds(x["prio"], s, w, S)
     _, lse_dense = kv.masked_attn_fwd(x["q"], x["k"], x["v"], rank_d, tau_d, s, w, S,
                                       out_dtype=torch.bfloat16)
     torch.cuda.synchronize()
-    qh = host(x["q"][:, hq:hq + 1])
+    qh = host(x["q"][:, qs])
     kh = host(x["k"][:, h:h + 1])
-    vh = host(x["v"][:, h:h + 1])
-    _, L = orc.dense_causal_attention(qh, kh, vh)            # teacher LSE [1, 1, S]
-    rows = _boundary_rows(S, s, w, 2048, 256, 7)
-    assert np.abs(host(lse_dense)[0, hq, rows] - L[0, 0, rows]).max() <= TOL["bf16"]["lse"]
+    L = oracle_pool.dense_lse_all_rows(qh, kh)                  # teacher LSE [1, G, S]
+    assert np.abs(host(lse_dense[:, qs]) - L).max() <= TOL["bf16"]["lse"]
     L32 = L.astype(np.float32)
-    lse_in = torch.from_numpy(L32).to(x["q"].device).expand(1, wl.n_q_heads, S).contiguous()
+    lse_in = lse_dense.clone()
+    lse_in[:, qs] = torch.from_numpy(L32).to(lse_in.device)
     tgt = kv.future_target(x["q"], x["k"], lse_in, w)
     torch.cuda.synchronize()
-    tg = host(tgt)[0, hq]
-    if S <= 16384:
-        T = orc.future_target_colsum(qh, kh, L32.astype(np.float64), w)[0, 0]
-        ts = np.arange(S)
-    else:
-        ts = _boundary_rows(S, s, w, 2048, 384, 9)
-        T = orc.future_target_eq8(qh, kh, L32.astype(np.float64), w, ts=ts)[0, 0]
-    tg = tg[ts]
+    ts = np.arange(S) if S <= 16384 else _boundary_rows(S, s, w, 2048, 1024, 9)
+    T = oracle_pool.future_target_all_tokens(qh, kh, L32.astype(np.float64), w, ts=ts)
+    tg = host(tgt[:, qs])[..., ts]
     assert np.array_equal(np.isneginf(tg), np.isneginf(T))
     sel = T > -20
-    assert sel.sum() > len(ts) // 2
+    assert sel.sum() > T.size // 2
     assert np.abs(tg[sel] - T[sel]).max() <= TOL["bf16"]["tgt"], np.abs(tg[sel] - T[sel]).max()
 
 
@@ -260,9 +293,11 @@ def test_full_handoff_b2048_then_decode():
 
 def test_full_boundary_labels():
     """Teacher boundary labels on the 16k layer's shape (8 KV heads, S = 16384,
-    s 16, w 512, k 1520, decay step 64) from seeded stand-in target scores;
-    sampled rows (the first labelled rows, rows around k eligible tokens,
-    random rows and the last rows) are compared exactly with the oracle."""
+    s 16, w 512, k 1520, decay step 64) from seeded stand-in target scores
+    whose decay and spread leave the newcomer kept in a mix of rows (about
+    35-60 % per head), so both labels occur in every head; sampled rows (the
+    first labelled rows, rows around k eligible tokens, random rows and the
+    last rows) are compared exactly with the oracle."""
     wl = W.QWEN3_4B_S16K
     announce("full boundary labels 8 x S16384")
     s, w, k, S = wl.sink, wl.window, wl.topk, wl.seq_len
@@ -274,7 +309,7 @@ def test_full_boundary_labels():
     tb, y = host(tb), host(y)
     rng = np.random.default_rng(17)
     rows = sorted(set(list(range(s + w - 3, s + w + 40)) + list(range(s + w + k - 20, s + w + k + 20))
-                      + rng.integers(0, S, 150).tolist() + list(range(S - 30, S))))
+                      + rng.integers(0, S, 400).tolist() + list(range(S - 30, S))))
     want_t, want_y = orc.boundary_labels(x["score"], x["log_gamma"], W.LABEL_DECAY_STEP, s, w, k,
                                          rows=rows)
     assert np.array_equal(tb[..., rows], want_t[..., rows])
@@ -285,6 +320,12 @@ def test_full_boundary_labels():
     assert (y[..., ~lab] == 0).all() and (tb[..., ~lab] == -1).all()
     assert (np.abs(y[..., lab]) == 1).all()
     assert ((tb[..., lab] >= s) & (tb[..., lab] <= (q - w)[lab])).all()
+    # a mixed input: both labels in every head, and in the sampled rows too
+    kept = (y[..., lab] == 1).mean(axis=-1)[0]
+    assert 0.3 <= kept.mean() <= 0.7, kept
+    assert ((kept > 0.2) & (kept < 0.8)).all(), kept
+    ys = want_y[..., rows]
+    assert (ys == 1).sum() > 100 and (ys == -1).sum() > 100
 
 
 def test_full_masked_bwd_one_kv_head():

@@ -89,6 +89,89 @@ def test_target_with_sparse_lse():
     assert (tgt_sparse[fin] >= T_d[fin] - TOL["bf16"]["tgt"]).all()
 
 
+RESCALE_CASES = [
+    # b, Hq, Hkv, S, D, w, lse kind, dtype
+    (1, 4, 2, 600, 128, 20, "minus100", "bf16"),   # every exponent up to ~+100 nats: overflow
+    (1, 4, 2, 600, 128, 20, "plus120", "bf16"),    # every term below e^-100: underflow
+    (1, 4, 1, 900, 128, 7, "early", "bf16"),       # only the first tile's rows overflow
+    (1, 2, 1, 300, 64, 5, "minus100", "f32"),      # float32 inputs, D = 64
+    (1, 4, 2, 520, 64, 0, "plus120", "bf16"),      # w = 0, D = 64
+]
+
+
+@pytest.mark.parametrize("case", RESCALE_CASES, ids=lambda c: "b{}q{}kv{}S{}D{}w{}-{}-{}".format(*c))
+def test_target_any_lse(case):
+    """The target for an LSE that does not bound the row's logits (or sits far
+    above them): the max-free sum would overflow (or underflow), so those tiles
+    take the running-maximum pass; every finite target matches the oracle
+    (float64, the same LSE), and no non-empty range gives +-inf."""
+    b, hq, hkv, S, D, w, kind, dt = case
+    announce(f"target any lse {case}")
+    device()
+    td = torch.bfloat16 if dt == "bf16" else torch.float32
+    q = _rand((b, hq, S, D), 111)
+    kk = _rand((b, hkv, S, D), 112, scale_keys=True)
+    if dt == "bf16":
+        q, kk = _bf16(q), _bf16(kk)
+    _, LD = orc.dense_causal_attention(q, kk, kk)
+    L = LD.copy()
+    if kind == "minus100":
+        L -= 100.0
+    elif kind == "plus120":
+        L += 120.0
+    elif kind == "early":
+        L[..., :200] -= 100.0        # queries d < 200: only tokens t < 200 - w see them
+    L32 = L.astype(np.float32)
+    tgt = host(kv.future_target(to_dev(q, td), to_dev(kk, td), to_dev(L32), w))
+    T = orc.future_target_colsum(q, kk, L32.astype(np.float64), w)
+    assert np.array_equal(np.isneginf(tg := tgt), np.isneginf(T))
+    assert not np.isposinf(tg).any() and not np.isnan(tg).any()
+    fin = np.isfinite(T)
+    tol = TOL[dt]["tgt"]
+    assert np.abs(tg[fin] - T[fin]).max() <= tol, np.abs(tg[fin] - T[fin]).max()
+    # the score stays finite and exact for targets far above ln N_t
+    if kind != "plus120":
+        R = orc.target_score(q, kk, L32.astype(np.float64), w, 1e-6)
+        r = host(kv.target_score(to_dev(tg.astype(np.float32)), hkv, w, 1e-6))
+        assert np.array_equal(np.isfinite(r), np.isfinite(R))
+        f = np.isfinite(R)
+        assert np.abs(r[f] - R[f]).max() <= tol, np.abs(r[f] - R[f]).max()
+
+
+def test_target_planted_dropped_key():
+    """A key dropped by the sparse mask whose logit exceeds the sparse LSE of
+    later queries by about 150 nats ([Notes] §2.3: the sparse LSE approximates
+    the dense one and must be checked): the target driven by that sparse LSE
+    matches the oracle fed the same LSE, with no overflow."""
+    device()
+    b, hq, hkv, S, D, s, w, k = 1, 4, 1, 400, 128, 2, 8, 20
+    announce("target with a planted dropped key")
+    q = _rand((b, hq, S, D), 121)
+    kk = _rand((b, hkv, S, D), 122)
+    v = _rand((b, hkv, S, D), 123)
+    t_star = 50
+    prio = _rand((b, hkv, S), 124)
+    prio[..., t_star] = -1e9                                    # never kept once it leaves the window
+    q, v = _bf16(q), _bf16(v)
+    # aligned with the last query of head 0: a logit of about 200 there
+    u = q[0, 0, S - 1]
+    kk[0, 0, t_star] = u * (200.0 * np.sqrt(D) / float(u @ u))
+    kk = _bf16(kk)
+    td = torch.bfloat16
+    rank, tau = kv.thresholds(to_dev(prio), s, w, k)
+    _, lse_sparse = kv.masked_attn_fwd(to_dev(q, td), to_dev(kk, td), to_dev(v, td), rank, tau, s,
+                                       w, k, out_dtype=torch.float32)
+    L = host(lse_sparse)
+    logit = float(q[0, 0, S - 1].astype(np.float64) @ kk[0, 0, t_star]) / np.sqrt(D)
+    assert logit - L[0, 0, S - 1] > 88.0                       # beyond float32's exp range
+    tgt = host(kv.future_target(to_dev(q, td), to_dev(kk, td), lse_sparse, w))
+    T = orc.future_target_colsum(q, kk, L.astype(np.float64), w)
+    assert np.isfinite(tgt[..., t_star]).all() and tgt[0, 0, t_star] > 80
+    assert np.array_equal(np.isneginf(tgt), np.isneginf(T))
+    fin = np.isfinite(T)
+    assert np.abs(tgt[fin] - T[fin]).max() <= TOL["bf16"]["tgt"], np.abs(tgt[fin] - T[fin]).max()
+
+
 # ---------------------------------------------------------------- handoff
 HANDOFF_CASES = [
     # nseq, Hkv, D, S, s, w, k, prio kind, dtype
