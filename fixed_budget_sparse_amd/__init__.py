@@ -19,6 +19,7 @@ from .binding import (  # noqa: F401
     masked_attn_fwd,
     future_target,
     decode_step,
+    decode_step_noalloc,
     new_decode_cache,
     cache_from_prefill,
     target_score,

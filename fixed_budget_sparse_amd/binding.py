@@ -27,6 +27,7 @@ EXPORTED_SYMBOLS = (
     "kvpop_masked_attn_fwd",
     "kvpop_future_target",
     "kvpop_decode_step",
+    "kvpop_decode_step_noalloc",
     "kvpop_cache_from_prefill",
     "kvpop_target_score",
     "kvpop_boundary_labels",
@@ -77,12 +78,14 @@ def lib() -> ctypes.CDLL:
         L.kvpop_future_target.argtypes = [P, vp, vp, vp, vp, vp, sz, vp]
         L.kvpop_decode_step.argtypes = [P, ctypes.POINTER(_Cache), vp, vp, vp, vp, vp, vp, vp,
                                         vp, sz, vp]
+        L.kvpop_decode_step_noalloc.argtypes = [P, ctypes.POINTER(_Cache), vp, vp, vp, vp, vp,
+                                                vp, vp, vp]
         L.kvpop_cache_from_prefill.argtypes = [P, ctypes.POINTER(_Cache), vp, vp, vp, vp, vp, vp]
         L.kvpop_target_score.argtypes = [P, vp, ctypes.c_float, vp, vp]
         L.kvpop_boundary_labels.argtypes = [P, vp, vp, ctypes.c_int32, vp, vp, vp]
         L.kvpop_masked_attn_bwd.argtypes = [P] + [vp] * 12 + [sz, vp]
         for f in ("kvpop_thresholds", "kvpop_masked_attn_fwd", "kvpop_future_target",
-                  "kvpop_decode_step", "kvpop_cache_from_prefill", "kvpop_target_score",
+                  "kvpop_decode_step", "kvpop_decode_step_noalloc", "kvpop_cache_from_prefill", "kvpop_target_score",
                   "kvpop_boundary_labels", "kvpop_masked_attn_bwd"):
             getattr(L, f).restype = ctypes.c_int
         L.kvpop_status_string.argtypes = [ctypes.c_int]
@@ -306,6 +309,42 @@ def decode_step(cache: DecodeCache, pos: torch.Tensor, q: torch.Tensor, k_new: t
     _status(lib().kvpop_decode_step(ctypes.byref(c), ctypes.byref(cc), _vp(pos), _vp(q),
                                     _vp(k_new), _vp(v_new), _vp(prio_leaving), _vp(o), _vp(lse),
                                     _vp(ws), n, _stream(dev)), "kvpop_decode_step")
+    return o, lse
+
+
+def decode_step_noalloc(cache: DecodeCache, pos: torch.Tensor, q: torch.Tensor,
+                        k_new: torch.Tensor, v_new: torch.Tensor, prio_leaving: torch.Tensor,
+                        sink: int, window: int, topk: int, softmax_scale: float = 0.0,
+                        out_dtype: torch.dtype = torch.float32,
+                        o: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None):
+    """decode_step through kvpop_decode_step_noalloc: the library's fixed device
+    scratch instead of a workspace (no allocation inside the call; pass `o`
+    and `lse` to allocate nothing here either)."""
+    b, hq, D = q.shape
+    hkv = k_new.shape[1]
+    dev = q.device
+    Bc = sink + window + topk
+    _need(q, "q", (b, hq, D), q.dtype)
+    _need(k_new, "k_new", (b, hkv, D), q.dtype, dev)
+    _need(v_new, "v_new", (b, hkv, D), q.dtype, dev)
+    _need(prio_leaving, "prio_leaving", (b, hkv), torch.float32, dev)
+    _need(pos, "pos", (b,), torch.int32, dev)
+    _need(cache.k, "cache.k", (b, hkv, Bc, D), q.dtype, dev)
+    _need(cache.v, "cache.v", (b, hkv, Bc, D), q.dtype, dev)
+    _need(cache.slot_pos, "cache.slot_pos", (b, hkv, Bc), torch.int32, dev)
+    _need(cache.slot_prio, "cache.slot_prio", (b, hkv, Bc), torch.float32, dev)
+    _need(cache.ring, "cache.ring", (b, hkv, window), torch.int32, dev)
+    o = torch.empty((b, hq, D), dtype=out_dtype, device=dev) if o is None else o
+    lse = torch.empty((b, hq), dtype=torch.float32, device=dev) if lse is None else lse
+    _need(o, "o", (b, hq, D), out_dtype, dev)
+    _need(lse, "lse", (b, hq), torch.float32, dev)
+    pr = Problem(b, hq, hkv, 0, D, sink, window, topk, softmax_scale, _dtype_code(q.dtype),
+                 _dtype_code(out_dtype))
+    cc = cache.c()
+    c = pr.c()
+    _status(lib().kvpop_decode_step_noalloc(ctypes.byref(c), ctypes.byref(cc), _vp(pos), _vp(q),
+                                            _vp(k_new), _vp(v_new), _vp(prio_leaving), _vp(o),
+                                            _vp(lse), _stream(dev)), "kvpop_decode_step_noalloc")
     return o, lse
 
 

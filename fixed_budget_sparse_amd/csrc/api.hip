@@ -144,6 +144,25 @@ KVPOP_EXPORT kvpop_status kvpop_decode_step(const kvpop_problem* pr, const kvpop
   return finish(kvpop::launch_decode(d, c, pos, q, k_new, v_new, prio_leaving, o, lse, ws, stream));
 }
 
+KVPOP_EXPORT kvpop_status kvpop_decode_step_noalloc(const kvpop_problem* pr,
+                                                    const kvpop_cache* cache, const int32_t* pos,
+                                                    const void* q, const void* k_new,
+                                                    const void* v_new, const float* prio_leaving,
+                                                    void* o, float* lse, hipStream_t stream) {
+  Dims d;
+  kvpop_status st = make_dims(KVPOP_CALL_DECODE, pr, &d);
+  if (st != KVPOP_OK) return st;
+  if (!cache || !cache->k || !cache->v || !cache->slot_pos || !cache->slot_prio || !cache->ring)
+    return KVPOP_ERR_ARG;
+  if (!pos || !q || !k_new || !v_new || !prio_leaving || !o) return KVPOP_ERR_ARG;
+  const size_t need = ws_bytes(KVPOP_CALL_DECODE, d);
+  if (need > kvpop::decode_noalloc_scratch_bytes()) return KVPOP_ERR_SCRATCH;
+  void* ws = nullptr;
+  if (need > 0 && kvpop::decode_noalloc_scratch(stream, &ws) != hipSuccess) return KVPOP_ERR_HIP;
+  kvpop::CacheArgs c{cache->k, cache->v, cache->slot_pos, cache->slot_prio, cache->ring};
+  return finish(kvpop::launch_decode(d, c, pos, q, k_new, v_new, prio_leaving, o, lse, ws, stream));
+}
+
 KVPOP_EXPORT kvpop_status kvpop_cache_from_prefill(const kvpop_problem* pr,
                                                    const kvpop_cache* cache, const void* k,
                                                    const void* v, const float* prio,
@@ -205,6 +224,7 @@ KVPOP_EXPORT const char* kvpop_status_string(kvpop_status st) {
     case KVPOP_ERR_UNSUPPORTED: return "unsupported problem";
     case KVPOP_ERR_WORKSPACE: return "workspace too small";
     case KVPOP_ERR_HIP: return "HIP launch failed";
+    case KVPOP_ERR_SCRATCH: return "problem exceeds the fixed scratch of the no-allocation entry point";
     default: return "unknown status";
   }
 }

@@ -28,8 +28,11 @@
 // A device-scope fence per workgroup (to let the last one merge) would write
 // back and invalidate the L2 of its XCD on this multi-XCD part, so the merge
 // across workgroups is a separate kernel.
+#include <atomic>
+#include <mutex>
 #include <type_traits>
 
+#include "kvpop.h"
 #include "kvpop_device.h"
 #include "kvpop_internal.h"
 
@@ -623,6 +626,48 @@ hipError_t launch_decode(const Dims& d, const CacheArgs& c, const int* pos, cons
     }
   }
   return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- no-alloc
+// Scratch of kvpop_decode_step_noalloc: the split-K partials and decision
+// records that kvpop_decode_step keeps in the caller's workspace live here
+// instead, one copy per GPU (each device holds the array from the library's
+// first use on it until the process ends).  In host code `scratch` names a
+// host-side stand-in, not device memory: kernels and copies get the device
+// address looked up once per device by hipGetSymbolAddress.
+static __device__ __align__(256) unsigned char scratch[KVPOP_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_addr[kMaxDevices];
+std::mutex g_scratch_mu;
+}  // namespace
+
+size_t decode_noalloc_scratch_bytes() { return sizeof(scratch); }
+
+hipError_t decode_noalloc_scratch(hipStream_t st, void** out) {
+  *out = nullptr;
+  int cur = -1;
+  hipError_t e = hipGetDevice(&cur);
+  if (e != hipSuccess) return e;
+  hipDevice_t sdev = cur;
+  e = hipStreamGetDevice(st, &sdev);
+  if (e != hipSuccess) return e;
+  // the address is looked up with the stream's device current; a stream of
+  // another device is refused rather than switching devices under the caller
+  if ((int)sdev != cur || cur < 0 || cur >= kMaxDevices) return hipErrorInvalidDevice;
+  void* p = g_scratch_addr[cur].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    p = g_scratch_addr[cur].load(std::memory_order_relaxed);
+    if (!p) {
+      e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      if (e != hipSuccess || !p) return e != hipSuccess ? e : hipErrorInvalidSymbol;
+      g_scratch_addr[cur].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return hipSuccess;
 }
 
 }  // namespace kvpop

@@ -66,6 +66,11 @@ size_t decode_ws_bytes(const Dims& d);
 hipError_t launch_decode(const Dims& d, const CacheArgs& c, const int* pos, const void* q,
                          const void* k_new, const void* v_new, const float* prio_leaving,
                          void* o, float* lse, void* ws, hipStream_t st);
+// The fixed device scratch of the no-allocation decode entry point: its size,
+// and its device address on the device of stream `st` (which must be the
+// current device; hipErrorInvalidDevice otherwise).
+size_t decode_noalloc_scratch_bytes();
+hipError_t decode_noalloc_scratch(hipStream_t st, void** out);
 
 hipError_t launch_cache_from_prefill(const Dims& d, const CacheArgs& c, const void* k,
                                      const void* v, const float* prio, const int* rank,

@@ -42,15 +42,20 @@
 extern "C" {
 #endif
 
-#define KVPOP_ABI_VERSION 4
+#define KVPOP_ABI_VERSION 5
 
 typedef enum {
   KVPOP_OK = 0,
   KVPOP_ERR_ARG = 1,          /* invalid argument (shape, NULL pointer, budget) */
   KVPOP_ERR_UNSUPPORTED = 2,  /* valid but outside what the kernels implement  */
   KVPOP_ERR_WORKSPACE = 3,    /* ws_bytes smaller than kvpop_workspace_size()   */
-  KVPOP_ERR_HIP = 4           /* a kernel launch failed                          */
+  KVPOP_ERR_HIP = 4,          /* a kernel launch failed                          */
+  KVPOP_ERR_SCRATCH = 5       /* kvpop_decode_step_noalloc: the problem needs more
+                                 than KVPOP_NOALLOC_SCRATCH_BYTES of scratch    */
 } kvpop_status;
+
+/* Size of the fixed device scratch of kvpop_decode_step_noalloc (per GPU). */
+#define KVPOP_NOALLOC_SCRATCH_BYTES (8u << 20)
 
 typedef enum { KVPOP_BF16 = 0, KVPOP_F32 = 1 } kvpop_dtype;
 
@@ -186,6 +191,28 @@ kvpop_status kvpop_decode_step(const kvpop_problem* pr, const kvpop_cache* cache
                                const void* k_new, const void* v_new,
                                const float* prio_leaving, void* o, float* lse,
                                void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* kvpop_decode_step without a workspace argument and without any device
+ * allocation, for callers that cannot allocate: code being captured into a
+ * HIP graph, tight per-token serving loops, harnesses that forbid hipMalloc.
+ * Same arguments, kernels, results and cache update as kvpop_decode_step
+ * (bit for bit).  The split-K partials that kvpop_decode_step keeps in `ws`
+ * live instead in a fixed array of KVPOP_NOALLOC_SCRATCH_BYTES (8 MiB) in
+ * device memory, one per GPU, held from the library's first call on that GPU
+ * until the process ends; a problem needing more (kvpop_workspace_size of
+ * KVPOP_CALL_DECODE above that size: only very small pair counts with large
+ * query groups) returns KVPOP_ERR_SCRATCH and launches nothing.  Nothing in
+ * the array has to start at any value (every word a step reads is written
+ * earlier in the same step), but every call on one GPU shares it: calls that
+ * overlap in time on one GPU (two streams, two threads) race and must be
+ * ordered by the caller.  When the problem uses scratch (several splits),
+ * `stream` must belong to the current device (KVPOP_ERR_HIP otherwise), and
+ * the first such call on a device looks the array's address up once (no
+ * allocation). */
+kvpop_status kvpop_decode_step_noalloc(const kvpop_problem* pr, const kvpop_cache* cache,
+                                       const int32_t* pos, const void* q, const void* k_new,
+                                       const void* v_new, const float* prio_leaving, void* o,
+                                       float* lse, hipStream_t stream);
 
 /* Prefill -> decode handoff ([Notes] §2.3: inference keeps only the compact
  * cache; after a prompt it holds the kept set of the prompt's last row under

@@ -26,7 +26,7 @@ def test_header_symbols_exported():
     assert declared == set(kv.EXPORTED_SYMBOLS)
     for name in declared:
         assert hasattr(L, name), name
-    assert kv.abi_version() == 4
+    assert kv.abi_version() == 5
     assert L.kvpop_status_string(3).decode() == "workspace too small"
 
 
@@ -93,6 +93,32 @@ def test_error_paths_return_before_launch():
                                vp(256), 1 << 40, vp(0)) == 1
     assert L.kvpop_decode_step(ctypes.byref(c), ctypes.byref(cache), *[vp(1)] * 7, vp(256), 16,
                                vp(0)) == 3
+
+
+def test_decode_noalloc_error_paths():
+    """The no-allocation decode refuses, before touching the device, problems
+    whose split-K scratch exceeds its fixed array, and invalid arguments."""
+    L = _lib()
+    vp = ctypes.c_void_p
+    cache = B._Cache(1, 1, 1, 1, 1)
+    # one (sequence, KV head) pair with a 32-head query group and a 2^24-token
+    # budget: 511 splits x 32 heads x 130 floats > 8 MiB
+    big = _pr(n_q_heads=32, n_kv_heads=1, topk=1 << 24)
+    assert kv.workspace_size(B.CALL_DECODE, big) > 8 << 20
+    c = big.c()
+    assert L.kvpop_decode_step_noalloc(ctypes.byref(c), ctypes.byref(cache), *[vp(1)] * 7,
+                                       vp(0)) == 5
+    assert L.kvpop_status_string(5).decode().startswith("problem exceeds the fixed scratch")
+    # the benchmark's long-context decode fits (8 sequences, B = 4096)
+    long8 = _pr(batch=8, window=1024, topk=3056)
+    assert 0 < kv.workspace_size(B.CALL_DECODE, long8) <= 8 << 20
+    c = _pr().c()
+    assert L.kvpop_decode_step_noalloc(ctypes.byref(c), None, *[vp(1)] * 7, vp(0)) == 1
+    assert L.kvpop_decode_step_noalloc(ctypes.byref(c), ctypes.byref(cache), *[vp(1)] * 5, vp(0),
+                                       vp(1), vp(0)) == 1
+    c = _pr(window=0).c()
+    assert L.kvpop_decode_step_noalloc(ctypes.byref(c), ctypes.byref(cache), *[vp(1)] * 7,
+                                       vp(0)) == 1
 
 
 def test_label_error_paths():
