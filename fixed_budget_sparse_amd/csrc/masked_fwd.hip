@@ -20,8 +20,12 @@
 //    row, as the interval test t <= q <= q_end(t) (q_end from a small
 //    pre-pass: tau never increases with q, so the rows that keep a token are
 //    one interval), online softmax in the exp2
-//    domain, and O^T = V^T P^T with V staged transposed, so P feeds the second
-//    MFMA straight from registers and O stays row-per-lane.
+//    domain, and O^T = V^T P^T, so P feeds the second MFMA straight from
+//    registers and O stays row-per-lane.  V is gathered like K (16 lanes per
+//    256-byte row, coalesced) and kept row-major in LDS with its 16-byte
+//    pieces XOR-swizzled by row; the V^T operand is read with gfx950's
+//    transposing LDS load (ds_read_b64_tr_b16), which hands each lane four
+//    consecutive keys of one dim, so no lane shuffles or pairs rows itself.
 //  * float32 inputs use v_mfma_f32_32x32x2_f32 with the same lane layouts.
 #include <type_traits>
 
@@ -166,13 +170,59 @@ __global__ __launch_bounds__(256) void tile_list_kernel(const int* __restrict__ 
 // LDS geometry
 template <int D, bool kF32>
 struct FwdLds {
-  // bf16: K row-major [64][D+8]; V transposed [D][64+8] with permuted columns
+  // bf16: K row-major [64][D+8]; V row-major [64][D], 16-byte pieces swizzled
   // f32:  K row-major [64][D+1]; V row-major [64][D+4]
   static constexpr int KS = kF32 ? D + 1 : D + 8;
-  static constexpr int VS = kF32 ? D + 4 : kChunk + 8;
+  static constexpr int VS = kF32 ? D + 4 : D;
   static constexpr int kBytes = kF32 ? kChunk * KS * 4 : kChunk * KS * 2;
-  static constexpr int vBytes = kF32 ? kChunk * VS * 4 : D * VS * 2;
+  static constexpr int vBytes = kF32 ? kChunk * VS * 4 : kChunk * VS * 2;
 };
+
+typedef short short4v __attribute__((ext_vector_type(4)));
+
+// Byte offset of 16-byte piece `piece` of key row `key` in a bf16 V chunk.
+// The piece index is XORed with a function of the row that stays inside the
+// row (D = 128: 16 pieces, XOR 4 (key mod 4); D = 64: 8 pieces, XOR
+// 4 ((key / 2) mod 2)), so that the transposed reads below, where a half wave
+// reads 32- or 64-byte runs of four consecutive rows, touch 64 distinct banks.
+template <int D>
+__device__ __forceinline__ int v_piece_offset(int key, int piece) {
+  const int sw = D == 128 ? 4 * (key & 3) : 4 * ((key >> 1) & 1);
+  return key * (D * 2) + ((piece ^ sw) << 4);
+}
+
+// Per-lane byte offsets, one per 32-dim output block db, of the transposed
+// V^T operand reads.  ds_read_b64_tr_b16 gives lane i of a 16-lane group
+// element (i mod 4) of the 64-bit words read by lanes 4e + i/4 (e = 0..3) of
+// the group (checked on the device).  Lane j of the group reading row
+// key0 + j/4, dims d0 + 4(j mod 4) .. +3 therefore receives
+// V[key0 + e][d0 + i] for e = 0..3: four consecutive keys of one dim.  For
+// lane (li, hh) of the wave: key0 = 16 ks + 8 a + 4 hh, d0 = 32 db + 16 (li/16),
+// so the pair of reads (a = 0, 1) is the MFMA operand element 4a + r =
+// V[16 ks + 8 a + 4 hh + r][32 db + li], the key order of the P operand.
+template <int D>
+__device__ __forceinline__ void v_tr_offsets(int lane, int (&off)[D / 32]) {
+  const int hh = lane >> 5, li = lane & 31;
+  const int half = li >> 4, j = li & 15, jq = j >> 2;
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) {
+    const int dim = 32 * db + 16 * half + 4 * (j & 3);
+    off[db] = v_piece_offset<D>(4 * hh + jq, dim >> 3) + (dim & 7) * 2;
+  }
+}
+
+// V^T operand (output block db, k-step ks) from a bf16 V chunk at `vb`.
+template <int D>
+__device__ __forceinline__ bf16x8 v_tr_operand(const unsigned char* vb, const int (&off)[D / 32],
+                                               int db, int ks) {
+  typedef __attribute__((address_space(3))) short4v lds_s4;
+  const unsigned char* p = vb + off[db] + 16 * ks * (D * 2);
+  const short4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)(p));
+  const short4v hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)(p + 8 * (D * 2)));
+  typedef short short8v __attribute__((ext_vector_type(8)));
+  const short8v v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  return __builtin_bit_cast(bf16x8, v);
+}
 
 template <int D, bool kF32In, bool kF32Out>
 __global__ __launch_bounds__(kThreads, 1) void masked_fwd_kernel(FwdArgs a) {
@@ -295,18 +345,19 @@ __global__ __launch_bounds__(kThreads, 1) void masked_fwd_kernel(FwdArgs a) {
   };
 
   // ---- gathers: HBM -> registers -> LDS.  K of chunk j is staged two
-  // chunks ahead, V (transposed) one chunk ahead.
+  // chunks ahead, V one chunk ahead; both coalesced (consecutive lanes read
+  // consecutive 16-byte pieces of one row).
   constexpr int PPR = kF32In ? D / 4 : D / 8;            // 16-byte pieces per row
-  constexpr int KP = kChunk * PPR / kThreads;            // K (or f32 V) pieces per thread
-  // bf16 V^T tasks: (key pair, 8-dim octet); two 16-byte row loads each
-  constexpr int NVT = 32 * (D / 8);
-  constexpr int VT = kF32In ? 1 : (NVT + kThreads - 1) / kThreads;  // per thread
+  constexpr int KP = kChunk * PPR / kThreads;            // K (or V) pieces per thread
+  static_assert(kChunk * PPR % kThreads == 0, "pieces per thread");
   // native 4-wide vectors: HIP's uint4 arrays captured by the lambdas below
   // were placed in scratch memory
   typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
   u32x4v kst[KP];
-  u32x4v vst4[kF32In ? KP : 1];
-  u32x4v vpair[kF32In ? 1 : 2 * VT];
+  u32x4v vst4[KP];
+  // per-lane offsets of the transposed V^T operand reads (bf16)
+  int vtr_off[D / 32];
+  if constexpr (!kF32In) v_tr_offsets<D>(lane, vtr_off);
   // Padding slots (token -1) load row 0 instead: every such key is masked
   // (its probability is exactly 0), so only finiteness matters, and the loads
   // stay unconditional (no exec-masked branches, all addresses issued at once).
@@ -320,25 +371,12 @@ __global__ __launch_bounds__(kThreads, 1) void masked_fwd_kernel(FwdArgs a) {
     }
   };
   auto load_v = [&](int db) {
-    if constexpr (!kF32In) {
-      const uint16_t* vg = (const uint16_t*)a.v + kvbase;
+    const unsigned char* vg = (const unsigned char*)a.v + kvbase * (kF32In ? 4 : 2);
 #pragma unroll
-      for (int i = 0; i < VT; ++i) {
-        const int task = tid + i * kThreads;
-        if (NVT % kThreads != 0 && task >= NVT) break;
-        const int pr = task & 31, oc = task >> 5;   // pairs fastest: distinct LDS banks
-        const int t0 = max(kd_t[db][2 * pr], 0), t1 = max(kd_t[db][2 * pr + 1], 0);
-        vpair[2 * i] = *(const u32x4v*)(vg + (size_t)t0 * D + 8 * oc);
-        vpair[2 * i + 1] = *(const u32x4v*)(vg + (size_t)t1 * D + 8 * oc);
-      }
-    } else {
-      const float* vg = (const float*)a.v + kvbase;
-#pragma unroll
-      for (int i = 0; i < KP; ++i) {
-        const int p = tid + i * kThreads;
-        const int t = max(kd_t[db][p / PPR], 0);
-        vst4[i] = *(const u32x4v*)(vg + (size_t)t * D + (p % PPR) * 4);
-      }
+    for (int i = 0; i < KP; ++i) {
+      const int p = tid + i * kThreads;
+      const int t = max(kd_t[db][p / PPR], 0);
+      vst4[i] = *(const u32x4v*)(vg + ((size_t)t * PPR + p % PPR) * 16);
     }
   };
   auto store_k = [&](int kb) {
@@ -358,31 +396,13 @@ __global__ __launch_bounds__(kThreads, 1) void masked_fwd_kernel(FwdArgs a) {
     }
   };
   auto store_v = [&](int vb) {
-    if constexpr (!kF32In) {
-      uint16_t* vl = (uint16_t*)v_lds[vb];
-      // V^T: column c = 16*ks + 8*hh + 4*a + r of LDS row d holds key
-      // 16*ks + 8*a + 4*hh + r of the chunk (the P operand layout); a key pair
-      // (2pr, 2pr+1) lands in two adjacent columns, so each dim is one word
 #pragma unroll
-      for (int i = 0; i < VT; ++i) {
-        const int task = tid + i * kThreads;
-        if (NVT % kThreads != 0 && task >= NVT) break;
-        const int pr = task & 31, oc = task >> 5;
-        const int j0 = 2 * pr;
-        const int c0 = 16 * (j0 >> 4) + 8 * ((j0 >> 2) & 1) + 4 * ((j0 >> 3) & 1) + (j0 & 3);
-        const u32x4v x0 = vpair[2 * i], x1 = vpair[2 * i + 1];
-        uint16_t* col = vl + (8 * oc) * L::VS + c0;
-#pragma unroll
-        for (int dp = 0; dp < 4; ++dp) {
-          *(uint32_t*)(col + (2 * dp) * L::VS) = (x0[dp] & 0xffffu) | (x1[dp] << 16);
-          *(uint32_t*)(col + (2 * dp + 1) * L::VS) = (x0[dp] >> 16) | (x1[dp] & 0xffff0000u);
-        }
-      }
-    } else {
-      float* vl = (float*)v_lds[vb];
-#pragma unroll
-      for (int i = 0; i < KP; ++i) {
-        const int p = tid + i * kThreads;
+    for (int i = 0; i < KP; ++i) {
+      const int p = tid + i * kThreads;
+      if constexpr (!kF32In) {
+        *(u32x4v*)(v_lds[vb] + v_piece_offset<D>(p / PPR, p % PPR)) = vst4[i];
+      } else {
+        float* vl = (float*)v_lds[vb];
         *(u32x4v*)(vl + (p / PPR) * L::VS + (p % PPR) * 4) = vst4[i];
       }
     }
@@ -480,12 +500,10 @@ __global__ __launch_bounds__(kThreads, 1) void masked_fwd_kernel(FwdArgs a) {
   auto pv = [&](int vb, const POp (&pk)[NP]) {
     if constexpr (!kF32In) {
 #pragma unroll
-      for (int d2 = 0; d2 < D / 32; ++d2) {
-        const uint16_t* vl = (const uint16_t*)v_lds[vb] + (32 * d2 + li) * L::VS + 8 * hh;
+      for (int d2 = 0; d2 < D / 32; ++d2)
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks)
-          oacc[d2] = mfma32x32x16(as_bf16x8(*(const uint4*)(vl + 16 * ks)), pk[ks], oacc[d2]);
-      }
+          oacc[d2] = mfma32x32x16(v_tr_operand<D>(v_lds[vb], vtr_off, d2, ks), pk[ks], oacc[d2]);
     } else {
 #pragma unroll
       for (int d2 = 0; d2 < D / 32; ++d2) {
@@ -519,12 +537,11 @@ __global__ __launch_bounds__(kThreads, 1) void masked_fwd_kernel(FwdArgs a) {
                     POp (&pkc)[NP], int vb, float& ps, int kb_st, int vb_st) {
     if constexpr (!kF32In) {
       const uint16_t* kl = (const uint16_t*)k_lds[kb] + li * L::KS + 8 * hh;
-      const uint16_t* vl = (const uint16_t*)v_lds[vb] + li * L::VS + 8 * hh;
       auto rk = [&](int i) {   // QK operand i: block i & 1, k-step i >> 1
         return as_bf16x8(*(const uint4*)(kl + (i & 1) * 32 * L::KS + 16 * (i >> 1)));
       };
       auto rv = [&](int j) {   // PV operand j: output block j % NB, k-step j / NB
-        return as_bf16x8(*(const uint4*)(vl + (j % NB) * 32 * L::VS + 16 * (j / NB)));
+        return v_tr_operand<D>(v_lds[vb], vtr_off, j % NB, j / NB);
       };
       auto pack = [&](int pidx) {
         const f32x16& src = sc[pidx >> 1];
