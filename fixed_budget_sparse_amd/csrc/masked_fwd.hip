@@ -170,15 +170,26 @@ __global__ __launch_bounds__(256) void tile_list_kernel(const int* __restrict__ 
 // LDS geometry
 template <int D, bool kF32>
 struct FwdLds {
-  // bf16: K row-major [64][D+8]; V row-major [64][D], 16-byte pieces swizzled
+  // bf16: K and V row-major [64][D], 16-byte pieces XOR-swizzled by row
   // f32:  K row-major [64][D+1]; V row-major [64][D+4]
-  static constexpr int KS = kF32 ? D + 1 : D + 8;
+  static constexpr int KS = kF32 ? D + 1 : D;
   static constexpr int VS = kF32 ? D + 4 : D;
   static constexpr int kBytes = kF32 ? kChunk * KS * 4 : kChunk * KS * 2;
   static constexpr int vBytes = kF32 ? kChunk * VS * 4 : kChunk * VS * 2;
 };
 
 typedef short short4v __attribute__((ext_vector_type(4)));
+
+// Byte offset of 16-byte piece `piece` of key row `key` in a bf16 K chunk.
+// The QK operand read has the 16 lanes served together read one piece of 16
+// consecutive rows; XORing the piece index with key mod 16 (D = 128) or
+// (key / 2) mod 8 (D = 64, where two rows share a 64-bank line) spreads them
+// over all 64 banks.
+template <int D>
+__device__ __forceinline__ int k_piece_offset(int key, int piece) {
+  const int sw = D == 128 ? (key & 15) : ((key >> 1) & 7);
+  return key * (D * 2) + ((piece ^ sw) << 4);
+}
 
 // Byte offset of 16-byte piece `piece` of key row `key` in a bf16 V chunk.
 // The piece index is XORed with a function of the row that stays inside the
@@ -227,8 +238,27 @@ __device__ __forceinline__ bf16x8 v_tr_operand(const unsigned char* vb, const in
 template <int D, bool kF32In, bool kF32Out>
 __global__ __launch_bounds__(kThreads, 1) void masked_fwd_kernel(FwdArgs a) {
   using L = FwdLds<D, kF32In>;
-  __shared__ __attribute__((aligned(16))) unsigned char k_lds[2][L::kBytes];
-  __shared__ __attribute__((aligned(16))) unsigned char v_lds[2][L::vBytes];
+  // two K and two V buffers as separate arrays: the bf16 pipeline names each
+  // by a compile-time index, so the compiler can tell that the direct loads
+  // into one buffer never alias the reads of the other and need not wait for
+  // them before every LDS read
+  __shared__ __attribute__((aligned(16))) unsigned char k_lds0[L::kBytes];
+  __shared__ __attribute__((aligned(16))) unsigned char k_lds1[L::kBytes];
+  __shared__ __attribute__((aligned(16))) unsigned char v_lds0[L::vBytes];
+  __shared__ __attribute__((aligned(16))) unsigned char v_lds1[L::vBytes];
+  // buffer i: a run-time int (float32 path) or a std::integral_constant
+  auto kbuf = [&](auto i) -> unsigned char* {
+    if constexpr (std::is_integral<decltype(i)>::value) return i ? k_lds1 : k_lds0;
+    else if constexpr (decltype(i)::value == 0) return k_lds0;
+    else return k_lds1;
+  };
+  auto vbuf = [&](auto i) -> unsigned char* {
+    if constexpr (std::is_integral<decltype(i)>::value) return i ? v_lds1 : v_lds0;
+    else if constexpr (decltype(i)::value == 0) return v_lds0;
+    else return v_lds1;
+  };
+  using C0 = std::integral_constant<int, 0>;
+  using C1 = std::integral_constant<int, 1>;
   __shared__ __attribute__((aligned(16))) int kd_t[kDesc][kChunk];
   __shared__ __attribute__((aligned(16))) int kd_r[kDesc][kChunk];
   __shared__ int s_flag[kDesc];
@@ -344,25 +374,57 @@ __global__ __launch_bounds__(kThreads, 1) void masked_fwd_kernel(FwdArgs a) {
     }
   };
 
-  // ---- gathers: HBM -> registers -> LDS.  K of chunk j is staged two
-  // chunks ahead, V one chunk ahead; both coalesced (consecutive lanes read
-  // consecutive 16-byte pieces of one row).
+  // ---- gathers of K and V rows.  bf16: direct loads from global memory into
+  // LDS (global_load_lds_dwordx4), no registers and no LDS store
+  // instructions: K of chunk c+2 and V of chunk c are issued at the start of
+  // iteration c into the buffers the previous iteration finished reading, and
+  // awaited only before the iteration's closing barrier.  Each instruction
+  // fills 1 KB of LDS (lane L writes bytes 16L .. 16L+15 of its block, checked
+  // on the device), i.e. 1024 / (2 D) rows; lane L fetches the global piece
+  // that the row's swizzle places at its slot.  float32: registers -> LDS,
+  // K two chunks ahead, V one chunk ahead.
   constexpr int PPR = kF32In ? D / 4 : D / 8;            // 16-byte pieces per row
-  constexpr int KP = kChunk * PPR / kThreads;            // K (or V) pieces per thread
+  constexpr int KP = kChunk * PPR / kThreads;            // f32 pieces per thread
   static_assert(kChunk * PPR % kThreads == 0, "pieces per thread");
+  constexpr int RPI = 512 / D;                           // rows per 1 KB direct load
+  constexpr int NDMA = kChunk / RPI / (kThreads / 64);   // direct loads per wave per chunk
+  static_assert(kF32In || NDMA * RPI * (kThreads / 64) == kChunk, "direct-load tiling");
   // native 4-wide vectors: HIP's uint4 arrays captured by the lambdas below
   // were placed in scratch memory
   typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
-  u32x4v kst[KP];
-  u32x4v vst4[KP];
-  // per-lane offsets of the transposed V^T operand reads (bf16)
+  u32x4v kst[kF32In ? KP : 1];
+  u32x4v vst4[kF32In ? KP : 1];
+  // per-lane offsets of the transposed V^T operand reads and of the swizzled
+  // K operand reads (bf16: row li, piece 2 ks + hh)
   int vtr_off[D / 32];
-  if constexpr (!kF32In) v_tr_offsets<D>(lane, vtr_off);
+  int k_off[NKS];
+  if constexpr (!kF32In) {
+    v_tr_offsets<D>(lane, vtr_off);
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) k_off[ks] = k_piece_offset<D>(li, 2 * ks + hh);
+  }
   // Padding slots (token -1) load row 0 instead: every such key is masked
   // (its probability is exactly 0), so only finiteness matters, and the loads
   // stay unconditional (no exec-masked branches, all addresses issued at once).
+  typedef __attribute__((address_space(3))) void lds_void;
+  auto dma_rows = [&](const void* src, unsigned char* dst, int db, bool is_k) {
+    const unsigned char* g = (const unsigned char*)src + kvbase * 2;
+#pragma unroll
+    for (int i = 0; i < NDMA; ++i) {
+      const int r0 = (wave * NDMA + i) * RPI;      // first row of this 1 KB block
+      const int row = r0 + lane / PPR, slot = lane % PPR;
+      const int t = max(kd_t[db][row], 0);
+      const int sw = is_k ? k_piece_offset<D>(row, slot) : v_piece_offset<D>(row, slot);
+      const int piece = (sw >> 4) & (PPR - 1);     // the logical piece stored at this slot
+      __builtin_amdgcn_global_load_lds((const void*)(g + ((size_t)t * PPR + piece) * 16),
+                                       (lds_void*)(dst + r0 * (D * 2)), 16, 0, 0);
+    }
+  };
+  auto dma_k = [&](int db, auto kb) { dma_rows(a.k, kbuf(kb), db, true); };
+  auto dma_v = [&](int db, auto vb) { dma_rows(a.v, vbuf(vb), db, false); };
+  auto dma_wait = [] { __builtin_amdgcn_s_waitcnt(0x0F70); };   // vmcnt(0)
   auto load_k = [&](int db) {
-    const unsigned char* kg = (const unsigned char*)a.k + kvbase * (kF32In ? 4 : 2);
+    const unsigned char* kg = (const unsigned char*)a.k + kvbase * 4;
 #pragma unroll
     for (int i = 0; i < KP; ++i) {
       const int p = tid + i * kThreads;
@@ -371,7 +433,7 @@ __global__ __launch_bounds__(kThreads, 1) void masked_fwd_kernel(FwdArgs a) {
     }
   };
   auto load_v = [&](int db) {
-    const unsigned char* vg = (const unsigned char*)a.v + kvbase * (kF32In ? 4 : 2);
+    const unsigned char* vg = (const unsigned char*)a.v + kvbase * 4;
 #pragma unroll
     for (int i = 0; i < KP; ++i) {
       const int p = tid + i * kThreads;
@@ -379,47 +441,38 @@ __global__ __launch_bounds__(kThreads, 1) void masked_fwd_kernel(FwdArgs a) {
       vst4[i] = *(const u32x4v*)(vg + ((size_t)t * PPR + p % PPR) * 16);
     }
   };
-  auto store_k = [&](int kb) {
+  auto store_k = [&](auto kb) {
 #pragma unroll
     for (int i = 0; i < KP; ++i) {
       const int p = tid + i * kThreads;
-      const int key = p / PPR, piece = p % PPR;
-      if constexpr (!kF32In) {
-        *(u32x4v*)((uint16_t*)k_lds[kb] + key * L::KS + piece * 8) = kst[i];
-      } else {
-        float* kd = (float*)k_lds[kb] + key * L::KS + piece * 4;
-        kd[0] = __uint_as_float(kst[i].x);
-        kd[1] = __uint_as_float(kst[i].y);
-        kd[2] = __uint_as_float(kst[i].z);
-        kd[3] = __uint_as_float(kst[i].w);
-      }
+      float* kd = (float*)kbuf(kb) + (p / PPR) * L::KS + (p % PPR) * 4;
+      kd[0] = __uint_as_float(kst[i].x);
+      kd[1] = __uint_as_float(kst[i].y);
+      kd[2] = __uint_as_float(kst[i].z);
+      kd[3] = __uint_as_float(kst[i].w);
     }
   };
-  auto store_v = [&](int vb) {
+  auto store_v = [&](auto vb) {
 #pragma unroll
     for (int i = 0; i < KP; ++i) {
       const int p = tid + i * kThreads;
-      if constexpr (!kF32In) {
-        *(u32x4v*)(v_lds[vb] + v_piece_offset<D>(p / PPR, p % PPR)) = vst4[i];
-      } else {
-        float* vl = (float*)v_lds[vb];
-        *(u32x4v*)(vl + (p / PPR) * L::VS + (p % PPR) * 4) = vst4[i];
-      }
+      float* vl = (float*)vbuf(vb);
+      *(u32x4v*)(vl + (p / PPR) * L::VS + (p % PPR) * 4) = vst4[i];
     }
   };
 
   // ---- S^T = K Q^T for one chunk (32 keys x 32 rows per block, 2 blocks)
-  auto qk = [&](int kb, f32x16 (&acc)[2]) {
+  auto qk = [&](auto kb, f32x16 (&acc)[2]) {
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk) {
       acc[blk] = f32x16{};
       if constexpr (!kF32In) {
-        const uint16_t* kl = (const uint16_t*)k_lds[kb] + (32 * blk + li) * L::KS + 8 * hh;
+        const unsigned char* kl = kbuf(kb) + 32 * blk * (D * 2);
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks)
-          acc[blk] = mfma32x32x16(as_bf16x8(*(const uint4*)(kl + 16 * ks)), qop[ks], acc[blk]);
+          acc[blk] = mfma32x32x16(as_bf16x8(*(const uint4*)(kl + k_off[ks])), qop[ks], acc[blk]);
       } else {
-        const float* kl = (const float*)k_lds[kb] + (32 * blk + li) * L::KS + hh;
+        const float* kl = (const float*)kbuf(kb) + (32 * blk + li) * L::KS + hh;
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks) acc[blk] = mfma32x32x2(kl[2 * ks], qop[ks], acc[blk]);
       }
@@ -497,17 +550,17 @@ __global__ __launch_bounds__(kThreads, 1) void masked_fwd_kernel(FwdArgs a) {
   };
 
   // ---- O^T += V^T P^T
-  auto pv = [&](int vb, const POp (&pk)[NP]) {
+  auto pv = [&](auto vb, const POp (&pk)[NP]) {
     if constexpr (!kF32In) {
 #pragma unroll
       for (int d2 = 0; d2 < D / 32; ++d2)
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks)
-          oacc[d2] = mfma32x32x16(v_tr_operand<D>(v_lds[vb], vtr_off, d2, ks), pk[ks], oacc[d2]);
+          oacc[d2] = mfma32x32x16(v_tr_operand<D>(vbuf(vb), vtr_off, d2, ks), pk[ks], oacc[d2]);
     } else {
 #pragma unroll
       for (int d2 = 0; d2 < D / 32; ++d2) {
-        const float* vl = (const float*)v_lds[vb] + 32 * d2 + li;
+        const float* vl = (const float*)vbuf(vb) + 32 * d2 + li;
 #pragma unroll
         for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
@@ -533,15 +586,15 @@ __global__ __launch_bounds__(kThreads, 1) void masked_fwd_kernel(FwdArgs a) {
   constexpr int NPV = NB * 4;           // PV MFMAs per chunk
   constexpr int EPM = 32 / NQM;         // exps per slot
   static_assert(kF32In || (NQM == NPV && NQM >= 4 && 32 % NQM == 0), "slot schedule");
-  auto region = [&](int kb, f32x16 (&nx)[2], f32x16 (&sc)[2], float mb, const POp (&pkp)[NP],
-                    POp (&pkc)[NP], int vb, float& ps, int kb_st, int vb_st) {
+  auto region = [&](auto kb, f32x16 (&nx)[2], f32x16 (&sc)[2], float mb, const POp (&pkp)[NP],
+                    POp (&pkc)[NP], auto vb, float& ps) {
     if constexpr (!kF32In) {
-      const uint16_t* kl = (const uint16_t*)k_lds[kb] + li * L::KS + 8 * hh;
+      const unsigned char* kl = kbuf(kb);
       auto rk = [&](int i) {   // QK operand i: block i & 1, k-step i >> 1
-        return as_bf16x8(*(const uint4*)(kl + (i & 1) * 32 * L::KS + 16 * (i >> 1)));
+        return as_bf16x8(*(const uint4*)(kl + (i & 1) * 32 * (D * 2) + k_off[i >> 1]));
       };
       auto rv = [&](int j) {   // PV operand j: output block j % NB, k-step j / NB
-        return v_tr_operand<D>(v_lds[vb], vtr_off, j % NB, j / NB);
+        return v_tr_operand<D>(vbuf(vb), vtr_off, j % NB, j / NB);
       };
       auto pack = [&](int pidx) {
         const f32x16& src = sc[pidx >> 1];
@@ -573,8 +626,6 @@ __global__ __launch_bounds__(kThreads, 1) void masked_fwd_kernel(FwdArgs a) {
             const int e = EPM * i + u;
             sc[e >> 4][e & 15] = exp2_fast(fmaf(sc[e >> 4][e & 15], c, mb));
           }
-          if (i == NQM / 4) store_k(kb_st);
-          if (i == NQM / 2) store_v(vb_st);
         }
         if (i > 0) {
 #pragma unroll
@@ -608,64 +659,72 @@ __global__ __launch_bounds__(kThreads, 1) void masked_fwd_kernel(FwdArgs a) {
   if constexpr (!kF32In) {
     // ---- bf16 software pipeline.  Entering iteration c >= 1: the scores of
     // chunk c and P of chunk c-1 are in registers, K(c+1) and V(c-1) are in
-    // LDS, descriptors of c .. c+2 are published.  Per iteration: gathers of
-    // K(c+2) and V(c) and the descriptor reads of chunk c+3 are issued;
-    // mask / max of chunk c (a rescale of O first completes PV(c-1)); the
-    // fused region (QK c+1, exps c, PV c-1, LDS stores of K(c+2) and V(c));
-    // descriptors of chunk c+3; barrier.  Past the last chunk the gathers
-    // and QK run on descriptors of tokens -1 (row 0) and their results are
-    // unused, which keeps the region free of branches.  Unrolled by two so
-    // score and P buffers swap roles without register copies.
-    load_k(0);
-    store_k(0);
-    load_k(1);
-    store_k(1);
+    // LDS, descriptors of c .. c+2 are published.  Per iteration: direct
+    // loads of K(c+2) and V(c) into the buffers read last in iteration c-1,
+    // and the descriptor reads of chunk c+3, are issued; mask / max of chunk
+    // c (a rescale of O first completes PV(c-1)); the fused region (QK c+1,
+    // exps c, PV c-1); descriptors of chunk c+3; the direct loads are
+    // awaited; barrier.  Past the last chunk the loads and QK run on
+    // descriptors of tokens -1 (row 0) and their results are unused, which
+    // keeps the region free of branches.  Unrolled by two so score and P
+    // buffers swap roles without register copies.
+    dma_k(0, C0{});
+    dma_k(1, C1{});
     {   // V buffer 1 starts at zero: iteration 0 runs its PV slots on it
-      uint4* vz = (uint4*)v_lds[1];
+      uint4* vz = (uint4*)vbuf(C1{});
       for (int i = tid; i < (int)(L::vBytes / 16); i += kThreads) vz[i] = make_uint4(0, 0, 0, 0);
     }
+    dma_wait();
     __syncthreads();
-    qk(0, sA);
+    qk(C0{}, sA);
     {   // iteration 0: no PV yet
-      load_k(2 % kDesc);
-      load_v(0);
+      dma_v(0, C0{});
       desc_load(3 * kChunk);
       const float mb = softmax_pre(sA, 0, [] {});
 #pragma unroll
       for (int p = 0; p < NP; ++p) pkB[p] = POp{};
-      // the region stores K(2) over K(0): every wave's qk(0) must have read
-      // it (later iterations overwrite a buffer read before the last barrier)
+      // K(2) goes over K(0): every wave's qk(0) must have read it (later
+      // iterations overwrite a buffer read before the last barrier)
       __syncthreads();
+      dma_k(2 % kDesc, C0{});
       float ps;
-      region(1, sB, sA, mb, pkB, pkA, 1, ps, 0, 0);
+      region(C1{}, sB, sA, mb, pkB, pkA, C1{}, ps);
       l_run += ps;
       desc_store(3 % kDesc);
+      dma_wait();
       __syncthreads();
     }
-    auto step = [&](int c, f32x16 (&cur)[2], f32x16 (&nxt)[2], POp (&pkp)[NP], POp (&pkc)[NP]) {
-      load_k((c + 2) % kDesc);
-      load_v(c % kDesc);
+    // iteration c (parity P = c & 1, a compile-time constant: the loop below
+    // is unrolled by two): loads into buffers P, reads of buffers 1 - P
+    auto step = [&](int c, auto par, f32x16 (&cur)[2], f32x16 (&nxt)[2], POp (&pkp)[NP],
+                    POp (&pkc)[NP]) {
+      constexpr int P = decltype(par)::value;
+      using Cp = std::integral_constant<int, P>;
+      using Cq = std::integral_constant<int, 1 - P>;
+      dma_k((c + 2) % kDesc, Cp{});
+      dma_v(c % kDesc, Cp{});
       desc_load((c + 3) * kChunk);
       // a rescale first completes PV(c-1) and zeroes P(c-1), so the region's
       // PV MFMAs then add exactly 0
       const float mb = softmax_pre(cur, c % kDesc, [&] {
-        pv((c - 1) & 1, pkp);
+        pv(Cq{}, pkp);
 #pragma unroll
         for (int p = 0; p < NP; ++p) pkp[p] = POp{};
       });
       float ps;
-      region((c + 1) & 1, nxt, cur, mb, pkp, pkc, (c - 1) & 1, ps, c & 1, c & 1);
+      region(Cq{}, nxt, cur, mb, pkp, pkc, Cq{}, ps);
       l_run += ps;
       desc_store((c + 3) % kDesc);
+      dma_wait();
       __syncthreads();
     };
     for (int c = 1; c < nchunk; c += 2) {
-      step(c, sB, sA, pkA, pkB);
-      if (c + 1 < nchunk) step(c + 1, sA, sB, pkB, pkA);
+      step(c, C1{}, sB, sA, pkA, pkB);
+      if (c + 1 < nchunk) step(c + 1, C0{}, sA, sB, pkB, pkA);
     }
     // PV of the last chunk (its P is in pkA when its index is even)
-    if ((nchunk - 1) & 1) pv((nchunk - 1) & 1, pkB);
-    else pv((nchunk - 1) & 1, pkA);
+    if ((nchunk - 1) & 1) pv(C1{}, pkB);
+    else pv(C0{}, pkA);
   } else {
     // ---- float32 inputs: K one chunk ahead, V staged with it, steps in order
     load_k(0);
