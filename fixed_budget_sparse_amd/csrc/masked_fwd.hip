@@ -55,25 +55,15 @@ struct FwdArgs {
   float scale_log2;    // softmax scale * log2(e)
 };
 
-// order[rank[t]] = t
-__global__ __launch_bounds__(256) void order_from_rank_kernel(const int* __restrict__ rank,
-                                                              int* __restrict__ order, int S,
-                                                              long long total) {
-  const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
-  if (i >= total) return;
-  const long long seg = i / S;
-  const int t = (int)(i - seg * S);
-  const int r = rank[i];
-  if ((unsigned)r < (unsigned)S) order[seg * S + r] = t;
-}
-
-// q_end(t): the last row that keeps token t.  tau never increases with q, so
-// the rows that keep t are the interval [t, q_end(t)]: S - 1 for a sink or a
-// token whose window reaches the end, t + w - 1 when the token is not kept
-// once it leaves the window, else the last q >= t + w with tau_q >= rank(t),
-// found by bisection.  Row q then keeps t iff t <= q <= q_end(t).
+// Per token t of each (sequence, KV head): order[rank[t]] = t, and q_end(t),
+// the last row that keeps t.  tau never increases with q, so the rows that
+// keep t are the interval [t, q_end(t)]: S - 1 for a sink or a token whose
+// window reaches the end, t + w - 1 when the token is not kept once it
+// leaves the window, else the last q >= t + w with tau_q >= rank(t), found
+// by bisection.  Row q then keeps t iff t <= q <= q_end(t).
 __global__ __launch_bounds__(256) void key_end_kernel(const int* __restrict__ rank,
                                                       const int* __restrict__ tau,
+                                                      int* __restrict__ order,
                                                       int* __restrict__ qend, int S, int s, int w,
                                                       long long total) {
   const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
@@ -81,11 +71,12 @@ __global__ __launch_bounds__(256) void key_end_kernel(const int* __restrict__ ra
   const long long seg = i / S;
   const int t = (int)(i - seg * S);
   const int* tq = tau + seg * S;
+  const int r = rank[i];
+  if ((unsigned)r < (unsigned)S) order[seg * S + r] = t;
   int e;
   if (t < s || t + w > S - 1) {
     e = S - 1;
   } else {
-    const int r = rank[i];
     int lo = t + w, hi = S - 1;
     if (tq[lo] < r) {
       e = t + w - 1;
@@ -102,19 +93,20 @@ __global__ __launch_bounds__(256) void key_end_kernel(const int* __restrict__ ra
 }
 
 // Lists, in rank order, the long-range keys of each tile's first row q0 when
-// its cutoff is finite: tokens t in [s, q0 - w] with rank(t) <= tau_q0.  A
-// round covers 4 x 256 places of the rank order, each wave a contiguous run of
-// 256 of them (four loads in flight per lane, ballots in place order), and
-// ends in one barrier (the wave counts are double-buffered).  Entries are
-// (token, q_end(token)).
-__global__ __launch_bounds__(256) void tile_list_kernel(const int* __restrict__ order,
-                                                        const int* __restrict__ tau,
-                                                        const int* __restrict__ qend, int S,
-                                                        int s, int w, int m, int ntiles, int cap,
-                                                        int2* __restrict__ list,
-                                                        int* __restrict__ count) {
-  constexpr int kU = 4;
-  __shared__ int wsum[2][4];
+// its cutoff is finite: tokens t in [s, q0 - w] with rank(t) <= tau_q0.  The
+// places 0 .. tau_q0 of the rank order (up to the whole sequence for the
+// first tiles, where few tokens are eligible) are split into one contiguous
+// run per wave: a counting pass (eight loads in flight per lane, a ballot per
+// 64 places), one barrier for the prefix over the waves, then a placing pass
+// over the same run.  Entries are (token, q_end(token)).
+constexpr int kListThreads = 512;
+__global__ __launch_bounds__(kListThreads) void tile_list_kernel(
+    const int* __restrict__ order, const int* __restrict__ tau, const int* __restrict__ qend,
+    int S, int s, int w, int m, int ntiles, int cap, int2* __restrict__ list,
+    int* __restrict__ count) {
+  constexpr int kU = 8;
+  constexpr int kWaves = kListThreads / 64;
+  __shared__ int wsum[kWaves];
   const int tile = blockIdx.x, seg = blockIdx.y;
   const int tid = threadIdx.x, lane = lane_id(), wave = wave_id();
   const int q0 = tile * m;
@@ -125,46 +117,51 @@ __global__ __launch_bounds__(256) void tile_list_kernel(const int* __restrict__ 
     if (tid == 0) *cnt_out = 0;
     return;
   }
-  const int scan_end = min(tq0, S - 1);
+  const int n_places = min(tq0, S - 1) + 1;
   const int* ord = order + (size_t)seg * S;
   const int* qe = qend + (size_t)seg * S;
   int2* out = list + ((size_t)seg * ntiles + tile) * cap;
-  int base = 0;
-  for (int i0 = 0, r = 0; i0 <= scan_end; i0 += 256 * kU, ++r) {
-    const int w0 = i0 + wave * 64 * kU;   // this wave's run: places w0 .. w0 + 255
+  // this wave's run of places, a multiple of 64 long
+  const int per = ((n_places + kWaves * 64 - 1) / (kWaves * 64)) * 64;
+  const int r0 = wave * per, r1 = min(r0 + per, n_places);
+  auto eligible = [&](int t) { return t >= s && t <= e_hi; };
+  int wcount = 0;
+  for (int b0 = r0; b0 < r1; b0 += 64 * kU) {
     int t[kU];
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
-      const int i = w0 + 64 * u + lane;
-      t[u] = ord[min(i, scan_end)];
-      if (i > scan_end) t[u] = -1;
-    }
-    uint64_t bal[kU];
-    int wcount = 0;
-#pragma unroll
-    for (int u = 0; u < kU; ++u) {
-      bal[u] = wave_ballot(t[u] >= s && t[u] <= e_hi);
-      wcount += __builtin_popcountll(bal[u]);
-    }
-    if (lane == 0) wsum[r & 1][wave] = wcount;
-    __syncthreads();
-    int pos = base, total = 0;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int c = wsum[r & 1][j];
-      pos += j < wave ? c : 0;
-      total += c;
+      const int i = b0 + 64 * u + lane;
+      t[u] = i < r1 ? ord[i] : -1;
     }
 #pragma unroll
-    for (int u = 0; u < kU; ++u) {
-      const bool keep = t[u] >= s && t[u] <= e_hi;
-      const int at = pos + lanes_below(bal[u]);
-      if (keep && at < cap) out[at] = make_int2(t[u], qe[max(t[u], 0)]);
-      pos += __builtin_popcountll(bal[u]);
-    }
-    base += total;
+    for (int u = 0; u < kU; ++u) wcount += __builtin_popcountll(wave_ballot(eligible(t[u])));
   }
-  if (tid == 0) *cnt_out = min(base, cap);
+  if (lane == 0) wsum[wave] = wcount;
+  __syncthreads();
+  int pos = 0, total = 0;
+#pragma unroll
+  for (int j = 0; j < kWaves; ++j) {
+    const int c = wsum[j];
+    pos += j < wave ? c : 0;
+    total += c;
+  }
+  for (int b0 = r0; b0 < r1; b0 += 64 * kU) {
+    int t[kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int i = b0 + 64 * u + lane;
+      t[u] = i < r1 ? ord[i] : -1;
+    }
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const bool keep = eligible(t[u]);
+      const uint64_t bal = wave_ballot(keep);
+      const int at = pos + lanes_below(bal);
+      if (keep && at < cap) out[at] = make_int2(t[u], qe[t[u]]);
+      pos += __builtin_popcountll(bal);
+    }
+  }
+  if (tid == 0) *cnt_out = min(total, cap);
 }
 
 // LDS geometry
@@ -810,12 +807,10 @@ FwdPlan launch_fwd_plan(const Dims& d, const int* rank, const int* tau, void* ws
 
   const long long total = (long long)nseg * d.S;
   const unsigned nblk = (unsigned)((total + 255) / 256);
-  hipLaunchKernelGGL(order_from_rank_kernel, dim3(nblk), dim3(256), 0, st, rank, order, d.S,
-                     total);
-  hipLaunchKernelGGL(key_end_kernel, dim3(nblk), dim3(256), 0, st, rank, tau, qend, d.S, d.s, d.w,
-                     total);
-  hipLaunchKernelGGL(tile_list_kernel, dim3(nt, nseg), dim3(256), 0, st, order, tau, qend, d.S,
-                     d.s, d.w, m, nt, cap, list, count);
+  hipLaunchKernelGGL(key_end_kernel, dim3(nblk), dim3(256), 0, st, rank, tau, order, qend, d.S,
+                     d.s, d.w, total);
+  hipLaunchKernelGGL(tile_list_kernel, dim3(nt, nseg), dim3(kListThreads), 0, st, order, tau,
+                     qend, d.S, d.s, d.w, m, nt, cap, list, count);
   FwdPlan pl;
   pl.list = list; pl.count = count; pl.qend = qend; pl.m = m; pl.ntiles = nt; pl.cap = cap;
   return pl;
