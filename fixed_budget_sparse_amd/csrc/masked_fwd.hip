@@ -259,9 +259,11 @@ __global__ __launch_bounds__(kThreads, 1) void masked_fwd_kernel(FwdArgs a) {
   __shared__ __attribute__((aligned(16))) int kd_t[kDesc][kChunk];
   __shared__ __attribute__((aligned(16))) int kd_r[kDesc][kChunk];
   __shared__ int s_flag[kDesc];
+  __shared__ int s_redo;   // some row needs the exact (running-maximum) mode
 
   const int tid = threadIdx.x, lane = lane_id(), wave = wave_id();
   const int hh = lane >> 5, li = lane & 31;
+  if (tid == 0) s_redo = 0;   // read only after the barriers that follow
   const int Lb = xcd_logical_block((int)blockIdx.x, (int)gridDim.x);
   const int tile = Lb % a.ntiles;
   const int h = (Lb / a.ntiles) % a.Hkv;
@@ -476,9 +478,9 @@ __global__ __launch_bounds__(kThreads, 1) void masked_fwd_kernel(FwdArgs a) {
     }
   };
 
-  // ---- mask and online-softmax bookkeeping of one chunk (in place on the
-  // scores); returns the exponent bias -m_run * c
-  auto softmax_pre = [&](f32x16 (&sc)[2], int db, auto&& before_rescale) -> float {
+  // ---- the A8 mask of one chunk (in place on the scores), only on chunks
+  // that some row of the tile does not keep wholly
+  auto apply_mask = [&](f32x16 (&sc)[2], int db) {
     const int mclass = __builtin_amdgcn_readfirstlane(s_flag[db]);   // uniform
     if (mclass != 0) {
       // branch-free: one unsigned compare and a select per score (a
@@ -493,15 +495,18 @@ __global__ __launch_bounds__(kThreads, 1) void masked_fwd_kernel(FwdArgs a) {
           sc[blk][e] = keep ? sc[blk][e] : kNegInf;
         }
     }
+  };
+  // ---- online-softmax bookkeeping of one chunk; returns the exponent bias
+  // -m_run * c.  A lazily moved reference max (m_run, raw units) moves only
+  // when some row's max grows by more than 2^8 in the exp2 domain, so the O
+  // rescale is skipped on most chunks; probabilities stay <= 2^8
+  auto update_max = [&](f32x16 (&sc)[2], auto&& before_rescale) -> float {
     float mc = sc[0][0];
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
       for (int e = 0; e < 16; ++e) mc = fmaxf(mc, sc[blk][e]);
     mc = halves_max(mc);
-    // lazily moved reference max (m_run, raw units): it moves only when some
-    // row's max grows by more than 2^8 in the exp2 domain, so the O rescale is
-    // skipped on most chunks; probabilities stay <= 2^8
     const float c = a.scale_log2;
     if (wave_ballot(mc * c > m_run * c + 8.0f) != 0) {
       const float m_new = fmaxf(m_run, mc);
@@ -513,6 +518,10 @@ __global__ __launch_bounds__(kThreads, 1) void masked_fwd_kernel(FwdArgs a) {
       for (int d2 = 0; d2 < D / 32; ++d2) oacc[d2] *= alpha;
     }
     return m_run == kNegInf ? 0.0f : -m_run * c;
+  };
+  auto softmax_pre = [&](f32x16 (&sc)[2], int db, auto&& before_rescale) -> float {
+    apply_mask(sc, db);
+    return update_max(sc, before_rescale);
   };
   // ---- probabilities: exp2, row sum, bf16 pack (straight-line)
   typedef typename std::conditional<kF32In, f32x16, bf16x8>::type POp;
@@ -625,6 +634,8 @@ __global__ __launch_bounds__(kThreads, 1) void masked_fwd_kernel(FwdArgs a) {
           }
         }
         if (i > 0) {
+          // row sums in float32 (summing the bf16-rounded values instead
+          // moves a row dominated by one key by up to 2^-9 relative)
 #pragma unroll
           for (int u = 0; u < EPM; ++u) {
             const int e = EPM * (i - 1) + u;
@@ -645,85 +656,120 @@ __global__ __launch_bounds__(kThreads, 1) void masked_fwd_kernel(FwdArgs a) {
   };
 
   const int nchunk = (nk + kChunk - 1) / kChunk;
+  auto publish_first_descriptors = [&] {
 #pragma unroll
-  for (int j = 0; j < kDesc - 1; ++j) {   // every slot starts valid (tokens -1 past the end)
-    desc_load(j * kChunk);
-    desc_store(j);
-  }
-  __syncthreads();
+    for (int j = 0; j < kDesc - 1; ++j) {   // every slot starts valid (tokens -1 past the end)
+      desc_load(j * kChunk);
+      desc_store(j);
+    }
+    __syncthreads();
+  };
   f32x16 sA[2], sB[2];
   POp pkA[NP], pkB[NP];
+  float l_tot;
   if constexpr (!kF32In) {
     // ---- bf16 software pipeline.  Entering iteration c >= 1: the scores of
     // chunk c and P of chunk c-1 are in registers, K(c+1) and V(c-1) are in
     // LDS, descriptors of c .. c+2 are published.  Per iteration: direct
     // loads of K(c+2) and V(c) into the buffers read last in iteration c-1,
-    // and the descriptor reads of chunk c+3, are issued; mask / max of chunk
-    // c (a rescale of O first completes PV(c-1)); the fused region (QK c+1,
-    // exps c, PV c-1); descriptors of chunk c+3; the direct loads are
-    // awaited; barrier.  Past the last chunk the loads and QK run on
-    // descriptors of tokens -1 (row 0) and their results are unused, which
-    // keeps the region free of branches.  Unrolled by two so score and P
-    // buffers swap roles without register copies.
-    dma_k(0, C0{});
-    dma_k(1, C1{});
-    {   // V buffer 1 starts at zero: iteration 0 runs its PV slots on it
-      uint4* vz = (uint4*)vbuf(C1{});
-      for (int i = tid; i < (int)(L::vBytes / 16); i += kThreads) vz[i] = make_uint4(0, 0, 0, 0);
-    }
-    dma_wait();
-    __syncthreads();
-    qk(C0{}, sA);
-    {   // iteration 0: no PV yet
-      dma_v(0, C0{});
-      desc_load(3 * kChunk);
-      const float mb = softmax_pre(sA, 0, [] {});
-#pragma unroll
-      for (int p = 0; p < NP; ++p) pkB[p] = POp{};
-      // K(2) goes over K(0): every wave's qk(0) must have read it (later
-      // iterations overwrite a buffer read before the last barrier)
-      __syncthreads();
-      dma_k(2 % kDesc, C0{});
-      float ps;
-      region(C1{}, sB, sA, mb, pkB, pkA, C1{}, ps);
-      l_run += ps;
-      desc_store(3 % kDesc);
+    // and the descriptor reads of chunk c+3, are issued; mask of chunk c;
+    // the fused region (QK c+1, exps c, PV c-1); descriptors of chunk c+3;
+    // the direct loads are awaited; barrier.  Past the last chunk the loads
+    // and QK run on descriptors of tokens -1 (row 0) and their results are
+    // unused, which keeps the region free of branches.  Unrolled by two so
+    // score and P buffers swap roles without register copies.
+    //
+    // Two modes.  Fixed reference (first run): each row's maximum over the
+    // first chunk is its reference for the whole tile, so later chunks need
+    // no maximum and O is never rescaled; a probability of up to 2^64 (a
+    // later score up to 64 binary orders above the reference) is harmless in
+    // float32 (sums of thousands of such terms stay far below 2^128, and the
+    // relative precision of every term is unchanged).  A row whose final sum
+    // leaves [2^-64, 2^64] (a larger score, a row with nothing kept in the
+    // first chunk, NaN) makes the workgroup rerun the tile in the exact mode:
+    // the running maximum, moved lazily by more than 2^8, with rescales.
+    auto run = [&](auto exact) {
+      constexpr bool kExact = decltype(exact)::value;
+      publish_first_descriptors();
+      dma_k(0, C0{});
+      dma_k(1, C1{});
+      {   // V buffer 1 starts at zero: iteration 0 runs its PV slots on it
+        uint4* vz = (uint4*)vbuf(C1{});
+        for (int i = tid; i < (int)(L::vBytes / 16); i += kThreads) vz[i] = make_uint4(0, 0, 0, 0);
+      }
       dma_wait();
       __syncthreads();
-    }
-    // iteration c (parity P = c & 1, a compile-time constant: the loop below
-    // is unrolled by two): loads into buffers P, reads of buffers 1 - P
-    auto step = [&](int c, auto par, f32x16 (&cur)[2], f32x16 (&nxt)[2], POp (&pkp)[NP],
-                    POp (&pkc)[NP]) {
-      constexpr int P = decltype(par)::value;
-      using Cp = std::integral_constant<int, P>;
-      using Cq = std::integral_constant<int, 1 - P>;
-      dma_k((c + 2) % kDesc, Cp{});
-      dma_v(c % kDesc, Cp{});
-      desc_load((c + 3) * kChunk);
-      // a rescale first completes PV(c-1) and zeroes P(c-1), so the region's
-      // PV MFMAs then add exactly 0
-      const float mb = softmax_pre(cur, c % kDesc, [&] {
-        pv(Cq{}, pkp);
+      qk(C0{}, sA);
+      float mb0;
+      {   // iteration 0: no PV yet
+        dma_v(0, C0{});
+        desc_load(3 * kChunk);
+        mb0 = softmax_pre(sA, 0, [] {});
 #pragma unroll
-        for (int p = 0; p < NP; ++p) pkp[p] = POp{};
-      });
-      float ps;
-      region(Cq{}, nxt, cur, mb, pkp, pkc, Cq{}, ps);
-      l_run += ps;
-      desc_store((c + 3) % kDesc);
-      dma_wait();
-      __syncthreads();
+        for (int p = 0; p < NP; ++p) pkB[p] = POp{};
+        // K(2) goes over K(0): every wave's qk(0) must have read it (later
+        // iterations overwrite a buffer read before the last barrier)
+        __syncthreads();
+        dma_k(2 % kDesc, C0{});
+        float ps;
+        region(C1{}, sB, sA, mb0, pkB, pkA, C1{}, ps);
+        l_run += ps;
+        desc_store(3 % kDesc);
+        dma_wait();
+        __syncthreads();
+      }
+      // iteration c (parity P = c & 1, a compile-time constant: the loop
+      // below is unrolled by two): loads into buffers P, reads of buffers 1 - P
+      auto step = [&](int c, auto par, f32x16 (&cur)[2], f32x16 (&nxt)[2], POp (&pkp)[NP],
+                      POp (&pkc)[NP]) {
+        constexpr int P = decltype(par)::value;
+        using Cp = std::integral_constant<int, P>;
+        using Cq = std::integral_constant<int, 1 - P>;
+        dma_k((c + 2) % kDesc, Cp{});
+        dma_v(c % kDesc, Cp{});
+        desc_load((c + 3) * kChunk);
+        float mb = mb0;
+        if constexpr (kExact) {
+          // a rescale first completes PV(c-1) and zeroes P(c-1), so the
+          // region's PV MFMAs then add exactly 0
+          mb = softmax_pre(cur, c % kDesc, [&] {
+            pv(Cq{}, pkp);
+#pragma unroll
+            for (int p = 0; p < NP; ++p) pkp[p] = POp{};
+          });
+        } else {
+          apply_mask(cur, c % kDesc);
+        }
+        float ps;
+        region(Cq{}, nxt, cur, mb, pkp, pkc, Cq{}, ps);
+        l_run += ps;
+        desc_store((c + 3) % kDesc);
+        dma_wait();
+        __syncthreads();
+      };
+      for (int c = 1; c < nchunk; c += 2) {
+        step(c, C1{}, sB, sA, pkA, pkB);
+        if (c + 1 < nchunk) step(c + 1, C0{}, sA, sB, pkB, pkA);
+      }
+      // PV of the last chunk (its P is in pkA when its index is even)
+      if ((nchunk - 1) & 1) pv(C1{}, pkB);
+      else pv(C0{}, pkA);
+      l_tot = halves_sum(l_run);
     };
-    for (int c = 1; c < nchunk; c += 2) {
-      step(c, C1{}, sB, sA, pkA, pkB);
-      if (c + 1 < nchunk) step(c + 1, C0{}, sA, sB, pkB, pkA);
+    run(std::false_type{});
+    const bool bad = row_ok && !(l_tot >= 0x1p-64f && l_tot <= 0x1p64f);
+    if (wave_ballot(bad) != 0 && lane == 0) s_redo = 1;
+    __syncthreads();
+    if (s_redo) {
+      m_run = kNegInf;
+      l_run = 0.0f;
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) oacc[db] = f32x16{};
+      run(std::true_type{});
     }
-    // PV of the last chunk (its P is in pkA when its index is even)
-    if ((nchunk - 1) & 1) pv(C1{}, pkB);
-    else pv(C0{}, pkA);
   } else {
     // ---- float32 inputs: K one chunk ahead, V staged with it, steps in order
+    publish_first_descriptors();
     load_k(0);
     load_v(0);
     store_k(0);
@@ -742,10 +788,10 @@ __global__ __launch_bounds__(kThreads, 1) void masked_fwd_kernel(FwdArgs a) {
       desc_store((c + 3) % kDesc);
       __syncthreads();
     }
+    l_tot = halves_sum(l_run);
   }
 
   // ---- epilogue: O = acc / l, LSE = (m + log2 l) ln 2
-  const float l_tot = halves_sum(l_run);
   if (row_ok) {
     const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
     const size_t orow = (((size_t)b * a.Hq + hq) * S + q) * D;

@@ -136,6 +136,37 @@ def test_masked_fwd_parity(case):
     assert torch.equal(lse_bf, lse)
 
 
+def test_masked_fwd_far_logit_reruns_exact():
+    """The forward takes each row's maximum over its first key chunk as the
+    reference for the whole tile and checks the row sums at the end; a kept
+    key whose logit lies about 800 above that reference (far beyond float32's
+    exponent range) makes the tile run again with a running maximum.  Both
+    bf16 and float32 outputs match the oracle (float64)."""
+    device()
+    b, hq, hkv, S, D, s, w, k = 1, 8, 2, 700, 128, 4, 40, 100
+    announce("masked_fwd far logit: exact rerun")
+    q, kk, v, prio = _fwd_inputs(b, hq, hkv, S, D, "bf16", 19)
+    t_star, row = 500, 520                      # in the window of rows 500..539
+    u = q[0, 0, row].astype(np.float64)
+    kk[0, 0, t_star] = (u * (800.0 * np.sqrt(D) / (u @ u))).astype(np.float32)
+    kk = _bf16_exact(kk)
+    td = torch.bfloat16
+    rank, tau = kv.thresholds(to_dev(prio), s, w, k)
+    outs = [kv.masked_attn_fwd(to_dev(q, td), to_dev(kk, td), to_dev(v, td), rank, tau, s, w, k,
+                               out_dtype=dt) for dt in (torch.float32, torch.bfloat16)]
+    torch.cuda.synchronize()
+    rank_o = orc.priority_ranks(prio)
+    tau_o = orc.thresholds_by_selection(rank_o, s, w, k)
+    O, LSE = orc.masked_attention(q, kk, v, rank_o, tau_o, s, w)
+    assert LSE[0, 0, row] > 700
+    for o, lse in outs:
+        og, lg = host(o), host(lse)
+        assert np.isfinite(og).all() and np.isfinite(lg).all()
+        ulp = 2.0 ** (np.floor(np.log2(np.maximum(np.abs(O), 1e-30))) - 8)
+        assert (np.abs(og - O) - ulp).max() <= TOL["bf16"]["o"]
+        assert np.abs(lg - LSE).max() <= TOL["bf16"]["lse"], np.abs(lg - LSE).max()
+
+
 # ---------------------------------------------------------------- target
 TGT_CASES = [
     (1, 2, 1, 512, 64, 32, "f32"),
