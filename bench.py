@@ -154,6 +154,42 @@ def bench_labels(kv, torch, score, s, w, k, ev, reps=5):
             "rows_per_s": round(rows / (ms * 1e-3), 1), "frac_newcomer_kept": round(kept, 4)}
 
 
+def bench_tiny(kv, torch, dev, ev, reps=21):
+    """The tiny float32 layer (S 512, D 64, 2 query / 1 KV head, s 4, w 32,
+    k 64): thresholds, masked forward (float32 MFMA) and future target on the
+    teacher LSE, each timed alone (median of `reps`).  Launch-bound at this
+    size; reported, not a performance target."""
+    from workloads import TINY as wl, make_prefill
+    s, w, k, S, D, Hq = wl.sink, wl.window, wl.topk, wl.seq_len, wl.head_dim, wl.n_q_heads
+    x = make_prefill(wl)
+    q, kk, v, prio = (torch.from_numpy(x[n]).to(dev) for n in ("q", "k", "v", "prio"))
+    f32 = torch.float32
+    rank_d, tau_d = kv.thresholds(prio, s, w, S)
+    _, lse_t = kv.masked_attn_fwd(q, kk, v, rank_d, tau_d, s, w, S, out_dtype=f32)
+    rank, tau = kv.thresholds(prio, s, w, k)
+    o, lse = kv.masked_attn_fwd(q, kk, v, rank, tau, s, w, k, out_dtype=f32)
+    tgt = kv.future_target(q, kk, lse_t, w)
+    calls = {"thresholds": lambda: kv.thresholds(prio, s, w, k, rank=rank, tau=tau),
+             "fwd": lambda: kv.masked_attn_fwd(q, kk, v, rank, tau, s, w, k, out_dtype=f32, o=o,
+                                               lse=lse),
+             "target": lambda: kv.future_target(q, kk, lse_t, w, target=tgt)}
+    out = {"workload": wl.name, "dtype": "f32", "reps": reps}
+    for name, fn in calls.items():
+        ts = []
+        for _ in range(reps):
+            a, b = ev(), ev()
+            a.record()
+            fn()
+            b.record()
+            torch.cuda.synchronize()
+            ts.append(a.elapsed_time(b))
+        out[name + "_us"] = round(sorted(ts)[len(ts) // 2] * 1e3, 1)
+    f_fwd = 4 * D * Hq * fwd_pairs(S, s + w + k)
+    f_tgt = 2 * D * Hq * tgt_pairs(S, w)
+    out["fwd_flop"], out["target_flop"] = f_fwd, f_tgt
+    return out
+
+
 def bench_layer_c3(kv, torch, dev, ev, reps=5):
     """The Qwen3-8B-shaped layer (S 32768, B 4096): thresholds, masked forward
     and target pass, each timed on its own and end to end (teacher LSE from
@@ -344,41 +380,128 @@ def parse():
     return ap.parse_args()
 
 
-def cpu_baseline(x, s, w, k, sample_rows=3072, sample_t=512):
-    """Time the oracle (as it stands) on a bounded sample of the same workload."""
-    import numpy as np
-    import oracle as orc
+def host_description():
+    """The host the oracle runs on: CPU model, logical CPUs, NumPy's BLAS."""
+    info = {"nproc": os.cpu_count()}
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                info["cpu_model"] = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
     try:
         from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+        blas = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        if blas:
+            info["blas"] = {k: blas[0].get(k) for k in ("internal_api", "version", "num_threads",
+                                                        "threading_layer", "architecture")}
     except Exception:  # pragma: no cover
-        cores = os.cpu_count() or 1
-    q, kk, v, prio = x["q"], x["k"], x["v"], x["prio"]
-    S, D, Hq = q.shape[2], q.shape[3], q.shape[1]
-    B = s + w + k
-    rows = np.linspace(0, S - 1, sample_rows).astype(np.int64)
-    # target tokens from the last sixteenth, so the (untimed) teacher LSE is
-    # only needed for the last rows
-    ts = np.linspace(S - S // 16, S - 1 - w, sample_t).astype(np.int64)
-    t0 = time.perf_counter()
-    rank = orc.priority_ranks(prio)
-    tau = orc.thresholds_by_selection(rank, s, w, k, rows=range(S))
-    orc.masked_attention(q, kk, v, rank, tau, s, w, rows=rows)
-    t1 = time.perf_counter()
-    lse_dense = np.zeros((1, Hq, S))
-    need = np.arange(int(ts.min()) + w, S)
-    _, lse_dense[:, :, need] = orc.dense_causal_attention(q, kk, kk, rows=need, block=512)
-    t2 = time.perf_counter()
-    orc.future_target_eq8(q, kk, lse_dense, w, ts=ts)
-    t3 = time.perf_counter()
-    flops = 4 * D * Hq * sum(min(int(r) + 1, B) for r in rows)
-    flops += 2 * D * Hq * sum(S - int(t) - w for t in ts)
-    secs = (t1 - t0) + (t3 - t2)
-    return {"value": flops / secs / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"thresholds for all {S} rows; masked forward on {sample_rows} rows x {Hq} "
-                      f"heads; future target on {sample_t} tokens x {Hq} heads (teacher LSE "
-                      f"untimed); {secs:.1f} s of CPU work",
-            "seconds": round(secs, 2)}
+        pass
+    return info
+
+
+def cpu_baseline(x, s, w, k):
+    """The oracle as it stands (float64 NumPy, one process) timed on the host
+    on a bounded sample of every workload, pass by pass (about 20 s of CPU
+    work): the tiny float32 layer in full; the 16k and 32k layers, the
+    long-context layer and the 64-sequence decode on stated samples.  Each
+    pass reports its algorithmic work and rate; `value` is the 16k layer's
+    forward + target sample (the headline metric's unit)."""
+    import numpy as np
+    import oracle as orc
+    import workloads as W
+    host = host_description()
+    cores = int((host.get("blas") or {}).get("num_threads") or 1)
+    passes = {}
+
+    def timed(fn):
+        t0 = time.perf_counter()
+        r = fn()
+        return r, time.perf_counter() - t0
+
+    def rate(flop, secs):
+        return round(flop / secs / 1e12, 6)
+
+    def prefill(wl, x_, rows_fwd, ts_tgt, label, target=True):
+        S_, D_, Hq_ = x_["q"].shape[2], x_["q"].shape[3], x_["q"].shape[1]
+        s_, w_, k_ = wl.sink, wl.window, wl.topk
+        B_ = s_ + w_ + k_
+        thr_rows = np.arange(S_) if S_ <= 16384 else np.linspace(0, S_ - 1, 2048).astype(np.int64)
+        (rank, _), t_rank = timed(lambda: (orc.priority_ranks(x_["prio"]), None))
+        tau_s, t_tau = timed(lambda: orc.thresholds_by_selection(rank, s_, w_, k_, rows=thr_rows))
+        tau = np.zeros(rank.shape, np.int64)
+        tau[..., thr_rows] = tau_s
+        if S_ > 16384:            # the forward's rows need their own cutoffs
+            tau[..., rows_fwd] = orc.thresholds_by_selection(rank, s_, w_, k_, rows=rows_fwd)
+        _, t_fwd = timed(lambda: orc.masked_attention(x_["q"], x_["k"], x_["v"], rank, tau, s_, w_,
+                                                      rows=rows_fwd))
+        f_fwd = 4 * D_ * Hq_ * sum(min(int(r) + 1, B_) for r in rows_fwd)
+        out = {"thresholds": {"rows": len(thr_rows), "seconds": round(t_rank + t_tau, 3),
+                              "rows_per_s": round(len(thr_rows) / (t_rank + t_tau), 1)},
+               "masked_fwd": {"rows": len(rows_fwd), "heads": Hq_, "seconds": round(t_fwd, 3),
+                              "flop": f_fwd, "TFLOP/s": rate(f_fwd, t_fwd)}}
+        if target:
+            # the teacher LSE of the rows the sampled tokens need (untimed)
+            need = np.arange(int(min(ts_tgt)) + w_, S_)
+            lse = np.zeros((1, Hq_, S_))
+            _, lse[:, :, need] = orc.dense_causal_attention(x_["q"], x_["k"], x_["k"], rows=need,
+                                                           block=512)
+            _, t_tgt = timed(lambda: orc.future_target_eq8(x_["q"], x_["k"], lse, w_, ts=ts_tgt))
+            f_tgt = 2 * D_ * Hq_ * sum(max(0, S_ - int(t) - w_) for t in ts_tgt)
+            out["future_target"] = {"tokens": len(ts_tgt), "heads": Hq_, "seconds": round(t_tgt, 3),
+                                    "flop": f_tgt, "TFLOP/s": rate(f_tgt, t_tgt)}
+        passes[label] = out
+        return out
+
+    # tiny float32 layer: every row and token
+    xt = W.make_prefill(W.TINY)
+    St = W.TINY.seq_len
+    prefill(W.TINY, xt, np.arange(St), np.arange(St - W.TINY.window), W.TINY.name)
+    # 16k layer (the step's inputs): 1536 forward rows, 1024 target tokens
+    # among the last 2048 that have future queries
+    S = x["q"].shape[2]
+    r16 = prefill(W.QWEN3_4B_S16K, x, np.linspace(0, S - 1, 1536).astype(np.int64),
+                  np.linspace(S - w - 2048, S - 1 - w, 1024).astype(np.int64), W.QWEN3_4B_S16K.name)
+    # 32k layer and long context: one KV head with its 4 query heads (the same
+    # recipe), cutoffs of 2048 sampled rows, 576 / 144 forward rows
+    for wl_, nrows in ((W.QWEN3_8B_S32K, 576), (W.LONG_S128K, 144)):
+        one = W.scaled(wl_, n_q_heads=wl_.group, n_kv_heads=1)
+        xs = W.make_prefill(one)
+        Sx = one.seq_len
+        prefill(one, xs, np.linspace(0, Sx - 1, nrows).astype(np.int64), None,
+                wl_.name + " (one KV head)", target=False)
+        del xs
+    # decode: one (sequence, KV head) simulated over 3072 positions (the cache
+    # fills at 2048), and the attention of one sequence's 32 query heads at 96
+    # of those steps
+    wd = W.DECODE_B2048
+    n_steps, D, Hq, Hkv = 3072, wd.head_dim, wd.n_q_heads, wd.n_kv_heads
+    table = W.make_decode_prio_table(wd, n_tokens=n_steps, batch=1)
+    _, t_sim = timed(lambda: orc.decode_simulate(table[0, 0], wd.sink, wd.window, wd.topk,
+                                                 n_steps, record=[]))
+    rng = np.random.default_rng(7)
+    kt = rng.standard_normal((Hkv, n_steps, D)).astype(np.float32)
+    vt = rng.standard_normal((Hkv, n_steps, D)).astype(np.float32)
+    steps = np.linspace(wd.budget, n_steps - 1, 96).astype(int)
+    held, _ = orc.decode_simulate(table[0, 0], wd.sink, wd.window, wd.topk, n_steps, record=steps)
+    qd = rng.standard_normal((Hq, D)).astype(np.float32)
+    _, t_att = timed(lambda: [orc.decode_attention(qd, kt, vt, [held[p]] * Hkv) for p in steps])
+    bytes_att = 2 * Hkv * wd.budget * D * 2 * len(steps)
+    passes[wd.name] = {"membership": {"positions": n_steps, "seconds": round(t_sim, 3),
+                                      "steps_per_s": round(n_steps / t_sim, 1)},
+                       "attention": {"steps": len(steps), "sequences": 1, "seconds": round(t_att, 3),
+                                     "cache_bytes": bytes_att,
+                                     "GB/s": round(bytes_att / t_att / 1e9, 4)}}
+    f16 = r16["masked_fwd"]["flop"] + r16["future_target"]["flop"]
+    t16 = r16["masked_fwd"]["seconds"] + r16["future_target"]["seconds"]
+    total = sum(v["seconds"] for p in passes.values() for v in p.values())
+    return {"value": f16 / t16 / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": "16k layer: masked forward on 1536 rows x 32 heads and future target on 1024 "
+                      "tokens x 32 heads (teacher LSE untimed); every pass of every workload in "
+                      f"`passes`; {total:.1f} s of CPU work in all",
+            "precision": "float64 (the oracle's arithmetic)", "host": host, "passes": passes,
+            "seconds": round(total, 2)}
 
 
 def main():
@@ -470,20 +593,24 @@ def main():
         step_ev.append(e0.elapsed_time(e3))
     ms_step = wall * 1e3 / args.steps
     # after the timed region: the forward and the target each alone on the
-    # chip (in the step they share it), 10 launches each
+    # chip (in the step they share it): 7 batches of 10 back-to-back calls,
+    # the median batch's time per call
     iso = {}
     alone = (("fwd", lambda: kv.masked_attn_fwd(q, kk, v, rank, tau, s, w, k, out_dtype=bf,
                                                 o=o, lse=lse)),
              ("tgt", lambda: kv.future_target(q, kk, lse_teacher, w, target=tgt)))
     for name, fn in alone if args.isolated else ():
         fn()
-        ea, eb = ev(), ev()
-        ea.record()
-        for _ in range(10):
-            fn()
-        eb.record()
-        torch.cuda.synchronize()
-        iso[name] = ea.elapsed_time(eb) / 10
+        per = []
+        for _ in range(7):
+            ea, eb = ev(), ev()
+            ea.record()
+            for _ in range(10):
+                fn()
+            eb.record()
+            torch.cuda.synchronize()
+            per.append(ea.elapsed_time(eb) / 10)
+        iso[name] = sorted(per)[len(per) // 2]
     # the target score per KV head, timed alone, then the sparse-LSE study
     # (untimed): `lse` holds the last step's sparse LSE, `tgt` the exact target
     eps = 1e-6
@@ -504,6 +631,7 @@ def main():
     f_fwd = 4 * D * Hq * fwd_pairs(S, B)
     f_tgt = 2 * D * Hq * tgt_pairs(S, w)
     avg = {n: sum(t) / len(t) for n, t in times.items()}
+    med = {n: sorted(t)[len(t) // 2] for n, t in times.items()}
     value = (f_fwd + f_tgt) / (ms_step * 1e-3) / 1e12
     tgt_tflops = f_tgt / (avg["tgt"] * 1e-3) / 1e12
     fwd_tflops = f_fwd / (avg["fwd"] * 1e-3) / 1e12
@@ -531,7 +659,9 @@ def main():
                    "decode_workload": DECODE_B2048.name},
         "frac_mfma_peak": round(value / MFMA_BF16_PEAK_TFLOPS, 4),
         "kernels_ms": {n: round(t, 4) for n, t in avg.items()},
+        "kernels_ms_median": {n: round(t, 4) for n, t in med.items()},
         "step_ms_events": round(sum(step_ev) / len(step_ev), 4),
+        "step_ms_median": round(sorted(step_ev)[len(step_ev) // 2], 4),
         "isolated_ms": {n: round(t, 4) for n, t in iso.items()} or None,
         "isolated_tflops": {"fwd": round(f_fwd / (iso["fwd"] * 1e-3) / 1e12, 2),
                             "tgt": round(f_tgt / (iso["tgt"] * 1e-3) / 1e12, 2)} if iso else None,
@@ -552,10 +682,38 @@ def main():
 
     if not args.no_decode:
         out["decode"] = bench_decode(kv, torch, np, dev, args.decode_steps)
+    # every hot kernel against its roofline, from launches alone on the chip:
+    # the forward and target calls (7 x 10 launches, median), the decode step
+    # (1024 steps) and the backward (3 calls)
+    rl = {}
+    if iso:
+        for name, flop, kern in (("masked_fwd", f_fwd, ["key_end_kernel", "tile_list_kernel",
+                                                        "masked_fwd_kernel"]),
+                                 ("future_target", f_tgt, ["future_target_kernel"])):
+            ms = iso["fwd" if name == "masked_fwd" else "tgt"]
+            ach = flop / (ms * 1e-3) / 1e12
+            rl[name] = {"bound": "mfma", "kernels": kern, "ms_per_call": round(ms, 4),
+                        "algorithmic": flop, "achieved": round(ach, 2),
+                        "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                        "frac": round(ach / MFMA_BF16_PEAK_TFLOPS, 4)}
+    if "decode" in out:
+        dd = out["decode"]
+        rl["decode_step"] = {"bound": "hbm", "kernels": ["decode_attend_kernel"],
+                             "us_per_call": dd["us_per_step"], "algorithmic": dd["bytes_per_step"],
+                             "achieved": dd["GB/s"], "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                             "frac": dd["frac_hbm_peak"], "traffic": dd["traffic"]}
+    rl["masked_bwd"] = {"bound": "mfma", "kernels": ["key_end_kernel", "tile_list_kernel",
+                                                     "bwd_dot_kernel", "bwd_key_order_kernel",
+                                                     "bwd_dq_kernel", "bwd_dkdv_kernel"],
+                        "ms_per_call": backward["ms"], "algorithmic": backward["flop"],
+                        "achieved": backward["tflops"], "peak": MFMA_BF16_PEAK_TFLOPS,
+                        "unit": "TFLOP/s", "frac": backward["frac_mfma_peak"]}
+    out["rooflines"] = rl
     if not args.no_other_configs:
         del q, kk, v, o, lse, tgt, lse_teacher, rank_d, tau_d
         torch.cuda.empty_cache()
-        out["other_configs"] = {"qwen3-8b-layer": bench_layer_c3(kv, torch, dev, ev),
+        out["other_configs"] = {"tiny": bench_tiny(kv, torch, dev, ev),
+                                "qwen3-8b-layer": bench_layer_c3(kv, torch, dev, ev),
                                 "long-context": bench_long_c5(kv, torch, dev, ev)}
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(x, s, w, k)
