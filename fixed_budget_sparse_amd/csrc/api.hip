@@ -27,6 +27,14 @@ kvpop_status make_dims(int32_t call, const kvpop_problem* pr, Dims* d) {
   if (budget > kMaxBudget) return KVPOP_ERR_ARG;
   if (!dtype_ok(pr->qkv_dtype) || !dtype_ok(pr->out_dtype)) return KVPOP_ERR_ARG;
   if (!(pr->softmax_scale == pr->softmax_scale) || isinf(pr->softmax_scale)) return KVPOP_ERR_ARG;
+  // sizes whose products the launch geometry and the index arithmetic hold:
+  // (sequence, KV head) pairs on a grid's y/z axis, query heads x sequences
+  // in a 30-bit grid, and at most 2^40 elements per prefill tensor
+  if ((long long)pr->batch * pr->n_kv_heads > 65535) return KVPOP_ERR_UNSUPPORTED;
+  if ((long long)pr->batch * pr->n_q_heads > (1LL << 20)) return KVPOP_ERR_UNSUPPORTED;
+  if (call != KVPOP_CALL_DECODE &&
+      (long long)pr->batch * pr->n_q_heads * (long long)pr->seq_len * pr->head_dim > (1LL << 40))
+    return KVPOP_ERR_UNSUPPORTED;
   const int G = pr->n_q_heads / pr->n_kv_heads;
   if (call != KVPOP_CALL_THRESHOLDS && call != KVPOP_CALL_TARGET_SCORE &&
       call != KVPOP_CALL_BOUNDARY_LABELS) {
@@ -217,7 +225,7 @@ KVPOP_EXPORT kvpop_status kvpop_boundary_labels(const kvpop_problem* pr, const f
   return finish(kvpop::launch_boundary_labels(d, score, log_gamma, decay_step, t_bnd, y, stream));
 }
 
-KVPOP_EXPORT const char* kvpop_status_string(kvpop_status st) {
+KVPOP_EXPORT const char* kvpop_status_string(int32_t st) {
   switch (st) {
     case KVPOP_OK: return "ok";
     case KVPOP_ERR_ARG: return "invalid argument";

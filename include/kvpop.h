@@ -72,7 +72,9 @@ typedef enum {
 
 /* Problem description shared by all calls.
  *   batch       sequences (>= 1)
- *   n_q_heads   Hq; n_kv_heads Hkv; Hq % Hkv == 0 and 1 <= Hq/Hkv <= 32
+ *   n_q_heads   Hq; n_kv_heads Hkv; Hq % Hkv == 0 and 1 <= Hq/Hkv <= 32;
+ *               batch * Hkv <= 65535, batch * Hq <= 2^20 and, for prefill
+ *               calls, batch * Hq * S * D <= 2^40 (KVPOP_ERR_UNSUPPORTED above)
  *   seq_len     S (prefill calls; 1 <= S <= 262144); ignored by decode
  *   head_dim    D in {64, 128}
  *   sink, window, topk   s >= 0, w >= 0, k >= 0 with s + w + k <= 2^30;
@@ -298,7 +300,9 @@ kvpop_status kvpop_masked_attn_bwd(const kvpop_problem* pr, const void* q, const
                                    float* dq, float* dk, float* dv, void* ws, size_t ws_bytes,
                                    hipStream_t stream);
 
-const char* kvpop_status_string(kvpop_status st);
+/* A short description of status `st` (a kvpop_status value; any other value
+ * gives "unknown status").  The returned string is static. */
+const char* kvpop_status_string(int32_t st);
 int32_t kvpop_abi_version(void);
 
 #ifdef __cplusplus

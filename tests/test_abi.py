@@ -153,3 +153,32 @@ def test_binding_refuses_cpu_tensors():
     _lib()
     with pytest.raises(kv.KvpopError):
         kv.thresholds(torch.zeros(1, 1, 8), 0, 1, 2)
+
+
+def test_abi_validation_under_sanitizers(tmp_path):
+    """The library's host code built with AddressSanitizer and
+    UndefinedBehaviorSanitizer, driven through every error path by
+    tests/abi_check.c (no GPU: every call returns before a launch)."""
+    import shutil
+    import subprocess
+    from fixed_budget_sparse_amd import build as Bd
+    try:
+        rt = Bd.asan_runtime_dir()
+        clang = Bd._llvm_bin("clang")
+    except RuntimeError:
+        pytest.skip("ROCm toolchain not found")
+    if not rt or not os.path.exists(clang):
+        pytest.skip("clang sanitizer runtime not found")
+    lib = Bd.build_sanitized(str(tmp_path))
+    exe = str(tmp_path / "abi_check")
+    rocm = os.path.join(os.path.dirname(os.path.realpath(Bd._hipcc())), "..")
+    cmd = [clang, "-g", "-O1", "-fsanitize=address,undefined", "-fno-sanitize-recover=undefined",
+           "-shared-libsan", "-D__HIP_PLATFORM_AMD__", "-I", os.path.join(ROOT, "include"),
+           "-I", os.path.join(rocm, "include"), os.path.join(ROOT, "tests", "abi_check.c"),
+           lib, "-Wl,-rpath," + str(tmp_path), "-Wl,-rpath," + rt, "-o", exe]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    env = dict(os.environ, ASAN_OPTIONS="detect_leaks=0", UBSAN_OPTIONS="print_stacktrace=1")
+    env["LD_LIBRARY_PATH"] = rt + ":" + os.path.join(rocm, "lib") + ":" + env.get("LD_LIBRARY_PATH", "")
+    r = subprocess.run([exe], capture_output=True, text=True, env=env, timeout=120)
+    assert r.returncode == 0 and "abi_check ok" in r.stdout, r.stdout + r.stderr

@@ -340,7 +340,6 @@ def test_boundary_labels_parity(case):
 
 
 # ---------------------------------------------------------------- backward
-BWD_FRO, BWD_MAX = BWD_TOL["fro"], BWD_TOL["max"]
 BWD_CASES = [
     # b, Hq, Hkv, S, D, s, w, k, forward output dtype
     (1, 8, 2, 300, 128, 4, 16, 40, "f32"),
@@ -375,4 +374,5 @@ def test_masked_attn_bwd_parity(case):
         err = got.astype(np.float64) - ref
         fro = np.linalg.norm(err) / np.linalg.norm(ref)
         mx = np.abs(err).max() / np.abs(ref).max()
-        assert fro <= BWD_FRO and mx <= BWD_MAX, (name, fro, mx)
+        tol = BWD_TOL[odt]
+        assert fro <= tol["fro"] and mx <= tol["max"], (name, fro, mx)
