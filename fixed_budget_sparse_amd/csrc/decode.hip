@@ -517,49 +517,96 @@ __global__ __launch_bounds__(kThreads, 2) void decode_attend_kernel(DecArgs a) {
   }
 }
 
-// Merges the per-split partials of one (sequence, KV head) into o and lse,
-// and applies the step's metadata update (recorded by split 0: every split
-// has read the metadata by now).
-template <int D, bool kF32Out>
-__global__ __launch_bounds__(kThreads) void decode_combine_kernel(DecArgs a) {
+// Merges the per-split partials into o and lse: one workgroup per
+// (sequence, query head), one thread per output dim, every partial of the
+// row read at once (the split maxima, sums and this dim's unnormalised O);
+// the workgroup of the first query head of each KV head also applies the
+// step's metadata update (recorded by split 0: every split has read the
+// metadata by now).
+template <int D, bool kF32Out, int kMaxSplit>
+__global__ __launch_bounds__(D) void decode_combine_kernel(DecArgs a) {
   constexpr int RS = D + 2;
-  const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+  const int hq = blockIdx.x, b = blockIdx.y, d = threadIdx.x;
   const int G = a.G, nsplit = a.nsplit;
-  if (tid == 0) {
-    const size_t seg = (size_t)b * a.Hkv + h;
+  if (hq % G == 0 && d == 0) {
+    const size_t seg = (size_t)b * a.Hkv + hq / G;
     const int* rec = a.dec + seg * 4;
     const Decision dc{rec[0], rec[1], __int_as_float(rec[3]), rec[2] != 0};
     apply_decision(a, seg, a.pos[b], dc);
   }
-  for (int idx = tid; idx < G * D; idx += kThreads) {
-    const int g = idx / D, d = idx % D;
-    const size_t hq = (size_t)b * a.Hq + h * G + g;
-    const float* pp = a.part + hq * nsplit * RS;
-    float M = kNegInf;
-    for (int j = 0; j < nsplit; ++j) M = fmaxf(M, pp[j * RS]);
-    float Ls = 0.0f, Od = 0.0f;
-    if (M != kNegInf) {
-#pragma unroll 4
-      for (int j = 0; j < nsplit; ++j) {
-        const float wt = exp2_fast(pp[j * RS] - M);
-        Ls += pp[j * RS + 1] * wt;
-        Od += pp[j * RS + 2 + d] * wt;
-      }
-    }
-    const float inv = Ls > 0.0f ? 1.0f / Ls : 0.0f;
-    if constexpr (kF32Out) ((float*)a.o)[hq * D + d] = Od * inv;
-    else ((__bf16*)a.o)[hq * D + d] = (__bf16)(Od * inv);
-    if (d == 0 && a.lse) a.lse[hq] = Ls > 0.0f ? (M + log2f(Ls)) * kLn2 : kNegInf;
+  const size_t row = (size_t)b * a.Hq + hq;
+  const float* pp = a.part + row * nsplit * RS;
+  float m[kMaxSplit], l[kMaxSplit], od[kMaxSplit];
+#pragma unroll
+  for (int j = 0; j < kMaxSplit; ++j) {
+    const bool ok = j < nsplit;
+    m[j] = ok ? pp[j * RS] : kNegInf;
+    l[j] = ok ? pp[j * RS + 1] : 0.0f;
+    od[j] = ok ? pp[j * RS + 2 + d] : 0.0f;
   }
+  float M = kNegInf;
+#pragma unroll
+  for (int j = 0; j < kMaxSplit; ++j) M = fmaxf(M, m[j]);
+  float Ls = 0.0f, Od = 0.0f;
+  if (M != kNegInf) {
+#pragma unroll
+    for (int j = 0; j < kMaxSplit; ++j) {
+      const float wt = m[j] == kNegInf ? 0.0f : exp2_fast(m[j] - M);
+      Ls += l[j] * wt;
+      Od += od[j] * wt;
+    }
+  }
+  const float inv = Ls > 0.0f ? 1.0f / Ls : 0.0f;
+  if constexpr (kF32Out) ((float*)a.o)[row * D + d] = Od * inv;
+  else ((__bf16*)a.o)[row * D + d] = (__bf16)(Od * inv);
+  if (d == 0 && a.lse) a.lse[row] = Ls > 0.0f ? (M + log2f(Ls)) * kLn2 : kNegInf;
+}
+
+// The same merge for any number of splits (more than the unrolled variants
+// hold): the partials of a row are read in a loop.
+template <int D, bool kF32Out>
+__global__ __launch_bounds__(D) void decode_combine_any_kernel(DecArgs a) {
+  constexpr int RS = D + 2;
+  const int hq = blockIdx.x, b = blockIdx.y, d = threadIdx.x;
+  const int G = a.G, nsplit = a.nsplit;
+  if (hq % G == 0 && d == 0) {
+    const size_t seg = (size_t)b * a.Hkv + hq / G;
+    const int* rec = a.dec + seg * 4;
+    const Decision dc{rec[0], rec[1], __int_as_float(rec[3]), rec[2] != 0};
+    apply_decision(a, seg, a.pos[b], dc);
+  }
+  const size_t row = (size_t)b * a.Hq + hq;
+  const float* pp = a.part + row * nsplit * RS;
+  float M = kNegInf;
+  for (int j = 0; j < nsplit; ++j) M = fmaxf(M, pp[j * RS]);
+  float Ls = 0.0f, Od = 0.0f;
+  if (M != kNegInf) {
+    for (int j = 0; j < nsplit; ++j) {
+      const float mj = pp[j * RS];
+      const float wt = mj == kNegInf ? 0.0f : exp2_fast(mj - M);
+      Ls += pp[j * RS + 1] * wt;
+      Od += pp[j * RS + 2 + d] * wt;
+    }
+  }
+  const float inv = Ls > 0.0f ? 1.0f / Ls : 0.0f;
+  if constexpr (kF32Out) ((float*)a.o)[row * D + d] = Od * inv;
+  else ((__bf16*)a.o)[row * D + d] = (__bf16)(Od * inv);
+  if (d == 0 && a.lse) a.lse[row] = Ls > 0.0f ? (M + log2f(Ls)) * kLn2 : kNegInf;
 }
 
 template <int D, bool kF32, bool kF32Out>
 void launch_dec(const DecArgs& a, int b, hipStream_t st) {
   hipLaunchKernelGGL((decode_attend_kernel<D, kF32, kF32Out>), dim3(a.nsplit, a.Hkv, b),
                      dim3(kThreads), 0, st, a);
-  if (a.nsplit > 1)
-    hipLaunchKernelGGL((decode_combine_kernel<D, kF32Out>), dim3(a.Hkv, b), dim3(kThreads), 0, st,
-                       a);
+  if (a.nsplit > 1) {
+    const dim3 grid(a.Hq, b);
+    if (a.nsplit <= 8)
+      hipLaunchKernelGGL((decode_combine_kernel<D, kF32Out, 8>), grid, dim3(D), 0, st, a);
+    else if (a.nsplit <= 16)
+      hipLaunchKernelGGL((decode_combine_kernel<D, kF32Out, 16>), grid, dim3(D), 0, st, a);
+    else
+      hipLaunchKernelGGL((decode_combine_any_kernel<D, kF32Out>), grid, dim3(D), 0, st, a);
+  }
 }
 
 }  // namespace
