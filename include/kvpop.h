@@ -202,8 +202,8 @@ kvpop_status kvpop_decode_step(const kvpop_problem* pr, const kvpop_cache* cache
  * live instead in a fixed array of KVPOP_NOALLOC_SCRATCH_BYTES (8 MiB) in
  * device memory, one per GPU, held from the library's first call on that GPU
  * until the process ends; a problem needing more (kvpop_workspace_size of
- * KVPOP_CALL_DECODE above that size: only very small pair counts with large
- * query groups) returns KVPOP_ERR_SCRATCH and launches nothing.  Nothing in
+ * KVPOP_CALL_DECODE above that size: only 32-head query groups with at
+ * most about 32 (sequence, KV head) pairs) returns KVPOP_ERR_SCRATCH and launches nothing.  Nothing in
  * the array has to start at any value (every word a step reads is written
  * earlier in the same step), but every call on one GPU shares it: calls that
  * overlap in time on one GPU (two streams, two threads) race and must be

@@ -138,9 +138,10 @@ int main(void) {
                                (const int32_t*)d, d, (float*)d, (float*)d, (float*)d, d, big, NULL),
          KVPOP_ERR_UNSUPPORTED);
   p = base();
-  p.n_q_heads = 32;
-  p.n_kv_heads = 1;
-  p.topk = 1 << 24;   /* ~511 splits x 32 query heads exceed the fixed scratch */
+  p.batch = 4;
+  p.n_q_heads = 256;
+  p.n_kv_heads = 8;
+  p.topk = 1 << 16;   /* 16 splits x 1024 query rows exceed the fixed scratch */
   EXPECT(kvpop_decode_step_noalloc(&p, &c, (const int32_t*)d, d, d, d, (const float*)d, d,
                                    (float*)d, NULL),
          KVPOP_ERR_SCRATCH);

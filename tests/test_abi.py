@@ -101,9 +101,9 @@ def test_decode_noalloc_error_paths():
     L = _lib()
     vp = ctypes.c_void_p
     cache = B._Cache(1, 1, 1, 1, 1)
-    # one (sequence, KV head) pair with a 32-head query group and a 2^24-token
-    # budget: 511 splits x 32 heads x 130 floats > 8 MiB
-    big = _pr(n_q_heads=32, n_kv_heads=1, topk=1 << 24)
+    # 32 (sequence, KV head) pairs with 32-head query groups and a 2^16-token
+    # budget: 16 splits x 1024 query rows x 130 floats > 8 MiB
+    big = _pr(batch=4, n_q_heads=256, n_kv_heads=8, topk=1 << 16)
     assert kv.workspace_size(B.CALL_DECODE, big) > 8 << 20
     c = big.c()
     assert L.kvpop_decode_step_noalloc(ctypes.byref(c), ctypes.byref(cache), *[vp(1)] * 7,

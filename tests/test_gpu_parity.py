@@ -218,6 +218,8 @@ DEC_CASES = [
     (2, 4, 2, 64, 0, 3, 5, 60, "f32"),
     (2, 4, 1, 128, 4, 5, 0, 40, "bf16"),       # k = 0
     (1, 2, 1, 128, 1, 2, 300, 200, "bf16"),    # budget larger than the run: 3 splits, partial fill
+    (2, 8, 2, 64, 3, 20, 400, 640, "f32"),     # 4 splits past the fill, D = 64, float32
+    (1, 4, 1, 128, 4, 300, 0, 420, "bf16"),    # 3 splits past the fill, k = 0
 ]
 
 
