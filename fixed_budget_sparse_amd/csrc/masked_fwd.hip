@@ -38,7 +38,7 @@ namespace {
 constexpr int kThreads = 512;       // 8 waves
 constexpr int kRowsPerTile = 256;   // stacked query rows per workgroup (8 waves x 32)
 constexpr int kChunk = 64;          // keys per chunk
-constexpr int kDesc = 4;            // key-descriptor slots (chunks c .. c+3 live)
+constexpr int kDesc = 8;            // key-descriptor slots (bf16: chunks c .. c+4 live)
 
 struct FwdArgs {
   const void* q;
@@ -177,6 +177,13 @@ struct FwdLds {
 
 typedef short short4v __attribute__((ext_vector_type(4)));
 
+// One key of a chunk as fetched by the descriptor reads: its token (-2: token
+// and q_end come from the tile's list entry l), and q_end(t) otherwise.
+struct KeyDesc {
+  int t, r;
+  int2 l;
+};
+
 // Byte offset of 16-byte piece `piece` of key row `key` in a bf16 K chunk.
 // The QK operand read has the 16 lanes served together read one piece of 16
 // consecutive rows; XORing the piece index with key mod 16 (D = 128) or
@@ -235,27 +242,39 @@ __device__ __forceinline__ bf16x8 v_tr_operand(const unsigned char* vb, const in
 template <int D, bool kF32In, bool kF32Out>
 __global__ __launch_bounds__(kThreads, 1) void masked_fwd_kernel(FwdArgs a) {
   using L = FwdLds<D, kF32In>;
-  // two K and two V buffers as separate arrays: the bf16 pipeline names each
-  // by a compile-time index, so the compiler can tell that the direct loads
-  // into one buffer never alias the reads of the other and need not wait for
-  // them before every LDS read
-  __shared__ __attribute__((aligned(16))) unsigned char k_lds0[L::kBytes];
-  __shared__ __attribute__((aligned(16))) unsigned char k_lds1[L::kBytes];
-  __shared__ __attribute__((aligned(16))) unsigned char v_lds0[L::vBytes];
-  __shared__ __attribute__((aligned(16))) unsigned char v_lds1[L::vBytes];
-  // buffer i: a run-time int (float32 path) or a std::integral_constant
+  // K and V buffers as separate arrays (bf16: three of each, float32: two):
+  // the bf16 pipeline names each by a compile-time index, so the compiler can
+  // tell that the direct loads into one buffer never alias the reads of
+  // another and need not wait for them before every LDS read.  The compiler
+  // lays arrays of one size out in name order, so the V buffers come first:
+  // the three V buffers and K buffer 0 then lie where the 16-bit immediate
+  // offset of an LDS read reaches them from one set of per-lane offsets; K
+  // buffers 1 and 2 (D = 128: above 64 KB) are read through a second base
+  // 64 KB higher.  (Any other layout stays correct, with a few more adds.)
+  constexpr int kThirdK = kF32In ? 16 : L::kBytes;
+  constexpr int kThirdV = kF32In ? 16 : L::vBytes;
+  __shared__ __attribute__((aligned(16))) unsigned char ldsa_v0[L::vBytes];
+  __shared__ __attribute__((aligned(16))) unsigned char ldsa_v1[L::vBytes];
+  __shared__ __attribute__((aligned(16))) unsigned char ldsa_v2[kThirdV];
+  __shared__ __attribute__((aligned(16))) unsigned char ldsb_k0[L::kBytes];
+  __shared__ __attribute__((aligned(16))) unsigned char ldsb_k1[L::kBytes];
+  __shared__ __attribute__((aligned(16))) unsigned char ldsb_k2[kThirdK];
+  // buffer i: a run-time int (float32 path, 0 or 1) or a std::integral_constant
   auto kbuf = [&](auto i) -> unsigned char* {
-    if constexpr (std::is_integral<decltype(i)>::value) return i ? k_lds1 : k_lds0;
-    else if constexpr (decltype(i)::value == 0) return k_lds0;
-    else return k_lds1;
+    if constexpr (std::is_integral<decltype(i)>::value) return i ? ldsb_k1 : ldsb_k0;
+    else if constexpr (decltype(i)::value == 0) return ldsb_k0;
+    else if constexpr (decltype(i)::value == 1) return ldsb_k1;
+    else return ldsb_k2;
   };
   auto vbuf = [&](auto i) -> unsigned char* {
-    if constexpr (std::is_integral<decltype(i)>::value) return i ? v_lds1 : v_lds0;
-    else if constexpr (decltype(i)::value == 0) return v_lds0;
-    else return v_lds1;
+    if constexpr (std::is_integral<decltype(i)>::value) return i ? ldsa_v1 : ldsa_v0;
+    else if constexpr (decltype(i)::value == 0) return ldsa_v0;
+    else if constexpr (decltype(i)::value == 1) return ldsa_v1;
+    else return ldsa_v2;
   };
   using C0 = std::integral_constant<int, 0>;
   using C1 = std::integral_constant<int, 1>;
+  using C2 = std::integral_constant<int, 2>;
   __shared__ __attribute__((aligned(16))) int kd_t[kDesc][kChunk];
   __shared__ __attribute__((aligned(16))) int kd_r[kDesc][kChunk];
   __shared__ int s_flag[kDesc];
@@ -323,11 +342,15 @@ __global__ __launch_bounds__(kThreads, 1) void masked_fwd_kernel(FwdArgs a) {
     }
   }
 
-  // complete the query loads here: loads still in flight at the loop entry
-  // made the compiler wait for every newer load (the whole next-chunk gather)
-  // before the first MFMA of each chunk
+  // the query loads stay in flight while the prologue fetches descriptors
+  // and the first chunks; complete_q marks them complete before the chunk
+  // loop (loads still in flight at the loop entry made the compiler wait for
+  // every newer load, the whole next-chunk gather, before the first MFMA of
+  // each chunk)
+  auto complete_q = [&] {
 #pragma unroll
-  for (int ks = 0; ks < NKS; ++ks) asm volatile("" : "+v"(qop[ks]));
+    for (int ks = 0; ks < NKS; ++ks) asm volatile("" : "+v"(qop[ks]));
+  };
 
   f32x16 oacc[D / 32];
 #pragma unroll
@@ -344,9 +367,7 @@ __global__ __launch_bounds__(kThreads, 1) void masked_fwd_kernel(FwdArgs a) {
   // mask runs, else 2: row q keeps key t iff t <= q <= q_end(t), the A8 mask
   // as one unsigned compare (tau never increases with q, so the rows that
   // keep a key are one interval); padding keys (token -1, span 0) fail it.
-  int pd_t = -1, pd_r = 0;
-  int2 pd_l = make_int2(-1, 0);
-  auto desc_load = [&](int c0) {
+  auto desc_fetch = [&](int c0, KeyDesc& d) {
     if (wave == 0) {
       const int j = c0 + lane;
       const bool in_sink = j < n_sink;
@@ -355,15 +376,15 @@ __global__ __launch_bounds__(kThreads, 1) void masked_fwd_kernel(FwdArgs a) {
       const int t = in_sink ? j
                     : in_long ? s + (j - n_sink)
                     : in_band ? band_lo + (j - n_sink - n_long) : -1;
-      if (listed) pd_l = lst[min(max(j - n_sink, 0), max(n_long - 1, 0))];
-      pd_r = qend[min(max(t, 0), S - 1)];
-      pd_t = (in_long && listed) ? -2 : t;    // -2: token and q_end from the list
+      if (listed) d.l = lst[min(max(j - n_sink, 0), max(n_long - 1, 0))];
+      d.r = qend[min(max(t, 0), S - 1)];
+      d.t = (in_long && listed) ? -2 : t;    // -2: token and q_end from the list
     }
   };
-  auto desc_store = [&](int db) {
+  auto desc_put = [&](int db, const KeyDesc& d) {
     if (wave == 0) {
-      int t = pd_t == -2 ? pd_l.x : pd_t;
-      const int e = pd_t == -2 ? pd_l.y : pd_r;
+      int t = d.t == -2 ? d.l.x : d.t;
+      const int e = d.t == -2 ? d.l.y : d.r;
       if (t >= S) t = -1;
       kd_t[db][lane] = t;
       kd_r[db][lane] = t >= 0 ? e - t : 0;
@@ -372,12 +393,17 @@ __global__ __launch_bounds__(kThreads, 1) void masked_fwd_kernel(FwdArgs a) {
       if (lane == 0) s_flag[db] = not_always == 0 ? 0 : 2;
     }
   };
+  KeyDesc pd{-1, 0, make_int2(-1, 0)};   // the chunk in flight in the loop
+  auto desc_load = [&](int c0) { desc_fetch(c0, pd); };
+  auto desc_store = [&](int db) { desc_put(db, pd); };
 
   // ---- gathers of K and V rows.  bf16: direct loads from global memory into
   // LDS (global_load_lds_dwordx4), no registers and no LDS store
-  // instructions: K of chunk c+2 and V of chunk c are issued at the start of
-  // iteration c into the buffers the previous iteration finished reading, and
-  // awaited only before the iteration's closing barrier.  Each instruction
+  // instructions: K of chunk c+3 and V of chunk c+1 are issued at the start
+  // of iteration c into the buffers the previous iteration finished reading,
+  // and awaited before the closing barrier of iteration c+1, so each load has
+  // two iterations to arrive (waiting on the loads of the same iteration made
+  // every chunk pay a full cache round trip).  Each instruction
   // fills 1 KB of LDS (lane L writes bytes 16L .. 16L+15 of its block, checked
   // on the device), i.e. 1024 / (2 D) rows; lane L fetches the global piece
   // that the row's swizzle places at its slot.  float32: registers -> LDS,
@@ -396,12 +422,30 @@ __global__ __launch_bounds__(kThreads, 1) void masked_fwd_kernel(FwdArgs a) {
   // per-lane offsets of the transposed V^T operand reads and of the swizzled
   // K operand reads (bf16: row li, piece 2 ks + hh)
   int vtr_off[D / 32];
-  int k_off[NKS];
+  // K: the offset of piece 2 ks + hh of row li is k_piece_offset(li, hh) XOR
+  // 32 ks (the swizzle XORs the piece index, and 2 ks only sets piece bits
+  // that the row offset does not use), so one per-lane base serves every
+  // k-step; k_hi is the same base plus 64 KB for the buffers above 64 KB
+  int k_lo = 0, k_hi = 0;
   if constexpr (!kF32In) {
     v_tr_offsets<D>(lane, vtr_off);
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) k_off[ks] = k_piece_offset<D>(li, 2 * ks + hh);
+    k_lo = k_piece_offset<D>(li, hh);
+    k_hi = k_lo + 65536;
   }
+  // K operand of k-step ks, 32-key block blk, from K buffer kb; `base` is
+  // k_lo or k_hi as rebound by k_base (opaque to the compiler, so that the
+  // eight XORs stay in the loop instead of occupying eight registers)
+  constexpr bool kHiK = !kF32In && 3 * L::vBytes + 2 * L::kBytes > 65536;
+  auto k_base = [&](auto kb) {
+    int x = (kHiK && decltype(kb)::value >= 1) ? k_hi : k_lo;
+    asm volatile("" : "+v"(x));
+    return x;
+  };
+  auto k_operand = [&](auto kb, int base, int ks, int blk) {
+    constexpr int bias = (kHiK && decltype(kb)::value >= 1) ? 65536 : 0;
+    const unsigned char* p = kbuf(kb) + blk * 32 * (D * 2) + ((base ^ (32 * ks)) - bias);
+    return as_bf16x8(*(const uint4*)p);
+  };
   // Padding slots (token -1) load row 0 instead: every such key is masked
   // (its probability is exactly 0), so only finiteness matters, and the loads
   // stay unconditional (no exec-masked branches, all addresses issued at once).
@@ -412,7 +456,7 @@ __global__ __launch_bounds__(kThreads, 1) void masked_fwd_kernel(FwdArgs a) {
     for (int i = 0; i < NDMA; ++i) {
       const int r0 = (wave * NDMA + i) * RPI;      // first row of this 1 KB block
       const int row = r0 + lane / PPR, slot = lane % PPR;
-      const int t = max(kd_t[db][row], 0);
+      const int t = min(max(kd_t[db][row], 0), S - 1);   // padding (-1) reads row 0
       const int sw = is_k ? k_piece_offset<D>(row, slot) : v_piece_offset<D>(row, slot);
       const int piece = (sw >> 4) & (PPR - 1);     // the logical piece stored at this slot
       __builtin_amdgcn_global_load_lds((const void*)(g + ((size_t)t * PPR + piece) * 16),
@@ -422,6 +466,9 @@ __global__ __launch_bounds__(kThreads, 1) void masked_fwd_kernel(FwdArgs a) {
   auto dma_k = [&](int db, auto kb) { dma_rows(a.k, kbuf(kb), db, true); };
   auto dma_v = [&](int db, auto vb) { dma_rows(a.v, vbuf(vb), db, false); };
   auto dma_wait = [] { __builtin_amdgcn_s_waitcnt(0x0F70); };   // vmcnt(0)
+  // vmcnt(2 NDMA): every load but the direct loads of the current iteration
+  auto dma_wait_prev = [] { __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * NDMA)); };
+  static_assert(kF32In || 2 * NDMA < 16, "vmcnt field");
   auto load_k = [&](int db) {
     const unsigned char* kg = (const unsigned char*)a.k + kvbase * 4;
 #pragma unroll
@@ -466,10 +513,10 @@ __global__ __launch_bounds__(kThreads, 1) void masked_fwd_kernel(FwdArgs a) {
     for (int blk = 0; blk < 2; ++blk) {
       acc[blk] = f32x16{};
       if constexpr (!kF32In) {
-        const unsigned char* kl = kbuf(kb) + 32 * blk * (D * 2);
+        const int base = k_base(kb);
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks)
-          acc[blk] = mfma32x32x16(as_bf16x8(*(const uint4*)(kl + k_off[ks])), qop[ks], acc[blk]);
+          acc[blk] = mfma32x32x16(k_operand(kb, base, ks, blk), qop[ks], acc[blk]);
       } else {
         const float* kl = (const float*)kbuf(kb) + (32 * blk + li) * L::KS + hh;
 #pragma unroll
@@ -592,12 +639,12 @@ __global__ __launch_bounds__(kThreads, 1) void masked_fwd_kernel(FwdArgs a) {
   constexpr int NPV = NB * 4;           // PV MFMAs per chunk
   constexpr int EPM = 32 / NQM;         // exps per slot
   static_assert(kF32In || (NQM == NPV && NQM >= 4 && 32 % NQM == 0), "slot schedule");
-  auto region = [&](auto kb, f32x16 (&nx)[2], f32x16 (&sc)[2], float mb, const POp (&pkp)[NP],
-                    POp (&pkc)[NP], auto vb, float& ps) {
+  auto region = [&](auto kb, f32x16 (&nx)[2], f32x16 (&sc)[2], float mb, POp (&pk)[NP], auto vb,
+                    float& ps) {
     if constexpr (!kF32In) {
-      const unsigned char* kl = kbuf(kb);
+      const int kbase = k_base(kb);
       auto rk = [&](int i) {   // QK operand i: block i & 1, k-step i >> 1
-        return as_bf16x8(*(const uint4*)(kl + (i & 1) * 32 * (D * 2) + k_off[i >> 1]));
+        return k_operand(kb, kbase, i >> 1, i & 1);
       };
       auto rv = [&](int j) {   // PV operand j: output block j % NB, k-step j / NB
         return v_tr_operand<D>(vbuf(vb), vtr_off, j % NB, j / NB);
@@ -610,7 +657,7 @@ __global__ __launch_bounds__(kThreads, 1) void masked_fwd_kernel(FwdArgs a) {
         u.y = pack_bf16x2(src[o8 + 2], src[o8 + 3]);
         u.z = pack_bf16x2(src[o8 + 4], src[o8 + 5]);
         u.w = pack_bf16x2(src[o8 + 6], src[o8 + 7]);
-        pkc[pidx] = as_bf16x8(u);
+        pk[pidx] = as_bf16x8(u);
       };
       const float c = a.scale_log2;
       bf16x8 kn = rk(0), vn = rv(0);   // operands one slot ahead
@@ -626,7 +673,7 @@ __global__ __launch_bounds__(kThreads, 1) void masked_fwd_kernel(FwdArgs a) {
             vn = rv(i + 1);
           }
           nx[i & 1] = mfma32x32x16(ak, qop[i >> 1], nx[i & 1]);
-          oacc[i % NB] = mfma32x32x16(av, pkp[i / NB], oacc[i % NB]);
+          oacc[i % NB] = mfma32x32x16(av, pk[i / NB], oacc[i % NB]);
 #pragma unroll
           for (int u = 0; u < EPM; ++u) {
             const int e = EPM * i + u;
@@ -646,7 +693,7 @@ __global__ __launch_bounds__(kThreads, 1) void masked_fwd_kernel(FwdArgs a) {
             pack(pidx);
             // used here: P(c) is consumed only in the next iteration, and the
             // exps would otherwise be sunk past the region to the loop's end
-            asm volatile("" ::"v"(pkc[pidx]));
+            asm volatile("" ::"v"(pk[pidx]));
           }
         }
         __builtin_amdgcn_sched_barrier(0);
@@ -656,28 +703,39 @@ __global__ __launch_bounds__(kThreads, 1) void masked_fwd_kernel(FwdArgs a) {
   };
 
   const int nchunk = (nk + kChunk - 1) / kChunk;
-  auto publish_first_descriptors = [&] {
+  // descriptors of chunks 0 .. n-1 (tokens -1 past the end): every read
+  // issued before the first store, so the prologue waits once
+  auto publish_first_descriptors = [&](auto n) {
+    constexpr int N = decltype(n)::value;
+    KeyDesc d0[N];
 #pragma unroll
-    for (int j = 0; j < kDesc - 1; ++j) {   // every slot starts valid (tokens -1 past the end)
-      desc_load(j * kChunk);
-      desc_store(j);
+    for (int j = 0; j < N; ++j) {
+      d0[j] = KeyDesc{-1, 0, make_int2(-1, 0)};
+      desc_fetch(j * kChunk, d0[j]);
     }
+#pragma unroll
+    for (int j = 0; j < N; ++j) desc_put(j, d0[j]);
     __syncthreads();
   };
   f32x16 sA[2], sB[2];
-  POp pkA[NP], pkB[NP];
+  // P operands: in the bf16 region P(c-1) operand p is last read by a PV
+  // MFMA one slot before P(c) operand p is packed into the same registers
+  POp pk[NP];
   float l_tot;
   if constexpr (!kF32In) {
     // ---- bf16 software pipeline.  Entering iteration c >= 1: the scores of
-    // chunk c and P of chunk c-1 are in registers, K(c+1) and V(c-1) are in
-    // LDS, descriptors of c .. c+2 are published.  Per iteration: direct
-    // loads of K(c+2) and V(c) into the buffers read last in iteration c-1,
-    // and the descriptor reads of chunk c+3, are issued; mask of chunk c;
-    // the fused region (QK c+1, exps c, PV c-1); descriptors of chunk c+3;
-    // the direct loads are awaited; barrier.  Past the last chunk the loads
+    // chunk c and P of chunk c-1 are in registers; K(c+1) and V(c-1) are in
+    // LDS, K(c+2) and V(c) are arriving; descriptors of c .. c+3 are
+    // published.  Per iteration: the descriptor reads of chunk c+4 and the
+    // direct loads of K(c+3) and V(c+1) are issued (into the buffers read
+    // last in iteration c-1); mask of chunk c; the fused region (QK c+1, exps
+    // c, PV c-1); descriptors of chunk c+4 are stored; the loads issued one
+    // iteration earlier are awaited; barrier.  Past the last chunk the loads
     // and QK run on descriptors of tokens -1 (row 0) and their results are
-    // unused, which keeps the region free of branches.  Unrolled by two so
-    // score and P buffers swap roles without register copies.
+    // unused, which keeps the region free of branches (the direct loads still
+    // in flight when the workgroup ends are awaited by its end of program).  Buffers rotate over
+    // three and score / P registers over two, so the loop is unrolled by six
+    // and every buffer index is a compile-time constant.
     //
     // Two modes.  Fixed reference (first run): each row's maximum over the
     // first chunk is its reference for the whole tile, so later chunks need
@@ -690,70 +748,90 @@ __global__ __launch_bounds__(kThreads, 1) void masked_fwd_kernel(FwdArgs a) {
     // the running maximum, moved lazily by more than 2^8, with rescales.
     auto run = [&](auto exact) {
       constexpr bool kExact = decltype(exact)::value;
-      publish_first_descriptors();
+      publish_first_descriptors(std::integral_constant<int, 4>{});
       dma_k(0, C0{});
       dma_k(1, C1{});
-      {   // V buffer 1 starts at zero: iteration 0 runs its PV slots on it
-        uint4* vz = (uint4*)vbuf(C1{});
+      dma_k(2, C2{});
+      dma_v(0, C0{});
+      {   // V buffer 2 starts at zero: iteration 0 runs its PV slots on it
+        uint4* vz = (uint4*)vbuf(C2{});
         for (int i = tid; i < (int)(L::vBytes / 16); i += kThreads) vz[i] = make_uint4(0, 0, 0, 0);
       }
       dma_wait();
+      complete_q();
       __syncthreads();
       qk(C0{}, sA);
       float mb0;
       {   // iteration 0: no PV yet
-        dma_v(0, C0{});
-        desc_load(3 * kChunk);
+        desc_load(4 * kChunk);
+        __builtin_amdgcn_sched_barrier(0);   // descriptor reads before the direct loads
+        dma_v(1, C1{});
         mb0 = softmax_pre(sA, 0, [] {});
 #pragma unroll
-        for (int p = 0; p < NP; ++p) pkB[p] = POp{};
-        // K(2) goes over K(0): every wave's qk(0) must have read it (later
+        for (int p = 0; p < NP; ++p) pk[p] = POp{};
+        // K(3) goes over K(0): every wave's qk(0) must have read it (later
         // iterations overwrite a buffer read before the last barrier)
         __syncthreads();
-        dma_k(2 % kDesc, C0{});
+        dma_k(3, C0{});
         float ps;
-        region(C1{}, sB, sA, mb0, pkB, pkA, C1{}, ps);
+        region(C1{}, sB, sA, mb0, pk, C2{}, ps);
         l_run += ps;
-        desc_store(3 % kDesc);
-        dma_wait();
+        desc_store(4);
+        dma_wait_prev();
         __syncthreads();
       }
-      // iteration c (parity P = c & 1, a compile-time constant: the loop
-      // below is unrolled by two): loads into buffers P, reads of buffers 1 - P
-      auto step = [&](int c, auto par, f32x16 (&cur)[2], f32x16 (&nxt)[2], POp (&pkp)[NP],
-                      POp (&pkc)[NP]) {
-        constexpr int P = decltype(par)::value;
-        using Cp = std::integral_constant<int, P>;
-        using Cq = std::integral_constant<int, 1 - P>;
-        dma_k((c + 2) % kDesc, Cp{});
-        dma_v(c % kDesc, Cp{});
-        desc_load((c + 3) * kChunk);
+      // iteration c with R = c mod 3 (compile-time): direct loads into K
+      // buffer R and V buffer (R+1) mod 3, reads of K buffer (R+1) mod 3 and
+      // V buffer (R+2) mod 3; scores of chunks c and c+1 alternate between
+      // sA and sB with the parity of c
+      auto step = [&](int c, auto rr, f32x16 (&cur)[2], f32x16 (&nxt)[2]) {
+        constexpr int R = decltype(rr)::value;
+        using Kw = std::integral_constant<int, R>;
+        using Vw = std::integral_constant<int, (R + 1) % 3>;
+        using Kr = std::integral_constant<int, (R + 1) % 3>;
+        using Vr = std::integral_constant<int, (R + 2) % 3>;
+        desc_load((c + 4) * kChunk);
+        __builtin_amdgcn_sched_barrier(0);
+        dma_k((c + 3) % kDesc, Kw{});
+        dma_v((c + 1) % kDesc, Vw{});
         float mb = mb0;
         if constexpr (kExact) {
           // a rescale first completes PV(c-1) and zeroes P(c-1), so the
           // region's PV MFMAs then add exactly 0
           mb = softmax_pre(cur, c % kDesc, [&] {
-            pv(Cq{}, pkp);
+            pv(Vr{}, pk);
 #pragma unroll
-            for (int p = 0; p < NP; ++p) pkp[p] = POp{};
+            for (int p = 0; p < NP; ++p) pk[p] = POp{};
           });
         } else {
           apply_mask(cur, c % kDesc);
         }
         float ps;
-        region(Cq{}, nxt, cur, mb, pkp, pkc, Cq{}, ps);
+        region(Kr{}, nxt, cur, mb, pk, Vr{}, ps);
         l_run += ps;
-        desc_store((c + 3) % kDesc);
-        dma_wait();
+        desc_store((c + 4) % kDesc);
+        dma_wait_prev();
         __syncthreads();
       };
-      for (int c = 1; c < nchunk; c += 2) {
-        step(c, C1{}, sB, sA, pkA, pkB);
-        if (c + 1 < nchunk) step(c + 1, C0{}, sA, sB, pkB, pkA);
+      for (int c = 1; c < nchunk; c += 6) {
+        step(c, C1{}, sB, sA);
+        if (c + 1 >= nchunk) break;
+        step(c + 1, C2{}, sA, sB);
+        if (c + 2 >= nchunk) break;
+        step(c + 2, C0{}, sB, sA);
+        if (c + 3 >= nchunk) break;
+        step(c + 3, C1{}, sA, sB);
+        if (c + 4 >= nchunk) break;
+        step(c + 4, C2{}, sB, sA);
+        if (c + 5 >= nchunk) break;
+        step(c + 5, C0{}, sA, sB);
       }
-      // PV of the last chunk (its P is in pkA when its index is even)
-      if ((nchunk - 1) & 1) pv(C1{}, pkB);
-      else pv(C0{}, pkA);
+      // PV of the last chunk: its V is in buffer (nchunk - 1) mod 3
+      switch ((nchunk - 1) % 3) {
+        case 0: pv(C0{}, pk); break;
+        case 1: pv(C1{}, pk); break;
+        default: pv(C2{}, pk); break;
+      }
       l_tot = halves_sum(l_run);
     };
     run(std::false_type{});
@@ -769,7 +847,8 @@ __global__ __launch_bounds__(kThreads, 1) void masked_fwd_kernel(FwdArgs a) {
     }
   } else {
     // ---- float32 inputs: K one chunk ahead, V staged with it, steps in order
-    publish_first_descriptors();
+    publish_first_descriptors(std::integral_constant<int, 3>{});
+    complete_q();
     load_k(0);
     load_v(0);
     store_k(0);
@@ -781,8 +860,8 @@ __global__ __launch_bounds__(kThreads, 1) void masked_fwd_kernel(FwdArgs a) {
       desc_load((c + 3) * kChunk);
       qk(c & 1, sA);
       const float mb = softmax_pre(sA, c % kDesc, [] {});
-      softmax_exp(sA, mb, pkA);
-      pv(c & 1, pkA);
+      softmax_exp(sA, mb, pk);
+      pv(c & 1, pk);
       store_k((c + 1) & 1);
       store_v((c + 1) & 1);
       desc_store((c + 3) % kDesc);
@@ -815,10 +894,9 @@ __global__ __launch_bounds__(kThreads, 1) void masked_fwd_kernel(FwdArgs a) {
 }
 
 template <int D, bool kF32In, bool kF32Out>
-void launch_fwd_kernel(const FwdArgs& a, int b, hipStream_t st) {
-  const long long n = (long long)a.ntiles * a.Hkv * b;
-  hipLaunchKernelGGL((masked_fwd_kernel<D, kF32In, kF32Out>), dim3((unsigned)n), dim3(kThreads), 0,
-                     st, a);
+void launch_fwd_kernel(const FwdArgs& a, int n_wg, hipStream_t st) {
+  hipLaunchKernelGGL((masked_fwd_kernel<D, kF32In, kF32Out>), dim3((unsigned)n_wg), dim3(kThreads),
+                     0, st, a);
 }
 
 }  // namespace
@@ -877,21 +955,22 @@ hipError_t launch_masked_fwd(const Dims& d, const void* q, const void* k, const 
   a.S = d.S; a.Hq = d.Hq; a.Hkv = d.Hkv; a.G = d.G; a.m = m; a.ntiles = nt;
   a.s = d.s; a.w = d.w; a.cap = cap;
   a.scale_log2 = d.scale * 1.4426950408889634f;
+  const int n_wg = nt * d.Hkv * d.b;   // one workgroup per tile
   if (d.D == 128) {
     if (d.f32_in) {
-      if (d.f32_out) launch_fwd_kernel<128, true, true>(a, d.b, st);
-      else launch_fwd_kernel<128, true, false>(a, d.b, st);
+      if (d.f32_out) launch_fwd_kernel<128, true, true>(a, n_wg, st);
+      else launch_fwd_kernel<128, true, false>(a, n_wg, st);
     } else {
-      if (d.f32_out) launch_fwd_kernel<128, false, true>(a, d.b, st);
-      else launch_fwd_kernel<128, false, false>(a, d.b, st);
+      if (d.f32_out) launch_fwd_kernel<128, false, true>(a, n_wg, st);
+      else launch_fwd_kernel<128, false, false>(a, n_wg, st);
     }
   } else {
     if (d.f32_in) {
-      if (d.f32_out) launch_fwd_kernel<64, true, true>(a, d.b, st);
-      else launch_fwd_kernel<64, true, false>(a, d.b, st);
+      if (d.f32_out) launch_fwd_kernel<64, true, true>(a, n_wg, st);
+      else launch_fwd_kernel<64, true, false>(a, n_wg, st);
     } else {
-      if (d.f32_out) launch_fwd_kernel<64, false, true>(a, d.b, st);
-      else launch_fwd_kernel<64, false, false>(a, d.b, st);
+      if (d.f32_out) launch_fwd_kernel<64, false, true>(a, n_wg, st);
+      else launch_fwd_kernel<64, false, false>(a, n_wg, st);
     }
   }
   return hipGetLastError();
