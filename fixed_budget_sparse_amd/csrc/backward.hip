@@ -106,26 +106,45 @@ __global__ __launch_bounds__(256) void bwd_dot_kernel(const uint16_t* __restrict
   if (part == 0 && row < rows) dvec[row] = acc;
 }
 
-// Key order of the dK/dV tiles, one workgroup per (sequence, KV head):
-// bucket = t / 64 for keys living at most w + 64 rows, else S/64 + q_end / 64;
-// a counting sort over the buckets (order inside a bucket is free).
+// Buckets of the dK/dV key order for sequence length S: keys living at most
+// w + 64 rows by t / 64 (a tile of them visits about w + 64 rows); the
+// others by (q_end band, t band) with S / 8-row q_end bands and S / 64-token
+// t bands, so the keys of a tile end and start near each other and the rows
+// it streams ([min t, max q_end]) are mostly rows its keys keep.  (On the
+// 16k layer this keeps about two thirds of the streamed (key, row) pairs,
+// against one half when long-lived keys are ordered by q_end alone.)
+struct KeyBuckets {
+  int nb1, qb, tb, ntb, nb;
+  __host__ __device__ explicit KeyBuckets(int S) {
+    nb1 = (S + 63) / 64;
+    qb = ((S + 7) / 8 + 63) / 64 * 64;
+    tb = ((S + 63) / 64 + 63) / 64 * 64;
+    ntb = (S + tb - 1) / tb;
+    nb = nb1 + ((S + qb - 1) / qb) * ntb;
+  }
+};
+
+// Key order of the dK/dV tiles, one workgroup per (sequence, KV head): a
+// counting sort over the KeyBuckets (order inside a bucket is free: a key's
+// sums do not depend on its tile).
 __global__ __launch_bounds__(1024) void bwd_key_order_kernel(const int* __restrict__ qend,
                                                              int* __restrict__ korder, int S,
                                                              int w) {
   extern __shared__ int bk[];       // nb counters, then nb offsets
   const int seg = blockIdx.x, tid = threadIdx.x;
-  const int nb1 = (S + 63) / 64, nb = 2 * nb1;
+  const KeyBuckets kb(S);
+  const int nb = kb.nb;
   const int* qe = qend + (size_t)seg * S;
   int* out = korder + (size_t)seg * S;
   for (int i = tid; i < nb; i += 1024) bk[i] = 0;
   __syncthreads();
   auto bucket = [&](int t) {
     const int e = qe[t];
-    return (e - t + 1 <= w + 64) ? t / 64 : nb1 + e / 64;
+    return (e - t + 1 <= w + 64) ? t / 64 : kb.nb1 + (e / kb.qb) * kb.ntb + t / kb.tb;
   };
   for (int t = tid; t < S; t += 1024) atomicAdd(&bk[bucket(t)], 1);
   __syncthreads();
-  if (tid == 0) {                   // exclusive scan (nb <= 8192)
+  if (tid == 0) {                   // exclusive scan (nb <= S / 64 + 512)
     int run = 0;
     for (int i = 0; i < nb; ++i) {
       const int c = bk[i];
@@ -149,6 +168,9 @@ struct BwdArgs {
   const int* tau;
   const int* qend;
   const int* korder;
+  const int4* tplan;   // [nseg, 2 ktiles] dK/dV work items (tile, part, first chunk, end chunk)
+  const int* tsplit;   // [nseg, ktiles] 1 if the tile's rows are split over two items
+  float* part1;        // [nseg, ktiles, kKTile, 2, D] second-half sums of split tiles
   const int2* list;
   const int* count;
   float* dq;
@@ -346,6 +368,113 @@ __global__ __launch_bounds__(kQThreads, 1) void bwd_dq_kernel(BwdArgs a) {
   }
 }
 
+// ---------------------------------------------------------------- dK, dV plan
+// Work items of the dK/dV kernel, one workgroup per (sequence, KV head): each
+// 128-key tile of the key order needs the 32-row chunks [min t, max q_end];
+// a tile needing more than half the sequence's chunks is split into two
+// items (the first and second half of its chunks), so that no single
+// workgroup streams the whole sequence (the sinks' tile and the tiles of
+// early tokens kept to the end otherwise set the kernel's length alone).
+// The items are listed longest first (a counting sort on the chunk count),
+// so each XCD starts its longest items first; empty item slots (the second
+// slot of an unsplit tile) come last and exit at once.  A tile's keys are
+// those of the key order, so the split changes no key's chunk sums; the
+// second half's sums are added to the first half's in a fixed order.
+__device__ __forceinline__ int split_threshold(int S) { return max((S + 63) / 64, 1); }
+// bins of the longest-first sort: one per chunk count up to 4095 (32 KB of
+// LDS for counters and offsets), longer items share the last bin
+__host__ __device__ inline int plan_bins(int S) { return min(S / kRChunk + 2, 4096); }
+
+__global__ __launch_bounds__(1024) void bwd_tile_plan_kernel(const int* __restrict__ korder,
+                                                             const int* __restrict__ qend, int S,
+                                                             int ktiles, int4* __restrict__ tmp,
+                                                             int4* __restrict__ plan,
+                                                             int* __restrict__ tsplit) {
+  extern __shared__ int hist[];     // nbins counters, then nbins offsets
+  const int seg = blockIdx.x, tid = threadIdx.x, lane = lane_id(), wave = wave_id();
+  const int nbins = plan_bins(S);     // chunk counts, the longest in one bin
+  const int n_ent = 2 * ktiles;
+  const int* ko = korder + (size_t)seg * S;
+  const int* qe = qend + (size_t)seg * S;
+  int4* tm = tmp + (size_t)seg * n_ent;
+  int4* pl = plan + (size_t)seg * n_ent;
+  for (int i = tid; i < 2 * nbins; i += 1024) hist[i] = 0;
+  __syncthreads();
+  // one wave per tile: 64 lanes x 2 keys, then a wave reduction
+  for (int tile = wave; tile < ktiles; tile += 1024 / 64) {
+    int lo = kInt32Max, hi = -1;
+#pragma unroll
+    for (int r = 0; r < kKTile / 64; ++r) {
+      const int slot = tile * kKTile + 64 * r + lane;
+      if (slot < S) {
+        const int t = ko[slot];
+        lo = min(lo, t);
+        hi = max(hi, qe[t]);
+      }
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+      lo = min(lo, __shfl_xor(lo, off));
+      hi = max(hi, __shfl_xor(hi, off));
+    }
+    if (lane == 0) {
+      const int c0 = lo <= hi ? lo / kRChunk : 0;
+      const int n = lo <= hi ? hi / kRChunk - c0 + 1 : 0;
+      int4 e0, e1;
+      if (n > split_threshold(S)) {
+        const int h = n / 2;
+        e0 = make_int4(tile, 0, c0, c0 + h);
+        e1 = make_int4(tile, 1, c0 + h, c0 + n);
+      } else {
+        e0 = make_int4(tile, 0, c0, c0 + n);
+        e1 = make_int4(tile, -1, 0, 0);
+      }
+      tsplit[(size_t)seg * ktiles + tile] = e1.y >= 0 ? 1 : 0;
+      tm[2 * tile] = e0;
+      tm[2 * tile + 1] = e1;
+      atomicAdd(&hist[min(e0.w - e0.z, nbins - 1)], 1);
+      atomicAdd(&hist[min(e1.w - e1.z, nbins - 1)], 1);
+    }
+  }
+  __syncthreads();
+  if (tid == 0) {   // offsets, longest first
+    int run = 0;
+    for (int i = nbins - 1; i >= 0; --i) {
+      hist[nbins + i] = run;
+      run += hist[i];
+    }
+  }
+  __syncthreads();
+  for (int i = tid; i < n_ent; i += 1024) {
+    const int4 e = tm[i];
+    pl[atomicAdd(&hist[nbins + min(e.w - e.z, nbins - 1)], 1)] = e;
+  }
+}
+
+// dK, dV of split tiles: the first half's sums (written to dk, dv) plus the
+// second half's, one float32 add per element.
+template <int D>
+__global__ __launch_bounds__(256) void bwd_dkdv_merge_kernel(BwdArgs a) {
+  const int tile = blockIdx.x % a.ktiles, sg = blockIdx.x / a.ktiles;
+  if (!a.tsplit[(size_t)sg * a.ktiles + tile]) return;
+  const int S = a.S;
+  const size_t kvbase = (size_t)sg * S * D;
+  const float* src = a.part1 + ((size_t)sg * a.ktiles + tile) * kKTile * 2 * D;
+  constexpr int PPK = 2 * D / 4;   // float4 pieces per key (dK then dV)
+  for (int task = threadIdx.x; task < kKTile * PPK; task += 256) {
+    const int j = task / PPK, pc = task % PPK;
+    const int slot = tile * kKTile + j;
+    if (slot >= S) continue;
+    const int t = a.korder[(size_t)sg * S + slot];
+    if (t < 0) continue;
+    float* dst = (pc < D / 4 ? a.dk : a.dv) + kvbase + (size_t)t * D + 4 * (pc % (D / 4));
+    const float4 x = *(const float4*)(src + (size_t)j * 2 * D + 4 * pc);
+    float4 y = *(float4*)dst;
+    y.x += x.x; y.y += x.y; y.z += x.z; y.w += x.w;
+    *(float4*)dst = y;
+  }
+}
+
 // ---------------------------------------------------------------- dK, dV
 template <int D>
 struct KLds {
@@ -370,14 +499,17 @@ __global__ __launch_bounds__(kKThreads) void bwd_dkdv_kernel(BwdArgs a) {
   constexpr int TPT = (NTASK + kKThreads - 1) / kKThreads;   // tasks per thread
   constexpr bool kPartial = NTASK % kKThreads != 0;           // some threads idle (D = 64)
   __shared__ __attribute__((aligned(16))) unsigned char stage[3][L::kStage];
-  __shared__ int s_lo[kKWaves], s_hi[kKWaves];
 
   const int tid = threadIdx.x, lane = lane_id(), wave = wave_id();
   const int hh = lane >> 5, li = lane & 31;
-  // tiles of one (sequence, KV head) go to one XCD in plan order, so the
-  // workgroups sharing an L2 read overlapping rows
+  // the items of one (sequence, KV head) go to one XCD, longest first, so
+  // the workgroups sharing an L2 read overlapping rows
   const int Lb = xcd_logical_block((int)blockIdx.x, (int)gridDim.x);
-  const int tile = Lb % a.ktiles, sg = Lb / a.ktiles;
+  const int n_ent = 2 * a.ktiles;
+  const int sg = Lb / n_ent;
+  const int4 item = a.tplan[(size_t)sg * n_ent + Lb % n_ent];
+  if (item.y < 0) return;            // the empty slot of an unsplit tile (uniform)
+  const int tile = item.x, part = item.y;
   const int h = sg % a.Hkv, b = sg / a.Hkv;
   const int S = a.S, G = a.G;
   const size_t seg = (size_t)b * a.Hkv + h;
@@ -397,17 +529,6 @@ __global__ __launch_bounds__(kKThreads) void bwd_dkdv_kernel(BwdArgs a) {
   const int t_m = t >= 0 ? t : S + kRChunk;
   const size_t kvbase = seg * (size_t)S * D;
 
-  // rows the tile needs: [min t, max q_end]
-  int lo = t >= 0 ? t : kInt32Max, hi = t >= 0 ? qe : -1;
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) {
-    lo = min(lo, __shfl_xor(lo, off));
-    hi = max(hi, __shfl_xor(hi, off));
-  }
-  if (lane == 0) {
-    s_lo[wave] = lo;
-    s_hi[wave] = hi;
-  }
 
   // B operands: K^T and V^T of this lane's key, dims [16 ks + 8 hh, +8)
   // (loaded unconditionally from a clamped row, then zeroed for padding, and
@@ -433,16 +554,11 @@ __global__ __launch_bounds__(kKThreads) void bwd_dkdv_kernel(BwdArgs a) {
     dkacc[d2] = f32x16{};
     dvacc[d2] = f32x16{};
   }
-  __syncthreads();
-  int r_lo = s_lo[0], r_hi = s_hi[0];
-#pragma unroll
-  for (int wv = 1; wv < kKWaves; ++wv) {
-    r_lo = min(r_lo, s_lo[wv]);
-    r_hi = max(r_hi, s_hi[wv]);
-  }
-  // work items: (query head, 32-row chunk) pairs, chunks aligned to 32 rows
-  const int c_first = r_lo <= r_hi ? r_lo / kRChunk : 0;
-  const int n_chunk = r_lo <= r_hi ? r_hi / kRChunk - c_first + 1 : 0;
+  // work items: (query head, 32-row chunk) pairs over the item's chunks,
+  // aligned to 32 rows (the plan's [min t, max q_end] of the tile, or one
+  // half of it)
+  const int c_first = item.z;
+  const int n_chunk = item.w - item.z;
   const int n_items = G * n_chunk;
 
   // staging: each task is (row pair p, piece pc); lanes of a wave cover 16
@@ -621,8 +737,11 @@ __global__ __launch_bounds__(kKThreads) void bwd_dkdv_kernel(BwdArgs a) {
   }
 
   if (t >= 0) {
-    float* dko = a.dk + kvbase + (size_t)t * D;
-    float* dvo = a.dv + kvbase + (size_t)t * D;
+    // the first (or only) part writes dk, dv; the second half of a split
+    // tile writes its sums beside them for the merge
+    float* p1 = a.part1 + (((size_t)sg * a.ktiles + tile) * kKTile + 32 * wave + li) * 2 * D;
+    float* dko = part ? p1 : a.dk + kvbase + (size_t)t * D;
+    float* dvo = part ? p1 + D : a.dv + kvbase + (size_t)t * D;
 #pragma unroll
     for (int d2 = 0; d2 < D / 32; ++d2)
 #pragma unroll
@@ -650,15 +769,23 @@ void launch_bwd_kernels(const Dims& d, BwdArgs a, const void* o, hipStream_t st)
                        (float*)a.dvec, rows);
   const long long nq = (long long)a.ntiles * d.Hkv * d.b;
   hipLaunchKernelGGL((bwd_dq_kernel<D>), dim3((unsigned)nq), dim3(kQThreads), 0, st, a);
-  hipLaunchKernelGGL((bwd_dkdv_kernel<D>), dim3((unsigned)(a.ktiles * d.nseg())), dim3(kKThreads), 0,
+  hipLaunchKernelGGL((bwd_dkdv_kernel<D>), dim3((unsigned)(2 * a.ktiles * d.nseg())),
+                     dim3(kKThreads), 0, st, a);
+  hipLaunchKernelGGL((bwd_dkdv_merge_kernel<D>), dim3((unsigned)(a.ktiles * d.nseg())), dim3(256), 0,
                      st, a);
 }
 
 }  // namespace
 
+static int bwd_ktiles(const Dims& d) { return (d.S + kKTile - 1) / kKTile; }
+
 size_t bwd_ws_bytes(const Dims& d) {
   const size_t rows = (size_t)d.b * d.Hq * d.S, keys = (size_t)d.nseg() * d.S;
-  return fwd_ws_bytes(d) + align256(rows * 4) + align256(keys * 4);
+  const size_t nt = (size_t)d.nseg() * bwd_ktiles(d);
+  return fwd_ws_bytes(d) + align256(rows * 4) + align256(keys * 4) +
+         2 * align256(nt * 2 * 16) +                  // item plan and its unsorted copy
+         align256(nt * 4) +                           // split flags
+         align256(nt * kKTile * 2 * (size_t)d.D * 4);  // second-half sums of split tiles
 }
 
 hipError_t launch_masked_bwd(const Dims& d, const void* q, const void* k, const void* v,
@@ -669,20 +796,29 @@ hipError_t launch_masked_bwd(const Dims& d, const void* q, const void* k, const 
   char* p = (char*)ws + fwd_ws_bytes(d);
   const size_t rows = (size_t)d.b * d.Hq * d.S, keys = (size_t)d.nseg() * d.S;
   float* dvec = (float*)p; p += align256(rows * 4);
-  int* korder = (int*)p;
+  int* korder = (int*)p; p += align256(keys * 4);
+  const int ktiles = bwd_ktiles(d);
+  const size_t nt = (size_t)d.nseg() * ktiles;
+  int4* tplan = (int4*)p; p += align256(nt * 2 * 16);
+  int4* tplan_tmp = (int4*)p; p += align256(nt * 2 * 16);
+  int* tsplit = (int*)p; p += align256(nt * 4);
+  float* part1 = (float*)p;
   const int* qend = pl.qend;   // q_end(t), computed by the forward plan
-  (void)keys;
-  const int nb = 2 * ((d.S + 63) / 64);
+  const int nb = KeyBuckets(d.S).nb;
   hipLaunchKernelGGL(bwd_key_order_kernel, dim3(d.nseg()), dim3(1024), (size_t)nb * 2 * 4, st, qend,
                      korder, d.S, d.w);
+  const int nbins = plan_bins(d.S);
+  hipLaunchKernelGGL(bwd_tile_plan_kernel, dim3(d.nseg()), dim3(1024), (size_t)nbins * 2 * 4, st,
+                     korder, qend, d.S, ktiles, tplan_tmp, tplan, tsplit);
 
   BwdArgs a;
   a.q = (const uint16_t*)q; a.k = (const uint16_t*)k; a.v = (const uint16_t*)v;
   a.dout = (const uint16_t*)dout; a.lse = lse; a.dvec = dvec; a.rank = rank; a.tau = tau;
   a.qend = qend; a.korder = korder; a.list = pl.list; a.count = pl.count;
+  a.tplan = tplan; a.tsplit = tsplit; a.part1 = part1;
   a.dq = dq; a.dk = dk; a.dv = dv;
   a.S = d.S; a.Hq = d.Hq; a.Hkv = d.Hkv; a.G = d.G; a.m = pl.m; a.ntiles = pl.ntiles;
-  a.ktiles = (d.S + kKTile - 1) / kKTile;
+  a.ktiles = ktiles;
   a.s = d.s; a.w = d.w; a.cap = pl.cap;
   a.scale = d.scale;
   a.scale_log2 = d.scale * 1.4426950408889634f;
