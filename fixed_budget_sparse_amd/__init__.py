@@ -14,6 +14,7 @@ from .binding import (  # noqa: F401
     lib,
     library_path,
     abi_version,
+    debug_reverse_launch_order,
     workspace_size,
     thresholds,
     masked_attn_fwd,

@@ -34,6 +34,7 @@ EXPORTED_SYMBOLS = (
     "kvpop_masked_attn_bwd",
     "kvpop_status_string",
     "kvpop_abi_version",
+    "kvpop_debug_reverse_launch_order",
 )
 
 
@@ -92,12 +93,20 @@ def lib() -> ctypes.CDLL:
         L.kvpop_status_string.restype = ctypes.c_char_p
         L.kvpop_abi_version.argtypes = []
         L.kvpop_abi_version.restype = ctypes.c_int32
+        L.kvpop_debug_reverse_launch_order.argtypes = [ctypes.c_int32]
+        L.kvpop_debug_reverse_launch_order.restype = None
         _lib = L
     return _lib
 
 
 def abi_version() -> int:
     return int(lib().kvpop_abi_version())
+
+
+def debug_reverse_launch_order(on: bool) -> None:
+    """Testing aid: launch the forward's, target's and backward's workgroups
+    last tile first (outputs must not change)."""
+    lib().kvpop_debug_reverse_launch_order(1 if on else 0)
 
 
 @dataclasses.dataclass

@@ -3,6 +3,8 @@
 // validates all arguments before its first launch.
 #include <math.h>
 
+#include <atomic>
+
 #include "kvpop.h"
 #include "kvpop_internal.h"
 
@@ -238,3 +240,14 @@ KVPOP_EXPORT const char* kvpop_status_string(int32_t st) {
 }
 
 KVPOP_EXPORT int32_t kvpop_abi_version(void) { return KVPOP_ABI_VERSION; }
+
+namespace kvpop {
+namespace {
+std::atomic<int> g_reverse_launch{0};
+}  // namespace
+int launch_order_reversed() { return g_reverse_launch.load(std::memory_order_relaxed); }
+}  // namespace kvpop
+
+KVPOP_EXPORT void kvpop_debug_reverse_launch_order(int32_t on) {
+  kvpop::g_reverse_launch.store(on != 0 ? 1 : 0, std::memory_order_relaxed);
+}

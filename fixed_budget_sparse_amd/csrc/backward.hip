@@ -177,6 +177,7 @@ struct BwdArgs {
   float* dk;
   float* dv;
   int S, Hq, Hkv, G, m, ntiles, ktiles, s, w, cap;
+  int reverse;         // launch order reversed (testing aid)
   float scale, scale_log2;
 };
 
@@ -199,9 +200,10 @@ __global__ __launch_bounds__(kQThreads, 1) void bwd_dq_kernel(BwdArgs a) {
 
   const int tid = threadIdx.x, lane = lane_id(), wave = wave_id();
   const int hh = lane >> 5, li = lane & 31;
-  const int tile = blockIdx.x % a.ntiles;
-  const int h = (blockIdx.x / a.ntiles) % a.Hkv;
-  const int b = blockIdx.x / (a.ntiles * a.Hkv);
+  const int bid = launch_block(a.reverse);
+  const int tile = bid % a.ntiles;
+  const int h = (bid / a.ntiles) % a.Hkv;
+  const int b = bid / (a.ntiles * a.Hkv);
   const int S = a.S, s = a.s, w = a.w, m = a.m, G = a.G;
   const size_t seg = (size_t)b * a.Hkv + h;
   const int* qend = a.qend + seg * S;
@@ -504,7 +506,7 @@ __global__ __launch_bounds__(kKThreads) void bwd_dkdv_kernel(BwdArgs a) {
   const int hh = lane >> 5, li = lane & 31;
   // the items of one (sequence, KV head) go to one XCD, longest first, so
   // the workgroups sharing an L2 read overlapping rows
-  const int Lb = xcd_logical_block((int)blockIdx.x, (int)gridDim.x);
+  const int Lb = xcd_logical_block(launch_block(a.reverse), (int)gridDim.x);
   const int n_ent = 2 * a.ktiles;
   const int sg = Lb / n_ent;
   const int4 item = a.tplan[(size_t)sg * n_ent + Lb % n_ent];
@@ -820,6 +822,7 @@ hipError_t launch_masked_bwd(const Dims& d, const void* q, const void* k, const 
   a.S = d.S; a.Hq = d.Hq; a.Hkv = d.Hkv; a.G = d.G; a.m = pl.m; a.ntiles = pl.ntiles;
   a.ktiles = ktiles;
   a.s = d.s; a.w = d.w; a.cap = pl.cap;
+  a.reverse = launch_order_reversed();
   a.scale = d.scale;
   a.scale_log2 = d.scale * 1.4426950408889634f;
   if (d.D == 128) launch_bwd_kernels<128>(d, a, o, st);

@@ -57,6 +57,7 @@ struct TgtArgs {
   const float* lse;
   float* target;
   int S, Hq, Hkv, G, w, ntiles;
+  int reverse;         // launch order reversed (testing aid)
   float scale_log2;
 };
 
@@ -182,7 +183,7 @@ __global__ __launch_bounds__(kThreads, 2) void future_target_kernel(TgtArgs a) {
 
   const int tid = threadIdx.x, lane = lane_id(), wave = wave_id();
   const int hh = lane >> 5, li = lane & 31;
-  const int L = xcd_logical_block((int)blockIdx.x, (int)gridDim.x);
+  const int L = xcd_logical_block(launch_block(a.reverse), (int)gridDim.x);
   const int tile = L % a.ntiles;
   const int hq = (L / a.ntiles) % a.Hq;
   const int b = L / (a.ntiles * a.Hq);
@@ -490,6 +491,7 @@ hipError_t launch_future_target(const Dims& d, const void* q, const void* k, con
   TgtArgs a;
   a.q = q; a.k = k; a.lse = lse; a.target = target;
   a.S = d.S; a.Hq = d.Hq; a.Hkv = d.Hkv; a.G = d.G; a.w = d.w; a.ntiles = 0;
+  a.reverse = launch_order_reversed();
   a.scale_log2 = d.scale * 1.4426950408889634f;
   if (d.D == 128) {
     if (d.f32_in) launch_tgt<128, true>(a, d.b, st);

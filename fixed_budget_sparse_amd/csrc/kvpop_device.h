@@ -47,6 +47,13 @@ __device__ __forceinline__ void wave_lds_fence() {
 // with its own L2.  This maps the hardware block id to a logical id such that
 // every XCD receives a contiguous range of logical ids (a bijection on
 // [0, n)), so neighbouring logical blocks, which share data, share an L2.
+// The hardware block index a workgroup takes its work from: blockIdx.x, or
+// counted from the end when the launch order is reversed (a testing aid: no
+// result depends on the order in which workgroups run).
+__device__ __forceinline__ int launch_block(int reversed) {
+  return reversed ? (int)(gridDim.x - 1 - blockIdx.x) : (int)blockIdx.x;
+}
+
 __device__ __forceinline__ int xcd_logical_block(int bid, int n) {
   constexpr int kXcds = 8;
   const int q = n / kXcds, r = n % kXcds;

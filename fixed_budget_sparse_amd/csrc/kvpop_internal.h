@@ -26,6 +26,7 @@ size_t thresholds_ws_bytes(const Dims& d);
 hipError_t launch_thresholds(const Dims& d, const float* prio, int* rank, int* tau,
                              void* ws, hipStream_t st);
 
+int launch_order_reversed();               // testing aid: last tile first when nonzero
 int fwd_rows_per_head(const Dims& d);          // query rows per head in one tile
 size_t fwd_ws_bytes(const Dims& d);
 hipError_t launch_masked_fwd(const Dims& d, const void* q, const void* k, const void* v,

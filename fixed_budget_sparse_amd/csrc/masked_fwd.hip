@@ -52,6 +52,7 @@ struct FwdArgs {
   void* o;
   float* lse;
   int S, Hq, Hkv, G, m, ntiles, s, w, cap;
+  int reverse;         // launch order reversed (testing aid)
   float scale_log2;    // softmax scale * log2(e)
 };
 
@@ -283,7 +284,7 @@ __global__ __launch_bounds__(kThreads, 1) void masked_fwd_kernel(FwdArgs a) {
   const int tid = threadIdx.x, lane = lane_id(), wave = wave_id();
   const int hh = lane >> 5, li = lane & 31;
   if (tid == 0) s_redo = 0;   // read only after the barriers that follow
-  const int Lb = xcd_logical_block((int)blockIdx.x, (int)gridDim.x);
+  const int Lb = xcd_logical_block(launch_block(a.reverse), (int)gridDim.x);
   const int tile = Lb % a.ntiles;
   const int h = (Lb / a.ntiles) % a.Hkv;
   const int b = Lb / (a.ntiles * a.Hkv);
@@ -954,6 +955,7 @@ hipError_t launch_masked_fwd(const Dims& d, const void* q, const void* k, const 
   a.o = o; a.lse = lse;
   a.S = d.S; a.Hq = d.Hq; a.Hkv = d.Hkv; a.G = d.G; a.m = m; a.ntiles = nt;
   a.s = d.s; a.w = d.w; a.cap = cap;
+  a.reverse = launch_order_reversed();
   a.scale_log2 = d.scale * 1.4426950408889634f;
   const int n_wg = nt * d.Hkv * d.b;   // one workgroup per tile
   if (d.D == 128) {

@@ -305,6 +305,14 @@ kvpop_status kvpop_masked_attn_bwd(const kvpop_problem* pr, const void* q, const
 const char* kvpop_status_string(int32_t st);
 int32_t kvpop_abi_version(void);
 
+/* Testing aid, for callers that check determinism: with on != 0, the
+ * masked forward, the future target and the masked backward launch their
+ * workgroups in reverse order (the last tile first) until called again with
+ * 0.  Each workgroup's result depends only on its own tile, so every output
+ * is unchanged bit for bit; only timing and cache locality change.  The
+ * setting is process-wide and read when a call launches. */
+void kvpop_debug_reverse_launch_order(int32_t on);
+
 #ifdef __cplusplus
 }
 #endif

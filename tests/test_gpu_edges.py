@@ -191,3 +191,44 @@ def test_tiny_workload_seed0():
     assert np.array_equal(np.isneginf(tg), np.isneginf(T))
     sel = T > -20
     assert np.abs(tg[sel] - T[sel]).max() <= tol["tgt"], np.abs(tg[sel] - T[sel]).max()
+
+
+def test_reversed_launch_order_bit_identical():
+    """Every tile of the forward, the target and the backward is computed by
+    one workgroup from its own inputs, so the order in which workgroups run
+    must not change a bit of any output: the same calls with the launch
+    order reversed (last tile first) are compared bit for bit.  S = 4096
+    gives 64 forward tiles per KV head and dK/dV tiles that are split in two."""
+    dev = device()
+    announce("reversed launch order")
+    b, hq, hkv, S, D = 1, 8, 2, 4096, 128
+    s, w, k = 8, 256, 700
+    g = torch.Generator(device=dev)
+    g.manual_seed(77)
+    bf = torch.bfloat16
+    q = torch.randn((b, hq, S, D), generator=g, device=dev).to(bf)
+    kk = torch.randn((b, hkv, S, D), generator=g, device=dev).to(bf)
+    v = torch.randn((b, hkv, S, D), generator=g, device=dev).to(bf)
+    prio = torch.randn((b, hkv, S), generator=g, device=dev)
+    dout = torch.randn((b, hq, S, D), generator=g, device=dev).to(bf)
+
+    def run():
+        rank, tau = kv.thresholds(prio, s, w, k)
+        o, lse = kv.masked_attn_fwd(q, kk, v, rank, tau, s, w, k, out_dtype=bf)
+        rank_d, tau_d = kv.thresholds(prio, 0, 1, S)                   # k >= S: dense causal
+        _, lse_d = kv.masked_attn_fwd(q, kk, v, rank_d, tau_d, 0, 1, S)
+        tgt = kv.future_target(q, kk, lse_d, w)
+        dq, dk, dv = kv.masked_attn_bwd(q, kk, v, o, lse, rank, tau, dout, s, w, k)
+        torch.cuda.synchronize()
+        return [x.clone() for x in (o, lse, lse_d, tgt, dq, dk, dv)]
+
+    ref = run()
+    try:
+        kv.debug_reverse_launch_order(True)
+        rev = run()
+    finally:
+        kv.debug_reverse_launch_order(False)
+    names = ("o", "lse", "dense lse", "target", "dq", "dk", "dv")
+    for n, a, c in zip(names, ref, rev):
+        assert torch.equal(a.view(torch.int16 if a.dtype == bf else torch.int32),
+                           c.view(torch.int16 if c.dtype == bf else torch.int32)), n
