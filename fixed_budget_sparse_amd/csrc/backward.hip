@@ -56,6 +56,8 @@ constexpr int kKThreads = 64 * kKWaves;
 constexpr int kRChunk = 32;         // dK/dV: query rows per chunk
 
 typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
+typedef short short4v __attribute__((ext_vector_type(4)));
+typedef short short8v __attribute__((ext_vector_type(8)));
 
 // LDS column of key j (0..63) in a transposed tile whose columns follow the
 // register layout of an MFMA result used as a B operand: column
@@ -181,22 +183,80 @@ struct BwdArgs {
   float scale, scale_log2;
 };
 
+// LDS layout of the dQ kernel's K and V chunks: row-major 64-key chunks of
+// 16-byte pieces, piece p of row r in slot p XOR dq_swz(r).  Row reads (the A
+// operands of S^T = K Q^T and dP^T = V dO^T: 16 lanes read one piece of 16
+// aligned rows) need dq_swz to take 16 distinct slot values over those rows;
+// the transposed reads of K (the A operand K^T of dQ^T += K^T dS^T: a wave
+// reads 64 bytes of each of 8 aligned rows, 16 lanes 32 bytes of 4 rows)
+// need every 16-byte slot of the bank line hit exactly twice.  D = 128 (one
+// row per 256-byte bank line): the two bit pairs of r mod 16 swapped;
+// D = 64 (two rows per line, the row's parity picking the half): a
+// permutation of (r / 2) mod 8 whose top bit is r / 2 mod 2.
 template <int D>
-struct QLds {
-  static constexpr int RS = D + 8;          // row-major rows (bf16 elements)
-  static constexpr int TS = kQChunk + 8;    // transposed rows
-};
+__device__ __forceinline__ int dq_swz(int r) {
+  return D == 128 ? (((r & 3) << 2) | ((r >> 2) & 3)) : ((((r >> 1) & 1) << 2) | ((r >> 2) & 3));
+}
 
+// Byte offsets, per lane, of the transposed K^T operand reads (output block
+// db, half a of the k-step's 8 keys): lane (li, hh) reads row
+// 16 ks + 8 a + 4 hh + jq, dims 32 db + 16 (li / 16) + 4 (j mod 4) .. + 3 with
+// j = li mod 16, jq = j / 4; ds_read_b64_tr_b16 then hands lane i of each
+// 16-lane group element (i mod 4) of the words read by lanes 4e + i/4, so
+// the pair a = 0, 1 is the MFMA operand element 4 a + r = K[16 ks + 8 a +
+// 4 hh + r][32 db + li].  The row's swizzle depends on a but not on ks, so
+// ks enters as an immediate.
+template <int D>
+__device__ __forceinline__ void dq_tr_offsets(int lane, int (&off)[D / 32][2]) {
+  const int hh = lane >> 5, li = lane & 31;
+  const int half = li >> 4, j = li & 15, jq = j >> 2;
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int a8 = 0; a8 < 2; ++a8) {
+      const int row = 8 * a8 + 4 * hh + jq;          // ks = 0
+      const int dim = 32 * db + 16 * half + 4 * (j & 3);
+      off[db][a8] = row * (D * 2) + (((dim >> 3) ^ dq_swz<D>(row)) << 4) + (dim & 7) * 2;
+    }
+}
+
+// dQ, query-major on the forward's tiles and key plan (8 waves, 256 stacked
+// rows): per 64-key chunk, S^T = K Q^T and dP^T = V dO^T on MFMA (each lane
+// owns one row), P = exp(S scale - LSE) on kept keys, dS = P (dP - D) packed
+// to bf16, and dQ^T += K^T dS^T with the K^T operand read transposed from
+// the same LDS chunk.  K and V arrive by direct loads into two LDS stages:
+// the gathers of chunk c+2 are issued after the barrier that ends chunk c
+// into the buffers chunk c used, and awaited before the barrier that ends
+// chunk c+1; the key descriptors (token, q_end - t) of chunk c+2 are read by
+// wave 0 during chunk c and stored before that barrier.
 template <int D>
 __global__ __launch_bounds__(kQThreads, 1) void bwd_dq_kernel(BwdArgs a) {
-  using L = QLds<D>;
   constexpr int NKS = D / 16;
   constexpr int PPR = D / 8;                 // 16-byte pieces per row
-  __shared__ __attribute__((aligned(16))) uint16_t k_lds[kQChunk * L::RS];
-  __shared__ __attribute__((aligned(16))) uint16_t v_lds[kQChunk * L::RS];
-  __shared__ __attribute__((aligned(16))) uint16_t kt_lds[D * L::TS];
-  __shared__ __attribute__((aligned(16))) int kd_t[kQChunk];
-  __shared__ __attribute__((aligned(16))) int kd_span[kQChunk];   // q_end(t) - t
+  constexpr int RB = D * 2;                  // bytes per row
+  constexpr int CB = kQChunk * RB;           // bytes per chunk buffer
+  constexpr int RPI = 1024 / RB;             // rows per 1 KB direct load
+  constexpr int NDMA = kQChunk / RPI / (kQThreads / 64);   // direct loads per wave per chunk
+  static_assert(NDMA * RPI * (kQThreads / 64) == kQChunk, "direct-load tiling");
+  constexpr int kSlots = 4;                  // descriptor slots (chunks c .. c+2 live)
+  // K buffers first (their transposed reads reach furthest past their base);
+  // equal-sized arrays are laid out in name order
+  __shared__ __attribute__((aligned(16))) unsigned char dqa_k0[CB];
+  __shared__ __attribute__((aligned(16))) unsigned char dqa_k1[CB];
+  __shared__ __attribute__((aligned(16))) unsigned char dqb_v0[CB];
+  __shared__ __attribute__((aligned(16))) unsigned char dqb_v1[CB];
+  __shared__ __attribute__((aligned(16))) int kd_t[kSlots][kQChunk];
+  __shared__ __attribute__((aligned(16))) int kd_span[kSlots][kQChunk];   // q_end(t) - t
+  auto kbuf = [&](auto i) -> unsigned char* {
+    if constexpr (decltype(i)::value == 0) return dqa_k0;
+    else return dqa_k1;
+  };
+  auto vbuf = [&](auto i) -> unsigned char* {
+    if constexpr (decltype(i)::value == 0) return dqb_v0;
+    else return dqb_v1;
+  };
+  using C0 = std::integral_constant<int, 0>;
+  using C1 = std::integral_constant<int, 1>;
 
   const int tid = threadIdx.x, lane = lane_id(), wave = wave_id();
   const int hh = lane >> 5, li = lane & 31;
@@ -237,11 +297,12 @@ __global__ __launch_bounds__(kQThreads, 1) void bwd_dq_kernel(BwdArgs a) {
   const int band_lo = max(s, q0 - w + 1);
   const int n_band = max(0, q_hi - band_lo + 1);
   const int nk = n_sink + n_long + n_band;
+  const int nchunk = (nk + kQChunk - 1) / kQChunk;
   const int2* lst = a.list + (seg * a.ntiles + tile) * (size_t)a.cap;
 
   // B operands: Q^T and dO^T of this lane's row, dims [16 ks + 8 hh, +8)
-  // (unconditional loads of a valid row, zeroed for padding rows, completed
-  // here so that the chunk loop does not wait on them)
+  // (unconditional loads of a valid row, zeroed for padding rows; completed
+  // before the chunk loop so that it does not wait on them)
   bf16x8 qop[NKS], dop[NKS];
 #pragma unroll
   for (int ks = 0; ks < NKS; ++ks) {
@@ -251,87 +312,98 @@ __global__ __launch_bounds__(kQThreads, 1) void bwd_dq_kernel(BwdArgs a) {
     qop[ks] = __builtin_bit_cast(bf16x8, u);
     dop[ks] = __builtin_bit_cast(bf16x8, x);
   }
-#pragma unroll
-  for (int ks = 0; ks < NKS; ++ks) asm volatile("" : "+v"(qop[ks]), "+v"(dop[ks]));
   f32x16 dqacc[D / 32];
 #pragma unroll
   for (int d2 = 0; d2 < D / 32; ++d2) dqacc[d2] = f32x16{};
 
-  const size_t kvbase = seg * (size_t)S * D;
-  for (int c0 = 0; c0 < nk; c0 += kQChunk) {
-    // descriptors: token and span q_end(t) - t of the chunk's keys (token
-    // -1 and span 0 for padding).  Row q keeps key t iff t <= q <= q_end(t)
-    // (tau never increases with q, so the rows that keep a key are one
-    // interval), one unsigned compare per score; a padding key fails it
-    // (q + 1 > 0).
-    if (tid < kQChunk) {
-      const int j = c0 + tid;
-      int t = -1;
-      if (j < n_sink) {
-        t = j;
-      } else if (j < n_sink + n_long) {
-        t = listed ? lst[j - n_sink].x : s + (j - n_sink);
-      } else if (j < nk) {
-        t = band_lo + (j - n_sink - n_long);
-      }
-      kd_t[tid] = t;
-      kd_span[tid] = t >= 0 ? qend[t] - t : 0;
+  // ---- key descriptors of the chunk starting at c0: wave 0 reads them
+  // (branch-free, clamped) into registers, and stores token and span
+  // q_end(t) - t (token -1, span 0 for padding) one phase later
+  struct Desc {
+    int t, r;
+    int2 l;
+  };
+  auto desc_fetch = [&](int c0, Desc& d) {
+    if (wave == 0) {
+      const int j = c0 + lane;
+      const bool in_sink = j < n_sink;
+      const bool in_long = !in_sink && j < n_sink + n_long;
+      const bool in_band = !in_sink && !in_long && j < nk;
+      const int t = in_sink ? j
+                    : in_long ? s + (j - n_sink)
+                    : in_band ? band_lo + (j - n_sink - n_long) : -1;
+      if (listed) d.l = lst[min(max(j - n_sink, 0), max(n_long - 1, 0))];
+      d.r = qend[min(max(t, 0), S - 1)];
+      d.t = (in_long && listed) ? -2 : t;    // -2: token and q_end from the list
     }
-    __syncthreads();
-    // gather K, V rows: row-major K and V, transposed K with permuted columns.
-    // A task is (key pair, 16-byte piece); keys 2p and 2p+1 sit in adjacent
-    // transposed columns, so each dim is one 32-bit word, and the 32 pairs of
-    // a half-wave spread over the banks.  Loads are unconditional from a
-    // valid row (padding slots read row 0 and are zeroed).
-    for (int task = tid; task < (kQChunk / 2) * PPR; task += kQThreads) {
-      const int p = task & (kQChunk / 2 - 1), pc = task / (kQChunk / 2);
-      u32x4v kx[2], vx[2];
-#pragma unroll
-      for (int r = 0; r < 2; ++r) {
-        const int t = kd_t[2 * p + r];
-        const size_t row = kvbase + (size_t)max(t, 0) * D + 8 * pc;
-        kx[r] = *(const u32x4v*)(a.k + row);
-        vx[r] = *(const u32x4v*)(a.v + row);
-        if (t < 0) kx[r] = vx[r] = u32x4v{0, 0, 0, 0};
-        *(u32x4v*)(k_lds + (2 * p + r) * L::RS + 8 * pc) = kx[r];
-        *(u32x4v*)(v_lds + (2 * p + r) * L::RS + 8 * pc) = vx[r];
-      }
-      uint32_t* ktw = (uint32_t*)kt_lds;
-      const int cw = perm_col(2 * p) >> 1;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const uint32_t ka = kx[0][e], kb = kx[1][e];
-        const int d0 = 8 * pc + 2 * e;
-        ktw[d0 * (L::TS / 2) + cw] = (ka & 0xffffu) | (kb << 16);
-        ktw[(d0 + 1) * (L::TS / 2) + cw] = (ka >> 16) | (kb & 0xffff0000u);
-      }
+  };
+  auto desc_put = [&](int slot, const Desc& d) {
+    if (wave == 0) {
+      int t = d.t == -2 ? d.l.x : d.t;
+      const int e = d.t == -2 ? d.l.y : d.r;
+      if (t >= S) t = -1;
+      kd_t[slot][lane] = t;
+      kd_span[slot][lane] = t >= 0 ? e - t : 0;
     }
-    __syncthreads();
+  };
 
-    // S^T = K Q^T and dP^T = V dO^T: two 32-key blocks, lane owns its row
+  // ---- gathers: each 1 KB direct load fills RPI rows; lane L fetches the
+  // global piece that the row's swizzle places at its slot (padding keys
+  // read row 0: they are masked, so only finiteness matters)
+  typedef __attribute__((address_space(3))) void lds_void;
+  const size_t kvbase = seg * (size_t)S * D;
+  auto dma_rows = [&](const uint16_t* src, unsigned char* dst, int slot) {
+    const unsigned char* gsrc = (const unsigned char*)(src + kvbase);
+#pragma unroll
+    for (int i = 0; i < NDMA; ++i) {
+      const int r0 = (wave * NDMA + i) * RPI;
+      const int row = r0 + lane / PPR, sl = lane % PPR;
+      const int t = min(max(kd_t[slot][row], 0), S - 1);
+      const int piece = sl ^ dq_swz<D>(row);
+      __builtin_amdgcn_global_load_lds((const void*)(gsrc + ((size_t)t * PPR + piece) * 16),
+                                       (lds_void*)(dst + r0 * RB), 16, 0, 0);
+    }
+  };
+  auto dma_chunk = [&](int c, auto bi) {
+    dma_rows(a.k, kbuf(bi), c % kSlots);
+    dma_rows(a.v, vbuf(bi), c % kSlots);
+  };
+
+  // per-lane LDS offsets: row reads (row li, piece 2 ks + hh: base XOR 32 ks)
+  // and the transposed K^T reads
+  int tro[D / 32][2];
+  dq_tr_offsets<D>(lane, tro);
+  const int row_base = li * RB + ((hh ^ dq_swz<D>(li)) << 4);
+
+  // ---- one chunk from the buffers bi: S, dP, dS, dQ
+  auto chunk = [&](int c, auto bi) {
+    const unsigned char* kl = kbuf(bi);
+    const unsigned char* vl = vbuf(bi);
+    int rb = row_base;
+    asm volatile("" : "+v"(rb));   // keeps the eight XORs below in the loop
     f32x16 sacc[2], pacc[2];
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk) {
       sacc[blk] = f32x16{};
       pacc[blk] = f32x16{};
-      const uint16_t* kl = k_lds + (32 * blk + li) * L::RS + 8 * hh;
-      const uint16_t* vl = v_lds + (32 * blk + li) * L::RS + 8 * hh;
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) {
-        sacc[blk] = mfma32x32x16(as_bf16x8(*(const uint4*)(kl + 16 * ks)), qop[ks], sacc[blk]);
-        pacc[blk] = mfma32x32x16(as_bf16x8(*(const uint4*)(vl + 16 * ks)), dop[ks], pacc[blk]);
+        const int off = 32 * blk * RB + (rb ^ (32 * ks));
+        sacc[blk] = mfma32x32x16(as_bf16x8(*(const uint4*)(kl + off)), qop[ks], sacc[blk]);
+        pacc[blk] = mfma32x32x16(as_bf16x8(*(const uint4*)(vl + off)), dop[ks], pacc[blk]);
       }
     }
     // dS = P (dP - D_i), P = exp(S scale - LSE_i) on kept keys (branch-free:
-    // the exp of every score, then a select; the key data in 4-wide reads)
+    // the exp of every score, then a select; key data in 4-wide reads)
+    const int slot = c % kSlots;
     float dsv[2][16];
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
         const int j0 = 32 * blk + 8 * jj + 4 * hh;
-        const int4 t4 = *(const int4*)(kd_t + j0);
-        const int4 r4 = *(const int4*)(kd_span + j0);
+        const int4 t4 = *(const int4*)(&kd_t[slot][j0]);
+        const int4 r4 = *(const int4*)(&kd_span[slot][j0]);
         const int tv[4] = {t4.x, t4.y, t4.z, t4.w}, rv[4] = {r4.x, r4.y, r4.z, r4.w};
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
@@ -346,14 +418,51 @@ __global__ __launch_bounds__(kQThreads, 1) void bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) pk[ks] = pack_bf16x8(&dsv[ks >> 1][8 * (ks & 1)]);
     // dQ^T += K^T dS^T
+    typedef __attribute__((address_space(3))) short4v lds_s4;
 #pragma unroll
-    for (int d2 = 0; d2 < D / 32; ++d2) {
-      const uint16_t* ktl = kt_lds + (32 * d2 + li) * L::TS + 8 * hh;
+    for (int d2 = 0; d2 < D / 32; ++d2)
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks)
-        dqacc[d2] = mfma32x32x16(as_bf16x8(*(const uint4*)(ktl + 16 * ks)), pk[ks], dqacc[d2]);
-    }
-    __syncthreads();   // the chunk's LDS is rewritten next
+      for (int ks = 0; ks < 4; ++ks) {
+        const short4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_s4*)(kl + tro[d2][0] + 16 * ks * RB));
+        const short4v hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_s4*)(kl + tro[d2][1] + 16 * ks * RB));
+        const short8v v8 = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        dqacc[d2] = mfma32x32x16(__builtin_bit_cast(bf16x8, v8), pk[ks], dqacc[d2]);
+      }
+  };
+
+  // ---- prologue: descriptors of chunks 0 and 1 (every read issued before
+  // the first store), their gathers, the query loads completed
+  {
+    Desc d0{-1, 0, make_int2(-1, 0)}, d1{-1, 0, make_int2(-1, 0)};
+    desc_fetch(0, d0);
+    desc_fetch(kQChunk, d1);
+    desc_put(0, d0);
+    desc_put(1, d1);
+    __syncthreads();
+    dma_chunk(0, C0{});
+    dma_chunk(1, C1{});
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) asm volatile("" : "+v"(qop[ks]), "+v"(dop[ks]));
+    __syncthreads();
+  }
+  // ---- chunk c reads buffers c mod 2; after the barrier that ends it, the
+  // gathers of chunk c+2 go into those buffers (compile-time buffer indices:
+  // unrolled by two)
+  Desc pd{-1, 0, make_int2(-1, 0)};
+  auto step = [&](int c, auto bi) {
+    desc_fetch((c + 2) * kQChunk, pd);
+    chunk(c, bi);
+    desc_put((c + 2) % kSlots, pd);
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): the gathers of chunk c+1
+    __syncthreads();
+    if (c + 2 < nchunk) dma_chunk(c + 2, bi);
+  };
+  for (int c = 0; c < nchunk; c += 2) {
+    step(c, C0{});
+    if (c + 1 < nchunk) step(c + 1, C1{});
   }
 
   if (row_ok) {
@@ -373,16 +482,19 @@ __global__ __launch_bounds__(kQThreads, 1) void bwd_dq_kernel(BwdArgs a) {
 // ---------------------------------------------------------------- dK, dV plan
 // Work items of the dK/dV kernel, one workgroup per (sequence, KV head): each
 // 128-key tile of the key order needs the 32-row chunks [min t, max q_end];
-// a tile needing more than half the sequence's chunks is split into two
-// items (the first and second half of its chunks), so that no single
-// workgroup streams the whole sequence (the sinks' tile and the tiles of
-// early tokens kept to the end otherwise set the kernel's length alone).
-// The items are listed longest first (a counting sort on the chunk count),
-// so each XCD starts its longest items first; empty item slots (the second
-// slot of an unsplit tile) come last and exit at once.  A tile's keys are
-// those of the key order, so the split changes no key's chunk sums; the
-// second half's sums are added to the first half's in a fixed order.
-__device__ __forceinline__ int split_threshold(int S) { return max((S + 63) / 64, 1); }
+// a tile whose chunks cross the fixed split row R = S/2 (rounded down to a
+// chunk) becomes two items, the chunks below R and the chunks from R on, so
+// no single workgroup streams more than half the sequence (the sinks' tile
+// and the tiles of early tokens kept to the end otherwise set the kernel's
+// length alone).  The split row is the same for every tile, so every key
+// whose rows cross R is summed as (rows below R) + (rows from R), and any
+// other key gets an exact zero from its tile's other half, whatever tile the
+// key order put it in (the order inside a bucket is not fixed): dk and dv do
+// not depend on the order.  The items are listed longest first (a counting
+// sort on the chunk count), so each XCD starts its longest items first;
+// empty item slots (the second slot of an unsplit tile) come last and exit
+// at once.
+__device__ __forceinline__ int split_chunk(int S) { return (S / 2) / kRChunk; }
 // bins of the longest-first sort: one per chunk count up to 4095 (32 KB of
 // LDS for counters and offsets), longer items share the last bin
 __host__ __device__ inline int plan_bins(int S) { return min(S / kRChunk + 2, 4096); }
@@ -423,10 +535,10 @@ __global__ __launch_bounds__(1024) void bwd_tile_plan_kernel(const int* __restri
       const int c0 = lo <= hi ? lo / kRChunk : 0;
       const int n = lo <= hi ? hi / kRChunk - c0 + 1 : 0;
       int4 e0, e1;
-      if (n > split_threshold(S)) {
-        const int h = n / 2;
-        e0 = make_int4(tile, 0, c0, c0 + h);
-        e1 = make_int4(tile, 1, c0 + h, c0 + n);
+      const int cs = split_chunk(S);
+      if (c0 < cs && cs < c0 + n) {
+        e0 = make_int4(tile, 0, c0, cs);
+        e1 = make_int4(tile, 1, cs, c0 + n);
       } else {
         e0 = make_int4(tile, 0, c0, c0 + n);
         e1 = make_int4(tile, -1, 0, 0);
