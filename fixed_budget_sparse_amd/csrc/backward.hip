@@ -591,30 +591,43 @@ __global__ __launch_bounds__(256) void bwd_dkdv_merge_kernel(BwdArgs a) {
 
 // ---------------------------------------------------------------- dK, dV
 template <int D>
-struct KLds {
-  static constexpr int RS = D + 8;          // row-major rows (bf16 elements)
-  static constexpr int TS = kRChunk + 8;    // transposed rows
-  // one stage: Q and dO row-major and transposed, then LSE and D per row
-  static constexpr int kQ = 0;
-  static constexpr int kO = kQ + kRChunk * RS * 2;
-  static constexpr int kQT = kO + kRChunk * RS * 2;
-  static constexpr int kOT = kQT + D * TS * 2;
-  static constexpr int kLse = kOT + D * TS * 2;
-  static constexpr int kD = kLse + kRChunk * 4;
-  static constexpr int kStage = kD + kRChunk * 4;
-};
-
-template <int D>
 __global__ __launch_bounds__(kKThreads) void bwd_dkdv_kernel(BwdArgs a) {
-  using L = KLds<D>;
   constexpr int NKS = D / 16;
   constexpr int PPR = D / 8;                         // 16-byte pieces per row
-  constexpr int NTASK = (kRChunk / 2) * PPR;         // (row pair, piece) per tensor
-  constexpr int TPT = (NTASK + kKThreads - 1) / kKThreads;   // tasks per thread
-  constexpr bool kPartial = NTASK % kKThreads != 0;           // some threads idle (D = 64)
-  __shared__ __attribute__((aligned(16))) unsigned char stage[3][L::kStage];
+  constexpr int RB = D * 2;                          // bytes per row
+  constexpr int CB = kRChunk * RB;                   // bytes of one tensor's chunk
+  constexpr int RPI = 1024 / RB;                     // rows per 1 KB direct load
+  constexpr int NDMA = kRChunk / RPI / kKWaves;      // direct loads per wave per tensor
+  constexpr int NLD = 2 * NDMA + 1;                  // direct loads per wave per item
+  static_assert(NDMA >= 1 && NDMA * RPI * kKWaves == kRChunk, "direct-load tiling");
+  static_assert(kRChunk == 32 && kKWaves == 4, "row-value load: 64 floats, 16 per wave");
+  // Four stages, each one array: the rows' LSE and D (64 floats), then the
+  // Q rows, then the dO rows (row-major, swizzled like the dQ kernel's K:
+  // read as rows for S and dP and transposed for dK and dV).  One array per
+  // stage keeps the direct-load targets few enough for the compiler to tell
+  // them apart (it then knows that loads in flight into one stage do not
+  // alias the reads of another) and every stage offset an immediate.
+  constexpr int SB = 2 * kRChunk * 4 + 2 * CB;       // bytes per stage
+  __shared__ __attribute__((aligned(16))) unsigned char kvst0[SB];
+  __shared__ __attribute__((aligned(16))) unsigned char kvst1[SB];
+  __shared__ __attribute__((aligned(16))) unsigned char kvst2[SB];
+  __shared__ __attribute__((aligned(16))) unsigned char kvst3[SB];
+  auto stage = [&](auto i) -> unsigned char* {
+    constexpr int I = decltype(i)::value;
+    if constexpr (I == 0) return kvst0;
+    else if constexpr (I == 1) return kvst1;
+    else if constexpr (I == 2) return kvst2;
+    else return kvst3;
+  };
+  auto rbuf = [&](auto i) { return (float*)stage(i); };
+  auto qbuf = [&](auto i) { return stage(i) + 2 * kRChunk * 4; };
+  auto obuf = [&](auto i) { return stage(i) + 2 * kRChunk * 4 + CB; };
+  using C0 = std::integral_constant<int, 0>;
+  using C1 = std::integral_constant<int, 1>;
+  using C2 = std::integral_constant<int, 2>;
+  using C3 = std::integral_constant<int, 3>;
 
-  const int tid = threadIdx.x, lane = lane_id(), wave = wave_id();
+  const int lane = lane_id(), wave = wave_id();
   const int hh = lane >> 5, li = lane & 31;
   // the items of one (sequence, KV head) go to one XCD, longest first, so
   // the workgroups sharing an L2 read overlapping rows
@@ -643,7 +656,6 @@ __global__ __launch_bounds__(kKThreads) void bwd_dkdv_kernel(BwdArgs a) {
   const int t_m = t >= 0 ? t : S + kRChunk;
   const size_t kvbase = seg * (size_t)S * D;
 
-
   // B operands: K^T and V^T of this lane's key, dims [16 ks + 8 hh, +8)
   // (loaded unconditionally from a clamped row, then zeroed for padding, and
   // completed here: loads still pending at the loop would make the compiler
@@ -670,151 +682,124 @@ __global__ __launch_bounds__(kKThreads) void bwd_dkdv_kernel(BwdArgs a) {
   }
   // work items: (query head, 32-row chunk) pairs over the item's chunks,
   // aligned to 32 rows (the plan's [min t, max q_end] of the tile, or one
-  // half of it)
+  // part of it)
   const int c_first = item.z;
   const int n_chunk = item.w - item.z;
   const int n_items = G * n_chunk;
 
-  // staging: each task is (row pair p, piece pc); lanes of a wave cover 16
-  // pairs of 4 pieces, so their transposed word stores spread over the banks
-  u32x4v rq_[1][TPT][2], ro_[1][TPT][2];
-  float rv_[1][2] = {{0.0f, 0.0f}};
   // items in order: query head gg, then chunk ci; the (gg, ci) of an item are
-  // stepped rather than divided out of its index (scalar division is a long
-  // instruction sequence, and one wave per SIMD runs it in line)
+  // stepped rather than divided out of its index
   struct ItemPos {
     int gg, ci;
   };
   auto next_pos = [&](ItemPos p) {
     return p.ci + 1 < n_chunk ? ItemPos{p.gg, p.ci + 1} : ItemPos{p.gg + 1, 0};
   };
-  auto load = [&](ItemPos ip, auto slot) {
-    constexpr int sl = decltype(slot)::value;
-    auto& rq = rq_[sl];
-    auto& ro = ro_[sl];
-    auto& r_val = rv_[sl];
-    const int gg = ip.gg, c0 = (c_first + ip.ci) * kRChunk;
-    const size_t hrow = ((size_t)b * a.Hq + h * G + gg) * S;
+  // ---- staging of one item, all by direct loads (lane L of a load writes
+  // 16 L, or 4 L, bytes past the load's LDS base): the Q and dO rows, lane L
+  // fetching the global piece its swizzled slot holds, and the rows' LSE
+  // (lanes 0..31) and D (lanes 32..63), 16 lanes in each wave.  Rows past
+  // the end read row S - 1 and are masked.  Each wave issues NLD loads.
+  auto dma_item = [&](ItemPos ip, auto st) {
+    const size_t hrow = ((size_t)b * a.Hq + h * G + ip.gg) * S;
+    const int c0 = (c_first + ip.ci) * kRChunk;
 #pragma unroll
-    for (int i = 0; i < TPT; ++i) {
-      const int task = tid + i * kKThreads;
-      if (kPartial && task >= NTASK) break;           // whole waves idle
-      const int p = task & 15, pc = task >> 4;
-#pragma unroll
-      for (int r = 0; r < 2; ++r) {
-        const int qq = min(c0 + 2 * p + r, S - 1);   // rows past the end: masked below
-        rq[i][r] = *(const u32x4v*)(a.q + (hrow + qq) * D + 8 * pc);
-        ro[i][r] = *(const u32x4v*)(a.dout + (hrow + qq) * D + 8 * pc);
-      }
+    for (int i = 0; i < NDMA; ++i) {
+      const int r0 = (wave * NDMA + i) * RPI;
+      const int row = r0 + lane / PPR, sl = lane % PPR;
+      const int qq = min(c0 + row, S - 1);
+      const size_t off = ((hrow + qq) * PPR + (sl ^ dq_swz<D>(row))) * 16;
+      dma_lds_x4((const unsigned char*)a.q + off, qbuf(st) + r0 * RB);
+      dma_lds_x4((const unsigned char*)a.dout + off, obuf(st) + r0 * RB);
     }
-    {   // every lane loads (no exec-masked loads); lanes below kRChunk store
-      const int qq = min(c0 + (tid & (kRChunk - 1)), S - 1);
-      r_val[0] = a.lse[hrow + qq];
-      r_val[1] = a.dvec[hrow + qq];
-    }
-  };
-  auto store = [&](int buf, auto slot) {
-    constexpr int sl = decltype(slot)::value;
-    auto& rq = rq_[sl];
-    auto& ro = ro_[sl];
-    auto& r_val = rv_[sl];
-    unsigned char* st = stage[buf];
-    uint16_t* ql = (uint16_t*)(st + L::kQ);
-    uint16_t* ol = (uint16_t*)(st + L::kO);
-    uint32_t* qt = (uint32_t*)(st + L::kQT);
-    uint32_t* ot = (uint32_t*)(st + L::kOT);
-#pragma unroll
-    for (int i = 0; i < TPT; ++i) {
-      const int task = tid + i * kKThreads;
-      if (kPartial && task >= NTASK) break;
-      const int p = task & 15, pc = task >> 4;
-#pragma unroll
-      for (int r = 0; r < 2; ++r) {
-        *(u32x4v*)(ql + (2 * p + r) * L::RS + 8 * pc) = rq[i][r];
-        *(u32x4v*)(ol + (2 * p + r) * L::RS + 8 * pc) = ro[i][r];
-      }
-      // rows 2p and 2p+1 sit in adjacent columns: one word per dim
-      const int cw = perm_col(2 * p) >> 1;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const uint32_t qa = rq[i][0][e], qb = rq[i][1][e];
-        const uint32_t oa = ro[i][0][e], ob = ro[i][1][e];
-        const int d0 = 8 * pc + 2 * e;
-        qt[d0 * (L::TS / 2) + cw] = (qa & 0xffffu) | (qb << 16);
-        qt[(d0 + 1) * (L::TS / 2) + cw] = (qa >> 16) | (qb & 0xffff0000u);
-        ot[d0 * (L::TS / 2) + cw] = (oa & 0xffffu) | (ob << 16);
-        ot[(d0 + 1) * (L::TS / 2) + cw] = (oa >> 16) | (ob & 0xffff0000u);
-      }
-    }
-    if (tid < kRChunk) {
-      ((float*)(st + L::kLse))[tid] = r_val[0] * kLog2e;
-      ((float*)(st + L::kD))[tid] = r_val[1];
+    if ((lane >> 4) == wave) {
+      const int qq = min(c0 + (lane & 31), S - 1);
+      dma_lds_x1((hh ? a.dvec : a.lse) + hrow + qq, rbuf(st));
     }
   };
 
-  // Item it is staged in LDS buffer it % 3, and the dV and dK products of an
-  // item run one iteration late: iteration it runs the S and dP products of
-  // item it beside the store of item it+1 (loaded one iteration earlier) into
-  // the buffer of item it-2, then the probability and dS math of item it
-  // beside the dV and dK products of item it-1 (its P and dS kept in
-  // registers), and issues the loads of item it+2 into the freed registers.
-  // The loads are unconditional (past the last item they repeat it): loads
-  // into one of two register sets chosen at run time were compiled as loads
-  // into temporaries plus copies that waited for them at once, which exposed
-  // the whole load latency on every item.
-  using S0 = std::integral_constant<int, 0>;
-  auto dkdv = [&](int buf, const bf16x8 (&pp)[2], const bf16x8 (&ps)[2]) {
-    const unsigned char* st = stage[buf];
+  // per-lane LDS offsets: row reads (row li, piece 2 ks + hh: base XOR 32 ks)
+  // and the transposed reads
+  int tro[D / 32][2];
+  dq_tr_offsets<D>(lane, tro);
+  const int row_base = li * RB + ((hh ^ dq_swz<D>(li)) << 4);
+  typedef __attribute__((address_space(3))) short4v lds_s4;
+  auto tr_operand = [&](const unsigned char* buf, int db, int ks) {
+    const short4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)(buf + tro[db][0] + 16 * ks * RB));
+    const short4v hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)(buf + tro[db][1] + 16 * ks * RB));
+    const short8v v8 = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    return __builtin_bit_cast(bf16x8, v8);
+  };
+  // dV^T += dO^T P and dK^T += Q^T dS of an item staged in st
+  auto dkdv = [&](auto st, const bf16x8 (&pp)[2], const bf16x8 (&ps)[2]) {
 #pragma unroll
-    for (int d2 = 0; d2 < D / 32; ++d2) {   // dV^T += dO^T P and dK^T += Q^T dS
-      const uint16_t* otl = (const uint16_t*)(st + L::kOT) + (32 * d2 + li) * L::TS + 8 * hh;
-      const uint16_t* qtl = (const uint16_t*)(st + L::kQT) + (32 * d2 + li) * L::TS + 8 * hh;
+    for (int d2 = 0; d2 < D / 32; ++d2)
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
-        dvacc[d2] = mfma32x32x16(as_bf16x8(*(const uint4*)(otl + 16 * ks)), pp[ks], dvacc[d2]);
-        dkacc[d2] = mfma32x32x16(as_bf16x8(*(const uint4*)(qtl + 16 * ks)), ps[ks], dkacc[d2]);
+        dvacc[d2] = mfma32x32x16(tr_operand(obuf(st), d2, ks), pp[ks], dvacc[d2]);
+        dkacc[d2] = mfma32x32x16(tr_operand(qbuf(st), d2, ks), ps[ks], dkacc[d2]);
+      }
+  };
+
+  // Item it is staged in stage it mod 4, two items ahead, and the dV and dK
+  // products of an item run one iteration late: iteration it issues the
+  // direct loads of item it+2 into the stage of item it-2 (whose last reads,
+  // its dV and dK products, were in the previous iteration), runs the S and
+  // dP products of item it, then the probability and dS math of item it
+  // beside the dV and dK products of item it-1 (its P and dS kept in
+  // registers), waits for this wave's loads of item it+1 (those of item it+2
+  // may stay in flight: the counter drains in order) and ends with a barrier
+  // that publishes every wave's part.  The loop body is four iterations with
+  // no exit between them (the stages rotate over four and the P / dS
+  // register sets over two, all compile-time): the item count is padded to a
+  // multiple of four with masked items, whose P and dS are zero, and loads
+  // past the last item repeat the last item's rows into a stage no later
+  // read uses.
+  const int n_pad = (n_items + 3) & ~3;
+  auto clamp_pos = [&](ItemPos p) { return ItemPos{min(p.gg, G - 1), p.ci}; };
+  ItemPos cur{0, 0}, nx1{0, 0}, nx2{0, 0};   // items it, it+1, it+2
+  if (n_items > 0) {
+    dma_item(cur, C0{});
+    nx1 = next_pos(cur);
+    dma_item(clamp_pos(nx1), C1{});
+    nx2 = next_pos(nx1);
+    {   // the first iteration's dV and dK products read stage 3 with zero P
+        // and dS: zero it (0 times a stale NaN is not 0)
+      uint4* zq = (uint4*)qbuf(C3{});
+      uint4* zo = (uint4*)obuf(C3{});
+      for (int i = threadIdx.x; i < CB / 16; i += kKThreads) {
+        zq[i] = make_uint4(0, 0, 0, 0);
+        zo[i] = make_uint4(0, 0, 0, 0);
       }
     }
-  };
-  ItemPos cur{0, 0};                                  // item it
-  ItemPos ahead = n_items > 1 ? next_pos(cur) : cur;  // item min(it + 1, n_items - 1)
-  if (n_items > 0) {
-    load(cur, S0{});
-    store(0, S0{});
-    load(ahead, S0{});
-    {   // the first iteration's dV and dK products read buffer 2's transposed
-        // tiles with zero P and dS: zero them (0 times a stale NaN is not 0)
-      uint4* z = (uint4*)(stage[2] + L::kQT);
-      for (int i = tid; i < (L::kLse - L::kQT) / 16; i += kKThreads) z[i] = make_uint4(0, 0, 0, 0);
-    }
-    __syncthreads();
+    __builtin_amdgcn_s_waitcnt(0x0F70 | NLD);   // item 0 landed
+    lds_barrier();
   }
   bf16x8 ppA[2] = {}, psA[2] = {}, ppB[2] = {}, psB[2] = {};
-  auto step = [&](int it, const bf16x8 (&pp_prev)[2], const bf16x8 (&ps_prev)[2],
-                  bf16x8 (&pp)[2], bf16x8 (&ps)[2]) {
-    const int b_cur = it % 3, b_prev = (it + 2) % 3, b_st = (it + 1) % 3;
-    const int c0 = (c_first + cur.ci) * kRChunk;
-    const unsigned char* st = stage[b_cur];
-    const uint16_t* ql = (const uint16_t*)(st + L::kQ) + li * L::RS + 8 * hh;
-    const uint16_t* ol = (const uint16_t*)(st + L::kO) + li * L::RS + 8 * hh;
-    const float* r_lse = (const float*)(st + L::kLse);
-    const float* r_d = (const float*)(st + L::kD);
-
+  auto step = [&](int it, auto s_cur, auto s_prev, auto s_far, const bf16x8 (&pp_prev)[2],
+                  const bf16x8 (&ps_prev)[2], bf16x8 (&pp)[2], bf16x8 (&ps)[2]) {
+    // rows of a padding item fall outside every key's span
+    const int c0 = it < n_items ? (c_first + cur.ci) * kRChunk : -(1 << 30);
+    dma_item(clamp_pos(nx2), s_far);
+    const unsigned char* ql = qbuf(s_cur);
+    const unsigned char* ol = obuf(s_cur);
+    int rb = row_base;
+    asm volatile("" : "+v"(rb));   // keeps the XORs below in the loop
     // S = Q K^T and dP = dO V^T (32 rows x 32 keys): lane owns its key
     f32x16 sacc = f32x16{}, pacc = f32x16{};
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
-      sacc = mfma32x32x16(as_bf16x8(*(const uint4*)(ql + 16 * ks)), kop[ks], sacc);
-      pacc = mfma32x32x16(as_bf16x8(*(const uint4*)(ol + 16 * ks)), vop[ks], pacc);
+      const int off = rb ^ (32 * ks);
+      sacc = mfma32x32x16(as_bf16x8(*(const uint4*)(ql + off)), kop[ks], sacc);
+      pacc = mfma32x32x16(as_bf16x8(*(const uint4*)(ol + off)), vop[ks], pacc);
     }
-    // item it+1 into item it-2's buffer (its last reads were the dV and dK
-    // products of the previous iteration)
-    if (it + 1 < n_items) store(b_st, S0{});
     // dV and dK of item it-1 (in the first iteration zero operands on the
-    // zeroed transposed tiles of buffer 2, which add exactly 0)
-    dkdv(b_prev, pp_prev, ps_prev);
+    // zeroed stage 3, which add exactly 0)
+    dkdv(s_prev, pp_prev, ps_prev);
     // branch-free: the exp of every score, then a select (a masked score's
     // exp may overflow; it is never used); the row values in 4-wide reads
+    const float* r_lse = rbuf(s_cur);
+    const float* r_d = r_lse + kRChunk;
     float pv[16], dsv[16];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -825,7 +810,7 @@ __global__ __launch_bounds__(kKThreads) void bwd_dkdv_kernel(BwdArgs a) {
       for (int r = 0; r < 4; ++r) {
         const int e = 4 * j + r;
         const bool kp = (unsigned)(c0 + i0 + r - t_m) <= span;
-        const float ex = exp2_fast(fmaf(sacc[e], a.scale_log2, -lse4[r]));
+        const float ex = exp2_fast(fmaf(sacc[e], a.scale_log2, -(lse4[r] * kLog2e)));
         const float p = kp ? ex : 0.0f;
         pv[e] = p;
         dsv[e] = p * (pacc[e] - d4[r]);
@@ -836,22 +821,25 @@ __global__ __launch_bounds__(kKThreads) void bwd_dkdv_kernel(BwdArgs a) {
       pp[ks] = pack_bf16x8(&pv[8 * ks]);
       ps[ks] = pack_bf16x8(&dsv[8 * ks]);
     }
-    if (it + 2 < n_items) ahead = next_pos(ahead);    // item min(it + 2, n_items - 1)
-    load(ahead, S0{});                                // into the freed registers
-    cur = next_pos(cur);
-    __syncthreads();
+    __builtin_amdgcn_s_waitcnt(0x0F70 | NLD);   // item it+1 landed
+    cur = nx1;
+    nx1 = nx2;
+    nx2 = next_pos(nx2);
+    lds_barrier();
   };
-  for (int it = 0; it < n_items; it += 2) {   // by two: the P / dS sets swap roles
-    step(it, ppB, psB, ppA, psA);
-    if (it + 1 < n_items) step(it + 1, ppA, psA, ppB, psB);
+  for (int it = 0; it < n_pad; it += 4) {
+    step(it, C0{}, C3{}, C2{}, ppB, psB, ppA, psA);
+    step(it + 1, C1{}, C0{}, C3{}, ppA, psA, ppB, psB);
+    step(it + 2, C2{}, C1{}, C0{}, ppB, psB, ppA, psA);
+    step(it + 3, C3{}, C2{}, C1{}, ppA, psA, ppB, psB);
   }
-  if (n_items > 0) {   // dV and dK of the last item
-    if ((n_items - 1) & 1) dkdv((n_items - 1) % 3, ppB, psB);
-    else dkdv((n_items - 1) % 3, ppA, psA);
+  if (n_items > 0) {
+    dkdv(C3{}, ppB, psB);            // dV and dK of the last (padded) item
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // the repeated loads past the end
   }
 
   if (t >= 0) {
-    // the first (or only) part writes dk, dv; the second half of a split
+    // the first (or only) part writes dk, dv; the second part of a split
     // tile writes its sums beside them for the merge
     float* p1 = a.part1 + (((size_t)sg * a.ktiles + tile) * kKTile + 32 * wave + li) * 2 * D;
     float* dko = part ? p1 : a.dk + kvbase + (size_t)t * D;

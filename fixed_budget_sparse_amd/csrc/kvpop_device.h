@@ -43,6 +43,39 @@ __device__ __forceinline__ void wave_lds_fence() {
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 }
 
+// Workgroup barrier that hands over LDS only: each wave waits for its own
+// LDS operations, then all waves meet.  Unlike __syncthreads, whose release
+// fence also waits for every vector-memory operation in flight (direct loads
+// into LDS included), it leaves this wave's direct loads running; the caller
+// awaits the ones the other waves will read (s_waitcnt vmcnt) before it.  The
+// memory clobber keeps the compiler from moving memory accesses across.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// Direct loads from global memory into LDS, 16 or 4 bytes per lane: lane L
+// writes lds_base + 16 L (or 4 L), lds_base being the same for the whole
+// wave.  Issued from inline asm, so the compiler does not see the LDS write
+// and adds no wait for it of its own (it would otherwise wait, at the first
+// LDS read it cannot prove disjoint, for every load in flight); the caller
+// awaits these loads with s_waitcnt vmcnt before the barrier that hands the
+// data to the other waves.  The compiler's own vmcnt waits stay correct: the
+// counter drains in order, and loads it does not know of only make them
+// wait longer.  The asm sets M0 itself: a kernel using these must not keep
+// another value in M0 (no direct-load builtins, no indexed register access).
+typedef __attribute__((address_space(3))) void lds_void_t;
+__device__ __forceinline__ uint32_t lds_address(const void* p) {
+  return (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(uintptr_t)(lds_void_t*)p);
+}
+__device__ __forceinline__ void dma_lds_x4(const void* g, const void* lds_base) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds_address(lds_base))
+               : "memory");
+}
+__device__ __forceinline__ void dma_lds_x1(const void* g, const void* lds_base) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(g), "s"(lds_address(lds_base))
+               : "memory");
+}
+
 // Workgroups of a 1-D grid are dispatched round-robin over the 8 XCDs, each
 // with its own L2.  This maps the hardware block id to a logical id such that
 // every XCD receives a contiguous range of logical ids (a bijection on
