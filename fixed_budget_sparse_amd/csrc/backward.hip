@@ -12,32 +12,31 @@
 // with dK, dV summed over the query heads that share the KV head.
 //
 // Design (gfx950):
-//  * bwd_dot_kernel: D_i from dO and the forward's O.
+//  * bwd_dot_kernel: D_i from dO and the forward's O, and the row's LSE in
+//    the exp2 domain.
 //  * dQ, query-major (bwd_dq_kernel): the forward's tiles (m rows of each of
 //    the G query heads stacked into 256 rows, 8 waves of 32) and its key plan
 //    (sinks, the listed long-range keys of the tile's first row, the band);
-//    per 64-key chunk K and V are gathered into LDS (K also transposed with
-//    the columns permuted to the register layout of dS), then per wave
-//    S^T = K Q^T and dP^T = V dO^T on MFMA, dS in registers, and
-//    dQ^T += K^T dS^T on MFMA with dS as the B operand.
+//    per 64-key chunk the K and V rows are direct-loaded into one of two
+//    swizzled LDS stages (the next chunk's loads in flight during the math),
+//    then per wave S^T = K Q^T and dP^T = V dO^T on MFMA, dS in registers,
+//    and dQ^T += K^T dS^T on MFMA with K^T read transposed from the same
+//    stage and dS as the B operand.
 //  * dK, dV, key-major (bwd_dkdv_kernel): key t is kept by the contiguous rows
 //    [t, q_end(t)] (tau never increases with q), so a tile of keys needs the
 //    rows [min t, max q_end], and the mask of a (row, key) pair is the
-//    interval test t <= q <= q_end(t).  The forward plan finds q_end(t) by
-//    binary search on tau; bwd_key_order_kernel groups keys into 64-key tiles: keys that
-//    live at most w + 64 rows in token order, the others by q_end (a counting
-//    sort over 64-row buckets), which keeps the rows a tile visits close to
-//    the rows its keys need.  Per workgroup (4 waves of 32 keys: two
-//    consecutive 64-key groups of the plan share every staged chunk; K and V
-//    operands in registers) the rows stream in 32-row chunks aligned to
-//    multiples of 32 (so every key's sums are formed in the same order
-//    whatever its tile), in three LDS stages, with the loads of the chunk
-//    after next in flight during the math, workgroups mapped so that each
-//    XCD works through whole (sequence, KV head)s in plan order:
-//    S = Q K^T and dP = dO V^T on MFMA, then dV^T += dO^T P and
-//    dK^T += Q^T dS with Q and dO staged transposed (permuted columns, one
-//    32-bit word per dim for each pair of rows); the dV and dK products of a
-//    chunk run during the next chunk's P and dS math.
+//    interval test t <= q <= q_end(t).  The forward plan finds q_end(t);
+//    bwd_key_order_kernel orders the keys into 128-key tiles (short-lived
+//    keys by token, long-lived ones by q_end band and token band), and
+//    bwd_tile_plan_kernel lists each tile's 32-row chunks as one work item,
+//    or two split at the fixed row S / 2 when it spans more than half the
+//    sequence (the second half's sums added by bwd_dkdv_merge_kernel in a
+//    fixed order).  Per workgroup (4 waves of 32 keys, K and V operands in
+//    registers) the (query head, chunk) items stream through six LDS stages
+//    by direct loads, three items ahead: S = Q K^T and dP = dO V^T of the
+//    next item, dV^T += dO^T P and dK^T += Q^T dS of the previous one (Q^T
+//    and dO^T read transposed from the same stage) and the P / dS math of
+//    the current one are interleaved MFMA by MFMA.
 //  * bf16 inputs, float32 accumulation, P and dS rounded to bf16 as MFMA
 //    operands; dQ, dK, dV are written in float32.
 #include <type_traits>
@@ -59,19 +58,14 @@ typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
 typedef short short4v __attribute__((ext_vector_type(4)));
 typedef short short8v __attribute__((ext_vector_type(8)));
 
-// LDS column of key j (0..63) in a transposed tile whose columns follow the
-// register layout of an MFMA result used as a B operand: column
-// 16 ks + 8 hh + 4 a + r holds key 16 ks + 8 a + 4 hh + r.
-__device__ __forceinline__ int perm_col(int j) {
-  return 16 * (j >> 4) + 8 * ((j >> 2) & 1) + 4 * ((j >> 3) & 1) + (j & 3);
-}
-
-
 // ---------------------------------------------------------------- D_i
+// D_i = sum_d dO[i, d] O[i, d] per row, and the row's LSE times log2 e
 template <int D, bool kF32Out>
 __global__ __launch_bounds__(256) void bwd_dot_kernel(const uint16_t* __restrict__ dout,
                                                       const void* __restrict__ o,
-                                                      float* __restrict__ dvec, long long rows) {
+                                                      const float* __restrict__ lse,
+                                                      float* __restrict__ dvec,
+                                                      float* __restrict__ lse2, long long rows) {
   constexpr int LPR = D / 8;          // lanes per row, 8 elements each
   constexpr int RPW = 64 / LPR;       // rows per wave
   const long long wv = ((long long)blockIdx.x * 256 + threadIdx.x) >> 6;
@@ -105,7 +99,10 @@ __global__ __launch_bounds__(256) void bwd_dot_kernel(const uint16_t* __restrict
   }
 #pragma unroll
   for (int off = LPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
-  if (part == 0 && row < rows) dvec[row] = acc;
+  if (part == 0 && row < rows) {
+    dvec[row] = acc;
+    lse2[row] = lse[row] * kLog2e;   // the LSE in the exp2 domain, for both kernels
+  }
 }
 
 // Buckets of the dK/dV key order for sequence length S: keys living at most
@@ -166,6 +163,7 @@ struct BwdArgs {
   const uint16_t* dout;
   const float* lse;
   const float* dvec;
+  const float* lse2;   // LSE log2 e per row
   const int* rank;
   const int* tau;
   const int* qend;
@@ -277,7 +275,7 @@ __global__ __launch_bounds__(kQThreads, 1) void bwd_dq_kernel(BwdArgs a) {
   const bool row_ok = g < G && q < S;
   const int hq = h * G + (g < G ? g : 0);
   const size_t qrow = ((size_t)b * a.Hq + hq) * S + (row_ok ? q : 0);
-  const float lse2 = row_ok ? a.lse[qrow] * kLog2e : 0.0f;
+  const float lse2 = row_ok ? a.lse2[qrow] : 0.0f;
   const float drow = row_ok ? a.dvec[qrow] : 0.0f;
 
   // key segments of the tile: sinks | long-range | band
@@ -593,6 +591,7 @@ __global__ __launch_bounds__(256) void bwd_dkdv_merge_kernel(BwdArgs a) {
 template <int D>
 __global__ __launch_bounds__(kKThreads) void bwd_dkdv_kernel(BwdArgs a) {
   constexpr int NKS = D / 16;
+  constexpr int NB = D / 32;                         // 32-dim output blocks
   constexpr int PPR = D / 8;                         // 16-byte pieces per row
   constexpr int RB = D * 2;                          // bytes per row
   constexpr int CB = kRChunk * RB;                   // bytes of one tensor's chunk
@@ -601,31 +600,16 @@ __global__ __launch_bounds__(kKThreads) void bwd_dkdv_kernel(BwdArgs a) {
   constexpr int NLD = 2 * NDMA + 1;                  // direct loads per wave per item
   static_assert(NDMA >= 1 && NDMA * RPI * kKWaves == kRChunk, "direct-load tiling");
   static_assert(kRChunk == 32 && kKWaves == 4, "row-value load: 64 floats, 16 per wave");
-  // Four stages, each one array: the rows' LSE and D (64 floats), then the
-  // Q rows, then the dO rows (row-major, swizzled like the dQ kernel's K:
-  // read as rows for S and dP and transposed for dK and dV).  One array per
-  // stage keeps the direct-load targets few enough for the compiler to tell
-  // them apart (it then knows that loads in flight into one stage do not
-  // alias the reads of another) and every stage offset an immediate.
-  constexpr int SB = 2 * kRChunk * 4 + 2 * CB;       // bytes per stage
-  __shared__ __attribute__((aligned(16))) unsigned char kvst0[SB];
-  __shared__ __attribute__((aligned(16))) unsigned char kvst1[SB];
-  __shared__ __attribute__((aligned(16))) unsigned char kvst2[SB];
-  __shared__ __attribute__((aligned(16))) unsigned char kvst3[SB];
-  auto stage = [&](auto i) -> unsigned char* {
-    constexpr int I = decltype(i)::value;
-    if constexpr (I == 0) return kvst0;
-    else if constexpr (I == 1) return kvst1;
-    else if constexpr (I == 2) return kvst2;
-    else return kvst3;
-  };
-  auto rbuf = [&](auto i) { return (float*)stage(i); };
-  auto qbuf = [&](auto i) { return stage(i) + 2 * kRChunk * 4; };
-  auto obuf = [&](auto i) { return stage(i) + 2 * kRChunk * 4 + CB; };
-  using C0 = std::integral_constant<int, 0>;
-  using C1 = std::integral_constant<int, 1>;
-  using C2 = std::integral_constant<int, 2>;
-  using C3 = std::integral_constant<int, 3>;
+  // Six stages of one item each: the rows' LSE log2 e and D (64 floats),
+  // then the Q rows, then the dO rows (row-major, swizzled like the dQ
+  // kernel's K: read as rows for S and dP and transposed for dK and dV).
+  // Stage offsets are multiples of 256 bytes, so adding one to a lane's
+  // in-stage offset commutes with the XORs of the swizzle (bits 4..7).
+  constexpr int NST = 6;
+  constexpr int RV = 2 * kRChunk * 4;                // bytes of row values
+  constexpr int SB = RV + 2 * CB;                    // bytes per stage
+  static_assert(SB % 256 == 0, "stage alignment");
+  __shared__ __attribute__((aligned(256))) unsigned char kvst[NST * SB];
 
   const int lane = lane_id(), wave = wave_id();
   const int hh = lane >> 5, li = lane & 31;
@@ -674,9 +658,9 @@ __global__ __launch_bounds__(kKThreads) void bwd_dkdv_kernel(BwdArgs a) {
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) asm volatile("" : "+v"(kop[ks]), "+v"(vop[ks]));
   }
-  f32x16 dkacc[D / 32], dvacc[D / 32];
+  f32x16 dkacc[NB], dvacc[NB];
 #pragma unroll
-  for (int d2 = 0; d2 < D / 32; ++d2) {
+  for (int d2 = 0; d2 < NB; ++d2) {
     dkacc[d2] = f32x16{};
     dvacc[d2] = f32x16{};
   }
@@ -695,147 +679,217 @@ __global__ __launch_bounds__(kKThreads) void bwd_dkdv_kernel(BwdArgs a) {
   auto next_pos = [&](ItemPos p) {
     return p.ci + 1 < n_chunk ? ItemPos{p.gg, p.ci + 1} : ItemPos{p.gg + 1, 0};
   };
-  // ---- staging of one item, all by direct loads (lane L of a load writes
-  // 16 L, or 4 L, bytes past the load's LDS base): the Q and dO rows, lane L
-  // fetching the global piece its swizzled slot holds, and the rows' LSE
-  // (lanes 0..31) and D (lanes 32..63), 16 lanes in each wave.  Rows past
-  // the end read row S - 1 and are masked.  Each wave issues NLD loads.
-  auto dma_item = [&](ItemPos ip, auto st) {
+  // positions past the last item (query head G and beyond) load the last
+  // head's rows instead; those items are masked or never used
+  auto clamp_pos = [&](ItemPos p) { return ItemPos{min(p.gg, G - 1), p.ci}; };
+  // ---- staging of one item into the stage at byte offset so, all by
+  // direct loads (lane L of a load writes 16 L, or 4 L, bytes past the
+  // load's LDS base): the Q and dO rows, lane L fetching the global piece its
+  // swizzled slot holds, and the rows' LSE log2 e (lanes 0..31) and D (lanes
+  // 32..63).  Rows past the end read row S - 1 and are masked.  Each wave
+  // issues NLD loads.
+  auto dma_item = [&](ItemPos ip, int so) {
     const size_t hrow = ((size_t)b * a.Hq + h * G + ip.gg) * S;
     const int c0 = (c_first + ip.ci) * kRChunk;
+    const unsigned char* qh = (const unsigned char*)a.q + hrow * RB;
+    const unsigned char* oh = (const unsigned char*)a.dout + hrow * RB;
 #pragma unroll
     for (int i = 0; i < NDMA; ++i) {
       const int r0 = (wave * NDMA + i) * RPI;
       const int row = r0 + lane / PPR, sl = lane % PPR;
       const int qq = min(c0 + row, S - 1);
-      const size_t off = ((hrow + qq) * PPR + (sl ^ dq_swz<D>(row))) * 16;
-      dma_lds_x4((const unsigned char*)a.q + off, qbuf(st) + r0 * RB);
-      dma_lds_x4((const unsigned char*)a.dout + off, obuf(st) + r0 * RB);
+      const uint32_t off = (uint32_t)qq * RB + ((sl ^ dq_swz<D>(row)) << 4);
+      dma_lds_x4_so(qh, off, kvst + so + RV + r0 * RB);
+      dma_lds_x4_so(oh, off, kvst + so + RV + CB + r0 * RB);
     }
-    if ((lane >> 4) == wave) {
-      const int qq = min(c0 + (lane & 31), S - 1);
-      dma_lds_x1((hh ? a.dvec : a.lse) + hrow + qq, rbuf(st));
+    {   // every wave loads all 64 values (the same bytes): no branch
+      const int qq = min(c0 + li, S - 1);
+      dma_lds_x1((hh ? a.dvec : a.lse2) + hrow + qq, kvst + so);
     }
   };
 
-  // per-lane LDS offsets: row reads (row li, piece 2 ks + hh: base XOR 32 ks)
-  // and the transposed reads
-  int tro[D / 32][2];
+  // per-lane in-stage LDS offsets: row reads (row li, piece 2 ks + hh: base
+  // XOR 32 ks) and the transposed reads
+  int tro[NB][2];
   dq_tr_offsets<D>(lane, tro);
   const int row_base = li * RB + ((hh ^ dq_swz<D>(li)) << 4);
   typedef __attribute__((address_space(3))) short4v lds_s4;
-  auto tr_operand = [&](const unsigned char* buf, int db, int ks) {
-    const short4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)(buf + tro[db][0] + 16 * ks * RB));
-    const short4v hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)(buf + tro[db][1] + 16 * ks * RB));
-    const short8v v8 = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-    return __builtin_bit_cast(bf16x8, v8);
-  };
-  // dV^T += dO^T P and dK^T += Q^T dS of an item staged in st
-  auto dkdv = [&](auto st, const bf16x8 (&pp)[2], const bf16x8 (&ps)[2]) {
-#pragma unroll
-    for (int d2 = 0; d2 < D / 32; ++d2)
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        dvacc[d2] = mfma32x32x16(tr_operand(obuf(st), d2, ks), pp[ks], dvacc[d2]);
-        dkacc[d2] = mfma32x32x16(tr_operand(qbuf(st), d2, ks), ps[ks], dkacc[d2]);
-      }
+
+  // ---- the pipeline.  Item i lives in stage i mod 6.  Iteration it, with
+  // S and dP of item it already in registers (set it mod 2):
+  //   * direct loads of item it+3 (two iterations of cover),
+  //   * S and dP of item it+1 (32 rows x 32 keys, the lane owning its key),
+  //   * dV^T += dO^T P and dK^T += Q^T dS of item it-1 (P and dS from the
+  //     previous iteration's registers, Q^T and dO^T read transposed),
+  //   * the probability and dS math of item it, spread between those 32
+  //     MFMAs (it depends on neither product),
+  //   * a wait for this wave's loads of item it+2 and a barrier that
+  //     publishes every wave's part.
+  // One wave per SIMD, so the layout of the step is the whole overlap: 32
+  // slots, each one MFMA, the LDS read of an operand kPf MFMAs ahead and a
+  // share of the math, fenced so the compiler keeps them in that order.
+  // Iterations past the last item (the count is padded to even with masked
+  // items) and the S / dP of the item after the last run on staged rows
+  // that exist and are not used.
+  constexpr int kPf = 4;                             // operand reads ahead of their MFMA
+  const int n_pad = (n_items + 1) & ~1;
+  auto stage_of = [&](int i) { return (i % NST) * SB; };
+  auto mask_c0 = [&](int i, ItemPos p) {   // first row of item i, or far away when padding
+    return i < n_items ? (c_first + p.ci) * kRChunk : -(1 << 30);
   };
 
-  // Item it is staged in stage it mod 4, two items ahead, and the dV and dK
-  // products of an item run one iteration late: iteration it issues the
-  // direct loads of item it+2 into the stage of item it-2 (whose last reads,
-  // its dV and dK products, were in the previous iteration), runs the S and
-  // dP products of item it, then the probability and dS math of item it
-  // beside the dV and dK products of item it-1 (its P and dS kept in
-  // registers), waits for this wave's loads of item it+1 (those of item it+2
-  // may stay in flight: the counter drains in order) and ends with a barrier
-  // that publishes every wave's part.  The loop body is four iterations with
-  // no exit between them (the stages rotate over four and the P / dS
-  // register sets over two, all compile-time): the item count is padded to a
-  // multiple of four with masked items, whose P and dS are zero, and loads
-  // past the last item repeat the last item's rows into a stage no later
-  // read uses.
-  const int n_pad = (n_items + 3) & ~3;
-  auto clamp_pos = [&](ItemPos p) { return ItemPos{min(p.gg, G - 1), p.ci}; };
-  ItemPos cur{0, 0}, nx1{0, 0}, nx2{0, 0};   // items it, it+1, it+2
+  ItemPos cur{0, 0}, nx1{0, 0}, nx2{0, 0}, nx3{0, 0};   // items it .. it+3
+  f32x16 sA, pA, sB, pB;               // S and dP of items with even / odd index
+  bf16x8 ppA[2] = {}, psA[2] = {}, ppB[2] = {}, psB[2] = {};   // P and dS likewise
+  // operand q of the 2 NKS S / dP MFMAs (k-step q / 2; Q rows for even q,
+  // dO rows for odd q) of the item whose row-read base (row_base plus its
+  // stage offset) is rb
+  auto sd_operand = [&](int rb, int q) {
+    const unsigned char* p = kvst + (rb ^ (32 * (q >> 1)));
+    return as_bf16x8(*(const uint4*)(p + ((q & 1) ? CB : 0)));
+  };
   if (n_items > 0) {
-    dma_item(cur, C0{});
+    dma_item(cur, stage_of(0));
     nx1 = next_pos(cur);
-    dma_item(clamp_pos(nx1), C1{});
+    dma_item(clamp_pos(nx1), stage_of(1));
     nx2 = next_pos(nx1);
-    {   // the first iteration's dV and dK products read stage 3 with zero P
+    dma_item(clamp_pos(nx2), stage_of(2));
+    nx3 = next_pos(nx2);
+    {   // the first iteration's dV and dK products read stage 5 with zero P
         // and dS: zero it (0 times a stale NaN is not 0)
-      uint4* zq = (uint4*)qbuf(C3{});
-      uint4* zo = (uint4*)obuf(C3{});
-      for (int i = threadIdx.x; i < CB / 16; i += kKThreads) {
-        zq[i] = make_uint4(0, 0, 0, 0);
-        zo[i] = make_uint4(0, 0, 0, 0);
-      }
+      uint4* z = (uint4*)(kvst + stage_of(NST - 1));
+      for (int i = threadIdx.x; i < SB / 16; i += kKThreads) z[i] = make_uint4(0, 0, 0, 0);
     }
-    __builtin_amdgcn_s_waitcnt(0x0F70 | NLD);   // item 0 landed
+    __builtin_amdgcn_s_waitcnt(0x0F70 | NLD);   // items 0 and 1 landed
     lds_barrier();
-  }
-  bf16x8 ppA[2] = {}, psA[2] = {}, ppB[2] = {}, psB[2] = {};
-  auto step = [&](int it, auto s_cur, auto s_prev, auto s_far, const bf16x8 (&pp_prev)[2],
-                  const bf16x8 (&ps_prev)[2], bf16x8 (&pp)[2], bf16x8 (&ps)[2]) {
-    // rows of a padding item fall outside every key's span
-    const int c0 = it < n_items ? (c_first + cur.ci) * kRChunk : -(1 << 30);
-    dma_item(clamp_pos(nx2), s_far);
-    const unsigned char* ql = qbuf(s_cur);
-    const unsigned char* ol = obuf(s_cur);
-    int rb = row_base;
-    asm volatile("" : "+v"(rb));   // keeps the XORs below in the loop
-    // S = Q K^T and dP = dO V^T (32 rows x 32 keys): lane owns its key
-    f32x16 sacc = f32x16{}, pacc = f32x16{};
+    const int rb = row_base + stage_of(0) + RV;
+    sA = f32x16{};
+    pA = f32x16{};
 #pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
-      const int off = rb ^ (32 * ks);
-      sacc = mfma32x32x16(as_bf16x8(*(const uint4*)(ql + off)), kop[ks], sacc);
-      pacc = mfma32x32x16(as_bf16x8(*(const uint4*)(ol + off)), vop[ks], pacc);
+    for (int q = 0; q < 2 * NKS; ++q) {
+      if (q & 1) pA = mfma32x32x16(sd_operand(rb, q), vop[q >> 1], pA);
+      else sA = mfma32x32x16(sd_operand(rb, q), kop[q >> 1], sA);
     }
-    // dV and dK of item it-1 (in the first iteration zero operands on the
-    // zeroed stage 3, which add exactly 0)
-    dkdv(s_prev, pp_prev, ps_prev);
-    // branch-free: the exp of every score, then a select (a masked score's
-    // exp may overflow; it is never used); the row values in 4-wide reads
-    const float* r_lse = rbuf(s_cur);
-    const float* r_d = r_lse + kRChunk;
-    float pv[16], dsv[16];
+  }
+  // iteration it; Sc/Pc: S and dP of item it, Sn/Pn: of item it+1; pp_prev:
+  // P and dS of item it-1, pp: of item it
+  auto step = [&](int it, f32x16& Sc, f32x16& Pc, f32x16& Sn, f32x16& Pn,
+                  const bf16x8 (&pp_prev)[2], const bf16x8 (&ps_prev)[2], bf16x8 (&pp)[2],
+                  bf16x8 (&ps)[2]) {
+    constexpr int NSD = 2 * NKS;                     // S / dP MFMAs
+    constexpr int NKV = 4 * NB;                      // dV / dK MFMAs
+    const int c0 = mask_c0(it, cur);
+    dma_item(clamp_pos(nx3), stage_of(it + 3));
+    __builtin_amdgcn_sched_barrier(0);
+    int rb = row_base + stage_of(it + 1) + RV;                 // item it+1
+    asm volatile("" : "+v"(rb));
+    // transposed operand m of the dV / dK MFMAs of item it-1 (stage
+    // (it-1) mod 6): block d2 = m / 4, k-step (m / 2) mod 2, dO^T (even m,
+    // for dV) or Q^T (odd m, for dK); the per-lane bases are made opaque so
+    // that every constant part of an address goes to the instruction's
+    // offset field
+    int trb[NB][2];
+#pragma unroll
+    for (int d2 = 0; d2 < NB; ++d2)
+#pragma unroll
+      for (int x = 0; x < 2; ++x) {
+        trb[d2][x] = tro[d2][x] + stage_of(it + NST - 1) + RV;
+        asm volatile("" : "+v"(trb[d2][x]));
+      }
+    auto tr_operand = [&](int m) {
+      const int d2 = m >> 2, ks = (m >> 1) & 1;
+      const unsigned char* p0 = kvst + trb[d2][0] + (16 * ks * RB + ((m & 1) ? 0 : CB));
+      const unsigned char* p1 = kvst + trb[d2][1] + (16 * ks * RB + ((m & 1) ? 0 : CB));
+      const short4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)p0);
+      const short4v hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)p1);
+      const short8v v8 = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      return __builtin_bit_cast(bf16x8, v8);
+    };
+    auto operand = [&](int q) { return q < NSD ? sd_operand(rb, q) : tr_operand(q - NSD); };
+    // row values of item it
+    const float* r_lse = (const float*)(kvst + stage_of(it));
+    f32x4 lse4[4], d4[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int i0 = 8 * j + 4 * hh;
-      const f32x4 lse4 = *(const f32x4*)(r_lse + i0);
-      const f32x4 d4 = *(const f32x4*)(r_d + i0);
+      lse4[j] = *(const f32x4*)(r_lse + 8 * j + 4 * hh);
+      d4[j] = *(const f32x4*)(r_lse + kRChunk + 8 * j + 4 * hh);
+    }
+    bf16x8 op[NSD + NKV];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int e = 4 * j + r;
+    for (int q = 0; q < kPf; ++q) op[q] = operand(q);
+    __builtin_amdgcn_sched_barrier(0);
+    Sn = f32x16{};
+    Pn = f32x16{};
+    float pv[16], dsv[16];
+#pragma unroll
+    for (int q = 0; q < NSD + NKV; ++q) {
+      if (q + kPf < NSD + NKV) op[q + kPf] = operand(q + kPf);
+      if (q < NSD) {
+        if (q & 1) Pn = mfma32x32x16(op[q], vop[q >> 1], Pn);
+        else Sn = mfma32x32x16(op[q], kop[q >> 1], Sn);
+      } else {
+        const int m = q - NSD, d2 = m >> 2, ks = (m >> 1) & 1;
+        if (m & 1) dkacc[d2] = mfma32x32x16(op[q], ps_prev[ks], dkacc[d2]);
+        else dvacc[d2] = mfma32x32x16(op[q], pp_prev[ks], dvacc[d2]);
+      }
+      // the math of item it: score e = q for the first 16 slots (the exp of
+      // every score, then a select: a masked score's exp may overflow and is
+      // never used), the bf16 packing in the next four
+      if (q < 16) {
+        const int e = q, j = e >> 2, r = e & 3, i0 = 8 * j + 4 * hh;
         const bool kp = (unsigned)(c0 + i0 + r - t_m) <= span;
-        const float ex = exp2_fast(fmaf(sacc[e], a.scale_log2, -(lse4[r] * kLog2e)));
+        const float ex = exp2_fast(fmaf(Sc[e], a.scale_log2, -lse4[j][r]));
         const float p = kp ? ex : 0.0f;
         pv[e] = p;
-        dsv[e] = p * (pacc[e] - d4[r]);
+        dsv[e] = p * (Pc[e] - d4[j][r]);
+      } else if (q < 20) {
+        const int ks = (q - 16) >> 1;
+        if (q & 1) ps[ks] = pack_bf16x8(&dsv[8 * ks]);
+        else pp[ks] = pack_bf16x8(&pv[8 * ks]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    static_assert(NSD + NKV >= 16, "one slot per score");
+    if constexpr (NSD + NKV < 20) {   // D = 64: 16 slots, the packing after them
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        pp[ks] = pack_bf16x8(&pv[8 * ks]);
+        ps[ks] = pack_bf16x8(&dsv[8 * ks]);
       }
     }
+    // the packed P and dS complete in this iteration (left alone, the
+    // compiler moves that math next to its use in the next one)
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      pp[ks] = pack_bf16x8(&pv[8 * ks]);
-      ps[ks] = pack_bf16x8(&dsv[8 * ks]);
-    }
-    __builtin_amdgcn_s_waitcnt(0x0F70 | NLD);   // item it+1 landed
+    for (int ks = 0; ks < 2; ++ks) asm volatile("" ::"v"(pp[ks]), "v"(ps[ks]));
+    __builtin_amdgcn_s_waitcnt(0x0F70 | NLD);   // item it+2 landed
     cur = nx1;
     nx1 = nx2;
-    nx2 = next_pos(nx2);
+    nx2 = nx3;
+    nx3 = next_pos(nx3);
     lds_barrier();
   };
-  for (int it = 0; it < n_pad; it += 4) {
-    step(it, C0{}, C3{}, C2{}, ppB, psB, ppA, psA);
-    step(it + 1, C1{}, C0{}, C3{}, ppA, psA, ppB, psB);
-    step(it + 2, C2{}, C1{}, C0{}, ppB, psB, ppA, psA);
-    step(it + 3, C3{}, C2{}, C1{}, ppA, psA, ppB, psB);
+  for (int it = 0; it < n_pad; it += 2) {
+    step(it, sA, pA, sB, pB, ppB, psB, ppA, psA);
+    step(it + 1, sB, pB, sA, pA, ppA, psA, ppB, psB);
   }
-  if (n_items > 0) {
-    dkdv(C3{}, ppB, psB);            // dV and dK of the last (padded) item
-    __builtin_amdgcn_s_waitcnt(0x0F70);   // the repeated loads past the end
+  if (n_items > 0) {   // dV and dK of the last (padded) item
+    const unsigned char* tb = kvst + stage_of(n_pad - 1) + RV;
+#pragma unroll
+    for (int d2 = 0; d2 < NB; ++d2)
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const unsigned char* p0 = tb + tro[d2][0] + 16 * ks * RB;
+        const unsigned char* p1 = tb + tro[d2][1] + 16 * ks * RB;
+        const short4v ol = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)(p0 + CB));
+        const short4v oh = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)(p1 + CB));
+        const short4v ql = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)p0);
+        const short4v qh = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)p1);
+        const short8v o8 = {ol[0], ol[1], ol[2], ol[3], oh[0], oh[1], oh[2], oh[3]};
+        const short8v q8 = {ql[0], ql[1], ql[2], ql[3], qh[0], qh[1], qh[2], qh[3]};
+        dvacc[d2] = mfma32x32x16(__builtin_bit_cast(bf16x8, o8), ppB[ks], dvacc[d2]);
+        dkacc[d2] = mfma32x32x16(__builtin_bit_cast(bf16x8, q8), psB[ks], dkacc[d2]);
+      }
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // the loads past the end
   }
 
   if (t >= 0) {
@@ -864,11 +918,11 @@ void launch_bwd_kernels(const Dims& d, BwdArgs a, const void* o, hipStream_t st)
   constexpr int RPB = 4 * (64 / (D / 8));     // rows per 256-thread block
   const unsigned nblk = (unsigned)((rows + RPB - 1) / RPB);
   if (d.f32_out)
-    hipLaunchKernelGGL((bwd_dot_kernel<D, true>), dim3(nblk), dim3(256), 0, st, a.dout, o,
-                       (float*)a.dvec, rows);
+    hipLaunchKernelGGL((bwd_dot_kernel<D, true>), dim3(nblk), dim3(256), 0, st, a.dout, o, a.lse,
+                       (float*)a.dvec, (float*)a.lse2, rows);
   else
-    hipLaunchKernelGGL((bwd_dot_kernel<D, false>), dim3(nblk), dim3(256), 0, st, a.dout, o,
-                       (float*)a.dvec, rows);
+    hipLaunchKernelGGL((bwd_dot_kernel<D, false>), dim3(nblk), dim3(256), 0, st, a.dout, o, a.lse,
+                       (float*)a.dvec, (float*)a.lse2, rows);
   const long long nq = (long long)a.ntiles * d.Hkv * d.b;
   hipLaunchKernelGGL((bwd_dq_kernel<D>), dim3((unsigned)nq), dim3(kQThreads), 0, st, a);
   hipLaunchKernelGGL((bwd_dkdv_kernel<D>), dim3((unsigned)(2 * a.ktiles * d.nseg())),
@@ -884,7 +938,7 @@ static int bwd_ktiles(const Dims& d) { return (d.S + kKTile - 1) / kKTile; }
 size_t bwd_ws_bytes(const Dims& d) {
   const size_t rows = (size_t)d.b * d.Hq * d.S, keys = (size_t)d.nseg() * d.S;
   const size_t nt = (size_t)d.nseg() * bwd_ktiles(d);
-  return fwd_ws_bytes(d) + align256(rows * 4) + align256(keys * 4) +
+  return fwd_ws_bytes(d) + 2 * align256(rows * 4) + align256(keys * 4) +
          2 * align256(nt * 2 * 16) +                  // item plan and its unsorted copy
          align256(nt * 4) +                           // split flags
          align256(nt * kKTile * 2 * (size_t)d.D * 4);  // second-half sums of split tiles
@@ -898,6 +952,7 @@ hipError_t launch_masked_bwd(const Dims& d, const void* q, const void* k, const 
   char* p = (char*)ws + fwd_ws_bytes(d);
   const size_t rows = (size_t)d.b * d.Hq * d.S, keys = (size_t)d.nseg() * d.S;
   float* dvec = (float*)p; p += align256(rows * 4);
+  float* lse2 = (float*)p; p += align256(rows * 4);
   int* korder = (int*)p; p += align256(keys * 4);
   const int ktiles = bwd_ktiles(d);
   const size_t nt = (size_t)d.nseg() * ktiles;
@@ -915,7 +970,8 @@ hipError_t launch_masked_bwd(const Dims& d, const void* q, const void* k, const 
 
   BwdArgs a;
   a.q = (const uint16_t*)q; a.k = (const uint16_t*)k; a.v = (const uint16_t*)v;
-  a.dout = (const uint16_t*)dout; a.lse = lse; a.dvec = dvec; a.rank = rank; a.tau = tau;
+  a.dout = (const uint16_t*)dout; a.lse = lse; a.dvec = dvec; a.lse2 = lse2;
+  a.rank = rank; a.tau = tau;
   a.qend = qend; a.korder = korder; a.list = pl.list; a.count = pl.count;
   a.tplan = tplan; a.tsplit = tsplit; a.part1 = part1;
   a.dq = dq; a.dk = dk; a.dv = dv;

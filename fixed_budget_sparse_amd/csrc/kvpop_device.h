@@ -75,6 +75,19 @@ __device__ __forceinline__ void dma_lds_x1(const void* g, const void* lds_base) 
   asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(g), "s"(lds_address(lds_base))
                : "memory");
 }
+// The 16-byte form with a wave-uniform 64-bit base and an unsigned 32-bit
+// per-lane byte offset (one VGPR of address arithmetic per lane).
+__device__ __forceinline__ const void* uniform_ptr(const void* p) {
+  const uint64_t u = (uint64_t)(uintptr_t)p;
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)u);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(u >> 32));
+  return (const void*)(uintptr_t)(((uint64_t)hi << 32) | lo);
+}
+__device__ __forceinline__ void dma_lds_x4_so(const void* base, uint32_t off, const void* lds_base) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(uniform_ptr(base)),
+               "s"(lds_address(lds_base))
+               : "memory");
+}
 
 // Workgroups of a 1-D grid are dispatched round-robin over the 8 XCDs, each
 // with its own L2.  This maps the hardware block id to a logical id such that
