@@ -34,17 +34,9 @@ COMMON = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-fvisibility=h
           "-I", os.path.join(ROOT, "include"), "-Wall", "-Wno-unused-function"]
 
 
-# Per-source code generation options.  backward.hip: MFMA results in
-# ordinary VGPRs where they fit (the dK/dV kernel's scores feed VALU math,
-# which cannot read the accumulation registers: without it every score is
-# copied out of them first).
-PER_SOURCE = {"backward.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
-
-
 def _compile(src: str, extra) -> str:
     obj = os.path.join(BUILD, src.replace(".hip", ".o"))
-    cmd = [_hipcc(), *COMMON, *PER_SOURCE.get(src, []), *extra, "-c", os.path.join(CSRC, src),
-           "-o", obj]
+    cmd = [_hipcc(), *COMMON, *extra, "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     errs = "\n".join(l for l in r.stderr.splitlines()
                      if "packed-fp32-ops' is not a recognized feature" not in l)

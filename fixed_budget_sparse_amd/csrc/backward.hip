@@ -245,6 +245,7 @@ __global__ __launch_bounds__(kQThreads, 1) void bwd_dq_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(16))) unsigned char dqb_v1[CB];
   __shared__ __attribute__((aligned(16))) int kd_t[kSlots][kQChunk];
   __shared__ __attribute__((aligned(16))) int kd_span[kSlots][kQChunk];   // q_end(t) - t
+  __shared__ int kd_flag[kSlots];   // 0: every row of the tile keeps every key of the chunk
   auto kbuf = [&](auto i) -> unsigned char* {
     if constexpr (decltype(i)::value == 0) return dqa_k0;
     else return dqa_k1;
@@ -316,7 +317,9 @@ __global__ __launch_bounds__(kQThreads, 1) void bwd_dq_kernel(BwdArgs a) {
 
   // ---- key descriptors of the chunk starting at c0: wave 0 reads them
   // (branch-free, clamped) into registers, and stores token and span
-  // q_end(t) - t (token -1, span 0 for padding) one phase later
+  // q_end(t) - t (token -1, span 0 for padding) one phase later, with the
+  // chunk's mask flag: 0 when every key is kept by every row of the tile
+  // (t <= q0 and q_end(t) >= q_hi), so no mask runs
   struct Desc {
     int t, r;
     int2 l;
@@ -342,6 +345,9 @@ __global__ __launch_bounds__(kQThreads, 1) void bwd_dq_kernel(BwdArgs a) {
       if (t >= S) t = -1;
       kd_t[slot][lane] = t;
       kd_span[slot][lane] = t >= 0 ? e - t : 0;
+      const bool always = (t >= 0) & (t <= q0) & (e >= q_hi);
+      const uint64_t not_always = wave_ballot(!always);
+      if (lane == 0) kd_flag[slot] = not_always == 0 ? 0 : 2;
     }
   };
 
@@ -391,27 +397,40 @@ __global__ __launch_bounds__(kQThreads, 1) void bwd_dq_kernel(BwdArgs a) {
         pacc[blk] = mfma32x32x16(as_bf16x8(*(const uint4*)(vl + off)), dop[ks], pacc[blk]);
       }
     }
-    // dS = P (dP - D_i), P = exp(S scale - LSE_i) on kept keys (branch-free:
-    // the exp of every score, then a select; key data in 4-wide reads)
+    // dS = P (dP - D_i), P = exp(S scale - LSE_i) on kept keys: the exp of
+    // every score, then, only on chunks with a key that some row of the
+    // tile does not keep (a wave-uniform branch), a select (a masked score's
+    // exp may overflow; it is never used; key data in 4-wide reads).  Rows
+    // past the tile need no mask: their Q and dO operands are zero and their
+    // LSE and D are 0, so their dS is exactly 0.
     const int slot = c % kSlots;
+    float pr[2][16];
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) pr[blk][e] = exp2_fast(fmaf(sacc[blk][e], a.scale_log2, -lse2));
+    if (__builtin_amdgcn_readfirstlane(kd_flag[slot]) != 0) {
+#pragma unroll
+      for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          const int j0 = 32 * blk + 8 * jj + 4 * hh;
+          const int4 t4 = *(const int4*)(&kd_t[slot][j0]);
+          const int4 r4 = *(const int4*)(&kd_span[slot][j0]);
+          const int tv[4] = {t4.x, t4.y, t4.z, t4.w}, rv[4] = {r4.x, r4.y, r4.z, r4.w};
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int e = 4 * jj + r;
+            const bool kp = row_ok & ((unsigned)(q - tv[r]) <= (unsigned)rv[r]);
+            pr[blk][e] = kp ? pr[blk][e] : 0.0f;
+          }
+        }
+    }
     float dsv[2][16];
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        const int j0 = 32 * blk + 8 * jj + 4 * hh;
-        const int4 t4 = *(const int4*)(&kd_t[slot][j0]);
-        const int4 r4 = *(const int4*)(&kd_span[slot][j0]);
-        const int tv[4] = {t4.x, t4.y, t4.z, t4.w}, rv[4] = {r4.x, r4.y, r4.z, r4.w};
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int e = 4 * jj + r;
-          const bool kp = row_ok & ((unsigned)(q - tv[r]) <= (unsigned)rv[r]);
-          const float ex = exp2_fast(fmaf(sacc[blk][e], a.scale_log2, -lse2));
-          const float p = kp ? ex : 0.0f;
-          dsv[blk][e] = p * (pacc[blk][e] - drow);
-        }
-      }
+      for (int e = 0; e < 16; ++e) dsv[blk][e] = pr[blk][e] * (pacc[blk][e] - drow);
     bf16x8 pk[4];
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) pk[ks] = pack_bf16x8(&dsv[ks >> 1][8 * (ks & 1)]);
