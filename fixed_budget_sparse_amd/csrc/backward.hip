@@ -39,6 +39,7 @@
 //    the current one are interleaved MFMA by MFMA.
 //  * bf16 inputs, float32 accumulation, P and dS rounded to bf16 as MFMA
 //    operands; dQ, dK, dV are written in float32.
+#include <mutex>
 #include <type_traits>
 
 #include "kvpop_device.h"
@@ -257,7 +258,7 @@ __global__ __launch_bounds__(kQThreads, 1) void bwd_dq_kernel(BwdArgs a) {
   using C0 = std::integral_constant<int, 0>;
   using C1 = std::integral_constant<int, 1>;
 
-  const int tid = threadIdx.x, lane = lane_id(), wave = wave_id();
+  const int lane = lane_id(), wave = wave_id();
   const int hh = lane >> 5, li = lane & 31;
   const int bid = launch_block(a.reverse);
   const int tile = bid % a.ntiles;
@@ -932,7 +933,7 @@ __global__ __launch_bounds__(kKThreads) void bwd_dkdv_kernel(BwdArgs a) {
 }
 
 template <int D>
-void launch_bwd_kernels(const Dims& d, BwdArgs a, const void* o, hipStream_t st) {
+void launch_dot_dq(const Dims& d, BwdArgs a, const void* o, hipStream_t st, hipEvent_t dot_done) {
   const long long rows = (long long)d.b * d.Hq * d.S;
   constexpr int RPB = 4 * (64 / (D / 8));     // rows per 256-thread block
   const unsigned nblk = (unsigned)((rows + RPB - 1) / RPB);
@@ -942,12 +943,57 @@ void launch_bwd_kernels(const Dims& d, BwdArgs a, const void* o, hipStream_t st)
   else
     hipLaunchKernelGGL((bwd_dot_kernel<D, false>), dim3(nblk), dim3(256), 0, st, a.dout, o, a.lse,
                        (float*)a.dvec, (float*)a.lse2, rows);
+  if (dot_done) (void)hipEventRecord(dot_done, st);   // a failure shows in hipGetLastError
   const long long nq = (long long)a.ntiles * d.Hkv * d.b;
   hipLaunchKernelGGL((bwd_dq_kernel<D>), dim3((unsigned)nq), dim3(kQThreads), 0, st, a);
+}
+
+template <int D>
+void launch_dkdv(const Dims& d, BwdArgs a, hipStream_t st) {
   hipLaunchKernelGGL((bwd_dkdv_kernel<D>), dim3((unsigned)(2 * a.ktiles * d.nseg())),
                      dim3(kKThreads), 0, st, a);
   hipLaunchKernelGGL((bwd_dkdv_merge_kernel<D>), dim3((unsigned)(a.ktiles * d.nseg())), dim3(256), 0,
                      st, a);
+}
+
+// A second stream per device for the key-major half of the backward (key
+// order, tile plan, dK/dV, merge), which needs only q_end and D_i: it runs
+// beside the dot product and dQ, forked from the caller's stream after the
+// forward plan and joined back before the call returns, through events.
+// Created on the first backward on a device (default priority); a device
+// where that fails runs everything on the caller's stream (so does a first
+// call made while the caller's stream is being captured).  The lock makes
+// concurrent callers enqueue one at a time (each wait refers to the event's
+// record made just before it, so the events can be reused at once).
+constexpr int kMaxBwdDevices = 64;
+struct SideStream {
+  hipStream_t s = nullptr;
+  hipEvent_t fork = nullptr, dot_done = nullptr, join = nullptr;
+  int state = 0;   // 0: not tried, 1: ready, -1: unavailable
+};
+SideStream g_side[kMaxBwdDevices];
+std::mutex g_side_mu;
+
+SideStream* side_stream(hipStream_t caller) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxBwdDevices) return nullptr;
+  SideStream& ss = g_side[dev];
+  if (ss.state == 0) {
+    // no creation while the caller's stream is being captured into a graph
+    // (it would end the capture); such a call runs on the caller's stream
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(caller, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone) {
+      (void)hipGetLastError();
+      return nullptr;
+    }
+    bool ok = hipStreamCreateWithFlags(&ss.s, hipStreamNonBlocking) == hipSuccess;
+    ok = ok && hipEventCreateWithFlags(&ss.fork, hipEventDisableTiming) == hipSuccess;
+    ok = ok && hipEventCreateWithFlags(&ss.dot_done, hipEventDisableTiming) == hipSuccess;
+    ok = ok && hipEventCreateWithFlags(&ss.join, hipEventDisableTiming) == hipSuccess;
+    ss.state = ok ? 1 : -1;
+    if (!ok) (void)hipGetLastError();   // leave no error behind for the launches
+  }
+  return ss.state == 1 ? &ss : nullptr;
 }
 
 }  // namespace
@@ -980,12 +1026,6 @@ hipError_t launch_masked_bwd(const Dims& d, const void* q, const void* k, const 
   int* tsplit = (int*)p; p += align256(nt * 4);
   float* part1 = (float*)p;
   const int* qend = pl.qend;   // q_end(t), computed by the forward plan
-  const int nb = KeyBuckets(d.S).nb;
-  hipLaunchKernelGGL(bwd_key_order_kernel, dim3(d.nseg()), dim3(1024), (size_t)nb * 2 * 4, st, qend,
-                     korder, d.S, d.w);
-  const int nbins = plan_bins(d.S);
-  hipLaunchKernelGGL(bwd_tile_plan_kernel, dim3(d.nseg()), dim3(1024), (size_t)nbins * 2 * 4, st,
-                     korder, qend, d.S, ktiles, tplan_tmp, tplan, tsplit);
 
   BwdArgs a;
   a.q = (const uint16_t*)q; a.k = (const uint16_t*)k; a.v = (const uint16_t*)v;
@@ -1000,8 +1040,35 @@ hipError_t launch_masked_bwd(const Dims& d, const void* q, const void* k, const 
   a.reverse = launch_order_reversed();
   a.scale = d.scale;
   a.scale_log2 = d.scale * 1.4426950408889634f;
-  if (d.D == 128) launch_bwd_kernels<128>(d, a, o, st);
-  else launch_bwd_kernels<64>(d, a, o, st);
+
+  std::lock_guard<std::mutex> lk(g_side_mu);
+  SideStream* ss = side_stream(st);
+  hipStream_t ks = st;   // stream of the key-major half
+  if (ss) {
+    hipError_t e = hipEventRecord(ss->fork, st);
+    if (e == hipSuccess) e = hipStreamWaitEvent(ss->s, ss->fork, 0);
+    if (e != hipSuccess) return e;
+    ks = ss->s;
+  }
+  const int nb = KeyBuckets(d.S).nb;
+  hipLaunchKernelGGL(bwd_key_order_kernel, dim3(d.nseg()), dim3(1024), (size_t)nb * 2 * 4, ks, qend,
+                     korder, d.S, d.w);
+  const int nbins = plan_bins(d.S);
+  hipLaunchKernelGGL(bwd_tile_plan_kernel, dim3(d.nseg()), dim3(1024), (size_t)nbins * 2 * 4, ks,
+                     korder, qend, d.S, ktiles, tplan_tmp, tplan, tsplit);
+  if (d.D == 128) launch_dot_dq<128>(d, a, o, st, ss ? ss->dot_done : nullptr);
+  else launch_dot_dq<64>(d, a, o, st, ss ? ss->dot_done : nullptr);
+  if (ss) {
+    const hipError_t e = hipStreamWaitEvent(ks, ss->dot_done, 0);
+    if (e != hipSuccess) return e;
+  }
+  if (d.D == 128) launch_dkdv<128>(d, a, ks);
+  else launch_dkdv<64>(d, a, ks);
+  if (ss) {
+    hipError_t e = hipEventRecord(ss->join, ks);
+    if (e == hipSuccess) e = hipStreamWaitEvent(st, ss->join, 0);
+    if (e != hipSuccess) return e;
+  }
   return hipGetLastError();
 }
 
