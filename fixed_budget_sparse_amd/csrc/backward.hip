@@ -50,9 +50,9 @@ namespace {
 
 constexpr int kQThreads = 512;      // dQ: 8 waves x 32 stacked rows
 constexpr int kQChunk = 64;         // dQ: keys per chunk
-constexpr int kKWaves = 4;          // dK/dV: waves per workgroup, 32 keys each
-constexpr int kKTile = 32 * kKWaves;
-constexpr int kKThreads = 64 * kKWaves;
+constexpr int kKGroups = 4;         // dK/dV: 32-key groups per tile, one wave pair each
+constexpr int kKTile = 32 * kKGroups;
+constexpr int kKThreads = 128 * kKGroups;
 constexpr int kRChunk = 32;         // dK/dV: query rows per chunk
 
 typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
@@ -616,23 +616,35 @@ __global__ __launch_bounds__(kKThreads) void bwd_dkdv_kernel(BwdArgs a) {
   constexpr int RB = D * 2;                          // bytes per row
   constexpr int CB = kRChunk * RB;                   // bytes of one tensor's chunk
   constexpr int RPI = 1024 / RB;                     // rows per 1 KB direct load
-  constexpr int NDMA = kRChunk / RPI / kKWaves;      // direct loads per wave per tensor
-  constexpr int NLD = 2 * NDMA + 1;                  // direct loads per wave per item
-  static_assert(NDMA >= 1 && NDMA * RPI * kKWaves == kRChunk, "direct-load tiling");
-  static_assert(kRChunk == 32 && kKWaves == 4, "row-value load: 64 floats, 16 per wave");
+  constexpr int NW = kKThreads / 64;                 // waves
+  constexpr int NBLK = kRChunk / RPI;                // 1 KB blocks per tensor and item
+  constexpr int LPW = 2 * NBLK / NW;                 // row loads per wave and item
+  constexpr int NLD = LPW + 1;                       // direct loads per wave and item
+  static_assert(LPW >= 1 && LPW * NW == 2 * NBLK, "direct-load tiling");
+  static_assert(kRChunk == 32, "row values: 64 floats per item");
   // Six stages of one item each: the rows' LSE log2 e and D (64 floats),
   // then the Q rows, then the dO rows (row-major, swizzled like the dQ
   // kernel's K: read as rows for S and dP and transposed for dK and dV).
   // Stage offsets are multiples of 256 bytes, so adding one to a lane's
   // in-stage offset commutes with the XORs of the swizzle (bits 4..7).
+  // Then the exchange of P from the S waves to the dP waves: per step
+  // parity, per key group, 16 floats per lane in the MFMA result layout.
   constexpr int NST = 6;
   constexpr int RV = 2 * kRChunk * 4;                // bytes of row values
   constexpr int SB = RV + 2 * CB;                    // bytes per stage
   static_assert(SB % 256 == 0, "stage alignment");
-  __shared__ __attribute__((aligned(256))) unsigned char kvst[NST * SB];
+  constexpr int XB = kKGroups * 16 * 64 * 4;         // bytes of one exchange buffer
+  __shared__ __attribute__((aligned(256))) unsigned char kvst[NST * SB + 2 * XB];
+  unsigned char* const xbuf = kvst + NST * SB;
 
   const int lane = lane_id(), wave = wave_id();
   const int hh = lane >> 5, li = lane & 31;
+  // Two roles per key group, one wave each (waves g and g + 4 share a SIMD):
+  // role 0 computes S, P and dV, role 1 dP, dS and dK.  The roles split the
+  // work of a group without repeating any of it, and each holds half the
+  // operands and accumulators, so two waves fit on every SIMD and the MFMA
+  // stream of one overlaps the exp and select math of the other.
+  const int grp = wave & 3, role = wave >> 2;
   // the items of one (sequence, KV head) go to one XCD, longest first, so
   // the workgroups sharing an L2 read overlapping rows
   const int Lb = xcd_logical_block(launch_block(a.reverse), (int)gridDim.x);
@@ -646,7 +658,7 @@ __global__ __launch_bounds__(kKThreads) void bwd_dkdv_kernel(BwdArgs a) {
   const size_t seg = (size_t)b * a.Hkv + h;
 
   // this lane's key
-  const int slot = tile * kKTile + 32 * wave + li;
+  const int slot = tile * kKTile + 32 * grp + li;
   const int t = slot < S ? a.korder[seg * S + slot] : -1;
   const int qe = t >= 0 ? a.qend[seg * S + t] : -1;
   // The rows that keep key t are exactly [t, q_end(t)]: tau never increases
@@ -660,29 +672,22 @@ __global__ __launch_bounds__(kKThreads) void bwd_dkdv_kernel(BwdArgs a) {
   const int t_m = t >= 0 ? t : S + kRChunk;
   const size_t kvbase = seg * (size_t)S * D;
 
-  // B operands: K^T and V^T of this lane's key, dims [16 ks + 8 hh, +8)
-  // (loaded unconditionally from a clamped row, then zeroed for padding, and
-  // completed here: loads still pending at the loop would make the compiler
-  // wait for the loop's own prefetch before the first MFMA of every chunk)
-  bf16x8 kop[NKS], vop[NKS];
+  // B operand of the role's S or dP product: K^T (role 0) or V^T (role 1)
+  // of this lane's key, dims [16 ks + 8 hh, +8) (loaded unconditionally from
+  // a clamped row, then zeroed for padding, and completed here: loads still
+  // pending at the loop would make the compiler wait for the loop's own
+  // prefetch before the first MFMA of every chunk)
+  bf16x8 bop[NKS];
   {
-    const size_t krow = kvbase + (size_t)(t >= 0 ? t : 0) * D;
+    const uint16_t* src = (role ? a.v : a.k) + kvbase + (size_t)(t >= 0 ? t : 0) * D;
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
-      u32x4v u = *(const u32x4v*)(a.k + krow + 16 * ks + 8 * hh);
-      u32x4v x = *(const u32x4v*)(a.v + krow + 16 * ks + 8 * hh);
-      if (t < 0) u = x = u32x4v{0, 0, 0, 0};
-      kop[ks] = __builtin_bit_cast(bf16x8, u);
-      vop[ks] = __builtin_bit_cast(bf16x8, x);
+      u32x4v u = *(const u32x4v*)(src + 16 * ks + 8 * hh);
+      if (t < 0) u = u32x4v{0, 0, 0, 0};
+      bop[ks] = __builtin_bit_cast(bf16x8, u);
     }
 #pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) asm volatile("" : "+v"(kop[ks]), "+v"(vop[ks]));
-  }
-  f32x16 dkacc[NB], dvacc[NB];
-#pragma unroll
-  for (int d2 = 0; d2 < NB; ++d2) {
-    dkacc[d2] = f32x16{};
-    dvacc[d2] = f32x16{};
+    for (int ks = 0; ks < NKS; ++ks) asm volatile("" : "+v"(bop[ks]));
   }
   // work items: (query head, 32-row chunk) pairs over the item's chunks,
   // aligned to 32 rows (the plan's [min t, max q_end] of the tile, or one
@@ -704,28 +709,26 @@ __global__ __launch_bounds__(kKThreads) void bwd_dkdv_kernel(BwdArgs a) {
   auto clamp_pos = [&](ItemPos p) { return ItemPos{min(p.gg, G - 1), p.ci}; };
   // ---- staging of one item into the stage at byte offset so, all by
   // direct loads (lane L of a load writes 16 L, or 4 L, bytes past the
-  // load's LDS base): the Q and dO rows, lane L fetching the global piece its
-  // swizzled slot holds, and the rows' LSE log2 e (lanes 0..31) and D (lanes
-  // 32..63).  Rows past the end read row S - 1 and are masked.  Each wave
-  // issues NLD loads.
+  // load's LDS base): the Q and dO rows (1 KB blocks spread over the waves),
+  // lane L fetching the global piece its swizzled slot holds, and the rows'
+  // LSE log2 e (lanes 0..31) and D (lanes 32..63), loaded by every wave (the
+  // same bytes; no branch).  Rows past the end read row S - 1 and are
+  // masked.  Each wave issues NLD loads.
   auto dma_item = [&](ItemPos ip, int so) {
     const size_t hrow = ((size_t)b * a.Hq + h * G + ip.gg) * S;
     const int c0 = (c_first + ip.ci) * kRChunk;
-    const unsigned char* qh = (const unsigned char*)a.q + hrow * RB;
-    const unsigned char* oh = (const unsigned char*)a.dout + hrow * RB;
 #pragma unroll
-    for (int i = 0; i < NDMA; ++i) {
-      const int r0 = (wave * NDMA + i) * RPI;
+    for (int i = 0; i < LPW; ++i) {
+      const int L = wave * LPW + i;
+      const int tensor = L / NBLK, r0 = (L % NBLK) * RPI;   // tensor: wave-uniform
       const int row = r0 + lane / PPR, sl = lane % PPR;
       const int qq = min(c0 + row, S - 1);
       const uint32_t off = (uint32_t)qq * RB + ((sl ^ dq_swz<D>(row)) << 4);
-      dma_lds_x4_so(qh, off, kvst + so + RV + r0 * RB);
-      dma_lds_x4_so(oh, off, kvst + so + RV + CB + r0 * RB);
+      const unsigned char* base = (const unsigned char*)(tensor ? a.dout : a.q) + hrow * RB;
+      dma_lds_x4_so(base, off, kvst + so + RV + tensor * CB + r0 * RB);
     }
-    {   // every wave loads all 64 values (the same bytes): no branch
-      const int qq = min(c0 + li, S - 1);
-      dma_lds_x1((hh ? a.dvec : a.lse2) + hrow + qq, kvst + so);
-    }
+    const int qq = min(c0 + li, S - 1);
+    dma_lds_x1((hh ? a.dvec : a.lse2) + hrow + qq, kvst + so);
   };
 
   // per-lane in-stage LDS offsets: row reads (row li, piece 2 ks + hh: base
@@ -735,39 +738,38 @@ __global__ __launch_bounds__(kKThreads) void bwd_dkdv_kernel(BwdArgs a) {
   const int row_base = li * RB + ((hh ^ dq_swz<D>(li)) << 4);
   typedef __attribute__((address_space(3))) short4v lds_s4;
 
-  // ---- the pipeline.  Item i lives in stage i mod 6.  Iteration it, with
-  // S and dP of item it already in registers (set it mod 2):
-  //   * direct loads of item it+3 (two iterations of cover),
-  //   * S and dP of item it+1 (32 rows x 32 keys, the lane owning its key),
-  //   * dV^T += dO^T P and dK^T += Q^T dS of item it-1 (P and dS from the
-  //     previous iteration's registers, Q^T and dO^T read transposed),
-  //   * the probability and dS math of item it, spread between those 32
-  //     MFMAs (it depends on neither product),
-  //   * a wait for this wave's loads of item it+2 and a barrier that
-  //     publishes every wave's part.
-  // One wave per SIMD, so the layout of the step is the whole overlap: 32
-  // slots, each one MFMA, the LDS read of an operand kPf MFMAs ahead and a
-  // share of the math, fenced so the compiler keeps them in that order.
-  // Iterations past the last item (the count is padded to even with masked
-  // items) and the S / dP of the item after the last run on staged rows
-  // that exist and are not used.
+  // ---- the pipeline.  Item i lives in stage i mod 6; every wave loads
+  // its share of item it+3 in iteration it, waits for its loads of item
+  // it+2 at the end and meets the others at a barrier.  Iteration it:
+  //   role 0: S of item it+1; dV^T += dO^T P of item it-1 (P packed in the
+  //           previous iteration); P of item it from its S (computed in the
+  //           previous iteration): exp, then the interval select, written to
+  //           the exchange buffer and packed.
+  //   role 1: dP of item it; dK^T += Q^T dS of item it-2 (dS packed in the
+  //           previous iteration); dS of item it-1 = P (from the exchange
+  //           buffer, written by role 0 in the previous iteration) times
+  //           (dP - D), packed.
+  // Each role's MFMAs read their operands kPf MFMAs ahead, with the math
+  // between them.  The count is padded to even with masked items and runs
+  // two iterations past the last so that role 1 finishes; stages and
+  // exchange buffers that those and the first iterations read before any
+  // item reaches them are zeroed (zero P or dS times stale data could be
+  // NaN).
   constexpr int kPf = 4;                             // operand reads ahead of their MFMA
   const int n_pad = (n_items + 1) & ~1;
+  const int n_loop = n_pad > 0 ? n_pad + 2 : 0;
   auto stage_of = [&](int i) { return (i % NST) * SB; };
   auto mask_c0 = [&](int i, ItemPos p) {   // first row of item i, or far away when padding
     return i < n_items ? (c_first + p.ci) * kRChunk : -(1 << 30);
   };
+  // operand ks of the S (role 0, Q rows) or dP (role 1, dO rows) product of
+  // the item whose row-read base (row_base plus its stage offset) is rb
+  auto row_operand = [&](int rb, int ks) {
+    const unsigned char* p = kvst + (rb ^ (32 * ks)) + (role ? CB : 0);
+    return as_bf16x8(*(const uint4*)p);
+  };
 
   ItemPos cur{0, 0}, nx1{0, 0}, nx2{0, 0}, nx3{0, 0};   // items it .. it+3
-  f32x16 sA, pA, sB, pB;               // S and dP of items with even / odd index
-  bf16x8 ppA[2] = {}, psA[2] = {}, ppB[2] = {}, psB[2] = {};   // P and dS likewise
-  // operand q of the 2 NKS S / dP MFMAs (k-step q / 2; Q rows for even q,
-  // dO rows for odd q) of the item whose row-read base (row_base plus its
-  // stage offset) is rb
-  auto sd_operand = [&](int rb, int q) {
-    const unsigned char* p = kvst + (rb ^ (32 * (q >> 1)));
-    return as_bf16x8(*(const uint4*)(p + ((q & 1) ? CB : 0)));
-  };
   if (n_items > 0) {
     dma_item(cur, stage_of(0));
     nx1 = next_pos(cur);
@@ -775,159 +777,154 @@ __global__ __launch_bounds__(kKThreads) void bwd_dkdv_kernel(BwdArgs a) {
     nx2 = next_pos(nx1);
     dma_item(clamp_pos(nx2), stage_of(2));
     nx3 = next_pos(nx2);
-    {   // the first iteration's dV and dK products read stage 5 with zero P
-        // and dS: zero it (0 times a stale NaN is not 0)
-      uint4* z = (uint4*)(kvst + stage_of(NST - 1));
-      for (int i = threadIdx.x; i < SB / 16; i += kKThreads) z[i] = make_uint4(0, 0, 0, 0);
+    // stages 4 and 5 (read as items -2 and -1) and both exchange buffers
+    uint4* z = (uint4*)(kvst + stage_of(4));
+    for (int i = threadIdx.x; i < (2 * SB + 2 * XB) / 16; i += kKThreads) {
+      uint4* zp = i < 2 * SB / 16 ? z + i : (uint4*)xbuf + (i - 2 * SB / 16);
+      *zp = make_uint4(0, 0, 0, 0);
     }
     __builtin_amdgcn_s_waitcnt(0x0F70 | NLD);   // items 0 and 1 landed
     lds_barrier();
-    const int rb = row_base + stage_of(0) + RV;
-    sA = f32x16{};
-    pA = f32x16{};
-#pragma unroll
-    for (int q = 0; q < 2 * NKS; ++q) {
-      if (q & 1) pA = mfma32x32x16(sd_operand(rb, q), vop[q >> 1], pA);
-      else sA = mfma32x32x16(sd_operand(rb, q), kop[q >> 1], sA);
-    }
-  }
-  // iteration it; Sc/Pc: S and dP of item it, Sn/Pn: of item it+1; pp_prev:
-  // P and dS of item it-1, pp: of item it
-  auto step = [&](int it, f32x16& Sc, f32x16& Pc, f32x16& Sn, f32x16& Pn,
-                  const bf16x8 (&pp_prev)[2], const bf16x8 (&ps_prev)[2], bf16x8 (&pp)[2],
-                  bf16x8 (&ps)[2]) {
-    constexpr int NSD = 2 * NKS;                     // S / dP MFMAs
-    constexpr int NKV = 4 * NB;                      // dV / dK MFMAs
-    const int c0 = mask_c0(it, cur);
-    dma_item(clamp_pos(nx3), stage_of(it + 3));
-    __builtin_amdgcn_sched_barrier(0);
-    int rb = row_base + stage_of(it + 1) + RV;                 // item it+1
-    asm volatile("" : "+v"(rb));
-    // transposed operand m of the dV / dK MFMAs of item it-1 (stage
-    // (it-1) mod 6): block d2 = m / 4, k-step (m / 2) mod 2, dO^T (even m,
-    // for dV) or Q^T (odd m, for dK); the per-lane bases are made opaque so
-    // that every constant part of an address goes to the instruction's
-    // offset field
-    int trb[NB][2];
-#pragma unroll
-    for (int d2 = 0; d2 < NB; ++d2)
-#pragma unroll
-      for (int x = 0; x < 2; ++x) {
-        trb[d2][x] = tro[d2][x] + stage_of(it + NST - 1) + RV;
-        asm volatile("" : "+v"(trb[d2][x]));
-      }
-    auto tr_operand = [&](int m) {
-      const int d2 = m >> 2, ks = (m >> 1) & 1;
-      const unsigned char* p0 = kvst + trb[d2][0] + (16 * ks * RB + ((m & 1) ? 0 : CB));
-      const unsigned char* p1 = kvst + trb[d2][1] + (16 * ks * RB + ((m & 1) ? 0 : CB));
-      const short4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)p0);
-      const short4v hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)p1);
-      const short8v v8 = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-      return __builtin_bit_cast(bf16x8, v8);
-    };
-    auto operand = [&](int q) { return q < NSD ? sd_operand(rb, q) : tr_operand(q - NSD); };
-    // row values of item it
-    const float* r_lse = (const float*)(kvst + stage_of(it));
-    f32x4 lse4[4], d4[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      lse4[j] = *(const f32x4*)(r_lse + 8 * j + 4 * hh);
-      d4[j] = *(const f32x4*)(r_lse + kRChunk + 8 * j + 4 * hh);
-    }
-    bf16x8 op[NSD + NKV];
-#pragma unroll
-    for (int q = 0; q < kPf; ++q) op[q] = operand(q);
-    __builtin_amdgcn_sched_barrier(0);
-    Sn = f32x16{};
-    Pn = f32x16{};
-    float pv[16], dsv[16];
-#pragma unroll
-    for (int q = 0; q < NSD + NKV; ++q) {
-      if (q + kPf < NSD + NKV) op[q + kPf] = operand(q + kPf);
-      if (q < NSD) {
-        if (q & 1) Pn = mfma32x32x16(op[q], vop[q >> 1], Pn);
-        else Sn = mfma32x32x16(op[q], kop[q >> 1], Sn);
-      } else {
-        const int m = q - NSD, d2 = m >> 2, ks = (m >> 1) & 1;
-        if (m & 1) dkacc[d2] = mfma32x32x16(op[q], ps_prev[ks], dkacc[d2]);
-        else dvacc[d2] = mfma32x32x16(op[q], pp_prev[ks], dvacc[d2]);
-      }
-      // the math of item it: score e = q for the first 16 slots (the exp of
-      // every score, then a select: a masked score's exp may overflow and is
-      // never used), the bf16 packing in the next four
-      if (q < 16) {
-        const int e = q, j = e >> 2, r = e & 3, i0 = 8 * j + 4 * hh;
-        const bool kp = (unsigned)(c0 + i0 + r - t_m) <= span;
-        const float ex = exp2_fast(fmaf(Sc[e], a.scale_log2, -lse4[j][r]));
-        const float p = kp ? ex : 0.0f;
-        pv[e] = p;
-        dsv[e] = p * (Pc[e] - d4[j][r]);
-      } else if (q < 20) {
-        const int ks = (q - 16) >> 1;
-        if (q & 1) ps[ks] = pack_bf16x8(&dsv[8 * ks]);
-        else pp[ks] = pack_bf16x8(&pv[8 * ks]);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    static_assert(NSD + NKV >= 16, "one slot per score");
-    if constexpr (NSD + NKV < 20) {   // D = 64: 16 slots, the packing after them
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        pp[ks] = pack_bf16x8(&pv[8 * ks]);
-        ps[ks] = pack_bf16x8(&dsv[8 * ks]);
-      }
-    }
-    // the packed P and dS complete in this iteration (left alone, the
-    // compiler moves that math next to its use in the next one)
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) asm volatile("" ::"v"(pp[ks]), "v"(ps[ks]));
-    __builtin_amdgcn_s_waitcnt(0x0F70 | NLD);   // item it+2 landed
-    cur = nx1;
-    nx1 = nx2;
-    nx2 = nx3;
-    nx3 = next_pos(nx3);
-    lds_barrier();
-  };
-  for (int it = 0; it < n_pad; it += 2) {
-    step(it, sA, pA, sB, pB, ppB, psB, ppA, psA);
-    step(it + 1, sB, pB, sA, pA, ppA, psA, ppB, psB);
-  }
-  if (n_items > 0) {   // dV and dK of the last (padded) item
-    const unsigned char* tb = kvst + stage_of(n_pad - 1) + RV;
-#pragma unroll
-    for (int d2 = 0; d2 < NB; ++d2)
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        const unsigned char* p0 = tb + tro[d2][0] + 16 * ks * RB;
-        const unsigned char* p1 = tb + tro[d2][1] + 16 * ks * RB;
-        const short4v ol = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)(p0 + CB));
-        const short4v oh = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)(p1 + CB));
-        const short4v ql = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)p0);
-        const short4v qh = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)p1);
-        const short8v o8 = {ol[0], ol[1], ol[2], ol[3], oh[0], oh[1], oh[2], oh[3]};
-        const short8v q8 = {ql[0], ql[1], ql[2], ql[3], qh[0], qh[1], qh[2], qh[3]};
-        dvacc[d2] = mfma32x32x16(__builtin_bit_cast(bf16x8, o8), ppB[ks], dvacc[d2]);
-        dkacc[d2] = mfma32x32x16(__builtin_bit_cast(bf16x8, q8), psB[ks], dkacc[d2]);
-      }
-    __builtin_amdgcn_s_waitcnt(0x0F70);   // the loads past the end
   }
 
-  if (t >= 0) {
-    // the first (or only) part writes dk, dv; the second part of a split
-    // tile writes its sums beside them for the merge
-    float* p1 = a.part1 + (((size_t)sg * a.ktiles + tile) * kKTile + 32 * wave + li) * 2 * D;
-    float* dko = part ? p1 : a.dk + kvbase + (size_t)t * D;
-    float* dvo = part ? p1 + D : a.dv + kvbase + (size_t)t * D;
+  f32x16 acc[NB];                    // dV (role 0) or dK (role 1)
 #pragma unroll
-    for (int d2 = 0; d2 < D / 32; ++d2)
+  for (int d2 = 0; d2 < NB; ++d2) acc[d2] = f32x16{};
+
+  // one role's loop; X: S (role 0) or dP (role 1) of items with even / odd
+  // index, pk: packed P (role 0) or dS (role 1) likewise
+  auto run = [&](auto role_c) {
+    constexpr int R = decltype(role_c)::value;
+    f32x16 XA = f32x16{}, XB_ = f32x16{};
+    bf16x8 pkA[2] = {}, pkB[2] = {};
+    if constexpr (R == 0) {
+      if (n_items > 0) {   // S of item 0
+        const int rb = row_base + stage_of(0) + RV;
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) XA = mfma32x32x16(row_operand(rb, ks), bop[ks], XA);
+      }
+    }
+    // iteration it: Xp / Xn: X of the item this role reads / writes in it
+    // (role 0: S of it / it+1; role 1: dP of it-1 / it), pk_use: packed P or
+    // dS consumed (role 0: item it-1; role 1: it-2), pk_new: produced
+    // (role 0: item it; role 1: it-1)
+    auto step = [&](int it, f32x16& Xp, f32x16& Xn, const bf16x8 (&pk_use)[2],
+                    bf16x8 (&pk_new)[2]) {
+      constexpr int NMF = NKS + 2 * NB;              // MFMAs of the role per iteration
+      constexpr int EPS = (16 + NMF - 1) / NMF;      // scores per MFMA slot
+      const int c0 = mask_c0(it, cur);
+      dma_item(clamp_pos(nx3), stage_of(it + 3));
+      __builtin_amdgcn_sched_barrier(0);
+      // row reads: S of it+1 (role 0) or dP of it (role 1)
+      int rb = row_base + stage_of(R == 0 ? it + 1 : it) + RV;
+      asm volatile("" : "+v"(rb));
+      // transposed reads: dO^T of item it-1 (role 0) or Q^T of item it-2
+      // (role 1); opaque per-lane bases, constant parts in the offset field
+      int trb[NB][2];
+#pragma unroll
+      for (int d2 = 0; d2 < NB; ++d2)
+#pragma unroll
+        for (int x = 0; x < 2; ++x) {
+          trb[d2][x] = tro[d2][x] + stage_of(it + NST - (R == 0 ? 1 : 2)) + RV + (R == 0 ? CB : 0);
+          asm volatile("" : "+v"(trb[d2][x]));
+        }
+      auto tr_operand = [&](int m) {   // block m / 2, k-step m mod 2
+        const int d2 = m >> 1, ks = m & 1;
+        const short4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_s4*)(kvst + trb[d2][0] + 16 * ks * RB));
+        const short4v hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_s4*)(kvst + trb[d2][1] + 16 * ks * RB));
+        const short8v v8 = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        return __builtin_bit_cast(bf16x8, v8);
+      };
+      auto operand = [&](int q) { return q < NKS ? row_operand(rb, q) : tr_operand(q - NKS); };
+      // the math's inputs: role 0 the LSE of item it; role 1 D of item it-1
+      // and P of item it-1 from the exchange buffer
+      const float* rvals = (const float*)(kvst + stage_of(R == 0 ? it : it + NST - 1));
+      float4* xb = (float4*)(xbuf + ((R == 0 ? it : it + 1) & 1) * XB) + grp * 4 * 64 + lane;
+      f32x4 rv4[4];
+      float4 px[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        rv4[j] = *(const f32x4*)(rvals + (R == 0 ? 0 : kRChunk) + 8 * j + 4 * hh);
+        if constexpr (R == 1) px[j] = xb[64 * j];
+      }
+      bf16x8 op[NMF];
+#pragma unroll
+      for (int q = 0; q < kPf; ++q) op[q] = operand(q);
+      __builtin_amdgcn_sched_barrier(0);
+      Xn = f32x16{};
+      float pv[16];
+#pragma unroll
+      for (int q = 0; q < NMF; ++q) {
+        if (q + kPf < NMF) op[q + kPf] = operand(q + kPf);
+        if (q < NKS) {
+          Xn = mfma32x32x16(op[q], bop[q], Xn);
+        } else {
+          const int m = q - NKS;
+          acc[m >> 1] = mfma32x32x16(op[q], pk_use[m & 1], acc[m >> 1]);
+        }
+#pragma unroll
+        for (int e = q * EPS; e < (q + 1) * EPS && e < 16; ++e) {
+          const int j = e >> 2, r = e & 3;
+          if constexpr (R == 0) {
+            // P: the exp of every score, then a select (a masked score's
+            // exp may overflow; it is never used)
+            const bool kp = (unsigned)(c0 + 8 * j + 4 * hh + r - t_m) <= span;
+            const float ex = exp2_fast(fmaf(Xp[e], a.scale_log2, -rv4[j][r]));
+            pv[e] = kp ? ex : 0.0f;
+          } else {
+            const float p = r == 0 ? px[j].x : r == 1 ? px[j].y : r == 2 ? px[j].z : px[j].w;
+            pv[e] = p * (Xp[e] - rv4[j][r]);   // dS
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      if constexpr (R == 0) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          xb[64 * j] = make_float4(pv[4 * j], pv[4 * j + 1], pv[4 * j + 2], pv[4 * j + 3]);
+      }
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) pk_new[ks] = pack_bf16x8(&pv[8 * ks]);
+      // the packed values complete in this iteration (left alone, the
+      // compiler moves that math next to its use in the next one)
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) asm volatile("" ::"v"(pk_new[ks]));
+      __builtin_amdgcn_s_waitcnt(0x0F70 | NLD);   // item it+2 landed
+      cur = nx1;
+      nx1 = nx2;
+      nx2 = nx3;
+      nx3 = next_pos(nx3);
+      lds_barrier();
+    };
+    for (int it = 0; it < n_loop; it += 2) {
+      if constexpr (R == 0) {
+        step(it, XA, XB_, pkB, pkA);         // S of it (even) / it+1; P of it-1 / it
+        step(it + 1, XB_, XA, pkA, pkB);
+      } else {
+        step(it, XB_, XA, pkA, pkB);         // dP of it-1 (odd) / it; dS of it-2 / it-1
+        step(it + 1, XA, XB_, pkB, pkA);
+      }
+    }
+  };
+  if (role == 0) run(std::integral_constant<int, 0>{});
+  else run(std::integral_constant<int, 1>{});
+  if (n_items > 0) __builtin_amdgcn_s_waitcnt(0x0F70);   // the loads past the end
+
+  if (t >= 0) {
+    // the first (or only) part writes dk (role 1) or dv (role 0); the second
+    // part of a split tile writes its sums beside them for the merge
+    float* p1 = a.part1 + (((size_t)sg * a.ktiles + tile) * kKTile + 32 * grp + li) * 2 * D;
+    float* out = part ? p1 + (role ? 0 : D) : (role ? a.dk : a.dv) + kvbase + (size_t)t * D;
+    const float sc = role ? a.scale : 1.0f;
+#pragma unroll
+    for (int d2 = 0; d2 < NB; ++d2)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int d = 32 * d2 + 8 * j + 4 * hh;
-        *(float4*)(dko + d) = make_float4(dkacc[d2][4 * j] * a.scale, dkacc[d2][4 * j + 1] * a.scale,
-                                          dkacc[d2][4 * j + 2] * a.scale,
-                                          dkacc[d2][4 * j + 3] * a.scale);
-        *(float4*)(dvo + d) = make_float4(dvacc[d2][4 * j], dvacc[d2][4 * j + 1],
-                                          dvacc[d2][4 * j + 2], dvacc[d2][4 * j + 3]);
+        *(float4*)(out + d) = make_float4(acc[d2][4 * j] * sc, acc[d2][4 * j + 1] * sc,
+                                          acc[d2][4 * j + 2] * sc, acc[d2][4 * j + 3] * sc);
       }
   }
 }
