@@ -112,21 +112,25 @@ def sparse_lse_study(kv, torch, q, kk, lse_sparse, tgt, score, s, w, k, eps):
                                       "min": round(overlap.min().item(), 4)}}
 
 
-def bench_backward(kv, torch, q, kk, v, o, lse, rank, tau, s, w, k, ev, reps=3):
+def bench_backward(kv, torch, q, kk, v, o, lse, rank, tau, s, w, k, ev, reps=3, batches=5):
     """Backward of the step's sparse forward (its O and LSE) for a seeded
-    upstream gradient dO; algorithmic work 8 D flop per kept pair per query
-    head (the dP, dQ, dK and dV products)."""
+    upstream gradient dO, the median over `batches` batches of `reps` calls;
+    algorithmic work 8 D flop per kept pair per query head (the dP, dQ, dK
+    and dV products)."""
     from workloads import QWEN3_4B_S16K, make_grad_device
     dout = make_grad_device(QWEN3_4B_S16K, q.device)
     dq, dk, dv = kv.masked_attn_bwd(q, kk, v, o, lse, rank, tau, dout, s, w, k)
     torch.cuda.synchronize()
-    e0, e1 = ev(), ev()
-    e0.record()
-    for _ in range(reps):
-        kv.masked_attn_bwd(q, kk, v, o, lse, rank, tau, dout, s, w, k, dq=dq, dk=dk, dv=dv)
-    e1.record()
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / reps
+    per_batch = []
+    for _ in range(batches):
+        e0, e1 = ev(), ev()
+        e0.record()
+        for _ in range(reps):
+            kv.masked_attn_bwd(q, kk, v, o, lse, rank, tau, dout, s, w, k, dq=dq, dk=dk, dv=dv)
+        e1.record()
+        torch.cuda.synchronize()
+        per_batch.append(e0.elapsed_time(e1) / reps)
+    ms = sorted(per_batch)[len(per_batch) // 2]
     Hq, S, D = q.shape[1], q.shape[2], q.shape[3]
     flop = 8 * D * Hq * fwd_pairs(S, s + w + k)
     return {"ms": round(ms, 4), "tflops": round(flop / (ms * 1e-3) / 1e12, 2), "flop": flop,
