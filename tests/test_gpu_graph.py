@@ -1,4 +1,5 @@
-"""Decode steps replayed from a captured HIP graph give the eager results.
+"""Decode steps and the masked backward replayed from captured HIP graphs give
+the eager results.
 
 A decode step takes every input as a device pointer (the position included)
 and makes no allocation, copy, memset or host synchronisation, so a model can
@@ -101,3 +102,47 @@ def test_decode_graph_replays_match_eager(per_graph):
         assert torch.equal(l_s.view(torch.int32), ref_l[p].view(torch.int32)), (r, p)
     for a, b in zip(caches, ref):
         assert _same_cache(a, b)
+
+
+def test_backward_graph_replays_match_eager():
+    """The masked backward captured in a HIP graph (its key-major half forked to
+    the library's second stream and joined back, as events in the capture)
+    replays the eager gradients bit for bit, with eager work between replays."""
+    announce("masked backward graph replay (S 1500, split dK/dV tiles)")
+    dev = device()
+    b, hq, hkv, S, D, s, w, k = 1, 8, 2, 1500, 128, 8, 64, 200
+    bf = torch.bfloat16
+    g = torch.Generator(device=dev)
+    g.manual_seed(91)
+    q = torch.randn((b, hq, S, D), generator=g, device=dev).to(bf)
+    kk = (torch.randn((b, hkv, S, D), generator=g, device=dev) * 0.3).to(bf)
+    v = torch.randn((b, hkv, S, D), generator=g, device=dev).to(bf)
+    dout = torch.randn((b, hq, S, D), generator=g, device=dev).to(bf)
+    prio = torch.randn((b, hkv, S), generator=g, device=dev)
+    rank, tau = kv.thresholds(prio, s, w, k)
+    o, lse = kv.masked_attn_fwd(q, kk, v, rank, tau, s, w, k, out_dtype=bf)
+    ref = kv.masked_attn_bwd(q, kk, v, o, lse, rank, tau, dout, s, w, k)
+    torch.cuda.synchronize()
+
+    f32 = torch.float32
+    dq = torch.empty((b, hq, S, D), dtype=f32, device=dev)
+    dk = torch.empty((b, hkv, S, D), dtype=f32, device=dev)
+    dv = torch.empty((b, hkv, S, D), dtype=f32, device=dev)
+    side = torch.cuda.Stream(device=dev)
+    side.wait_stream(torch.cuda.current_stream(dev))
+    with torch.cuda.stream(side):
+        kv.masked_attn_bwd(q, kk, v, o, lse, rank, tau, dout, s, w, k, dq=dq, dk=dk, dv=dv)
+    torch.cuda.current_stream(dev).wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        kv.masked_attn_bwd(q, kk, v, o, lse, rank, tau, dout, s, w, k, dq=dq, dk=dk, dv=dv)
+    scratch = torch.randn((256, 256), device=dev)
+    for r in range(3):
+        dq.zero_()
+        dk.zero_()
+        dv.zero_()
+        graph.replay()
+        scratch = torch.tanh(scratch @ scratch.t() * 1e-3)
+        torch.cuda.synchronize()
+        for name, got, want in (("dq", dq, ref[0]), ("dk", dk, ref[1]), ("dv", dv, ref[2])):
+            assert torch.equal(got.view(torch.int32), want.view(torch.int32)), (r, name)

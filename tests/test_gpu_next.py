@@ -8,7 +8,7 @@ import torch
 
 import fixed_budget_sparse_amd as kv
 import oracle as orc
-from gpu_util import BWD_TOL, TOL, announce, device, host, to_dev
+from gpu_util import BF16_U, BWD_TOL, TOL, announce, device, host, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -348,7 +348,42 @@ BWD_CASES = [
     (1, 8, 1, 130, 128, 1, 1, 500, "f32"),      # k >= S: dense causal; w = 1; G = 8
     (1, 2, 2, 64, 128, 0, 5, 10, "f32"),        # s = 0
     (1, 8, 2, 1500, 128, 8, 64, 200, "bf16"),   # several tiles, listed long-range keys
+    (1, 4, 2, 700, 64, 2, 40, 90, "f32"),       # D = 64, G = 2, split dK/dV tiles
+    (1, 6, 2, 333, 128, 3, 20, 50, "bf16"),     # G = 3: odd item counts (padded items)
 ]
+
+
+def _bwd_rounding_bounds(q, k, v, dout, rank, tau, s, w, o_bf16):
+    """First-order bound on each gradient element's error from the bfloat16
+    roundings of the path: the forward's probabilities in O (and O itself
+    when it is bfloat16) through D_i = <dO_i, O_i>, dS before the dQ and dK
+    products, P before the dV product.  Every term is taken with its largest
+    rounding and its absolute value, so no cancellation can hide behind it;
+    float32 sums add far less (n 2^-24 relative)."""
+    b, hq, S, D = q.shape
+    G = hq // k.shape[1]
+    sc = orc.default_scale(D, 0.0)
+    u = BF16_U
+    bq, bk, bv = np.zeros(q.shape), np.zeros(k.shape), np.zeros(v.shape)
+    qs = np.arange(S)
+    for bi in range(b):
+        for hh in range(hq):
+            h = hh // G
+            K, V = k[bi, h].astype(np.float64), v[bi, h].astype(np.float64)
+            Q, dO = q[bi, hh].astype(np.float64), dout[bi, hh].astype(np.float64)
+            keep = orc.mask_rows(rank[bi, h], tau[bi, h, qs], qs, s, w)
+            z = np.where(keep, sc * (Q @ K.T), -np.inf)
+            e = np.where(keep, np.exp(z - z.max(1, keepdims=True)), 0.0)
+            P = e / e.sum(1, keepdims=True)
+            O = P @ V
+            dS = P * (dO @ V.T - (dO * O).sum(1, keepdims=True))
+            o_err = u * (P @ np.abs(V)) + (u * np.abs(O) if o_bf16 else 0.0)
+            d_err = (np.abs(dO) * o_err).sum(1, keepdims=True)
+            ds_err = u * np.abs(dS) + P * d_err
+            bq[bi, hh] = sc * (ds_err @ np.abs(K))
+            bk[bi, h] += sc * (ds_err.T @ np.abs(Q))
+            bv[bi, h] += u * (P.T @ np.abs(dO))
+    return bq, bk, bv
 
 
 @pytest.mark.parametrize("case", BWD_CASES, ids=lambda c: "b{}q{}kv{}S{}D{}s{}w{}k{}-{}".format(*c))
@@ -370,9 +405,13 @@ def test_masked_attn_bwd_parity(case):
     rank_o = orc.priority_ranks(prio)
     tau_o = orc.thresholds_by_selection(rank_o, s, w, k)
     rq, rk, rv = orc.masked_attention_backward(q, kk, v, rank_o, tau_o, s, w, dout)
-    for name, got, ref in (("dq", host(dq), rq), ("dk", host(dk), rk), ("dv", host(dv), rv)):
+    bounds = _bwd_rounding_bounds(q, kk, v, dout, rank_o, tau_o, s, w, odt == "bf16")
+    for name, got, ref, bd in zip(("dq", "dk", "dv"), (host(dq), host(dk), host(dv)),
+                                  (rq, rk, rv), bounds):
         err = got.astype(np.float64) - ref
         fro = np.linalg.norm(err) / np.linalg.norm(ref)
-        mx = np.abs(err).max() / np.abs(ref).max()
-        tol = BWD_TOL[odt]
-        assert fro <= tol["fro"] and mx <= tol["max"], (name, fro, mx)
+        assert fro <= BWD_TOL[odt]["fro"], (name, fro)
+        # every element within its rounding bound (plus float32 noise where
+        # the bound vanishes: a row whose one kept key gives dS = 0)
+        over = np.abs(err) - (bd + 1e-6 * np.abs(ref).max())
+        assert (over <= 0).all(), (name, np.unravel_index(over.argmax(), over.shape), over.max())
