@@ -53,7 +53,11 @@ class _Problem(ctypes.Structure):
 
 class _Cache(ctypes.Structure):
     _fields_ = [("k", ctypes.c_void_p), ("v", ctypes.c_void_p), ("slot_pos", ctypes.c_void_p),
-                ("slot_prio", ctypes.c_void_p), ("ring", ctypes.c_void_p)]
+                ("slot_prio", ctypes.c_void_p), ("ring", ctypes.c_void_p),
+                ("state", ctypes.c_void_p)]
+
+
+CACHE_STATE_WORDS = 8   # KVPOP_CACHE_STATE_WORDS
 
 
 _lib = None
@@ -252,10 +256,14 @@ class DecodeCache:
     slot_pos: torch.Tensor   # [b, Hkv, Bc] int32
     slot_prio: torch.Tensor  # [b, Hkv, Bc] float32
     ring: torch.Tensor       # [b, Hkv, w] int32
+    # [b, Hkv, CACHE_STATE_WORDS] int32: the next step's record, or None (every
+    # full step then scans the slots)
+    state: Optional[torch.Tensor] = None
 
     def c(self) -> _Cache:
         return _Cache(self.k.data_ptr(), self.v.data_ptr(), self.slot_pos.data_ptr(),
-                      self.slot_prio.data_ptr(), self.ring.data_ptr())
+                      self.slot_prio.data_ptr(), self.ring.data_ptr(),
+                      self.state.data_ptr() if self.state is not None else None)
 
     def reset(self) -> None:
         """Back to the empty state of new_decode_cache, in place (same memory)."""
@@ -264,10 +272,27 @@ class DecodeCache:
         self.slot_pos.fill_(-1)
         self.slot_prio.zero_()
         self.ring.zero_()
+        if self.state is not None:
+            self.state.zero_()
+
+    def arrays(self):
+        """Every array of the cache (the state included when present)."""
+        return tuple(t for t in (self.k, self.v, self.slot_pos, self.slot_prio, self.ring,
+                                 self.state) if t is not None)
 
     def clone(self) -> "DecodeCache":
-        return DecodeCache(*(t.clone() for t in (self.k, self.v, self.slot_pos, self.slot_prio,
-                                                 self.ring)))
+        return DecodeCache(*(t.clone() if t is not None else None
+                             for t in (self.k, self.v, self.slot_pos, self.slot_prio,
+                                       self.ring, self.state)))
+
+    def check(self, b: int, hkv: int, Bc: int, D: int, window: int, dtype, dev) -> None:
+        _need(self.k, "cache.k", (b, hkv, Bc, D), dtype, dev)
+        _need(self.v, "cache.v", (b, hkv, Bc, D), dtype, dev)
+        _need(self.slot_pos, "cache.slot_pos", (b, hkv, Bc), torch.int32, dev)
+        _need(self.slot_prio, "cache.slot_prio", (b, hkv, Bc), torch.float32, dev)
+        _need(self.ring, "cache.ring", (b, hkv, window), torch.int32, dev)
+        if self.state is not None:
+            _need(self.state, "cache.state", (b, hkv, CACHE_STATE_WORDS), torch.int32, dev)
 
 
 def new_decode_cache(batch: int, n_kv_heads: int, head_dim: int, sink: int, window: int,
@@ -279,7 +304,8 @@ def new_decode_cache(batch: int, n_kv_heads: int, head_dim: int, sink: int, wind
         torch.zeros((batch, n_kv_heads, Bc, head_dim), dtype=dtype, **z),
         torch.full((batch, n_kv_heads, Bc), -1, dtype=torch.int32, **z),
         torch.zeros((batch, n_kv_heads, Bc), dtype=torch.float32, **z),
-        torch.zeros((batch, n_kv_heads, max(window, 1)), dtype=torch.int32, **z))
+        torch.zeros((batch, n_kv_heads, max(window, 1)), dtype=torch.int32, **z),
+        torch.zeros((batch, n_kv_heads, CACHE_STATE_WORDS), dtype=torch.int32, **z))
 
 
 def decode_step(cache: DecodeCache, pos: torch.Tensor, q: torch.Tensor, k_new: torch.Tensor,
@@ -297,11 +323,7 @@ def decode_step(cache: DecodeCache, pos: torch.Tensor, q: torch.Tensor, k_new: t
     _need(v_new, "v_new", (b, hkv, D), q.dtype, dev)
     _need(prio_leaving, "prio_leaving", (b, hkv), torch.float32, dev)
     _need(pos, "pos", (b,), torch.int32, dev)
-    _need(cache.k, "cache.k", (b, hkv, Bc, D), q.dtype, dev)
-    _need(cache.v, "cache.v", (b, hkv, Bc, D), q.dtype, dev)
-    _need(cache.slot_pos, "cache.slot_pos", (b, hkv, Bc), torch.int32, dev)
-    _need(cache.slot_prio, "cache.slot_prio", (b, hkv, Bc), torch.float32, dev)
-    _need(cache.ring, "cache.ring", (b, hkv, window), torch.int32, dev)
+    cache.check(b, hkv, Bc, D, window, q.dtype, dev)
     o = torch.empty((b, hq, D), dtype=out_dtype, device=dev) if o is None else o
     lse = torch.empty((b, hq), dtype=torch.float32, device=dev) if lse is None else lse
     _need(o, "o", (b, hq, D), out_dtype, dev)
@@ -338,11 +360,7 @@ def decode_step_noalloc(cache: DecodeCache, pos: torch.Tensor, q: torch.Tensor,
     _need(v_new, "v_new", (b, hkv, D), q.dtype, dev)
     _need(prio_leaving, "prio_leaving", (b, hkv), torch.float32, dev)
     _need(pos, "pos", (b,), torch.int32, dev)
-    _need(cache.k, "cache.k", (b, hkv, Bc, D), q.dtype, dev)
-    _need(cache.v, "cache.v", (b, hkv, Bc, D), q.dtype, dev)
-    _need(cache.slot_pos, "cache.slot_pos", (b, hkv, Bc), torch.int32, dev)
-    _need(cache.slot_prio, "cache.slot_prio", (b, hkv, Bc), torch.float32, dev)
-    _need(cache.ring, "cache.ring", (b, hkv, window), torch.int32, dev)
+    cache.check(b, hkv, Bc, D, window, q.dtype, dev)
     o = torch.empty((b, hq, D), dtype=out_dtype, device=dev) if o is None else o
     lse = torch.empty((b, hq), dtype=torch.float32, device=dev) if lse is None else lse
     _need(o, "o", (b, hq, D), out_dtype, dev)
@@ -370,11 +388,7 @@ def cache_from_prefill(cache: DecodeCache, k: torch.Tensor, v: torch.Tensor, pri
     _need(prio, "prio", (b, hkv, S), torch.float32, dev)
     _need(rank, "rank", (b, hkv, S), torch.int32, dev)
     _need(tau, "tau", (b, hkv, S), torch.int32, dev)
-    _need(cache.k, "cache.k", (b, hkv, Bc, D), k.dtype, dev)
-    _need(cache.v, "cache.v", (b, hkv, Bc, D), k.dtype, dev)
-    _need(cache.slot_pos, "cache.slot_pos", (b, hkv, Bc), torch.int32, dev)
-    _need(cache.slot_prio, "cache.slot_prio", (b, hkv, Bc), torch.float32, dev)
-    _need(cache.ring, "cache.ring", (b, hkv, window), torch.int32, dev)
+    cache.check(b, hkv, Bc, D, window, k.dtype, dev)
     pr = Problem(b, hkv, hkv, S, D, sink, window, topk, 0.0, _dtype_code(k.dtype), 0)
     c, cc = pr.c(), cache.c()
     _status(lib().kvpop_cache_from_prefill(ctypes.byref(c), ctypes.byref(cc), _vp(k), _vp(v),

@@ -150,7 +150,8 @@ KVPOP_EXPORT kvpop_status kvpop_decode_step(const kvpop_problem* pr, const kvpop
   if (!pos || !q || !k_new || !v_new || !prio_leaving || !o) return KVPOP_ERR_ARG;
   st = check_ws(KVPOP_CALL_DECODE, d, ws, ws_bytes_);
   if (st != KVPOP_OK) return st;
-  kvpop::CacheArgs c{cache->k, cache->v, cache->slot_pos, cache->slot_prio, cache->ring};
+  kvpop::CacheArgs c{cache->k, cache->v, cache->slot_pos, cache->slot_prio, cache->ring,
+                     cache->state};
   return finish(kvpop::launch_decode(d, c, pos, q, k_new, v_new, prio_leaving, o, lse, ws, stream));
 }
 
@@ -169,7 +170,8 @@ KVPOP_EXPORT kvpop_status kvpop_decode_step_noalloc(const kvpop_problem* pr,
   if (need > kvpop::decode_noalloc_scratch_bytes()) return KVPOP_ERR_SCRATCH;
   void* ws = nullptr;
   if (need > 0 && kvpop::decode_noalloc_scratch(stream, &ws) != hipSuccess) return KVPOP_ERR_HIP;
-  kvpop::CacheArgs c{cache->k, cache->v, cache->slot_pos, cache->slot_prio, cache->ring};
+  kvpop::CacheArgs c{cache->k, cache->v, cache->slot_pos, cache->slot_prio, cache->ring,
+                     cache->state};
   return finish(kvpop::launch_decode(d, c, pos, q, k_new, v_new, prio_leaving, o, lse, ws, stream));
 }
 
@@ -184,7 +186,8 @@ KVPOP_EXPORT kvpop_status kvpop_cache_from_prefill(const kvpop_problem* pr,
   if (!cache || !cache->k || !cache->v || !cache->slot_pos || !cache->slot_prio || !cache->ring)
     return KVPOP_ERR_ARG;
   if (!k || !v || !prio || !rank || !tau) return KVPOP_ERR_ARG;
-  kvpop::CacheArgs c{cache->k, cache->v, cache->slot_pos, cache->slot_prio, cache->ring};
+  kvpop::CacheArgs c{cache->k, cache->v, cache->slot_pos, cache->slot_prio, cache->ring,
+                     cache->state};
   return finish(kvpop::launch_cache_from_prefill(d, c, k, v, prio, rank, tau, stream));
 }
 

@@ -7,11 +7,16 @@
 //
 // One kernel per step (two with split-K), on the caller's stream:
 //  1. attend, one workgroup per (sequence, KV head, split): first the step's
-//     decision from the slot metadata as it stands — the slot token p takes
-//     (slot p while the cache fills; afterwards the slot of u when u is
-//     dropped, or of the worst held long-range token when u replaces it),
-//     exact integer/compare work with the worst token found by wave shuffle
-//     and LDS reductions; every split of the pair computes the same decision.
+//     decision — the slot token p takes (slot p while the cache fills;
+//     afterwards the slot of u when u is dropped, or of the worst held
+//     long-range token when u replaces it).  The worst token comes from the
+//     pair's record in the cache's state array, written by the previous step
+//     for this one; without a current record (no state array, a new handoff,
+//     a record marked stale) every slot's metadata is scanned, with wave
+//     shuffle and LDS reductions.  Every split computes the same decision,
+//     and each also scans its own slots, as the update leaves them, for the
+//     next step's worst token (one split: it writes the record; several:
+//     their candidates go to the combine, which writes it).
 //     Then every wave streams 32-slot blocks of K and V from HBM with
 //     coalesced loads, the new token's row read from k_new / v_new in place
 //     of its slot, prefetching the next block into registers while the
@@ -23,8 +28,8 @@
 //     the decision.  The split owning the new token's slot writes its K/V row
 //     there at the end (no other workgroup reads that slot in this step).
 //  2. combine (only with several splits, after every split has read the
-//     metadata): applies the recorded metadata update and merges the
-//     partials into o and lse.
+//     metadata): applies the recorded metadata update, writes the next
+//     step's record and merges the partials into o and lse.
 // A device-scope fence per workgroup (to let the last one merge) would write
 // back and invalidate the L2 of its XCD on this multi-XCD part, so the merge
 // across workgroups is a separate kernel.
@@ -59,6 +64,8 @@ struct DecArgs {
   float* lse;
   float* part;          // [b, Hq, nsplit, D + 2]: max (log2 units), sum, unnormalised O
   int* dec;             // [b, Hkv, 4] the step's decision, applied by the combine (splits > 1)
+  int* cand;            // [b, Hkv, nsplit, 4] each split's worst candidate for the next step
+  int* state;           // [b, Hkv, 8] the next step's worst long-range token per pair, or null
   int Hq, Hkv, G, s, w, k, Bc, spl, nsplit;
   float scale_log2;
 };
@@ -76,6 +83,8 @@ __device__ __forceinline__ bool worse_than(const Worst& a, const Worst& b) {
 
 constexpr int kDecideThreads = 256;
 constexpr int kDecideUnroll = 8;   // slot loads in flight per thread
+constexpr int kStateWords = KVPOP_CACHE_STATE_WORDS;   // per-pair record of the next step
+constexpr int kRescanEarly = 2;    // next-step candidate slots per thread loaded before the math
 
 __device__ __forceinline__ void wave_reduce_worst(Worst& best) {
 #pragma unroll
@@ -122,10 +131,23 @@ __device__ Decision decide_step(const DecArgs& a, size_t seg, int p, Worst* s_wo
     // full: u = p - w >= s + k; it is kept iff it beats the worst long-range token
     dc.u_slot = ring[p % w];
     dc.pu = canonical_priority(a.prio_leaving[seg]);
+    // the worst held long-range token: from the pair's record when the
+    // previous step wrote it for this step, else from a scan of every slot
+    Worst best{__builtin_huge_valf(), -1, -1};
+    bool have = false;
+    if (k > 0 && a.state) {
+      const int4 r = *(const int4*)(a.state + seg * kStateWords);
+      if (__builtin_amdgcn_readfirstlane(r.x) == p) {
+        best = Worst{__int_as_float(r.y), r.z, r.w};
+        have = true;
+      }
+    }
     if (k == 0) {
       dc.ns = dc.u_slot;
+    } else if (have) {
+      dc.keep_u = best.slot >= 0 && dc.pu > best.p;
+      dc.ns = dc.keep_u ? best.slot : dc.u_slot;
     } else {
-      Worst best{__builtin_huge_valf(), -1, -1};
       for (int j0 = tid; j0 < Bc; j0 += kDecideThreads * kDecideUnroll) {
         int sp[kDecideUnroll];
         float pr[kDecideUnroll];
@@ -168,6 +190,19 @@ __device__ __forceinline__ void apply_decision(const DecArgs& a, size_t seg, int
   sprio[dc.ns] = 0.0f;
 }
 
+// Folds slot j into the next step's worst long-range candidate `best`, with
+// the metadata (sp, pr) as read before step p's update dc: after the update
+// slot dc.ns holds token p (not a candidate), slot dc.u_slot holds u = p - w
+// with priority dc.pu when u is kept; a candidate of step p + 1 has
+// s <= position <= p - w.
+__device__ __forceinline__ void fold_candidate(Worst& best, int j, int sp, float pr,
+                                               const Decision& dc, int s, int u) {
+  if (j == dc.ns) return;
+  if (dc.keep_u && j == dc.u_slot) pr = dc.pu;
+  const Worst c{pr, sp, j};
+  if (sp >= s && sp <= u && worse_than(c, best)) best = c;
+}
+
 template <int D, bool kF32>
 struct DecLds {
   // bf16: K [32][D+8]; V^T [D][32+8] (permuted columns)
@@ -183,8 +218,10 @@ struct DecLds {
   static constexpr int VTL = (kBlk / 2) * (D / 8) / 64;
 };
 
+// Two workgroups per CU, except for float32 caches at D = 128, whose staging
+// registers allow one.
 template <int D, bool kF32, bool kF32Out>
-__global__ __launch_bounds__(kThreads, 2) void decode_attend_kernel(DecArgs a) {
+__global__ __launch_bounds__(kThreads, (kF32 && D == 128) ? 1 : 2) void decode_attend_kernel(DecArgs a) {
   using L = DecLds<D, kF32>;
   static_assert(kWaves * L::waveBytes >= kWaves * 32 * (D + 2) * 4, "merge area");
   __shared__ __attribute__((aligned(16))) unsigned char lds[kWaves * L::waveBytes];
@@ -237,7 +274,8 @@ __global__ __launch_bounds__(kThreads, 2) void decode_attend_kernel(DecArgs a) {
   uint4 kst[L::KPL];
   u32x4v vpair[kF32 ? 1 : 2 * L::VTL];
   uint4 vst4[kF32 ? L::KPL : 1];
-  auto load_blk = [&](int blk) {
+  // (slots at or past `lim` read as zeros)
+  auto load_blk = [&](int blk, int lim) {
     if constexpr (!kF32) {
       const uint16_t* kg = (const uint16_t*)a.ck + cbase;
       const uint16_t* vg = (const uint16_t*)a.cv + cbase;
@@ -250,7 +288,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_attend_kernel(DecArgs a) {
       for (int i = 0; i < L::KPL; ++i) {
         const int pi = lane + 64 * i;
         const int slot = blk + pi / PPR;
-        kst[i] = slot < j_hi ? *(const uint4*)(krow(slot) + (pi % PPR) * 8)
+        kst[i] = slot < lim ? *(const uint4*)(krow(slot) + (pi % PPR) * 8)
                              : make_uint4(0, 0, 0, 0);
       }
 #pragma unroll
@@ -259,8 +297,8 @@ __global__ __launch_bounds__(kThreads, 2) void decode_attend_kernel(DecArgs a) {
         const int pr = task & 15, oc = task >> 4;      // pairs fastest: distinct LDS banks
         const int s0 = blk + 2 * pr;
         const u32x4v z = {0u, 0u, 0u, 0u};
-        vpair[2 * i] = s0 < j_hi ? *(const u32x4v*)(vrow(s0) + 8 * oc) : z;
-        vpair[2 * i + 1] = s0 + 1 < j_hi ? *(const u32x4v*)(vrow(s0 + 1) + 8 * oc) : z;
+        vpair[2 * i] = s0 < lim ? *(const u32x4v*)(vrow(s0) + 8 * oc) : z;
+        vpair[2 * i + 1] = s0 + 1 < lim ? *(const u32x4v*)(vrow(s0 + 1) + 8 * oc) : z;
       }
     } else {
       const float* kg = (const float*)a.ck + cbase;
@@ -275,8 +313,8 @@ __global__ __launch_bounds__(kThreads, 2) void decode_attend_kernel(DecArgs a) {
         const int piece = (pi % PPR) * 4;
         const float* kr = slot == ns_sub ? kn : kg + (size_t)slot * D;
         const float* vr = slot == ns_sub ? vn : vg + (size_t)slot * D;
-        kst[i] = slot < j_hi ? *(const uint4*)(kr + piece) : make_uint4(0, 0, 0, 0);
-        vst4[i] = slot < j_hi ? *(const uint4*)(vr + piece) : make_uint4(0, 0, 0, 0);
+        kst[i] = slot < lim ? *(const uint4*)(kr + piece) : make_uint4(0, 0, 0, 0);
+        vst4[i] = slot < lim ? *(const uint4*)(vr + piece) : make_uint4(0, 0, 0, 0);
       }
     }
   };
@@ -325,27 +363,67 @@ __global__ __launch_bounds__(kThreads, 2) void decode_attend_kernel(DecArgs a) {
     }
   };
 
-  // the first block's loads are issued before the step's decision (its slot
-  // is patched afterwards); the new token's K/V row is written to its slot
-  // at the end by the split that owns the slot (no other workgroup reads
-  // that slot in this step)
+  // the first block's loads are issued before the step's position arrives,
+  // bounded by the split's end in the cache (every such slot exists; those
+  // past the held ones are zeroed below), and before the step's decision
+  // (the new token's slot is patched afterwards); the new token's K/V row is
+  // written to its slot at the end by the split that owns the slot (no other
+  // workgroup reads that slot in this step)
   int blk = j_lo + wave * kBlk;
-  if (blk < j_hi) load_blk(blk);
+  const int j_cap = min(j_lo + a.spl, Bc);
+  if (blk < j_cap) load_blk(blk, j_cap);
   const Decision dc = decide_step(a, seg, p, s_worst);
   const int ns = dc.ns;
-  __syncthreads();   // every metadata read of this workgroup is done
-  if (tid == 0) {
-    if (a.nsplit == 1) {
-      apply_decision(a, seg, p, dc);
-    } else if (split == 0) {
-      int* rec = a.dec + seg * 4;
-      rec[0] = ns;
-      rec[1] = dc.u_slot;
-      rec[2] = dc.keep_u ? 1 : 0;
-      rec[3] = __float_as_int(dc.pu);
-    }
+  // The next step's record: this split's share of the scan for the worst
+  // long-range token after this step's update.  The metadata is read before
+  // anything updates it (with one split the update is applied at the end of
+  // this workgroup; with several, by the combine kernel); the first
+  // kRescanEarly slots per thread are loaded now, behind the K/V stream.
+  const bool track = a.state != nullptr && p >= 0;
+  const int* spos = a.slot_pos + seg * Bc;
+  const float* sprio = a.slot_prio + seg * Bc;
+  int r_sp[kRescanEarly];
+  float r_pr[kRescanEarly];
+#pragma unroll
+  for (int i = 0; i < kRescanEarly; ++i) {
+    const int j = j_lo + tid + i * kThreads;
+    const bool ok = track && j < j_hi;
+    r_sp[i] = ok ? spos[j] : -1;
+    r_pr[i] = ok ? sprio[j] : 0.0f;
+  }
+  if (tid == 0 && a.nsplit > 1 && split == 0) {
+    int* rec = a.dec + seg * 4;
+    rec[0] = ns;
+    rec[1] = dc.u_slot;
+    rec[2] = dc.keep_u ? 1 : 0;
+    rec[3] = __float_as_int(dc.pu);
   }
   ns_sub = ns;
+  if (blk < j_hi && blk + kBlk > j_hi) {
+    // the first block straddles the held slots' end (a filling cache): rows
+    // past it become zeros, as for every later block
+    if constexpr (!kF32) {
+      constexpr int PPR = D / 8;
+#pragma unroll
+      for (int i = 0; i < L::KPL; ++i)
+        if (blk + (lane + 64 * i) / PPR >= j_hi) kst[i] = make_uint4(0, 0, 0, 0);
+#pragma unroll
+      for (int i = 0; i < L::VTL; ++i) {
+        const int s0 = blk + 2 * ((lane + 64 * i) & 15);
+        const u32x4v z = {0u, 0u, 0u, 0u};
+        if (s0 >= j_hi) vpair[2 * i] = z;
+        if (s0 + 1 >= j_hi) vpair[2 * i + 1] = z;
+      }
+    } else {
+      constexpr int PPR = D / 4;
+#pragma unroll
+      for (int i = 0; i < L::KPL; ++i)
+        if (blk + (lane + 64 * i) / PPR >= j_hi) {
+          kst[i] = make_uint4(0, 0, 0, 0);
+          vst4[i] = make_uint4(0, 0, 0, 0);
+        }
+    }
+  }
   if (blk < j_hi && ns >= blk && ns < blk + kBlk) {
     // patch the new token's row into the first block (unconditional loads of
     // the one new row, then selects)
@@ -387,7 +465,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_attend_kernel(DecArgs a) {
   for (; blk < j_hi; blk += kWaves * kBlk) {
     store_blk();
     wave_lds_fence();
-    if (blk + kWaves * kBlk < j_hi) load_blk(blk + kWaves * kBlk);   // in flight during the math
+    if (blk + kWaves * kBlk < j_hi) load_blk(blk + kWaves * kBlk, j_hi);   // in flight during the math
 
     // ---- S^T = K Q^T (32 slots x 32 rows)
     f32x16 sacc = f32x16{};
@@ -503,6 +581,44 @@ __global__ __launch_bounds__(kThreads, 2) void decode_attend_kernel(DecArgs a) {
       pp[2 + d] = Od;
     }
   }
+  // this split's candidate for the next step's record (the slots loaded
+  // early, then the rest of its range, kDecideUnroll loads in flight)
+  if (track) {
+    Worst best{__builtin_huge_valf(), -1, -1};
+    const int u = p - a.w;
+#pragma unroll
+    for (int i = 0; i < kRescanEarly; ++i)
+      fold_candidate(best, j_lo + tid + i * kThreads, r_sp[i], r_pr[i], dc, a.s, u);
+    for (int j0 = j_lo + tid + kRescanEarly * kThreads; j0 < j_hi;
+         j0 += kThreads * kDecideUnroll) {
+      int sp[kDecideUnroll];
+      float pr[kDecideUnroll];
+#pragma unroll
+      for (int i = 0; i < kDecideUnroll; ++i) {
+        const int j = j0 + i * kThreads;
+        sp[i] = j < j_hi ? spos[j] : -1;
+        pr[i] = j < j_hi ? sprio[j] : 0.0f;
+      }
+#pragma unroll
+      for (int i = 0; i < kDecideUnroll; ++i)
+        fold_candidate(best, j0 + i * kThreads, sp[i], pr[i], dc, a.s, u);
+    }
+    wave_reduce_worst(best);
+    if (lane == 0) s_worst[wave] = best;
+    __syncthreads();
+    if (tid == 0) {
+      best = s_worst[0];
+#pragma unroll
+      for (int i = 1; i < kWaves; ++i)
+        if (worse_than(s_worst[i], best)) best = s_worst[i];
+      const int4 rec = make_int4(p + 1, __float_as_int(best.p), best.pos, best.slot);
+      if (nsplit == 1) *(int4*)(a.state + seg * kStateWords) = rec;
+      else *(int4*)(a.cand + (seg * nsplit + split) * 4) = rec;
+    }
+  }
+  // with one split the metadata update is this workgroup's (every read of
+  // the metadata above is complete)
+  if (tid == 0 && nsplit == 1) apply_decision(a, seg, p, dc);
   // the new token's K/V row into its slot, by the split that owns the slot
   if (ns >= j_lo && ns < j_hi) {
     constexpr int kWords = D * (kF32 ? 4 : 2) / 4;
@@ -517,6 +633,32 @@ __global__ __launch_bounds__(kThreads, 2) void decode_attend_kernel(DecArgs a) {
   }
 }
 
+// The metadata side of the combine for one (sequence, KV head): the step's
+// update (recorded by split 0; every split has read the metadata by now) and
+// the next step's record, the worst of the splits' candidates (wave 0, one
+// candidate per lane).
+__device__ __forceinline__ void combine_metadata(const DecArgs& a, int b, int h, int d) {
+  const size_t seg = (size_t)b * a.Hkv + h;
+  const int p = a.pos[b];
+  if (a.state && p >= 0 && d < 64) {
+    Worst best{__builtin_huge_valf(), -1, -1};
+    for (int j = d; j < a.nsplit; j += 64) {
+      const int4 c = *(const int4*)(a.cand + (seg * a.nsplit + j) * 4);
+      const Worst cw{__int_as_float(c.y), c.z, c.w};
+      if (worse_than(cw, best)) best = cw;
+    }
+    wave_reduce_worst(best);
+    if (d == 0)
+      *(int4*)(a.state + seg * kStateWords) =
+          make_int4(p + 1, __float_as_int(best.p), best.pos, best.slot);
+  }
+  if (d == 0) {
+    const int* rec = a.dec + seg * 4;
+    const Decision dc{rec[0], rec[1], __int_as_float(rec[3]), rec[2] != 0};
+    apply_decision(a, seg, p, dc);
+  }
+}
+
 // Merges the per-split partials into o and lse: one workgroup per
 // (sequence, query head), one thread per output dim, every partial of the
 // row read at once (the split maxima, sums and this dim's unnormalised O);
@@ -528,12 +670,7 @@ __global__ __launch_bounds__(D) void decode_combine_kernel(DecArgs a) {
   constexpr int RS = D + 2;
   const int hq = blockIdx.x, b = blockIdx.y, d = threadIdx.x;
   const int G = a.G, nsplit = a.nsplit;
-  if (hq % G == 0 && d == 0) {
-    const size_t seg = (size_t)b * a.Hkv + hq / G;
-    const int* rec = a.dec + seg * 4;
-    const Decision dc{rec[0], rec[1], __int_as_float(rec[3]), rec[2] != 0};
-    apply_decision(a, seg, a.pos[b], dc);
-  }
+  if (hq % G == 0) combine_metadata(a, b, hq / G, d);
   const size_t row = (size_t)b * a.Hq + hq;
   const float* pp = a.part + row * nsplit * RS;
   float m[kMaxSplit], l[kMaxSplit], od[kMaxSplit];
@@ -569,12 +706,7 @@ __global__ __launch_bounds__(D) void decode_combine_any_kernel(DecArgs a) {
   constexpr int RS = D + 2;
   const int hq = blockIdx.x, b = blockIdx.y, d = threadIdx.x;
   const int G = a.G, nsplit = a.nsplit;
-  if (hq % G == 0 && d == 0) {
-    const size_t seg = (size_t)b * a.Hkv + hq / G;
-    const int* rec = a.dec + seg * 4;
-    const Decision dc{rec[0], rec[1], __int_as_float(rec[3]), rec[2] != 0};
-    apply_decision(a, seg, a.pos[b], dc);
-  }
+  if (hq % G == 0) combine_metadata(a, b, hq / G, d);
   const size_t row = (size_t)b * a.Hq + hq;
   const float* pp = a.part + row * nsplit * RS;
   float M = kNegInf;
@@ -636,7 +768,7 @@ int decode_splits(const Dims& d) {
 size_t decode_ws_bytes(const Dims& d) {
   const int ns = decode_splits(d);
   return ns > 1 ? align256((size_t)d.b * d.Hq * ns * (d.D + 2) * 4) +
-                      align256((size_t)d.nseg() * 4 * 4)
+                      align256((size_t)d.nseg() * 4 * 4) + align256((size_t)d.nseg() * ns * 4 * 4)
                 : 0;
 }
 
@@ -652,6 +784,8 @@ hipError_t launch_decode(const Dims& d, const CacheArgs& c, const int* pos, cons
   a.part = (float*)ws;
   a.dec = nsplit > 1 ? (int*)((char*)ws + align256((size_t)d.b * d.Hq * nsplit * (d.D + 2) * 4))
                      : nullptr;
+  a.cand = nsplit > 1 ? a.dec + align256((size_t)d.nseg() * 4 * 4) / 4 : nullptr;
+  a.state = c.state;
   a.Hq = d.Hq; a.Hkv = d.Hkv; a.G = d.G; a.s = d.s; a.w = d.w; a.k = d.k;
   a.Bc = (int)d.budget(); a.spl = spl; a.nsplit = nsplit;
   a.scale_log2 = d.scale * 1.4426950408889634f;

@@ -21,7 +21,10 @@
 // block's slot metadata and ring entries and keeps the block's token
 // positions in LDS; after a barrier it copies its K and V rows, 16 bytes per
 // lane.  Decode then continues at p = S; while S < Bc the next tokens take
-// slots S, S+1, ... as in a decode that started at 0.
+// slots S, S+1, ... as in a decode that started at 0.  The pair's record of
+// the next step's worst long-range token is marked stale (step 0), so the
+// first step scans the slots.
+#include "kvpop.h"
 #include "kvpop_device.h"
 #include "kvpop_internal.h"
 
@@ -33,6 +36,7 @@ constexpr int kWaves = kThreads / 64;
 constexpr int kUnroll = 8;    // rank loads in flight per lane
 constexpr int kSlots = 512;   // cache slots per workgroup
 constexpr int kCopyUnroll = 4;
+constexpr int kStateWords = KVPOP_CACHE_STATE_WORDS;   // first word: the step it is for
 
 struct HandoffArgs {
   void* ck;
@@ -40,6 +44,7 @@ struct HandoffArgs {
   int* slot_pos;
   float* slot_prio;
   int* ring;
+  int* state;
   const void* k;
   const void* v;
   const float* prio;
@@ -63,6 +68,7 @@ __global__ __launch_bounds__(kThreads) void cache_from_prefill_kernel(HandoffArg
   int* spos = a.slot_pos + seg * Bc;
   float* sprio = a.slot_prio + seg * Bc;
   int* ring = a.ring + seg * w;
+  if (a.state && blockIdx.z == 0 && tid == 0) a.state[seg * kStateWords] = 0;
 
   const int n_sink = min(s, S);
   const int e_lo = s, e_hi = p - w;                    // E(p)
@@ -167,6 +173,7 @@ hipError_t launch_cache_from_prefill(const Dims& d, const CacheArgs& c, const vo
                                      const int* tau, hipStream_t st) {
   HandoffArgs a;
   a.ck = c.k; a.cv = c.v; a.slot_pos = c.slot_pos; a.slot_prio = c.slot_prio; a.ring = c.ring;
+  a.state = c.state;
   a.k = k; a.v = v; a.prio = prio; a.rank = rank; a.tau = tau;
   a.Hkv = d.Hkv; a.S = d.S; a.s = d.s; a.w = d.w; a.topk = d.k;
   a.Bc = (int)d.budget();

@@ -61,6 +61,7 @@ struct CacheArgs {
   int* slot_pos;
   float* slot_prio;
   int* ring;
+  int* state;   // may be null
 };
 int decode_splits(const Dims& d);
 size_t decode_ws_bytes(const Dims& d);

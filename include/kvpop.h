@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define KVPOP_ABI_VERSION 5
+#define KVPOP_ABI_VERSION 6
 
 typedef enum {
   KVPOP_OK = 0,
@@ -104,14 +104,26 @@ typedef struct {
  *   slot_pos   [batch, Hkv, Bc] int32: token position held by each slot
  *   slot_prio  [batch, Hkv, Bc] float: priority of the long-range token held
  *   ring       [batch, Hkv, w]  int32: slot of window position p mod w
+ *   state      [batch, Hkv, KVPOP_CACHE_STATE_WORDS] int32, or NULL: a record
+ *              derived from the arrays above that spares the next step a scan
+ *              of every slot: the step p + 1 it is for, then the priority
+ *              (float bits), position and slot of the worst held long-range
+ *              token after step p (slot -1: none), then spare words.  Each
+ *              decode step writes it for the next step; a step uses it only
+ *              when its first word equals the step's p, and otherwise scans
+ *              the slots (as every step does with NULL).  Zero-filled is
+ *              valid; kvpop_cache_from_prefill marks it stale.  Save and
+ *              restore it together with the other arrays.
  * Slots 0 .. min(p, Bc)-1 are the held tokens before step p; slot order is
  * unspecified. */
+#define KVPOP_CACHE_STATE_WORDS 8
 typedef struct {
   void* k;
   void* v;
   int32_t* slot_pos;
   float* slot_prio;
   int32_t* ring;
+  int32_t* state;
 } kvpop_cache;
 
 /* Bytes of scratch the call needs for problem `pr` (0 for an invalid problem). */

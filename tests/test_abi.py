@@ -26,7 +26,9 @@ def test_header_symbols_exported():
     assert declared == set(kv.EXPORTED_SYMBOLS)
     for name in declared:
         assert hasattr(L, name), name
-    assert kv.abi_version() == 5
+    assert kv.abi_version() == 6
+    words = re.search(r"#define KVPOP_CACHE_STATE_WORDS (\d+)", open(HEADER).read())
+    assert words and int(words.group(1)) == B.CACHE_STATE_WORDS
     assert L.kvpop_status_string(3).decode() == "workspace too small"
 
 

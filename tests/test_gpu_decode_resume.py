@@ -1,8 +1,9 @@
 """A decode run checkpointed to host memory and resumed in a fresh cache is
 bit-identical to the uninterrupted run.
 
-The cache arrays (K, V, slot positions and priorities, the window ring) are the
-whole decode state: the library keeps nothing between calls.  So copying them
+The cache arrays (K, V, slot positions and priorities, the window ring and the
+next step's record) are the whole decode state: the library keeps nothing
+between calls.  So copying them
 to the host at some position, restoring them into newly allocated device
 arrays and continuing must reproduce every later output and the final cache
 bit for bit, including across the fill (p < B) to steady-state boundary and
@@ -17,7 +18,7 @@ pytestmark = pytest.mark.gpu
 
 
 def _cache_arrays(c):
-    return (c.k, c.v, c.slot_pos, c.slot_prio, c.ring)
+    return c.arrays()
 
 
 @pytest.mark.parametrize("cut", [37, 150, 301])

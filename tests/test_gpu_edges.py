@@ -59,6 +59,11 @@ def test_decode_ties_bit_exact(case):
         Ks, Vs, Qs = (W.round_to_bf16(x) for x in (Ks, Vs, Qs))
     canon = orc.canonical_priority(prio_table)
     cache = kv.new_decode_cache(nseq, hkv, D, s, w, k, dtype=td, device=dev)
+    # the same steps on a cache without the next-step record (every full step
+    # scans its slots): outputs and arrays must agree bit for bit
+    bare = kv.new_decode_cache(nseq, hkv, D, s, w, k, dtype=td, device=dev)
+    bare.state = None
+    stale_at = {Bc + 3, steps - 7}   # steps entered with the record marked stale
     states = [[orc.DecodeState(s, w, k) for _ in range(hkv)] for _ in range(nseq)]
     tol = TOL[dt]
     n_equal_worst = 0   # leaving token equal to the worst held one (it must stay out)
@@ -71,13 +76,34 @@ def test_decode_ties_bit_exact(case):
                 if u >= s and len(st.long) == k and k > 0:
                     worst = min(st.long.values())
                     n_equal_worst += int(canon[bi, h, u] == worst)
-        o, lse = kv.decode_step(cache, to_dev(np.full(nseq, p, np.int32)), to_dev(Qs[p], td),
-                                to_dev(np.ascontiguousarray(Ks[:, :, p]), td),
-                                to_dev(np.ascontiguousarray(Vs[:, :, p]), td), to_dev(pl),
-                                s, w, k)
+        if p in stale_at:
+            cache.state[..., 0] = 0
+        args = (to_dev(np.full(nseq, p, np.int32)), to_dev(Qs[p], td),
+                to_dev(np.ascontiguousarray(Ks[:, :, p]), td),
+                to_dev(np.ascontiguousarray(Vs[:, :, p]), td), to_dev(pl), s, w, k)
+        o, lse = kv.decode_step(cache, *args)
+        o2, lse2 = kv.decode_step(bare, *args)
+        assert torch.equal(o.view(torch.int32), o2.view(torch.int32)), p
+        assert torch.equal(lse.view(torch.int32), lse2.view(torch.int32)), p
+        for x, y in zip(cache.arrays()[:5], bare.arrays()):
+            assert torch.equal(x.view(torch.uint8), y.view(torch.uint8)), p
         for bi in range(nseq):
             for h in range(hkv):
                 states[bi][h].step(p, float(prio_table[bi, h, u]) if u >= s else float("nan"))
+        # the record for step p + 1: the worst held long-range token (lowest
+        # priority, ties to the highest position), or none
+        rec = host(cache.state)
+        for bi in range(nseq):
+            for h in range(hkv):
+                lr = states[bi][h].long
+                r = rec[bi, h]
+                assert r[0] == p + 1, (p, bi, h)
+                if not lr:
+                    assert r[3] == -1, (p, bi, h)
+                    continue
+                t = min(lr, key=lambda x: (lr[x], -x))
+                assert r[2] == t and r[1] == _bits(canon[bi, h, t]).view(np.int32), (p, bi, h)
+                assert host(cache.slot_pos)[bi, h, r[3]] == t, (p, bi, h)
         n = min(p + 1, Bc)
         sp, spr = host(cache.slot_pos), host(cache.slot_prio)
         oh, lh = host(o), host(lse)

@@ -21,7 +21,7 @@ def _same_cache(a, b):
     return all(torch.equal(x, y) for x, y in
                ((a.k, b.k), (a.v, b.v), (a.slot_pos, b.slot_pos),
                 (a.slot_prio.view(torch.int32), b.slot_prio.view(torch.int32)),
-                (a.ring, b.ring)))
+                (a.ring, b.ring), (a.state, b.state)))
 
 
 @pytest.mark.parametrize("per_graph", [1, 4])

@@ -41,7 +41,7 @@ def _run(nseq, hq, hkv, D, s, w, k, steps, cdt, odt, seed):
         mismatch += (~torch.eq(oa, ob)).sum() + (~torch.eq(la, lb)).sum()
     torch.cuda.synchronize()
     assert int(mismatch) == 0
-    for name in ("k", "v", "slot_pos", "slot_prio", "ring"):
+    for name in ("k", "v", "slot_pos", "slot_prio", "ring", "state"):
         assert torch.equal(getattr(ca, name), getattr(cb, name)), name
     # the cache filled and then evicted: every slot holds a token
     assert int((ca.slot_pos >= 0).sum()) == nseq * hkv * min(steps, Bc)
