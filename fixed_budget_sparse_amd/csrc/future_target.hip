@@ -331,8 +331,9 @@ __global__ __launch_bounds__(kThreads, 2) void future_target_kernel(TgtArgs a) {
   };
   // The MFMAs of one block interleaved with the exp work of another
   // (independent) block, in a fixed order so the matrix and vector units run
-  // together: all operand reads first, then 8 groups of two MFMAs and four
-  // scores (fma, exp2, add) each, pinned with scheduling barriers.
+  // together: the first operand reads and the block's biases first, then 8
+  // groups of two MFMAs and four scores (fma, exp2, add) each, pinned with
+  // scheduling barriers.
   auto fused = [&](auto doM, auto doE, auto maskE, f32x16 (&accM)[kRB], int mbuf, int mcb,
                    const f32x16 (&accE)[kRB], int eslot, int ecb, int d0E) {
     constexpr bool kM = decltype(doM)::value, kE = decltype(doE)::value;
@@ -341,23 +342,24 @@ __global__ __launch_bounds__(kThreads, 2) void future_target_kernel(TgtArgs a) {
     constexpr int kPer = 32 / NK;            // scores per group: 4, all with one bias vector
     const uint16_t* ql = (const uint16_t*)q_lds[mbuf] + (32 * mcb + li) * Gm::QS + 8 * hh;
     const float* nb = &nlse[eslot][32 * ecb + 4 * hh];
-    // operands two k-steps ahead, bias one group ahead; each group reads its
-    // bias before its operand, so the next group waits only for the bias and
-    // the operand read stays in flight
+    // operands two k-steps ahead; the block's biases (four vectors per lane:
+    // its columns 8j + 4hh + r, shared by both row blocks) are read once, at
+    // the start, instead of once per group
     bf16x8 a0{}, a1{};
-    f32x4 b0{};
+    f32x4 bb[4] = {};
+    if constexpr (kE) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) bb[j] = *(const f32x4*)(nb + 8 * j);
+    }
     if constexpr (kM) {
       a0 = as_bf16x8(*(const uint4*)(ql));
       a1 = as_bf16x8(*(const uint4*)(ql + 16));
       accM[0] = accM[1] = f32x16{};
     }
-    if constexpr (kE) b0 = *(const f32x4*)(nb);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int ks = 0; ks < NK; ++ks) {
-      f32x4 b1 = b0;
-      if constexpr (kE)
-        if (ks + 1 < NK) b1 = *(const f32x4*)(nb + 8 * ((((ks + 1) * kPer) & 15) >> 2));
+      const f32x4 b0 = bb[ks & 3];
       bf16x8 a2 = a1;
       if constexpr (kM)
         if (ks + 2 < NK) a2 = as_bf16x8(*(const uint4*)(ql + 16 * (ks + 2)));
@@ -379,7 +381,16 @@ __global__ __launch_bounds__(kThreads, 2) void future_target_kernel(TgtArgs a) {
       }
       a0 = a1;
       a1 = a2;
-      b0 = b1;
+      // within the group: one MFMA, half the scores' VALU work, the other
+      // MFMA, the rest (each MFMA then has VALU work of this wave to overlap;
+      // two MFMAs back to back measured 2-4 % slower)
+      if constexpr (kM && kE) {
+        constexpr int kV = kMask ? 12 : 6;
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, kV, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, kV, 0);
+      }
       __builtin_amdgcn_sched_barrier(0);
     }
   };
