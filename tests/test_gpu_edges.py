@@ -158,6 +158,10 @@ def test_handoff_then_decode_ties():
     for bi in range(nseq):
         for h in range(hkv):
             assert sorted(sp[bi, h, :n].tolist()) == states[bi][h].held().tolist(), (bi, h)
+    # the handoff marks the next-step record stale: the first step scans the
+    # slots, and every step leaves the record of the worst long-range token
+    assert (host(cache.state)[..., 0] == 0).all()
+    canon = orc.canonical_priority(prio)
     for p in range(S, T):
         u = p - w
         o, lse = kv.decode_step(cache, to_dev(np.full(nseq, p, np.int32)), to_dev(Qd[p], td),
@@ -178,6 +182,13 @@ def test_handoff_then_decode_ties():
             oo, ll = orc.decode_attention(Qd[p, bi], K[bi], V[bi], held)
             assert np.abs(host(o)[bi] - oo).max() <= TOL["bf16"]["o"], (p, bi)
             assert np.abs(host(lse)[bi] - ll).max() <= TOL["bf16"]["lse"], (p, bi)
+        rec = host(cache.state)
+        for bi in range(nseq):
+            for h in range(hkv):
+                lr = states[bi][h].long
+                t = min(lr, key=lambda x: (lr[x], -x))
+                assert rec[bi, h, 0] == p + 1 and rec[bi, h, 2] == t, (p, bi, h)
+                assert rec[bi, h, 1] == _bits(canon[bi, h, t]).view(np.int32), (p, bi, h)
 
 
 def test_tiny_workload_seed0():
