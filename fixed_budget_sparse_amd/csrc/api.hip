@@ -147,6 +147,7 @@ KVPOP_EXPORT kvpop_status kvpop_decode_step(const kvpop_problem* pr, const kvpop
   if (st != KVPOP_OK) return st;
   if (!cache || !cache->k || !cache->v || !cache->slot_pos || !cache->slot_prio || !cache->ring)
     return KVPOP_ERR_ARG;
+  if ((uintptr_t)cache->state % 16 != 0) return KVPOP_ERR_ARG;   // read as 16-byte records
   if (!pos || !q || !k_new || !v_new || !prio_leaving || !o) return KVPOP_ERR_ARG;
   st = check_ws(KVPOP_CALL_DECODE, d, ws, ws_bytes_);
   if (st != KVPOP_OK) return st;
@@ -165,6 +166,7 @@ KVPOP_EXPORT kvpop_status kvpop_decode_step_noalloc(const kvpop_problem* pr,
   if (st != KVPOP_OK) return st;
   if (!cache || !cache->k || !cache->v || !cache->slot_pos || !cache->slot_prio || !cache->ring)
     return KVPOP_ERR_ARG;
+  if ((uintptr_t)cache->state % 16 != 0) return KVPOP_ERR_ARG;   // read as 16-byte records
   if (!pos || !q || !k_new || !v_new || !prio_leaving || !o) return KVPOP_ERR_ARG;
   const size_t need = ws_bytes(KVPOP_CALL_DECODE, d);
   if (need > kvpop::decode_noalloc_scratch_bytes()) return KVPOP_ERR_SCRATCH;
@@ -185,6 +187,7 @@ KVPOP_EXPORT kvpop_status kvpop_cache_from_prefill(const kvpop_problem* pr,
   if (st != KVPOP_OK) return st;
   if (!cache || !cache->k || !cache->v || !cache->slot_pos || !cache->slot_prio || !cache->ring)
     return KVPOP_ERR_ARG;
+  if ((uintptr_t)cache->state % 16 != 0) return KVPOP_ERR_ARG;   // read as 16-byte records
   if (!k || !v || !prio || !rank || !tau) return KVPOP_ERR_ARG;
   kvpop::CacheArgs c{cache->k, cache->v, cache->slot_pos, cache->slot_prio, cache->ring,
                      cache->state};

@@ -113,7 +113,8 @@ typedef struct {
  *              when its first word equals the step's p, and otherwise scans
  *              the slots (as every step does with NULL).  Zero-filled is
  *              valid; kvpop_cache_from_prefill marks it stale.  Save and
- *              restore it together with the other arrays.
+ *              restore it together with the other arrays.  16-byte aligned
+ *              (KVPOP_ERR_ARG otherwise).
  * Slots 0 .. min(p, Bc)-1 are the held tokens before step p; slot order is
  * unspecified. */
 #define KVPOP_CACHE_STATE_WORDS 8

@@ -123,6 +123,28 @@ def test_decode_noalloc_error_paths():
                                        vp(0)) == 1
 
 
+def test_cache_state_alignment_refused():
+    """A cache state array not aligned to 16 bytes (its records are read 16
+    bytes at a time) is refused by every call that takes a cache, before any
+    launch; NULL is accepted (every full step then scans the slots)."""
+    L = _lib()
+    vp = ctypes.c_void_p
+    bad = B._Cache(1, 1, 1, 1, 1, 8)
+    c = _pr().c()
+    assert L.kvpop_decode_step(ctypes.byref(c), ctypes.byref(bad), *[vp(1)] * 8, 1 << 20,
+                               vp(0)) == 1
+    assert L.kvpop_decode_step_noalloc(ctypes.byref(c), ctypes.byref(bad), *[vp(1)] * 7,
+                                       vp(0)) == 1
+    cp = _pr(n_q_heads=8).c()
+    assert L.kvpop_cache_from_prefill(ctypes.byref(cp), ctypes.byref(bad), *[vp(1)] * 5,
+                                      vp(0)) == 1
+    # a NULL state passes the cache checks: the no-alloc call then refuses
+    # the oversized problem for its scratch, not for the cache
+    big = _pr(batch=4, n_q_heads=256, n_kv_heads=8, topk=1 << 16).c()
+    assert L.kvpop_decode_step_noalloc(ctypes.byref(big), ctypes.byref(B._Cache(1, 1, 1, 1, 1)),
+                                       *[vp(1)] * 7, vp(0)) == 5
+
+
 def test_label_error_paths():
     L = _lib()
     vp = ctypes.c_void_p
