@@ -592,18 +592,34 @@ __global__ __launch_bounds__(256) void bwd_dkdv_merge_kernel(BwdArgs a) {
   const int S = a.S;
   const size_t kvbase = (size_t)sg * S * D;
   const float* src = a.part1 + ((size_t)sg * a.ktiles + tile) * kKTile * 2 * D;
-  constexpr int PPK = 2 * D / 4;   // float4 pieces per key (dK then dV)
-  for (int task = threadIdx.x; task < kKTile * PPK; task += 256) {
-    const int j = task / PPK, pc = task % PPK;
-    const int slot = tile * kKTile + j;
-    if (slot >= S) continue;
-    const int t = a.korder[(size_t)sg * S + slot];
-    if (t < 0) continue;
-    float* dst = (pc < D / 4 ? a.dk : a.dv) + kvbase + (size_t)t * D + 4 * (pc % (D / 4));
-    const float4 x = *(const float4*)(src + (size_t)j * 2 * D + 4 * pc);
-    float4 y = *(float4*)dst;
-    y.x += x.x; y.y += x.y; y.z += x.z; y.w += x.w;
-    *(float4*)dst = y;
+  constexpr int PPK = 2 * D / 4;          // float4 pieces per key (dK then dV)
+  constexpr int KPI = 256 / PPK;          // keys per pass of the workgroup
+  constexpr int NIT = kKTile / KPI;       // passes
+  constexpr int kU = 8;                   // passes in flight: their key, part and row reads issued together
+  static_assert(NIT % kU == 0, "merge passes");
+  const int pc = threadIdx.x % PPK, j0 = threadIdx.x / PPK;
+  const size_t col = 4 * (pc % (D / 4));
+  float* base = pc < D / 4 ? a.dk : a.dv;
+  for (int i0 = 0; i0 < NIT; i0 += kU) {
+    int t[kU];
+    float4 x[kU], y[kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int j = j0 + KPI * (i0 + u);
+      const int slot = tile * kKTile + j;
+      t[u] = slot < S ? a.korder[(size_t)sg * S + slot] : -1;
+      x[u] = *(const float4*)(src + (size_t)j * 2 * D + 4 * pc);
+    }
+#pragma unroll
+    for (int u = 0; u < kU; ++u)
+      y[u] = t[u] >= 0 ? *(const float4*)(base + kvbase + (size_t)t[u] * D + col)
+                       : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      if (t[u] < 0) continue;
+      y[u].x += x[u].x; y[u].y += x[u].y; y[u].z += x[u].z; y[u].w += x[u].w;
+      *(float4*)(base + kvbase + (size_t)t[u] * D + col) = y[u];
+    }
   }
 }
 
