@@ -124,6 +124,40 @@ struct KeyBuckets {
   }
 };
 
+// Exclusive prefix sums of cnt[0 .. n) into off[0 .. n) by all 1024 threads
+// of the workgroup (n <= 8192): with rev, in descending index order (off[i]
+// = the sum of cnt[j] for j > i).  Integer sums: the same offsets as a serial
+// pass.  cnt and off must not overlap; wtot holds 16 wave totals.
+__device__ void block_excl_scan_1024(const int* cnt, int* off, int n, int* wtot, bool rev) {
+  constexpr int kPer = 8;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int v[kPer];
+  int local = 0;
+#pragma unroll
+  for (int u = 0; u < kPer; ++u) {
+    const int i = tid * kPer + u;
+    v[u] = i < n ? cnt[rev ? n - 1 - i : i] : 0;
+    local += v[u];
+  }
+  int incl = local;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(incl, o);
+    if (lane >= o) incl += y;
+  }
+  if (lane == 63) wtot[wave] = incl;
+  __syncthreads();
+  int run = incl - local;
+  for (int j = 0; j < wave; ++j) run += wtot[j];
+#pragma unroll
+  for (int u = 0; u < kPer; ++u) {
+    const int i = tid * kPer + u;
+    if (i < n) off[rev ? n - 1 - i : i] = run;
+    run += v[u];
+  }
+  __syncthreads();
+}
+
 // Key order of the dK/dV tiles, one workgroup per (sequence, KV head): a
 // counting sort over the KeyBuckets (order inside a bucket is free: a key's
 // sums do not depend on its tile).
@@ -131,6 +165,7 @@ __global__ __launch_bounds__(1024) void bwd_key_order_kernel(const int* __restri
                                                              int* __restrict__ korder, int S,
                                                              int w) {
   extern __shared__ int bk[];       // nb counters, then nb offsets
+  __shared__ int wtot[16];
   const int seg = blockIdx.x, tid = threadIdx.x;
   const KeyBuckets kb(S);
   const int nb = kb.nb;
@@ -144,15 +179,7 @@ __global__ __launch_bounds__(1024) void bwd_key_order_kernel(const int* __restri
   };
   for (int t = tid; t < S; t += 1024) atomicAdd(&bk[bucket(t)], 1);
   __syncthreads();
-  if (tid == 0) {                   // exclusive scan (nb <= S / 64 + 512)
-    int run = 0;
-    for (int i = 0; i < nb; ++i) {
-      const int c = bk[i];
-      bk[nb + i] = run;
-      run += c;
-    }
-  }
-  __syncthreads();
+  block_excl_scan_1024(bk, bk + nb, nb, wtot, false);   // nb <= S / 64 + 512
   for (int t = tid; t < S; t += 1024) out[atomicAdd(&bk[nb + bucket(t)], 1)] = t;
 }
 
@@ -523,6 +550,7 @@ __global__ __launch_bounds__(1024) void bwd_tile_plan_kernel(const int* __restri
                                                              int4* __restrict__ plan,
                                                              int* __restrict__ tsplit) {
   extern __shared__ int hist[];     // nbins counters, then nbins offsets
+  __shared__ int wtot[16];
   const int seg = blockIdx.x, tid = threadIdx.x, lane = lane_id(), wave = wave_id();
   const int nbins = plan_bins(S);     // chunk counts, the longest in one bin
   const int n_ent = 2 * ktiles;
@@ -569,14 +597,7 @@ __global__ __launch_bounds__(1024) void bwd_tile_plan_kernel(const int* __restri
     }
   }
   __syncthreads();
-  if (tid == 0) {   // offsets, longest first
-    int run = 0;
-    for (int i = nbins - 1; i >= 0; --i) {
-      hist[nbins + i] = run;
-      run += hist[i];
-    }
-  }
-  __syncthreads();
+  block_excl_scan_1024(hist, hist + nbins, nbins, wtot, true);   // offsets, longest first
   for (int i = tid; i < n_ent; i += 1024) {
     const int4 e = tm[i];
     pl[atomicAdd(&hist[nbins + min(e.w - e.z, nbins - 1)], 1)] = e;
