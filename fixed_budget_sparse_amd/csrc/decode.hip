@@ -664,13 +664,16 @@ __device__ __forceinline__ void combine_metadata(const DecArgs& a, int b, int h,
 // row read at once (the split maxima, sums and this dim's unnormalised O);
 // the workgroup of the first query head of each KV head also applies the
 // step's metadata update (recorded by split 0: every split has read the
-// metadata by now).
+// metadata by now) and writes the next step's record, the worst of the
+// splits' candidates (wave 0, one candidate per lane).  Every load of the
+// workgroup is issued before its first store, so the metadata costs no
+// round trip of its own.
 template <int D, bool kF32Out, int kMaxSplit>
 __global__ __launch_bounds__(D) void decode_combine_kernel(DecArgs a) {
+  static_assert(kMaxSplit <= 64, "one split candidate per lane of wave 0");
   constexpr int RS = D + 2;
   const int hq = blockIdx.x, b = blockIdx.y, d = threadIdx.x;
   const int G = a.G, nsplit = a.nsplit;
-  if (hq % G == 0) combine_metadata(a, b, hq / G, d);
   const size_t row = (size_t)b * a.Hq + hq;
   const float* pp = a.part + row * nsplit * RS;
   float m[kMaxSplit], l[kMaxSplit], od[kMaxSplit];
@@ -680,6 +683,15 @@ __global__ __launch_bounds__(D) void decode_combine_kernel(DecArgs a) {
     m[j] = ok ? pp[j * RS] : kNegInf;
     l[j] = ok ? pp[j * RS + 1] : 0.0f;
     od[j] = ok ? pp[j * RS + 2 + d] : 0.0f;
+  }
+  const bool meta = hq % G == 0;
+  const size_t seg = (size_t)b * a.Hkv + hq / G;
+  int p = -1;
+  int4 rec = make_int4(-1, -1, 0, 0), cnd = make_int4(0, 0, -1, -1);
+  if (meta) {
+    p = a.pos[b];
+    rec = *(const int4*)(a.dec + seg * 4);
+    if (a.state && d < nsplit) cnd = *(const int4*)(a.cand + (seg * nsplit + d) * 4);
   }
   float M = kNegInf;
 #pragma unroll
@@ -697,6 +709,17 @@ __global__ __launch_bounds__(D) void decode_combine_kernel(DecArgs a) {
   if constexpr (kF32Out) ((float*)a.o)[row * D + d] = Od * inv;
   else ((__bf16*)a.o)[row * D + d] = (__bf16)(Od * inv);
   if (d == 0 && a.lse) a.lse[row] = Ls > 0.0f ? (M + log2f(Ls)) * kLn2 : kNegInf;
+  if (!meta) return;
+  if (a.state && p >= 0 && d < 64) {
+    Worst best{__builtin_huge_valf(), -1, -1};
+    const Worst cw{__int_as_float(cnd.y), cnd.z, cnd.w};
+    if (d < nsplit && worse_than(cw, best)) best = cw;
+    wave_reduce_worst(best);
+    if (d == 0)
+      *(int4*)(a.state + seg * kStateWords) =
+          make_int4(p + 1, __float_as_int(best.p), best.pos, best.slot);
+  }
+  if (d == 0) apply_decision(a, seg, p, Decision{rec.x, rec.y, __int_as_float(rec.w), rec.z != 0});
 }
 
 // The same merge for any number of splits (more than the unrolled variants
