@@ -220,6 +220,8 @@ DEC_CASES = [
     (1, 2, 1, 128, 1, 2, 300, 200, "bf16"),    # budget larger than the run: 3 splits, partial fill
     (2, 8, 2, 64, 3, 20, 400, 640, "f32"),     # 4 splits past the fill, D = 64, float32
     (1, 4, 1, 128, 4, 300, 0, 420, "bf16"),    # 3 splits past the fill, k = 0
+    (1, 2, 1, 64, 2, 30, 1568, 1700, "bf16"),  # one pair, B = 1600: 13 splits (the 16-split merge)
+    (1, 2, 1, 64, 2, 30, 2268, 2400, "bf16"),  # one pair, B = 2300: 18 splits (the looping merge)
 ]
 
 
